@@ -1,0 +1,387 @@
+"""Float64 reference of the mHC and xHC residual-stream layer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Notation follows the pages: a token's state is X in R^{N x C} (N streams of
+C channels); vec X is its stream-major flattening (index i*C + c); the
+sublayer F is given, so its output ``out`` is an input here.  Tokens are
+batched as T = B*S rows in batch-major order (t = b*S + s); only the causal
+convolution looks across tokens, and only within one batch item.
+
+Readings of points the pages leave open are listed in the design notes and
+repeated at the function that takes them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+EPS_NORM = 1e-6   # RMSNorm / LayerNorm epsilon (explainer, "What xHC changes")
+EPS_MGS = 1e-6    # Gram-Schmidt epsilon on <v, v> (same listing; the paper
+                  # text leaves it unstated: explainer, "What I could not check")
+
+
+# --------------------------------------------------------------------------
+# elementary pieces
+# --------------------------------------------------------------------------
+
+def sigmoid(z):
+    """Logistic function 1 / (1 + e^{-z}), evaluated without overflow."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def rms_normalize(v, eps=EPS_NORM):
+    """x / sqrt(mean(x^2) + eps) over the last axis, no gain.
+
+    The RMSNorm that feeds the pre-map and the active-stream maps
+    (explainer, "What xHC changes"; xHC paper, "Mapping generation").
+    """
+    v = np.asarray(v, dtype=np.float64)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps)
+
+
+def ln_normalize(v, eps=EPS_NORM):
+    """(x - mean) / (population std + eps) over the last axis, no affine.
+
+    The LayerNorm of the router (explainer, "What xHC changes"; summary
+    3.4.1).  Reading: the std is the population one and eps is added to the
+    std, not to the variance, as in the explainer's sublayer code.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    mu = np.mean(v, axis=-1, keepdims=True)
+    sd = np.sqrt(np.mean((v - mu) ** 2, axis=-1, keepdims=True))
+    return (v - mu) / (sd + eps)
+
+
+def sinkhorn(logits, iters):
+    """Sinkhorn-Knopp projection of a (batch of) square logit matrices.
+
+    Exponentiate (after subtracting the largest logit of each matrix, which
+    changes nothing mathematically), then ``iters`` times: divide every
+    column by its sum, then every row by its sum.  Rows are normalised last,
+    so every row sums to one and the residual error sits on the columns
+    (explainer, "mHC: keep the mixing doubly stochastic"; xHC paper,
+    "Manifold-Constrained HC").
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    M = np.exp(L - L.max(axis=(-2, -1), keepdims=True))
+    for _ in range(iters):
+        M = M / M.sum(axis=-2, keepdims=True)   # columns
+        M = M / M.sum(axis=-1, keepdims=True)   # rows
+    return M
+
+
+def row_clamp(H):
+    """Divide each row by max(row sum, 1).
+
+    The post-Sinkhorn patch of xHC's appendix A as reported in the explainer
+    ("Which constraint survives").  Reading: applied to xHC's k x k map only.
+    """
+    H = np.asarray(H, dtype=np.float64)
+    rs = H.sum(axis=-1, keepdims=True)
+    return H / np.maximum(rs, 1.0)
+
+
+def round_to_bf16(x):
+    """Round float64 values to the nearest bfloat16 (ties to even), as float64.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range; values
+    here are far from its subnormal and overflow ranges.  Rounding is done
+    directly from float64 (no float32 step, so no double rounding).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                 # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.rint(m * 256.0)             # 8 significant bits, ties to even
+    return np.ldexp(q / 256.0, e)
+
+
+def round_state(x, dtype):
+    """Round once to the state dtype ('bf16' or 'f32'), returned as float64."""
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# mHC (dense N x N mixing)
+# --------------------------------------------------------------------------
+
+def mhc_pre(X, W_full, alpha, b_pre, b_post, b_res, iters=20):
+    """mHC mapping generation and dense read for T tokens.
+
+    X: [T, N, C].  W_full: [N*C, 2N + N^2], columns ordered pre | post | res
+    (res row-major, entry (i, j) at column 2N + i*N + j).
+    alpha = (alpha_pre, alpha_post, alpha_res).
+
+    x' = RMSNorm(vec X); one projection gives the three logit groups;
+    H_pre = sigmoid, H_post = 2*sigmoid, H_res = Sinkhorn; every logit is
+    alpha * (x' W) + b (xHC paper, "Manifold-Constrained HC"; summary 3.1;
+    explainer, "mHC: keep the mixing doubly stochastic").  The sublayer input
+    is the H_pre-weighted sum of the N streams (summary 3.1).
+
+    Returns inp [T, C], H_pre [T, N], H_post [T, N], H_res [T, N, N].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    T, N, C = X.shape
+    a_pre, a_post, a_res = alpha
+    x = X.reshape(T, N * C)
+    z = rms_normalize(x) @ np.asarray(W_full, dtype=np.float64)
+    h_pre = sigmoid(a_pre * z[:, :N] + np.asarray(b_pre))
+    h_post = 2.0 * sigmoid(a_post * z[:, N:2 * N] + np.asarray(b_post))
+    L = a_res * z[:, 2 * N:].reshape(T, N, N) + np.asarray(b_res).reshape(N, N)
+    H_res = sinkhorn(L, iters)
+    inp = np.einsum("tn,tnc->tc", h_pre, X)
+    return inp, h_pre, h_post, H_res
+
+
+def mhc_post(X, out, H_post, H_res):
+    """mHC write-back and mix: row i of the new state is
+    sum_j H_res[i, j] X_j + H_post[i] * out  (xHC paper, "Hyper-Connections"
+    and "Information Supply Bottleneck"; summary 3.1-3.2).
+
+    X: [T, N, C]; out: [T, C].  Returns the unrounded new state.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    mixed = np.einsum("tij,tjc->tic", H_res, X)
+    return mixed + H_post[:, :, None] * out[:, None, :]
+
+
+# --------------------------------------------------------------------------
+# xHC (router, dense read, sparse k x k mix, temporal augmentation)
+# --------------------------------------------------------------------------
+
+def xhc_router_logits(X, W_r):
+    """z = LN(vec X) W_r, one logit per stream (summary 3.4.1; explainer,
+    "What xHC changes").  No scale or bias.  Returns [T, N]."""
+    X = np.asarray(X, dtype=np.float64)
+    T, N, C = X.shape
+    return ln_normalize(X.reshape(T, N * C)) @ np.asarray(W_r, dtype=np.float64)
+
+
+def xhc_select(z, m, k):
+    """Fixed-m plus routed top-(k-m) active set and router weights.
+
+    Streams 0..m-1 are always active; the k-m streams of m..N-1 with the
+    largest score join them (summary 3.4.1; explainer, "What xHC changes").
+    The score is sigmoid(z); ranking uses z itself, which orders identically
+    and does not saturate.  Reading: the routed streams are listed by
+    descending score, ties to the lower stream index; p is 1 for fixed
+    streams and the sigmoid score for routed ones.
+
+    Returns I [T, k] (int64) and p [T, k].
+    """
+    z = np.asarray(z, dtype=np.float64)
+    T, N = z.shape
+    I = np.empty((T, k), dtype=np.int64)
+    p = np.empty((T, k), dtype=np.float64)
+    s = sigmoid(z)
+    for t in range(T):
+        I[t, :m] = np.arange(m)
+        cand = list(range(m, N))
+        # descending z, ties -> lower index
+        cand.sort(key=lambda i: (-z[t, i], i))
+        I[t, m:] = cand[: k - m]
+    p[:, :m] = 1.0
+    if k > m:
+        p[:, m:] = np.take_along_axis(s, I[:, m:], axis=1)
+    return I, p
+
+
+def xhc_topk_margin(z, m, k):
+    """Smallest gap between consecutive routed logits among the top k-m+1
+    candidates: when it is positive the routed set and its order are unique.
+    Returns +inf where no routed choice exists (k == m or N - m == k - m)."""
+    z = np.asarray(z, dtype=np.float64)
+    T, N = z.shape
+    r = k - m
+    if r == 0 or N - m <= r:
+        return np.full(T, np.inf)
+    zs = -np.sort(-z[:, m:], axis=1)[:, : r + 1]
+    return np.min(zs[:, :-1] - zs[:, 1:], axis=1)
+
+
+def xhc_pre(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, iters=20):
+    """xHC mapping generation and dense read for T tokens.
+
+    X: [T, N, C].
+    W_full: [N*C, 2N]; columns 0..N-1 are the router W_r, N..2N-1 the
+        pre-map W_pre (rows stream-major).
+    W_act: [k*C, k*k + k*K_r]; rows j*C + c for position j of the active
+        list; columns 0..k^2-1 are W_res (entry (i, j) at i*k + j), then
+        W_post (entry (j, r) at k^2 + j*K_r + r).
+    alpha = (alpha_pre, alpha_res, alpha_post); the router has none.
+
+    Steps (summary 3.4.1-3.4.3; xHC paper, "Mapping generation";
+    explainer, "What xHC changes"):
+      router: z = LN(vec X) W_r; I, p by fixed-m + routed top-(k-m);
+      dense read: H_pre = sigmoid(alpha_pre * RMSNorm(vec X) W_pre + b_pre),
+                  inp = sum_i H_pre[i] X_i over all N streams;
+      active maps from X_act = X[I] (k x C), x~ = RMSNorm(vec X_act):
+        H_res  = rowclamp(SK(alpha_res * mat_kxk(x~ W_res) + b_res)),
+        H_post = 2 sigmoid(alpha_post * mat_kxK_r(x~ W_post) + b_post).
+
+    Returns dict with inp [T,C], z [T,N], I [T,k], p [T,k], h_pre [T,N],
+    h_res [T,k,k], h_post [T,k,K_r].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W_full = np.asarray(W_full, dtype=np.float64)
+    W_act = np.asarray(W_act, dtype=np.float64)
+    T, N, C = X.shape
+    a_pre, a_res, a_post = alpha
+    x = X.reshape(T, N * C)
+
+    z = ln_normalize(x) @ W_full[:, :N]
+    I, p = xhc_select(z, m, k)
+
+    h_pre = sigmoid(a_pre * (rms_normalize(x) @ W_full[:, N:2 * N]) + np.asarray(b_pre))
+    inp = np.einsum("tn,tnc->tc", h_pre, X)
+
+    Xa = np.take_along_axis(X, I[:, :, None], axis=1)          # [T, k, C]
+    la = rms_normalize(Xa.reshape(T, k * C)) @ W_act            # [T, k^2 + k K_r]
+    L = a_res * la[:, : k * k].reshape(T, k, k) + np.asarray(b_res).reshape(k, k)
+    h_res = row_clamp(sinkhorn(L, iters))
+    h_post = 2.0 * sigmoid(a_post * la[:, k * k:].reshape(T, k, K_r)
+                           + np.asarray(b_post).reshape(k, K_r))
+    return dict(inp=inp, z=z, I=I, p=p, h_pre=h_pre, h_res=h_res, h_post=h_post)
+
+
+def causal_dwconv(out, w):
+    """Causal depthwise 1-D convolution along the sequence.
+
+    out: [B, S, C]; w: [kappa, C].  g[b, t] = sum_{i<kappa} w[i] * out[b, t-i],
+    with out[b, t'] = 0 for t' < 0 (no history before a sequence starts, and
+    nothing crosses batch items).  Reading: w[i] multiplies lag i, no bias
+    (explainer, "What xHC changes"; summary 3.3).
+    """
+    out = np.asarray(out, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, S, C = out.shape
+    g = np.zeros_like(out)
+    for i in range(w.shape[0]):
+        if i >= S:
+            break
+        g[:, i:, :] += w[i][None, None, :] * out[:, : S - i, :]
+    return g
+
+
+def gram_schmidt(comps, eps=EPS_MGS):
+    """Modified Gram-Schmidt along C, token by token, without normalisation.
+
+    comps: list [out, g_1, ..., g_r] of [..., C] arrays.  v_1 = out; for each
+    g_j in order, the projection on each earlier v_i is removed one at a time
+    from the running vector, u <- u - <u, v_i> / (<v_i, v_i> + eps) v_i, and
+    the result is v_{j+1} (summary 3.3; explainer, "What xHC changes").
+    """
+    vs = [np.asarray(comps[0], dtype=np.float64)]
+    for g in comps[1:]:
+        u = np.asarray(g, dtype=np.float64).copy()
+        for v in vs:
+            coef = np.sum(u * v, axis=-1, keepdims=True) / (np.sum(v * v, axis=-1, keepdims=True) + eps)
+            u = u - coef * v
+        vs.append(u)
+    return vs
+
+
+def xhc_write_basis(out, conv_ws, use_mgs=True, eps=EPS_MGS):
+    """The K_r write components for every token: [B, S, K_r, C].
+
+    Attention-type sublayers (no kernels): the single component out.
+    MLP-type: out and one causal conv of out per kernel, Gram-Schmidt'ed
+    (or left as they are when use_mgs is False, the Muon variant of the
+    xHC paper's optimizer section).
+    """
+    out = np.asarray(out, dtype=np.float64)
+    comps = [out] + [causal_dwconv(out, w) for w in conv_ws]
+    if use_mgs and len(comps) > 1:
+        comps = gram_schmidt(comps, eps)
+    return np.stack(comps, axis=2)
+
+
+def xhc_post(X, out, I, p, h_res, h_post, conv_ws=(), use_mgs=True, eps=EPS_MGS):
+    """xHC sparse mix, gated write and scatter.
+
+    X: [B*S, N, C]; out: [B, S, C]; I, p: [T, k]; h_res [T, k, k];
+    h_post [T, k, K_r]; conv_ws: list of [kappa_j, C] (empty for attention).
+
+    New active rows: X_act' = H_res X_act + diag(p) H_post [v_1; ...; v_K_r];
+    they are scattered back to positions I and the other N-k streams are
+    returned unchanged (summary 3.4.3; explainer, "What xHC changes").
+    The router weight gates only the write, not the mix.
+
+    Returns the unrounded new state [T, N, C].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    T, N, C = X.shape
+    B, S, _ = np.shape(out)
+    assert B * S == T
+    V = xhc_write_basis(out, conv_ws, use_mgs, eps).reshape(T, -1, C)   # [T, K_r, C]
+    Xa = np.take_along_axis(X, I[:, :, None], axis=1)                   # [T, k, C]
+    new_a = np.einsum("tij,tjc->tic", h_res, Xa) + p[:, :, None] * np.einsum("tjr,trc->tjc", h_post, V)
+    Xn = X.copy()
+    np.put_along_axis(Xn, I[:, :, None], new_a, axis=1)
+    return Xn
+
+
+# --------------------------------------------------------------------------
+# whole sublayers (pre, then the given sublayer output, then post)
+# --------------------------------------------------------------------------
+
+def mhc_sublayer(X, out, W_full, alpha, b_pre, b_post, b_res, iters=20, dtype="f64"):
+    """One mHC sublayer; inp and the new state are rounded once to dtype."""
+    inp, h_pre, h_post, H_res = mhc_pre(X, W_full, alpha, b_pre, b_post, b_res, iters)
+    Xn = mhc_post(X, out.reshape(-1, np.shape(X)[2]), h_post, H_res)
+    return dict(inp=round_state(inp, dtype), X=round_state(Xn, dtype),
+                h_pre=h_pre, h_post=h_post, h_res=H_res)
+
+
+def xhc_sublayer(X, out, W_full, W_act, m, k, conv_ws, alpha, b_pre, b_res, b_post,
+                 iters=20, use_mgs=True, dtype="f64"):
+    """One xHC sublayer; K_r = 1 + len(conv_ws).  out: [B, S, C]."""
+    K_r = 1 + len(conv_ws)
+    pre = xhc_pre(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, iters)
+    Xn = xhc_post(X, out, pre["I"], pre["p"], pre["h_res"], pre["h_post"], conv_ws, use_mgs)
+    res = dict(pre)
+    res["inp"] = round_state(pre["inp"], dtype)
+    res["X"] = round_state(Xn, dtype)
+    return res
+
+
+def effective_mixing(I, h_res, N):
+    """The full N x N mixing map of one xHC sublayer for each token: the
+    k x k block on the active streams, identity elsewhere (explainer,
+    "Which constraint survives").  Returns [T, N, N]."""
+    T, k = I.shape
+    E = np.tile(np.eye(N), (T, 1, 1))
+    for t in range(T):
+        idx = I[t]
+        E[t][np.ix_(idx, idx)] = h_res[t]
+    return E
+
+
+def xhc_param_count(N, k, C, conv_kernels=(4, 8, 12)):
+    """Parameters of one Transformer layer (attention + MLP sublayer) with
+    the weight shapes used here: router N^2 C, pre-map N^2 C, residual map
+    k^3 C, post map k^2 C (attention) or k^2 K_r C (MLP), conv sum(kappa) C
+    (xHC paper, Appendix C).  Scales and biases are O(1) and not counted."""
+    K_r = 1 + len(conv_kernels)
+    attn = N * C * N + N * C * N + k * C * k * k + k * C * k
+    mlp = N * C * N + N * C * N + k * C * k * k + k * C * k * K_r + sum(conv_kernels) * C
+    return attn + mlp
+
+
+def mhc_param_count(N, C):
+    """Parameters of one Transformer layer of mHC: two sublayers, each
+    with an N C x (2N + N^2) projection (xHC paper, Appendix C)."""
+    return 2 * (N * C * (2 * N + N * N))

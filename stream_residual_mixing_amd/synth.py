@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for the residual-stream layer.
+
+Shared by the tests and the benchmark; holds none of the method's
+arithmetic.  Every tensor is drawn as float64 standard normals from
+``numpy.random.default_rng(key)`` scaled by its standard deviation, then
+rounded once to its storage dtype by PyTorch on the CPU.  Keys:
+
+* state X, token t, attempt a:       [seed, 0, 0, t, a]   (one row per token,
+  so any token can be regenerated alone; a > 0 only when a test redraws a
+  token whose routing margin is too small)
+* sublayer output, layer l, token t: [seed, 1, l, t]
+* full-state projection, layer l:     [seed, 2, l]
+* active-state projection, layer l:   [seed, 3, l]
+* conv kernel j, layer l:             [seed, 4 + j, l]
+
+Distributions (the workloads' own): X, out ~ N(0, 1); projection weights
+~ N(0, 0.02); conv kernel of size kappa ~ N(0, 1/kappa) (second argument
+read as the standard deviation).  Scales alpha = 0.01, biases 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+PROJ_STD = 0.02
+ALPHA = 0.01
+
+
+def _draw(key, shape, std=1.0):
+    return np.random.default_rng(list(key)).standard_normal(shape) * std
+
+
+def _round(a64: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a64)).to(DTYPES[dtype])
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a bf16 / f32 tensor's values."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def state_rows(seed, tokens, N, C, dtype, attempts=None) -> torch.Tensor:
+    """State rows [len(tokens), N, C] in the storage dtype (CPU)."""
+    tokens = list(tokens)
+    attempts = attempts or {}
+    a = np.empty((len(tokens), N * C))
+    for r, t in enumerate(tokens):
+        a[r] = _draw((seed, 0, 0, int(t), int(attempts.get(int(t), 0))), N * C)
+    return _round(a, dtype).reshape(len(tokens), N, C)
+
+
+def state(seed, T, N, C, dtype, attempts=None, chunk=256) -> torch.Tensor:
+    """Full state [T, N, C] in the storage dtype (CPU), built row by row."""
+    X = torch.empty((T, N, C), dtype=DTYPES[dtype])
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        X[t0:t1] = state_rows(seed, range(t0, t1), N, C, dtype, attempts)
+    return X
+
+
+def out_rows(seed, layer, tokens, C, dtype) -> torch.Tensor:
+    """Sublayer-output rows [len(tokens), C] for flat token ids t = b*S + s."""
+    tokens = list(tokens)
+    a = np.empty((len(tokens), C))
+    for r, t in enumerate(tokens):
+        a[r] = _draw((seed, 1, layer, int(t)), C)
+    return _round(a, dtype)
+
+
+def sublayer_out(seed, layer, B, S, C, dtype, chunk=1024) -> torch.Tensor:
+    """Sublayer output [B, S, C] in the storage dtype (CPU)."""
+    T = B * S
+    o = torch.empty((T, C), dtype=DTYPES[dtype])
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        o[t0:t1] = out_rows(seed, layer, range(t0, t1), C, dtype)
+    return o.reshape(B, S, C)
+
+
+def proj_weight(seed, tensor_id, layer, rows, cols, dtype, std=PROJ_STD) -> torch.Tensor:
+    return _round(_draw((seed, tensor_id, layer), (rows, cols), std), dtype)
+
+
+def conv_kernels(seed, layer, C, kernels=(4, 8, 12)):
+    """List of fp32 kernels [kappa_j, C], kernel j ~ N(0, 1/kappa_j)."""
+    return [_round(_draw((seed, 4 + j, layer), (kap, C), 1.0 / kap), "f32")
+            for j, kap in enumerate(kernels)]
+
+
+def xhc_layer_weights(seed, layer, N, k, C, K_r, dtype, kernels=(4, 8, 12)):
+    """Weights of one xHC sublayer: dict of CPU tensors plus scalars."""
+    n_res, n_post = k * k, k * K_r
+    return dict(
+        w_full=proj_weight(seed, 2, layer, N * C, 2 * N, dtype),
+        w_act=proj_weight(seed, 3, layer, k * C, n_res + n_post, dtype),
+        conv=conv_kernels(seed, layer, C, kernels) if K_r > 1 else [],
+        b_pre=torch.zeros(N), b_res=torch.zeros(n_res), b_post=torch.zeros(n_post),
+        alpha_pre=ALPHA, alpha_res=ALPHA, alpha_post=ALPHA,
+    )
+
+
+def mhc_layer_weights(seed, layer, N, C, dtype):
+    """Weights of one mHC sublayer (columns pre | post | res)."""
+    return dict(
+        w_full=proj_weight(seed, 2, layer, N * C, 2 * N + N * N, dtype),
+        b_pre=torch.zeros(N), b_post=torch.zeros(N), b_res=torch.zeros(N * N),
+        alpha_pre=ALPHA, alpha_res=ALPHA, alpha_post=ALPHA,
+    )
