@@ -1,0 +1,167 @@
+/*
+ * libxhc — hyper-connection residual-stream layer (mHC and xHC) for one
+ * AMD Instinct MI355X (gfx950) GPU.
+ *
+ * One sublayer of a multi-stream residual network keeps, per token, a state
+ * X in R^{N x C} (N streams of C channels).  Around the sublayer F (attention
+ * or MLP, not part of this library) two calls run:
+ *
+ *   *_pre  : mapping generation from the state and the dense read that forms
+ *            F's input  (xHC paper "xHC: Expanded Hyper-Connections",
+ *            paragraphs "Mapping generation" and "Mapping application");
+ *   *_post : after F, the write-back of F's output and the stream mix,
+ *            in place on X (same paragraphs; summary "小红书xHC：时序特征增强
+ *            + 稀疏写回", sections 3.1 and 3.4.3).
+ *
+ * mHC (dense): H_pre = sigmoid, H_post = 2 sigmoid and H_res = 20-step
+ * Sinkhorn-Knopp of one projection of RMSNorm(vec X) (xHC paper,
+ * "Manifold-Constrained HC"; explainer "xHC: sixteen residual streams, four
+ * written at a time", section "mHC: keep the mixing doubly stochastic").
+ *
+ * xHC (sparse): a sigmoid router over LayerNorm(vec X) picks m fixed and
+ * k-m routed active streams per token; the read stays dense over all N
+ * streams; only the k active streams are mixed (k x k Sinkhorn, then each
+ * row divided by max(row sum, 1)) and written; after MLP-type sublayers the
+ * write basis is F's output plus three causal depthwise convolutions of it
+ * (kernel sizes 4, 8, 12) orthogonalised by modified Gram-Schmidt along C
+ * (explainer, "What xHC changes" and "Which constraint survives"; summary
+ * 3.3-3.4).
+ *
+ * Conventions
+ *   - Tokens: T = batch * seq, flat index t = b * seq + s (batch-major).
+ *     The causal convolutions run along s inside one batch item.
+ *   - X: [T][N][C], out and inp: [T][C], all of the state dtype (cfg.dtype),
+ *     row-major, device memory, 16-byte aligned.
+ *   - vec X is stream-major: element (i, c) is row i*C + c of the
+ *     full-state projection weight.
+ *   - Every pointer in these calls is a device pointer unless it is the
+ *     config or weights struct itself (host memory, read during the call).
+ *   - The caller owns every buffer.  The library allocates nothing on the
+ *     GPU and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` and stream-ordered: *_pre, then F,
+ *     then *_post on the same workspace.  Calls that share a workspace must
+ *     not overlap.
+ *   - Arguments are checked before anything is launched; a check that fails
+ *     returns XHC_ERR_INVALID_ARG or XHC_ERR_UNSUPPORTED and launches
+ *     nothing.  A launch error returns XHC_ERR_HIP.  xhc_last_error() gives
+ *     the message (per host thread).  No C++ exception crosses this ABI.
+ *   - Results are deterministic: fixed reduction orders, no float atomics.
+ *   - T == 0 is valid and launches nothing.
+ */
+#ifndef XHC_H
+#define XHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same object as HIP's hipStream_t; NULL selects the default stream. */
+typedef struct ihipStream_t* xhc_stream_t;
+
+typedef enum {
+  XHC_OK = 0,
+  XHC_ERR_INVALID_ARG = 1,
+  XHC_ERR_UNSUPPORTED = 2,
+  XHC_ERR_HIP = 3
+} xhc_status;
+
+typedef enum { XHC_F32 = 0, XHC_BF16 = 1 } xhc_dtype;
+
+/* Layer shape and options (host struct, read during the call). */
+typedef struct {
+  int32_t n_streams;      /* N: 1..16 (mHC: 1, 2, 4, 8, 16; xHC: see below) */
+  int32_t k_active;       /* k: active streams (xHC only) */
+  int32_t m_fixed;        /* m: always-active streams 0..m-1, 0 <= m <= k (xHC only) */
+  int32_t channels;       /* C: multiple of 32 */
+  int32_t batch;          /* B >= 0 */
+  int32_t seq;            /* S >= 0 */
+  int32_t n_convs;        /* 0: attention-type, K_r = 1; 3: MLP-type, K_r = 4 (xHC only) */
+  int32_t conv_kernel[3]; /* kernel sizes when n_convs == 3: {4, 8, 12} */
+  int32_t use_mgs;        /* 1: Gram-Schmidt the write basis; 0: use it as is */
+  int32_t sinkhorn_iters; /* 0..1000, 20 in the pages */
+  int32_t dtype;          /* xhc_dtype of X, out, inp and projection weights */
+  float eps_norm;         /* RMSNorm / LayerNorm epsilon, 1e-6 in the pages */
+  float eps_mgs;          /* Gram-Schmidt epsilon on <v, v>, 1e-6 */
+} xhc_config;
+
+/* Weights of one sublayer (host struct holding device pointers). */
+typedef struct {
+  /* xHC: [N*C][2N], columns 0..N-1 router W_r, N..2N-1 pre-map W_pre.
+   * mHC: [N*C][2N + N*N], columns pre | post | res (res entry (i, j) at
+   *      column 2N + i*N + j).  State dtype, row-major. */
+  const void* w_full;
+  /* xHC: [k*C][k*k + k*K_r]; row j*C + c multiplies channel c of the j-th
+   * active stream (order of the active list); columns 0..k^2-1 W_res
+   * (entry (i, j) at i*k + j), then W_post (entry (j, r) at k^2 + j*K_r + r).
+   * State dtype.  mHC: unused (may be NULL). */
+  const void* w_act;
+  /* xHC MLP-type: [4 + 8 + 12][C] float; row off_j + i holds kernel j's
+   * weight for lag i (it multiplies out[t - i]).  NULL when n_convs == 0. */
+  const float* conv_w;
+  /* Biases, float.  xHC: b_pre [N], b_res [k*k], b_post [k*K_r].
+   *                 mHC: b_pre [N], b_res [N*N], b_post [N]. */
+  const float* b_pre;
+  const float* b_res;
+  const float* b_post;
+  float alpha_pre, alpha_res, alpha_post;  /* learnable scales */
+} xhc_weights;
+
+/* Byte offsets of the public arrays inside a workspace; fields that do not
+ * apply are SIZE_MAX.  All arrays are float except idx (int32). */
+typedef struct {
+  size_t idx;       /* xHC: [T][k] active streams: 0..m-1, then routed by descending score */
+  size_t p;         /* xHC: [T][k] router weights (1 for fixed streams) */
+  size_t h_pre;     /* [T][N] */
+  size_t h_res;     /* xHC: [T][k][k]; mHC: [T][N][N] */
+  size_t h_post;    /* xHC: [T][k][K_r]; mHC: [T][N] */
+  size_t z_router;  /* xHC: [T][N] router logits */
+  size_t total;     /* bytes the caller must allocate (0 when T == 0) */
+} xhc_ws_layout;
+
+/* Workspace needed by xhc_pre / xhc_post (resp. mhc_pre / mhc_post) for
+ * this config; 0 for an invalid config or T == 0. */
+size_t xhc_workspace_bytes(const xhc_config* cfg);
+size_t mhc_workspace_bytes(const xhc_config* cfg);
+xhc_status xhc_workspace_layout(const xhc_config* cfg, xhc_ws_layout* out);
+xhc_status mhc_workspace_layout(const xhc_config* cfg, xhc_ws_layout* out);
+
+/* xHC before the sublayer: router logits, active set I and weights p, H_pre,
+ * dense read inp = sum_i H_pre[i] X_i (all N streams), and the active maps
+ * H_res, H_post from RMSNorm(vec X[I]).  X: [T][N][C] (read only);
+ * inp: [T][C] (written); ws: xhc_workspace_bytes(cfg) bytes (written).
+ * (xHC paper, "Mapping generation"; summary 3.4.1-3.4.3.)
+ * Supported (N, k): (16, 4), (16, 2), (8, 4), (4, 4), (1, 1). */
+xhc_status xhc_pre(const xhc_config* cfg, const xhc_weights* w,
+                   const void* X, void* inp, void* ws, xhc_stream_t stream);
+
+/* xHC after the sublayer: for MLP-type configs the causal convolutions of
+ * out and Gram-Schmidt; then for each token the k active rows become
+ * H_res X_act + diag(p) H_post [v_1..v_K_r], written in place; the other
+ * N - k rows are not touched.  X: [T][N][C] (in place); out: [T][C];
+ * ws: the workspace filled by xhc_pre (also used as scratch).
+ * (xHC paper, "Mapping application" and "Temporal feature augmentation";
+ * summary 3.3, 3.4.3.) */
+xhc_status xhc_post(const xhc_config* cfg, const xhc_weights* w,
+                    void* X, const void* out, void* ws, xhc_stream_t stream);
+
+/* mHC before the sublayer: H_pre, H_post, H_res (Sinkhorn, no clamp) from
+ * RMSNorm(vec X), and inp = sum_i H_pre[i] X_i.
+ * (xHC paper, "Manifold-Constrained HC"; summary 3.1.) */
+xhc_status mhc_pre(const xhc_config* cfg, const xhc_weights* w,
+                   const void* X, void* inp, void* ws, xhc_stream_t stream);
+
+/* mHC after the sublayer: X <- H_res X + H_post out^T for all N rows, in
+ * place.  (xHC paper, "Hyper-Connections"; summary 3.1-3.2.) */
+xhc_status mhc_post(const xhc_config* cfg, const xhc_weights* w,
+                    void* X, const void* out, void* ws, xhc_stream_t stream);
+
+/* Message for the last non-OK status returned on this host thread. */
+const char* xhc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* XHC_H */

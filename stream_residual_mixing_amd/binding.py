@@ -1,0 +1,279 @@
+"""ctypes binding of libxhc: the same calls as include/xhc.h.
+
+Argument marshalling only: PyTorch tensors are checked (device, dtype,
+shape, contiguity) so that no host pointer or undersized buffer reaches a
+kernel, then their device pointers and the current HIP stream are passed to
+the C ABI.  Every step of the layer runs in the HIP library; there is no
+other code path.  ``load()`` raises when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libxhc.so")
+
+XHC_OK, XHC_ERR_INVALID_ARG, XHC_ERR_UNSUPPORTED, XHC_ERR_HIP = 0, 1, 2, 3
+XHC_F32, XHC_BF16 = 0, 1
+_DT = {"f32": (XHC_F32, torch.float32), "bf16": (XHC_BF16, torch.bfloat16)}
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+# Exported symbols, in the order include/xhc.h declares them.
+EXPORTS = (
+    "xhc_workspace_bytes", "mhc_workspace_bytes", "xhc_workspace_layout", "mhc_workspace_layout",
+    "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_last_error",
+)
+
+
+class XhcConfig(ctypes.Structure):
+    _fields_ = [
+        ("n_streams", ctypes.c_int32), ("k_active", ctypes.c_int32), ("m_fixed", ctypes.c_int32),
+        ("channels", ctypes.c_int32), ("batch", ctypes.c_int32), ("seq", ctypes.c_int32),
+        ("n_convs", ctypes.c_int32), ("conv_kernel", ctypes.c_int32 * 3), ("use_mgs", ctypes.c_int32),
+        ("sinkhorn_iters", ctypes.c_int32), ("dtype", ctypes.c_int32), ("eps_norm", ctypes.c_float),
+        ("eps_mgs", ctypes.c_float),
+    ]
+
+
+class XhcWeights(ctypes.Structure):
+    _fields_ = [
+        ("w_full", ctypes.c_void_p), ("w_act", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
+        ("b_pre", ctypes.c_void_p), ("b_res", ctypes.c_void_p), ("b_post", ctypes.c_void_p),
+        ("alpha_pre", ctypes.c_float), ("alpha_res", ctypes.c_float), ("alpha_post", ctypes.c_float),
+    ]
+
+
+class XhcWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre", "h_res", "h_post", "z_router", "total")]
+
+
+class XhcError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"libxhc status {status}: {msg}")
+        self.status = status
+
+
+@dataclass
+class Config:
+    """Python view of xhc_config.  K_r = 4 when n_convs == 3, else 1."""
+    N: int
+    C: int
+    B: int
+    S: int
+    k: int = 0
+    m: int = 0
+    n_convs: int = 0
+    kernels: tuple = (4, 8, 12)
+    use_mgs: int = 1
+    iters: int = 20
+    dtype: str = "bf16"
+    eps_norm: float = 1e-6
+    eps_mgs: float = 1e-6
+
+    @property
+    def T(self):
+        return self.B * self.S
+
+    @property
+    def K_r(self):
+        return 4 if self.n_convs == 3 else 1
+
+    @property
+    def torch_dtype(self):
+        return _DT[self.dtype][1]
+
+    def c(self) -> XhcConfig:
+        c = XhcConfig()
+        c.n_streams, c.k_active, c.m_fixed, c.channels = self.N, self.k, self.m, self.C
+        c.batch, c.seq, c.n_convs = self.B, self.S, self.n_convs
+        for i in range(3):
+            c.conv_kernel[i] = int(self.kernels[i]) if i < len(self.kernels) else 0
+        c.use_mgs, c.sinkhorn_iters = int(self.use_mgs), self.iters
+        c.dtype = _DT[self.dtype][0] if self.dtype in _DT else int(self.dtype)
+        c.eps_norm, c.eps_mgs = self.eps_norm, self.eps_mgs
+        return c
+
+
+@dataclass
+class Weights:
+    """Device tensors of one sublayer (kept alive by this object)."""
+    w_full: torch.Tensor
+    b_pre: torch.Tensor
+    b_res: torch.Tensor
+    b_post: torch.Tensor
+    alpha_pre: float
+    alpha_res: float
+    alpha_post: float
+    w_act: torch.Tensor | None = None
+    conv_w: torch.Tensor | None = None   # [sum kappa, C] float32, lag-major
+    _keep: list = field(default_factory=list, repr=False)
+
+    def c(self) -> XhcWeights:
+        w = XhcWeights()
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+        w.w_full, w.w_act, w.conv_w = ptr(self.w_full), ptr(self.w_act), ptr(self.conv_w)
+        w.b_pre, w.b_res, w.b_post = ptr(self.b_pre), ptr(self.b_res), ptr(self.b_post)
+        w.alpha_pre, w.alpha_res, w.alpha_post = self.alpha_pre, self.alpha_res, self.alpha_post
+        return w
+
+
+def _check(t, name, shape, dtype):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_out(t, cfg):
+    shape = (cfg.T, cfg.C) if (t is not None and t.dim() == 2) else (cfg.B, cfg.S, cfg.C)
+    _check(t, "out", shape, cfg.torch_dtype)
+
+
+def _stream_ptr(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Lib:
+    def __init__(self, path=LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(f"libxhc is not built ({path} missing): run __graft_entry__.build()")
+        self.path = path
+        self.dll = ctypes.CDLL(path)
+        d = self.dll
+        d.xhc_workspace_bytes.restype = ctypes.c_size_t
+        d.xhc_workspace_bytes.argtypes = [ctypes.POINTER(XhcConfig)]
+        d.mhc_workspace_bytes.restype = ctypes.c_size_t
+        d.mhc_workspace_bytes.argtypes = [ctypes.POINTER(XhcConfig)]
+        for fn in (d.xhc_workspace_layout, d.mhc_workspace_layout):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWsLayout)]
+        for fn in (d.xhc_pre, d.xhc_post, d.mhc_pre, d.mhc_post):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.c_void_p,
+                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        d.xhc_last_error.restype = ctypes.c_char_p
+        d.xhc_last_error.argtypes = []
+
+    # -------------------------------------------------------------- helpers
+    def last_error(self) -> str:
+        return self.dll.xhc_last_error().decode()
+
+    def _ok(self, status):
+        if status != XHC_OK:
+            raise XhcError(status, self.last_error())
+
+    def workspace_bytes(self, cfg: Config, mhc=False) -> int:
+        c = cfg.c()
+        fn = self.dll.mhc_workspace_bytes if mhc else self.dll.xhc_workspace_bytes
+        return int(fn(ctypes.byref(c)))
+
+    def layout(self, cfg: Config, mhc=False) -> XhcWsLayout:
+        c, L = cfg.c(), XhcWsLayout()
+        fn = self.dll.mhc_workspace_layout if mhc else self.dll.xhc_workspace_layout
+        self._ok(fn(ctypes.byref(c), ctypes.byref(L)))
+        return L
+
+    def workspace(self, cfg: Config, mhc=False, device="cuda") -> torch.Tensor:
+        n = self.workspace_bytes(cfg, mhc)
+        if n == 0 and cfg.T > 0:
+            self.layout(cfg, mhc)   # raises with the library's message
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def ws_arrays(self, cfg: Config, ws: torch.Tensor, mhc=False) -> dict:
+        """Views of the public workspace arrays (see xhc_ws_layout)."""
+        L = self.layout(cfg, mhc)
+        T, N, k, Kr = cfg.T, cfg.N, (cfg.N if mhc else cfg.k), cfg.K_r
+
+        def view(off, shape, dt=torch.float32):
+            n = 1
+            for s in shape:
+                n *= s
+            return ws[off: off + 4 * n].view(dt).reshape(shape)
+
+        if mhc:
+            return dict(h_pre=view(L.h_pre, (T, N)), h_res=view(L.h_res, (T, N, N)),
+                        h_post=view(L.h_post, (T, N)))
+        return dict(idx=view(L.idx, (T, k), torch.int32), p=view(L.p, (T, k)), h_pre=view(L.h_pre, (T, N)),
+                    h_res=view(L.h_res, (T, k, k)), h_post=view(L.h_post, (T, k, Kr)),
+                    z=view(L.z_router, (T, N)))
+
+    def _check_common(self, cfg, w, X, ws, mhc, pre):
+        dt = cfg.torch_dtype
+        _check(X, "X", (cfg.T, cfg.N, cfg.C), dt)
+        need = self.workspace_bytes(cfg, mhc)
+        if ws is None or not ws.is_cuda or ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace must be a GPU tensor of at least {need} bytes")
+        if pre:
+            ncol = 2 * cfg.N + (cfg.N * cfg.N if mhc else 0)
+            _check(w.w_full, "w_full", (cfg.N * cfg.C, ncol), dt)
+            k = cfg.N if mhc else cfg.k
+            _check(w.b_pre, "b_pre", (cfg.N,), torch.float32)
+            _check(w.b_res, "b_res", (k * k,), torch.float32)
+            _check(w.b_post, "b_post", ((cfg.N,) if mhc else (k * cfg.K_r,)), torch.float32)
+            if not mhc:
+                _check(w.w_act, "w_act", (k * cfg.C, k * k + k * cfg.K_r), dt)
+        elif not mhc and cfg.K_r == 4:
+            _check(w.conv_w, "conv_w", (sum(cfg.kernels), cfg.C), torch.float32)
+
+    # -------------------------------------------------------------- the ABI
+    def xhc_pre(self, cfg: Config, w: Weights, X, inp, ws, stream=None):
+        self._check_common(cfg, w, X, ws, False, True)
+        _check(inp, "inp", (cfg.T, cfg.C), cfg.torch_dtype)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_pre(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), inp.data_ptr(),
+                                  ws.data_ptr(), _stream_ptr(stream)))
+
+    def xhc_post(self, cfg: Config, w: Weights, X, out, ws, stream=None):
+        self._check_common(cfg, w, X, ws, False, False)
+        _check_out(out, cfg)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_post(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
+                                   ws.data_ptr(), _stream_ptr(stream)))
+
+    def mhc_pre(self, cfg: Config, w: Weights, X, inp, ws, stream=None):
+        self._check_common(cfg, w, X, ws, True, True)
+        _check(inp, "inp", (cfg.T, cfg.C), cfg.torch_dtype)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.mhc_pre(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), inp.data_ptr(),
+                                  ws.data_ptr(), _stream_ptr(stream)))
+
+    def mhc_post(self, cfg: Config, w: Weights | None, X, out, ws, stream=None):
+        self._check_common(cfg, w, X, ws, True, False)
+        _check_out(out, cfg)
+        c = cfg.c()
+        cw = w.c() if w is not None else XhcWeights()
+        self._ok(self.dll.mhc_post(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
+                                   ws.data_ptr(), _stream_ptr(stream)))
+
+
+_INSTANCE = None
+
+
+def load(path=LIB_PATH) -> Lib:
+    """The loaded library (cached).  Raises RuntimeError if it is not built."""
+    global _INSTANCE
+    if _INSTANCE is None or _INSTANCE.path != path:
+        _INSTANCE = Lib(path)
+    return _INSTANCE
+
+
+def weights_to_device(wd: dict, device="cuda") -> Weights:
+    """Move a dict from ``synth.xhc_layer_weights`` / ``mhc_layer_weights``
+    (CPU tensors) to the GPU as a Weights object."""
+    conv = wd.get("conv") or []
+    conv_w = torch.cat(conv, 0).contiguous().to(device) if conv else None
+    return Weights(
+        w_full=wd["w_full"].contiguous().to(device), w_act=(wd["w_act"].contiguous().to(device)
+                                                            if wd.get("w_act") is not None else None),
+        conv_w=conv_w, b_pre=wd["b_pre"].float().contiguous().to(device),
+        b_res=wd["b_res"].float().contiguous().to(device), b_post=wd["b_post"].float().contiguous().to(device),
+        alpha_pre=float(wd["alpha_pre"]), alpha_res=float(wd["alpha_res"]), alpha_post=float(wd["alpha_post"]))

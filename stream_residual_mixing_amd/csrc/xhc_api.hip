@@ -1,0 +1,266 @@
+// libxhc host side: argument checks, workspace layout, launches, errors.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "xhc.h"
+#include "xhc_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+xhc_status fail(xhc_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool sync_mode() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("XHC_SYNC");
+    v = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+bool xhc_shape_supported(int N, int K) {
+  return (N == 16 && K == 4) || (N == 16 && K == 2) || (N == 8 && K == 4) || (N == 4 && K == 4) ||
+         (N == 1 && K == 1);
+}
+
+// Validate the config and derive the plan (no device calls).
+xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
+  using xhc::Plan;
+  if (!cfg) return fail(XHC_ERR_INVALID_ARG, "config is NULL");
+  Plan q;
+  q.mhc = mhc;
+  q.N = cfg->n_streams;
+  q.C = cfg->channels;
+  q.B = cfg->batch;
+  q.S = cfg->seq;
+  q.dtype = cfg->dtype;
+  q.iters = cfg->sinkhorn_iters;
+  q.use_mgs = cfg->use_mgs ? 1 : 0;
+  q.eps_norm = cfg->eps_norm;
+  q.eps_mgs = cfg->eps_mgs;
+  if (q.dtype != XHC_F32 && q.dtype != XHC_BF16) return fail(XHC_ERR_UNSUPPORTED, "dtype %d not supported", q.dtype);
+  if (q.N < 1 || q.N > 16) return fail(XHC_ERR_INVALID_ARG, "n_streams=%d outside 1..16", q.N);
+  if (q.C <= 0 || q.C % 32 != 0) return fail(XHC_ERR_INVALID_ARG, "channels=%d must be a positive multiple of 32", q.C);
+  if (q.C > 65536) return fail(XHC_ERR_UNSUPPORTED, "channels=%d above 65536", q.C);
+  if (q.B < 0 || q.S < 0) return fail(XHC_ERR_INVALID_ARG, "batch=%d, seq=%d must be >= 0", q.B, q.S);
+  q.T = (long)q.B * (long)q.S;
+  if (q.T > (1L << 30)) return fail(XHC_ERR_UNSUPPORTED, "batch*seq=%ld too large", q.T);
+  if ((double)q.T * q.N * q.C > 9.0e15) return fail(XHC_ERR_UNSUPPORTED, "state too large");
+  if (q.iters < 0 || q.iters > 1000) return fail(XHC_ERR_INVALID_ARG, "sinkhorn_iters=%d outside 0..1000", q.iters);
+  if (!(std::isfinite(q.eps_norm) && q.eps_norm >= 0.f))
+    return fail(XHC_ERR_INVALID_ARG, "eps_norm must be finite and >= 0");
+  if (!(std::isfinite(q.eps_mgs) && q.eps_mgs >= 0.f))
+    return fail(XHC_ERR_INVALID_ARG, "eps_mgs must be finite and >= 0");
+  const int KB = q.dtype == XHC_BF16 ? 32 : 16;
+  q.nslices = (q.C + xhc::PSLICE - 1) / xhc::PSLICE;
+  if (mhc) {
+    if (q.N != 1 && q.N != 2 && q.N != 4 && q.N != 8 && q.N != 16)
+      return fail(XHC_ERR_UNSUPPORTED, "mHC supports N in {1,2,4,8,16}, got %d", q.N);
+    q.K = q.N;
+    q.ncol_full = 2 * q.N + q.N * q.N;
+  } else {
+    q.K = cfg->k_active;
+    q.m = cfg->m_fixed;
+    if (q.K < 1 || q.K > q.N) return fail(XHC_ERR_INVALID_ARG, "k_active=%d outside 1..N=%d", q.K, q.N);
+    if (q.m < 0 || q.m > q.K) return fail(XHC_ERR_INVALID_ARG, "m_fixed=%d outside 0..k=%d", q.m, q.K);
+    if (!xhc_shape_supported(q.N, q.K))
+      return fail(XHC_ERR_UNSUPPORTED, "xHC (N=%d, k=%d) not built; supported: (16,4) (16,2) (8,4) (4,4) (1,1)",
+                  q.N, q.K);
+    if (cfg->n_convs == 0) {
+      q.KR = 1;
+    } else if (cfg->n_convs == 3) {
+      if (cfg->conv_kernel[0] != 4 || cfg->conv_kernel[1] != 8 || cfg->conv_kernel[2] != 12)
+        return fail(XHC_ERR_UNSUPPORTED, "conv kernel sizes {%d,%d,%d} not built; supported: {4,8,12}",
+                    cfg->conv_kernel[0], cfg->conv_kernel[1], cfg->conv_kernel[2]);
+      q.KR = 4;
+    } else {
+      return fail(XHC_ERR_INVALID_ARG, "n_convs=%d must be 0 or 3", cfg->n_convs);
+    }
+    q.ncol_full = 2 * q.N;
+    q.ncol_act = q.K * q.K + q.K * q.KR;
+    q.NTA = (q.ncol_act + 15) / 16;
+    q.nkb_act = (long)q.K * q.C / KB;
+  }
+  q.NTF = (q.ncol_full + 15) / 16;
+  q.nkb_full = (long)q.N * q.C / KB;
+  const long nblk_t = (q.T + 63) / 64;
+  long ks = nblk_t > 0 ? (1024 + nblk_t - 1) / nblk_t : 1;
+  if (ks > 8) ks = 8;
+  if (ks > q.nkb_full) ks = q.nkb_full;
+  if (ks < 1) ks = 1;
+  q.KS = (int)ks;
+
+  // workspace layout: public arrays first, then internal scratch
+  const size_t T = (size_t)q.T, N = q.N, K = q.K;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  if (mhc) {
+    q.o_hpre = take(T * N * 4);
+    q.o_hres = take(T * N * N * 4);
+    q.o_hpost = take(T * N * 4);
+  } else {
+    q.o_idx = take(T * K * 4);
+    q.o_p = take(T * K * 4);
+    q.o_hpre = take(T * N * 4);
+    q.o_hres = take(T * K * K * 4);
+    q.o_hpost = take(T * K * q.KR * 4);
+    q.o_z = take(T * N * 4);
+    q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
+    q.o_colsum = take(N * 4);
+    q.o_gram = take((size_t)q.nslices * T * 10 * 4);
+  }
+  q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
+  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
+  q.o_stats = take((size_t)q.KS * T * 2 * 4);
+  q.total = q.T == 0 ? 0 : off;
+  *P = q;
+  return XHC_OK;
+}
+
+xhc_status check_weights(const xhc::Plan& P, const xhc_weights* w, bool need_pre) {
+  if (!w) return fail(XHC_ERR_INVALID_ARG, "weights is NULL");
+  if (!std::isfinite(w->alpha_pre) || !std::isfinite(w->alpha_res) || !std::isfinite(w->alpha_post))
+    return fail(XHC_ERR_INVALID_ARG, "alpha scales must be finite");
+  if (need_pre) {
+    if (!w->w_full || !aligned16(w->w_full)) return fail(XHC_ERR_INVALID_ARG, "w_full must be a 16-byte aligned pointer");
+    if (!P.mhc && (!w->w_act || !aligned16(w->w_act)))
+      return fail(XHC_ERR_INVALID_ARG, "w_act must be a 16-byte aligned pointer");
+    if (!w->b_pre || !w->b_res || !w->b_post) return fail(XHC_ERR_INVALID_ARG, "bias pointers must not be NULL");
+  }
+  if (!need_pre && !P.mhc && P.KR == 4 && (!w->conv_w || !aligned16(w->conv_w)))
+    return fail(XHC_ERR_INVALID_ARG, "conv_w must be a 16-byte aligned pointer for MLP-type configs");
+  return XHC_OK;
+}
+
+xhc_status finish(hipStream_t st) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(XHC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (sync_mode()) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(XHC_ERR_HIP, "stream synchronize failed: %s", hipGetErrorString(e));
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(XHC_ERR_HIP, "kernel failed: %s", hipGetErrorString(e));
+  }
+  return XHC_OK;
+}
+
+xhc_status fill_layout(const xhc::Plan& P, xhc_ws_layout* out) {
+  if (!out) return fail(XHC_ERR_INVALID_ARG, "layout output is NULL");
+  out->idx = P.o_idx;
+  out->p = P.o_p;
+  out->h_pre = P.o_hpre;
+  out->h_res = P.o_hres;
+  out->h_post = P.o_hpost;
+  out->z_router = P.o_z;
+  out->total = P.total;
+  return XHC_OK;
+}
+
+xhc_status pre_common(const xhc_config* cfg, const xhc_weights* w, const void* X, void* inp, void* ws,
+                      xhc_stream_t stream, bool mhc) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, mhc, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_weights(P, w, true)) != XHC_OK) return s;
+  if (P.T == 0) return XHC_OK;
+  if (!X || !inp || !ws) return fail(XHC_ERR_INVALID_ARG, "X, inp and ws must not be NULL");
+  if (!aligned16(X) || !aligned16(inp) || !aligned16(ws))
+    return fail(XHC_ERR_INVALID_ARG, "X, inp and ws must be 16-byte aligned");
+  if (X == inp || X == ws || inp == ws) return fail(XHC_ERR_INVALID_ARG, "X, inp and ws must not alias");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool ok = mhc ? xhc::launch_mhc_pre(P, X, inp, w, static_cast<char*>(ws), st)
+                      : xhc::launch_xhc_pre(P, X, inp, w, static_cast<char*>(ws), st);
+  if (!ok) return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status post_common(const xhc_config* cfg, const xhc_weights* w, void* X, const void* out, void* ws,
+                       xhc_stream_t stream, bool mhc) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, mhc, &P);
+  if (s != XHC_OK) return s;
+  if (!mhc && (s = check_weights(P, w, false)) != XHC_OK) return s;
+  if (P.T == 0) return XHC_OK;
+  if (!X || !out || !ws) return fail(XHC_ERR_INVALID_ARG, "X, out and ws must not be NULL");
+  if (!aligned16(X) || !aligned16(out) || !aligned16(ws))
+    return fail(XHC_ERR_INVALID_ARG, "X, out and ws must be 16-byte aligned");
+  if (X == out || X == ws || out == ws) return fail(XHC_ERR_INVALID_ARG, "X, out and ws must not alias");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool ok = mhc ? xhc::launch_mhc_post(P, X, out, static_cast<char*>(ws), st)
+                      : xhc::launch_xhc_post(P, X, out, w, static_cast<char*>(ws), st);
+  if (!ok) return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t xhc_workspace_bytes(const xhc_config* cfg) {
+  xhc::Plan P;
+  return make_plan(cfg, false, &P) == XHC_OK ? P.total : 0;
+}
+
+size_t mhc_workspace_bytes(const xhc_config* cfg) {
+  xhc::Plan P;
+  return make_plan(cfg, true, &P) == XHC_OK ? P.total : 0;
+}
+
+xhc_status xhc_workspace_layout(const xhc_config* cfg, xhc_ws_layout* out) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, false, &P);
+  return s != XHC_OK ? s : fill_layout(P, out);
+}
+
+xhc_status mhc_workspace_layout(const xhc_config* cfg, xhc_ws_layout* out) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, true, &P);
+  return s != XHC_OK ? s : fill_layout(P, out);
+}
+
+xhc_status xhc_pre(const xhc_config* cfg, const xhc_weights* w, const void* X, void* inp, void* ws,
+                   xhc_stream_t stream) {
+  return pre_common(cfg, w, X, inp, ws, stream, false);
+}
+
+xhc_status xhc_post(const xhc_config* cfg, const xhc_weights* w, void* X, const void* out, void* ws,
+                    xhc_stream_t stream) {
+  return post_common(cfg, w, X, out, ws, stream, false);
+}
+
+xhc_status mhc_pre(const xhc_config* cfg, const xhc_weights* w, const void* X, void* inp, void* ws,
+                   xhc_stream_t stream) {
+  return pre_common(cfg, w, X, inp, ws, stream, true);
+}
+
+xhc_status mhc_post(const xhc_config* cfg, const xhc_weights* w, void* X, const void* out, void* ws,
+                    xhc_stream_t stream) {
+  return post_common(cfg, w, X, out, ws, stream, true);
+}
+
+const char* xhc_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Host/device shared definitions internal to libxhc (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "xhc.h"
+
+namespace xhc {
+
+constexpr int PT = 64;             // tokens per post block
+constexpr int PCH = 4;             // channels per post thread
+constexpr int PSLICE = 256 * PCH;  // channels per post block
+
+// Everything a call needs, derived once from the config.
+struct Plan {
+  bool mhc = false;
+  int N = 0, K = 0, m = 0, C = 0, B = 0, S = 0, KR = 1;
+  long T = 0;
+  int dtype = XHC_BF16;
+  int iters = 20, use_mgs = 1;
+  float eps_norm = 1e-6f, eps_mgs = 1e-6f;
+  int ncol_full = 0, ncol_act = 0;  // logical projection widths
+  int NTF = 0, NTA = 0;             // 16-column MFMA tiles
+  long nkb_full = 0, nkb_act = 0;   // contraction blocks
+  int KS = 1;                       // split of the full-state contraction
+  int nslices = 1;                  // channel slices of the post kernels
+  // workspace byte offsets
+  size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,
+         o_z = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
+         o_gram = SIZE_MAX, total = 0;
+};
+
+struct XhcReadArgs {
+  const void* X;
+  void* inp;
+  int T, C, m, KS;
+  const float* part;
+  const float* stats;
+  const float* colsum;
+  const uint4* wact;
+  const float *b_pre, *b_res, *b_post;
+  float a_pre, a_res, a_post;
+  int iters;
+  float eps;
+  int* idx;
+  float *p, *h_pre, *h_res, *h_post, *z;
+};
+
+struct MhcReadArgs {
+  const void* X;
+  void* inp;
+  int T, C, KS;
+  const float* part;
+  const float* stats;
+  const float *b_pre, *b_res, *b_post;
+  float a_pre, a_res, a_post;
+  int iters;
+  float eps;
+  float *h_pre, *h_res, *h_post;
+};
+
+struct XhcPostArgs {
+  void* X;
+  const void* out;
+  int T, S, C, N, nslices;
+  const int* idx;
+  const float *p, *h_res, *h_post;
+  const float* conv_w;
+  int use_mgs;
+  float eps_mgs;
+  float* gram;
+};
+
+struct MhcPostArgs {
+  void* X;
+  const void* out;
+  int T, C, nslices;
+  const float *h_res, *h_post;
+};
+
+bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
+bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st);
+bool launch_mhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
+bool launch_mhc_post(const Plan& P, void* X, const void* out, char* ws, hipStream_t st);
+
+}  // namespace xhc

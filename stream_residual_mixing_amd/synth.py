@@ -19,6 +19,9 @@ read as the standard deviation).  Scales alpha = 0.01, biases 0.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -50,13 +53,25 @@ def state_rows(seed, tokens, N, C, dtype, attempts=None) -> torch.Tensor:
     return _round(a, dtype).reshape(len(tokens), N, C)
 
 
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _fill_rows(dst, T, chunk, make):
+    """dst[t0:t1] = make(t0, t1) over row chunks, in a thread pool (each row
+    has its own generator, so the values do not depend on the schedule)."""
+    def job(t0):
+        t1 = min(T, t0 + chunk)
+        dst[t0:t1] = make(t0, t1)
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(0, T, chunk)))
+    return dst
+
+
 def state(seed, T, N, C, dtype, attempts=None, chunk=256) -> torch.Tensor:
     """Full state [T, N, C] in the storage dtype (CPU), built row by row."""
     X = torch.empty((T, N, C), dtype=DTYPES[dtype])
-    for t0 in range(0, T, chunk):
-        t1 = min(T, t0 + chunk)
-        X[t0:t1] = state_rows(seed, range(t0, t1), N, C, dtype, attempts)
-    return X
+    return _fill_rows(X, T, chunk, lambda t0, t1: state_rows(seed, range(t0, t1), N, C, dtype, attempts))
 
 
 def out_rows(seed, layer, tokens, C, dtype) -> torch.Tensor:
@@ -72,9 +87,7 @@ def sublayer_out(seed, layer, B, S, C, dtype, chunk=1024) -> torch.Tensor:
     """Sublayer output [B, S, C] in the storage dtype (CPU)."""
     T = B * S
     o = torch.empty((T, C), dtype=DTYPES[dtype])
-    for t0 in range(0, T, chunk):
-        t1 = min(T, t0 + chunk)
-        o[t0:t1] = out_rows(seed, layer, range(t0, t1), C, dtype)
+    _fill_rows(o, T, chunk, lambda t0, t1: out_rows(seed, layer, range(t0, t1), C, dtype))
     return o.reshape(B, S, C)
 
 

@@ -1,0 +1,152 @@
+"""CPU checks of the C ABI: the library loads and exports every function
+include/xhc.h declares; workspace sizing and layout; argument checks that
+reject bad calls before anything is launched.  No compute call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from stream_residual_mixing_amd import binding
+from stream_residual_mixing_amd.binding import Config, XhcConfig, XhcWeights
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xhc.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from stream_residual_mixing_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return [n for n in names if n not in ("defined",)]
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS), names
+    for n in names:
+        assert hasattr(lib.dll, n), n
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors have the sizes and field offsets a C compiler
+    gives the header's structs."""
+    import subprocess
+    structs = {"xhc_config": XhcConfig, "xhc_weights": XhcWeights, "xhc_ws_layout": binding.XhcWsLayout}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "xhc.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines())
+    for cname, cls in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
+
+
+def _cfg(**kw):
+    base = dict(N=16, k=4, m=2, C=4096, B=2, S=8192, n_convs=3, dtype="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
+def test_workspace_layout_is_aligned_and_sized(lib):
+    for mhc, cfg in ((False, _cfg()), (False, _cfg(n_convs=0)), (True, _cfg(k=0, m=0, n_convs=0)),
+                     (True, _cfg(N=4, C=256, B=1, S=64, dtype="f32"))):
+        L = lib.layout(cfg, mhc)
+        T, N = cfg.T, cfg.N
+        offs = [getattr(L, f) for f in ("idx", "p", "h_pre", "h_res", "h_post", "z_router")]
+        used = [o for o in offs if o != binding.SIZE_MAX]
+        assert all(o % 256 == 0 for o in used)
+        assert L.total == lib.workspace_bytes(cfg, mhc) > 0
+        if mhc:
+            assert L.h_res + T * N * N * 4 <= L.total
+        else:
+            assert L.z_router + T * N * 4 <= L.total
+            assert L.h_post - L.h_res >= T * cfg.k * cfg.k * 4
+
+
+def test_empty_batch_needs_no_workspace_and_launches_nothing(lib):
+    cfg = _cfg(B=0)
+    assert lib.workspace_bytes(cfg) == 0
+    c, w = cfg.c(), XhcWeights()
+    w.w_full = w.w_act = w.b_pre = w.b_res = w.b_post = w.conv_w = 0x10000
+    for fn in (lib.dll.xhc_pre, lib.dll.xhc_post):
+        assert fn(ctypes.byref(c), ctypes.byref(w), None, None, None, None) == binding.XHC_OK
+
+
+BAD = [
+    (dict(k=17), binding.XHC_ERR_INVALID_ARG, "k_active"),
+    (dict(k=5), binding.XHC_ERR_UNSUPPORTED, "not built"),
+    (dict(m=5), binding.XHC_ERR_INVALID_ARG, "m_fixed"),
+    (dict(C=4100), binding.XHC_ERR_INVALID_ARG, "multiple of 32"),
+    (dict(n_convs=2), binding.XHC_ERR_INVALID_ARG, "n_convs"),
+    (dict(kernels=(3, 8, 12)), binding.XHC_ERR_UNSUPPORTED, "kernel sizes"),
+    (dict(N=17), binding.XHC_ERR_INVALID_ARG, "n_streams"),
+    (dict(iters=-1), binding.XHC_ERR_INVALID_ARG, "sinkhorn_iters"),
+    (dict(eps_norm=float("nan")), binding.XHC_ERR_INVALID_ARG, "eps_norm"),
+    (dict(B=-1), binding.XHC_ERR_INVALID_ARG, "batch"),
+]
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers: run on a host without a GPU only")
+@pytest.mark.parametrize("kw,status,msg", BAD)
+def test_bad_configs_are_rejected_before_launch(lib, kw, status, msg):
+    cfg = _cfg(**kw)
+    c, w = cfg.c(), XhcWeights()
+    w.w_full = w.w_act = w.b_pre = w.b_res = w.b_post = w.conv_w = 0x10000
+    rc = lib.dll.xhc_pre(ctypes.byref(c), ctypes.byref(w), 0x20000, 0x30000, 0x40000, None)
+    assert rc == status
+    assert msg in lib.last_error()
+    assert lib.workspace_bytes(cfg) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers: run on a host without a GPU only")
+def test_bad_pointers_are_rejected_before_launch(lib):
+    cfg = _cfg(B=1, S=16)
+    c, w = cfg.c(), XhcWeights()
+    w.w_full = w.w_act = w.b_pre = w.b_res = w.b_post = w.conv_w = 0x10000
+    pre = lib.dll.xhc_pre
+    assert pre(ctypes.byref(c), ctypes.byref(w), 0x20001, 0x30000, 0x40000, None) == binding.XHC_ERR_INVALID_ARG
+    assert "aligned" in lib.last_error()
+    assert pre(ctypes.byref(c), ctypes.byref(w), 0x20000, 0x20000, 0x40000, None) == binding.XHC_ERR_INVALID_ARG
+    assert "alias" in lib.last_error()
+    assert pre(ctypes.byref(c), ctypes.byref(w), None, 0x30000, 0x40000, None) == binding.XHC_ERR_INVALID_ARG
+    w2 = XhcWeights()
+    w2.w_full = 0x10000
+    assert pre(ctypes.byref(c), ctypes.byref(w2), 0x20000, 0x30000, 0x40000, None) == binding.XHC_ERR_INVALID_ARG
+    assert pre(None, ctypes.byref(w), 0x20000, 0x30000, 0x40000, None) == binding.XHC_ERR_INVALID_ARG
+    # post of an MLP-type layer needs the conv kernels
+    w.conv_w = 0
+    rc = lib.dll.xhc_post(ctypes.byref(c), ctypes.byref(w), 0x20000, 0x30000, 0x40000, None)
+    assert rc == binding.XHC_ERR_INVALID_ARG and "conv_w" in lib.last_error()
+    # mHC shapes
+    cm = _cfg(N=3, k=0, m=0, n_convs=0).c()
+    assert lib.dll.mhc_pre(ctypes.byref(cm), ctypes.byref(w), 0x20000, 0x30000, 0x40000, None) == \
+        binding.XHC_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_host_tensors(lib):
+    cfg = _cfg(C=64, B=1, S=4)
+    wd = binding.Weights(w_full=torch.zeros(16 * 64, 32, dtype=torch.bfloat16), b_pre=torch.zeros(16),
+                         b_res=torch.zeros(16), b_post=torch.zeros(16), alpha_pre=0.01, alpha_res=0.01,
+                         alpha_post=0.01, w_act=torch.zeros(4 * 64, 32, dtype=torch.bfloat16))
+    X = torch.zeros(4, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lib.xhc_pre(cfg, wd, X, torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(1 << 20, dtype=torch.uint8))
