@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of the hyper-connection residual-stream layer on one GPU.
+
+A step is one pass of the whole layer path over one batch of synthetic
+input: for the default workload, the 8-layer xHC chain at N=16 streams,
+k=4 active (m=2 fixed), C=4096, batch 2 x seq 8192, bf16, layers
+alternating attention-type (K_r=1) and MLP-type (causal convolutions
+{4,8,12} + Gram-Schmidt, K_r=4), the state carried in place from layer to
+layer.  Every layer is xhc_pre then xhc_post through the C ABI; the
+sublayer F is a given tensor per layer (its cost is not part of the layer).
+
+Prints ONE JSON line.  ``value`` is tokens/s per layer (tokens x layers /
+elapsed); ``hbm`` gives the algorithmic bytes moved (state read/write
+counted once per the byte model below) as GB/s and as a fraction of the
+MI355X peak of 8 TB/s.  ``roofline`` covers the call that dominates the
+step, timed with HIP events on the stream the kernels are launched on.
+``cpu_baseline`` times the float64 oracle on a bounded sample of the same
+workload on the host cores.
+
+Byte model per token and layer (C-element units, state dtype): pre reads
+the N streams and writes the sublayer input (N + 1); post reads F's output
+and the k active rows and writes the k rows back (1 + 2k).  Weights (a few
+MiB per layer) and per-token coefficients (< 1%) are not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    # name: (kind, N, k, m, C, B, S, layer kinds)
+    "xhc_chain_n16k4_c4096": ("xhc", 16, 4, 2, 4096, 2, 8192, "AMAMAMAM"),
+    "xhc_mlp_n16k4_c2048": ("xhc", 16, 4, 2, 2048, 4, 4096, "M"),
+    "mhc_n4_c4096": ("mhc", 4, 4, 0, 4096, 4, 4096, "D"),
+    "mhc_n16_c4096": ("mhc", 16, 16, 0, 4096, 4, 4096, "D"),
+}
+DEFAULT = "xhc_chain_n16k4_c4096"
+SEED = {"xhc_chain_n16k4_c4096": 3, "xhc_mlp_n16k4_c2048": 2, "mhc_n4_c4096": 1, "mhc_n16_c4096": 4}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_configs(name):
+    from stream_residual_mixing_amd.binding import Config
+    kind, N, k, m, C, B, S, kinds = WORKLOADS[name]
+    cfgs = []
+    for lk in kinds:
+        if kind == "mhc":
+            cfgs.append(Config(N=N, C=C, B=B, S=S, dtype="bf16"))
+        else:
+            cfgs.append(Config(N=N, k=k, m=m, C=C, B=B, S=S, n_convs=3 if lk == "M" else 0, dtype="bf16"))
+    return kind, cfgs, kinds
+
+
+def bytes_per_token(kind, cfg, esz=2):
+    """Algorithmic bytes per token of (pre, post)."""
+    if kind == "mhc":
+        return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.N) * cfg.C * esz
+    return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.k) * cfg.C * esz
+
+
+def flops_per_token(kind, cfg):
+    if kind == "mhc":
+        return 2 * cfg.N * cfg.C * (2 * cfg.N + cfg.N * cfg.N)
+    return 2 * cfg.N * cfg.C * 2 * cfg.N + 2 * cfg.k * cfg.C * (cfg.k * cfg.k + cfg.k * cfg.K_r)
+
+
+def make_inputs(name, kind, cfgs, kinds):
+    """Seeded synthetic inputs (CPU) moved to the GPU."""
+    import torch
+    from stream_residual_mixing_amd import synth
+    from stream_residual_mixing_amd.binding import weights_to_device
+    seed = SEED[name]
+    c0 = cfgs[0]
+    t = time.time()
+    X = synth.state(seed, c0.T, c0.N, c0.C, "bf16").to("cuda")
+    outs, ws_ = [], []
+    for l, cfg in enumerate(cfgs):
+        outs.append(synth.sublayer_out(seed, l, cfg.B, cfg.S, cfg.C, "bf16").to("cuda"))
+        if kind == "mhc":
+            wd = synth.mhc_layer_weights(seed, l, cfg.N, cfg.C, "bf16")
+        else:
+            wd = synth.xhc_layer_weights(seed, l, cfg.N, cfg.k, cfg.C, cfg.K_r, "bf16")
+        ws_.append(weights_to_device(wd))
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t:.1f} s (X {tuple(X.shape)} {X.dtype})")
+    return X, outs, ws_
+
+
+def run_gpu(name, steps, warmup):
+    import torch
+    from stream_residual_mixing_amd import binding
+    kind, cfgs, kinds = layer_configs(name)
+    lib = binding.load()
+    X, outs, weights = make_inputs(name, kind, cfgs, kinds)
+    c0 = cfgs[0]
+    T = c0.T
+    inp = torch.empty((T, c0.C), dtype=torch.bfloat16, device="cuda")
+    mhc = kind == "mhc"
+    ws = lib.workspace(max(cfgs, key=lambda c: lib.workspace_bytes(c, mhc)), mhc)
+    stream = torch.cuda.current_stream()
+    pre = lib.mhc_pre if mhc else lib.xhc_pre
+    post = lib.mhc_post if mhc else lib.xhc_post
+    calls = [(f"{'mhc' if mhc else 'xhc'}_pre_{lk}", f"{'mhc' if mhc else 'xhc'}_post_{lk}") for lk in kinds]
+
+    def step(evs=None):
+        for l, cfg in enumerate(cfgs):
+            if evs is not None:
+                evs[l][0].record(stream)
+            pre(cfg, weights[l], X, inp, ws, stream)
+            if evs is not None:
+                evs[l][1].record(stream)
+            post(cfg, weights[l], X, outs[l], ws, stream)
+            if evs is not None:
+                evs[l][2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs_all = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in cfgs] for _ in range(steps)]
+    log(f"timing {steps} steps of {len(cfgs)} layers ({name})")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs_all[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_call = {}
+    for s in range(steps):
+        for l in range(len(cfgs)):
+            e = evs_all[s][l]
+            for j, (a, b) in enumerate(((e[0], e[1]), (e[1], e[2]))):
+                per_call.setdefault(calls[l][j], []).append(a.elapsed_time(b) * 1e-3)
+    return dict(kind=kind, cfgs=cfgs, kinds=kinds, elapsed=elapsed, per_call=per_call, T=T)
+
+
+def cpu_baseline(name, tokens=256):
+    """The oracle on the first `tokens` tokens of batch item 0, one layer of
+    each kind in the workload; tokens/s per layer."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import cases as K
+    from stream_residual_mixing_amd import synth
+    from stream_residual_mixing_amd.binding import Config
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    kind, cfgs, kinds = layer_configs(name)
+    seed = SEED[name]
+    done = {}
+    total_t, total_tok = 0.0, 0
+    for l, (cfg, lk) in enumerate(zip(cfgs, kinds)):
+        if lk in done:
+            continue
+        sub = Config(N=cfg.N, k=cfg.k, m=cfg.m, C=cfg.C, B=1, S=tokens, n_convs=cfg.n_convs, dtype="bf16")
+        X = K.f64(synth.state_rows(seed, range(tokens), cfg.N, cfg.C, "bf16"))
+        out = K.f64(synth.out_rows(seed, l, range(tokens), cfg.C, "bf16")).reshape(1, tokens, cfg.C)
+        if kind == "mhc":
+            ow = K.oracle_weights(synth.mhc_layer_weights(seed, l, cfg.N, cfg.C, "bf16"))
+            t = time.perf_counter()
+            K.oracle_mhc(sub, X, out, ow)
+        else:
+            ow = K.oracle_weights(synth.xhc_layer_weights(seed, l, cfg.N, cfg.k, cfg.C, cfg.K_r, "bf16"))
+            t = time.perf_counter()
+            K.oracle_xhc(sub, X, out, ow)
+        dt = time.perf_counter() - t
+        done[lk] = dt
+        total_t += dt
+        total_tok += tokens
+    kinds_s = "+".join({"A": "attention", "M": "MLP", "D": "dense"}[k] for k in done)
+    return dict(value=total_tok / total_t, unit="tokens/s per layer", cores=int(cores), kind="oracle",
+                sample=f"first {tokens} tokens of batch item 0, one {kinds_s} layer each, float64 NumPy")
+
+
+def copy_probe(nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of known size: the reference that scales
+    the hardware byte counters, and the achievable-bandwidth yardstick."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    dt = a.elapsed_time(b) * 1e-3 / reps
+    print(json.dumps({"copy_probe_bytes": nbytes, "read_plus_write_GBps": round(2 * nbytes / dt / 1e9, 1),
+                      "avg_us": round(dt * 1e6, 2)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the layer has no multi-GPU path in this library "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
+    r = run_gpu(args.workload, args.steps, args.warmup)
+    kind, cfgs, kinds, T = r["kind"], r["cfgs"], r["kinds"], r["T"]
+    L = len(cfgs)
+    ms_per_step = r["elapsed"] / args.steps * 1e3
+    value = T * L * args.steps / r["elapsed"]
+    # algorithmic bytes
+    step_bytes = 0
+    call_bytes = {}
+    for cfg, lk in zip(cfgs, kinds):
+        b_pre, b_post = bytes_per_token(kind, cfg)
+        step_bytes += T * (b_pre + b_post)
+        p = "mhc" if kind == "mhc" else "xhc"
+        call_bytes[f"{p}_pre_{lk}"] = T * b_pre
+        call_bytes[f"{p}_post_{lk}"] = T * b_post
+    hbm_gbps = step_bytes * args.steps / r["elapsed"] / 1e9
+    calls = {}
+    for name, ts in r["per_call"].items():
+        avg = sum(ts) / len(ts)
+        calls[name] = dict(avg_us=round(avg * 1e6, 2), share=None,
+                           GBps=round(call_bytes[name] / avg / 1e9, 1))
+    tot = sum(sum(ts) for ts in r["per_call"].values())
+    for name, ts in r["per_call"].items():
+        calls[name]["share"] = round(sum(ts) / tot, 3)
+    dom = max(r["per_call"], key=lambda n: sum(r["per_call"][n]))
+    dom_avg = sum(r["per_call"][dom]) / len(r["per_call"][dom])
+    achieved = call_bytes[dom] / dom_avg / 1e9
+    c0 = cfgs[0]
+    res = {
+        "metric": "xHC layer tokens/s + HBM GB/s (% of peak), N=16 k=4 C=4096, 1 MI355X"
+        if args.workload == DEFAULT else f"{args.workload} layer tokens/s",
+        "value": round(value, 1),
+        "unit": "tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "kind": kind, "N": c0.N, "k": c0.k if kind == "xhc" else c0.N,
+                   "m": c0.m, "C": c0.C, "batch": c0.B, "seq": c0.S, "tokens": T, "layers": kinds,
+                   "sinkhorn_iters": c0.iters},
+        "hbm": {"GBps": round(hbm_gbps, 1), "frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+                "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+                     "bytes_per_launch": call_bytes[dom], "avg_us": round(dom_avg * 1e6, 2)},
+        "calls": calls,
+        "mfma": {"flop_per_token_layer": [flops_per_token(kind, c) for c in cfgs][:2],
+                 "peak_TFLOPs_bf16": MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a CPU sample")
+        res["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -118,6 +118,8 @@ typedef struct {
   size_t h_res;     /* xHC: [T][k][k]; mHC: [T][N][N] */
   size_t h_post;    /* xHC: [T][k][K_r]; mHC: [T][N] */
   size_t z_router;  /* xHC: [T][N] router logits */
+  size_t status;    /* xHC: one int32, 0 after a normal xhc_pre; 1 if a wait between
+                       workgroups of the one-pass kernel gave up (results invalid) */
   size_t total;     /* bytes the caller must allocate (0 when T == 0) */
 } xhc_ws_layout;
 

@@ -48,7 +48,7 @@ class XhcWeights(ctypes.Structure):
 
 
 class XhcWsLayout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre", "h_res", "h_post", "z_router", "total")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre", "h_res", "h_post", "z_router", "status", "total")]
 
 
 class XhcError(RuntimeError):
@@ -204,7 +204,7 @@ class Lib:
                         h_post=view(L.h_post, (T, N)))
         return dict(idx=view(L.idx, (T, k), torch.int32), p=view(L.p, (T, k)), h_pre=view(L.h_pre, (T, N)),
                     h_res=view(L.h_res, (T, k, k)), h_post=view(L.h_post, (T, k, Kr)),
-                    z=view(L.z_router, (T, N)))
+                    z=view(L.z_router, (T, N)), status=view(L.status, (1,), torch.int32))
 
     def _check_common(self, cfg, w, X, ws, mhc, pre):
         dt = cfg.torch_dtype

@@ -95,6 +95,7 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     } else {
       return fail(XHC_ERR_INVALID_ARG, "n_convs=%d must be 0 or 3", cfg->n_convs);
     }
+    if (q.C > 32768) return fail(XHC_ERR_UNSUPPORTED, "xHC channels=%d above 32768", q.C);
     q.ncol_full = 2 * q.N;
     q.ncol_act = q.K * q.K + q.K * q.KR;
     q.NTA = (q.ncol_act + 15) / 16;
@@ -121,20 +122,29 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     q.o_hpre = take(T * N * 4);
     q.o_hres = take(T * N * N * 4);
     q.o_hpost = take(T * N * 4);
+    q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
+    q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
+    q.o_stats = take((size_t)q.KS * T * 2 * 4);
   } else {
+    // one-pass pre: 16-token tiles, G channel slices of 256 (bf16) / 128 (f32)
+    const long nkbC = q.C / KB;
+    q.G = (int)((nkbC + 7) / 8);
+    q.ntiles = (q.T + 15) / 16;
+    const size_t P1 = 16 * (size_t)q.NTF * 16 + 2 * 16 + 16;
+    const size_t P2 = 16 * (size_t)q.NTA * 16 + 16;
+    q.o_sync = take((2 + 3 * (size_t)q.ntiles) * 4);
     q.o_idx = take(T * K * 4);
     q.o_p = take(T * K * 4);
     q.o_hpre = take(T * N * 4);
     q.o_hres = take(T * K * K * 4);
     q.o_hpost = take(T * K * q.KR * 4);
     q.o_z = take(T * N * 4);
+    q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
     q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
-    q.o_colsum = take(N * 4);
+    q.o_part = take((size_t)q.ntiles * q.G * P1 * 4);
+    q.o_part2 = take((size_t)q.ntiles * q.G * P2 * 4);
     q.o_gram = take((size_t)q.nslices * T * 10 * 4);
   }
-  q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
-  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
-  q.o_stats = take((size_t)q.KS * T * 2 * 4);
   q.total = q.T == 0 ? 0 : off;
   *P = q;
   return XHC_OK;
@@ -175,6 +185,7 @@ xhc_status fill_layout(const xhc::Plan& P, xhc_ws_layout* out) {
   out->h_res = P.o_hres;
   out->h_post = P.o_hpost;
   out->z_router = P.o_z;
+  out->status = P.o_sync == SIZE_MAX ? SIZE_MAX : P.o_sync + 4;
   out->total = P.total;
   return XHC_OK;
 }

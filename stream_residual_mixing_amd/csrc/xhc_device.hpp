@@ -15,6 +15,8 @@ namespace xhc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte fragment as a native vector (register arrays of it stay in VGPRs)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
@@ -54,6 +56,18 @@ struct Bf16 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
   }
+  __device__ static __forceinline__ void unpack(const u32x4_t& v, float (&f)[8]) {
+    f[0] = bf16_lo(v[0]); f[1] = bf16_hi(v[0]); f[2] = bf16_lo(v[1]); f[3] = bf16_hi(v[1]);
+    f[4] = bf16_lo(v[2]); f[5] = bf16_hi(v[2]); f[6] = bf16_lo(v[3]); f[7] = bf16_hi(v[3]);
+  }
+  __device__ static __forceinline__ u32x4_t packv(const float (&f)[8]) {
+    return u32x4_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7])};
+  }
+  __device__ static __forceinline__ f32x4_t mma(f32x4_t acc, const u32x4_t& a, const u32x4_t& b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
 };
 
 struct F32 {
@@ -73,6 +87,19 @@ struct F32 {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    return acc;
+  }
+  __device__ static __forceinline__ void unpack(const u32x4_t& v, float (&f)[4]) {
+    f[0] = __uint_as_float(v[0]); f[1] = __uint_as_float(v[1]);
+    f[2] = __uint_as_float(v[2]); f[3] = __uint_as_float(v[3]);
+  }
+  __device__ static __forceinline__ u32x4_t packv(const float (&f)[4]) {
+    return u32x4_t{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  }
+  __device__ static __forceinline__ f32x4_t mma(f32x4_t acc, const u32x4_t& a, const u32x4_t& b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[s]), __uint_as_float(b[s]), acc, 0, 0, 0);
     return acc;
   }
 };

@@ -24,26 +24,30 @@ struct Plan {
   int ncol_full = 0, ncol_act = 0;  // logical projection widths
   int NTF = 0, NTA = 0;             // 16-column MFMA tiles
   long nkb_full = 0, nkb_act = 0;   // contraction blocks
-  int KS = 1;                       // split of the full-state contraction
+  int KS = 1;                       // split of the full-state contraction (mHC)
   int nslices = 1;                  // channel slices of the post kernels
+  int G = 1;                        // xHC pre: workgroups (channel slices) per 16-token tile
+  long ntiles = 0;                  // xHC pre: 16-token tiles
   // workspace byte offsets
   size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,
          o_z = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
-         o_gram = SIZE_MAX, total = 0;
+         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, total = 0;
 };
 
-struct XhcReadArgs {
+// xHC pre, fused one-pass kernel.  sync: [0] ticket counter, [1] status
+// word, then per tile: arrivals of phase 1, release flag, arrivals of phase 3.
+struct XhcPreArgs {
   const void* X;
   void* inp;
-  int T, C, m, KS;
-  const float* part;
-  const float* stats;
-  const float* colsum;
+  int T, C, m, G, ntiles;
+  const uint4* wfull;
   const uint4* wact;
   const float *b_pre, *b_res, *b_post;
-  float a_pre, a_res, a_post;
+  float a_pre, a_res, a_post, eps;
   int iters;
-  float eps;
+  float* part1;
+  float* part2;
+  int* sync;
   int* idx;
   float *p, *h_pre, *h_res, *h_post, *z;
 };

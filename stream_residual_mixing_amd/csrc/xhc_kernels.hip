@@ -1,16 +1,12 @@
 // libxhc kernels for gfx950.
 //
-// Pre stage (mapping generation + dense read):
+// mHC pre stage (mapping generation + dense read):
 //   pack_b      weights -> MFMA B fragments (once per call, a few MiB)
-//   colsum      column sums of the router weights (LayerNorm correction)
 //   proj_gen    one pass over X: split-K bf16/f32 MFMA projection of the raw
 //               (un-normalised) flattened state, plus sum x and sum x^2
-//   xhc_read    per 16 tokens: norm corrections, router, fixed + routed
-//               top-k, H_pre, dense read -> inp, gather of the active rows,
-//               active RMS, active MFMA projection, k x k Sinkhorn + row
-//               clamp, H_post
 //   mhc_read    per 16 tokens: RMS correction, H_pre / H_post, N x N
 //               Sinkhorn, dense read -> inp
+// (the xHC pre stage is the one-pass kernel of xhc_pre.hip)
 // Post stage:
 //   xhc_gram    MLP-type only: causal convolutions of out and the 4 x 4 Gram
 //               matrix of [out, g1, g2, g3] per token (partial per C slice)
@@ -48,24 +44,6 @@ __global__ __launch_bounds__(256) void pack_b_kernel(const typename E::T* __rest
     frag.v[e] = col < ncol ? W[row * ncol + col] : T(0);
   }
   out[f] = frag.u;
-}
-
-__device__ __forceinline__ float to_f32(uint16_t h) { return bf16_lo(h); }
-__device__ __forceinline__ float to_f32(float f) { return f; }
-
-// Column sums (float) of the first ncols columns of W [K][ncol]; one block
-// per column, fixed reduction order.
-template <class E>
-__global__ __launch_bounds__(256) void colsum_kernel(const typename E::T* __restrict__ W, long K, int ncol,
-                                                     float* __restrict__ out) {
-  const int col = blockIdx.x;
-  float s = 0.f;
-  for (long r = threadIdx.x; r < K; r += 256) s += to_f32(W[r * ncol + col]);
-  s = wave_sum(s);
-  __shared__ float sh[4];
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) out[col] = (sh[0] + sh[1]) + (sh[2] + sh[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -133,185 +111,7 @@ __global__ __launch_bounds__(256) void proj_gen_kernel(const typename E::T* __re
   }
 }
 
-// ---------------------------------------------------------------------------
-// xhc_read: block = 16 tokens; wave 0 routes, then the 4 waves split the
-// channels for the dense read and the active projection.
-// ---------------------------------------------------------------------------
-constexpr int RT = 16;  // tokens per read block
-
-template <class E, int N, int K, int KR>
-__global__ __launch_bounds__(256) void xhc_read_kernel(XhcReadArgs a) {
-  using T = typename E::T;
-  constexpr int NTF = (2 * N + 15) / 16;
-  constexpr int NA = K * K + K * KR;
-  constexpr int NTA = (NA + 15) / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * RT;
-  const int C = a.C;
-  const T* __restrict__ X = reinterpret_cast<const T*>(a.X);
-  T* __restrict__ inp = reinterpret_cast<T*>(a.inp);
-
-  __shared__ float s_hpre[RT][N];
-  __shared__ int s_idx[RT][K];
-  __shared__ float s_act[4][RT][NTA * 16];
-  __shared__ float s_ss[4][RT];
-
-  // 1. norm corrections, router, fixed + routed selection, H_pre
-  if (wave == 0 && lane < RT) {
-    const int t = t0 + lane;
-    if (t < a.T) {
-      float raw[2 * N];
-#pragma unroll
-      for (int j = 0; j < 2 * N; ++j) raw[j] = 0.f;
-      float s1 = 0.f, s2 = 0.f;
-      for (int ks = 0; ks < a.KS; ++ks) {
-        const float* pp = a.part + ((size_t)ks * a.T + t) * (NTF * 16);
-#pragma unroll
-        for (int j = 0; j < 2 * N; ++j) raw[j] += pp[j];
-        s1 += a.stats[((size_t)ks * a.T + t) * 2 + 0];
-        s2 += a.stats[((size_t)ks * a.T + t) * 2 + 1];
-      }
-      const float n_el = (float)N * (float)C;
-      const float mu = s1 / n_el, nu = s2 / n_el;
-      const float sd = sqrtf(fmaxf(nu - mu * mu, 0.f));
-      const float rstd_ln = 1.f / (sd + a.eps);
-      const float rrms = 1.f / sqrtf(nu + a.eps);
-      float z[N];
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        z[i] = (raw[i] - mu * a.colsum[i]) * rstd_ln;
-        a.z[(size_t)t * N + i] = z[i];
-        const float hp = sigmoidf_(fmaf(a.a_pre * raw[N + i], rrms, a.b_pre[i]));
-        a.h_pre[(size_t)t * N + i] = hp;
-        s_hpre[lane][i] = hp;
-      }
-      uint32_t taken = 0;
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        int sel;
-        float pj;
-        if (j < a.m) {
-          sel = j;
-          pj = 1.f;
-        } else {
-          int best = -1;
-          float bz = 0.f;
-#pragma unroll
-          for (int i = 0; i < N; ++i) {
-            const bool cand = (i >= a.m) && !((taken >> i) & 1u);
-            if (cand && (best < 0 || z[i] > bz)) { best = i; bz = z[i]; }
-          }
-          sel = best < 0 ? 0 : best;
-          pj = sigmoidf_(bz);
-        }
-        taken |= 1u << sel;
-        a.idx[(size_t)t * K + j] = sel;
-        a.p[(size_t)t * K + j] = pj;
-        s_idx[lane][j] = sel;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) s_hpre[lane][i] = 0.f;
-#pragma unroll
-      for (int j = 0; j < K; ++j) s_idx[lane][j] = j;
-    }
-  }
-  __syncthreads();
-
-  // 2. dense read over all N streams + active gather / RMS / projection
-  {
-    const int g = lane >> 4, r = lane & 15;
-    const int t = t0 + r;
-    const bool valid = t < a.T;
-    const int tt = valid ? t : t0;
-    float hp[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) hp[i] = s_hpre[r][i];
-    int I[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) I[j] = s_idx[r][j];
-    const int nkbC = C / E::KB;
-    const int kbA = wave * nkbC / 4, kbB = (wave + 1) * nkbC / 4;
-    f32x4_t acc[NTA];
-#pragma unroll
-    for (int n = 0; n < NTA; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
-    const T* xt = X + (size_t)tt * N * C + E::VEC * g;
-    for (int kb = kbA; kb < kbB; ++kb) {
-      const int c = kb * E::KB;
-      float o[E::VEC];
-#pragma unroll
-      for (int e = 0; e < E::VEC; ++e) o[e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float f[E::VEC];
-        E::unpack(ld16(xt + (size_t)i * C + c), f);
-#pragma unroll
-        for (int e = 0; e < E::VEC; ++e) o[e] = fmaf(hp[i], f[e], o[e]);
-      }
-      if (valid) st16(inp + (size_t)t * C + c + E::VEC * g, E::pack(o));
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const uint4 v = ld16(xt + (size_t)I[j] * C + c);
-        float f[E::VEC];
-        E::unpack(v, f);
-#pragma unroll
-        for (int e = 0; e < E::VEC; ++e) ss = fmaf(f[e], f[e], ss);
-        const uint4* wp = a.wact + ((size_t)(j * nkbC + kb) * NTA) * WAVE + lane;
-#pragma unroll
-        for (int n = 0; n < NTA; ++n) acc[n] = E::mma(acc[n], v, wp[n * WAVE]);
-      }
-    }
-    ss += __shfl_xor(ss, 16, WAVE);
-    ss += __shfl_xor(ss, 32, WAVE);
-    if (g == 0) s_ss[wave][r] = ss;
-#pragma unroll
-    for (int n = 0; n < NTA; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_act[wave][4 * g + i][n * 16 + r] = acc[n][i];
-  }
-  __syncthreads();
-
-  // 3. active maps: K lanes per token, one row of H_res per lane
-  if (wave == 0) {
-    constexpr int TPP = WAVE / K;               // tokens per pass
-    constexpr int PASSES = (RT + TPP - 1) / TPP;
-#pragma unroll
-    for (int pass = 0; pass < PASSES; ++pass) {
-      const int tau = pass * TPP + lane / K;
-      const int row = lane % K;
-      const int t = t0 + tau;
-      const bool valid = tau < RT && t < a.T;
-      const int tq = tau < RT ? tau : 0;
-      const float ss = (s_ss[0][tq] + s_ss[1][tq]) + (s_ss[2][tq] + s_ss[3][tq]);
-      const float rr = 1.f / sqrtf(ss / ((float)K * (float)C) + a.eps);
-      float L[K];
-#pragma unroll
-      for (int b = 0; b < K; ++b) {
-        const int col = row * K + b;
-        const float v = (s_act[0][tq][col] + s_act[1][tq][col]) + (s_act[2][tq][col] + s_act[3][tq][col]);
-        L[b] = fmaf(a.a_res * v, rr, a.b_res[col]);
-      }
-      sinkhorn_rows<K>(L, a.iters);
-      float rs = 0.f;
-#pragma unroll
-      for (int b = 0; b < K; ++b) rs += L[b];
-      const float d = fmaxf(rs, 1.f);
-#pragma unroll
-      for (int b = 0; b < K; ++b) L[b] = L[b] / d;
-      if (valid) {
-#pragma unroll
-        for (int b = 0; b < K; ++b) a.h_res[((size_t)t * K + row) * K + b] = L[b];
-#pragma unroll
-        for (int q = 0; q < KR; ++q) {
-          const int col = K * K + row * KR + q;
-          const float v = (s_act[0][tq][col] + s_act[1][tq][col]) + (s_act[2][tq][col] + s_act[3][tq][col]);
-          a.h_post[((size_t)t * K + row) * KR + q] = 2.f * sigmoidf_(fmaf(a.a_post * v, rr, a.b_post[row * KR + q]));
-        }
-      }
-    }
-  }
-}
+constexpr int RT = 16;  // tokens per mHC read block
 
 // ---------------------------------------------------------------------------
 // mhc_read: block = 16 tokens.  N lanes per token (one row of H_res each)
@@ -683,11 +483,6 @@ static void launch_pack(const void* W, long nkb, int ncol, int NT, void* out, hi
                                                                 ncol, NT, reinterpret_cast<uint4*>(out));
 }
 
-template <class E>
-static void launch_colsum(const void* W, long K, int ncol, int ncols, float* out, hipStream_t st) {
-  colsum_kernel<E><<<ncols, 256, 0, st>>>(reinterpret_cast<const typename E::T*>(W), K, ncol, out);
-}
-
 template <class E, int NT>
 static void launch_gen(const void* X, int T, long K, const void* Wp, long nkb, int KS, float* part, float* stats,
                        hipStream_t st) {
@@ -708,11 +503,6 @@ static bool gen_dispatch(int NT, const void* X, int T, long K, const void* Wp, l
   }
 }
 
-template <class E, int N, int K, int KR>
-static void launch_xhc_read(const XhcReadArgs& a, hipStream_t st) {
-  xhc_read_kernel<E, N, K, KR><<<(a.T + RT - 1) / RT, 256, 0, st>>>(a);
-}
-
 template <class E, int K, int KR>
 static void launch_xhc_apply(const XhcPostArgs& a, hipStream_t st) {
   dim3 grid((a.T + PT - 1) / PT, a.nslices);
@@ -728,45 +518,6 @@ template <class E, int N>
 static void launch_mhc_post(const MhcPostArgs& a, hipStream_t st) {
   dim3 grid((a.T + 31) / 32, a.nslices);
   mhc_post_kernel<E, N><<<grid, 256, 0, st>>>(a);
-}
-
-template <class E>
-static bool xhc_pre_launch(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st) {
-  launch_pack<E>(w->w_full, P.nkb_full, P.ncol_full, P.NTF, ws + P.o_wfull, st);
-  launch_pack<E>(w->w_act, P.nkb_act, P.ncol_act, P.NTA, ws + P.o_wact, st);
-  launch_colsum<E>(w->w_full, (long)P.N * P.C, P.ncol_full, P.N, reinterpret_cast<float*>(ws + P.o_colsum), st);
-  if (!gen_dispatch<E>(P.NTF, X, (int)P.T, (long)P.N * P.C, ws + P.o_wfull, P.nkb_full, P.KS,
-                       reinterpret_cast<float*>(ws + P.o_part), reinterpret_cast<float*>(ws + P.o_stats), st))
-    return false;
-  XhcReadArgs a;
-  a.X = X; a.inp = inp; a.T = (int)P.T; a.C = P.C; a.m = P.m; a.KS = P.KS;
-  a.part = reinterpret_cast<const float*>(ws + P.o_part);
-  a.stats = reinterpret_cast<const float*>(ws + P.o_stats);
-  a.colsum = reinterpret_cast<const float*>(ws + P.o_colsum);
-  a.wact = reinterpret_cast<const uint4*>(ws + P.o_wact);
-  a.b_pre = w->b_pre; a.b_res = w->b_res; a.b_post = w->b_post;
-  a.a_pre = w->alpha_pre; a.a_res = w->alpha_res; a.a_post = w->alpha_post;
-  a.iters = P.iters; a.eps = P.eps_norm;
-  a.idx = reinterpret_cast<int*>(ws + P.o_idx);
-  a.p = reinterpret_cast<float*>(ws + P.o_p);
-  a.h_pre = reinterpret_cast<float*>(ws + P.o_hpre);
-  a.h_res = reinterpret_cast<float*>(ws + P.o_hres);
-  a.h_post = reinterpret_cast<float*>(ws + P.o_hpost);
-  a.z = reinterpret_cast<float*>(ws + P.o_z);
-  const int key = P.N * 100 + P.K * 10 + P.KR;
-  switch (key) {
-    case 1641: launch_xhc_read<E, 16, 4, 1>(a, st); return true;
-    case 1644: launch_xhc_read<E, 16, 4, 4>(a, st); return true;
-    case 1621: launch_xhc_read<E, 16, 2, 1>(a, st); return true;
-    case 1624: launch_xhc_read<E, 16, 2, 4>(a, st); return true;
-    case 841: launch_xhc_read<E, 8, 4, 1>(a, st); return true;
-    case 844: launch_xhc_read<E, 8, 4, 4>(a, st); return true;
-    case 441: launch_xhc_read<E, 4, 4, 1>(a, st); return true;
-    case 444: launch_xhc_read<E, 4, 4, 4>(a, st); return true;
-    case 111: launch_xhc_read<E, 1, 1, 1>(a, st); return true;
-    case 114: launch_xhc_read<E, 1, 1, 4>(a, st); return true;
-    default: return false;
-  }
 }
 
 template <class E>
@@ -836,9 +587,6 @@ static bool mhc_post_launch(const Plan& P, void* X, const void* out, char* ws, h
   }
 }
 
-bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st) {
-  return P.dtype == XHC_BF16 ? xhc_pre_launch<Bf16>(P, X, inp, w, ws, st) : xhc_pre_launch<F32>(P, X, inp, w, ws, st);
-}
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
   return P.dtype == XHC_BF16 ? xhc_post_launch<Bf16>(P, X, out, w, ws, st) : xhc_post_launch<F32>(P, X, out, w, ws, st);
 }

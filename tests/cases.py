@@ -102,6 +102,7 @@ def gpu_xhc(lib, cfg: Config, X, out, wd, stream=None):
     ws = lib.workspace(cfg)
     lib.xhc_pre(cfg, w, Xd, inp, ws, stream)
     arrays = {k: v.clone() for k, v in lib.ws_arrays(cfg, ws).items()}
+    assert int(arrays.pop("status").item()) == 0, "a wait between workgroups gave up"
     lib.xhc_post(cfg, w, Xd, outd, ws, stream)
     torch.cuda.synchronize()
     return dict(inp=inp.cpu(), X=Xd.cpu(), **{k: v.cpu() for k, v in arrays.items()})
