@@ -104,24 +104,26 @@ struct F32 {
   }
 };
 
-// Small vectors of CH channels (CH = 4) used by the post kernels.
+// Small vectors of 4 channels used by the post kernels (native vector types,
+// so that register arrays of them are not demoted to scratch memory).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <class E> struct Quad;
 template <> struct Quad<Bf16> {
-  using V = uint2;   // 4 bf16
+  using V = u32x2_t;   // 4 bf16
   __device__ static __forceinline__ void unpack(const V& v, float (&f)[4]) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
   }
   __device__ static __forceinline__ V pack(const float (&f)[4]) {
-    return make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+    return V{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
   }
 };
 template <> struct Quad<F32> {
-  using V = float4;
+  using V = f32x4_t;
   __device__ static __forceinline__ void unpack(const V& v, float (&f)[4]) {
     f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
   }
   __device__ static __forceinline__ V pack(const float (&f)[4]) {
-    return make_float4(f[0], f[1], f[2], f[3]);
+    return V{f[0], f[1], f[2], f[3]};
   }
 };
 

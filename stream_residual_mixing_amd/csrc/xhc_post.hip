@@ -1,0 +1,399 @@
+// xHC after the sublayer (gfx950): write basis, Gram-Schmidt, mix and the
+// gated write of the k active rows, in place.
+//
+// After an MLP-type sublayer the write basis of a token is F's output plus
+// three causal depthwise convolutions of it along the sequence (kernel sizes
+// 4, 8, 12), made mutually orthogonal along C by modified Gram-Schmidt
+// (explainer "xHC: sixteen residual streams, four written at a time",
+// section "What xHC changes"; summary "小红书xHC：时序特征增强 + 稀疏写回",
+// section 3.3).  Gram-Schmidt needs inner products over all C channels of a
+// token before any channel can be written, so the work is done in two passes
+// over the same tiling (a block = PT consecutive tokens x 1024 channels, a
+// thread = 4 channels):
+//
+//   xhc_gram   the Gram matrix of [out, g1, g2, g3] per token, partial over
+//              the block's channels (10 numbers per token and slice);
+//   xhc_apply  Gram-Schmidt coefficients from the summed Gram matrix (the same
+//              sequence of projections, carried out on coefficient vectors),
+//              then for each of the k active rows
+//                x_j <- sum_i H_res[j][i] x_i + p_j sum_r H_post[j][r] v_r,
+//              written in place; the other N - k rows are never touched
+//              (xHC paper "xHC: Expanded Hyper-Connections", paragraph
+//              "Mapping application"; summary 3.4.3).
+//
+// Each thread keeps its conv weights and the last 11 rows of `out` for its
+// channels in registers and slides along the tokens of its block, so `out`
+// is read once per pass (plus an 11-row history at the start of a block).
+// Attention-type sublayers (K_r = 1) skip the first pass.
+#include "xhc_device.hpp"
+#include "xhc_internal.hpp"
+
+namespace xhc {
+
+namespace {
+
+template <class E>
+__device__ __forceinline__ typename Quad<E>::V ldq(const typename E::T* p) {
+  return *reinterpret_cast<const typename Quad<E>::V*>(p);
+}
+
+__device__ __forceinline__ void load_conv_weights(const float* __restrict__ cw, int C, int c, bool act,
+                                                  float (&w1)[4][4], float (&w2)[8][4], float (&w3)[12][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = act ? *reinterpret_cast<const float4*>(cw + (size_t)i * C + c) : make_float4(0, 0, 0, 0);
+    w1[i][0] = v.x; w1[i][1] = v.y; w1[i][2] = v.z; w1[i][3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = act ? *reinterpret_cast<const float4*>(cw + (size_t)(4 + i) * C + c) : make_float4(0, 0, 0, 0);
+    w2[i][0] = v.x; w2[i][1] = v.y; w2[i][2] = v.z; w2[i][3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const float4 v = act ? *reinterpret_cast<const float4*>(cw + (size_t)(12 + i) * C + c) : make_float4(0, 0, 0, 0);
+    w3[i][0] = v.x; w3[i][1] = v.y; w3[i][2] = v.z; w3[i][3] = v.w;
+  }
+}
+
+// Start of a block, before its first token t0 (position s0 in its sequence)
+// is pushed: h[i] = out[t0 - 1 - i] for the rows inside that sequence, zero
+// before its start, so that after the push h[i] = out[t0 - i].
+template <class E>
+__device__ __forceinline__ void load_history(const typename E::T* __restrict__ out, int t0, int s0, int C, int c,
+                                             bool act, float (&h)[12][4]) {
+  typename Quad<E>::V v[11];
+#pragma unroll
+  for (int i = 0; i < 11; ++i) {
+    if (act && i + 1 <= s0) v[i] = ldq<E>(out + (size_t)(t0 - 1 - i) * C + c);
+    else v[i] = typename Quad<E>::V{};
+  }
+#pragma unroll
+  for (int i = 0; i < 11; ++i) Quad<E>::unpack(v[i], h[i]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[11][e] = 0.f;
+}
+
+// Move to the next token (position s): shift the history by one, drop it
+// entirely at a sequence start, and insert the token's own row at lag 0.
+__device__ __forceinline__ void push_history(float (&h)[12][4], const float (&row)[4], int s) {
+#pragma unroll
+  for (int i = 11; i >= 1; --i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[i][e] = s == 0 ? 0.f : h[i - 1][e];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[0][e] = row[e];
+}
+
+// Basis [out, g1, g2, g3] for this thread's 4 channels from the history:
+// g_j = sum_{i < kappa_j} w_j[i] * out[t - i] (lag i; kappa = 4, 8, 12).
+__device__ __forceinline__ void conv_basis(const float (&h)[12][4], const float (&w1)[4][4],
+                                           const float (&w2)[8][4], const float (&w3)[12][4], float (&b)[4][4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    b[0][e] = h[0][e];
+    float g1 = 0.f, g2 = 0.f, g3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g1 = fmaf(w1[i][e], h[i][e], g1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g2 = fmaf(w2[i][e], h[i][e], g2);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) g3 = fmaf(w3[i][e], h[i][e], g3);
+    b[1][e] = g1;
+    b[2][e] = g2;
+    b[3][e] = g3;
+  }
+}
+
+// One step of a reduce-scatter butterfly over the wave: lanes whose bit m is
+// set keep the upper half of their values, the others the lower half, and
+// each adds its partner's copy of the half it keeps.
+template <int H>
+__device__ __forceinline__ void rs_step(const float (&v)[2 * H], float (&o)[H], int lane, int m) {
+  const bool up = (lane & m) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float keep = up ? v[H + i] : v[i];
+    const float give = up ? v[i] : v[H + i];
+    o[i] = keep + __shfl_xor(give, m, WAVE);
+  }
+}
+
+// Sum of 16 values over the 64 lanes of a wave.  On return every lane holds
+// one total: the one with index 8 b5 + 4 b4 + 2 b3 + b2 (bits of the lane
+// id); the four lanes of a group of 4 hold the same value.  17 shuffles.
+__device__ __forceinline__ float wave_sum16(const float (&v)[16], int lane) {
+  float a[8], b[4], c[2], d[1];
+  rs_step<8>(v, a, lane, 32);
+  rs_step<4>(a, b, lane, 16);
+  rs_step<2>(b, c, lane, 8);
+  rs_step<1>(c, d, lane, 4);
+  float x = d[0];
+  x += __shfl_xor(x, 2, WAVE);
+  x += __shfl_xor(x, 1, WAVE);
+  return x;
+}
+__device__ __forceinline__ int wave_sum16_index(int lane) {
+  return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+}
+
+// Modified Gram-Schmidt on coefficient vectors: v_j = sum_a Tm[j][a] basis_a,
+// with <x, y> = x^T G y (G = Gram matrix of the basis).  The same sequence
+// of projections and the same eps as on the vectors themselves (summary
+// 3.3), so the result is exact in real arithmetic.
+__device__ __forceinline__ void mgs_from_gram(const float (&G)[4][4], float eps, float (&Tm)[4][4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.f : 0.f;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    float u[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) u[b] = (j == b) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 0; i < j; ++i) {
+      float Gt[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        float s = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) s = fmaf(G[x][y], Tm[i][y], s);
+        Gt[x] = s;
+      }
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        num = fmaf(u[x], Gt[x], num);
+        den = fmaf(Tm[i][x], Gt[x], den);
+      }
+      const float cf = num / (den + eps);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) u[x] = fmaf(-cf, Tm[i][x], u[x]);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Tm[j][b] = u[b];
+  }
+}
+
+constexpr int GB = 8;   // tokens per load batch in the Gram pass
+
+}  // namespace
+
+// Gram matrix of [out, g1, g2, g3] per token over this block's channels.
+template <class E>
+__global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
+  using T = typename E::T;
+  using Qd = Quad<E>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slice = blockIdx.y;
+  const int c = slice * PSLICE + tid * PCH;
+  const bool act = c < a.C;
+  const int cc = act ? c : 0;
+  const int t0 = blockIdx.x * PT;
+  const int t1 = min(t0 + PT, a.T);
+  const T* __restrict__ out = reinterpret_cast<const T*>(a.out);
+  __shared__ float s_g[PT][4][10];
+
+  float w1[4][4], w2[8][4], w3[12][4];
+  load_conv_weights(a.conv_w, a.C, cc, act, w1, w2, w3);
+  float h[12][4];
+  load_history<E>(out, t0, t0 % a.S, a.C, cc, act, h);
+  const int myidx = wave_sum16_index(lane);
+
+  for (int tb = t0; tb < t1; tb += GB) {
+    typename Qd::V rows[GB];
+#pragma unroll
+    for (int q = 0; q < GB; ++q)
+      rows[q] = (act && tb + q < t1) ? ldq<E>(out + (size_t)(tb + q) * a.C + cc) : typename Qd::V{};
+#pragma unroll
+    for (int q = 0; q < GB; ++q) {
+      const int t = tb + q;
+      if (t >= t1) break;
+      float r[4];
+      Qd::unpack(rows[q], r);
+      push_history(h, r, t % a.S);
+      float b[4][4];
+      conv_basis(h, w1, w2, w3, b);
+      float pr[16];
+      int k = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = u; v < 4; ++v) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d = fmaf(b[u][e], b[v][e], d);
+          pr[k++] = d;
+        }
+#pragma unroll
+      for (int j = 10; j < 16; ++j) pr[j] = 0.f;
+      const float tot = wave_sum16(pr, lane);
+      if ((lane & 3) == 0 && myidx < 10) s_g[t - t0][wave][myidx] = tot;
+    }
+  }
+  __syncthreads();
+  for (int u = tid; u < (t1 - t0) * 10; u += 256) {
+    const int tau = u / 10, j = u % 10;
+    a.gram[((size_t)slice * a.T + t0 + tau) * 10 + j] =
+        (s_g[tau][0][j] + s_g[tau][1][j]) + (s_g[tau][2][j] + s_g[tau][3][j]);
+  }
+}
+
+// Mix + gated write of the k active rows, in place.  PB tokens per load batch.
+template <class E, int K, int KR, int PB>
+__global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
+  using T = typename E::T;
+  using Qd = Quad<E>;
+  const int tid = threadIdx.x;
+  const int slice = blockIdx.y;
+  const int c = slice * PSLICE + tid * PCH;
+  const bool act = c < a.C;
+  const int cc = act ? c : 0;
+  const int t0 = blockIdx.x * PT;
+  const int t1 = min(t0 + PT, a.T);
+  T* __restrict__ X = reinterpret_cast<T*>(a.X);
+  const T* __restrict__ out = reinterpret_cast<const T*>(a.out);
+  __shared__ float s_Q[PT][K][KR];
+  __shared__ float s_H[PT][K][K];
+  __shared__ int s_I[PT][K];
+
+  // per-token coefficients: Q = diag(p) H_post Tm (Tm = Gram-Schmidt map)
+  for (int tau = tid; tau < t1 - t0; tau += 256) {
+    const int t = t0 + tau;
+    float Tm[4][4];
+    if (KR == 4 && a.use_mgs) {
+      float pg[10];
+#pragma unroll
+      for (int j = 0; j < 10; ++j) pg[j] = 0.f;
+      for (int sl = 0; sl < a.nslices; ++sl)
+#pragma unroll
+        for (int j = 0; j < 10; ++j) pg[j] += a.gram[((size_t)sl * a.T + t) * 10 + j];
+      float G[4][4];
+      int q = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = u; v < 4; ++v) { G[u][v] = pg[q]; G[v][u] = pg[q]; ++q; }
+      mgs_from_gram(G, a.eps_mgs, Tm);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.f : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int ij = a.idx[(size_t)t * K + j];
+      ij = ij < 0 ? 0 : (ij >= a.N ? a.N - 1 : ij);
+      s_I[tau][j] = ij;
+      const float pj = a.p[(size_t)t * K + j];
+#pragma unroll
+      for (int i = 0; i < K; ++i) s_H[tau][j][i] = a.h_res[((size_t)t * K + j) * K + i];
+      float hpo[KR];
+#pragma unroll
+      for (int r = 0; r < KR; ++r) hpo[r] = a.h_post[((size_t)t * K + j) * KR + r];
+#pragma unroll
+      for (int b = 0; b < KR; ++b) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) s = fmaf(hpo[r], Tm[r][b], s);
+        s_Q[tau][j][b] = pj * s;
+      }
+    }
+  }
+  __syncthreads();
+  if (!act) return;
+
+  float w1[4][4], w2[8][4], w3[12][4];
+  float h[12][4];
+  if (KR == 4) {
+    load_conv_weights(a.conv_w, a.C, c, true, w1, w2, w3);
+    load_history<E>(out, t0, t0 % a.S, a.C, c, true, h);
+  }
+  for (int tb = t0; tb < t1; tb += PB) {
+    typename Qd::V orow[PB];
+    typename Qd::V xr[PB][K];
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      const int t = tb + q;
+      const bool ok = t < t1;
+      orow[q] = ok ? ldq<E>(out + (size_t)t * a.C + c) : typename Qd::V{};
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        xr[q][j] = ok ? ldq<E>(X + ((size_t)t * a.N + s_I[t - t0][j]) * a.C + c) : typename Qd::V{};
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      const int t = tb + q;
+      if (t >= t1) break;
+      const int tau = t - t0;
+      float b[KR][4];
+      float r[4];
+      Qd::unpack(orow[q], r);
+      if constexpr (KR == 4) {
+        push_history(h, r, t % a.S);
+        conv_basis(h, w1, w2, w3, b);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[0][e] = r[e];
+      }
+      float xa[K][4];
+#pragma unroll
+      for (int j = 0; j < K; ++j) Qd::unpack(xr[q][j], xa[j]);
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        float nv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = 0.f;
+#pragma unroll
+          for (int i = 0; i < K; ++i) s = fmaf(s_H[tau][j][i], xa[i][e], s);
+#pragma unroll
+          for (int v = 0; v < KR; ++v) s = fmaf(s_Q[tau][j][v], b[v][e], s);
+          nv[e] = s;
+        }
+        *reinterpret_cast<typename Qd::V*>(X + ((size_t)t * a.N + s_I[tau][j]) * a.C + c) = Qd::pack(nv);
+      }
+    }
+  }
+}
+
+template <class E, int K, int KR>
+static void launch_apply(const XhcPostArgs& a, hipStream_t st) {
+  dim3 grid((a.T + PT - 1) / PT, a.nslices);
+  constexpr int PB = KR == 4 ? 4 : 8;
+  xhc_apply_kernel<E, K, KR, PB><<<grid, 256, 0, st>>>(a);
+}
+
+template <class E>
+static bool xhc_post_launch(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
+  XhcPostArgs a;
+  a.X = X; a.out = out; a.T = (int)P.T; a.S = P.S; a.C = P.C; a.N = P.N; a.nslices = P.nslices;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.p = reinterpret_cast<const float*>(ws + P.o_p);
+  a.h_res = reinterpret_cast<const float*>(ws + P.o_hres);
+  a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+  a.conv_w = w->conv_w; a.use_mgs = P.use_mgs; a.eps_mgs = P.eps_mgs;
+  a.gram = reinterpret_cast<float*>(ws + P.o_gram);
+  if (P.KR == 4 && P.use_mgs) {
+    dim3 grid((a.T + PT - 1) / PT, a.nslices);
+    xhc_gram_kernel<E><<<grid, 256, 0, st>>>(a);
+  }
+  switch (P.K * 10 + P.KR) {
+    case 41: launch_apply<E, 4, 1>(a, st); return true;
+    case 44: launch_apply<E, 4, 4>(a, st); return true;
+    case 21: launch_apply<E, 2, 1>(a, st); return true;
+    case 24: launch_apply<E, 2, 4>(a, st); return true;
+    case 11: launch_apply<E, 1, 1>(a, st); return true;
+    case 14: launch_apply<E, 1, 4>(a, st); return true;
+    default: return false;
+  }
+}
+
+bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
+  return P.dtype == XHC_BF16 ? xhc_post_launch<Bf16>(P, X, out, w, ws, st)
+                             : xhc_post_launch<F32>(P, X, out, w, ws, st);
+}
+
+}  // namespace xhc
