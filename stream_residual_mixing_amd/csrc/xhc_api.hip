@@ -126,9 +126,10 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
     q.o_stats = take((size_t)q.KS * T * 2 * 4);
   } else {
-    // one-pass pre: 16-token tiles, G channel slices of 256 (bf16) / 128 (f32)
+    // one-pass pre: 16-token tiles, G channel slices of PRE_WV * PRE_NKW blocks
     const long nkbC = q.C / KB;
-    q.G = (int)((nkbC + 7) / 8);
+    constexpr int SB = xhc::PRE_WV * xhc::PRE_NKW;
+    q.G = (int)((nkbC + SB - 1) / SB);
     q.ntiles = (q.T + 15) / 16;
     const size_t P1 = 16 * (size_t)q.NTF * 16 + 2 * 16 + 16;
     const size_t P2 = 16 * (size_t)q.NTA * 16 + 16;

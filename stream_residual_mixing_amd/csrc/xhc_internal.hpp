@@ -12,6 +12,9 @@ namespace xhc {
 constexpr int PT = 64;             // tokens per post block
 constexpr int PCH = 4;             // channels per post thread
 constexpr int PSLICE = 256 * PCH;  // channels per post block
+constexpr int PRE_NKW = 1;         // xHC pre: contraction blocks per wave and stream
+constexpr int PRE_WV = 8;          // xHC pre: waves per workgroup
+                                   // (a channel slice is PRE_WV x PRE_NKW blocks)
 
 // Everything a call needs, derived once from the config.
 struct Plan {

@@ -36,7 +36,9 @@ namespace xhc {
 namespace {
 
 constexpr int TM = 16;    // tokens per tile (MFMA rows)
-constexpr int NKW = 2;    // contraction blocks per wave and stream
+constexpr int NKW = PRE_NKW;  // contraction blocks per wave and stream
+constexpr int WV = PRE_WV;    // waves per workgroup
+constexpr int NTHR = WV * 64;
 // A wait gives up after this many ticks of the 100 MHz real-time counter (2 s).
 constexpr uint64_t WAIT_LIMIT_TICKS = 200000000ull;
 
@@ -69,6 +71,10 @@ __device__ __forceinline__ float ld_co(const float* p) {
 __device__ __forceinline__ int ld_co(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t ld_co64(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait for all of this wave's outstanding memory operations.
 __device__ __forceinline__ void wait_mem() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -90,23 +96,35 @@ __device__ __forceinline__ void wait_flag(int* flag, int* status) {
 }
 
 // dst[u] = sum over s < G, in order s = 0, 1, ..., of src[s * stride + u], for
-// u < n, one element per thread in turn.  The loads of up to 16 slices are
-// issued together, so the latency of fetching the partials is paid once per
-// batch rather than once per slice.
+// u < n (n and stride even; two neighbouring elements per thread, read with
+// one 8-byte coherent load).  The loads of up to 16 slices are issued
+// together, so the latency of fetching the partials is paid once per batch
+// rather than once per slice.
 __device__ __forceinline__ void sum_slices(const float* __restrict__ src, int G, int stride, int n,
                                            float* __restrict__ dst, int tid) {
-  for (int u = tid; u < n; u += 256) {
-    float v = 0.f;
+  for (int u = 2 * tid; u < n; u += 2 * NTHR) {
+    float v0 = 0.f, v1 = 0.f;
     for (int s0 = 0; s0 < G; s0 += 16) {
-      float x[16];
+      uint64_t x[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_co(src + (size_t)(s0 + q) * stride + u) : 0.f;
+      for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_co64(src + (size_t)(s0 + q) * stride + u) : 0ull;
 #pragma unroll
       for (int q = 0; q < 16; ++q)
-        if (s0 + q < G) v += x[q];
+        if (s0 + q < G) {
+          v0 += __uint_as_float((uint32_t)x[q]);
+          v1 += __uint_as_float((uint32_t)(x[q] >> 32));
+        }
     }
-    dst[u] = v;
+    dst[u] = v0;
+    dst[u + 1] = v1;
   }
+}
+
+// Sum of the WV per-wave partials of element u, in a fixed order.
+template <int PM>
+__device__ __forceinline__ float sum_waves(const float (&r)[WV][PM], int u) {
+  static_assert(WV == 8, "fixed-order sum written for 8 waves");
+  return ((r[0][u] + r[1][u]) + (r[2][u] + r[3][u])) + ((r[4][u] + r[5][u]) + (r[6][u] + r[7][u]));
 }
 
 // A fragment of 1.0 in every element (bf16 0x3f80, f32 0x3f800000)
@@ -117,7 +135,7 @@ template <> __device__ __forceinline__ u32x4_t ones_frag<F32>() { return u32x4_t
 }  // namespace
 
 template <class E, int N, int K, int KR>
-__global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
+__global__ __launch_bounds__(NTHR, 4) void xhc_pre_fused_kernel(XhcPreArgs a) {
   using T = typename E::T;
   constexpr int NTF = (2 * N + 15) / 16;
   constexpr int NPF = NTF * 16;
@@ -135,7 +153,7 @@ __global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
   const int nkbC = C / KB;
 
   __shared__ int s_msg;
-  __shared__ float s_red[4][PMAX];
+  __shared__ float s_red[WV][PMAX];
   __shared__ float s_hpre[TM][N];
   __shared__ float s_z[TM][N];
   __shared__ int s_idx[TM][K];
@@ -152,7 +170,8 @@ __global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
   int* cnt2 = ready + a.ntiles;
 
   // ---------------------------------------------------------------- phase 1
-  const int kb0 = slice * (4 * NKW) + wave * NKW;   // first contraction block of this wave (within C)
+  const int kb0 = slice * (WV * NKW) + wave * NKW;   // first contraction block of this wave (within C)
+  static_assert(P1 % 2 == 0 && P2 % 2 == 0, "partials are read in pairs");
   const T* __restrict__ X = reinterpret_cast<const T*>(a.X);
   const T* xt = X + (size_t)(tvalid ? tok : 0) * N * C + VEC * g;
   u32x4_t xd[N][NKW];
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
   __syncthreads();
   if (wave == 0) {
     float* dst = a.part1 + (size_t)ticket * P1;
-    for (int u = lane; u < P1; u += WAVE) st_co(dst + u, (s_red[0][u] + s_red[1][u]) + (s_red[2][u] + s_red[3][u]));
+    for (int u = lane; u < P1; u += WAVE) st_co(dst + u, sum_waves(s_red, u));
     wait_mem();
     if (lane == 0) s_msg = __hip_atomic_fetch_add(cnt1 + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -216,7 +235,7 @@ __global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
     __syncthreads();
     const float* sm = &s_red[1][0];
     const float n_el = (float)N * (float)C;
-    for (int u = tid; u < TM * N; u += 256) {
+    for (int u = tid; u < TM * N; u += NTHR) {
       const int tau = u / N, i = u % N;
       const int t = t0 + tau;
       const float rr = sm[tau * NPF + i], rp = sm[tau * NPF + N + i];
@@ -289,13 +308,11 @@ __global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
   }
 
   // ---------------------------------------------------------------- phase 3
-  float hp[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) hp[i] = s_hpre[r][i];
+  // Gather + active projection first, so that the partial can be published
+  // before this wave's stores of the sublayer input are in flight.
   int I[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) I[j] = s_idx[r][j];
-  T* __restrict__ inp = reinterpret_cast<T*>(a.inp);
   f32x4_t acc2[NTA];
 #pragma unroll
   for (int n = 0; n < NTA; ++n) acc2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -304,17 +321,6 @@ __global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
   for (int q = 0; q < NKW; ++q) {
     const int kb = kb0 + q;
     if (kb < nkbC) {
-      float o[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        float f[VEC];
-        E::unpack(xd[i][q], f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = fmaf(hp[i], f[e], o[e]);
-      }
-      if (tvalid) st16_nt(inp + (size_t)tok * C + kb * KB + VEC * g, E::packv(o));
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         u32x4_t v = xd[0][q];
@@ -341,9 +347,30 @@ __global__ __launch_bounds__(256) void xhc_pre_fused_kernel(XhcPreArgs a) {
   __syncthreads();
   if (wave == 0) {
     float* dst = a.part2 + (size_t)ticket * P2;
-    for (int u = lane; u < P2; u += WAVE) st_co(dst + u, (s_red[0][u] + s_red[1][u]) + (s_red[2][u] + s_red[3][u]));
+    for (int u = lane; u < P2; u += WAVE) st_co(dst + u, sum_waves(s_red, u));
     wait_mem();
     if (lane == 0) s_msg = __hip_atomic_fetch_add(cnt2 + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // dense read over all N streams -> sublayer input
+  T* __restrict__ inp = reinterpret_cast<T*>(a.inp);
+#pragma unroll
+  for (int q = 0; q < NKW; ++q) {
+    const int kb = kb0 + q;
+    if (kb < nkbC) {
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float hpi = s_hpre[r][i];
+        float f[VEC];
+        E::unpack(xd[i][q], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = fmaf(hpi, f[e], o[e]);
+      }
+      if (tvalid) st16_nt(inp + (size_t)tok * C + kb * KB + VEC * g, E::packv(o));
+    }
   }
   __syncthreads();
   if (s_msg != G - 1) return;
@@ -429,7 +456,7 @@ __global__ __launch_bounds__(256) void xhc_prep_kernel(const typename E::T* __re
 
 template <class E, int N, int K, int KR>
 static void launch_fused(const Plan& P, const XhcPreArgs& a, hipStream_t st) {
-  xhc_pre_fused_kernel<E, N, K, KR><<<(unsigned)(a.ntiles * a.G), 256, 0, st>>>(a);
+  xhc_pre_fused_kernel<E, N, K, KR><<<(unsigned)(a.ntiles * a.G), NTHR, 0, st>>>(a);
 }
 
 template <class E>
