@@ -65,16 +65,24 @@ __device__ __forceinline__ void st_co(float* p, float v) {
 __device__ __forceinline__ void st_co(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_co(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-coherent buffer loads: the same sc1 cache policy as the atomic loads
+// above, but independent loads are issued back to back (the compiler waits
+// after each atomic load).  A buffer resource (gfx9 V#: base, no stride, byte
+// range) also turns any read past the range into zero instead of a fault.
+constexpr int CP_SC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ int ld_co(const int* p) {
-  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t ld_co64(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)byte_off, 0, CP_SC1));
 }
-__device__ __forceinline__ uint64_t ld_co64(const float* p) {
-  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float ld_co(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)byte_off, 0, CP_SC1));
 }
+__device__ __forceinline__ int ld_co_i(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)byte_off, 0, CP_SC1));
+}
+
 // Wait for all of this wave's outstanding memory operations.
 __device__ __forceinline__ void wait_mem() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -102,12 +110,13 @@ __device__ __forceinline__ void wait_flag(int* flag, int* status) {
 // rather than once per slice.
 __device__ __forceinline__ void sum_slices(const float* __restrict__ src, int G, int stride, int n,
                                            float* __restrict__ dst, int tid) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)((size_t)G * stride * 4));
   for (int u = 2 * tid; u < n; u += 2 * NTHR) {
     float v0 = 0.f, v1 = 0.f;
     for (int s0 = 0; s0 < G; s0 += 16) {
       uint64_t x[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_co64(src + (size_t)(s0 + q) * stride + u) : 0ull;
+      for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_co64(rs, (uint32_t)(((s0 + q) * stride + u) * 4)) : 0ull;
 #pragma unroll
       for (int q = 0; q < 16; ++q)
         if (s0 + q < G) {
@@ -294,13 +303,16 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_fused_kernel(XhcPreArgs a) {
   } else {
     if (wave == 0) {
       if (lane == 0) wait_flag(ready + tile, a.sync + 1);
+      const int rows = a.T - t0 < TM ? a.T - t0 : TM;
+      const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h_pre + (size_t)t0 * N, (uint32_t)(rows * N * 4));
+      const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.idx + (size_t)t0 * K, (uint32_t)(rows * K * 4));
       for (int u = lane; u < TM * N; u += WAVE) {
         const int tau = u / N, t = t0 + tau;
-        s_hpre[tau][u % N] = t < a.T ? ld_co(a.h_pre + (size_t)t * N + u % N) : 0.f;
+        s_hpre[tau][u % N] = t < a.T ? ld_co(rh, (uint32_t)(u * 4)) : 0.f;
       }
       for (int u = lane; u < TM * K; u += WAVE) {
         const int tau = u / K, j = u % K, t = t0 + tau;
-        const int v = t < a.T ? ld_co(a.idx + (size_t)t * K + j) : j;
+        const int v = t < a.T ? ld_co_i(ri, (uint32_t)(u * 4)) : j;
         s_idx[tau][j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
       }
     }
