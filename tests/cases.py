@@ -18,6 +18,7 @@ f64 = synth.as_f64
 # Tolerances: bf16 state with fp32 accumulation, and fp32 mode.
 TOL = {"bf16": 2e-2, "f32": 1e-4}
 MARGIN = 1e-4   # top-k logit margin below which a token is redrawn
+WINDOW = 12     # a token plus the longest conv kernel's 11 lags
 
 
 def rel_err(g, r, floor=1e-2):
@@ -89,6 +90,41 @@ def mhc_inputs(cfg: Config, seed, layer=0):
     X = synth.state(seed, cfg.T, cfg.N, cfg.C, cfg.dtype)
     out = synth.sublayer_out(seed, layer, cfg.B, cfg.S, cfg.C, cfg.dtype)
     return X, out, wd, oracle_weights(wd)
+
+
+# ------------------------------------------------------- sampled full-size
+
+def sample_tokens(B, S, n_random, seed):
+    """Flat token ids: sequence starts, the first conv window, tile (16) and
+    block edges, the middle and the end of every sequence, plus random ones."""
+    rng = np.random.default_rng([seed, 99])
+    fixed = [0, 1, 5, 11, 12, 15, 16, 63, 64, 1023, 1024, S // 2, S - 1]
+    toks = set()
+    for b in range(B):
+        toks.update(b * S + s for s in fixed if s < S)
+        toks.update(b * S + int(s) for s in rng.integers(0, S, n_random))
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def out_window(seed, layer, t, S, C, w):
+    """float64 rows out[t-w+1 .. t] of token t's sequence, zero before its start."""
+    b, s = divmod(int(t), S)
+    lo = max(0, s - w + 1)
+    win = np.zeros((w, C))
+    win[w - (s - lo + 1):] = f64(synth.out_rows(seed, layer, range(b * S + lo, b * S + s + 1), C, "bf16"))
+    return win
+
+
+def oracle_token(cfg, x_t, win, ow):
+    """Oracle sublayer for one token from its state row and output window;
+    returns that token's results and its routing margin."""
+    w = win.shape[0]
+    Xw = np.zeros((w, cfg.N, cfg.C))
+    Xw[-1] = x_t
+    sub = Config(N=cfg.N, k=cfg.k, m=cfg.m, C=cfg.C, B=1, S=w, n_convs=cfg.n_convs, dtype=cfg.dtype)
+    r = oracle_xhc(sub, Xw, win[None], ow)
+    margin = float(O.xhc_topk_margin(r["z"][-1:], cfg.m, cfg.k)[0])
+    return {key: v[-1] for key, v in r.items()}, margin
 
 
 # ------------------------------------------------------------------------ GPU
