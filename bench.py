@@ -98,7 +98,12 @@ def make_inputs(name, kind, cfgs, kinds):
     return X, outs, ws_
 
 
-def run_gpu(name, steps, warmup):
+def default_api(name):
+    kind, _, _, _, _, _, _, kinds = WORKLOADS[name]
+    return "chained" if kind == "xhc" and len(kinds) > 1 else "single"
+
+
+def run_gpu(name, steps, warmup, api):
     import torch
     from stream_residual_mixing_amd import binding
     kind, cfgs, kinds = layer_configs(name)
@@ -108,28 +113,45 @@ def run_gpu(name, steps, warmup):
     T = c0.T
     inp = torch.empty((T, c0.C), dtype=torch.bfloat16, device="cuda")
     mhc = kind == "mhc"
-    ws = lib.workspace(max(cfgs, key=lambda c: lib.workspace_bytes(c, mhc)), mhc)
+    big = max(cfgs, key=lambda c: lib.workspace_bytes(c, mhc))
     stream = torch.cuda.current_stream()
-    pre = lib.mhc_pre if mhc else lib.xhc_pre
-    post = lib.mhc_post if mhc else lib.xhc_post
-    calls = [(f"{'mhc' if mhc else 'xhc'}_pre_{lk}", f"{'mhc' if mhc else 'xhc'}_post_{lk}") for lk in kinds]
+    calls = []   # (name, bytes per token, launch function), in step order
+    b_pre, b_post = bytes_per_token(kind, c0)
+    if api == "chained":
+        wsp = [lib.workspace(big), lib.workspace(big)]
+        calls.append(("xhc_route", c0.N * c0.C * 2, lambda: lib.xhc_route(cfgs[0], weights[0], X, wsp[0], stream)))
+        for l, (cfg, lk) in enumerate(zip(cfgs, kinds)):
+            nx = l + 1 < len(cfgs)
+            cn, wn, wsn = (cfgs[l + 1], weights[l + 1], wsp[(l + 1) % 2]) if nx else (None, None, None)
+            ws = wsp[l % 2]
+            calls.append((f"xhc_pre_chained_{lk}", b_pre,
+                          lambda cfg=cfg, l=l, cn=cn, wn=wn, ws=ws, wsn=wsn:
+                          lib.xhc_pre_chained(cfg, weights[l], cn, wn, X, inp, ws, wsn, stream)))
+            calls.append((f"xhc_post_chained_{lk}", b_post,
+                          lambda cfg=cfg, l=l, cn=cn, wn=wn, ws=ws, wsn=wsn:
+                          lib.xhc_post_chained(cfg, weights[l], cn, wn, X, outs[l], ws, wsn, stream)))
+    else:
+        ws = lib.workspace(big, mhc)
+        pre = lib.mhc_pre if mhc else lib.xhc_pre
+        post = lib.mhc_post if mhc else lib.xhc_post
+        p = "mhc" if mhc else "xhc"
+        for l, (cfg, lk) in enumerate(zip(cfgs, kinds)):
+            calls.append((f"{p}_pre_{lk}", b_pre, lambda cfg=cfg, l=l: pre(cfg, weights[l], X, inp, ws, stream)))
+            calls.append((f"{p}_post_{lk}", b_post, lambda cfg=cfg, l=l: post(cfg, weights[l], X, outs[l], ws, stream)))
 
     def step(evs=None):
-        for l, cfg in enumerate(cfgs):
+        for j, (_, _, fn) in enumerate(calls):
             if evs is not None:
-                evs[l][0].record(stream)
-            pre(cfg, weights[l], X, inp, ws, stream)
-            if evs is not None:
-                evs[l][1].record(stream)
-            post(cfg, weights[l], X, outs[l], ws, stream)
-            if evs is not None:
-                evs[l][2].record(stream)
+                evs[j].record(stream)
+            fn()
+        if evs is not None:
+            evs[len(calls)].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs_all = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in cfgs] for _ in range(steps)]
-    log(f"timing {steps} steps of {len(cfgs)} layers ({name})")
+    evs_all = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    log(f"timing {steps} steps of {len(cfgs)} layers ({name}, {api} calls)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
@@ -139,11 +161,11 @@ def run_gpu(name, steps, warmup):
 
     per_call = {}
     for s in range(steps):
-        for l in range(len(cfgs)):
-            e = evs_all[s][l]
-            for j, (a, b) in enumerate(((e[0], e[1]), (e[1], e[2]))):
-                per_call.setdefault(calls[l][j], []).append(a.elapsed_time(b) * 1e-3)
-    return dict(kind=kind, cfgs=cfgs, kinds=kinds, elapsed=elapsed, per_call=per_call, T=T)
+        e = evs_all[s]
+        for j, (cname, _, _) in enumerate(calls):
+            per_call.setdefault(cname, []).append(e[j].elapsed_time(e[j + 1]) * 1e-3)
+    call_bytes = {cname: bpt * T for cname, bpt, _ in calls}
+    return dict(kind=kind, cfgs=cfgs, kinds=kinds, elapsed=elapsed, per_call=per_call, T=T, call_bytes=call_bytes)
 
 
 def cpu_baseline(name, tokens=256):
@@ -215,6 +237,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
+    ap.add_argument("--api", choices=("chained", "single"), default=None,
+                    help="xHC calls: chained (routing of layer l+1 prepared during layer l; default for "
+                         "multi-layer workloads) or single (xhc_pre / xhc_post per layer)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the layer has no multi-GPU path in this library "
@@ -228,20 +253,18 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    r = run_gpu(args.workload, args.steps, args.warmup)
+    api = args.api or default_api(args.workload)
+    r = run_gpu(args.workload, args.steps, args.warmup, api)
     kind, cfgs, kinds, T = r["kind"], r["cfgs"], r["kinds"], r["T"]
     L = len(cfgs)
     ms_per_step = r["elapsed"] / args.steps * 1e3
     value = T * L * args.steps / r["elapsed"]
-    # algorithmic bytes
+    # algorithmic bytes: the method's byte model, whatever the calls move
     step_bytes = 0
-    call_bytes = {}
     for cfg, lk in zip(cfgs, kinds):
         b_pre, b_post = bytes_per_token(kind, cfg)
         step_bytes += T * (b_pre + b_post)
-        p = "mhc" if kind == "mhc" else "xhc"
-        call_bytes[f"{p}_pre_{lk}"] = T * b_pre
-        call_bytes[f"{p}_post_{lk}"] = T * b_post
+    call_bytes = r["call_bytes"]
     hbm_gbps = step_bytes * args.steps / r["elapsed"] / 1e9
     calls = {}
     for name, ts in r["per_call"].items():
@@ -269,7 +292,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "kind": kind, "N": c0.N, "k": c0.k if kind == "xhc" else c0.N,
+        "config": {"workload": args.workload, "kind": kind, "api": api, "N": c0.N, "k": c0.k if kind == "xhc" else c0.N,
                    "m": c0.m, "C": c0.C, "batch": c0.B, "seq": c0.S, "tokens": T, "layers": kinds,
                    "sinkhorn_iters": c0.iters},
         "hbm": {"GBps": round(hbm_gbps, 1), "frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),

@@ -160,6 +160,52 @@ xhc_status mhc_pre(const xhc_config* cfg, const xhc_weights* w,
 xhc_status mhc_post(const xhc_config* cfg, const xhc_weights* w,
                     void* X, const void* out, void* ws, xhc_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * xHC sublayers in a chain.  The mapping generation of a sublayer is a linear
+ * contraction of vec X, and a sublayer changes only its k active rows, so the
+ * routing of sublayer l+1 (router logits, active set, router weights, H_pre)
+ * can be accumulated while sublayer l runs: the rows sublayer l leaves alone
+ * are contracted while xhc_pre_chained reads the state anyway, the k
+ * rewritten rows after xhc_post_chained has written them.  Results are those
+ * of xhc_pre / xhc_post up to rounding order (xHC paper "xHC: Expanded
+ * Hyper-Connections", paragraphs "Mapping generation" and "Mapping
+ * application"; explainer "xHC: sixteen residual streams, four written at a
+ * time", section "What xHC changes").
+ *
+ * Use, for sublayers 0..L-1 with configs cfg[l], weights w[l] and two
+ * workspaces used in turn (ws[l % 2], each xhc_workspace_bytes(cfg[l]) large
+ * for the layer it serves):
+ *
+ *   xhc_route(cfg[0], w[0], X, ws[0])
+ *   for l: xhc_pre_chained (cfg[l], w[l], cfg[l+1], w[l+1], X, inp, ws[l%2], ws[(l+1)%2])
+ *          F
+ *          xhc_post_chained(cfg[l], w[l], cfg[l+1], w[l+1], X, out, ws[l%2], ws[(l+1)%2])
+ *
+ * with cfg_next, w_next and ws_next NULL for the last sublayer.  cfg and
+ * cfg_next must agree in N, k, m, C, batch, seq and dtype (n_convs may
+ * differ).  The public arrays of a workspace after its layer's
+ * xhc_pre_chained are those xhc_pre writes (status stays 0).
+ * ------------------------------------------------------------------------- */
+
+/* Routing of the state X for the sublayer (cfg, w): router logits, active set
+ * and router weights, H_pre, into ws.  X: [T][N][C] (read only). */
+xhc_status xhc_route(const xhc_config* cfg, const xhc_weights* w, const void* X, void* ws, xhc_stream_t stream);
+
+/* xhc_pre for a sublayer whose routing is already in ws (from xhc_route or
+ * the previous sublayer's xhc_post_chained): inp, H_res and H_post.  With a
+ * next sublayer, also its partial routing over the rows this sublayer does
+ * not write, into ws_next.  X is read once. */
+xhc_status xhc_pre_chained(const xhc_config* cfg, const xhc_weights* w, const xhc_config* cfg_next,
+                           const xhc_weights* w_next, const void* X, void* inp, void* ws, void* ws_next,
+                           xhc_stream_t stream);
+
+/* xhc_post, then (with a next sublayer) the rewritten rows' share of the
+ * next sublayer's routing and that routing itself, into ws_next (the
+ * workspace given to this sublayer's xhc_pre_chained as ws_next). */
+xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const xhc_config* cfg_next,
+                            const xhc_weights* w_next, void* X, const void* out, void* ws, void* ws_next,
+                            xhc_stream_t stream);
+
 /* Message for the last non-OK status returned on this host thread. */
 const char* xhc_last_error(void);
 

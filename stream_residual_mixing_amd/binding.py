@@ -25,7 +25,8 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 # Exported symbols, in the order include/xhc.h declares them.
 EXPORTS = (
     "xhc_workspace_bytes", "mhc_workspace_bytes", "xhc_workspace_layout", "mhc_workspace_layout",
-    "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_last_error",
+    "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_route", "xhc_pre_chained", "xhc_post_chained",
+    "xhc_last_error",
 )
 
 
@@ -160,6 +161,14 @@ class Lib:
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        d.xhc_route.restype = ctypes.c_int
+        d.xhc_route.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p]
+        for fn in (d.xhc_pre_chained, d.xhc_post_chained):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.POINTER(XhcConfig),
+                           ctypes.POINTER(XhcWeights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                           ctypes.c_void_p, ctypes.c_void_p]
         d.xhc_last_error.restype = ctypes.c_char_p
         d.xhc_last_error.argtypes = []
 
@@ -238,6 +247,45 @@ class Lib:
         c, cw = cfg.c(), w.c()
         self._ok(self.dll.xhc_post(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
                                    ws.data_ptr(), _stream_ptr(stream)))
+
+    # chained sublayers: routing of sublayer l+1 prepared while sublayer l runs
+    def xhc_route(self, cfg: Config, w: Weights, X, ws, stream=None):
+        _check(X, "X", (cfg.T, cfg.N, cfg.C), cfg.torch_dtype)
+        _check(w.w_full, "w_full", (cfg.N * cfg.C, 2 * cfg.N), cfg.torch_dtype)
+        _check(w.b_pre, "b_pre", (cfg.N,), torch.float32)
+        self._check_ws(cfg, ws)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_route(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), ws.data_ptr(),
+                                    _stream_ptr(stream)))
+
+    def _check_ws(self, cfg, ws):
+        need = self.workspace_bytes(cfg)
+        if ws is None or not ws.is_cuda or ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace must be a GPU tensor of at least {need} bytes")
+
+    def _next(self, cfg_next, w_next, ws_next):
+        if cfg_next is None:
+            return None, None, 0
+        _check(w_next.w_full, "w_next.w_full", (cfg_next.N * cfg_next.C, 2 * cfg_next.N), cfg_next.torch_dtype)
+        _check(w_next.b_pre, "w_next.b_pre", (cfg_next.N,), torch.float32)
+        self._check_ws(cfg_next, ws_next)
+        return ctypes.byref(cfg_next.c()), ctypes.byref(w_next.c()), ws_next.data_ptr()
+
+    def xhc_pre_chained(self, cfg: Config, w: Weights, cfg_next, w_next, X, inp, ws, ws_next, stream=None):
+        self._check_common(cfg, w, X, ws, False, True)
+        _check(inp, "inp", (cfg.T, cfg.C), cfg.torch_dtype)
+        cn, wn, wsn = self._next(cfg_next, w_next, ws_next)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_pre_chained(ctypes.byref(c), ctypes.byref(cw), cn, wn, X.data_ptr(), inp.data_ptr(),
+                                          ws.data_ptr(), wsn, _stream_ptr(stream)))
+
+    def xhc_post_chained(self, cfg: Config, w: Weights, cfg_next, w_next, X, out, ws, ws_next, stream=None):
+        self._check_common(cfg, w, X, ws, False, False)
+        _check_out(out, cfg)
+        cn, wn, wsn = self._next(cfg_next, w_next, ws_next)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_post_chained(ctypes.byref(c), ctypes.byref(cw), cn, wn, X.data_ptr(), out.data_ptr(),
+                                           ws.data_ptr(), wsn, _stream_ptr(stream)))
 
     def mhc_pre(self, cfg: Config, w: Weights, X, inp, ws, stream=None):
         self._check_common(cfg, w, X, ws, True, True)

@@ -145,6 +145,7 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     q.o_part = take((size_t)q.ntiles * q.G * P1 * 4);
     q.o_part2 = take((size_t)q.ntiles * q.G * P2 * 4);
     q.o_gram = take((size_t)q.nslices * T * 10 * 4);
+    q.o_corr = take((size_t)q.ntiles * q.G * P1 * 4);
   }
   q.total = q.T == 0 ? 0 : off;
   *P = q;
@@ -227,6 +228,27 @@ xhc_status post_common(const xhc_config* cfg, const xhc_weights* w, void* X, con
   return finish(st);
 }
 
+// Plan of the next sublayer of a chain, checked against this one.
+xhc_status next_plan(const xhc::Plan& P, const xhc_config* cfg_next, xhc::Plan* Pn) {
+  xhc_status s = make_plan(cfg_next, false, Pn);
+  if (s != XHC_OK) return s;
+  if (Pn->N != P.N || Pn->K != P.K || Pn->m != P.m || Pn->C != P.C || Pn->B != P.B || Pn->S != P.S ||
+      Pn->dtype != P.dtype)
+    return fail(XHC_ERR_INVALID_ARG, "next sublayer must agree in n_streams, k_active, m_fixed, channels, batch, "
+                                     "seq and dtype");
+  return XHC_OK;
+}
+
+xhc_status check_state_ws(const void* X, const void* io, const void* ws, const void* ws_next, bool chained) {
+  if (!X || !io || !ws) return fail(XHC_ERR_INVALID_ARG, "X, inp/out and ws must not be NULL");
+  if (!aligned16(X) || !aligned16(io) || !aligned16(ws) || (ws_next && !aligned16(ws_next)))
+    return fail(XHC_ERR_INVALID_ARG, "X, inp/out and workspaces must be 16-byte aligned");
+  if (X == io || X == ws || io == ws) return fail(XHC_ERR_INVALID_ARG, "X, inp/out and ws must not alias");
+  if (chained && (ws_next == ws || ws_next == X || ws_next == io))
+    return fail(XHC_ERR_INVALID_ARG, "ws_next must be a workspace of its own");
+  return XHC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,6 +293,71 @@ xhc_status mhc_pre(const xhc_config* cfg, const xhc_weights* w, const void* X, v
 xhc_status mhc_post(const xhc_config* cfg, const xhc_weights* w, void* X, const void* out, void* ws,
                     xhc_stream_t stream) {
   return post_common(cfg, w, X, out, ws, stream, true);
+}
+
+xhc_status xhc_route(const xhc_config* cfg, const xhc_weights* w, const void* X, void* ws, xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if (!w) return fail(XHC_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->w_full || !aligned16(w->w_full)) return fail(XHC_ERR_INVALID_ARG, "w_full must be a 16-byte aligned pointer");
+  if (!w->b_pre) return fail(XHC_ERR_INVALID_ARG, "b_pre must not be NULL");
+  if (!std::isfinite(w->alpha_pre)) return fail(XHC_ERR_INVALID_ARG, "alpha scales must be finite");
+  if (P.T == 0) return XHC_OK;
+  if (!X || !ws) return fail(XHC_ERR_INVALID_ARG, "X and ws must not be NULL");
+  if (!aligned16(X) || !aligned16(ws)) return fail(XHC_ERR_INVALID_ARG, "X and ws must be 16-byte aligned");
+  if (X == ws) return fail(XHC_ERR_INVALID_ARG, "X and ws must not alias");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_route(P, X, w, static_cast<char*>(ws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status xhc_pre_chained(const xhc_config* cfg, const xhc_weights* w, const xhc_config* cfg_next,
+                           const xhc_weights* w_next, const void* X, void* inp, void* ws, void* ws_next,
+                           xhc_stream_t stream) {
+  xhc::Plan P, Pn;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_weights(P, w, true)) != XHC_OK) return s;
+  const bool chained = cfg_next != nullptr;
+  if (chained) {
+    if ((s = next_plan(P, cfg_next, &Pn)) != XHC_OK) return s;
+    if (!w_next || !w_next->w_full || !aligned16(w_next->w_full))
+      return fail(XHC_ERR_INVALID_ARG, "w_next->w_full must be a 16-byte aligned pointer");
+    if (!ws_next) return fail(XHC_ERR_INVALID_ARG, "ws_next must not be NULL with a next sublayer");
+  }
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, inp, ws, chained ? ws_next : nullptr, chained)) != XHC_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_pre_chained(P, w, chained ? &Pn : nullptr, w_next, X, inp, static_cast<char*>(ws),
+                                   static_cast<char*>(ws_next), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const xhc_config* cfg_next,
+                            const xhc_weights* w_next, void* X, const void* out, void* ws, void* ws_next,
+                            xhc_stream_t stream) {
+  xhc::Plan P, Pn;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_weights(P, w, false)) != XHC_OK) return s;
+  const bool chained = cfg_next != nullptr;
+  if (chained) {
+    if ((s = next_plan(P, cfg_next, &Pn)) != XHC_OK) return s;
+    if (!w_next || !w_next->b_pre || !std::isfinite(w_next->alpha_pre))
+      return fail(XHC_ERR_INVALID_ARG, "w_next needs b_pre and a finite alpha_pre");
+    if (!ws_next) return fail(XHC_ERR_INVALID_ARG, "ws_next must not be NULL with a next sublayer");
+  }
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, out, ws, chained ? ws_next : nullptr, chained)) != XHC_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_post(P, X, out, w, static_cast<char*>(ws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  if (chained && !xhc::launch_xhc_chain_tail(P, Pn, w_next, X, static_cast<char*>(ws), static_cast<char*>(ws_next), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
 }
 
 const char* xhc_last_error(void) { return g_err.c_str(); }

@@ -1,0 +1,755 @@
+// xHC sublayers in a chain, with each layer's routing prepared ahead (gfx950).
+//
+// A sublayer's mapping generation contracts the whole flattened state of a
+// token (xHC paper "xHC: Expanded Hyper-Connections", paragraph "Mapping
+// generation"), and the dense read of that same state needs its result
+// (paragraph "Mapping application").  Done inside one sublayer, that costs
+// either a second read of the state or a wait across workgroups while the
+// state is held on chip.  In a chain of sublayers the contraction can be done
+// earlier and exactly, because it is linear in the state and the state only
+// changes in the k rows a sublayer writes (explainer "xHC: sixteen residual
+// streams, four written at a time", section "What xHC changes"):
+//
+//   vec X_{l+1} . W = sum over the rows i not in I_l of x_i . W_i
+//                   + sum over the rows i in I_l of x'_i . W_i,
+//
+// and likewise the sums of x and x^2 behind LayerNorm and RMSNorm.  So
+//
+//   xhc_pre_chained (layer l)  reads X_l once: dense read with the routing
+//       already in the workspace, gather + partial active projection of
+//       layer l, and the partial routing projection of layer l+1 over the
+//       rows that layer l leaves untouched (its own rows masked to zero);
+//   act_fin                    sums the active partials: Sinkhorn + row clamp
+//       and H_post of layer l;
+//   (the sublayer F, then the usual post kernels of layer l)
+//   corr                       reads the k rewritten rows and adds their
+//       routing projection for layer l+1;
+//   route_fin                  sums both partials: router logits, H_pre, the
+//       active list and router weights of layer l+1.
+//
+// The first layer of a chain gets its routing from one projection pass over
+// its state (xhc_route).  No workgroup ever waits for another: partial
+// results cross launch boundaries only, and every sum runs in a fixed order.
+#include <type_traits>
+
+#include "xhc_internal.hpp"
+#include "xhc_tile.hpp"
+
+namespace xhc {
+
+namespace {
+
+constexpr int NTHR = TNTHR;
+constexpr int WD = 4;   // items of weight fragments in flight ahead of the MFMAs
+#ifndef XHC_PRE_WD
+#define XHC_PRE_WD 2
+#endif
+constexpr int WDP = XHC_PRE_WD;   // the same for the chained pre kernel (holds more)
+#ifndef XHC_CORR_WD
+#define XHC_CORR_WD 2
+#endif
+constexpr int WDC = XHC_CORR_WD;  // and for the correction kernel
+
+template <int N>
+struct RouteDims {
+  static constexpr int NTF = (2 * N + 15) / 16;  // 16-column MFMA tiles of [W_r | W_pre]
+  static constexpr int NPF = NTF * 16;
+  static constexpr int NSUM = TM * NPF + 2 * TM;  // projection + (sum x, sum x^2) per token
+  static constexpr int P1 = NSUM + 16;            // + column sums of W_r
+};
+
+template <int K, int KR>
+struct ActDims {
+  static constexpr int NA = K * K + K * KR;
+  static constexpr int NTA = (NA + 15) / 16;
+  static constexpr int NPA = NTA * 16;
+  static constexpr int P2 = TM * NPA + TM;  // projection + sum of squares per token
+};
+
+// Running sum of x and of x^2 over one fragment, in float.  (The packed bf16
+// dot product would do this in half the instructions, but in back-to-back
+// accumulation chains like these it returned wrong sums on gfx950, so it is
+// not used.)
+template <class E>
+__device__ __forceinline__ void add_stats(const u32x4_t& v, float& s1, float& s2) {
+  float f[E::VEC];
+  E::unpack(v, f);
+#pragma unroll
+  for (int e = 0; e < E::VEC; ++e) {
+    s1 += f[e];
+    s2 = fmaf(f[e], f[e], s2);
+  }
+}
+
+// Column-0..15 accumulators of one wave to LDS rows of a partial: element
+// (token 4 g + i, column n 16 + r) of the MFMA result.
+template <int NT, int NP, int PM>
+__device__ __forceinline__ void acc_to_lds(float (&dst)[TWV][PM], int wave, int g, int r, const f32x4_t (&acc)[NT]) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[wave][(4 * g + i) * NP + n * 16 + r] = acc[n][i];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Routing projection of a whole state (first layer of a chain): per 16-token
+// tile and channel slice, vec X . [W_r | W_pre], sum x, sum x^2 and the column
+// sums of W_r, over this slice's channels of all N streams.
+// ---------------------------------------------------------------------------
+struct ProjArgs {
+  const void* X;
+  int T, C, G;
+  const uint4* wfull;
+  float* part;
+};
+
+template <class E, int N>
+__global__ __launch_bounds__(NTHR, 4) void xhc_proj_kernel(ProjArgs a) {
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, P1 = D::P1;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  __shared__ float s_red[TWV][P1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int tile = blockIdx.x / G, slice = blockIdx.x % G;
+  const int t0 = tile * TM;
+  const int rows = a.T - t0 < TM ? a.T - t0 : TM;
+  const int kb0 = slice * TWV + wave;
+  const bool kvalid = kb0 < nkbC;
+
+  const __amdgpu_buffer_rsrc_t rwf = make_rsrc(a.wfull, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
+  const uint32_t vwf = kvalid ? (uint32_t)(((size_t)kb0 * NTF * WAVE + lane) * 16) : OUT_OF_RANGE;
+  const uint32_t wf_stream = (uint32_t)nkbC * NTF * WAVE * 16;
+  u32x4_t wb[WD][NTF];
+#pragma unroll
+  for (int d = 0; d < WD && d < N; ++d)
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) wb[d][n] = ld_b128(rwf, vwf + n * WAVE * 16, d * wf_stream);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(reinterpret_cast<const T*>(a.X) + (size_t)t0 * N * C, (uint32_t)((size_t)rows * N * C * sizeof(T)));
+  const uint32_t vx = kvalid ? (uint32_t)(((size_t)r * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
+  u32x4_t xd[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) xd[i] = ld_b128<CP_NT>(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4_t acc[NTF];
+#pragma unroll
+  for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float s1 = 0.f, s2 = 0.f;
+  const u32x4_t ones = ones_frag<E>();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    add_stats<E>(xd[i], s1, s2);
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], xd[i], wb[i % WD][n]);
+    acs = E::mma(acs, ones, wb[i % WD][0]);
+    if (i + WD < N) {
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) wb[i % WD][n] = ld_b128(rwf, vwf + n * WAVE * 16, (i + WD) * wf_stream);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  s1 += __shfl_xor(s1, 16, WAVE);
+  s1 += __shfl_xor(s1, 32, WAVE);
+  s2 += __shfl_xor(s2, 16, WAVE);
+  s2 += __shfl_xor(s2, 32, WAVE);
+  acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
+  if (g == 0) {
+    s_red[wave][TM * NPF + 2 * r] = s1;
+    s_red[wave][TM * NPF + 2 * r + 1] = s2;
+    s_red[wave][TM * NPF + 2 * TM + r] = acs[0];
+  }
+  __syncthreads();
+  float* dst = a.part + (size_t)blockIdx.x * P1;
+  for (int u = tid; u < P1; u += NTHR) dst[u] = sum_waves(s_red, u);
+}
+
+// ---------------------------------------------------------------------------
+// Routing of a tile from the summed partials: the G routing partials of the
+// state (or of its untouched rows), plus, when given, the G partials of the
+// rewritten rows; router logits, H_pre, active list and router weights.
+// ---------------------------------------------------------------------------
+struct RouteFinArgs {
+  int T, C, m, G;
+  const float* part;
+  const float* corr;   // may be null
+  const float* b_pre;
+  float a_pre, eps;
+  int* idx;
+  float *p, *h_pre, *z;
+};
+
+template <int N, int K>
+__global__ __launch_bounds__(256) void xhc_route_fin_kernel(RouteFinArgs a) {
+  using D = RouteDims<N>;
+  constexpr int NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  __shared__ float s_sum[P1];
+  __shared__ float s_z[TM][N];
+  __shared__ float s_hpre[TM][N];
+  const int tid = threadIdx.x, G = a.G;
+  const int tile = blockIdx.x, t0 = tile * TM;
+
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part + (size_t)tile * G * P1, (uint32_t)((size_t)G * P1 * 4));
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(a.corr ? a.corr + (size_t)tile * G * P1 : a.part, a.corr ? (uint32_t)((size_t)G * P1 * 4) : 0u);
+  for (int u = 2 * tid; u < P1; u += 2 * 256) {
+    float v0 = 0.f, v1 = 0.f;
+    for (int s0 = 0; s0 < G; s0 += 16) {
+      uint64_t x[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_b64(rp, (uint32_t)(((s0 + q) * P1 + u) * 4)) : 0ull;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (s0 + q < G) {
+          v0 += __uint_as_float((uint32_t)x[q]);
+          v1 += __uint_as_float((uint32_t)(x[q] >> 32));
+        }
+    }
+    if (a.corr && u < NSUM) {
+      for (int s0 = 0; s0 < G; s0 += 16) {
+        uint64_t x[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_b64(rc, (uint32_t)(((s0 + q) * P1 + u) * 4)) : 0ull;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (s0 + q < G) {
+            v0 += __uint_as_float((uint32_t)x[q]);
+            v1 += __uint_as_float((uint32_t)(x[q] >> 32));
+          }
+      }
+    }
+    s_sum[u] = v0;
+    s_sum[u + 1] = v1;
+  }
+  __syncthreads();
+  const float n_el = (float)N * (float)a.C;
+  for (int u = tid; u < TM * N; u += 256) {
+    const int tau = u / N, i = u % N;
+    route_logits(s_sum[tau * NPF + i], s_sum[tau * NPF + N + i], s_sum[TM * NPF + 2 * tau],
+                 s_sum[TM * NPF + 2 * tau + 1], s_sum[NSUM + i], n_el, a.eps, a.a_pre, a.b_pre[i], t0 + tau < a.T,
+                 &s_z[tau][i], &s_hpre[tau][i]);
+  }
+  __syncthreads();
+  for (int u = tid; u < TM * N; u += 256) {
+    const int tau = u / N, i = u % N, t = t0 + tau;
+    if (t < a.T) {
+      a.z[(size_t)t * N + i] = s_z[tau][i];
+      a.h_pre[(size_t)t * N + i] = s_hpre[tau][i];
+    }
+  }
+  if (tid < TM && t0 + tid < a.T) {
+    const int t = t0 + tid;
+    float zt[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) zt[i] = s_z[tid][i];
+    int sel[K];
+    route_select<N, K>(zt, a.m, sel);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a.idx[(size_t)t * K + j] = sel[j];
+      a.p[(size_t)t * K + j] = j < a.m ? 1.f : sigmoidf_(zt[sel[j]]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pre-application of a layer whose routing is in the workspace: dense read,
+// gather + partial active projection, and (LOOK) the next layer's partial
+// routing projection over the rows this layer does not write.
+// ---------------------------------------------------------------------------
+struct PreChainArgs {
+  const void* X;
+  void* inp;
+  int T, C, G, m;
+  const uint4* wact;   // this layer's packed [W_res | W_post]
+  const uint4* wnext;  // next layer's packed [W_r | W_pre] (LOOK)
+  const int* idx;
+  const float* h_pre;
+  float* part2;        // active partials [ntiles][G][P2]
+  float* look;         // next layer's routing partials [ntiles][G][P1] (LOOK)
+};
+
+template <class E, int N, int K, int KR, bool LOOK>
+__global__ __launch_bounds__(NTHR, 4) void xhc_pre_chained_kernel(PreChainArgs a) {
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  using A = ActDims<K, KR>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, P1 = D::P1;
+  constexpr int NTA = A::NTA, NPA = A::NPA, P2 = A::P2;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  // Weight items in order of use: N streams of the next layer's routing
+  // weights (LOOK), then the K positions of this layer's active weights.
+  constexpr int NL = LOOK ? N : 0;
+  constexpr int NI = NL + K;
+  constexpr int NTR = NTF > NTA ? NTF : NTA;
+  __shared__ float s_red2[TWV][P2];
+  __shared__ float s_red1[LOOK ? TWV : 1][LOOK ? P1 : 2];
+  __shared__ float s_hpre[TM][N];
+  __shared__ int s_idx[TM][K];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int tile = blockIdx.x / G, slice = blockIdx.x % G;
+  const int t0 = tile * TM;
+  const int rows = a.T - t0 < TM ? a.T - t0 : TM;
+  const int tok = t0 + r;
+  const bool tvalid = r < rows;
+  const int kb0 = slice * TWV + wave;
+  const bool kvalid = kb0 < nkbC;
+
+  // routing of the tile (written by an earlier launch)
+  if (tid < TM * N) {
+    const int tau = tid / N;
+    s_hpre[tau][tid % N] = tau < rows ? a.h_pre[(size_t)t0 * N + tid] : 0.f;
+  } else if (tid >= 256 && tid < 256 + TM * K) {
+    const int u = tid - 256, tau = u / K, j = u % K;
+    const int v = tau < rows ? a.idx[(size_t)t0 * K + u] : j;
+    s_idx[tau][j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
+  }
+
+  const __amdgpu_buffer_rsrc_t rwf =
+      make_rsrc(LOOK ? (const void*)a.wnext : (const void*)a.wact, LOOK ? (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16) : 0u);
+  const uint32_t vwf = kvalid ? (uint32_t)(((size_t)kb0 * NTF * WAVE + lane) * 16) : OUT_OF_RANGE;
+  const uint32_t wf_stream = (uint32_t)nkbC * NTF * WAVE * 16;
+  const __amdgpu_buffer_rsrc_t rwa = make_rsrc(a.wact, (uint32_t)((size_t)K * nkbC * NTA * WAVE * 16));
+  const uint32_t vwa = kvalid ? (uint32_t)(((size_t)kb0 * NTA * WAVE + lane) * 16) : OUT_OF_RANGE;
+  const uint32_t wa_pos = (uint32_t)nkbC * NTA * WAVE * 16;
+  u32x4_t wb[WDP][NTR];
+  auto fetch = [&](int q) {
+    if (q < NL) {
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) wb[q % WDP][n] = ld_b128(rwf, vwf + n * WAVE * 16, q * wf_stream);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NTA; ++n) wb[q % WDP][n] = ld_b128(rwa, vwa + n * WAVE * 16, (q - NL) * wa_pos);
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < WDP && q < NI; ++q) fetch(q);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(reinterpret_cast<const T*>(a.X) + (size_t)t0 * N * C, (uint32_t)((size_t)rows * N * C * sizeof(T)));
+  const uint32_t vx = kvalid ? (uint32_t)(((size_t)r * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
+  u32x4_t xd[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) xd[i] = ld_b128<CP_NT>(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+
+  int I[K];
+  uint32_t amask = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    I[j] = s_idx[r][j];
+    amask |= 1u << I[j];
+  }
+
+  // dense read over all N streams -> sublayer input
+  if (kvalid) {
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float hpi = s_hpre[r][i];
+      float f[VEC];
+      E::unpack(xd[i], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = fmaf(hpi, f[e], o[e]);
+    }
+    if (tvalid) st16_nt(reinterpret_cast<T*>(a.inp) + (size_t)tok * C + kb0 * KB + VEC * g, E::packv(o));
+  }
+
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  if constexpr (LOOK) {
+    // next layer's routing projection over the rows this layer leaves as they are
+    f32x4_t acc[NTF];
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float s1 = 0.f, s2 = 0.f;
+    const u32x4_t ones = ones_frag<E>();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const u32x4_t v = ((amask >> i) & 1u) ? zero : xd[i];
+      add_stats<E>(v, s1, s2);
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, wb[i % WDP][n]);
+      acs = E::mma(acs, ones, wb[i % WDP][0]);
+      if (i + WDP < NI) fetch(i + WDP);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s1 += __shfl_xor(s1, 16, WAVE);
+    s1 += __shfl_xor(s1, 32, WAVE);
+    s2 += __shfl_xor(s2, 16, WAVE);
+    s2 += __shfl_xor(s2, 32, WAVE);
+    acc_to_lds<NTF, NPF>(s_red1, wave, g, r, acc);
+    if (g == 0) {
+      s_red1[wave][TM * NPF + 2 * r] = s1;
+      s_red1[wave][TM * NPF + 2 * r + 1] = s2;
+      s_red1[wave][TM * NPF + 2 * TM + r] = acs[0];
+    }
+  }
+
+  // gather of the k active rows, their sum of squares and active projection
+  f32x4_t acc2[NTA];
+#pragma unroll
+  for (int n = 0; n < NTA; ++n) acc2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  float ss1 = 0.f;   // (sum of x over the active rows; not needed)
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    constexpr int Q0 = NL;
+    // position j < m holds stream j; a routed position holds one of m..N-1
+    u32x4_t v = xd[j < N ? j : 0];
+    if (j >= a.m) {
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (i != j) v = (I[j] == i) ? xd[i] : v;
+    }
+    add_stats<E>(v, ss1, ss);
+#pragma unroll
+    for (int n = 0; n < NTA; ++n) acc2[n] = E::mma(acc2[n], v, wb[(Q0 + j) % WDP][n]);
+    if (Q0 + j + WDP < NI) fetch(Q0 + j + WDP);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  ss += __shfl_xor(ss, 16, WAVE);
+  ss += __shfl_xor(ss, 32, WAVE);
+  acc_to_lds<NTA, NPA>(s_red2, wave, g, r, acc2);
+  if (g == 0) s_red2[wave][TM * NPA + r] = ss;
+  __syncthreads();
+  float* d2 = a.part2 + (size_t)blockIdx.x * P2;
+  for (int u = tid; u < P2; u += NTHR) d2[u] = sum_waves(s_red2, u);
+  if constexpr (LOOK) {
+    float* d1 = a.look + (size_t)blockIdx.x * P1;
+    for (int u = tid; u < P1; u += NTHR) d1[u] = sum_waves(s_red1, u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Active maps of a tile from the summed active partials: RMSNorm of the
+// gathered rows, k x k Sinkhorn + row clamp, and H_post.  One wave per tile.
+// ---------------------------------------------------------------------------
+struct ActFinArgs {
+  int T, C, G, ntiles;
+  const float* part2;
+  const float *b_res, *b_post;
+  float a_res, a_post, eps;
+  int iters;
+  float *h_res, *h_post;
+};
+
+template <int K, int KR>
+__global__ __launch_bounds__(256) void xhc_act_fin_kernel(ActFinArgs a) {
+  using A = ActDims<K, KR>;
+  constexpr int NPA = A::NPA, P2 = A::P2;
+  __shared__ float s_sum[4][P2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x * 4 + wave;
+  const bool live = tile < a.ntiles;
+  const int G = a.G, t0 = tile * TM;
+  if (live) sum_slices<WAVE, 0>(a.part2 + (size_t)tile * G * P2, G, P2, P2, &s_sum[wave][0], lane);
+  __syncthreads();
+  if (!live) return;
+  const float* sm = &s_sum[wave][0];
+  constexpr int TPP = WAVE / K;
+  constexpr int PASSES = (TM + TPP - 1) / TPP;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int tau = pass * TPP + lane / K;
+    const int row = lane % K;
+    const int t = t0 + tau;
+    const bool valid = tau < TM && t < a.T;
+    const int tq = tau < TM ? tau : 0;
+    const float rr = 1.f / sqrtf(sm[TM * NPA + tq] / ((float)K * (float)a.C) + a.eps);
+    float L[K];
+#pragma unroll
+    for (int b = 0; b < K; ++b) {
+      const int col = row * K + b;
+      L[b] = fmaf(a.a_res * sm[tq * NPA + col], rr, a.b_res[col]);
+    }
+    sinkhorn_rows<K>(L, a.iters);
+    float rs = 0.f;
+#pragma unroll
+    for (int b = 0; b < K; ++b) rs += L[b];
+    const float d = fmaxf(rs, 1.f);
+#pragma unroll
+    for (int b = 0; b < K; ++b) L[b] = L[b] / d;
+    if (valid) {
+#pragma unroll
+      for (int b = 0; b < K; ++b) a.h_res[((size_t)t * K + row) * K + b] = L[b];
+#pragma unroll
+      for (int q = 0; q < KR; ++q) {
+        const int col = K * K + row * KR + q;
+        a.h_post[((size_t)t * K + row) * KR + q] =
+            2.f * sigmoidf_(fmaf(a.a_post * sm[tq * NPA + col], rr, a.b_post[row * KR + q]));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The rewritten rows' share of the next layer's routing: per RB x 16 tokens
+// and channel slice, sum over the k active rows i of x'_i . W_i (the next
+// layer's [W_r | W_pre] rows of stream i), sum x' and sum x'^2.  Rows are
+// read with the active list of the layer that wrote them; each stream's MFMA
+// takes, per token, the active row that sits in that stream (or zero).
+// ---------------------------------------------------------------------------
+struct CorrArgs {
+  const void* X;
+  int T, C, G, ntiles, m;
+  const int* idx;
+  const uint4* wnext;
+  float* corr;   // [ntiles][G][P1] (the first NSUM entries of each)
+};
+
+template <class E, int N, int K, int RB>
+__global__ __launch_bounds__(NTHR, 2) void xhc_corr_kernel(CorrArgs a) {
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  constexpr int TB = TM * RB;   // tokens per block
+  __shared__ int s_idx[TB][K];
+  __shared__ float s_red[TWV][NSUM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int blk = blockIdx.x / G, slice = blockIdx.x % G;
+  const int t0 = blk * TB;
+  const int rows = a.T - t0 < TB ? a.T - t0 : TB;
+  const int kb0 = slice * TWV + wave;
+  const bool kvalid = kb0 < nkbC;
+
+  for (int u = tid; u < TB * K; u += NTHR) {
+    const int tau = u / K, j = u % K;
+    const int v = tau < rows ? a.idx[(size_t)t0 * K + u] : j;
+    s_idx[tau][j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
+  }
+
+  const __amdgpu_buffer_rsrc_t rwf = make_rsrc(a.wnext, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
+  const uint32_t vwf = kvalid ? (uint32_t)(((size_t)kb0 * NTF * WAVE + lane) * 16) : OUT_OF_RANGE;
+  const uint32_t wf_stream = (uint32_t)nkbC * NTF * WAVE * 16;
+  u32x4_t wb[WDC][NTF];
+#pragma unroll
+  for (int d = 0; d < WDC && d < N; ++d)
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) wb[d][n] = ld_b128(rwf, vwf + n * WAVE * 16, d * wf_stream);
+  __syncthreads();
+
+  int I[RB][K];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int j = 0; j < K; ++j) I[b][j] = s_idx[TM * b + r][j];
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(reinterpret_cast<const T*>(a.X) + (size_t)t0 * N * C, (uint32_t)((size_t)rows * N * C * sizeof(T)));
+  const uint32_t vk = (uint32_t)(((size_t)kb0 * KB + VEC * g) * sizeof(T));
+  u32x4_t xa[RB][K];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t off = kvalid ? (uint32_t)(((size_t)(TM * b + r) * N + I[b][j]) * C * sizeof(T)) + vk : OUT_OF_RANGE;
+      xa[b][j] = ld_b128<CP_NT>(rx, off, 0);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float s1[RB], s2[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    s1[b] = 0.f;
+    s2[b] = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) add_stats<E>(xa[b][j], s1[b], s2[b]);
+  }
+  f32x4_t acc[RB][NTF];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) acc[b][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      // stream i holds the active position that chose it, if any
+      u32x4_t v = zero;
+#pragma unroll
+      for (int j = 0; j < K; ++j) v = (I[b][j] == i) ? xa[b][j] : v;
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) acc[b][n] = E::mma(acc[b][n], v, wb[i % WDC][n]);
+    }
+    if (i + WDC < N) {
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) wb[i % WDC][n] = ld_b128(rwf, vwf + n * WAVE * 16, (i + WDC) * wf_stream);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    s1[b] += __shfl_xor(s1[b], 16, WAVE);
+    s1[b] += __shfl_xor(s1[b], 32, WAVE);
+    s2[b] += __shfl_xor(s2[b], 16, WAVE);
+    s2[b] += __shfl_xor(s2[b], 32, WAVE);
+  }
+  const int tile0 = t0 / TM;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    if (b > 0) __syncthreads();   // the previous block's sums have been read
+    acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc[b]);
+    if (g == 0) {
+      s_red[wave][TM * NPF + 2 * r] = s1[b];
+      s_red[wave][TM * NPF + 2 * r + 1] = s2[b];
+    }
+    __syncthreads();
+    if (tile0 + b < a.ntiles) {
+      float* dst = a.corr + ((size_t)(tile0 + b) * G + slice) * P1;
+      for (int u = tid; u < NSUM; u += NTHR) dst[u] = sum_waves(s_red, u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+#ifndef XHC_CORR_RB
+#define XHC_CORR_RB 3
+#endif
+constexpr int CORR_RB = XHC_CORR_RB;
+
+template <class E, int N, int K, int KR>
+void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, const void* X, void* inp, char* ws,
+                        char* wsn, hipStream_t st) {
+  PreChainArgs a;
+  a.X = X; a.inp = inp; a.T = (int)P.T; a.C = P.C; a.G = P.G; a.m = P.m;
+  a.wact = reinterpret_cast<const uint4*>(ws + P.o_wact);
+  a.wnext = Pn ? reinterpret_cast<const uint4*>(wsn + Pn->o_wfull) : nullptr;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.h_pre = reinterpret_cast<const float*>(ws + P.o_hpre);
+  a.part2 = reinterpret_cast<float*>(ws + P.o_part2);
+  a.look = Pn ? reinterpret_cast<float*>(wsn + Pn->o_part) : nullptr;
+  const unsigned grid = (unsigned)(P.ntiles * P.G);
+  if (Pn)
+    xhc_pre_chained_kernel<E, N, K, KR, true><<<grid, NTHR, 0, st>>>(a);
+  else
+    xhc_pre_chained_kernel<E, N, K, KR, false><<<grid, NTHR, 0, st>>>(a);
+
+  ActFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.G = P.G; f.ntiles = (int)P.ntiles;
+  f.part2 = a.part2;
+  f.b_res = w->b_res; f.b_post = w->b_post;
+  f.a_res = w->alpha_res; f.a_post = w->alpha_post; f.eps = P.eps_norm; f.iters = P.iters;
+  f.h_res = reinterpret_cast<float*>(ws + P.o_hres);
+  f.h_post = reinterpret_cast<float*>(ws + P.o_hpost);
+  xhc_act_fin_kernel<K, KR><<<(unsigned)((P.ntiles + 3) / 4), 256, 0, st>>>(f);
+}
+
+template <int N, int K>
+void route_fin_launch(const Plan& P, const xhc_weights* w, char* ws, bool with_corr, hipStream_t st) {
+  RouteFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.G;
+  f.part = reinterpret_cast<const float*>(ws + P.o_part);
+  f.corr = with_corr ? reinterpret_cast<const float*>(ws + P.o_corr) : nullptr;
+  f.b_pre = w->b_pre; f.a_pre = w->alpha_pre; f.eps = P.eps_norm;
+  f.idx = reinterpret_cast<int*>(ws + P.o_idx);
+  f.p = reinterpret_cast<float*>(ws + P.o_p);
+  f.h_pre = reinterpret_cast<float*>(ws + P.o_hpre);
+  f.z = reinterpret_cast<float*>(ws + P.o_z);
+  xhc_route_fin_kernel<N, K><<<(unsigned)P.ntiles, 256, 0, st>>>(f);
+}
+
+template <class E, int N, int K>
+void route_launch(const Plan& P, const xhc_weights* w, const void* X, char* ws, hipStream_t st) {
+  ProjArgs a;
+  a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.G;
+  a.wfull = reinterpret_cast<const uint4*>(ws + P.o_wfull);
+  a.part = reinterpret_cast<float*>(ws + P.o_part);
+  xhc_proj_kernel<E, N><<<(unsigned)(P.ntiles * P.G), NTHR, 0, st>>>(a);
+  route_fin_launch<N, K>(P, w, ws, false, st);
+}
+
+template <class E, int N, int K>
+void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws, char* wsn,
+                 hipStream_t st) {
+  CorrArgs a;
+  a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.G; a.ntiles = (int)P.ntiles; a.m = P.m;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.wnext = reinterpret_cast<const uint4*>(wsn + Pn.o_wfull);
+  a.corr = reinterpret_cast<float*>(wsn + Pn.o_corr);
+  const long nblk = (P.T + TM * CORR_RB - 1) / (TM * CORR_RB);
+  xhc_corr_kernel<E, N, K, CORR_RB><<<(unsigned)(nblk * P.G), NTHR, 0, st>>>(a);
+  route_fin_launch<N, K>(Pn, wn, wsn, true, st);
+}
+
+// Dispatch over the built (N, K) shapes; KR only matters for the active maps.
+template <class F>
+bool dispatch_shape(int N, int K, F&& f) {
+  const int key = N * 100 + K;
+  switch (key) {
+    case 1604: f(std::integral_constant<int, 16>{}, std::integral_constant<int, 4>{}); return true;
+    case 1602: f(std::integral_constant<int, 16>{}, std::integral_constant<int, 2>{}); return true;
+    case 804: f(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{}); return true;
+    case 404: f(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{}); return true;
+    case 101: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); return true;
+    default: return false;
+  }
+}
+
+template <class E>
+bool route_dispatch(const Plan& P, const xhc_weights* w, const void* X, char* ws, hipStream_t st) {
+  return dispatch_shape(P.N, P.K, [&](auto n, auto k) { route_launch<E, decltype(n)::value, decltype(k)::value>(P, w, X, ws, st); });
+}
+
+template <class E>
+bool pre_chained_dispatch(const Plan& P, const xhc_weights* w, const Plan* Pn, const void* X, void* inp, char* ws,
+                          char* wsn, hipStream_t st) {
+  return dispatch_shape(P.N, P.K, [&](auto n, auto k) {
+    constexpr int NN = decltype(n)::value, KK = decltype(k)::value;
+    if (P.KR == 4)
+      pre_chained_launch<E, NN, KK, 4>(P, w, Pn, X, inp, ws, wsn, st);
+    else
+      pre_chained_launch<E, NN, KK, 1>(P, w, Pn, X, inp, ws, wsn, st);
+  });
+}
+
+template <class E>
+bool tail_dispatch(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws, char* wsn,
+                   hipStream_t st) {
+  return dispatch_shape(P.N, P.K, [&](auto n, auto k) {
+    tail_launch<E, decltype(n)::value, decltype(k)::value>(P, Pn, wn, X, ws, wsn, st);
+  });
+}
+
+}  // namespace
+
+bool launch_xhc_route(const Plan& P, const void* X, const xhc_weights* w, char* ws, hipStream_t st) {
+  if (!launch_pack(&P, w, ws, nullptr, nullptr, nullptr, &P, ws, st)) return false;
+  return P.dtype == XHC_BF16 ? route_dispatch<Bf16>(P, w, X, ws, st) : route_dispatch<F32>(P, w, X, ws, st);
+}
+
+bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn, const xhc_weights* wn,
+                            const void* X, void* inp, char* ws, char* wsn, hipStream_t st) {
+  if (!launch_pack(Pn, wn, wsn, &P, w, ws, &P, ws, st)) return false;
+  return P.dtype == XHC_BF16 ? pre_chained_dispatch<Bf16>(P, w, Pn, X, inp, ws, wsn, st)
+                             : pre_chained_dispatch<F32>(P, w, Pn, X, inp, ws, wsn, st);
+}
+
+bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws,
+                           char* wsn, hipStream_t st) {
+  return P.dtype == XHC_BF16 ? tail_dispatch<Bf16>(P, Pn, wn, X, ws, wsn, st)
+                             : tail_dispatch<F32>(P, Pn, wn, X, ws, wsn, st);
+}
+
+}  // namespace xhc

@@ -34,7 +34,7 @@ struct Plan {
   // workspace byte offsets
   size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,
          o_z = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
-         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, total = 0;
+         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX, total = 0;
 };
 
 // xHC pre, fused one-pass kernel.  sync: [0] ticket counter, [1] status
@@ -91,5 +91,17 @@ bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* 
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_mhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_mhc_post(const Plan& P, void* X, const void* out, char* ws, hipStream_t st);
+
+// Weight packing into MFMA B fragments: wf->w_full into wsf (layout Pf),
+// wa->w_act into wsa (layout Pa), and the sync words of wsz (layout Pz)
+// cleared; each part is skipped when its plan is null.
+bool launch_pack(const Plan* Pf, const xhc_weights* wf, char* wsf, const Plan* Pa, const xhc_weights* wa, char* wsa,
+                 const Plan* Pz, char* wsz, hipStream_t st);
+// Chained xHC sublayers (xhc_chain.hip).
+bool launch_xhc_route(const Plan& P, const void* X, const xhc_weights* w, char* ws, hipStream_t st);
+bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn, const xhc_weights* wn,
+                            const void* X, void* inp, char* ws, char* wsn, hipStream_t st);
+bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws,
+                           char* wsn, hipStream_t st);
 
 }  // namespace xhc

@@ -28,66 +28,19 @@
 // started; with room for G workgroups on the device at once every wait ends.
 // Each wait is also bounded: past the bound the kernel records a status word
 // and carries on (results are then invalid, and the host can see it).
-#include "xhc_device.hpp"
 #include "xhc_internal.hpp"
+#include "xhc_tile.hpp"
 
 namespace xhc {
 
 namespace {
 
-constexpr int TM = 16;    // tokens per tile (MFMA rows)
 constexpr int NKW = PRE_NKW;  // contraction blocks per wave and stream
 constexpr int WV = PRE_WV;    // waves per workgroup
 constexpr int NTHR = WV * 64;
+static_assert(WV == TWV, "tile workgroups are 8 waves");
 // A wait gives up after this many ticks of the 100 MHz real-time counter (2 s).
 constexpr uint64_t WAIT_LIMIT_TICKS = 200000000ull;
-
-__device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-__device__ __forceinline__ void st16_nt(void* p, const u32x4_t& v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
-}
-
-// Data exchanged between workgroups goes through device-coherent accesses:
-// agent-scope atomic stores and loads (gfx950: global_store / global_load with
-// the sc1 bit), which write through to, and read from, the level where all
-// compute units agree.  A publisher stores its data this way, waits until
-// every one of its memory operations has completed (s_waitcnt 0), and only
-// then bumps the counter or sets the flag; a consumer polls the counter or
-// flag, and reads the data with coherent loads issued after it has seen the
-// flag.  This orders data before flag without an agent-scope release fence,
-// which on this chip writes back the whole L2 and costs more than the rest
-// of the kernel.
-__device__ __forceinline__ void st_co(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_co(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Device-coherent buffer loads: the same sc1 cache policy as the atomic loads
-// above, but independent loads are issued back to back (the compiler waits
-// after each atomic load).  A buffer resource (gfx9 V#: base, no stride, byte
-// range) also turns any read past the range into zero instead of a fault.
-constexpr int CP_SC1 = 16;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint64_t ld_co64(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
-  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)byte_off, 0, CP_SC1));
-}
-__device__ __forceinline__ float ld_co(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)byte_off, 0, CP_SC1));
-}
-__device__ __forceinline__ int ld_co_i(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
-  return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)byte_off, 0, CP_SC1));
-}
-
-// Wait for all of this wave's outstanding memory operations.
-__device__ __forceinline__ void wait_mem() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-}
 
 // Wait until *flag != 0 (one lane); bounded in time.  The polling loads are
 // coherent but not acquiring (an acquire per poll would invalidate caches on
@@ -102,44 +55,6 @@ __device__ __forceinline__ void wait_flag(int* flag, int* status) {
     }
   }
 }
-
-// dst[u] = sum over s < G, in order s = 0, 1, ..., of src[s * stride + u], for
-// u < n (n and stride even; two neighbouring elements per thread, read with
-// one 8-byte coherent load).  The loads of up to 16 slices are issued
-// together, so the latency of fetching the partials is paid once per batch
-// rather than once per slice.
-__device__ __forceinline__ void sum_slices(const float* __restrict__ src, int G, int stride, int n,
-                                           float* __restrict__ dst, int tid) {
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)((size_t)G * stride * 4));
-  for (int u = 2 * tid; u < n; u += 2 * NTHR) {
-    float v0 = 0.f, v1 = 0.f;
-    for (int s0 = 0; s0 < G; s0 += 16) {
-      uint64_t x[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_co64(rs, (uint32_t)(((s0 + q) * stride + u) * 4)) : 0ull;
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (s0 + q < G) {
-          v0 += __uint_as_float((uint32_t)x[q]);
-          v1 += __uint_as_float((uint32_t)(x[q] >> 32));
-        }
-    }
-    dst[u] = v0;
-    dst[u + 1] = v1;
-  }
-}
-
-// Sum of the WV per-wave partials of element u, in a fixed order.
-template <int PM>
-__device__ __forceinline__ float sum_waves(const float (&r)[WV][PM], int u) {
-  static_assert(WV == 8, "fixed-order sum written for 8 waves");
-  return ((r[0][u] + r[1][u]) + (r[2][u] + r[3][u])) + ((r[4][u] + r[5][u]) + (r[6][u] + r[7][u]));
-}
-
-// A fragment of 1.0 in every element (bf16 0x3f80, f32 0x3f800000)
-template <class E> __device__ __forceinline__ u32x4_t ones_frag();
-template <> __device__ __forceinline__ u32x4_t ones_frag<Bf16>() { return u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}; }
-template <> __device__ __forceinline__ u32x4_t ones_frag<F32>() { return u32x4_t{0x3f800000u, 0x3f800000u, 0x3f800000u, 0x3f800000u}; }
 
 }  // namespace
 
@@ -240,45 +155,25 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_fused_kernel(XhcPreArgs a) {
 
   // ---------------------------------------------------------------- phase 2
   if (last1) {
-    sum_slices(a.part1 + (size_t)tile * G * P1, G, P1, P1, &s_red[1][0], tid);
+    sum_slices<NTHR, CP_SC1>(a.part1 + (size_t)tile * G * P1, G, P1, P1, &s_red[1][0], tid);
     __syncthreads();
     const float* sm = &s_red[1][0];
     const float n_el = (float)N * (float)C;
     for (int u = tid; u < TM * N; u += NTHR) {
       const int tau = u / N, i = u % N;
-      const int t = t0 + tau;
-      const float rr = sm[tau * NPF + i], rp = sm[tau * NPF + N + i];
-      const float q1 = sm[TM * NPF + 2 * tau], q2 = sm[TM * NPF + 2 * tau + 1], cs = sm[TM * NPF + 2 * TM + i];
-      const float mu = q1 / n_el, nu = q2 / n_el;
-      const float sd = sqrtf(fmaxf(nu - mu * mu, 0.f));
-      const float rstd = 1.f / (sd + a.eps);
-      const float rrms = 1.f / sqrtf(nu + a.eps);
-      s_z[tau][i] = (rr - mu * cs) * rstd;
-      s_hpre[tau][i] = t < a.T ? sigmoidf_(fmaf(a.a_pre * rp, rrms, a.b_pre[i])) : 0.f;
+      route_logits(sm[tau * NPF + i], sm[tau * NPF + N + i], sm[TM * NPF + 2 * tau], sm[TM * NPF + 2 * tau + 1],
+                   sm[TM * NPF + 2 * TM + i], n_el, a.eps, a.a_pre, a.b_pre[i], t0 + tau < a.T, &s_z[tau][i],
+                   &s_hpre[tau][i]);
     }
     __syncthreads();
     if (tid < TM) {
-      const int tau = tid;
-      uint32_t taken = 0;
+      float zt[N];
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        int sel;
-        if (j < a.m) {
-          sel = j;
-        } else {
-          int best = -1;
-          float bz = 0.f;
+      for (int i = 0; i < N; ++i) zt[i] = s_z[tid][i];
+      int sel[K];
+      route_select<N, K>(zt, a.m, sel);
 #pragma unroll
-          for (int i = 0; i < N; ++i) {
-            const float zi = s_z[tau][i];
-            const bool cand = (i >= a.m) && !((taken >> i) & 1u);
-            if (cand && (best < 0 || zi > bz)) { best = i; bz = zi; }
-          }
-          sel = best < 0 ? 0 : best;
-        }
-        taken |= 1u << sel;
-        s_idx[tau][j] = sel;
-      }
+      for (int j = 0; j < K; ++j) s_idx[tid][j] = sel[j];
     }
     __syncthreads();
     if (wave == 0) {
@@ -388,7 +283,7 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_fused_kernel(XhcPreArgs a) {
   if (s_msg != G - 1) return;
 
   // last workgroup of the tile: active maps (K lanes per token, one row each)
-  sum_slices(a.part2 + (size_t)tile * G * P2, G, P2, P2, &s_red[0][0], tid);
+  sum_slices<NTHR, CP_SC1>(a.part2 + (size_t)tile * G * P2, G, P2, P2, &s_red[0][0], tid);
   __syncthreads();
   if (wave == 0) {
     constexpr int TPP = WAVE / K;
@@ -514,6 +409,33 @@ static bool xhc_pre_fused_launch(const Plan& P, const void* X, void* inp, const 
     case 114: launch_fused<E, 1, 1, 4>(P, a, st); return true;
     default: return false;
   }
+}
+
+template <class E>
+static void pack_launch(const Plan* Pf, const xhc_weights* wf, char* wsf, const Plan* Pa, const xhc_weights* wa,
+                        char* wsa, const Plan* Pz, char* wsz, hipStream_t st) {
+  using TT = typename E::T;
+  const long nkbf = Pf ? Pf->nkb_full : 0, nkba = Pa ? Pa->nkb_act : 0;
+  const int NTF = Pf ? Pf->NTF : 1, NTA = Pa ? Pa->NTA : 1;
+  const int nsync = Pz ? 2 + 3 * (int)Pz->ntiles : 0;
+  const long nfrag = (nkbf * NTF + nkba * NTA) * WAVE;
+  const long nthreads = nfrag > nsync ? nfrag : nsync;
+  if (nthreads == 0) return;
+  xhc_prep_kernel<E><<<(unsigned)((nthreads + 255) / 256), 256, 0, st>>>(
+      Pf ? reinterpret_cast<const TT*>(wf->w_full) : nullptr, nkbf, Pf ? Pf->ncol_full : 0, NTF,
+      Pf ? reinterpret_cast<uint4*>(wsf + Pf->o_wfull) : nullptr, Pa ? reinterpret_cast<const TT*>(wa->w_act) : nullptr,
+      nkba, Pa ? Pa->ncol_act : 0, NTA, Pa ? reinterpret_cast<uint4*>(wsa + Pa->o_wact) : nullptr,
+      Pz ? reinterpret_cast<int*>(wsz + Pz->o_sync) : nullptr, nsync);
+}
+
+bool launch_pack(const Plan* Pf, const xhc_weights* wf, char* wsf, const Plan* Pa, const xhc_weights* wa, char* wsa,
+                 const Plan* Pz, char* wsz, hipStream_t st) {
+  const int dt = Pf ? Pf->dtype : Pa ? Pa->dtype : Pz ? Pz->dtype : XHC_BF16;
+  if (dt == XHC_BF16)
+    pack_launch<Bf16>(Pf, wf, wsf, Pa, wa, wsa, Pz, wsz, st);
+  else
+    pack_launch<F32>(Pf, wf, wsf, Pa, wa, wsa, Pz, wsz, st);
+  return true;
 }
 
 bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st) {

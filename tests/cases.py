@@ -127,6 +127,98 @@ def oracle_token(cfg, x_t, win, ow):
     return {key: v[-1] for key, v in r.items()}, margin
 
 
+# ------------------------------------------------------------------ chains
+
+CHAIN_MARGIN = 1e-2   # routing margin kept at every layer of a bf16 chain
+
+
+def chain_configs(N, k, m, C, B, S, kinds, dtype="bf16"):
+    return [Config(N=N, k=k, m=m, C=C, B=B, S=S, n_convs=3 if lk == "M" else 0, dtype=dtype) for lk in kinds]
+
+
+def oracle_chain(cfgs, X64, outs64, ows):
+    """The oracle's sublayers one after the other, each on the state the
+    previous one left (rounded to the state dtype).  Returns per-layer results."""
+    res = []
+    X = X64
+    for cfg, out, ow in zip(cfgs, outs64, ows):
+        r = oracle_xhc(cfg, X, out, ow)
+        res.append(r)
+        X = r["X"]
+    return res
+
+
+def xhc_chain_inputs(cfgs, seed, margin):
+    """Seeded state, per-layer outputs and weights of a chain; tokens whose
+    routing margin is below `margin` at any layer of the oracle chain are
+    redrawn (each state row has its own generator key)."""
+    c0 = cfgs[0]
+    wds = [synth.xhc_layer_weights(seed, l, c.N, c.k, c.C, c.K_r, c.dtype) for l, c in enumerate(cfgs)]
+    ows = [oracle_weights(wd) for wd in wds]
+    outs = [synth.sublayer_out(seed, l, c.B, c.S, c.C, c.dtype) for l, c in enumerate(cfgs)]
+    outs64 = [f64(o) for o in outs]
+    attempts = {}
+    X = synth.state(seed, c0.T, c0.N, c0.C, c0.dtype)
+    for _ in range(30):
+        ref = oracle_chain(cfgs, f64(X), outs64, ows)
+        bad = set()
+        for cfg, r in zip(cfgs, ref):
+            bad.update(np.nonzero(O.xhc_topk_margin(r["z"], cfg.m, cfg.k) < margin)[0].tolist())
+        if not bad:
+            return X, outs, wds, ref
+        bad = sorted(bad)
+        for t in bad:
+            attempts[t] = attempts.get(t, 0) + 1
+        X[bad] = synth.state_rows(seed, bad, c0.N, c0.C, c0.dtype, attempts)
+    raise AssertionError("could not draw a chain with the required routing margins")
+
+
+def gpu_xhc_chain(lib, cfgs, X, outs, wds, stream=None):
+    """The chained calls through the C ABI (two workspaces in turn); per layer
+    the public workspace arrays after xhc_pre_chained, inp, and the state
+    after xhc_post_chained (CPU copies)."""
+    ws_ = [weights_to_device(wd) for wd in wds]
+    Xd = X.to("cuda")
+    inp = torch.empty((cfgs[0].T, cfgs[0].C), dtype=cfgs[0].torch_dtype, device="cuda")
+    nb = max(lib.workspace_bytes(c) for c in cfgs)
+    wsp = [torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    lib.xhc_route(cfgs[0], ws_[0], Xd, wsp[0], stream)
+    res = []
+    for l, cfg in enumerate(cfgs):
+        nxt = l + 1 < len(cfgs)
+        cn, wn, wsn = (cfgs[l + 1], ws_[l + 1], wsp[(l + 1) % 2]) if nxt else (None, None, None)
+        lib.xhc_pre_chained(cfg, ws_[l], cn, wn, Xd, inp, wsp[l % 2], wsn, stream)
+        arrays = {k: v.clone() for k, v in lib.ws_arrays(cfg, wsp[l % 2]).items()}
+        assert int(arrays.pop("status").item()) == 0
+        lib.xhc_post_chained(cfg, ws_[l], cn, wn, Xd, outs[l].to("cuda"), wsp[l % 2], wsn, stream)
+        torch.cuda.synchronize()
+        res.append(dict(inp=inp.cpu(), X=Xd.cpu(), **{k: v.cpu() for k, v in arrays.items()}))
+    return res
+
+
+def compare_carried(g, o, l, dtype):
+    """Layer l >= 1 of a chain, where each side carries its own rounded state:
+    exact indices, per-element maps, and the state and sublayer input within a
+    normwise bound of (l + 1) steps per token.  One step is what a layer can
+    add to the difference of the two sides: in bf16 their roundings of an
+    element differ by at most one unit in the last place (2^-7 relative); in
+    fp32 the arithmetic dominates, sums of at most 2^10 terms at 2^-24 each
+    (2^-14).  The k x k mix has non-negative rows summing to at most one, so
+    it does not amplify a max-norm difference, and the maps' own inputs are
+    scaled by alpha = 0.01."""
+    assert np.array_equal(g["idx"].numpy(), o["I"]), "active indices differ"
+    errs = {key: rel_err(g[key].numpy().astype(np.float64), o[key]) for key in ("h_pre", "h_res", "h_post", "p")}
+    bound = (l + 1) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -14)
+    for key in ("inp", "X"):
+        d = (f64(g[key]) - o[key]).reshape(len(o[key]), -1)
+        r = o[key].reshape(len(o[key]), -1)
+        errs[key + "_norm"] = float(np.max(np.linalg.norm(d, axis=1) / np.linalg.norm(r, axis=1)))
+    bad = {key: v for key, v in errs.items() if key in ("h_pre", "h_res", "h_post", "p") and not v <= TOL[dtype]}
+    bad.update({key: v for key, v in errs.items() if key.endswith("_norm") and not v <= bound})
+    assert not bad, f"layer {l}: above bound (maps {TOL[dtype]}, state {bound:.3g}): {bad} (all: {errs})"
+    return errs
+
+
 # ------------------------------------------------------------------------ GPU
 
 def gpu_xhc(lib, cfg: Config, X, out, wd, stream=None):

@@ -1,0 +1,63 @@
+"""GPU parity of the chained xHC calls (xhc_route, xhc_pre_chained,
+xhc_post_chained) against the float64 oracle run sublayer after sublayer.
+
+In the chained calls, the routing of sublayer l+1 is accumulated while
+sublayer l runs: the rows sublayer l does not write are contracted in its
+pre-application, the k rewritten rows after its post-application.  The
+oracle computes every sublayer's routing from the whole state it receives,
+so these tests check that the split contraction gives the same routing,
+maps, sublayer inputs and states.  The first layer sees identical inputs on
+both sides (per-element bar); later layers carry each side's own rounded
+state (normwise bar, see cases.compare_carried).  Ragged tails, sequence
+starts inside a tile and every built (N, k) shape are covered.
+"""
+import numpy as np
+import pytest
+
+import cases as K
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def run_chain(lib, cfgs, seed, margin):
+    X, outs, wds, ref = K.xhc_chain_inputs(cfgs, seed, margin)
+    got = K.gpu_xhc_chain(lib, cfgs, X, outs, wds)
+    dt = cfgs[0].dtype
+    for l, (g, o) in enumerate(zip(got, ref)):
+        errs = K.compare_xhc(g, o, K.TOL[dt]) if l == 0 else K.compare_carried(g, o, l, dt)
+        if l == 0:
+            z = K.rel_err(g["z"].numpy().astype(np.float64), o["z"])
+            assert z <= K.TOL[dt], f"router logits {z}"
+            errs["z"] = z
+        _print(f"layer {l}:", {k: f"{v:.1e}" for k, v in errs.items()})
+
+
+def test_chain_bf16_n16_k4_attention_mlp_alternating(lib):
+    """4 sublayers A M A M, N=16, k=4, m=2, C=256, 2 x 37 tokens (ragged tile,
+    a sequence start inside a tile), bf16."""
+    run_chain(lib, K.chain_configs(16, 4, 2, 256, 2, 37, "AMAM"), seed=21, margin=K.CHAIN_MARGIN)
+
+
+def test_chain_f32_n16_k4(lib):
+    """3 sublayers M A M, N=16, k=4, m=2, C=128, 1 x 40 tokens, fp32 state."""
+    run_chain(lib, K.chain_configs(16, 4, 2, 128, 1, 40, "MAM", dtype="f32"), seed=22, margin=K.MARGIN)
+
+
+@pytest.mark.parametrize("N,k,m", [(16, 2, 1), (8, 4, 2), (4, 4, 2), (1, 1, 1)])
+def test_chain_other_shapes(lib, N, k, m):
+    """2 sublayers A M for every other built (N, k), C=64, 2 x 19 tokens, bf16."""
+    run_chain(lib, K.chain_configs(N, k, m, 64, 2, 19, "AM"), seed=30 + N + k, margin=K.CHAIN_MARGIN)
+
+
+def test_chain_single_sublayer_without_next(lib):
+    """A chain of one: xhc_route, then the chained calls with no next sublayer."""
+    run_chain(lib, K.chain_configs(16, 4, 2, 256, 1, 50, "M"), seed=23, margin=K.MARGIN)
+
+
+def test_chain_many_tiles_c4096(lib):
+    """3 sublayers A M A at C=4096 (16 channel slices), 1 x 160 tokens, bf16."""
+    run_chain(lib, K.chain_configs(16, 4, 2, 4096, 1, 160, "AMA"), seed=24, margin=K.CHAIN_MARGIN)

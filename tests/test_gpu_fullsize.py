@@ -83,23 +83,7 @@ def check_whole(cfg, X0, X1, arr):
     assert bool(torch.isfinite(X1).all()), "non-finite state"
 
 
-def compare_carried(g, o, l):
-    """Chain layer l >= 1: exact indices, per-element maps, normwise state."""
-    assert np.array_equal(g["idx"].numpy(), o["I"]), "active indices differ"
-    errs = {key: K.rel_err(g[key].numpy().astype(np.float64), o[key]) for key in ("h_pre", "h_res", "h_post", "p")}
-    bound = (l + 1) * 2.0 ** -7
-    for key in ("inp", "X"):
-        d = (K.f64(g[key]) - o[key]).reshape(len(o[key]), -1)
-        r = o[key].reshape(len(o[key]), -1)
-        errs[key + "_norm"] = float(np.max(np.linalg.norm(d, axis=1) / np.linalg.norm(r, axis=1)))
-        errs[key + "_elem"] = K.rel_err(K.f64(g[key]), o[key])   # reported, not bounded
-    bad = {key: v for key, v in errs.items() if key in ("h_pre", "h_res", "h_post", "p") and not v <= K.TOL["bf16"]}
-    bad.update({key: v for key, v in errs.items() if key.endswith("_norm") and not v <= bound})
-    assert not bad, f"layer {l}: above bound (maps {K.TOL['bf16']}, state {bound:.3g}): {bad} (all: {errs})"
-    return errs
-
-
-def run_xhc_layers(lib, N, k, m, C, B, S, kinds, seed, margin, n_random):
+def run_xhc_layers(lib, N, k, m, C, B, S, kinds, seed, margin, n_random, api="single"):
     cfgs = [Config(N=N, k=k, m=m, C=C, B=B, S=S, n_convs=3 if lk == "M" else 0, dtype="bf16") for lk in kinds]
     T = B * S
     toks = K.sample_tokens(B, S, n_random, seed)
@@ -132,18 +116,31 @@ def run_xhc_layers(lib, N, k, m, C, B, S, kinds, seed, margin, n_random):
     X = synth.state(seed, T, N, C, "bf16", attempts).to("cuda")
     outs = [synth.sublayer_out(seed, l, B, S, C, "bf16").to("cuda") for l in range(len(cfgs))]
     inp = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
-    ws = lib.workspace(max(cfgs, key=lambda c: lib.workspace_bytes(c)))
+    big = max(cfgs, key=lambda c: lib.workspace_bytes(c))
+    wsp = [lib.workspace(big), lib.workspace(big)] if api == "chained" else [lib.workspace(big)]
     stream = torch.cuda.current_stream()
     toks_d = torch.from_numpy(toks).to("cuda")
+    wdev = [weights_to_device(wd) for wd in wds]
+    if api == "chained":
+        lib.xhc_route(cfgs[0], wdev[0], X, wsp[0], stream)
     worst = {}
     for l, cfg in enumerate(cfgs):
-        _print(f"layer {l} ({kinds[l]}): N={N} k={k} C={C} T={T}")
-        w = weights_to_device(wds[l])
+        _print(f"layer {l} ({kinds[l]}, {api} calls): N={N} k={k} C={C} T={T}")
+        w = wdev[l]
         X0 = X.clone()
-        lib.xhc_pre(cfg, w, X, inp, ws, stream)
+        ws = wsp[l % len(wsp)]
+        if api == "chained":
+            nx = l + 1 < len(cfgs)
+            cn, wn, wsn = (cfgs[l + 1], wdev[l + 1], wsp[(l + 1) % 2]) if nx else (None, None, None)
+            lib.xhc_pre_chained(cfg, w, cn, wn, X, inp, ws, wsn, stream)
+        else:
+            lib.xhc_pre(cfg, w, X, inp, ws, stream)
         arr = {key: v.clone() for key, v in lib.ws_arrays(cfg, ws).items()}
         assert int(arr.pop("status").item()) == 0, "a wait between workgroups gave up"
-        lib.xhc_post(cfg, w, X, outs[l], ws, stream)
+        if api == "chained":
+            lib.xhc_post_chained(cfg, w, cn, wn, X, outs[l], ws, wsn, stream)
+        else:
+            lib.xhc_post(cfg, w, X, outs[l], ws, stream)
         torch.cuda.synchronize()
         check_whole(cfg, X0, X, arr)
         del X0
@@ -152,7 +149,7 @@ def run_xhc_layers(lib, N, k, m, C, B, S, kinds, seed, margin, n_random):
         g["X"] = X.index_select(0, toks_d).cpu()
         o = {key: np.stack([ref[int(t)][l][key] for t in toks])
              for key in ("I", "inp", "X", "h_pre", "h_res", "h_post", "p")}
-        errs = K.compare_xhc(g, o, K.TOL["bf16"]) if l == 0 else compare_carried(g, o, l)
+        errs = K.compare_xhc(g, o, K.TOL["bf16"]) if l == 0 else K.compare_carried(g, o, l, "bf16")
         for key, v in errs.items():
             worst[key] = max(worst.get(key, 0.0), v)
         _print("   ", {key: f"{v:.1e}" for key, v in errs.items()})
@@ -160,10 +157,13 @@ def run_xhc_layers(lib, N, k, m, C, B, S, kinds, seed, margin, n_random):
 
 
 @pytest.mark.timeout(300)
-def test_xhc_chain_n16_k4_c4096_full_size(lib):
+@pytest.mark.parametrize("api", ["single", "chained"])
+def test_xhc_chain_n16_k4_c4096_full_size(lib, api):
     """The 8-layer chain, N=16, k=4, m=2, C=4096, batch 2 x seq 8192, bf16;
-    attention- and MLP-type layers alternate and the state is carried in place."""
-    worst = run_xhc_layers(lib, 16, 4, 2, 4096, 2, 8192, "AMAMAMAM", seed=3, margin=CHAIN_MARGIN, n_random=24)
+    attention- and MLP-type layers alternate and the state is carried in place;
+    per-sublayer calls and chained calls."""
+    worst = run_xhc_layers(lib, 16, 4, 2, 4096, 2, 8192, "AMAMAMAM", seed=3, margin=CHAIN_MARGIN, n_random=24,
+                           api=api)
     _print("chain worst:", worst)
 
 
