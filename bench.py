@@ -208,6 +208,101 @@ def cpu_baseline(name, tokens=256):
                 sample=f"first {tokens} tokens of batch item 0, one {kinds_s} layer each, float64 NumPy")
 
 
+# ----------------------------------------------------------------- traffic
+# Measured HBM bytes per call come from two rocprofv3 counter runs of this
+# script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) and the same two
+# counters read for a plain 1 GiB device copy (--copy-probe), whose true bytes
+# are known: each counter is scaled by (true bytes / counter) of the copy.
+# --traffic-summary turns those runs into profiles/<workload>_traffic.json,
+# stamped with a hash of the kernel sources; a later run reports the traffic
+# only while the sources still hash the same.
+CSRC = os.path.join(ROOT, "stream_residual_mixing_amd", "csrc")
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not f:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = list(csv.DictReader(open(f[0])))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+
+def _split_calls(rows):
+    """Group this library's dispatches of one step into calls, in order: a
+    call starts at a weight-packing kernel, at the Gram kernel, or at an apply
+    kernel not preceded by the Gram kernel."""
+    calls, prev = [], ""
+    for name, v in rows:
+        if "xhc::" not in name:
+            continue
+        start = ("xhc_prep_kernel" in name or "xhc_gram_kernel" in name
+                 or ("xhc_apply_kernel" in name and "xhc_gram_kernel" not in prev))
+        if start or not calls:
+            calls.append([])
+        calls[-1].append((name, v))
+        prev = name
+    return calls
+
+
+def traffic_summary(workload, pmcdir):
+    """Writes profiles/<workload>_traffic.json from the four counter runs
+    under pmcdir (chain_fetch, chain_write, copy_fetch, copy_write)."""
+    copy_bytes = 1 << 30
+    scale = {}
+    for c, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
+        vals = [v for n, v in _pmc_rows(os.path.join(pmcdir, sub)) if "copyBuffer" in n and v > 1e5]
+        scale[c] = copy_bytes / (sum(vals) / len(vals) * 1024)
+    fetch = _split_calls(_pmc_rows(os.path.join(pmcdir, "chain_fetch")))
+    write = _split_calls(_pmc_rows(os.path.join(pmcdir, "chain_write")))
+    kind, cfgs, kinds = layer_configs(workload)
+    names = (["xhc_route"] if kind == "xhc" else []) + [
+        f"{p}_{lk}" for lk in kinds for p in (("xhc_pre_chained", "xhc_post_chained") if kind == "xhc"
+                                              else ("mhc_pre", "mhc_post"))]
+    if len(fetch) != len(names) or len(write) != len(names):
+        raise SystemExit(f"found {len(fetch)} / {len(write)} calls, expected {len(names)}")
+    per = {}
+    for name, fc, wc in zip(names, fetch, write):
+        fb = sum(v for _, v in fc) * 1024 * scale["FETCH_SIZE"]
+        wb = sum(v for _, v in wc) * 1024 * scale["WRITE_SIZE"]
+        per.setdefault(name, []).append((fb, wb, [n.split("(")[0] for n, _ in fc]))
+    out = {"workload": workload, "sources_sha256": sources_hash(), "copy_scale": scale, "calls": {}}
+    for name, lst in per.items():
+        out["calls"][name] = {"fetch_bytes": sum(x[0] for x in lst) / len(lst),
+                              "write_bytes": sum(x[1] for x in lst) / len(lst), "kernels": lst[0][2]}
+    with open(traffic_path(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def measured_traffic(workload, call):
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sources_hash() or call not in t.get("calls", {}):
+        return None
+    c = t["calls"][call]
+    return round(c["fetch_bytes"] + c["write_bytes"])
+
+
 def copy_probe(nbytes=1 << 30, reps=10):
     """A plain device-to-device copy of known size: the reference that scales
     the hardware byte counters, and the achievable-bandwidth yardstick."""
@@ -237,10 +332,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
+    ap.add_argument("--traffic-summary", metavar="PMCDIR", default=None,
+                    help="write profiles/<workload>_traffic.json from rocprofv3 counter runs and exit")
     ap.add_argument("--api", choices=("chained", "single"), default=None,
                     help="xHC calls: chained (routing of layer l+1 prepared during layer l; default for "
                          "multi-layer workloads) or single (xhc_pre / xhc_post per layer)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.workload, args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the layer has no multi-GPU path in this library "
               "(run with --gpus 1)", file=sys.stderr)
@@ -298,7 +398,9 @@ def main():
         "hbm": {"GBps": round(hbm_gbps, 1), "frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
                 "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.workload, dom) if api == default_api(args.workload) else None,
+                     "kernel": dom,
                      "bytes_per_launch": call_bytes[dom], "avg_us": round(dom_avg * 1e6, 2)},
         "calls": calls,
         "mfma": {"flop_per_token_layer": [flops_per_token(kind, c) for c in cfgs][:2],

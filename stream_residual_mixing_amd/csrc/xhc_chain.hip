@@ -81,6 +81,30 @@ __device__ __forceinline__ void add_stats(const u32x4_t& v, float& s1, float& s2
   }
 }
 
+// Per-token sums on the matrix cores.  With the A fragment of a 16-token
+// block in the same registers as a B operand, the MFMA computes A A^T, whose
+// diagonal holds each token's sum of squares over the block's contraction
+// range; with an all-ones B it computes every token's plain sum in each
+// column.  Lane (16 g + r) holds rows 4 g .. 4 g + 3 of the result, column r.
+template <class E>
+__device__ __forceinline__ void mma_sums(const u32x4_t& a, const u32x4_t& ones, f32x4_t& S1, f32x4_t& S2) {
+  S1 = E::mma(S1, a, ones);
+  S2 = E::mma(S2, a, a);
+}
+// Token r's entry of the diagonal (held by the lanes with r / 4 == g).
+__device__ __forceinline__ float diag_of(const f32x4_t& S, int r) {
+  const int i = r & 3;
+  return i == 0 ? S[0] : i == 1 ? S[1] : i == 2 ? S[2] : S[3];
+}
+// Write (sum x, sum x^2) of the block's 16 tokens to dst[2 tau], dst[2 tau + 1].
+__device__ __forceinline__ void sums_to_lds(float* dst, int g, int r, const f32x4_t& S1, const f32x4_t& S2) {
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[2 * (4 * g + i)] = S1[i];
+  }
+  if ((r >> 2) == g) dst[2 * r + 1] = diag_of(S2, r);
+}
+
 // Column-0..15 accumulators of one wave to LDS rows of a partial: element
 // (token 4 g + i, column n 16 + r) of the MFMA result.
 template <int NT, int NP, int PM>
@@ -143,11 +167,11 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_proj_kernel(ProjArgs a) {
 #pragma unroll
   for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float s1 = 0.f, s2 = 0.f;
+  f32x4_t S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
   const u32x4_t ones = ones_frag<E>();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    add_stats<E>(xd[i], s1, s2);
+    mma_sums<E>(xd[i], ones, S1, S2);
 #pragma unroll
     for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], xd[i], wb[i % WD][n]);
     acs = E::mma(acs, ones, wb[i % WD][0]);
@@ -157,16 +181,9 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_proj_kernel(ProjArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  s1 += __shfl_xor(s1, 16, WAVE);
-  s1 += __shfl_xor(s1, 32, WAVE);
-  s2 += __shfl_xor(s2, 16, WAVE);
-  s2 += __shfl_xor(s2, 32, WAVE);
   acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
-  if (g == 0) {
-    s_red[wave][TM * NPF + 2 * r] = s1;
-    s_red[wave][TM * NPF + 2 * r + 1] = s2;
-    s_red[wave][TM * NPF + 2 * TM + r] = acs[0];
-  }
+  sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+  if (g == 0) s_red[wave][TM * NPF + 2 * TM + r] = acs[0];
   __syncthreads();
   float* dst = a.part + (size_t)blockIdx.x * P1;
   for (int u = tid; u < P1; u += NTHR) dst[u] = sum_waves(s_red, u);
@@ -370,42 +387,34 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_chained_kernel(PreChainArgs a
   }
 
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  const u32x4_t ones = ones_frag<E>();
   if constexpr (LOOK) {
     // next layer's routing projection over the rows this layer leaves as they are
     f32x4_t acc[NTF];
 #pragma unroll
     for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float s1 = 0.f, s2 = 0.f;
-    const u32x4_t ones = ones_frag<E>();
+    f32x4_t S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const u32x4_t v = ((amask >> i) & 1u) ? zero : xd[i];
-      add_stats<E>(v, s1, s2);
+      mma_sums<E>(v, ones, S1, S2);
 #pragma unroll
       for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, wb[i % WDP][n]);
       acs = E::mma(acs, ones, wb[i % WDP][0]);
       if (i + WDP < NI) fetch(i + WDP);
       __builtin_amdgcn_sched_barrier(0);
     }
-    s1 += __shfl_xor(s1, 16, WAVE);
-    s1 += __shfl_xor(s1, 32, WAVE);
-    s2 += __shfl_xor(s2, 16, WAVE);
-    s2 += __shfl_xor(s2, 32, WAVE);
     acc_to_lds<NTF, NPF>(s_red1, wave, g, r, acc);
-    if (g == 0) {
-      s_red1[wave][TM * NPF + 2 * r] = s1;
-      s_red1[wave][TM * NPF + 2 * r + 1] = s2;
-      s_red1[wave][TM * NPF + 2 * TM + r] = acs[0];
-    }
+    sums_to_lds(&s_red1[wave][TM * NPF], g, r, S1, S2);
+    if (g == 0) s_red1[wave][TM * NPF + 2 * TM + r] = acs[0];
   }
 
   // gather of the k active rows, their sum of squares and active projection
   f32x4_t acc2[NTA];
 #pragma unroll
   for (int n = 0; n < NTA; ++n) acc2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float ss = 0.f;
-  float ss1 = 0.f;   // (sum of x over the active rows; not needed)
+  f32x4_t SS = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     constexpr int Q0 = NL;
@@ -416,16 +425,14 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_chained_kernel(PreChainArgs a
       for (int i = 0; i < N; ++i)
         if (i != j) v = (I[j] == i) ? xd[i] : v;
     }
-    add_stats<E>(v, ss1, ss);
+    SS = E::mma(SS, v, v);
 #pragma unroll
     for (int n = 0; n < NTA; ++n) acc2[n] = E::mma(acc2[n], v, wb[(Q0 + j) % WDP][n]);
     if (Q0 + j + WDP < NI) fetch(Q0 + j + WDP);
     __builtin_amdgcn_sched_barrier(0);
   }
-  ss += __shfl_xor(ss, 16, WAVE);
-  ss += __shfl_xor(ss, 32, WAVE);
   acc_to_lds<NTA, NPA>(s_red2, wave, g, r, acc2);
-  if (g == 0) s_red2[wave][TM * NPA + r] = ss;
+  if ((r >> 2) == g) s_red2[wave][TM * NPA + r] = diag_of(SS, r);
   __syncthreads();
   float* d2 = a.part2 + (size_t)blockIdx.x * P2;
   for (int u = tid; u < P2; u += NTHR) d2[u] = sum_waves(s_red2, u);
