@@ -6,14 +6,19 @@ input: for the default workload, the 8-layer xHC chain at N=16 streams,
 k=4 active (m=2 fixed), C=4096, batch 2 x seq 8192, bf16, layers
 alternating attention-type (K_r=1) and MLP-type (causal convolutions
 {4,8,12} + Gram-Schmidt, K_r=4), the state carried in place from layer to
-layer.  Every layer is xhc_pre then xhc_post through the C ABI; the
-sublayer F is a given tensor per layer (its cost is not part of the layer).
+layer.  The chain runs through the chained C-ABI calls (xhc_route once,
+then xhc_pre_chained + xhc_post_chained per layer: each layer's routing is
+accumulated while the layer before it runs); --api single times xhc_pre +
+xhc_post per layer instead.  The sublayer F is a given tensor per layer (its
+cost is not part of the layer).
 
 Prints ONE JSON line.  ``value`` is tokens/s per layer (tokens x layers /
 elapsed); ``hbm`` gives the algorithmic bytes moved (state read/write
 counted once per the byte model below) as GB/s and as a fraction of the
 MI355X peak of 8 TB/s.  ``roofline`` covers the call that dominates the
-step, timed with HIP events on the stream the kernels are launched on.
+step, timed with HIP events on the stream the kernels are launched on; its
+``traffic`` is the measured HBM bytes per launch from the committed counter
+summary, while the kernel sources are the ones it was measured on.
 ``cpu_baseline`` times the float64 oracle on a bounded sample of the same
 workload on the host cores.
 
