@@ -519,7 +519,8 @@ struct CorrArgs {
   float* corr;   // [ntiles][G][P1] (the first NSUM entries of each)
 };
 
-template <class E, int N, int K, int RB>
+// MS: the number of fixed streams when known at compile time (-1: a.m at run time).
+template <class E, int N, int K, int RB, int MS>
 __global__ __launch_bounds__(NTHR, 2) void xhc_corr_kernel(CorrArgs a) {
   using T = typename E::T;
   using D = RouteDims<N>;
@@ -589,10 +590,21 @@ __global__ __launch_bounds__(NTHR, 2) void xhc_corr_kernel(CorrArgs a) {
   for (int i = 0; i < N; ++i) {
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      // stream i holds the active position that chose it, if any
+      // stream i holds the active position that chose it, if any: with m
+      // known, stream i < m holds fixed position i and only routed positions
+      // can hold a stream i >= m
       u32x4_t v = zero;
+      if constexpr (MS >= 0) {
+        if (i < MS) {
+          v = xa[b][i < K ? i : 0];
+        } else {
 #pragma unroll
-      for (int j = 0; j < K; ++j) v = (I[b][j] == i) ? xa[b][j] : v;
+          for (int j = MS; j < K; ++j) v = (I[b][j] == i) ? xa[b][j] : v;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v = (I[b][j] == i) ? xa[b][j] : v;
+      }
 #pragma unroll
       for (int n = 0; n < NTF; ++n) acc[b][n] = E::mma(acc[b][n], v, wb[i % WDC][n]);
     }
@@ -632,7 +644,7 @@ __global__ __launch_bounds__(NTHR, 2) void xhc_corr_kernel(CorrArgs a) {
 namespace {
 
 #ifndef XHC_CORR_RB
-#define XHC_CORR_RB 3
+#define XHC_CORR_RB 4
 #endif
 constexpr int CORR_RB = XHC_CORR_RB;
 
@@ -696,7 +708,10 @@ void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* wn, const voi
   a.wnext = reinterpret_cast<const uint4*>(wsn + Pn.o_wfull);
   a.corr = reinterpret_cast<float*>(wsn + Pn.o_corr);
   const long nblk = (P.T + TM * CORR_RB - 1) / (TM * CORR_RB);
-  xhc_corr_kernel<E, N, K, CORR_RB><<<(unsigned)(nblk * P.G), NTHR, 0, st>>>(a);
+  if (P.m == 2 && K >= 2)
+    xhc_corr_kernel<E, N, K, CORR_RB, 2><<<(unsigned)(nblk * P.G), NTHR, 0, st>>>(a);
+  else
+    xhc_corr_kernel<E, N, K, CORR_RB, -1><<<(unsigned)(nblk * P.G), NTHR, 0, st>>>(a);
   route_fin_launch<N, K>(Pn, wn, wsn, true, st);
 }
 
