@@ -19,6 +19,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# hipBLASLt: the library GEMM of the wide mHC projection
+LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def hipcc() -> str:
@@ -32,7 +34,7 @@ def build(verbose: bool = False) -> str:
     """Compile libxhc.so (always recompiles) and return its path."""
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp, *LINK]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

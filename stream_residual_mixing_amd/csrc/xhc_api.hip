@@ -119,12 +119,21 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     return o;
   };
   if (mhc) {
+    // Wide maps (N >= 8, bf16): the projection [T x NC] . [NC x (2N + N^2)] is a
+    // real GEMM (N = 16: 618 GFLOP at T = 16384) and goes to the library GEMM,
+    // with the sums of squares from a streaming pass; no split.
+    q.mhc_gemm = q.N >= 8 && q.dtype == XHC_BF16;
+    if (q.mhc_gemm) q.KS = 1;
     q.o_hpre = take(T * N * 4);
     q.o_hres = take(T * N * N * 4);
     q.o_hpost = take(T * N * 4);
-    q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
+    q.o_wfull = take(q.mhc_gemm ? 0 : (size_t)q.nkb_full * q.NTF * 64 * 16);
     q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
     q.o_stats = take((size_t)q.KS * T * 2 * 4);
+    if (q.mhc_gemm) {
+      q.gemm_ws_bytes = (size_t)64 << 20;
+      q.o_gemm_ws = take(q.gemm_ws_bytes);
+    }
   } else {
     // one-pass pre: 16-token tiles, G channel slices of PRE_WV * PRE_NKW blocks
     const long nkbC = q.C / KB;
@@ -204,8 +213,10 @@ xhc_status pre_common(const xhc_config* cfg, const xhc_weights* w, const void* X
     return fail(XHC_ERR_INVALID_ARG, "X, inp and ws must be 16-byte aligned");
   if (X == inp || X == ws || inp == ws) return fail(XHC_ERR_INVALID_ARG, "X, inp and ws must not alias");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  xhc::g_launch_failure = nullptr;
   const bool ok = mhc ? xhc::launch_mhc_pre(P, X, inp, w, static_cast<char*>(ws), st)
                       : xhc::launch_xhc_pre(P, X, inp, w, static_cast<char*>(ws), st);
+  if (!ok && xhc::g_launch_failure) return fail(XHC_ERR_HIP, "%s", xhc::g_launch_failure);
   if (!ok) return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }

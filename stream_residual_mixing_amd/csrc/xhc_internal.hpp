@@ -28,13 +28,16 @@ struct Plan {
   int NTF = 0, NTA = 0;             // 16-column MFMA tiles
   long nkb_full = 0, nkb_act = 0;   // contraction blocks
   int KS = 1;                       // split of the full-state contraction (mHC)
+  bool mhc_gemm = false;            // mHC: projection by a library GEMM (wide maps)
   int nslices = 1;                  // channel slices of the post kernels
   int G = 1;                        // xHC pre: workgroups (channel slices) per 16-token tile
   long ntiles = 0;                  // xHC pre: 16-token tiles
   // workspace byte offsets
   size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,
          o_z = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
-         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX, total = 0;
+         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX, o_gemm_ws = SIZE_MAX,
+         total = 0;
+  size_t gemm_ws_bytes = 0;
 };
 
 // xHC pre, fused one-pass kernel.  sync: [0] ticket counter, [1] status
@@ -86,6 +89,10 @@ struct MhcPostArgs {
   int T, C, nslices;
   const float *h_res, *h_post;
 };
+
+// Set by a launcher that fails for a reason other than an unsupported shape
+// (e.g. the library GEMM); the host layer reports it as XHC_ERR_HIP.
+extern thread_local const char* g_launch_failure;
 
 bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st);

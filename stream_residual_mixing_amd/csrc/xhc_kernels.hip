@@ -17,7 +17,15 @@
 #include "xhc_device.hpp"
 #include "xhc_internal.hpp"
 
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
 namespace xhc {
+
+thread_local const char* g_launch_failure = nullptr;
 
 // ---------------------------------------------------------------------------
 // weight packing: fragment (kb, nt, lane = 16 g + col) holds
@@ -271,6 +279,112 @@ static bool gen_dispatch(int NT, const void* X, int T, long K, const void* Wp, l
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sums of x and x^2 over each token's flattened state (one wave per token,
+// 16-byte loads, eight in flight per lane), for the RMSNorm of the wide mHC
+// maps whose projection runs as a library GEMM.  stats[t] = (sum x, sum x^2).
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(256) void mhc_sumsq_kernel(const typename E::T* __restrict__ X, int T, long NC,
+                                                        float* __restrict__ stats) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const typename E::T* row = X + (size_t)t * NC;
+  constexpr int U = 8;
+  const long step = (long)WAVE * E::VEC;
+  float s1 = 0.f, s2 = 0.f;
+  long c = (long)lane * E::VEC;
+  for (; c + (U - 1) * step < NC; c += U * step) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld16(row + c + u * step);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float f[E::VEC];
+      E::unpack(v[u], f);
+#pragma unroll
+      for (int e = 0; e < E::VEC; ++e) { s1 += f[e]; s2 = fmaf(f[e], f[e], s2); }
+    }
+  }
+  for (; c < NC; c += step) {
+    float f[E::VEC];
+    E::unpack(ld16(row + c), f);
+#pragma unroll
+    for (int e = 0; e < E::VEC; ++e) { s1 += f[e]; s2 = fmaf(f[e], f[e], s2); }
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (lane == 0) {
+    stats[(size_t)t * 2] = s1;
+    stats[(size_t)t * 2 + 1] = s2;
+  }
+}
+
+// The library GEMM of the wide mHC projection: raw[t][0..ncol) = vec X_t . W
+// (bf16 in, float out, rows of raw NP floats apart).  hipBLASLt is column-major,
+// so it computes raw^T (ncol x T, ld NP) = W^T (ncol x NC, ld ncol) X^T (NC x T,
+// ld NC), reading both operands in their row-major layout untransposed.  One
+// handle per device and one algorithm per shape, chosen by the library's
+// heuristic on first use and kept for the process.
+struct LtShape {
+  int dev;
+  long T, NC, ncol, NP;
+  bool operator<(const LtShape& o) const {
+    return std::tie(dev, T, NC, ncol, NP) < std::tie(o.dev, o.T, o.NC, o.ncol, o.NP);
+  }
+};
+struct LtPlan {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, d = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  size_t ws = 0;
+};
+
+static bool lt_gemm(const void* X, const void* W, float* raw, long T, long NC, long ncol, long NP, void* ws,
+                    size_t ws_bytes, hipStream_t st) {
+  static std::mutex mu;
+  static hipblasLtHandle_t handles[64] = {};
+  static std::map<LtShape, LtPlan> plans;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!handles[dev] && hipblasLtCreate(&handles[dev]) != HIPBLAS_STATUS_SUCCESS) return false;
+  const LtShape key{dev, T, NC, ncol, NP};
+  auto it = plans.find(key);
+  if (it == plans.end()) {
+    LtPlan p;
+    const hipblasOperation_t opn = HIPBLAS_OP_N;
+    if (hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &opn, sizeof opn) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &opn, sizeof opn) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, ncol, NC, ncol) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, NC, T, NC) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&p.d, HIP_R_32F, ncol, T, NP) != HIPBLAS_STATUS_SUCCESS)
+      return false;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    const uint64_t maxws = ws_bytes;
+    hipblasLtMatmulHeuristicResult_t res[8];
+    int n = 0;
+    if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return false;
+    const bool ok = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &maxws,
+                                                          sizeof maxws) == HIPBLAS_STATUS_SUCCESS &&
+                    hipblasLtMatmulAlgoGetHeuristic(handles[dev], p.op, p.a, p.b, p.d, p.d, pref, 8, res, &n) ==
+                        HIPBLAS_STATUS_SUCCESS &&
+                    n > 0;
+    hipblasLtMatmulPreferenceDestroy(pref);
+    if (!ok) return false;
+    p.algo = res[0].algo;
+    p.ws = res[0].workspaceSize;
+    it = plans.emplace(key, p).first;
+  }
+  const LtPlan& p = it->second;
+  if (p.ws > ws_bytes) return false;
+  const float one = 1.f, zero = 0.f;
+  return hipblasLtMatmul(handles[dev], p.op, &one, W, p.a, X, p.b, &zero, raw, p.d, raw, p.d, &p.algo, ws, p.ws,
+                         st) == HIPBLAS_STATUS_SUCCESS;
+}
+
 template <class E, int N>
 static void launch_mhc_read(const MhcReadArgs& a, hipStream_t st) {
   mhc_read_kernel<E, N><<<(a.T + RT - 1) / RT, 256, 0, st>>>(a);
@@ -284,10 +398,22 @@ static void launch_mhc_post(const MhcPostArgs& a, hipStream_t st) {
 
 template <class E>
 static bool mhc_pre_launch(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st) {
-  launch_pack<E>(w->w_full, P.nkb_full, P.ncol_full, P.NTF, ws + P.o_wfull, st);
-  if (!gen_dispatch<E>(P.NTF, X, (int)P.T, (long)P.N * P.C, ws + P.o_wfull, P.nkb_full, P.KS,
-                       reinterpret_cast<float*>(ws + P.o_part), reinterpret_cast<float*>(ws + P.o_stats), st))
-    return false;
+  if (P.mhc_gemm) {
+    const long NC = (long)P.N * P.C;
+    mhc_sumsq_kernel<E><<<(unsigned)((P.T + 3) / 4), 256, 0, st>>>(reinterpret_cast<const typename E::T*>(X),
+                                                                      (int)P.T, NC,
+                                                                      reinterpret_cast<float*>(ws + P.o_stats));
+    if (!lt_gemm(X, w->w_full, reinterpret_cast<float*>(ws + P.o_part), P.T, NC, P.ncol_full, (long)P.NTF * 16,
+                 ws + P.o_gemm_ws, P.gemm_ws_bytes, st)) {
+      g_launch_failure = "hipBLASLt GEMM of the full-state projection failed";
+      return false;
+    }
+  } else {
+    launch_pack<E>(w->w_full, P.nkb_full, P.ncol_full, P.NTF, ws + P.o_wfull, st);
+    if (!gen_dispatch<E>(P.NTF, X, (int)P.T, (long)P.N * P.C, ws + P.o_wfull, P.nkb_full, P.KS,
+                         reinterpret_cast<float*>(ws + P.o_part), reinterpret_cast<float*>(ws + P.o_stats), st))
+      return false;
+  }
   MhcReadArgs a;
   a.X = X; a.inp = inp; a.T = (int)P.T; a.C = P.C; a.KS = P.KS;
   a.part = reinterpret_cast<const float*>(ws + P.o_part);
