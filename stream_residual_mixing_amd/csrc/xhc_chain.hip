@@ -160,7 +160,7 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_proj_kernel(ProjArgs a) {
   const uint32_t vx = kvalid ? (uint32_t)(((size_t)r * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
   u32x4_t xd[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) xd[i] = ld_b128<CP_NT>(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
+  for (int i = 0; i < N; ++i) xd[i] = ld_b128(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
   __builtin_amdgcn_sched_barrier(0);
 
   f32x4_t acc[NTF];
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_chained_kernel(PreChainArgs a
   const uint32_t vx = kvalid ? (uint32_t)(((size_t)r * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
   u32x4_t xd[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) xd[i] = ld_b128<CP_NT>(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
+  for (int i = 0; i < N; ++i) xd[i] = ld_b128(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(NTHR, 2) void xhc_corr_kernel(CorrArgs a) {
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const uint32_t off = kvalid ? (uint32_t)(((size_t)(TM * b + r) * N + I[b][j]) * C * sizeof(T)) + vk : OUT_OF_RANGE;
-      xa[b][j] = ld_b128<CP_NT>(rx, off, 0);
+      xa[b][j] = ld_b128(rx, off, 0);
     }
   __builtin_amdgcn_sched_barrier(0);
 

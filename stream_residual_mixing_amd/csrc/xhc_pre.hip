@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_fused_kernel(XhcPreArgs a) {
 #pragma unroll
     for (int q = 0; q < NKW; ++q) {
       const int kb = kb0 + q;
-      xd[i][q] = (tvalid && kb < nkbC) ? ld16_nt(xt + (size_t)i * C + kb * KB) : zero;
+      xd[i][q] = (tvalid && kb < nkbC) ? ld16v(xt + (size_t)i * C + kb * KB) : zero;
     }
 
   f32x4_t acc[NTF];

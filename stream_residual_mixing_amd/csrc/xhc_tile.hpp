@@ -12,6 +12,7 @@ constexpr int TM = 16;          // tokens per tile (MFMA rows)
 constexpr int TWV = 8;          // waves per tile workgroup
 constexpr int TNTHR = TWV * 64;
 
+__device__ __forceinline__ u32x4_t ld16v(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
@@ -39,7 +40,11 @@ __device__ __forceinline__ void st_co(int* p, int v) {
 // Buffer resources (gfx9 V#: base, no stride, byte range): any read past the
 // range returns zero instead of faulting, and independent loads through one
 // are issued back to back.  Cache policy bits: sc1 (device-coherent, the same
-// policy as the atomic loads above) and nt (streaming).
+// policy as the atomic loads above) and nt (streaming).  State reads use the
+// default policy: a wave reads 64-byte halves of 128-byte lines whose other
+// half a neighbouring wave reads moments later, and with nt the line tends to
+// be gone by then (measured: the streaming hint made these kernels ~10%
+// slower).
 constexpr int CP_SC1 = 16;
 constexpr int CP_NT = 2;
 // A byte offset past any resource's range: loads from it return zero.
