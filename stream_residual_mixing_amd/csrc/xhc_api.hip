@@ -139,6 +139,9 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     const long nkbC = q.C / KB;
     constexpr int SB = xhc::PRE_WV * xhc::PRE_NKW;
     q.G = (int)((nkbC + SB - 1) / SB);
+    // persistent chained kernels: slices of 4 blocks (their routing weights fit in LDS)
+    q.Gp = (int)((nkbC + 3) / 4);
+    const size_t GM = (size_t)(q.G > q.Gp ? q.G : q.Gp);
     q.ntiles = (q.T + 15) / 16;
     const size_t P1 = 16 * (size_t)q.NTF * 16 + 2 * 16 + 16;
     const size_t P2 = 16 * (size_t)q.NTA * 16 + 16;
@@ -151,10 +154,10 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     q.o_z = take(T * N * 4);
     q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
     q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
-    q.o_part = take((size_t)q.ntiles * q.G * P1 * 4);
-    q.o_part2 = take((size_t)q.ntiles * q.G * P2 * 4);
+    q.o_part = take((size_t)q.ntiles * GM * P1 * 4);
+    q.o_part2 = take((size_t)q.ntiles * GM * P2 * 4);
     q.o_gram = take((size_t)q.nslices * T * 10 * 4);
-    q.o_corr = take((size_t)q.ntiles * q.G * P1 * 4);
+    q.o_corr = take((size_t)q.ntiles * GM * P1 * 4);
   }
   q.total = q.T == 0 ? 0 : off;
   *P = q;

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_proj_kernel(ProjArgs a) {
 // rewritten rows; router logits, H_pre, active list and router weights.
 // ---------------------------------------------------------------------------
 struct RouteFinArgs {
-  int T, C, m, G;
+  int T, C, m, G, Gc;   // slices of part and of corr
   const float* part;
   const float* corr;   // may be null
   const float* b_pre;
@@ -211,12 +211,12 @@ __global__ __launch_bounds__(256) void xhc_route_fin_kernel(RouteFinArgs a) {
   __shared__ float s_sum[P1];
   __shared__ float s_z[TM][N];
   __shared__ float s_hpre[TM][N];
-  const int tid = threadIdx.x, G = a.G;
+  const int tid = threadIdx.x, G = a.G, Gc = a.Gc;
   const int tile = blockIdx.x, t0 = tile * TM;
 
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part + (size_t)tile * G * P1, (uint32_t)((size_t)G * P1 * 4));
   const __amdgpu_buffer_rsrc_t rc =
-      make_rsrc(a.corr ? a.corr + (size_t)tile * G * P1 : a.part, a.corr ? (uint32_t)((size_t)G * P1 * 4) : 0u);
+      make_rsrc(a.corr ? a.corr + (size_t)tile * Gc * P1 : a.part, a.corr ? (uint32_t)((size_t)Gc * P1 * 4) : 0u);
   for (int u = 2 * tid; u < P1; u += 2 * 256) {
     float v0 = 0.f, v1 = 0.f;
     for (int s0 = 0; s0 < G; s0 += 16) {
@@ -231,13 +231,13 @@ __global__ __launch_bounds__(256) void xhc_route_fin_kernel(RouteFinArgs a) {
         }
     }
     if (a.corr && u < NSUM) {
-      for (int s0 = 0; s0 < G; s0 += 16) {
+      for (int s0 = 0; s0 < Gc; s0 += 16) {
         uint64_t x[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_b64(rc, (uint32_t)(((s0 + q) * P1 + u) * 4)) : 0ull;
+        for (int q = 0; q < 16; ++q) x[q] = s0 + q < Gc ? ld_b64(rc, (uint32_t)(((s0 + q) * P1 + u) * 4)) : 0ull;
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-          if (s0 + q < G) {
+          if (s0 + q < Gc) {
             v0 += __uint_as_float((uint32_t)x[q]);
             v1 += __uint_as_float((uint32_t)(x[q] >> 32));
           }
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void xhc_route_fin_kernel(RouteFinArgs a) {
 struct PreChainArgs {
   const void* X;
   void* inp;
-  int T, C, G, m;
+  int T, C, G, m, ntiles;
   const uint4* wact;   // this layer's packed [W_res | W_post]
   const uint4* wnext;  // next layer's packed [W_r | W_pre] (LOOK)
   const int* idx;
@@ -294,14 +294,19 @@ struct PreChainArgs {
   float* look;         // next layer's routing partials [ntiles][G][P1] (LOOK)
 };
 
-template <class E, int N, int K, int KR, bool LOOK>
-__global__ __launch_bounds__(NTHR, 4) void xhc_pre_chained_kernel(PreChainArgs a) {
+// RB row blocks of 16 tokens per workgroup share every weight fragment
+// fetched.  RB = 2 halves the weight traffic, but the workgroup then holds
+// 128 VGPRs of state per lane and runs one per CU; measured no faster than
+// RB = 1, which is the default.  Partials are written per 16-token tile.
+template <class E, int N, int K, int KR, bool LOOK, int RB>
+__global__ __launch_bounds__(NTHR, RB == 1 ? 4 : 2) void xhc_pre_chained_kernel(PreChainArgs a) {
   using T = typename E::T;
   using D = RouteDims<N>;
   using A = ActDims<K, KR>;
   constexpr int NTF = D::NTF, NPF = D::NPF, P1 = D::P1;
   constexpr int NTA = A::NTA, NPA = A::NPA, P2 = A::P2;
   constexpr int KB = E::KB, VEC = E::VEC;
+  constexpr int TT = TM * RB;   // tokens per workgroup
   // Weight items in order of use: N streams of the next layer's routing
   // weights (LOOK), then the K positions of this layer's active weights.
   constexpr int NL = LOOK ? N : 0;
@@ -309,25 +314,24 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_chained_kernel(PreChainArgs a
   constexpr int NTR = NTF > NTA ? NTF : NTA;
   __shared__ float s_red2[TWV][P2];
   __shared__ float s_red1[LOOK ? TWV : 1][LOOK ? P1 : 2];
-  __shared__ float s_hpre[TM][N];
-  __shared__ int s_idx[TM][K];
+  __shared__ float s_hpre[TT][N];
+  __shared__ int s_idx[TT][K];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
   const int C = a.C, G = a.G, nkbC = C / KB;
   const int tile = blockIdx.x / G, slice = blockIdx.x % G;
-  const int t0 = tile * TM;
-  const int rows = a.T - t0 < TM ? a.T - t0 : TM;
-  const int tok = t0 + r;
-  const bool tvalid = r < rows;
+  const int t0 = tile * TT;
+  const int rows = a.T - t0 < TT ? a.T - t0 : TT;
   const int kb0 = slice * TWV + wave;
   const bool kvalid = kb0 < nkbC;
 
-  // routing of the tile (written by an earlier launch)
-  if (tid < TM * N) {
-    const int tau = tid / N;
-    s_hpre[tau][tid % N] = tau < rows ? a.h_pre[(size_t)t0 * N + tid] : 0.f;
-  } else if (tid >= 256 && tid < 256 + TM * K) {
-    const int u = tid - 256, tau = u / K, j = u % K;
+  // routing of the tokens (written by an earlier launch)
+  for (int u = tid; u < TT * N; u += NTHR) {
+    const int tau = u / N;
+    s_hpre[tau][u % N] = tau < rows ? a.h_pre[(size_t)t0 * N + u] : 0.f;
+  }
+  for (int u = tid; u < TT * K; u += NTHR) {
+    const int tau = u / K, j = u % K;
     const int v = tau < rows ? a.idx[(size_t)t0 * K + u] : j;
     s_idx[tau][j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
   }
@@ -355,90 +359,133 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_chained_kernel(PreChainArgs a
 
   const __amdgpu_buffer_rsrc_t rx =
       make_rsrc(reinterpret_cast<const T*>(a.X) + (size_t)t0 * N * C, (uint32_t)((size_t)rows * N * C * sizeof(T)));
-  const uint32_t vx = kvalid ? (uint32_t)(((size_t)r * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
-  u32x4_t xd[N];
+  u32x4_t xd[RB][N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) xd[i] = ld_b128(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
+  for (int b = 0; b < RB; ++b) {
+    const uint32_t vx =
+        kvalid ? (uint32_t)(((size_t)(TM * b + r) * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
+#pragma unroll
+    for (int i = 0; i < N; ++i) xd[b][i] = ld_b128(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
+  }
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
-  int I[K];
-  uint32_t amask = 0;
+  int I[RB][K];
+  uint32_t amask[RB];
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    I[j] = s_idx[r][j];
-    amask |= 1u << I[j];
+  for (int b = 0; b < RB; ++b) {
+    amask[b] = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      I[b][j] = s_idx[TM * b + r][j];
+      amask[b] |= 1u << I[b][j];
+    }
   }
 
   // dense read over all N streams -> sublayer input
   if (kvalid) {
-    float o[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+    for (int b = 0; b < RB; ++b) {
+      float o[VEC];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const float hpi = s_hpre[r][i];
-      float f[VEC];
-      E::unpack(xd[i], f);
+      for (int e = 0; e < VEC; ++e) o[e] = 0.f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] = fmaf(hpi, f[e], o[e]);
+      for (int i = 0; i < N; ++i) {
+        const float hpi = s_hpre[TM * b + r][i];
+        float f[VEC];
+        E::unpack(xd[b][i], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = fmaf(hpi, f[e], o[e]);
+      }
+      if (TM * b + r < rows)
+        st16_nt(reinterpret_cast<T*>(a.inp) + (size_t)(t0 + TM * b + r) * C + kb0 * KB + VEC * g, E::packv(o));
     }
-    if (tvalid) st16_nt(reinterpret_cast<T*>(a.inp) + (size_t)tok * C + kb0 * KB + VEC * g, E::packv(o));
   }
 
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
+  f32x4_t acc[LOOK ? RB : 1][NTF];
+  f32x4_t S1[LOOK ? RB : 1], S2[LOOK ? RB : 1];
+  f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (LOOK) {
     // next layer's routing projection over the rows this layer leaves as they are
-    f32x4_t acc[NTF];
 #pragma unroll
-    for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
+    for (int b = 0; b < RB; ++b) {
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) acc[b][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      S1[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      S2[b] = S1[b];
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const u32x4_t v = ((amask >> i) & 1u) ? zero : xd[i];
-      mma_sums<E>(v, ones, S1, S2);
 #pragma unroll
-      for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, wb[i % WDP][n]);
+      for (int b = 0; b < RB; ++b) {
+        const u32x4_t v = ((amask[b] >> i) & 1u) ? zero : xd[b][i];
+        mma_sums<E>(v, ones, S1[b], S2[b]);
+#pragma unroll
+        for (int n = 0; n < NTF; ++n) acc[b][n] = E::mma(acc[b][n], v, wb[i % WDP][n]);
+      }
       acs = E::mma(acs, ones, wb[i % WDP][0]);
       if (i + WDP < NI) fetch(i + WDP);
       __builtin_amdgcn_sched_barrier(0);
     }
-    acc_to_lds<NTF, NPF>(s_red1, wave, g, r, acc);
-    sums_to_lds(&s_red1[wave][TM * NPF], g, r, S1, S2);
-    if (g == 0) s_red1[wave][TM * NPF + 2 * TM + r] = acs[0];
+    if constexpr (RB == 1) {   // to LDS now, so the accumulators are free for the gather
+      acc_to_lds<NTF, NPF>(s_red1, wave, g, r, acc[0]);
+      sums_to_lds(&s_red1[wave][TM * NPF], g, r, S1[0], S2[0]);
+      if (g == 0) s_red1[wave][TM * NPF + 2 * TM + r] = acs[0];
+    }
   }
 
   // gather of the k active rows, their sum of squares and active projection
-  f32x4_t acc2[NTA];
+  f32x4_t acc2[RB][NTA];
+  f32x4_t SS[RB];
 #pragma unroll
-  for (int n = 0; n < NTA; ++n) acc2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t SS = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int n = 0; n < NTA; ++n) acc2[b][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    SS[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     constexpr int Q0 = NL;
-    // position j < m holds stream j; a routed position holds one of m..N-1
-    u32x4_t v = xd[j < N ? j : 0];
-    if (j >= a.m) {
 #pragma unroll
-      for (int i = 0; i < N; ++i)
-        if (i != j) v = (I[j] == i) ? xd[i] : v;
+    for (int b = 0; b < RB; ++b) {
+      // position j < m holds stream j; a routed position holds one of m..N-1
+      u32x4_t v = xd[b][j < N ? j : 0];
+      if (j >= a.m) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+          if (i != j) v = (I[b][j] == i) ? xd[b][i] : v;
+      }
+      SS[b] = E::mma(SS[b], v, v);
+#pragma unroll
+      for (int n = 0; n < NTA; ++n) acc2[b][n] = E::mma(acc2[b][n], v, wb[(Q0 + j) % WDP][n]);
     }
-    SS = E::mma(SS, v, v);
-#pragma unroll
-    for (int n = 0; n < NTA; ++n) acc2[n] = E::mma(acc2[n], v, wb[(Q0 + j) % WDP][n]);
     if (Q0 + j + WDP < NI) fetch(Q0 + j + WDP);
     __builtin_amdgcn_sched_barrier(0);
   }
-  acc_to_lds<NTA, NPA>(s_red2, wave, g, r, acc2);
-  if ((r >> 2) == g) s_red2[wave][TM * NPA + r] = diag_of(SS, r);
-  __syncthreads();
-  float* d2 = a.part2 + (size_t)blockIdx.x * P2;
-  for (int u = tid; u < P2; u += NTHR) d2[u] = sum_waves(s_red2, u);
-  if constexpr (LOOK) {
-    float* d1 = a.look + (size_t)blockIdx.x * P1;
-    for (int u = tid; u < P1; u += NTHR) d1[u] = sum_waves(s_red1, u);
+
+  // partials of each 16-token row block, summed over the waves in a fixed order
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int tile16 = (t0 / TM) + b;
+    if (b > 0) __syncthreads();   // the previous block's sums have been read
+    acc_to_lds<NTA, NPA>(s_red2, wave, g, r, acc2[b]);
+    if ((r >> 2) == g) s_red2[wave][TM * NPA + r] = diag_of(SS[b], r);
+    if constexpr (LOOK && RB > 1) {
+      acc_to_lds<NTF, NPF>(s_red1, wave, g, r, acc[b]);
+      sums_to_lds(&s_red1[wave][TM * NPF], g, r, S1[b], S2[b]);
+      if (g == 0) s_red1[wave][TM * NPF + 2 * TM + r] = acs[0];
+    }
+    __syncthreads();
+    if (tile16 < a.ntiles) {
+      float* d2 = a.part2 + ((size_t)tile16 * G + slice) * P2;
+      for (int u = tid; u < P2; u += NTHR) d2[u] = sum_waves(s_red2, u);
+      if constexpr (LOOK) {
+        float* d1 = a.look + ((size_t)tile16 * G + slice) * P1;
+        for (int u = tid; u < P1; u += NTHR) d1[u] = sum_waves(s_red1, u);
+      }
+    }
   }
 }
 
@@ -639,34 +686,424 @@ __global__ __launch_bounds__(NTHR, 2) void xhc_corr_kernel(CorrArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Persistent form of the routing projection and of the chained pre pass.
+//
+// The routing weights [W_r | W_pre] of one channel slice are as large as the
+// state a 16-token tile holds in that slice, and the kernels above read them
+// from L2 again for every tile, behind the state loads in the same memory
+// queue.  Here a workgroup owns one slice of PSB contraction blocks for the
+// whole launch, keeps that slice's routing fragments in LDS (read from L2
+// once per workgroup) and walks steps of PTL 16-token tiles, one wave per
+// (tile of the step, block of the slice).  The state of the next step is
+// loaded into a second register set while this step computes.  Partials keep
+// the per-tile layout, over Gp = ceil(C / (PSB KB)) slices.
+// ---------------------------------------------------------------------------
+constexpr int PSB = 4;                    // contraction blocks per slice
+constexpr int PTL = 2;                    // 16-token tiles per step
+constexpr int PNTHR = PSB * PTL * WAVE;   // 512 threads, 8 waves
+static_assert(PSB * PTL == TWV, "one wave per (tile, block)");
+
+template <int N>
+struct XTile {
+  u32x4_t x[N];
+};
+
+// One wave's share of a step: token r of tile b of the step, VEC channels of
+// block kb in every stream (lane_off covers b, r and kb, or is OUT_OF_RANGE
+// for a block past C).  The buffer resource spans the step's valid rows only
+// (rows, from step_rows), so rows past T read zeros without touching memory;
+// it depends on the step alone, which keeps it in scalar registers.
+template <class E, int N>
+__device__ __forceinline__ void load_xtile(XTile<N>& xs, const typename E::T* X, int C, int step, int rows,
+                                           uint32_t lane_off) {
+  using TT = typename E::T;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (size_t)(rows > 0 ? step : 0) * PTL * TM * N * C,
+                                              (uint32_t)((size_t)rows * N * C * sizeof(TT)));
+#pragma unroll
+  for (int i = 0; i < N; ++i) xs.x[i] = ld_b128(rx, lane_off, (uint32_t)(i * C * (int)sizeof(TT)));
+}
+
+// Valid rows of a step (full steps, then the ragged one, then none), written
+// with compares and selects only so that it stays a scalar.
+__device__ __forceinline__ int step_rows(int step, int full, int tail) {
+  return step < full ? PTL * TM : (step == full ? tail : 0);
+}
+
+// The slice's packed routing fragments -> LDS (zero for blocks past C).
+template <int N, int NTF>
+__device__ __forceinline__ void load_wslice(u32x4_t (&s_w)[PSB][N][NTF][WAVE], const uint4* wfull, int nkbC, int slice,
+                                            int tid) {
+  constexpr int TOT = PSB * N * NTF * WAVE;
+  constexpr int IT = (TOT + PNTHR - 1) / PNTHR;
+  u32x4_t v[IT];
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int u = tid + k * PNTHR;
+    const int l = u % WAVE, n = (u / WAVE) % NTF, i = (u / (WAVE * NTF)) % N, c = u / (WAVE * NTF * N);
+    const int kb = slice * PSB + c;
+    v[k] = u32x4_t{0u, 0u, 0u, 0u};
+    if (u < TOT && kb < nkbC)
+      v[k] = ld16v(wfull + (((size_t)i * nkbC + kb) * NTF + n) * WAVE + l);
+  }
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int u = tid + k * PNTHR;
+    if (u < TOT) (&s_w[0][0][0][0])[u] = v[k];
+  }
+}
+
+// Column sums of the slice's W_r (every routing partial carries them), summed
+// over the blocks in a fixed order.  Uses s_red as scratch; ends synchronized.
+template <class E, int N, int NTF, int PM>
+__device__ __forceinline__ void slice_colsums(const u32x4_t (&s_w)[PSB][N][NTF][WAVE], float (&s_red)[TWV][PM],
+                                              float* s_acs, int tid, int wave, int lane) {
+  if (wave < PSB) {
+    const u32x4_t ones = ones_frag<E>();
+    f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) acs = E::mma(acs, ones, s_w[wave][i][0][lane]);
+    if (lane < 16) s_red[wave][lane] = acs[0];
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float v = 0.f;
+#pragma unroll
+    for (int c = 0; c < PSB; ++c) v += s_red[c][tid];
+    s_acs[tid] = v;
+  }
+  __syncthreads();
+}
+
+// Next-layer routing projection of one tile (rows in amask masked to zero),
+// with the sums of x and x^2, B operands from LDS.
+template <class E, int N, int NTF>
+__device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)[N][NTF][WAVE], int lane, uint32_t amask,
+                                          f32x4_t (&acc)[NTF], f32x4_t& S1, f32x4_t& S2) {
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  const u32x4_t ones = ones_frag<E>();
+#pragma unroll
+  for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  S1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  S2 = S1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const u32x4_t v = ((amask >> i) & 1u) ? zero : xs.x[i];
+    mma_sums<E>(v, ones, S1, S2);
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, w[i][n][lane]);
+  }
+}
+
+// Routing partials of the step's PTL tiles: each wave's block to LDS, then
+// per tile the sum over its PSB blocks in order, plus the slice's column sums.
+template <int N, int PM>
+__device__ __forceinline__ void route_partials(float (&s_red)[TWV][PM], const float* s_acs, const f32x4_t (&acc)[RouteDims<N>::NTF],
+                                               const f32x4_t& S1, const f32x4_t& S2, float* dst, int G, int slice,
+                                               int step, int ntiles, int tid, int wave, int g, int r) {
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
+  sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+  __syncthreads();
+  constexpr int IT = (PTL * P1 + PNTHR - 1) / PNTHR;
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int u = tid + k * PNTHR;
+    if (u < PTL * P1) {
+      const int bb = u / P1, v = u % P1;
+      const int tile = PTL * step + bb;
+      float x;
+      if (v < NSUM) {
+        x = 0.f;
+#pragma unroll
+        for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+      } else {
+        x = s_acs[v - NSUM];
+      }
+      if (tile < ntiles) dst[((size_t)tile * G + slice) * P1 + v] = x;
+    }
+  }
+  __syncthreads();
+}
+
+struct ProjPArgs {
+  const void* X;
+  int T, C, G, ntiles;
+  const uint4* wfull;
+  float* part;
+};
+
+// Routing projection of a whole state (first layer of a chain).
+template <class E, int N>
+__global__ __launch_bounds__(PNTHR, 1) void xhc_proj_p_kernel(ProjPArgs a) {
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NSUM = D::NSUM;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  __shared__ u32x4_t s_w[PSB][N][NTF][WAVE];
+  __shared__ float s_red[TWV][NSUM];
+  __shared__ float s_acs[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform, so tile resources stay scalar
+  const int b = wave / PSB, cb = wave % PSB;
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int nsteps = (a.ntiles + PTL - 1) / PTL;
+  const int kb0 = slice * PSB + cb;
+  const uint32_t lane_off =
+      kb0 < nkbC ? (uint32_t)(((size_t)(TM * b + r) * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
+  const T* X = reinterpret_cast<const T*>(a.X);
+  const int full = a.T / (PTL * TM), tail = a.T % (PTL * TM);
+
+  XTile<N> xa, xb;
+  int p = team;
+  load_xtile<E, N>(xa, X, C, p, step_rows(p, full, tail), lane_off);
+  load_wslice<N, NTF>(s_w, a.wfull, nkbC, slice, tid);
+  __syncthreads();
+  slice_colsums<E, N, NTF>(s_w, s_red, s_acs, tid, wave, lane);
+
+  f32x4_t acc[NTF], S1, S2;
+  while (p < nsteps) {
+    // the next step's loads are always issued (past the end they read
+    // nothing), so the waits of this step never cover them
+    const int p1 = p + nteams;
+    load_xtile<E, N>(xb, X, C, p1, step_rows(p1, full, tail), lane_off);
+    __builtin_amdgcn_sched_barrier(0);
+    route_mma<E, N, NTF>(xa, s_w[cb], lane, 0u, acc, S1, S2);
+    route_partials<N>(s_red, s_acs, acc, S1, S2, a.part, G, slice, p, a.ntiles, tid, wave, g, r);
+    if (p1 >= nsteps) break;
+    const int p2 = p1 + nteams;
+    load_xtile<E, N>(xa, X, C, p2, step_rows(p2, full, tail), lane_off);
+    __builtin_amdgcn_sched_barrier(0);
+    route_mma<E, N, NTF>(xb, s_w[cb], lane, 0u, acc, S1, S2);
+    route_partials<N>(s_red, s_acs, acc, S1, S2, a.part, G, slice, p1, a.ntiles, tid, wave, g, r);
+    p = p2;
+  }
+}
+
+// Chained pre pass of a layer that has a next layer (dense read, gather +
+// active partials of this layer, masked routing partials of the next one).
+// The routing of the next step (h_pre rows, then active lists) is loaded by
+// the first RQ threads along with the state and moved to LDS after compute.
+template <class E, int N, int K, int KR>
+__global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArgs a) {
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  using A = ActDims<K, KR>;
+  constexpr int NTF = D::NTF, NSUM = D::NSUM;
+  constexpr int NTA = A::NTA, NPA = A::NPA, P2 = A::P2;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  constexpr int PM = NSUM > P2 ? NSUM : P2;
+  constexpr int HW = PTL * TM * N;        // h_pre words of a step
+  constexpr int RW = HW + PTL * TM * K;   // + active-list words
+  constexpr int HQ = HW / 4, RQ = RW / 4; // in 16-byte units
+  static_assert(HW % 4 == 0 && RW % 4 == 0 && RQ <= PNTHR, "routing rows of a step in 16-byte units");
+  __shared__ u32x4_t s_w[PSB][N][NTF][WAVE];
+  __shared__ float s_red[TWV][PM];
+  __shared__ float s_acs[16];
+  __shared__ u32x4_t s_rt[2][RQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform, so tile resources stay scalar
+  const int b = wave / PSB, cb = wave % PSB;
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int nsteps = (a.ntiles + PTL - 1) / PTL;
+  const int kb0 = slice * PSB + cb;
+  const bool kvalid = kb0 < nkbC;
+  const uint32_t lane_off =
+      kvalid ? (uint32_t)(((size_t)(TM * b + r) * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
+  const T* X = reinterpret_cast<const T*>(a.X);
+  const int full = a.T / (PTL * TM), tail = a.T % (PTL * TM);
+
+  auto load_route = [&](int step) {
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    const int valid = step_rows(step, full, tail);
+    const int ts = valid > 0 ? PTL * TM * step : 0;
+    if (wave * WAVE < RQ) {
+      // both loads with scalar resources; a lane reads one of them, the other
+      // offset is out of range
+      const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h_pre + (size_t)ts * N, (uint32_t)(valid * N * 4));
+      const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.idx + (size_t)ts * K, (uint32_t)(valid * K * 4));
+      const u32x4_t vh = ld_b128(rh, tid < HQ ? (uint32_t)(tid * 16) : OUT_OF_RANGE, 0);
+      const u32x4_t vi = ld_b128(ri, tid >= HQ && tid < RQ ? (uint32_t)((tid - HQ) * 16) : OUT_OF_RANGE, 0);
+      v = tid < HQ ? vh : vi;
+    }
+    return v;
+  };
+
+  // this layer's active weights of the wave's block, loaded at the start of
+  // each step ahead of the state prefetch (so they arrive with the current
+  // state) and used by the gather before the routing MFMAs
+  const __amdgpu_buffer_rsrc_t rwa = make_rsrc(a.wact, (uint32_t)((size_t)K * nkbC * NTA * WAVE * 16));
+  const uint32_t vwa = kvalid ? (uint32_t)(((size_t)kb0 * NTA * WAVE + lane) * 16) : OUT_OF_RANGE;
+  u32x4_t wa[K][NTA];
+  auto load_wact = [&]() {
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+      for (int n = 0; n < NTA; ++n)
+        wa[j][n] = ld_b128(rwa, vwa + n * WAVE * 16, (uint32_t)j * nkbC * NTA * WAVE * 16);
+  };
+  XTile<N> xa, xb;
+  int p = team;
+  u32x4_t rt = load_route(p);
+  load_xtile<E, N>(xa, X, C, p, step_rows(p, full, tail), lane_off);
+  load_wslice<N, NTF>(s_w, a.wnext, nkbC, slice, tid);
+  if (tid < RQ) s_rt[0][tid] = rt;
+  __syncthreads();
+  slice_colsums<E, N, NTF>(s_w, s_red, s_acs, tid, wave, lane);
+
+  auto compute = [&](const XTile<N>& xs, int step, int buf, const u32x4_t& rnext) {
+    const int tile = PTL * step + b;
+    const int tok = TM * tile + r;
+    const uint32_t* rw = reinterpret_cast<const uint32_t*>(&s_rt[buf][0]);
+    int I[K];
+    uint32_t amask = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int v = (int)rw[HW + (b * TM + r) * K + j];
+      v = v < 0 ? 0 : (v >= N ? N - 1 : v);
+      I[j] = v;
+      amask |= 1u << v;
+    }
+    // dense read over all N streams -> sublayer input
+    if (kvalid) {
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const float hpi = __uint_as_float(rw[(b * TM + r) * N + i]);
+        float f[VEC];
+        E::unpack(xs.x[i], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = fmaf(hpi, f[e], o[e]);
+      }
+      if (tile < a.ntiles && tok < a.T)
+        st16_nt(reinterpret_cast<T*>(a.inp) + (size_t)tok * C + kb0 * KB + VEC * g, E::packv(o));
+    }
+    // the next step's routing to the other buffer (every wave has finished
+    // reading it before the last barrier of the previous step)
+    if (tid < RQ) s_rt[buf ^ 1][tid] = rnext;
+    // gather of the k active rows, their sum of squares and active projection
+    f32x4_t acc2[NTA], SS = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NTA; ++n) acc2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      // position j < m holds stream j; a routed position holds one of m..N-1
+      u32x4_t v = xs.x[j < N ? j : 0];
+      if (j >= a.m) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+          if (i != j) v = (I[j] == i) ? xs.x[i] : v;
+      }
+      SS = E::mma(SS, v, v);
+#pragma unroll
+      for (int n = 0; n < NTA; ++n) acc2[n] = E::mma(acc2[n], v, wa[j][n]);
+    }
+    // next layer's routing over the rows this layer leaves as they are
+    f32x4_t acc[NTF], S1, S2;
+    route_mma<E, N, NTF>(xs, s_w[cb], lane, amask, acc, S1, S2);
+    route_partials<N>(s_red, s_acs, acc, S1, S2, a.look, G, slice, step, a.ntiles, tid, wave, g, r);
+    acc_to_lds<NTA, NPA>(s_red, wave, g, r, acc2);
+    if ((r >> 2) == g) s_red[wave][TM * NPA + r] = diag_of(SS, r);
+    __syncthreads();
+    constexpr int IT = (PTL * P2 + PNTHR - 1) / PNTHR;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int u = tid + k * PNTHR;
+      if (u < PTL * P2) {
+        const int bb = u / P2, v = u % P2;
+        const int t16 = PTL * step + bb;
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+        if (t16 < a.ntiles) a.part2[((size_t)t16 * G + slice) * P2 + v] = x;
+      }
+    }
+    __syncthreads();
+  };
+
+  while (p < nsteps) {
+    const int p1 = p + nteams;
+    load_wact();
+    rt = load_route(p1);
+    load_xtile<E, N>(xb, X, C, p1, step_rows(p1, full, tail), lane_off);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xa, p, 0, rt);
+    if (p1 >= nsteps) break;
+    const int p2 = p1 + nteams;
+    load_wact();
+    rt = load_route(p2);
+    load_xtile<E, N>(xa, X, C, p2, step_rows(p2, full, tail), lane_off);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(xb, p1, 1, rt);
+    p = p2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 namespace {
 
+#ifndef XHC_PRE_RB
+#define XHC_PRE_RB 1
+#endif
+constexpr int PRE_RB = XHC_PRE_RB;   // 16-token row blocks per chained pre workgroup
 #ifndef XHC_CORR_RB
 #define XHC_CORR_RB 4
 #endif
 constexpr int CORR_RB = XHC_CORR_RB;
 
+// Workgroups of a persistent launch: one per compute unit (their LDS allows
+// no more), Gp slices per team, no more teams than steps.
+int persist_grid(const Plan& P) {
+  static int ncu[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (ncu[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    ncu[dev] = v;
+  }
+  const long nsteps = (P.ntiles + PTL - 1) / PTL;
+  long teams = ncu[dev] / P.Gp;
+  if (teams < 1) teams = 1;
+  if (teams > nsteps) teams = nsteps;
+  if (teams < 1) teams = 1;
+  return (int)(teams * P.Gp);
+}
+
 template <class E, int N, int K, int KR>
 void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, const void* X, void* inp, char* ws,
                         char* wsn, hipStream_t st) {
   PreChainArgs a;
-  a.X = X; a.inp = inp; a.T = (int)P.T; a.C = P.C; a.G = P.G; a.m = P.m;
+  a.X = X; a.inp = inp; a.T = (int)P.T; a.C = P.C; a.G = P.G; a.m = P.m; a.ntiles = (int)P.ntiles;
   a.wact = reinterpret_cast<const uint4*>(ws + P.o_wact);
   a.wnext = Pn ? reinterpret_cast<const uint4*>(wsn + Pn->o_wfull) : nullptr;
   a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
   a.h_pre = reinterpret_cast<const float*>(ws + P.o_hpre);
   a.part2 = reinterpret_cast<float*>(ws + P.o_part2);
   a.look = Pn ? reinterpret_cast<float*>(wsn + Pn->o_part) : nullptr;
-  const unsigned grid = (unsigned)(P.ntiles * P.G);
-  if (Pn)
-    xhc_pre_chained_kernel<E, N, K, KR, true><<<grid, NTHR, 0, st>>>(a);
-  else
-    xhc_pre_chained_kernel<E, N, K, KR, false><<<grid, NTHR, 0, st>>>(a);
+  constexpr int RB = PRE_RB;
+  int Gpart;   // slices of the active partials
+  if (Pn) {
+    // persistent: routing weights of the next layer resident in LDS
+    a.G = P.Gp;
+    Gpart = P.Gp;
+    xhc_pre_chained_p_kernel<E, N, K, KR><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
+  } else {
+    Gpart = P.G;
+    const unsigned grid = (unsigned)(((P.T + TM * RB - 1) / (TM * RB)) * P.G);
+    xhc_pre_chained_kernel<E, N, K, KR, false, RB><<<grid, NTHR, 0, st>>>(a);
+  }
 
   ActFinArgs f;
-  f.T = (int)P.T; f.C = P.C; f.G = P.G; f.ntiles = (int)P.ntiles;
+  f.T = (int)P.T; f.C = P.C; f.G = Gpart; f.ntiles = (int)P.ntiles;
   f.part2 = a.part2;
   f.b_res = w->b_res; f.b_post = w->b_post;
   f.a_res = w->alpha_res; f.a_post = w->alpha_post; f.eps = P.eps_norm; f.iters = P.iters;
@@ -678,7 +1115,9 @@ void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, con
 template <int N, int K>
 void route_fin_launch(const Plan& P, const xhc_weights* w, char* ws, bool with_corr, hipStream_t st) {
   RouteFinArgs f;
-  f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.G;
+  // routing partials come from the persistent kernels, corrections from the
+  // correction kernel
+  f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.Gp; f.Gc = P.G;
   f.part = reinterpret_cast<const float*>(ws + P.o_part);
   f.corr = with_corr ? reinterpret_cast<const float*>(ws + P.o_corr) : nullptr;
   f.b_pre = w->b_pre; f.a_pre = w->alpha_pre; f.eps = P.eps_norm;
@@ -691,11 +1130,11 @@ void route_fin_launch(const Plan& P, const xhc_weights* w, char* ws, bool with_c
 
 template <class E, int N, int K>
 void route_launch(const Plan& P, const xhc_weights* w, const void* X, char* ws, hipStream_t st) {
-  ProjArgs a;
-  a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.G;
+  ProjPArgs a;
+  a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
   a.wfull = reinterpret_cast<const uint4*>(ws + P.o_wfull);
   a.part = reinterpret_cast<float*>(ws + P.o_part);
-  xhc_proj_kernel<E, N><<<(unsigned)(P.ntiles * P.G), NTHR, 0, st>>>(a);
+  xhc_proj_p_kernel<E, N><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
   route_fin_launch<N, K>(P, w, ws, false, st);
 }
 

@@ -31,6 +31,7 @@ struct Plan {
   bool mhc_gemm = false;            // mHC: projection by a library GEMM (wide maps)
   int nslices = 1;                  // channel slices of the post kernels
   int G = 1;                        // xHC pre: workgroups (channel slices) per 16-token tile
+  int Gp = 1;                       // xHC chained: channel slices of the persistent kernels
   long ntiles = 0;                  // xHC pre: 16-token tiles
   // workspace byte offsets
   size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,

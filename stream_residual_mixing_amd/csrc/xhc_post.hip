@@ -353,7 +353,9 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
           for (int v = 0; v < KR; ++v) s = fmaf(s_Q[tau][j][v], b[v][e], s);
           nv[e] = s;
         }
-        *reinterpret_cast<typename Qd::V*>(X + ((size_t)t * a.N + s_I[tau][j]) * a.C + c) = Qd::pack(nv);
+        // streaming store: nothing reads the rewritten rows again in this pass
+        __builtin_nontemporal_store(Qd::pack(nv),
+                                    reinterpret_cast<typename Qd::V*>(X + ((size_t)t * a.N + s_I[tau][j]) * a.C + c));
       }
     }
   }
