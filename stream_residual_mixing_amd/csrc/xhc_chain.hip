@@ -895,14 +895,16 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
   constexpr int NTA = A::NTA, NPA = A::NPA, P2 = A::P2;
   constexpr int KB = E::KB, VEC = E::VEC;
   constexpr int PM = NSUM > P2 ? NSUM : P2;
-  constexpr int HW = PTL * TM * N;        // h_pre words of a step
-  constexpr int RW = HW + PTL * TM * K;   // + active-list words
-  constexpr int HQ = HW / 4, RQ = RW / 4; // in 16-byte units
-  static_assert(HW % 4 == 0 && RW % 4 == 0 && RQ <= PNTHR, "routing rows of a step in 16-byte units");
+  // routing rows of a step in 16-byte units: h_pre rows (whole waves WH)
+  // then active lists (waves WI), each wave loading 64 units
+  constexpr int HQ = PTL * TM * N / 4, IQ = PTL * TM * K / 4;
+  constexpr int WH = (HQ + WAVE - 1) / WAVE, WI = (IQ + WAVE - 1) / WAVE;
+  static_assert((PTL * TM * N) % 4 == 0 && (PTL * TM * K) % 4 == 0 && WH + WI <= TWV, "routing rows of a step");
   __shared__ u32x4_t s_w[PSB][N][NTF][WAVE];
   __shared__ float s_red[TWV][PM];
   __shared__ float s_acs[16];
-  __shared__ u32x4_t s_rt[2][RQ];
+  __shared__ u32x4_t s_rh[2][WH * WAVE];
+  __shared__ u32x4_t s_ri[2][WI * WAVE];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform, so tile resources stay scalar
@@ -917,25 +919,31 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
   const T* X = reinterpret_cast<const T*>(a.X);
   const int full = a.T / (PTL * TM), tail = a.T % (PTL * TM);
 
+  // The step's routing rows; which array a wave loads is wave-uniform, so no
+  // lane waits for its data before the state prefetch is issued.  Units past
+  // the valid rows read zeros.
   auto load_route = [&](int step) {
     u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
     const int valid = step_rows(step, full, tail);
     const int ts = valid > 0 ? PTL * TM * step : 0;
-    if (wave * WAVE < RQ) {
-      // both loads with scalar resources; a lane reads one of them, the other
-      // offset is out of range
+    if (wave < WH) {
       const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h_pre + (size_t)ts * N, (uint32_t)(valid * N * 4));
+      v = ld_b128(rh, (uint32_t)((wave * WAVE + lane) * 16), 0);
+    } else if (wave < WH + WI) {
       const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.idx + (size_t)ts * K, (uint32_t)(valid * K * 4));
-      const u32x4_t vh = ld_b128(rh, tid < HQ ? (uint32_t)(tid * 16) : OUT_OF_RANGE, 0);
-      const u32x4_t vi = ld_b128(ri, tid >= HQ && tid < RQ ? (uint32_t)((tid - HQ) * 16) : OUT_OF_RANGE, 0);
-      v = tid < HQ ? vh : vi;
+      v = ld_b128(ri, (uint32_t)(((wave - WH) * WAVE + lane) * 16), 0);
     }
     return v;
   };
+  auto store_route = [&](int buf, const u32x4_t& v) {
+    if (wave < WH)
+      s_rh[buf][wave * WAVE + lane] = v;
+    else if (wave < WH + WI)
+      s_ri[buf][(wave - WH) * WAVE + lane] = v;
+  };
 
-  // this layer's active weights of the wave's block, loaded at the start of
-  // each step ahead of the state prefetch (so they arrive with the current
-  // state) and used by the gather before the routing MFMAs
+  // this layer's active weights of the wave's block, loaded once and held in
+  // registers for the whole launch
   const __amdgpu_buffer_rsrc_t rwa = make_rsrc(a.wact, (uint32_t)((size_t)K * nkbC * NTA * WAVE * 16));
   const uint32_t vwa = kvalid ? (uint32_t)(((size_t)kb0 * NTA * WAVE + lane) * 16) : OUT_OF_RANGE;
   u32x4_t wa[K][NTA];
@@ -948,22 +956,24 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
   };
   XTile<N> xa, xb;
   int p = team;
+  load_wact();
   u32x4_t rt = load_route(p);
   load_xtile<E, N>(xa, X, C, p, step_rows(p, full, tail), lane_off);
   load_wslice<N, NTF>(s_w, a.wnext, nkbC, slice, tid);
-  if (tid < RQ) s_rt[0][tid] = rt;
+  store_route(0, rt);
   __syncthreads();
   slice_colsums<E, N, NTF>(s_w, s_red, s_acs, tid, wave, lane);
 
   auto compute = [&](const XTile<N>& xs, int step, int buf, const u32x4_t& rnext) {
     const int tile = PTL * step + b;
     const int tok = TM * tile + r;
-    const uint32_t* rw = reinterpret_cast<const uint32_t*>(&s_rt[buf][0]);
+    const uint32_t* rh = reinterpret_cast<const uint32_t*>(&s_rh[buf][0]);
+    const uint32_t* ri = reinterpret_cast<const uint32_t*>(&s_ri[buf][0]);
     int I[K];
     uint32_t amask = 0;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      int v = (int)rw[HW + (b * TM + r) * K + j];
+      int v = (int)ri[(b * TM + r) * K + j];
       v = v < 0 ? 0 : (v >= N ? N - 1 : v);
       I[j] = v;
       amask |= 1u << v;
@@ -975,7 +985,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
       for (int e = 0; e < VEC; ++e) o[e] = 0.f;
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const float hpi = __uint_as_float(rw[(b * TM + r) * N + i]);
+        const float hpi = __uint_as_float(rh[(b * TM + r) * N + i]);
         float f[VEC];
         E::unpack(xs.x[i], f);
 #pragma unroll
@@ -986,7 +996,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
     }
     // the next step's routing to the other buffer (every wave has finished
     // reading it before the last barrier of the previous step)
-    if (tid < RQ) s_rt[buf ^ 1][tid] = rnext;
+    store_route(buf ^ 1, rnext);
     // gather of the k active rows, their sum of squares and active projection
     f32x4_t acc2[NTA], SS = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1029,14 +1039,12 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 
   while (p < nsteps) {
     const int p1 = p + nteams;
-    load_wact();
     rt = load_route(p1);
     load_xtile<E, N>(xb, X, C, p1, step_rows(p1, full, tail), lane_off);
     __builtin_amdgcn_sched_barrier(0);
     compute(xa, p, 0, rt);
     if (p1 >= nsteps) break;
     const int p2 = p1 + nteams;
-    load_wact();
     rt = load_route(p2);
     load_xtile<E, N>(xa, X, C, p2, step_rows(p2, full, tail), lane_off);
     __builtin_amdgcn_sched_barrier(0);
