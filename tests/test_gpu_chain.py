@@ -61,3 +61,28 @@ def test_chain_single_sublayer_without_next(lib):
 def test_chain_many_tiles_c4096(lib):
     """3 sublayers A M A at C=4096 (16 channel slices), 1 x 160 tokens, bf16."""
     run_chain(lib, K.chain_configs(16, 4, 2, 4096, 1, 160, "AMA"), seed=24, margin=K.CHAIN_MARGIN)
+
+
+# The persistent kernels run one workgroup per compute unit: a team of one
+# workgroup per 128-channel slice (64 in fp32) walks steps of 32 tokens.  With
+# wide C there are few teams, so each walks several steps, through both of its
+# register sets and both routing buffers, up to a ragged last step.
+
+@pytest.mark.timeout(300)
+def test_chain_one_team_many_steps_c32768(lib):
+    """2 sublayers A M, N=16, k=4, m=2, C=32768 (256 slices: a single team
+    walks all 4 steps of 1 x 100 tokens), bf16."""
+    run_chain(lib, K.chain_configs(16, 4, 2, 32768, 1, 100, "AM"), seed=25, margin=K.CHAIN_MARGIN)
+
+
+@pytest.mark.timeout(300)
+def test_chain_several_steps_per_team_c8192(lib):
+    """2 sublayers M A, N=16, k=4, m=2, C=8192 (4 teams, 10 steps of 2 x 150
+    tokens, a sequence start inside a step), bf16."""
+    run_chain(lib, K.chain_configs(16, 4, 2, 8192, 2, 150, "MA"), seed=26, margin=K.CHAIN_MARGIN)
+
+
+def test_chain_f32_several_steps_per_team_c4096(lib):
+    """3 sublayers M A M, N=16, k=4, m=2, C=4096 in fp32 (64 slices: 4 teams,
+    10 steps of 1 x 300 tokens)."""
+    run_chain(lib, K.chain_configs(16, 4, 2, 4096, 1, 300, "MAM", dtype="f32"), seed=27, margin=K.MARGIN)
