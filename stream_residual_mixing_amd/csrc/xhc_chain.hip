@@ -40,11 +40,10 @@ namespace xhc {
 namespace {
 
 constexpr int NTHR = TNTHR;
-constexpr int WD = 4;   // items of weight fragments in flight ahead of the MFMAs
 #ifndef XHC_PRE_WD
 #define XHC_PRE_WD 2
 #endif
-constexpr int WDP = XHC_PRE_WD;   // the same for the chained pre kernel (holds more)
+constexpr int WDP = XHC_PRE_WD;   // weight items in flight ahead of the MFMAs (last-sublayer pre kernel)
 #ifndef XHC_CORR_WD
 #define XHC_CORR_WD 2
 #endif
@@ -116,78 +115,6 @@ __device__ __forceinline__ void acc_to_lds(float (&dst)[TWV][PM], int wave, int 
 }
 
 }  // namespace
-
-// ---------------------------------------------------------------------------
-// Routing projection of a whole state (first layer of a chain): per 16-token
-// tile and channel slice, vec X . [W_r | W_pre], sum x, sum x^2 and the column
-// sums of W_r, over this slice's channels of all N streams.
-// ---------------------------------------------------------------------------
-struct ProjArgs {
-  const void* X;
-  int T, C, G;
-  const uint4* wfull;
-  float* part;
-};
-
-template <class E, int N>
-__global__ __launch_bounds__(NTHR, 4) void xhc_proj_kernel(ProjArgs a) {
-  using T = typename E::T;
-  using D = RouteDims<N>;
-  constexpr int NTF = D::NTF, NPF = D::NPF, P1 = D::P1;
-  constexpr int KB = E::KB, VEC = E::VEC;
-  __shared__ float s_red[TWV][P1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
-  const int C = a.C, G = a.G, nkbC = C / KB;
-  const int tile = blockIdx.x / G, slice = blockIdx.x % G;
-  const int t0 = tile * TM;
-  const int rows = a.T - t0 < TM ? a.T - t0 : TM;
-  const int kb0 = slice * TWV + wave;
-  const bool kvalid = kb0 < nkbC;
-
-  const __amdgpu_buffer_rsrc_t rwf = make_rsrc(a.wfull, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
-  const uint32_t vwf = kvalid ? (uint32_t)(((size_t)kb0 * NTF * WAVE + lane) * 16) : OUT_OF_RANGE;
-  const uint32_t wf_stream = (uint32_t)nkbC * NTF * WAVE * 16;
-  u32x4_t wb[WD][NTF];
-#pragma unroll
-  for (int d = 0; d < WD && d < N; ++d)
-#pragma unroll
-    for (int n = 0; n < NTF; ++n) wb[d][n] = ld_b128(rwf, vwf + n * WAVE * 16, d * wf_stream);
-  __builtin_amdgcn_sched_barrier(0);
-
-  const __amdgpu_buffer_rsrc_t rx =
-      make_rsrc(reinterpret_cast<const T*>(a.X) + (size_t)t0 * N * C, (uint32_t)((size_t)rows * N * C * sizeof(T)));
-  const uint32_t vx = kvalid ? (uint32_t)(((size_t)r * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
-  u32x4_t xd[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) xd[i] = ld_b128(rx, vx, (uint32_t)(i * C * (int)sizeof(T)));
-  __builtin_amdgcn_sched_barrier(0);
-
-  f32x4_t acc[NTF];
-#pragma unroll
-  for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
-  const u32x4_t ones = ones_frag<E>();
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    mma_sums<E>(xd[i], ones, S1, S2);
-#pragma unroll
-    for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], xd[i], wb[i % WD][n]);
-    acs = E::mma(acs, ones, wb[i % WD][0]);
-    if (i + WD < N) {
-#pragma unroll
-      for (int n = 0; n < NTF; ++n) wb[i % WD][n] = ld_b128(rwf, vwf + n * WAVE * 16, (i + WD) * wf_stream);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
-  sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
-  if (g == 0) s_red[wave][TM * NPF + 2 * TM + r] = acs[0];
-  __syncthreads();
-  float* dst = a.part + (size_t)blockIdx.x * P1;
-  for (int u = tid; u < P1; u += NTHR) dst[u] = sum_waves(s_red, u);
-}
 
 // ---------------------------------------------------------------------------
 // Routing of a tile from the summed partials: the G routing partials of the
