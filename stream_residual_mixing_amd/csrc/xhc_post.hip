@@ -25,6 +25,8 @@
 // channels in registers and slides along the tokens of its block, so `out`
 // is read once per pass (plus an 11-row history at the start of a block).
 // Attention-type sublayers (K_r = 1) skip the first pass.
+#include <type_traits>
+
 #include "xhc_device.hpp"
 #include "xhc_internal.hpp"
 
@@ -56,52 +58,72 @@ __device__ __forceinline__ void load_conv_weights(const float* __restrict__ cw, 
   }
 }
 
-// Start of a block, before its first token t0 (position s0 in its sequence)
-// is pushed: h[i] = out[t0 - 1 - i] for the rows inside that sequence, zero
-// before its start, so that after the push h[i] = out[t0 - i].
+// The history of `out` is a ring of HL = 12 rows (the longest conv kernel).
+// Tokens are taken in periods of HL, unrolled, so every index below is a
+// constant: the token at position q of a period writes its row to slot q,
+// and its lag-i row sits in slot (q - i) mod HL.  Nothing is shifted.
+constexpr int HL = 12;
+
+// Start of a block, before its first token t0 (position s0 in its sequence):
+// lag-(i+1) rows out[t0 - 1 - i] inside that sequence go to slot HL - 1 - i,
+// zero before its start.
 template <class E>
 __device__ __forceinline__ void load_history(const typename E::T* __restrict__ out, int t0, int s0, int C, int c,
-                                             bool act, float (&h)[12][4]) {
-  typename Quad<E>::V v[11];
+                                             bool act, float (&h)[HL][4]) {
+  typename Quad<E>::V v[HL - 1];
 #pragma unroll
-  for (int i = 0; i < 11; ++i) {
+  for (int i = 0; i < HL - 1; ++i) {
     if (act && i + 1 <= s0) v[i] = ldq<E>(out + (size_t)(t0 - 1 - i) * C + c);
     else v[i] = typename Quad<E>::V{};
   }
 #pragma unroll
-  for (int i = 0; i < 11; ++i) Quad<E>::unpack(v[i], h[i]);
+  for (int i = 0; i < HL - 1; ++i) Quad<E>::unpack(v[i], h[HL - 1 - i]);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) h[11][e] = 0.f;
+  for (int e = 0; e < 4; ++e) h[0][e] = 0.f;
 }
 
-// Move to the next token (position s): shift the history by one, drop it
-// entirely at a sequence start, and insert the token's own row at lag 0.
-__device__ __forceinline__ void push_history(float (&h)[12][4], const float (&row)[4], int s) {
+// Token at position Q of a period (position s in its sequence): a sequence
+// start clears the history (block-uniform branch), then its row takes slot Q.
+template <int Q>
+__device__ __forceinline__ void push_history(float (&h)[HL][4], const float (&row)[4], int s) {
+  if (s == 0) {
+    asm volatile("");   // keeps this a (rare, uniform) branch rather than 48 selects per token
 #pragma unroll
-  for (int i = 11; i >= 1; --i)
+    for (int i = 0; i < HL; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[i][e] = s == 0 ? 0.f : h[i - 1][e];
+      for (int e = 0; e < 4; ++e) h[i][e] = 0.f;
+  }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) h[0][e] = row[e];
+  for (int e = 0; e < 4; ++e) h[Q][e] = row[e];
 }
 
-// Basis [out, g1, g2, g3] for this thread's 4 channels from the history:
+// Basis [out, g1, g2, g3] for this thread's 4 channels, token at position Q:
 // g_j = sum_{i < kappa_j} w_j[i] * out[t - i] (lag i; kappa = 4, 8, 12).
-__device__ __forceinline__ void conv_basis(const float (&h)[12][4], const float (&w1)[4][4],
+template <int Q>
+__device__ __forceinline__ void conv_basis(const float (&h)[HL][4], const float (&w1)[4][4],
                                            const float (&w2)[8][4], const float (&w3)[12][4], float (&b)[4][4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    b[0][e] = h[0][e];
+    b[0][e] = h[Q][e];
     float g1 = 0.f, g2 = 0.f, g3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) g1 = fmaf(w1[i][e], h[i][e], g1);
+    for (int i = 0; i < 4; ++i) g1 = fmaf(w1[i][e], h[(Q - i + HL) % HL][e], g1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g2 = fmaf(w2[i][e], h[i][e], g2);
+    for (int i = 0; i < 8; ++i) g2 = fmaf(w2[i][e], h[(Q - i + HL) % HL][e], g2);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) g3 = fmaf(w3[i][e], h[i][e], g3);
+    for (int i = 0; i < 12; ++i) g3 = fmaf(w3[i][e], h[(Q - i + HL) % HL][e], g3);
     b[1][e] = g1;
     b[2][e] = g2;
     b[3][e] = g3;
+  }
+}
+
+// Calls f(std::integral_constant<int, Q>) for Q = 0 .. HL - 1.
+template <int Q = 0, class F>
+__device__ __forceinline__ void for_period(F&& f) {
+  if constexpr (Q < HL) {
+    f(std::integral_constant<int, Q>{});
+    for_period<Q + 1>(f);
   }
 }
 
@@ -176,7 +198,8 @@ __device__ __forceinline__ void mgs_from_gram(const float (&G)[4][4], float eps,
   }
 }
 
-constexpr int GB = 8;   // tokens per load batch in the Gram pass
+constexpr int GB = 4;   // tokens per load batch in the Gram pass (HL is a multiple)
+static_assert(HL % GB == 0, "load batches tile a history period");
 
 }  // namespace
 
@@ -197,40 +220,47 @@ __global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
 
   float w1[4][4], w2[8][4], w3[12][4];
   load_conv_weights(a.conv_w, a.C, cc, act, w1, w2, w3);
-  float h[12][4];
+  float h[HL][4];
   load_history<E>(out, t0, t0 % a.S, a.C, cc, act, h);
   const int myidx = wave_sum16_index(lane);
 
-  for (int tb = t0; tb < t1; tb += GB) {
+  // sequence position of the next token, kept in a scalar register so that
+  // the clearing at a sequence start is a branch, not per-element selects
+  int s = __builtin_amdgcn_readfirstlane(t0 % a.S);
+  for (int tp = t0; tp < t1; tp += HL) {
     typename Qd::V rows[GB];
+    for_period([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      const int t = tp + q;
+      if constexpr (q % GB == 0) {
 #pragma unroll
-    for (int q = 0; q < GB; ++q)
-      rows[q] = (act && tb + q < t1) ? ldq<E>(out + (size_t)(tb + q) * a.C + cc) : typename Qd::V{};
+        for (int u = 0; u < GB; ++u)
+          rows[u] = (act && t + u < t1) ? ldq<E>(out + (size_t)(t + u) * a.C + cc) : typename Qd::V{};
+      }
+      if (t < t1) {
+        float r[4];
+        Qd::unpack(rows[q % GB], r);
+        push_history<q>(h, r, s);
+        s = s + 1 == a.S ? 0 : s + 1;
+        float b[4][4];
+        conv_basis<q>(h, w1, w2, w3, b);
+        float pr[16];
+        int k = 0;
 #pragma unroll
-    for (int q = 0; q < GB; ++q) {
-      const int t = tb + q;
-      if (t >= t1) break;
-      float r[4];
-      Qd::unpack(rows[q], r);
-      push_history(h, r, t % a.S);
-      float b[4][4];
-      conv_basis(h, w1, w2, w3, b);
-      float pr[16];
-      int k = 0;
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+          for (int v = u; v < 4; ++v) {
+            float d = 0.f;
 #pragma unroll
-        for (int v = u; v < 4; ++v) {
-          float d = 0.f;
+            for (int e = 0; e < 4; ++e) d = fmaf(b[u][e], b[v][e], d);
+            pr[k++] = d;
+          }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) d = fmaf(b[u][e], b[v][e], d);
-          pr[k++] = d;
-        }
-#pragma unroll
-      for (int j = 10; j < 16; ++j) pr[j] = 0.f;
-      const float tot = wave_sum16(pr, lane);
-      if ((lane & 3) == 0 && myidx < 10) s_g[t - t0][wave][myidx] = tot;
-    }
+        for (int j = 10; j < 16; ++j) pr[j] = 0.f;
+        const float tot = wave_sum16(pr, lane);
+        if ((lane & 3) == 0 && myidx < 10) s_g[t - t0][wave][myidx] = tot;
+      }
+    });
   }
   __syncthreads();
   for (int u = tid; u < (t1 - t0) * 10; u += 256) {
@@ -305,15 +335,30 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
   __syncthreads();
   if (!act) return;
 
-  float w1[4][4], w2[8][4], w3[12][4];
-  float h[12][4];
-  if (KR == 4) {
-    load_conv_weights(a.conv_w, a.C, c, true, w1, w2, w3);
-    load_history<E>(out, t0, t0 % a.S, a.C, c, true, h);
-  }
-  for (int tb = t0; tb < t1; tb += PB) {
-    typename Qd::V orow[PB];
-    typename Qd::V xr[PB][K];
+  // the k new rows of token t from its unpacked active rows and basis
+  auto mix_store = [&](int t, const typename Qd::V (&xq)[K], const float (&b)[KR][4]) {
+    const int tau = t - t0;
+    float xa[K][4];
+#pragma unroll
+    for (int j = 0; j < K; ++j) Qd::unpack(xq[j], xa[j]);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float nv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) sum = fmaf(s_H[tau][j][i], xa[i][e], sum);
+#pragma unroll
+        for (int v = 0; v < KR; ++v) sum = fmaf(s_Q[tau][j][v], b[v][e], sum);
+        nv[e] = sum;
+      }
+      // streaming store: nothing reads the rewritten rows again in this pass
+      __builtin_nontemporal_store(Qd::pack(nv),
+                                  reinterpret_cast<typename Qd::V*>(X + ((size_t)t * a.N + s_I[tau][j]) * a.C + c));
+    }
+  };
+  auto load_batch = [&](int tb, typename Qd::V (&orow)[PB], typename Qd::V (&xr)[PB][K]) {
 #pragma unroll
     for (int q = 0; q < PB; ++q) {
       const int t = tb + q;
@@ -323,39 +368,48 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
       for (int j = 0; j < K; ++j)
         xr[q][j] = ok ? ldq<E>(X + ((size_t)t * a.N + s_I[t - t0][j]) * a.C + c) : typename Qd::V{};
     }
-#pragma unroll
-    for (int q = 0; q < PB; ++q) {
-      const int t = tb + q;
-      if (t >= t1) break;
-      const int tau = t - t0;
-      float b[KR][4];
-      float r[4];
-      Qd::unpack(orow[q], r);
-      if constexpr (KR == 4) {
-        push_history(h, r, t % a.S);
-        conv_basis(h, w1, w2, w3, b);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[0][e] = r[e];
-      }
-      float xa[K][4];
-#pragma unroll
-      for (int j = 0; j < K; ++j) Qd::unpack(xr[q][j], xa[j]);
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        float nv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = 0.f;
-#pragma unroll
-          for (int i = 0; i < K; ++i) s = fmaf(s_H[tau][j][i], xa[i][e], s);
-#pragma unroll
-          for (int v = 0; v < KR; ++v) s = fmaf(s_Q[tau][j][v], b[v][e], s);
-          nv[e] = s;
+  };
+
+  if constexpr (KR == 4) {
+    // MLP-type: the basis needs the conv history; tokens in periods of HL
+    static_assert(HL % PB == 0, "load batches tile a history period");
+    float w1[4][4], w2[8][4], w3[12][4];
+    float h[HL][4];
+    load_conv_weights(a.conv_w, a.C, c, true, w1, w2, w3);
+    load_history<E>(out, t0, t0 % a.S, a.C, c, true, h);
+    // sequence position of the next token, kept in a scalar register so that
+  // the clearing at a sequence start is a branch, not per-element selects
+  int s = __builtin_amdgcn_readfirstlane(t0 % a.S);
+    for (int tp = t0; tp < t1; tp += HL) {
+      typename Qd::V orow[PB];
+      typename Qd::V xr[PB][K];
+      for_period([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const int t = tp + q;
+        if constexpr (q % PB == 0) load_batch(t, orow, xr);
+        if (t < t1) {
+          float r[4];
+          Qd::unpack(orow[q % PB], r);
+          push_history<q>(h, r, s);
+          s = s + 1 == a.S ? 0 : s + 1;
+          float b[KR][4];
+          conv_basis<q>(h, w1, w2, w3, b);
+          mix_store(t, xr[q % PB], b);
         }
-        // streaming store: nothing reads the rewritten rows again in this pass
-        __builtin_nontemporal_store(Qd::pack(nv),
-                                    reinterpret_cast<typename Qd::V*>(X + ((size_t)t * a.N + s_I[tau][j]) * a.C + c));
+      });
+    }
+  } else {
+    for (int tb = t0; tb < t1; tb += PB) {
+      typename Qd::V orow[PB];
+      typename Qd::V xr[PB][K];
+      load_batch(tb, orow, xr);
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int t = tb + q;
+        if (t >= t1) break;
+        float b[KR][4];
+        Qd::unpack(orow[q], b[0]);
+        mix_store(t, xr[q], b);
       }
     }
   }
