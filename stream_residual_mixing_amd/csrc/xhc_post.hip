@@ -127,32 +127,52 @@ __device__ __forceinline__ void for_period(F&& f) {
   }
 }
 
-// One step of a reduce-scatter butterfly over the wave: lanes whose bit m is
-// set keep the upper half of their values, the others the lower half, and
-// each adds its partner's copy of the half it keeps.
-template <int H>
-__device__ __forceinline__ void rs_step(const float (&v)[2 * H], float (&o)[H], int lane, int m) {
-  const bool up = (lane & m) != 0;
-#pragma unroll
-  for (int i = 0; i < H; ++i) {
-    const float keep = up ? v[H + i] : v[i];
-    const float give = up ? v[i] : v[H + i];
-    o[i] = keep + __shfl_xor(give, m, WAVE);
-  }
+// Sum of 16 values over the 64 lanes of a wave, as a reduce-scatter: each
+// step halves the values a lane keeps and adds its partner's copy of that
+// half.  On return every lane holds one total: the one with index
+// 8 b5 + 4 b4 + 2 b3 + b2 (bits of the lane id); the four lanes of a group of
+// 4 hold the same value.  All exchanges are VALU lane operations, no LDS:
+//   b5: v_permlane32_swap of (low half, high half) leaves each lane with its
+//       own kept value and its partner's copy of it, so one add finishes it;
+//   b4: v_permlane16_swap (odd and even rows of 16 lanes), the same way;
+//   b3, b2: DPP row shifts by 8 and 4 within a row, each restricted by bank
+//       mask to the lanes that keep that half;
+//   b1, b0: DPP quad permutations (all lanes end with the group's total).
+// Every step adds a kept value and its partner's copy, in the same pairs as a
+// plain xor butterfly.
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, BANKS, false));
 }
+constexpr int DPP_ROW_SHL8 = 0x108, DPP_ROW_SHR8 = 0x118, DPP_ROW_SHL4 = 0x104, DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_QUAD_XOR2 = 0x4e, DPP_QUAD_XOR1 = 0xb1;   // quad_perm [2,3,0,1], [1,0,3,2]
 
-// Sum of 16 values over the 64 lanes of a wave.  On return every lane holds
-// one total: the one with index 8 b5 + 4 b4 + 2 b3 + b2 (bits of the lane
-// id); the four lanes of a group of 4 hold the same value.  17 shuffles.
 __device__ __forceinline__ float wave_sum16(const float (&v)[16], int lane) {
-  float a[8], b[4], c[2], d[1];
-  rs_step<8>(v, a, lane, 32);
-  rs_step<4>(a, b, lane, 16);
-  rs_step<2>(b, c, lane, 8);
-  rs_step<1>(c, d, lane, 4);
-  float x = d[0];
-  x += __shfl_xor(x, 2, WAVE);
-  x += __shfl_xor(x, 1, WAVE);
+  float a[8], b[4], c[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[8 + i]), false, false);
+    a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[4 + i]), false, false);
+    b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool u8 = (lane & 8) != 0, u4 = (lane & 4) != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // lanes 0-7 of a row (banks 0, 1) keep b[i] and add lane l + 8's copy;
+    // lanes 8-15 (banks 2, 3) keep b[2 + i] and add lane l - 8's
+    const float lo = b[i] + dpp_f<DPP_ROW_SHL8, 0x3>(b[i]);
+    const float hi = b[2 + i] + dpp_f<DPP_ROW_SHR8, 0xc>(b[2 + i]);
+    c[i] = u8 ? hi : lo;
+  }
+  const float lo = c[0] + dpp_f<DPP_ROW_SHL4, 0x5>(c[0]);
+  const float hi = c[1] + dpp_f<DPP_ROW_SHR4, 0xa>(c[1]);
+  float x = u4 ? hi : lo;
+  x += dpp_f<DPP_QUAD_XOR2, 0xf>(x);
+  x += dpp_f<DPP_QUAD_XOR1, 0xf>(x);
   return x;
 }
 __device__ __forceinline__ int wave_sum16_index(int lane) {
