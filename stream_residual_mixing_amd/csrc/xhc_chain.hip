@@ -45,9 +45,9 @@ constexpr int NTHR = TNTHR;
 #endif
 constexpr int WDP = XHC_PRE_WD;   // weight items in flight ahead of the MFMAs (last-sublayer pre kernel)
 #ifndef XHC_CORR_WD
-#define XHC_CORR_WD 2
+#define XHC_CORR_WD 4
 #endif
-constexpr int WDC = XHC_CORR_WD;  // and for the correction kernel
+constexpr int WDC = XHC_CORR_WD;  // and for the correction kernel (measured best of 2, 4, 8, 16)
 
 template <int N>
 struct RouteDims {
@@ -990,9 +990,9 @@ namespace {
 #endif
 constexpr int PRE_RB = XHC_PRE_RB;   // 16-token row blocks per chained pre workgroup
 #ifndef XHC_CORR_RB
-#define XHC_CORR_RB 4
+#define XHC_CORR_RB 2
 #endif
-constexpr int CORR_RB = XHC_CORR_RB;
+constexpr int CORR_RB = XHC_CORR_RB;   // 16-token row blocks per correction workgroup (best of 1, 2, 4)
 
 // Workgroups of a persistent launch: one per compute unit (their LDS allows
 // no more), Gp slices per team, no more teams than steps.
