@@ -438,7 +438,10 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
 template <class E, int K, int KR>
 static void launch_apply(const XhcPostArgs& a, hipStream_t st) {
   dim3 grid((a.T + PT - 1) / PT, a.nslices);
-  constexpr int PB = KR == 4 ? 4 : 8;
+  // tokens per load batch: measured best of 2, 3, 4, 6 for MLP-type bf16
+  // (the batch divides the 12-token history period; fp32 rows are twice as
+  // wide, so 4), and of 4, 8, 16 for attention-type
+  constexpr int PB = KR == 4 ? (sizeof(typename E::T) == 2 ? 6 : 4) : 8;
   xhc_apply_kernel<E, K, KR, PB><<<grid, 256, 0, st>>>(a);
 }
 
