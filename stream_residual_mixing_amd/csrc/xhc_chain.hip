@@ -438,7 +438,8 @@ __global__ __launch_bounds__(256) void xhc_act_fin_kernel(ActFinArgs a) {
   const int tile = blockIdx.x * 4 + wave;
   const bool live = tile < a.ntiles;
   const int G = a.G, t0 = tile * TM;
-  if (live) sum_slices<WAVE, 0>(a.part2 + (size_t)tile * G * P2, G, P2, P2, &s_sum[wave][0], lane);
+  static_assert(P2 % 4 == 0, "16-byte loads of the active partials");
+  if (live) sum_slices4<WAVE, 0>(a.part2 + (size_t)tile * G * P2, G, P2, P2, &s_sum[wave][0], lane);
   __syncthreads();
   if (!live) return;
   const float* sm = &s_sum[wave][0];

@@ -105,6 +105,31 @@ __device__ __forceinline__ void sum_slices(const float* __restrict__ src, int G,
 }
 
 // Sum of the 8 per-wave partials of element u, in a fixed order.
+// The same with 16-byte loads (n, stride multiples of 4; src 16-byte aligned):
+// twice the bytes in flight per load instruction.
+template <int NTHR, int AUX>
+__device__ __forceinline__ void sum_slices4(const float* __restrict__ src, int G, int stride, int n,
+                                            float* __restrict__ dst, int tid) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)((size_t)G * stride * 4));
+  for (int u = 4 * tid; u < n; u += 4 * NTHR) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < G; s0 += 16) {
+      u32x4_t x[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        x[q] = s0 + q < G ? ld_b128<AUX>(rs, (uint32_t)(((s0 + q) * stride + u) * 4), 0) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (s0 + q < G) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(x[q][e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[u + e] = v[e];
+  }
+}
+
 template <int PM>
 __device__ __forceinline__ float sum_waves(const float (&r)[TWV][PM], int u) {
   static_assert(TWV == 8, "fixed-order sum written for 8 waves");
