@@ -385,3 +385,129 @@ def mhc_param_count(N, C):
     """Parameters of one Transformer layer of mHC: two sublayers, each
     with an N C x (2N + N^2) projection (xHC paper, Appendix C)."""
     return 2 * (N * C * (2 * N + N * N))
+
+
+# --------------------------------------------------------------------------
+# xHC-Flash: one routing and two pre-maps shared by an attention + MLP block
+# --------------------------------------------------------------------------
+#
+# Readings (the pages' Algorithm 2 and the Appendix E.1 displays were lost in
+# extraction; the prose of the xHC paper's "xHC-Flash" section, its Eqs. 17-19
+# and the explainer's "What it costs" section fix the rest):
+#   * routing (z, I, p) and both pre-maps come from the block-entry state;
+#   * the attention sublayer has no residual map: its k active rows get
+#     x + p_j H_post^A_j out_A (Eq. 18), with H_post^A (K_r = 1) generated,
+#     like full xHC's active maps, from RMSNorm of the block-entry active rows;
+#   * the MLP's active maps H_res (k x k, Sinkhorn + row clamp) and H_post^M
+#     (k x K_r) are generated from the active rows as they stand after the
+#     attention write, the pages naming only routing and pre-maps as fixed at
+#     the block entry;
+#   * the MLP base readout is a stored tensor of the state dtype that the
+#     correction of Eq. 19 updates.
+
+def xhcf_pre(X, W_full, W_post_attn, m, k, alpha, b_pre_attn, b_pre_mlp, b_post_attn):
+    """xHC-Flash mapping generation and the two base readouts of a block.
+
+    X: [T, N, C] block-entry state.
+    W_full: [N*C, 3N]; columns 0..N-1 router W_r, N..2N-1 attention pre-map,
+        2N..3N-1 MLP pre-map (rows stream-major).
+    W_post_attn: [k*C, k]; row j*C + c for position j of the active list,
+        column j gives the attention post-map logit of position j.
+    alpha = (alpha_pre_attn, alpha_pre_mlp, alpha_post_attn); the router has
+    no scale or bias.
+
+    One projection of vec X gives the router and both pre-map logits; the two
+    readouts are the pre-map weighted sums of all N streams (xHC paper,
+    "xHC-Flash", Eq. 17, and "xHC-Flash kernel fusion").
+
+    Returns dict with z [T,N], I [T,k], p [T,k], h_pre_attn [T,N],
+    h_pre_mlp [T,N], inp_attn [T,C], inp_mlp [T,C] (base readout, unrounded),
+    h_post_attn [T,k].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W_full = np.asarray(W_full, dtype=np.float64)
+    T, N, C = X.shape
+    a_pa, a_pm, a_po = alpha
+    x = X.reshape(T, N * C)
+    z = ln_normalize(x) @ W_full[:, :N]
+    I, p = xhc_select(z, m, k)
+    xr = rms_normalize(x)
+    h_pa = sigmoid(a_pa * (xr @ W_full[:, N:2 * N]) + np.asarray(b_pre_attn))
+    h_pm = sigmoid(a_pm * (xr @ W_full[:, 2 * N:3 * N]) + np.asarray(b_pre_mlp))
+    inp_a = np.einsum("tn,tnc->tc", h_pa, X)
+    inp_m = np.einsum("tn,tnc->tc", h_pm, X)
+    Xa = np.take_along_axis(X, I[:, :, None], axis=1)
+    la = rms_normalize(Xa.reshape(T, k * C)) @ np.asarray(W_post_attn, dtype=np.float64)
+    h_po = 2.0 * sigmoid(a_po * la + np.asarray(b_post_attn))
+    return dict(z=z, I=I, p=p, h_pre_attn=h_pa, h_pre_mlp=h_pm, inp_attn=inp_a, inp_mlp=inp_m,
+                h_post_attn=h_po)
+
+
+def xhcf_attn_write(X, out_a, I, p, h_post_attn):
+    """Attention write-back of xHC-Flash: no residual mixing, each active row
+    gains p_j H_post^A_j out_A; the other streams are untouched (xHC paper,
+    "xHC-Flash", Eq. 18).  X: [T, N, C]; out_a: [T, C].  Returns the
+    unrounded new state."""
+    X = np.asarray(X, dtype=np.float64)
+    out_a = np.asarray(out_a, dtype=np.float64).reshape(X.shape[0], X.shape[2])
+    Xa = np.take_along_axis(X, I[:, :, None], axis=1)
+    new_a = Xa + (p * h_post_attn)[:, :, None] * out_a[:, None, :]
+    Xn = X.copy()
+    np.put_along_axis(Xn, I[:, :, None], new_a, axis=1)
+    return Xn
+
+
+def xhcf_mlp_input(inp_mlp, out_a, I, p, h_pre_mlp, h_post_attn):
+    """The MLP input from its base readout, corrected for the attention write
+    by one token-wise scalar: inp_M + a out_A with
+    a = sum_j H_pre^M[I_j] p_j H_post^A_j (xHC paper, "xHC-Flash", Eq. 19).
+    Returns (input [T, C] unrounded, a [T])."""
+    inp_mlp = np.asarray(inp_mlp, dtype=np.float64)
+    out_a = np.asarray(out_a, dtype=np.float64).reshape(inp_mlp.shape)
+    hpI = np.take_along_axis(np.asarray(h_pre_mlp, dtype=np.float64), I, axis=1)
+    a = np.sum(hpI * p * h_post_attn, axis=1)
+    return inp_mlp + a[:, None] * out_a, a
+
+
+def xhcf_mlp_maps(X1, I, W_act_mlp, K_r, alpha_res, alpha_post, b_res, b_post, iters=20):
+    """The MLP's active maps from the active rows after the attention write:
+    x~ = RMSNorm(vec X1[I]); H_res = rowclamp(SK(alpha_res mat_kxk(x~ W_res)
+    + b_res)), H_post = 2 sigmoid(alpha_post mat_kxK_r(x~ W_post) + b_post),
+    the same generation as full xHC's (W_act_mlp: [k*C, k^2 + k K_r], columns
+    W_res then W_post).  Returns (h_res [T,k,k], h_post [T,k,K_r])."""
+    X1 = np.asarray(X1, dtype=np.float64)
+    T, N, C = X1.shape
+    k = I.shape[1]
+    Xa = np.take_along_axis(X1, I[:, :, None], axis=1)
+    la = rms_normalize(Xa.reshape(T, k * C)) @ np.asarray(W_act_mlp, dtype=np.float64)
+    L = alpha_res * la[:, : k * k].reshape(T, k, k) + np.asarray(b_res).reshape(k, k)
+    h_res = row_clamp(sinkhorn(L, iters))
+    h_post = 2.0 * sigmoid(alpha_post * la[:, k * k:].reshape(T, k, K_r) + np.asarray(b_post).reshape(k, K_r))
+    return h_res, h_post
+
+
+def xhcf_block(X, out_a, out_m, W_full, W_post_attn, W_act_mlp, m, k, conv_ws, alpha, b_pre_attn,
+               b_pre_mlp, b_post_attn, b_res, b_post_mlp, iters=20, use_mgs=True, dtype="f64"):
+    """One xHC-Flash block (attention, then MLP) on T = B*S tokens.
+
+    X: [T, N, C]; out_a, out_m: [B, S, C] (the two sublayers' outputs, given).
+    alpha = (pre_attn, pre_mlp, post_attn, res, post_mlp).
+    Stored tensors are rounded once to dtype where the block stores them: the
+    attention input, the MLP base readout, the state after the attention
+    write, the corrected MLP input and the state after the MLP write.  The
+    MLP write is full xHC's (temporal augmentation, Gram-Schmidt, k x k mix).
+    """
+    a_pa, a_pm, a_po, a_res, a_pm2 = alpha
+    K_r = 1 + len(conv_ws)
+    pre = xhcf_pre(X, W_full, W_post_attn, m, k, (a_pa, a_pm, a_po), b_pre_attn, b_pre_mlp, b_post_attn)
+    I, p = pre["I"], pre["p"]
+    inp_a = round_state(pre["inp_attn"], dtype)
+    base_m = round_state(pre["inp_mlp"], dtype)
+    X1 = round_state(xhcf_attn_write(X, out_a, I, p, pre["h_post_attn"]), dtype)
+    inp_m, a = xhcf_mlp_input(base_m, out_a, I, p, pre["h_pre_mlp"], pre["h_post_attn"])
+    h_res, h_post = xhcf_mlp_maps(X1, I, W_act_mlp, K_r, a_res, a_pm2, b_res, b_post_mlp, iters)
+    X2 = xhc_post(X1, out_m, I, p, h_res, h_post, conv_ws, use_mgs)
+    res = dict(pre)
+    res.update(inp_attn=inp_a, inp_mlp_base=base_m, X1=X1, inp_mlp=round_state(inp_m, dtype), alpha=a,
+               h_res=h_res, h_post=h_post, X=round_state(X2, dtype))
+    return res

@@ -154,3 +154,62 @@ def xhc_sublayer(X, out, W_full, W_act, m, k, convs, alpha, b_pre, b_res, b_post
         res["h_res"].append(H)
         res["h_post"].append(P)
     return res
+
+
+def xhcf_block(X, out_a, out_m, W_full, W_pa, W_am, m, k, convs, alpha, b_pa, b_pm, b_po, b_res, b_pm2,
+               iters, use_mgs=True):
+    """One xHC-Flash block (attention, then MLP) by scalar loops, in float64
+    without rounding.  W_full has 3N columns (router | attention pre-map |
+    MLP pre-map); W_pa is [k*C][k]; W_am is [k*C][k*k + k*K_r].
+    alpha = (pre_attn, pre_mlp, post_attn, res, post_mlp).
+    Returns dict(inp_attn, inp_mlp, X1, X, I, p, alpha_corr)."""
+    B, S = len(out_m), len(out_m[0])
+    T, N, C = len(X), len(X[0]), len(X[0][0])
+    K_r = 1 + len(convs)
+    g_all = [[conv_seq(out_m[b], w) for w in convs] for b in range(B)]
+    res = dict(inp_attn=[], inp_mlp=[], X1=[], X=[], I=[], p=[], alpha_corr=[])
+    for t in range(T):
+        b, s = divmod(t, S)
+        Xt = X[t]
+        I, p, _ = xhc_route_token(Xt, W_full, m, k)
+        x = _flat(Xt)
+        sc = _rms_scale(x)
+        xn = [a * sc for a in x]
+        za = _matvec(xn, W_full, N, N)
+        zm = _matvec(xn, W_full, 2 * N, N)
+        hpa = [_sig(alpha[0] * za[i] + b_pa[i]) for i in range(N)]
+        hpm = [_sig(alpha[1] * zm[i] + b_pm[i]) for i in range(N)]
+        inp_a = [sum(hpa[i] * Xt[i][c] for i in range(N)) for c in range(C)]
+        xa = [v for j in range(k) for v in Xt[I[j]]]
+        sca = _rms_scale(xa)
+        la = _matvec([a * sca for a in xa], W_pa, 0, k)
+        hpo = [2 * _sig(alpha[2] * la[j] + b_po[j]) for j in range(k)]
+        oa = out_a[b][s]
+        # attention write, then the MLP input as the dense read of that state
+        X1 = [list(row) for row in Xt]
+        for j in range(k):
+            for c in range(C):
+                X1[I[j]][c] = Xt[I[j]][c] + p[j] * hpo[j] * oa[c]
+        inp_m = [sum(hpm[i] * X1[i][c] for i in range(N)) for c in range(C)]
+        acorr = sum(hpm[I[j]] * p[j] * hpo[j] for j in range(k))
+        # MLP maps from the rewritten active rows, then full xHC's write
+        xa1 = [v for j in range(k) for v in X1[I[j]]]
+        sc1 = _rms_scale(xa1)
+        l1 = _matvec([a * sc1 for a in xa1], W_am, 0, k * k + k * K_r)
+        L = [[alpha[3] * l1[i * k + j] + b_res[i * k + j] for j in range(k)] for i in range(k)]
+        H = _sinkhorn(L, iters)
+        H = [[a / max(sum(row), 1.0) for a in row] for row in H]
+        P = [[2 * _sig(alpha[4] * l1[k * k + j * K_r + r] + b_pm2[j * K_r + r]) for r in range(K_r)]
+             for j in range(k)]
+        comps = [out_m[b][s]] + [g_all[b][j][s] for j in range(len(convs))]
+        V = mgs_token(comps) if (use_mgs and len(comps) > 1) else comps
+        X2 = [list(row) for row in X1]
+        for j in range(k):
+            for c in range(C):
+                mix = sum(H[j][i] * X1[I[i]][c] for i in range(k))
+                wr = sum(P[j][r] * V[r][c] for r in range(K_r))
+                X2[I[j]][c] = mix + p[j] * wr
+        for key, v in (("inp_attn", inp_a), ("inp_mlp", inp_m), ("X1", X1), ("X", X2), ("I", I), ("p", p),
+                       ("alpha_corr", acorr)):
+            res[key].append(v)
+    return res
