@@ -47,9 +47,12 @@ WORKLOADS = {
     "xhc_mlp_n16k4_c2048": ("xhc", 16, 4, 2, 2048, 4, 4096, "M"),
     "mhc_n4_c4096": ("mhc", 4, 4, 0, 4096, 4, 4096, "D"),
     "mhc_n16_c4096": ("mhc", 16, 16, 0, 4096, 4, 4096, "D"),
+    # xHC-Flash: 4 blocks, each an attention + MLP pair sharing one routing
+    "xhcf_chain_n16k4_c4096": ("xhcf", 16, 4, 2, 4096, 2, 8192, "AMAMAMAM"),
 }
 DEFAULT = "xhc_chain_n16k4_c4096"
-SEED = {"xhc_chain_n16k4_c4096": 3, "xhc_mlp_n16k4_c2048": 2, "mhc_n4_c4096": 1, "mhc_n16_c4096": 4}
+SEED = {"xhc_chain_n16k4_c4096": 3, "xhc_mlp_n16k4_c2048": 2, "mhc_n4_c4096": 1, "mhc_n16_c4096": 4,
+        "xhcf_chain_n16k4_c4096": 3}
 
 
 def log(*a):
@@ -68,14 +71,31 @@ def layer_configs(name):
     return kind, cfgs, kinds
 
 
+def flash_bytes_per_token(cfg, esz=2):
+    """Algorithmic bytes per token of one xHC-Flash block's three calls, in
+    the pages' design of two full-state passes per block: pre reads the state
+    for the projection and again for both readouts and writes the two inputs
+    (2N + 2); mid reads the attention output, the k active rows and the MLP
+    base readout and writes both back (1 + k + 1, k + 1); post is full xHC's
+    (1 + 2k).  The active-row projections (k rows, twice) are not counted."""
+    N, k, C = cfg.N, cfg.k, cfg.C
+    return (2 * N + 2) * C * esz, (2 * k + 3) * C * esz, (1 + 2 * k) * C * esz
+
+
 def bytes_per_token(kind, cfg, esz=2):
     """Algorithmic bytes per token of (pre, post)."""
+    if kind == "xhcf":
+        # a block is two sublayers: half of its bytes per sublayer
+        return sum(flash_bytes_per_token(cfg, esz)) // 2, 0
     if kind == "mhc":
         return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.N) * cfg.C * esz
     return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.k) * cfg.C * esz
 
 
 def flops_per_token(kind, cfg):
+    if kind == "xhcf":   # per sublayer: half of a block's three projections
+        N, k, C = cfg.N, cfg.k, cfg.C
+        return (2 * N * C * 3 * N + 2 * k * C * k + 2 * k * C * (k * k + 4 * k)) // 2
     if kind == "mhc":
         return 2 * cfg.N * cfg.C * (2 * cfg.N + cfg.N * cfg.N)
     return 2 * cfg.N * cfg.C * 2 * cfg.N + 2 * cfg.k * cfg.C * (cfg.k * cfg.k + cfg.k * cfg.K_r)
@@ -93,6 +113,12 @@ def make_inputs(name, kind, cfgs, kinds):
     outs, ws_ = [], []
     for l, cfg in enumerate(cfgs):
         outs.append(synth.sublayer_out(seed, l, cfg.B, cfg.S, cfg.C, "bf16").to("cuda"))
+        if kind == "xhcf":
+            if l % 2 == 0:
+                from stream_residual_mixing_amd.binding import flash_weights_to_device
+                ws_.append(flash_weights_to_device(synth.xhcf_block_weights(seed, l // 2, cfg.N, cfg.k, cfg.C, 4,
+                                                                            "bf16")))
+            continue
         if kind == "mhc":
             wd = synth.mhc_layer_weights(seed, l, cfg.N, cfg.C, "bf16")
         else:
@@ -105,12 +131,15 @@ def make_inputs(name, kind, cfgs, kinds):
 
 def default_api(name):
     kind, _, _, _, _, _, _, kinds = WORKLOADS[name]
+    if kind == "xhcf":
+        return "flash"
     return "chained" if kind == "xhc" and len(kinds) > 1 else "single"
 
 
 def run_gpu(name, steps, warmup, api):
     import torch
     from stream_residual_mixing_amd import binding
+    from stream_residual_mixing_amd.binding import Config
     kind, cfgs, kinds = layer_configs(name)
     lib = binding.load()
     X, outs, weights = make_inputs(name, kind, cfgs, kinds)
@@ -122,7 +151,17 @@ def run_gpu(name, steps, warmup, api):
     stream = torch.cuda.current_stream()
     calls = []   # (name, bytes per token, launch function), in step order
     b_pre, b_post = bytes_per_token(kind, c0)
-    if api == "chained":
+    if kind == "xhcf":
+        fcfg = Config(N=c0.N, k=c0.k, m=c0.m, C=c0.C, B=c0.B, S=c0.S, n_convs=3, dtype="bf16")
+        ws = lib.flash_workspace(fcfg)
+        inp_m = torch.empty_like(inp)
+        bp, bm, bq = flash_bytes_per_token(fcfg)
+        for b in range(len(cfgs) // 2):
+            w = weights[b]
+            calls.append(("xhcf_pre", bp, lambda w=w: lib.xhcf_pre(fcfg, w, X, inp, inp_m, ws, stream)))
+            calls.append(("xhcf_mid", bm, lambda w=w, b=b: lib.xhcf_mid(fcfg, w, X, outs[2 * b], inp_m, ws, stream)))
+            calls.append(("xhcf_post", bq, lambda w=w, b=b: lib.xhcf_post(fcfg, w, X, outs[2 * b + 1], ws, stream)))
+    elif api == "chained":
         wsp = [lib.workspace(big), lib.workspace(big)]
         calls.append(("xhc_route", c0.N * c0.C * 2, lambda: lib.xhc_route(cfgs[0], weights[0], X, wsp[0], stream)))
         for l, (cfg, lk) in enumerate(zip(cfgs, kinds)):
@@ -196,6 +235,18 @@ def cpu_baseline(name, tokens=256):
         sub = Config(N=cfg.N, k=cfg.k, m=cfg.m, C=cfg.C, B=1, S=tokens, n_convs=cfg.n_convs, dtype="bf16")
         X = K.f64(synth.state_rows(seed, range(tokens), cfg.N, cfg.C, "bf16"))
         out = K.f64(synth.out_rows(seed, l, range(tokens), cfg.C, "bf16")).reshape(1, tokens, cfg.C)
+        if kind == "xhcf":
+            # one block: both sublayers of the pair
+            ow = K.flash_oracle_weights(synth.xhcf_block_weights(seed, 0, cfg.N, cfg.k, cfg.C, 4, "bf16"))
+            outm = K.f64(synth.out_rows(seed, 1, range(tokens), cfg.C, "bf16")).reshape(1, tokens, cfg.C)
+            sub.n_convs = 3
+            t = time.perf_counter()
+            K.oracle_flash(sub, X, out, outm, ow)
+            dt = time.perf_counter() - t
+            done["A"] = done["M"] = dt / 2
+            total_t += dt
+            total_tok += 2 * tokens
+            break
         if kind == "mhc":
             ow = K.oracle_weights(synth.mhc_layer_weights(seed, l, cfg.N, cfg.C, "bf16"))
             t = time.perf_counter()
@@ -209,6 +260,8 @@ def cpu_baseline(name, tokens=256):
         total_t += dt
         total_tok += tokens
     kinds_s = "+".join({"A": "attention", "M": "MLP", "D": "dense"}[k] for k in done)
+    if kind == "xhcf":
+        kinds_s = "xHC-Flash block (attention + MLP)"
     return dict(value=total_tok / total_t, unit="tokens/s per layer", cores=int(cores), kind="oracle",
                 sample=f"first {tokens} tokens of batch item 0, one {kinds_s} layer each, float64 NumPy")
 
@@ -339,7 +392,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
     ap.add_argument("--traffic-summary", metavar="PMCDIR", default=None,
                     help="write profiles/<workload>_traffic.json from rocprofv3 counter runs and exit")
-    ap.add_argument("--api", choices=("chained", "single"), default=None,
+    ap.add_argument("--api", choices=("chained", "single", "flash"), default=None,
                     help="xHC calls: chained (routing of layer l+1 prepared during layer l; default for "
                          "multi-layer workloads) or single (xhc_pre / xhc_post per layer)")
     args = ap.parse_args()
@@ -397,7 +450,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "kind": kind, "api": api, "N": c0.N, "k": c0.k if kind == "xhc" else c0.N,
+        "config": {"workload": args.workload, "kind": kind, "api": api, "N": c0.N,
+                   "k": c0.k if kind in ("xhc", "xhcf") else c0.N,
                    "m": c0.m, "C": c0.C, "batch": c0.B, "seq": c0.S, "tokens": T, "layers": kinds,
                    "sinkhorn_iters": c0.iters},
         "hbm": {"GBps": round(hbm_gbps, 1), "frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),

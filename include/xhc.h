@@ -206,6 +206,93 @@ xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const x
                             const xhc_weights* w_next, void* X, const void* out, void* ws, void* ws_next,
                             xhc_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * xHC-Flash: one attention + MLP block sharing a single routing decision
+ * (xHC paper "xHC: Expanded Hyper-Connections", section "xHC-Flash", Eqs.
+ * 17-19 and Appendix E.1; explainer "xHC: sixteen residual streams, four
+ * written at a time", section "What it costs").
+ *
+ * From the block-entry state X one projection gives the router logits and
+ * two separate pre-maps; the active set I and router weights p are shared by
+ * both sublayers.  The attention sublayer has no residual map: each active
+ * row gains p_j H_post^Attn_j out_Attn (Eq. 18).  The MLP input is the MLP
+ * pre-map's readout of the block-entry state corrected by one scalar per
+ * token, inp_M + a out_Attn with a = sum_j H_pre^MLP[I_j] p_j H_post^Attn_j
+ * (Eq. 19), which equals the MLP pre-map applied to the state after the
+ * attention write.  The MLP side is full xHC's: H_res (k x k, Sinkhorn + row
+ * clamp) and H_post^MLP (k x K_r) from RMSNorm of the active rows after the
+ * attention write, temporal augmentation and Gram-Schmidt when n_convs == 3,
+ * and the k x k mix with the gated write.
+ *
+ * Per block, on one stream and one workspace:
+ *
+ *   xhcf_pre (cfg, w, X, inp_attn, inp_mlp, ws)   inp_mlp = base readout
+ *   out_attn = Attention(inp_attn)
+ *   xhcf_mid (cfg, w, X, out_attn, inp_mlp, ws)   X written, inp_mlp corrected
+ *   out_mlp = MLP(inp_mlp)
+ *   xhcf_post(cfg, w, X, out_mlp, ws)             X written
+ *
+ * cfg is the block's config: N, k, m, C, batch, seq, dtype, sinkhorn_iters,
+ * eps; n_convs (0 or 3) and use_mgs describe the MLP sublayer.  Supported
+ * (N, k): (16, 4), (8, 4), (4, 4), (1, 1).  Every buffer is caller-owned
+ * device memory of the state dtype ([T][N][C] state, [T][C] inputs and
+ * outputs), 16-byte aligned; X must not alias any other argument.
+ * ------------------------------------------------------------------------- */
+
+/* Weights of one xHC-Flash block (host struct holding device pointers). */
+typedef struct {
+  /* [N*C][3N], state dtype: columns 0..N-1 router W_r, N..2N-1 attention
+   * pre-map, 2N..3N-1 MLP pre-map (rows stream-major, i*C + c). */
+  const void* w_full;
+  /* [k*C][k], state dtype: attention post-map; row j*C + c multiplies channel
+   * c of the j-th active stream, column j is position j's logit. */
+  const void* w_post_attn;
+  /* [k*C][k*k + k*K_r], state dtype: MLP residual map W_res (entry (i, j) at
+   * column i*k + j), then MLP post-map (entry (j, r) at k^2 + j*K_r + r). */
+  const void* w_act_mlp;
+  /* [4 + 8 + 12][C] float, lag-major (as xhc_weights.conv_w); NULL when
+   * n_convs == 0. */
+  const float* conv_w;
+  /* float biases: [N], [N], [k], [k*k], [k*K_r] */
+  const float *b_pre_attn, *b_pre_mlp, *b_post_attn, *b_res, *b_post_mlp;
+  float alpha_pre_attn, alpha_pre_mlp, alpha_post_attn, alpha_res, alpha_post_mlp;
+} xhcf_weights;
+
+/* Byte offsets of the public arrays of an xHC-Flash workspace (float unless
+ * noted).  After xhcf_pre: idx, p, h_pre_attn, h_pre_mlp, h_post_attn,
+ * z_router.  After xhcf_mid: h_res, h_post_mlp (the MLP maps). */
+typedef struct {
+  size_t idx;          /* [T][k] int32: 0..m-1, then routed streams by descending logit */
+  size_t p;            /* [T][k] router weights (1 for fixed streams) */
+  size_t h_pre_attn;   /* [T][N] */
+  size_t h_pre_mlp;    /* [T][N] */
+  size_t h_post_attn;  /* [T][k] */
+  size_t h_res;        /* [T][k][k] */
+  size_t h_post_mlp;   /* [T][k][K_r] */
+  size_t z_router;     /* [T][N] router logits */
+  size_t total;        /* bytes the caller must allocate (0 when T == 0) */
+} xhcf_ws_layout;
+
+size_t xhcf_workspace_bytes(const xhc_config* cfg);
+xhc_status xhcf_workspace_layout(const xhc_config* cfg, xhcf_ws_layout* out);
+
+/* Block entry: routing, both pre-maps and their readouts of X (read only),
+ * and the attention post-map.  inp_attn, inp_mlp: [T][C] (written; inp_mlp
+ * is the MLP pre-map's readout of X, corrected later by xhcf_mid). */
+xhc_status xhcf_pre(const xhc_config* cfg, const xhcf_weights* w, const void* X, void* inp_attn, void* inp_mlp,
+                    void* ws, xhc_stream_t stream);
+
+/* After the attention sublayer: the active rows of X gain p_j H_post^Attn_j
+ * out_attn (in place), inp_mlp gains a out_attn (in place), and the MLP maps
+ * H_res, H_post^MLP are generated from the rewritten active rows. */
+xhc_status xhcf_mid(const xhc_config* cfg, const xhcf_weights* w, void* X, const void* out_attn, void* inp_mlp,
+                    void* ws, xhc_stream_t stream);
+
+/* After the MLP sublayer: full xHC's write (temporal augmentation and
+ * Gram-Schmidt when n_convs == 3), in place on the k active rows of X. */
+xhc_status xhcf_post(const xhc_config* cfg, const xhcf_weights* w, void* X, const void* out_mlp, void* ws,
+                     xhc_stream_t stream);
+
 /* Message for the last non-OK status returned on this host thread. */
 const char* xhc_last_error(void);
 

@@ -26,6 +26,7 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 EXPORTS = (
     "xhc_workspace_bytes", "mhc_workspace_bytes", "xhc_workspace_layout", "mhc_workspace_layout",
     "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_route", "xhc_pre_chained", "xhc_post_chained",
+    "xhcf_workspace_bytes", "xhcf_workspace_layout", "xhcf_pre", "xhcf_mid", "xhcf_post",
     "xhc_last_error",
 )
 
@@ -50,6 +51,21 @@ class XhcWeights(ctypes.Structure):
 
 class XhcWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre", "h_res", "h_post", "z_router", "status", "total")]
+
+
+class XhcfWeights(ctypes.Structure):
+    _fields_ = [
+        ("w_full", ctypes.c_void_p), ("w_post_attn", ctypes.c_void_p), ("w_act_mlp", ctypes.c_void_p),
+        ("conv_w", ctypes.c_void_p), ("b_pre_attn", ctypes.c_void_p), ("b_pre_mlp", ctypes.c_void_p),
+        ("b_post_attn", ctypes.c_void_p), ("b_res", ctypes.c_void_p), ("b_post_mlp", ctypes.c_void_p),
+        ("alpha_pre_attn", ctypes.c_float), ("alpha_pre_mlp", ctypes.c_float), ("alpha_post_attn", ctypes.c_float),
+        ("alpha_res", ctypes.c_float), ("alpha_post_mlp", ctypes.c_float),
+    ]
+
+
+class XhcfWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre_attn", "h_pre_mlp", "h_post_attn", "h_res",
+                                               "h_post_mlp", "z_router", "total")]
 
 
 class XhcError(RuntimeError):
@@ -122,6 +138,35 @@ class Weights:
         return w
 
 
+@dataclass
+class FlashWeights:
+    """Device tensors of one xHC-Flash block (kept alive by this object)."""
+    w_full: torch.Tensor        # [N*C, 3N]
+    w_post_attn: torch.Tensor   # [k*C, k]
+    w_act_mlp: torch.Tensor     # [k*C, k*k + k*K_r]
+    b_pre_attn: torch.Tensor
+    b_pre_mlp: torch.Tensor
+    b_post_attn: torch.Tensor
+    b_res: torch.Tensor
+    b_post_mlp: torch.Tensor
+    alpha_pre_attn: float
+    alpha_pre_mlp: float
+    alpha_post_attn: float
+    alpha_res: float
+    alpha_post_mlp: float
+    conv_w: torch.Tensor | None = None
+
+    def c(self) -> XhcfWeights:
+        w = XhcfWeights()
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+        for name in ("w_full", "w_post_attn", "w_act_mlp", "conv_w", "b_pre_attn", "b_pre_mlp", "b_post_attn",
+                     "b_res", "b_post_mlp"):
+            setattr(w, name, ptr(getattr(self, name)))
+        for name in ("alpha_pre_attn", "alpha_pre_mlp", "alpha_post_attn", "alpha_res", "alpha_post_mlp"):
+            setattr(w, name, float(getattr(self, name)))
+        return w
+
+
 def _check(t, name, shape, dtype):
     if t is None:
         raise ValueError(f"{name} is required")
@@ -169,6 +214,17 @@ class Lib:
             fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.POINTER(XhcConfig),
                            ctypes.POINTER(XhcWeights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_void_p]
+        d.xhcf_workspace_bytes.restype = ctypes.c_size_t
+        d.xhcf_workspace_bytes.argtypes = [ctypes.POINTER(XhcConfig)]
+        d.xhcf_workspace_layout.restype = ctypes.c_int
+        d.xhcf_workspace_layout.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcfWsLayout)]
+        for fn in (d.xhcf_pre, d.xhcf_mid):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcfWeights), ctypes.c_void_p,
+                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        d.xhcf_post.restype = ctypes.c_int
+        d.xhcf_post.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcfWeights), ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         d.xhc_last_error.restype = ctypes.c_char_p
         d.xhc_last_error.argtypes = []
 
@@ -303,6 +359,82 @@ class Lib:
                                    ws.data_ptr(), _stream_ptr(stream)))
 
 
+    # xHC-Flash block: attention + MLP sharing one routing
+    def flash_workspace_bytes(self, cfg: Config) -> int:
+        c = cfg.c()
+        return int(self.dll.xhcf_workspace_bytes(ctypes.byref(c)))
+
+    def flash_layout(self, cfg: Config) -> XhcfWsLayout:
+        c, L = cfg.c(), XhcfWsLayout()
+        self._ok(self.dll.xhcf_workspace_layout(ctypes.byref(c), ctypes.byref(L)))
+        return L
+
+    def flash_workspace(self, cfg: Config, device="cuda") -> torch.Tensor:
+        n = self.flash_workspace_bytes(cfg)
+        if n == 0 and cfg.T > 0:
+            self.flash_layout(cfg)   # raises with the library's message
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def flash_ws_arrays(self, cfg: Config, ws: torch.Tensor) -> dict:
+        """Views of the public arrays of an xHC-Flash workspace."""
+        L = self.flash_layout(cfg)
+        T, N, k, Kr = cfg.T, cfg.N, cfg.k, cfg.K_r
+
+        def view(off, shape, dt=torch.float32):
+            n = 1
+            for s in shape:
+                n *= s
+            return ws[off: off + 4 * n].view(dt).reshape(shape)
+
+        return dict(idx=view(L.idx, (T, k), torch.int32), p=view(L.p, (T, k)),
+                    h_pre_attn=view(L.h_pre_attn, (T, N)), h_pre_mlp=view(L.h_pre_mlp, (T, N)),
+                    h_post_attn=view(L.h_post_attn, (T, k)), h_res=view(L.h_res, (T, k, k)),
+                    h_post_mlp=view(L.h_post_mlp, (T, k, Kr)), z=view(L.z_router, (T, N)))
+
+    def _check_flash(self, cfg, w, X, ws, stage):
+        dt = cfg.torch_dtype
+        _check(X, "X", (cfg.T, cfg.N, cfg.C), dt)
+        need = self.flash_workspace_bytes(cfg)
+        if ws is None or not ws.is_cuda or ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace must be a GPU tensor of at least {need} bytes")
+        k, N = cfg.k, cfg.N
+        if stage == 0:
+            _check(w.w_full, "w_full", (N * cfg.C, 3 * N), dt)
+            _check(w.w_post_attn, "w_post_attn", (k * cfg.C, k), dt)
+            _check(w.w_act_mlp, "w_act_mlp", (k * cfg.C, k * k + k * cfg.K_r), dt)
+            _check(w.b_pre_attn, "b_pre_attn", (N,), torch.float32)
+            _check(w.b_pre_mlp, "b_pre_mlp", (N,), torch.float32)
+            _check(w.b_post_attn, "b_post_attn", (k,), torch.float32)
+        elif stage == 1:
+            _check(w.b_res, "b_res", (k * k,), torch.float32)
+            _check(w.b_post_mlp, "b_post_mlp", (k * cfg.K_r,), torch.float32)
+        elif cfg.K_r == 4:
+            _check(w.conv_w, "conv_w", (sum(cfg.kernels), cfg.C), torch.float32)
+
+    def xhcf_pre(self, cfg: Config, w: FlashWeights, X, inp_attn, inp_mlp, ws, stream=None):
+        self._check_flash(cfg, w, X, ws, 0)
+        _check(inp_attn, "inp_attn", (cfg.T, cfg.C), cfg.torch_dtype)
+        _check(inp_mlp, "inp_mlp", (cfg.T, cfg.C), cfg.torch_dtype)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhcf_pre(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), inp_attn.data_ptr(),
+                                   inp_mlp.data_ptr(), ws.data_ptr(), _stream_ptr(stream)))
+
+    def xhcf_mid(self, cfg: Config, w: FlashWeights, X, out_attn, inp_mlp, ws, stream=None):
+        self._check_flash(cfg, w, X, ws, 1)
+        _check_out(out_attn, cfg)
+        _check(inp_mlp, "inp_mlp", (cfg.T, cfg.C), cfg.torch_dtype)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhcf_mid(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out_attn.data_ptr(),
+                                   inp_mlp.data_ptr(), ws.data_ptr(), _stream_ptr(stream)))
+
+    def xhcf_post(self, cfg: Config, w: FlashWeights, X, out_mlp, ws, stream=None):
+        self._check_flash(cfg, w, X, ws, 2)
+        _check_out(out_mlp, cfg)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhcf_post(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out_mlp.data_ptr(),
+                                    ws.data_ptr(), _stream_ptr(stream)))
+
+
 _INSTANCE = None
 
 
@@ -325,3 +457,15 @@ def weights_to_device(wd: dict, device="cuda") -> Weights:
         conv_w=conv_w, b_pre=wd["b_pre"].float().contiguous().to(device),
         b_res=wd["b_res"].float().contiguous().to(device), b_post=wd["b_post"].float().contiguous().to(device),
         alpha_pre=float(wd["alpha_pre"]), alpha_res=float(wd["alpha_res"]), alpha_post=float(wd["alpha_post"]))
+
+
+def flash_weights_to_device(wd: dict, device="cuda") -> FlashWeights:
+    """Move a dict from ``synth.xhcf_block_weights`` (CPU tensors) to the GPU."""
+    conv = wd.get("conv") or []
+    dev = lambda t: t.contiguous().to(device)
+    return FlashWeights(
+        w_full=dev(wd["w_full"]), w_post_attn=dev(wd["w_post_attn"]), w_act_mlp=dev(wd["w_act_mlp"]),
+        conv_w=torch.cat(conv, 0).contiguous().to(device) if conv else None,
+        **{n: dev(wd[n].float()) for n in ("b_pre_attn", "b_pre_mlp", "b_post_attn", "b_res", "b_post_mlp")},
+        **{n: float(wd[n]) for n in ("alpha_pre_attn", "alpha_pre_mlp", "alpha_post_attn", "alpha_res",
+                                     "alpha_post_mlp")})

@@ -164,6 +164,84 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
   return XHC_OK;
 }
 
+// xHC-Flash block plan: the xHC checks, then the block's own workspace.
+xhc_status make_flash_plan(const xhc_config* cfg, xhc::Plan* P) {
+  xhc::Plan q;
+  xhc_status s = make_plan(cfg, false, &q);
+  if (s != XHC_OK) return s;
+  if (!((q.N == 16 && q.K == 4) || (q.N == 8 && q.K == 4) || (q.N == 4 && q.K == 4) || (q.N == 1 && q.K == 1)))
+    return fail(XHC_ERR_UNSUPPORTED, "xHC-Flash (N=%d, k=%d) not built; supported: (16,4) (8,4) (4,4) (1,1)", q.N,
+                q.K);
+  q.flash = true;
+  const int KB = q.dtype == XHC_BF16 ? 32 : 16;
+  q.ncol_full = 3 * q.N;
+  q.NTF = (q.ncol_full + 15) / 16;
+  q.nkb_full = (long)q.N * q.C / KB;
+  q.ncol_act = q.K * q.K + q.K * q.KR;
+  q.NTA = (q.ncol_act + 15) / 16;
+  q.nkb_act = (long)q.K * q.C / KB;
+  q.ntiles = (q.T + 15) / 16;
+  // split-K of the full-state projection: about 1024 workgroups of 64 tokens
+  const long nblk_t = (q.T + 63) / 64;
+  long ks = nblk_t > 0 ? (1024 + nblk_t - 1) / nblk_t : 1;
+  q.KS = (int)(ks > 8 ? 8 : ks < 1 ? 1 : ks);
+  // splits of the active-row projections: about 1024 workgroups of 4 tiles
+  const long nblk_a = (q.ntiles + 3) / 4;
+  long g2 = nblk_a > 0 ? (1024 + nblk_a - 1) / nblk_a : 1;
+  if (g2 > 8) g2 = 8;
+  if (g2 > q.nkb_act) g2 = q.nkb_act;
+  q.G2 = (int)(g2 < 1 ? 1 : g2);
+
+  const size_t T = (size_t)q.T, N = q.N, K = q.K;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  q.o_sync = SIZE_MAX; q.o_corr = SIZE_MAX; q.o_gemm_ws = SIZE_MAX;
+  q.o_idx = take(T * K * 4);
+  q.o_p = take(T * K * 4);
+  q.o_hpre = take(T * N * 4);
+  q.o_hpre_m = take(T * N * 4);
+  q.o_hpost_a = take(T * K * 4);
+  q.o_hres = take(T * K * K * 4);
+  q.o_hpost = take(T * K * q.KR * 4);
+  q.o_z = take(T * N * 4);
+  q.o_colsum = take(N * 4);
+  q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
+  q.o_wact_a = take((size_t)q.nkb_act * 1 * 64 * 16);
+  q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
+  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
+  q.o_stats = take((size_t)q.KS * T * 2 * 4);
+  const size_t P2 = 16 * (size_t)(q.NTA > 1 ? q.NTA : 1) * 16 + 16;
+  q.o_part2 = take((size_t)q.ntiles * q.G2 * P2 * 4);
+  q.o_gram = take((size_t)q.nslices * T * 10 * 4);
+  q.total = q.T == 0 ? 0 : off;
+  *P = q;
+  return XHC_OK;
+}
+
+xhc_status check_flash_weights(const xhc::Plan& P, const xhcf_weights* w, int stage) {
+  if (!w) return fail(XHC_ERR_INVALID_ARG, "weights is NULL");
+  if (stage == 0) {
+    if (!w->w_full || !aligned16(w->w_full) || !w->w_post_attn || !aligned16(w->w_post_attn) || !w->w_act_mlp ||
+        !aligned16(w->w_act_mlp))
+      return fail(XHC_ERR_INVALID_ARG, "w_full, w_post_attn and w_act_mlp must be 16-byte aligned pointers");
+    if (!w->b_pre_attn || !w->b_pre_mlp || !w->b_post_attn)
+      return fail(XHC_ERR_INVALID_ARG, "b_pre_attn, b_pre_mlp and b_post_attn must not be NULL");
+    if (!std::isfinite(w->alpha_pre_attn) || !std::isfinite(w->alpha_pre_mlp) || !std::isfinite(w->alpha_post_attn))
+      return fail(XHC_ERR_INVALID_ARG, "alpha scales must be finite");
+  } else if (stage == 1) {
+    if (!w->b_res || !w->b_post_mlp) return fail(XHC_ERR_INVALID_ARG, "b_res and b_post_mlp must not be NULL");
+    if (!std::isfinite(w->alpha_res) || !std::isfinite(w->alpha_post_mlp))
+      return fail(XHC_ERR_INVALID_ARG, "alpha scales must be finite");
+  } else if (P.KR == 4 && (!w->conv_w || !aligned16(w->conv_w))) {
+    return fail(XHC_ERR_INVALID_ARG, "conv_w must be a 16-byte aligned pointer when n_convs == 3");
+  }
+  return XHC_OK;
+}
+
 xhc_status check_weights(const xhc::Plan& P, const xhc_weights* w, bool need_pre) {
   if (!w) return fail(XHC_ERR_INVALID_ARG, "weights is NULL");
   if (!std::isfinite(w->alpha_pre) || !std::isfinite(w->alpha_res) || !std::isfinite(w->alpha_post))
@@ -370,6 +448,78 @@ xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const x
   if (!xhc::launch_xhc_post(P, X, out, w, static_cast<char*>(ws), st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   if (chained && !xhc::launch_xhc_chain_tail(P, Pn, w_next, X, static_cast<char*>(ws), static_cast<char*>(ws_next), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+size_t xhcf_workspace_bytes(const xhc_config* cfg) {
+  xhc::Plan P;
+  return make_flash_plan(cfg, &P) == XHC_OK ? P.total : 0;
+}
+
+xhc_status xhcf_workspace_layout(const xhc_config* cfg, xhcf_ws_layout* out) {
+  xhc::Plan P;
+  xhc_status s = make_flash_plan(cfg, &P);
+  if (s != XHC_OK) return s;
+  if (!out) return fail(XHC_ERR_INVALID_ARG, "layout output is NULL");
+  out->idx = P.o_idx;
+  out->p = P.o_p;
+  out->h_pre_attn = P.o_hpre;
+  out->h_pre_mlp = P.o_hpre_m;
+  out->h_post_attn = P.o_hpost_a;
+  out->h_res = P.o_hres;
+  out->h_post_mlp = P.o_hpost;
+  out->z_router = P.o_z;
+  out->total = P.total;
+  return XHC_OK;
+}
+
+xhc_status xhcf_pre(const xhc_config* cfg, const xhcf_weights* w, const void* X, void* inp_attn, void* inp_mlp,
+                    void* ws, xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_flash_plan(cfg, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_flash_weights(P, w, 0)) != XHC_OK) return s;
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, inp_attn, ws, nullptr, false)) != XHC_OK) return s;
+  if (!inp_mlp || !aligned16(inp_mlp)) return fail(XHC_ERR_INVALID_ARG, "inp_mlp must be a 16-byte aligned pointer");
+  if (inp_mlp == X || inp_mlp == ws || inp_mlp == inp_attn)
+    return fail(XHC_ERR_INVALID_ARG, "inp_mlp must not alias X, ws or inp_attn");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhcf_pre(P, w, X, inp_attn, inp_mlp, static_cast<char*>(ws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status xhcf_mid(const xhc_config* cfg, const xhcf_weights* w, void* X, const void* out_attn, void* inp_mlp,
+                    void* ws, xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_flash_plan(cfg, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_flash_weights(P, w, 1)) != XHC_OK) return s;
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, out_attn, ws, nullptr, false)) != XHC_OK) return s;
+  if (!inp_mlp || !aligned16(inp_mlp)) return fail(XHC_ERR_INVALID_ARG, "inp_mlp must be a 16-byte aligned pointer");
+  if (inp_mlp == X || inp_mlp == ws || inp_mlp == out_attn)
+    return fail(XHC_ERR_INVALID_ARG, "inp_mlp must not alias X, ws or out_attn");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhcf_mid(P, w, X, out_attn, inp_mlp, static_cast<char*>(ws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status xhcf_post(const xhc_config* cfg, const xhcf_weights* w, void* X, const void* out_mlp, void* ws,
+                     xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_flash_plan(cfg, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_flash_weights(P, w, 2)) != XHC_OK) return s;
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, out_mlp, ws, nullptr, false)) != XHC_OK) return s;
+  xhc_weights wx{};
+  wx.conv_w = w->conv_w;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_post(P, X, out_mlp, &wx, static_cast<char*>(ws), st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }

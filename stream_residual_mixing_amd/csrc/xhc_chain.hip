@@ -1149,4 +1149,24 @@ bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn,
                              : tail_dispatch<F32>(P, Pn, wn, X, ws, wsn, st);
 }
 
+// Active maps from active-projection partials laid out [ntiles][G][P2] of
+// ActDims<K, KR> (used by the xHC-Flash MLP side).
+bool launch_act_fin(const Plan& P, int G, const float* part2, const float* b_res, const float* b_post, float a_res,
+                    float a_post, float* h_res, float* h_post, hipStream_t st) {
+  ActFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.G = G; f.ntiles = (int)P.ntiles;
+  f.part2 = part2;
+  f.b_res = b_res; f.b_post = b_post;
+  f.a_res = a_res; f.a_post = a_post; f.eps = P.eps_norm; f.iters = P.iters;
+  f.h_res = h_res; f.h_post = h_post;
+  const unsigned grid = (unsigned)((P.ntiles + 3) / 4);
+  switch (P.K * 10 + P.KR) {
+    case 44: xhc_act_fin_kernel<4, 4><<<grid, 256, 0, st>>>(f); return true;
+    case 41: xhc_act_fin_kernel<4, 1><<<grid, 256, 0, st>>>(f); return true;
+    case 14: xhc_act_fin_kernel<1, 4><<<grid, 256, 0, st>>>(f); return true;
+    case 11: xhc_act_fin_kernel<1, 1><<<grid, 256, 0, st>>>(f); return true;
+    default: return false;
+  }
+}
+
 }  // namespace xhc

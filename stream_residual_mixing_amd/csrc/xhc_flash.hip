@@ -1,0 +1,360 @@
+// xHC-Flash block (gfx950): one routing decision and two pre-maps shared by
+// an attention + MLP pair of sublayers (xHC paper "xHC: Expanded
+// Hyper-Connections", section "xHC-Flash", Eqs. 17-19, and paragraph
+// "xHC-Flash kernel fusion").
+//
+//   xhcf_pre   pack    the three weight matrices into MFMA B fragments
+//              colsum  column sums of the router weights (LayerNorm correction)
+//              proj    one split-K projection pass over X: [W_r | W_pre^A |
+//                      W_pre^M] and the sums of x and x^2 per token
+//              route   router logits, both pre-maps, top-k, router weights
+//              read    one pass over X: the two readouts (Eq. 17)
+//              proj_a  the k block-entry active rows against W_post^A
+//              fin_a   H_post^A
+//   xhcf_mid   the attention write of Eq. 18 fused with the Eq. 19 correction
+//              of the MLP input (the apply kernel of xhc_post.hip), then the
+//              rewritten active rows against [W_res | W_post^M] and the
+//              active-map finalize shared with the chained xHC calls
+//   xhcf_post  full xHC's MLP write (xhc_post.hip)
+//
+// Every partial sum is written per split and summed in split order, so
+// results do not depend on scheduling; nothing waits across workgroups.
+#include "xhc_device.hpp"
+#include "xhc_internal.hpp"
+#include "xhc_tile.hpp"
+
+namespace xhc {
+
+namespace {
+
+// cs[i] = sum over the rows of W (nrows x ncol, row-major) of W[row][i], for
+// the router columns i < N; one workgroup per column, fixed-order reduction.
+template <class E>
+__global__ __launch_bounds__(256) void flash_colsum_kernel(const typename E::T* __restrict__ W, long nrows, int ncol,
+                                                           float* __restrict__ cs) {
+  __shared__ float s[256];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  float v = 0.f;
+  for (long r = tid; r < nrows; r += 256) {
+    float f;
+    if constexpr (sizeof(typename E::T) == 2) f = bf16_lo((uint32_t)W[r * ncol + i]);
+    else f = W[r * ncol + i];
+    v += f;
+  }
+  s[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int o = 128; o >= 1; o >>= 1) {
+    if (tid < o) s[tid] += s[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) cs[i] = s[0];
+}
+
+struct FlashRouteArgs {
+  int T, m, KS, NP;
+  long n_el;
+  const float* part;    // [KS][T][NP]: router | pre^A | pre^M
+  const float* stats;   // [KS][T][2]: sum x, sum x^2
+  const float* cs;      // [N]
+  const float *b_pa, *b_pm;
+  float a_pa, a_pm, eps;
+  int* idx;
+  float *p, *h_pa, *h_pm, *z;
+};
+
+// One token per thread: LayerNorm-corrected router logits, both RMS-scaled
+// pre-maps, fixed-m + routed top-(k-m) and the router weights.
+template <int N, int K>
+__global__ __launch_bounds__(256) void flash_route_kernel(FlashRouteArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  float raw[3 * N];
+#pragma unroll
+  for (int c = 0; c < 3 * N; ++c) raw[c] = 0.f;
+  float q1 = 0.f, q2 = 0.f;
+  for (int ks = 0; ks < a.KS; ++ks) {
+    const float* pp = a.part + ((size_t)ks * a.T + t) * a.NP;
+#pragma unroll
+    for (int c = 0; c < 3 * N; ++c) raw[c] += pp[c];
+    q1 += a.stats[((size_t)ks * a.T + t) * 2];
+    q2 += a.stats[((size_t)ks * a.T + t) * 2 + 1];
+  }
+  const float n_el = (float)a.n_el;
+  float z[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float hpa, hpm, zz;
+    route_logits(raw[i], raw[N + i], q1, q2, a.cs[i], n_el, a.eps, a.a_pa, a.b_pa[i], true, &z[i], &hpa);
+    route_logits(raw[i], raw[2 * N + i], q1, q2, a.cs[i], n_el, a.eps, a.a_pm, a.b_pm[i], true, &zz, &hpm);
+    a.z[(size_t)t * N + i] = z[i];
+    a.h_pa[(size_t)t * N + i] = hpa;
+    a.h_pm[(size_t)t * N + i] = hpm;
+  }
+  int sel[K];
+  route_select<N, K>(z, a.m, sel);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    a.idx[(size_t)t * K + j] = sel[j];
+    a.p[(size_t)t * K + j] = j < a.m ? 1.f : sigmoidf_(z[sel[j]]);
+  }
+}
+
+struct FlashReadArgs {
+  const void* X;
+  void *inp_a, *inp_m;
+  int T, C;
+  const float *h_pa, *h_pm;
+};
+
+// Both readouts from one pass over X (Eq. 17).  Block = 16 tokens; lane
+// (g, r) holds token r and VEC channels of a contraction block, and the four
+// waves split the channels.
+template <class E, int N>
+__global__ __launch_bounds__(256) void flash_read_kernel(FlashReadArgs a) {
+  using T = typename E::T;
+  constexpr int VEC = E::VEC, KB = E::KB;
+  __shared__ float s_ha[TM][N], s_hm[TM][N];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int t0 = blockIdx.x * TM;
+  for (int u = tid; u < TM * N; u += 256) {
+    const int tau = u / N, t = t0 + tau;
+    s_ha[tau][u % N] = t < a.T ? a.h_pa[(size_t)t0 * N + u] : 0.f;
+    s_hm[tau][u % N] = t < a.T ? a.h_pm[(size_t)t0 * N + u] : 0.f;
+  }
+  __syncthreads();
+  const int t = t0 + r;
+  if (t >= a.T) return;
+  const int C = a.C, nkbC = C / KB;
+  float ha[N], hm[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) { ha[i] = s_ha[r][i]; hm[i] = s_hm[r][i]; }
+  const T* xt = reinterpret_cast<const T*>(a.X) + (size_t)t * N * C + VEC * g;
+  T* oa = reinterpret_cast<T*>(a.inp_a) + (size_t)t * C + VEC * g;
+  T* om = reinterpret_cast<T*>(a.inp_m) + (size_t)t * C + VEC * g;
+  const int kbA = wave * nkbC / 4, kbB = (wave + 1) * nkbC / 4;
+  for (int kb = kbA; kb < kbB; ++kb) {
+    const int c = kb * KB;
+    u32x4_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = ld16v(xt + (size_t)i * C + c);
+    float sa[VEC], sm[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) { sa[e] = 0.f; sm[e] = 0.f; }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float f[VEC];
+      E::unpack(v[i], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        sa[e] = fmaf(ha[i], f[e], sa[e]);
+        sm[e] = fmaf(hm[i], f[e], sm[e]);
+      }
+    }
+    st16_nt(oa + c, E::packv(sa));
+    st16_nt(om + c, E::packv(sm));
+  }
+}
+
+struct ActProjArgs {
+  const void* X;
+  int T, C, N, G, ntiles;
+  const int* idx;
+  const uint4* wp;   // packed [k*C][NT*16] B fragments
+  float* part;       // [ntiles][G][P]: token-major projection, then the sums of squares
+};
+
+// The k active rows of each token (in the order of the active list) against
+// a packed [k*C] x [NT*16] weight, split over G ranges of the k*C
+// contraction.  One wave per 16-token tile; lane (g, r) streams token r's
+// active rows.  Writes per (tile, split) the projection and sum x^2 per token.
+template <class E, int NT, int K>
+__global__ __launch_bounds__(256) void flash_act_proj_kernel(ActProjArgs a) {
+  using T = typename E::T;
+  constexpr int VEC = E::VEC, KB = E::KB, NP = NT * 16, P = TM * NP + TM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= a.ntiles) return;   // whole waves only; no barrier below
+  const int split = blockIdx.y;
+  const int C = a.C, nkbC = C / KB;
+  const long nkb = (long)K * nkbC;
+  const long kb0 = (long)split * nkb / a.G, kb1 = (long)(split + 1) * nkb / a.G;
+  const int tok = tile * TM + r;
+  const bool valid = tok < a.T;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float s2 = 0.f;
+  const uint4* wp = a.wp + lane;
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const long jb0 = (long)j * nkbC, jb1 = jb0 + nkbC;
+    const long lo = kb0 > jb0 ? kb0 : jb0, hi = kb1 < jb1 ? kb1 : jb1;
+    if (lo >= hi) continue;
+    int row = valid ? a.idx[(size_t)tok * K + j] : 0;
+    row = row < 0 ? 0 : (row >= a.N ? a.N - 1 : row);
+    const T* xr = reinterpret_cast<const T*>(a.X) + ((size_t)(valid ? tok : 0) * a.N + row) * C + VEC * g;
+    auto step = [&](const u32x4_t& v, long kb) {
+      float f[VEC];
+      E::unpack(v, f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s2 = fmaf(f[e], f[e], s2);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        acc[n] = E::mma(acc[n], v, __builtin_bit_cast(u32x4_t, wp[(kb * NT + n) * WAVE]));
+    };
+    constexpr int U = 4;
+    long kb = lo;
+    for (; kb + U <= hi; kb += U) {
+      u32x4_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = valid ? ld16v(xr + (kb + u - jb0) * KB) : zero;
+#pragma unroll
+      for (int u = 0; u < U; ++u) step(v[u], kb + u);
+    }
+    for (; kb < hi; ++kb) step(valid ? ld16v(xr + (kb - jb0) * KB) : zero, kb);
+  }
+  s2 += __shfl_xor(s2, 16, WAVE);
+  s2 += __shfl_xor(s2, 32, WAVE);
+  float* dst = a.part + ((size_t)tile * a.G + split) * P;
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(4 * g + i) * NP + n * 16 + r] = acc[n][i];
+  if (g == 0) dst[TM * NP + r] = s2;
+}
+
+struct AttnFinArgs {
+  int T, C, G;
+  const float* part;   // [ntiles][G][TM * 16 + TM]
+  const float* b_po;
+  float a_po, eps;
+  float* h_post_a;     // [T][K]
+};
+
+// H_post^A = 2 sigmoid(alpha RMSNorm(vec X_act) W_post^A + b), one token per thread.
+template <int K>
+__global__ __launch_bounds__(256) void flash_attn_fin_kernel(AttnFinArgs a) {
+  constexpr int P = TM * 16 + TM;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  const int tile = t / TM, tau = t % TM;
+  float raw[K], s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) raw[j] = 0.f;
+  for (int s = 0; s < a.G; ++s) {
+    const float* pp = a.part + ((size_t)tile * a.G + s) * P;
+#pragma unroll
+    for (int j = 0; j < K; ++j) raw[j] += pp[tau * 16 + j];
+    s2 += pp[TM * 16 + tau];
+  }
+  const float rr = 1.f / sqrtf(s2 / ((float)K * (float)a.C) + a.eps);
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    a.h_post_a[(size_t)t * K + j] = 2.f * sigmoidf_(fmaf(a.a_po * raw[j], rr, a.b_po[j]));
+}
+
+template <class E, int NT, int K>
+void act_proj_launch(const Plan& P, const void* X, const char* ws, const uint4* wp, float* part, hipStream_t st) {
+  ActProjArgs a;
+  a.X = X; a.T = (int)P.T; a.C = P.C; a.N = P.N; a.G = P.G2; a.ntiles = (int)P.ntiles;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.wp = wp;
+  a.part = part;
+  dim3 grid((unsigned)((P.ntiles + 3) / 4), (unsigned)P.G2);
+  flash_act_proj_kernel<E, NT, K><<<grid, 256, 0, st>>>(a);
+}
+
+template <class E, int N, int K>
+bool flash_pre_launch(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
+                      hipStream_t st) {
+  using TT = typename E::T;
+  launch_pack_b(P.dtype, w->w_full, P.nkb_full, P.ncol_full, P.NTF, ws + P.o_wfull, st);
+  launch_pack_b(P.dtype, w->w_post_attn, P.nkb_act, P.K, 1, ws + P.o_wact_a, st);
+  launch_pack_b(P.dtype, w->w_act_mlp, P.nkb_act, P.ncol_act, P.NTA, ws + P.o_wact, st);
+  float* cs = reinterpret_cast<float*>(ws + P.o_colsum);
+  flash_colsum_kernel<E><<<N, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C, P.ncol_full, cs);
+  float* part = reinterpret_cast<float*>(ws + P.o_part);
+  float* stats = reinterpret_cast<float*>(ws + P.o_stats);
+  if (!launch_projection(P.dtype, P.NTF, X, (int)P.T, (long)N * P.C, ws + P.o_wfull, P.nkb_full, P.KS, part, stats,
+                         st))
+    return false;
+
+  FlashRouteArgs r;
+  r.T = (int)P.T; r.m = P.m; r.KS = P.KS; r.NP = P.NTF * 16; r.n_el = (long)N * P.C;
+  r.part = part; r.stats = stats; r.cs = cs;
+  r.b_pa = w->b_pre_attn; r.b_pm = w->b_pre_mlp;
+  r.a_pa = w->alpha_pre_attn; r.a_pm = w->alpha_pre_mlp; r.eps = P.eps_norm;
+  r.idx = reinterpret_cast<int*>(ws + P.o_idx);
+  r.p = reinterpret_cast<float*>(ws + P.o_p);
+  r.h_pa = reinterpret_cast<float*>(ws + P.o_hpre);
+  r.h_pm = reinterpret_cast<float*>(ws + P.o_hpre_m);
+  r.z = reinterpret_cast<float*>(ws + P.o_z);
+  flash_route_kernel<N, K><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(r);
+
+  FlashReadArgs d;
+  d.X = X; d.inp_a = inp_a; d.inp_m = inp_m; d.T = (int)P.T; d.C = P.C;
+  d.h_pa = r.h_pa; d.h_pm = r.h_pm;
+  flash_read_kernel<E, N><<<(unsigned)P.ntiles, 256, 0, st>>>(d);
+
+  float* part2 = reinterpret_cast<float*>(ws + P.o_part2);
+  act_proj_launch<E, 1, K>(P, X, ws, reinterpret_cast<const uint4*>(ws + P.o_wact_a), part2, st);
+  AttnFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.G = P.G2; f.part = part2;
+  f.b_po = w->b_post_attn; f.a_po = w->alpha_post_attn; f.eps = P.eps_norm;
+  f.h_post_a = reinterpret_cast<float*>(ws + P.o_hpost_a);
+  flash_attn_fin_kernel<K><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(f);
+  return true;
+}
+
+template <class E, int K, int KR>
+bool flash_mid_launch(const Plan& P, const xhcf_weights* w, void* X, const void* out_a, void* inp_m, char* ws,
+                      hipStream_t st) {
+  if (!launch_flash_attn_write(P, X, out_a, inp_m, ws, st)) return false;
+  constexpr int NTA = (K * K + K * KR + 15) / 16;
+  float* part2 = reinterpret_cast<float*>(ws + P.o_part2);
+  act_proj_launch<E, NTA, K>(P, X, ws, reinterpret_cast<const uint4*>(ws + P.o_wact), part2, st);
+  return launch_act_fin(P, P.G2, part2, w->b_res, w->b_post_mlp, w->alpha_res, w->alpha_post_mlp,
+                        reinterpret_cast<float*>(ws + P.o_hres), reinterpret_cast<float*>(ws + P.o_hpost), st);
+}
+
+template <class E>
+bool flash_pre_dispatch(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
+                        hipStream_t st) {
+  switch (P.N * 10 + P.K) {
+    case 164: return flash_pre_launch<E, 16, 4>(P, w, X, inp_a, inp_m, ws, st);
+    case 84: return flash_pre_launch<E, 8, 4>(P, w, X, inp_a, inp_m, ws, st);
+    case 44: return flash_pre_launch<E, 4, 4>(P, w, X, inp_a, inp_m, ws, st);
+    case 11: return flash_pre_launch<E, 1, 1>(P, w, X, inp_a, inp_m, ws, st);
+    default: return false;
+  }
+}
+
+template <class E>
+bool flash_mid_dispatch(const Plan& P, const xhcf_weights* w, void* X, const void* out_a, void* inp_m, char* ws,
+                        hipStream_t st) {
+  switch (P.K * 10 + P.KR) {
+    case 44: return flash_mid_launch<E, 4, 4>(P, w, X, out_a, inp_m, ws, st);
+    case 41: return flash_mid_launch<E, 4, 1>(P, w, X, out_a, inp_m, ws, st);
+    case 14: return flash_mid_launch<E, 1, 4>(P, w, X, out_a, inp_m, ws, st);
+    case 11: return flash_mid_launch<E, 1, 1>(P, w, X, out_a, inp_m, ws, st);
+    default: return false;
+  }
+}
+
+}  // namespace
+
+bool launch_xhcf_pre(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
+                     hipStream_t st) {
+  return P.dtype == XHC_BF16 ? flash_pre_dispatch<Bf16>(P, w, X, inp_a, inp_m, ws, st)
+                             : flash_pre_dispatch<F32>(P, w, X, inp_a, inp_m, ws, st);
+}
+
+bool launch_xhcf_mid(const Plan& P, const xhcf_weights* w, void* X, const void* out_a, void* inp_m, char* ws,
+                     hipStream_t st) {
+  return P.dtype == XHC_BF16 ? flash_mid_dispatch<Bf16>(P, w, X, out_a, inp_m, ws, st)
+                             : flash_mid_dispatch<F32>(P, w, X, out_a, inp_m, ws, st);
+}
+
+}  // namespace xhc

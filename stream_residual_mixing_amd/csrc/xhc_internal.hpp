@@ -39,6 +39,10 @@ struct Plan {
          o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX, o_gemm_ws = SIZE_MAX,
          total = 0;
   size_t gemm_ws_bytes = 0;
+  // xHC-Flash block (attention + MLP sharing one routing)
+  bool flash = false;
+  int G2 = 1;                       // splits of the active-row projections
+  size_t o_hpre_m = SIZE_MAX, o_hpost_a = SIZE_MAX, o_wact_a = SIZE_MAX;
 };
 
 // xHC pre, fused one-pass kernel.  sync: [0] ticket counter, [1] status
@@ -82,6 +86,10 @@ struct XhcPostArgs {
   int use_mgs;
   float eps_mgs;
   float* gram;
+  // xHC-Flash attention write only: the MLP base readout [T][C] (updated in
+  // place) and the MLP pre-map [T][N]
+  void* inp_m = nullptr;
+  const float* h_pre_m = nullptr;
 };
 
 struct MhcPostArgs {
@@ -111,5 +119,18 @@ bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn,
                             const void* X, void* inp, char* ws, char* wsn, hipStream_t st);
 bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws,
                            char* wsn, hipStream_t st);
+
+// Helpers shared with the xHC-Flash launchers.
+void launch_pack_b(int dtype, const void* W, long nkb, int ncol, int NT, void* out, hipStream_t st);
+bool launch_projection(int dtype, int NT, const void* X, int T, long K, const void* Wp, long nkb, int KS,
+                       float* part, float* stats, hipStream_t st);
+bool launch_act_fin(const Plan& P, int G, const float* part2, const float* b_res, const float* b_post, float a_res,
+                    float a_post, float* h_res, float* h_post, hipStream_t st);
+bool launch_flash_attn_write(const Plan& P, void* X, const void* out, void* inp_m, const char* ws, hipStream_t st);
+// xHC-Flash block (xhc_flash.hip)
+bool launch_xhcf_pre(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
+                     hipStream_t st);
+bool launch_xhcf_mid(const Plan& P, const xhcf_weights* w, void* X, const void* out_a, void* inp_m, char* ws,
+                     hipStream_t st);
 
 }  // namespace xhc

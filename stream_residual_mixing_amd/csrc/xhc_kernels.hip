@@ -273,6 +273,7 @@ static bool gen_dispatch(int NT, const void* X, int T, long K, const void* Wp, l
   switch (NT) {
     case 1: launch_gen<E, 1>(X, T, K, Wp, nkb, KS, part, stats, st); return true;
     case 2: launch_gen<E, 2>(X, T, K, Wp, nkb, KS, part, stats, st); return true;
+    case 3: launch_gen<E, 3>(X, T, K, Wp, nkb, KS, part, stats, st); return true;
     case 5: launch_gen<E, 5>(X, T, K, Wp, nkb, KS, part, stats, st); return true;
     case 18: launch_gen<E, 18>(X, T, K, Wp, nkb, KS, part, stats, st); return true;
     default: return false;
@@ -455,6 +456,19 @@ bool launch_mhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* 
 }
 bool launch_mhc_post(const Plan& P, void* X, const void* out, char* ws, hipStream_t st) {
   return P.dtype == XHC_BF16 ? mhc_post_launch<Bf16>(P, X, out, ws, st) : mhc_post_launch<F32>(P, X, out, ws, st);
+}
+
+// Packing and split-K projection for other launchers (xHC-Flash): W [nkb*KB]
+// x [ncol] into NT-tile B fragments at out; X [T][K] . W -> part, stats.
+void launch_pack_b(int dtype, const void* W, long nkb, int ncol, int NT, void* out, hipStream_t st) {
+  if (dtype == XHC_BF16) launch_pack<Bf16>(W, nkb, ncol, NT, out, st);
+  else launch_pack<F32>(W, nkb, ncol, NT, out, st);
+}
+
+bool launch_projection(int dtype, int NT, const void* X, int T, long K, const void* Wp, long nkb, int KS,
+                       float* part, float* stats, hipStream_t st) {
+  return dtype == XHC_BF16 ? gen_dispatch<Bf16>(NT, X, T, K, Wp, nkb, KS, part, stats, st)
+                           : gen_dispatch<F32>(NT, X, T, K, Wp, nkb, KS, part, stats, st);
 }
 
 }  // namespace xhc

@@ -291,7 +291,11 @@ __global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
 }
 
 // Mix + gated write of the k active rows, in place.  PB tokens per load batch.
-template <class E, int K, int KR, int PB>
+// FL (xHC-Flash attention write, K_r = 1): no residual mix, each active row
+// gains p_j H_post_j out (xHC paper, "xHC-Flash", Eq. 18), and the MLP base
+// readout inp_m gains a out with a = sum_j H_pre^MLP[I_j] p_j H_post_j
+// (Eq. 19), read and rewritten in the same pass over out.
+template <class E, int K, int KR, int PB, bool FL = false>
 __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
   using T = typename E::T;
   using Qd = Quad<E>;
@@ -307,6 +311,8 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
   __shared__ float s_Q[PT][K][KR];
   __shared__ float s_H[PT][K][K];
   __shared__ int s_I[PT][K];
+  __shared__ float s_A[FL ? PT : 1];
+  static_assert(!FL || KR == 1, "the Flash attention write has one write component");
 
   // per-token coefficients: Q = diag(p) H_post Tm (Tm = Gram-Schmidt map)
   for (int tau = tid; tau < t1 - t0; tau += 256) {
@@ -332,6 +338,7 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.f : 0.f;
     }
+    float acorr = 0.f;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       int ij = a.idx[(size_t)t * K + j];
@@ -339,10 +346,11 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
       s_I[tau][j] = ij;
       const float pj = a.p[(size_t)t * K + j];
 #pragma unroll
-      for (int i = 0; i < K; ++i) s_H[tau][j][i] = a.h_res[((size_t)t * K + j) * K + i];
+      for (int i = 0; i < K; ++i) s_H[tau][j][i] = FL ? (i == j ? 1.f : 0.f) : a.h_res[((size_t)t * K + j) * K + i];
       float hpo[KR];
 #pragma unroll
       for (int r = 0; r < KR; ++r) hpo[r] = a.h_post[((size_t)t * K + j) * KR + r];
+      if constexpr (FL) acorr = fmaf(a.h_pre_m[(size_t)t * a.N + ij] * pj, hpo[0], acorr);
 #pragma unroll
       for (int b = 0; b < KR; ++b) {
         float s = 0.f;
@@ -351,6 +359,7 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
         s_Q[tau][j][b] = pj * s;
       }
     }
+    if constexpr (FL) s_A[tau] = acorr;
   }
   __syncthreads();
   if (!act) return;
@@ -419,10 +428,16 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
       });
     }
   } else {
+    T* __restrict__ inp_m = reinterpret_cast<T*>(a.inp_m);
     for (int tb = t0; tb < t1; tb += PB) {
       typename Qd::V orow[PB];
       typename Qd::V xr[PB][K];
+      typename Qd::V mrow[FL ? PB : 1];
       load_batch(tb, orow, xr);
+      if constexpr (FL) {
+#pragma unroll
+        for (int q = 0; q < PB; ++q) mrow[q] = tb + q < t1 ? ldq<E>(inp_m + (size_t)(tb + q) * a.C + c) : typename Qd::V{};
+      }
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
         const int t = tb + q;
@@ -430,6 +445,14 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
         float b[KR][4];
         Qd::unpack(orow[q], b[0]);
         mix_store(t, xr[q], b);
+        if constexpr (FL) {
+          float mv[4];
+          Qd::unpack(mrow[q], mv);
+          const float al = s_A[t - t0];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mv[e] = fmaf(al, b[0][e], mv[e]);
+          __builtin_nontemporal_store(Qd::pack(mv), reinterpret_cast<typename Qd::V*>(inp_m + (size_t)t * a.C + c));
+        }
       }
     }
   }
@@ -468,6 +491,31 @@ static bool xhc_post_launch(const Plan& P, void* X, const void* out, const xhc_w
     case 14: launch_apply<E, 1, 4>(a, st); return true;
     default: return false;
   }
+}
+
+// xHC-Flash attention write (Eq. 18) fused with the MLP input correction
+// (Eq. 19); a.h_post holds H_post^Attn [T][K], a.h_pre_m H_pre^MLP [T][N].
+template <class E>
+static bool flash_attn_launch(const XhcPostArgs& a, int K, hipStream_t st) {
+  dim3 grid((a.T + PT - 1) / PT, a.nslices);
+  switch (K) {
+    case 4: xhc_apply_kernel<E, 4, 1, 8, true><<<grid, 256, 0, st>>>(a); return true;
+    case 1: xhc_apply_kernel<E, 1, 1, 8, true><<<grid, 256, 0, st>>>(a); return true;
+    default: return false;
+  }
+}
+
+bool launch_flash_attn_write(const Plan& P, void* X, const void* out, void* inp_m, const char* ws, hipStream_t st) {
+  XhcPostArgs a{};
+  a.X = X; a.out = out; a.T = (int)P.T; a.S = P.S; a.C = P.C; a.N = P.N; a.nslices = P.nslices;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.p = reinterpret_cast<const float*>(ws + P.o_p);
+  a.h_res = nullptr;
+  a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost_a);
+  a.h_pre_m = reinterpret_cast<const float*>(ws + P.o_hpre_m);
+  a.inp_m = inp_m;
+  a.use_mgs = 0;
+  return P.dtype == XHC_BF16 ? flash_attn_launch<Bf16>(a, P.K, st) : flash_attn_launch<F32>(a, P.K, st);
 }
 
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {

@@ -12,6 +12,9 @@ rounded once to its storage dtype by PyTorch on the CPU.  Keys:
 * full-state projection, layer l:     [seed, 2, l]
 * active-state projection, layer l:   [seed, 3, l]
 * conv kernel j, layer l:             [seed, 4 + j, l]
+* xHC-Flash attention post-map, block b: [seed, 7, b] (a block's other
+  weights use the keys above with l = b; its attention and MLP outputs are
+  layers 2b and 2b + 1)
 
 Distributions (the workloads' own): X, out ~ N(0, 1); projection weights
 ~ N(0, 0.02); conv kernel of size kappa ~ N(0, 1/kappa) (second argument
@@ -119,4 +122,19 @@ def mhc_layer_weights(seed, layer, N, C, dtype):
         w_full=proj_weight(seed, 2, layer, N * C, 2 * N + N * N, dtype),
         b_pre=torch.zeros(N), b_post=torch.zeros(N), b_res=torch.zeros(N * N),
         alpha_pre=ALPHA, alpha_res=ALPHA, alpha_post=ALPHA,
+    )
+
+
+def xhcf_block_weights(seed, block, N, k, C, K_r, dtype, kernels=(4, 8, 12)):
+    """Weights of one xHC-Flash block: full-state projection [N*C, 3N]
+    (router | attention pre-map | MLP pre-map), attention post-map [k*C, k],
+    MLP active maps [k*C, k*k + k*K_r], conv kernels; biases 0, scales alpha."""
+    return dict(
+        w_full=proj_weight(seed, 2, block, N * C, 3 * N, dtype),
+        w_post_attn=proj_weight(seed, 7, block, k * C, k, dtype),
+        w_act_mlp=proj_weight(seed, 3, block, k * C, k * k + k * K_r, dtype),
+        conv=conv_kernels(seed, block, C, kernels) if K_r > 1 else [],
+        b_pre_attn=torch.zeros(N), b_pre_mlp=torch.zeros(N), b_post_attn=torch.zeros(k),
+        b_res=torch.zeros(k * k), b_post_mlp=torch.zeros(k * K_r),
+        alpha_pre_attn=ALPHA, alpha_pre_mlp=ALPHA, alpha_post_attn=ALPHA, alpha_res=ALPHA, alpha_post_mlp=ALPHA,
     )

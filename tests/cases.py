@@ -273,3 +273,133 @@ def compare_mhc(g, o, tol, tokens=None):
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"errors above {tol}: {bad} (all: {errs})"
     return errs
+
+
+# ---------------------------------------------------------------- xHC-Flash
+
+def flash_oracle_weights(wd):
+    o = {n: f64(wd[n]) for n in ("w_full", "w_post_attn", "w_act_mlp", "b_pre_attn", "b_pre_mlp", "b_post_attn",
+                                 "b_res", "b_post_mlp")}
+    o["conv"] = [f64(c) for c in (wd.get("conv") or [])]
+    o["alpha"] = tuple(wd[n] for n in ("alpha_pre_attn", "alpha_pre_mlp", "alpha_post_attn", "alpha_res",
+                                       "alpha_post_mlp"))
+    return o
+
+
+def flash_margins(cfg: Config, X64, ow):
+    z = O.xhc_router_logits(X64, ow["w_full"][:, :cfg.N])
+    return O.xhc_topk_margin(z, cfg.m, cfg.k)
+
+
+def flash_inputs(cfg: Config, seed, block=0):
+    """Seeded block-entry state, the two sublayer outputs and the block's
+    weights; tokens whose routing margin is below MARGIN are redrawn."""
+    wd = synth.xhcf_block_weights(seed, block, cfg.N, cfg.k, cfg.C, cfg.K_r, cfg.dtype)
+    ow = flash_oracle_weights(wd)
+    attempts = {}
+    X = synth.state(seed, cfg.T, cfg.N, cfg.C, cfg.dtype)
+    for _ in range(20):
+        bad = np.nonzero(flash_margins(cfg, f64(X), ow) < MARGIN)[0]
+        if bad.size == 0:
+            break
+        for t in bad:
+            attempts[int(t)] = attempts.get(int(t), 0) + 1
+        X[bad] = synth.state_rows(seed, bad, cfg.N, cfg.C, cfg.dtype, attempts)
+    out_a = synth.sublayer_out(seed, 2 * block, cfg.B, cfg.S, cfg.C, cfg.dtype)
+    out_m = synth.sublayer_out(seed, 2 * block + 1, cfg.B, cfg.S, cfg.C, cfg.dtype)
+    return X, out_a, out_m, wd, ow, attempts
+
+
+def oracle_flash(cfg: Config, X64, outa64, outm64, ow, dtype=None):
+    return O.xhcf_block(X64, outa64, outm64, ow["w_full"], ow["w_post_attn"], ow["w_act_mlp"], cfg.m, cfg.k,
+                        ow["conv"], ow["alpha"], ow["b_pre_attn"], ow["b_pre_mlp"], ow["b_post_attn"], ow["b_res"],
+                        ow["b_post_mlp"], iters=cfg.iters, use_mgs=bool(cfg.use_mgs), dtype=dtype or cfg.dtype)
+
+
+def gpu_flash(lib, cfg: Config, X, out_a, out_m, wd, stream=None):
+    """xhcf_pre, xhcf_mid, xhcf_post through the C ABI; CPU copies of the
+    inputs each call produces, the public workspace arrays, the state after
+    the attention write (X1) and after the block (X)."""
+    from stream_residual_mixing_amd.binding import flash_weights_to_device
+    w = flash_weights_to_device(wd)
+    Xd = X.to("cuda")
+    inp_a = torch.empty((cfg.T, cfg.C), dtype=cfg.torch_dtype, device="cuda")
+    inp_m = torch.empty_like(inp_a)
+    ws = lib.flash_workspace(cfg)
+    lib.xhcf_pre(cfg, w, Xd, inp_a, inp_m, ws, stream)
+    pre = {k: v.clone() for k, v in lib.flash_ws_arrays(cfg, ws).items() if k not in ("h_res", "h_post_mlp")}
+    base = inp_m.clone()
+    lib.xhcf_mid(cfg, w, Xd, out_a.to("cuda"), inp_m, ws, stream)
+    X1 = Xd.clone()
+    arr = lib.flash_ws_arrays(cfg, ws)
+    maps = dict(h_res=arr["h_res"].clone(), h_post=arr["h_post_mlp"].clone())
+    lib.xhcf_post(cfg, w, Xd, out_m.to("cuda"), ws, stream)
+    torch.cuda.synchronize()
+    res = dict(inp_attn=inp_a.cpu(), inp_mlp_base=base.cpu(), inp_mlp=inp_m.cpu(), X1=X1.cpu(), X=Xd.cpu())
+    res.update({k: v.cpu() for k, v in pre.items()})
+    res.update({k: v.cpu() for k, v in maps.items()})
+    return res
+
+
+FLASH_KEYS = (("inp_attn", "inp_attn"), ("inp_mlp_base", "inp_mlp_base"), ("inp_mlp", "inp_mlp"), ("X1", "X1"),
+              ("X", "X"), ("h_pre_attn", "h_pre_attn"), ("h_pre_mlp", "h_pre_mlp"), ("h_post_attn", "h_post_attn"),
+              ("h_res", "h_res"), ("h_post", "h_post"), ("p", "p"))
+
+
+def ulp(x, dtype):
+    """One unit in the last place of the state dtype at |x| (from float64
+    values): 2^(E - 7) for bfloat16 and 2^(E - 23) for float32, where
+    2^E <= |x| < 2^(E + 1)."""
+    _, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(1.0, e - (8 if dtype == "bf16" else 24))
+
+
+def corrected_input_err(g, r, base, dtype, floor=1e-2):
+    """Relative error of the corrected MLP input, allowing one unit in the
+    last place of the stored base readout.  Both sides store the base in the
+    state dtype before the correction, and two correct roundings of it may
+    differ by one unit; where a out_A nearly cancels the base, that unit is
+    large against the result.  The allowance uses the oracle's base only."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    den = np.maximum(np.abs(r), floor * rms)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.maximum(np.abs(g - r) - ulp(base, dtype), 0.0) / den)) if r.size else 0.0
+
+
+def mixed_state_err(g, r, X1, I, dtype, floor=1e-2):
+    """Relative error of the state after the MLP write, allowing one unit in
+    the last place of the rows it mixes.  Each side mixes the active rows it
+    stored after the attention write, and two correct roundings of a row may
+    differ by one unit; a mix with non-negative rows summing to at most one
+    moves that difference by at most one unit of the largest row mixed at
+    that channel.  The allowance uses the oracle's rows only."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    big = np.take_along_axis(np.abs(np.asarray(X1, np.float64)), np.asarray(I)[:, :, None], axis=1).max(axis=1)
+    allow = ulp(big, dtype)[:, None, :]
+    rms = float(np.sqrt(np.mean(r * r)))
+    den = np.maximum(np.abs(r), floor * rms)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.maximum(np.abs(g - r) - allow, 0.0) / den))
+
+
+def compare_flash(g, o, tol, tokens=None, dtype="bf16"):
+    """Errors per quantity of a block; active indices must match exactly."""
+    sel = slice(None) if tokens is None else tokens
+    assert np.array_equal(g["idx"].numpy()[sel], o["I"] if tokens is not None else o["I"]), "active indices differ"
+    errs = {}
+    for key, okey in FLASH_KEYS:
+        gv = g[key]
+        gv = (f64(gv) if gv.dtype != torch.float32 or key in ("inp_attn", "inp_mlp_base", "inp_mlp", "X1", "X")
+              else gv.numpy().astype(np.float64))[sel]
+        if key == "inp_mlp":
+            errs[key] = corrected_input_err(gv, o[okey], o["inp_mlp_base"], dtype)
+        elif key == "X":
+            errs[key] = mixed_state_err(gv, o[okey], o["X1"], o["I"], dtype)
+        else:
+            errs[key] = rel_err(gv, o[okey])
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"errors above {tol}: {bad} (all: {errs})"
+    return errs

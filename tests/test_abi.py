@@ -42,7 +42,8 @@ def test_struct_layouts_match_the_header(tmp_path):
     """The ctypes mirrors have the sizes and field offsets a C compiler
     gives the header's structs."""
     import subprocess
-    structs = {"xhc_config": XhcConfig, "xhc_weights": XhcWeights, "xhc_ws_layout": binding.XhcWsLayout}
+    structs = {"xhc_config": XhcConfig, "xhc_weights": XhcWeights, "xhc_ws_layout": binding.XhcWsLayout,
+               "xhcf_weights": binding.XhcfWeights, "xhcf_ws_layout": binding.XhcfWsLayout}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "xhc.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -150,3 +151,25 @@ def test_binding_refuses_host_tensors(lib):
     X = torch.zeros(4, 16, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         lib.xhc_pre(cfg, wd, X, torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+def test_flash_layout_and_unsupported_shapes(lib):
+    """xHC-Flash workspace sizing and layout; shapes without kernels are
+    refused before anything runs."""
+    cfg = Config(N=16, k=4, m=2, C=4096, B=2, S=8192, n_convs=3, dtype="bf16")
+    n = lib.flash_workspace_bytes(cfg)
+    L = lib.flash_layout(cfg)
+    assert L.total == n > 0
+    T = cfg.T
+    offs = sorted([(L.idx, T * 4 * 4), (L.p, T * 4 * 4), (L.h_pre_attn, T * 16 * 4), (L.h_pre_mlp, T * 16 * 4),
+                   (L.h_post_attn, T * 4 * 4), (L.h_res, T * 16 * 4), (L.h_post_mlp, T * 16 * 4),
+                   (L.z_router, T * 16 * 4)])
+    for (o1, s1), (o2, _) in zip(offs, offs[1:]):
+        assert o1 % 256 == 0 and o1 + s1 <= o2
+    assert offs[-1][0] + offs[-1][1] <= n
+    bad = Config(N=16, k=2, m=1, C=256, B=1, S=8, n_convs=3, dtype="bf16")
+    assert lib.flash_workspace_bytes(bad) == 0
+    with pytest.raises(binding.XhcError) as e:
+        lib.flash_layout(bad)
+    assert e.value.status == binding.XHC_ERR_UNSUPPORTED
+    assert lib.flash_workspace_bytes(Config(N=16, k=4, m=2, C=256, B=0, S=8, n_convs=3)) == 0
