@@ -208,7 +208,7 @@ xhc_status make_flash_plan(const xhc_config* cfg, xhc::Plan* P) {
   q.o_hres = take(T * K * K * 4);
   q.o_hpost = take(T * K * q.KR * 4);
   q.o_z = take(T * N * 4);
-  q.o_colsum = take(N * 4);
+  q.o_colsum = take((1 + 256) * N * 4);   // column sums, then the per-row-block partials
   q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
   q.o_wact_a = take((size_t)q.nkb_act * 1 * 64 * 16);
   q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);

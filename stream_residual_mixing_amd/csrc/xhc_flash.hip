@@ -28,27 +28,47 @@ namespace xhc {
 namespace {
 
 // cs[i] = sum over the rows of W (nrows x ncol, row-major) of W[row][i], for
-// the router columns i < N; one workgroup per column, fixed-order reduction.
-template <class E>
+// the router columns i < N, in two fixed-order stages: CSB workgroups each
+// sum a contiguous range of rows (a thread reads a row's N router weights at
+// a time) into part[b][i]; then one workgroup adds the CSB partials in order.
+constexpr int CSB = 256;
+template <class E, int N>
 __global__ __launch_bounds__(256) void flash_colsum_kernel(const typename E::T* __restrict__ W, long nrows, int ncol,
-                                                           float* __restrict__ cs) {
-  __shared__ float s[256];
-  const int i = blockIdx.x, tid = threadIdx.x;
-  float v = 0.f;
-  for (long r = tid; r < nrows; r += 256) {
-    float f;
-    if constexpr (sizeof(typename E::T) == 2) f = bf16_lo((uint32_t)W[r * ncol + i]);
-    else f = W[r * ncol + i];
-    v += f;
+                                                           float* __restrict__ part) {
+  __shared__ float s[256][N];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const long lo = (long)b * nrows / CSB, hi = (long)(b + 1) * nrows / CSB;
+  float acc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.f;
+  for (long r = lo + tid; r < hi; r += 256) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if constexpr (sizeof(typename E::T) == 2) acc[i] += bf16_lo((uint32_t)W[r * ncol + i]);
+      else acc[i] += W[r * ncol + i];
+    }
   }
-  s[tid] = v;
+#pragma unroll
+  for (int i = 0; i < N; ++i) s[tid][i] = acc[i];
   __syncthreads();
 #pragma unroll
   for (int o = 128; o >= 1; o >>= 1) {
-    if (tid < o) s[tid] += s[tid + o];
+    if (tid < o) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) s[tid][i] += s[tid + o][i];
+    }
     __syncthreads();
   }
-  if (tid == 0) cs[i] = s[0];
+  if (tid < N) part[(size_t)b * N + tid] = s[0][tid];
+}
+
+template <int N>
+__global__ __launch_bounds__(64) void flash_colsum_fin_kernel(const float* __restrict__ part, float* __restrict__ cs) {
+  const int i = threadIdx.x;
+  if (i >= N) return;
+  float v = 0.f;
+  for (int b = 0; b < CSB; ++b) v += part[(size_t)b * N + i];
+  cs[i] = v;
 }
 
 struct FlashRouteArgs {
@@ -107,53 +127,54 @@ struct FlashReadArgs {
   const float *h_pa, *h_pm;
 };
 
-// Both readouts from one pass over X (Eq. 17).  Block = 16 tokens; lane
-// (g, r) holds token r and VEC channels of a contraction block, and the four
-// waves split the channels.
+// Both readouts from one pass over X (Eq. 17).  A workgroup is one 16-token
+// tile times a slice of 8 contraction blocks; each wave loads its block of
+// all N streams at once (lane (g, r): token r, VEC channels), forms both
+// weighted sums and stores them.
 template <class E, int N>
-__global__ __launch_bounds__(256) void flash_read_kernel(FlashReadArgs a) {
+__global__ __launch_bounds__(512) void flash_read_kernel(FlashReadArgs a) {
   using T = typename E::T;
   constexpr int VEC = E::VEC, KB = E::KB;
   __shared__ float s_ha[TM][N], s_hm[TM][N];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
-  const int t0 = blockIdx.x * TM;
-  for (int u = tid; u < TM * N; u += 256) {
+  const int C = a.C, nkbC = C / KB;
+  const int G = (nkbC + TWV - 1) / TWV;
+  const int tile = blockIdx.x / G, slice = blockIdx.x % G;
+  const int t0 = tile * TM;
+  for (int u = tid; u < TM * N; u += TNTHR) {
     const int tau = u / N, t = t0 + tau;
     s_ha[tau][u % N] = t < a.T ? a.h_pa[(size_t)t0 * N + u] : 0.f;
     s_hm[tau][u % N] = t < a.T ? a.h_pm[(size_t)t0 * N + u] : 0.f;
   }
-  __syncthreads();
+  const int kb = slice * TWV + wave;
   const int t = t0 + r;
-  if (t >= a.T) return;
-  const int C = a.C, nkbC = C / KB;
-  float ha[N], hm[N];
+  const bool valid = kb < nkbC && t < a.T;
+  u32x4_t v[N];
+  const T* xt = reinterpret_cast<const T*>(a.X) + (size_t)(valid ? t : 0) * N * C + (size_t)(valid ? kb : 0) * KB +
+                VEC * g;
+  if (valid) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) { ha[i] = s_ha[r][i]; hm[i] = s_hm[r][i]; }
-  const T* xt = reinterpret_cast<const T*>(a.X) + (size_t)t * N * C + VEC * g;
-  T* oa = reinterpret_cast<T*>(a.inp_a) + (size_t)t * C + VEC * g;
-  T* om = reinterpret_cast<T*>(a.inp_m) + (size_t)t * C + VEC * g;
-  const int kbA = wave * nkbC / 4, kbB = (wave + 1) * nkbC / 4;
-  for (int kb = kbA; kb < kbB; ++kb) {
-    const int c = kb * KB;
-    u32x4_t v[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = ld16v(xt + (size_t)i * C + c);
-    float sa[VEC], sm[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) { sa[e] = 0.f; sm[e] = 0.f; }
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      float f[VEC];
-      E::unpack(v[i], f);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        sa[e] = fmaf(ha[i], f[e], sa[e]);
-        sm[e] = fmaf(hm[i], f[e], sm[e]);
-      }
-    }
-    st16_nt(oa + c, E::packv(sa));
-    st16_nt(om + c, E::packv(sm));
+    for (int i = 0; i < N; ++i) v[i] = ld16v(xt + (size_t)i * C);
   }
+  __syncthreads();
+  if (!valid) return;
+  float sa[VEC], sm[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) { sa[e] = 0.f; sm[e] = 0.f; }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float ha = s_ha[r][i], hm = s_hm[r][i];
+    float f[VEC];
+    E::unpack(v[i], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      sa[e] = fmaf(ha, f[e], sa[e]);
+      sm[e] = fmaf(hm, f[e], sm[e]);
+    }
+  }
+  const size_t o = (size_t)t * C + (size_t)kb * KB + VEC * g;
+  st16_nt(reinterpret_cast<T*>(a.inp_a) + o, E::packv(sa));
+  st16_nt(reinterpret_cast<T*>(a.inp_m) + o, E::packv(sm));
 }
 
 struct ActProjArgs {
@@ -274,7 +295,9 @@ bool flash_pre_launch(const Plan& P, const xhcf_weights* w, const void* X, void*
   launch_pack_b(P.dtype, w->w_post_attn, P.nkb_act, P.K, 1, ws + P.o_wact_a, st);
   launch_pack_b(P.dtype, w->w_act_mlp, P.nkb_act, P.ncol_act, P.NTA, ws + P.o_wact, st);
   float* cs = reinterpret_cast<float*>(ws + P.o_colsum);
-  flash_colsum_kernel<E><<<N, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C, P.ncol_full, cs);
+  flash_colsum_kernel<E, N><<<CSB, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C, P.ncol_full,
+                                                 cs + N);
+  flash_colsum_fin_kernel<N><<<1, 64, 0, st>>>(cs + N, cs);
   float* part = reinterpret_cast<float*>(ws + P.o_part);
   float* stats = reinterpret_cast<float*>(ws + P.o_stats);
   if (!launch_projection(P.dtype, P.NTF, X, (int)P.T, (long)N * P.C, ws + P.o_wfull, P.nkb_full, P.KS, part, stats,
@@ -296,7 +319,8 @@ bool flash_pre_launch(const Plan& P, const xhcf_weights* w, const void* X, void*
   FlashReadArgs d;
   d.X = X; d.inp_a = inp_a; d.inp_m = inp_m; d.T = (int)P.T; d.C = P.C;
   d.h_pa = r.h_pa; d.h_pm = r.h_pm;
-  flash_read_kernel<E, N><<<(unsigned)P.ntiles, 256, 0, st>>>(d);
+  const int nkbC = P.C / E::KB;
+  flash_read_kernel<E, N><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
 
   float* part2 = reinterpret_cast<float*>(ws + P.o_part2);
   act_proj_launch<E, 1, K>(P, X, ws, reinterpret_cast<const uint4*>(ws + P.o_wact_a), part2, st);
