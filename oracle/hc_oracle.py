@@ -511,3 +511,49 @@ def xhcf_block(X, out_a, out_m, W_full, W_post_attn, W_act_mlp, m, k, conv_ws, a
     res.update(inp_attn=inp_a, inp_mlp_base=base_m, X1=X1, inp_mlp=round_state(inp_m, dtype), alpha=a,
                h_res=h_res, h_post=h_post, X=round_state(X2, dtype))
     return res
+
+
+# --------------------------------------------------------------------------
+# single-token decode: the MLP-type write with the conv history in a ring
+# --------------------------------------------------------------------------
+
+RING = 12   # slots: the current output and the 11 lags of the longest kernel
+
+
+def xhc_decode_post(X, out, ring, steps, I, p, h_res, h_post, conv_ws, use_mgs=True, eps=EPS_MGS):
+    """One decode step of xHC's MLP-type write for B sequences, each adding
+    one token.  The causal convolutions need the sublayer outputs of the 11
+    tokens before the new one in its sequence; a decoder keeps them in a ring
+    (the pages' prefill computes the same convolutions over the whole
+    sequence: summary 3.3; explainer, "What xHC changes").
+
+    X: [B, N, C] the new tokens' states; out: [B, C] their sublayer outputs;
+    ring: [B, RING, C], slot s % RING holds the output of position s of the
+    sequence; steps: [B] position of the new token (earlier positions are
+    zero history when they do not exist).  I, p, h_res, h_post as xhc_post.
+
+    Returns (new state [B, N, C] unrounded, new ring with the new output in
+    slot steps % RING).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    ring = np.asarray(ring, dtype=np.float64)
+    B, N, C = X.shape
+    hist = np.zeros((B, RING, C))          # hist[b, i] = out of position steps[b] - i
+    hist[:, 0] = out
+    for b in range(B):
+        for i in range(1, RING):
+            if i <= steps[b]:
+                hist[b, i] = ring[b, (steps[b] - i) % RING]
+    comps = [out] + [np.einsum("ic,bic->bc", np.asarray(w, dtype=np.float64), hist[:, : len(w)]) for w in conv_ws]
+    if use_mgs and len(comps) > 1:
+        comps = gram_schmidt(comps, eps)
+    V = np.stack(comps, axis=1)                                         # [B, K_r, C]
+    Xa = np.take_along_axis(X, I[:, :, None], axis=1)
+    new_a = np.einsum("tij,tjc->tic", h_res, Xa) + p[:, :, None] * np.einsum("tjr,trc->tjc", h_post, V)
+    Xn = X.copy()
+    np.put_along_axis(Xn, I[:, :, None], new_a, axis=1)
+    ring_n = ring.copy()
+    for b in range(B):
+        ring_n[b, steps[b] % RING] = out[b]
+    return Xn, ring_n

@@ -496,3 +496,32 @@ def test_parameter_counts_reproduce_the_printed_figures():
             assert O.xhc_param_count(case["N"], case["k"], C, case["conv_kernels"]) == case["params_per_C"]
     ratio = O.mhc_param_count(16, 1) / O.xhc_param_count(16, 4, 1)
     assert round(ratio, 1) == g["ratio_mhc16_over_xhc"]
+
+
+# ---------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("use_mgs", [True, False])
+def test_decode_token_by_token_equals_the_prefill(use_mgs):
+    """Decoding a sequence one token at a time, with the conv history kept in
+    the ring, writes the same state as the prefill post over the whole
+    sequence (which convolves along the sequence directly), for sequences
+    shorter and longer than the ring and two sequences decoded side by side."""
+    r = rng(31, int(use_mgs))
+    B, S, N, k, C = 2, 29, 6, 3, 16
+    X = r.standard_normal((B * S, N, C))
+    out = r.standard_normal((B, S, C))
+    convs = [r.standard_normal((kap, C)) / kap for kap in (4, 8, 12)]
+    I = np.stack([np.concatenate([[0], r.choice(np.arange(1, N), k - 1, replace=False)]) for _ in range(B * S)])
+    p = np.concatenate([np.ones((B * S, 1)), r.uniform(0.1, 0.9, (B * S, k - 1))], axis=1)
+    h_res = O.row_clamp(O.sinkhorn(r.standard_normal((B * S, k, k)), 20))
+    h_post = r.uniform(0.1, 1.9, (B * S, k, 4))
+    ref = O.xhc_post(X, out, I, p, h_res, h_post, convs, use_mgs)
+    ring = r.standard_normal((B, O.RING, C))   # stale contents must not leak into a new sequence
+    for s in range(S):
+        rows = np.arange(B) * S + s
+        Xn, ring = O.xhc_decode_post(X[rows], out[:, s], ring, np.full(B, s), I[rows], p[rows], h_res[rows],
+                                     h_post[rows], convs, use_mgs)
+        np.testing.assert_allclose(Xn, ref[rows], rtol=0, atol=1e-12 * np.abs(ref).max())
+    for b in range(B):
+        for s in range(S - O.RING, S):
+            np.testing.assert_array_equal(ring[b, s % O.RING], out[b, s])
