@@ -49,10 +49,12 @@ WORKLOADS = {
     "mhc_n16_c4096": ("mhc", 16, 16, 0, 4096, 4, 4096, "D"),
     # xHC-Flash: 4 blocks, each an attention + MLP pair sharing one routing
     "xhcf_chain_n16k4_c4096": ("xhcf", 16, 4, 2, 4096, 2, 8192, "AMAMAMAM"),
+    # single-token decode: 256 sequences, one new token each, 8 sublayers
+    "xhc_decode_n16k4_c4096": ("xhcd", 16, 4, 2, 4096, 256, 1, "AMAMAMAM"),
 }
 DEFAULT = "xhc_chain_n16k4_c4096"
 SEED = {"xhc_chain_n16k4_c4096": 3, "xhc_mlp_n16k4_c2048": 2, "mhc_n4_c4096": 1, "mhc_n16_c4096": 4,
-        "xhcf_chain_n16k4_c4096": 3}
+        "xhcf_chain_n16k4_c4096": 3, "xhc_decode_n16k4_c4096": 5}
 
 
 def log(*a):
@@ -83,7 +85,12 @@ def flash_bytes_per_token(cfg, esz=2):
 
 
 def bytes_per_token(kind, cfg, esz=2):
-    """Algorithmic bytes per token of (pre, post)."""
+    """Algorithmic bytes per token of (pre, post).  Decode: the MLP-type
+    write also reads the 11 earlier outputs from the ring and stores the new
+    one (11 + 1 more)."""
+    if kind == "xhcd":
+        extra = 12 if cfg.K_r == 4 else 0
+        return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.k + extra) * cfg.C * esz
     if kind == "xhcf":
         # a block is two sublayers: half of its bytes per sublayer
         return sum(flash_bytes_per_token(cfg, esz)) // 2, 0
@@ -133,6 +140,8 @@ def default_api(name):
     kind, _, _, _, _, _, _, kinds = WORKLOADS[name]
     if kind == "xhcf":
         return "flash"
+    if kind == "xhcd":
+        return "decode"
     return "chained" if kind == "xhc" and len(kinds) > 1 else "single"
 
 
@@ -161,6 +170,19 @@ def run_gpu(name, steps, warmup, api):
             calls.append(("xhcf_pre", bp, lambda w=w: lib.xhcf_pre(fcfg, w, X, inp, inp_m, ws, stream)))
             calls.append(("xhcf_mid", bm, lambda w=w, b=b: lib.xhcf_mid(fcfg, w, X, outs[2 * b], inp_m, ws, stream)))
             calls.append(("xhcf_post", bq, lambda w=w, b=b: lib.xhcf_post(fcfg, w, X, outs[2 * b + 1], ws, stream)))
+    elif kind == "xhcd":
+        ws = lib.workspace(big)
+        ring = torch.zeros((c0.B, 12, c0.C), dtype=torch.bfloat16, device="cuda")
+        steps_t = torch.full((c0.B,), 100, dtype=torch.int32, device="cuda")
+        for l, (cfg, lk) in enumerate(zip(cfgs, kinds)):
+            bp, bq = bytes_per_token(kind, cfg)
+            calls.append((f"xhc_pre_{lk}", bp, lambda cfg=cfg, l=l: lib.xhc_pre(cfg, weights[l], X, inp, ws, stream)))
+            if lk == "M":
+                calls.append((f"xhc_post_decode_{lk}", bq, lambda cfg=cfg, l=l: lib.xhc_post_decode(
+                    cfg, weights[l], X, outs[l].reshape(cfg.T, cfg.C), ring, steps_t, ws, stream)))
+            else:
+                calls.append((f"xhc_post_{lk}", bq, lambda cfg=cfg, l=l: lib.xhc_post(cfg, weights[l], X, outs[l], ws,
+                                                                                      stream)))
     elif api == "chained":
         wsp = [lib.workspace(big), lib.workspace(big)]
         calls.append(("xhc_route", c0.N * c0.C * 2, lambda: lib.xhc_route(cfgs[0], weights[0], X, wsp[0], stream)))
@@ -392,7 +414,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
     ap.add_argument("--traffic-summary", metavar="PMCDIR", default=None,
                     help="write profiles/<workload>_traffic.json from rocprofv3 counter runs and exit")
-    ap.add_argument("--api", choices=("chained", "single", "flash"), default=None,
+    ap.add_argument("--api", choices=("chained", "single", "flash", "decode"), default=None,
                     help="xHC calls: chained (routing of layer l+1 prepared during layer l; default for "
                          "multi-layer workloads) or single (xhc_pre / xhc_post per layer)")
     args = ap.parse_args()

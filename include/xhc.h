@@ -206,6 +206,28 @@ xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const x
                             const xhc_weights* w_next, void* X, const void* out, void* ws, void* ws_next,
                             xhc_stream_t stream);
 
+/* Single-token decode of an MLP-type sublayer's write.  cfg.seq must be 1:
+ * each of the cfg.batch tokens is the newest token of its own sequence, and
+ * the causal convolutions take its 11 earlier outputs from a ring instead of
+ * from neighbouring tokens (the convolutions are those of xhc_post: explainer
+ * "xHC: sixteen residual streams, four written at a time", section "What xHC
+ * changes"; summary 3.3).  n_convs must be 3 (an attention-type sublayer has
+ * no history: use xhc_post).
+ *   X:          [B][N][C], the new tokens' states, written in place (k rows)
+ *   out:        [B][C], the sublayer outputs of the new tokens
+ *   conv_state: [B][12][C] of the state dtype, caller-owned: slot s % 12 of
+ *               sequence b holds the output of its position s.  Lag i of
+ *               the new token (position steps[b]) is read from slot
+ *               (steps[b] - i) % 12 when i <= steps[b] and is zero before
+ *               the sequence start; the new output is then stored to slot
+ *               steps[b] % 12.  Contents need no clearing between sequences.
+ *   steps:      [B] int32, device: position of each new token in its
+ *               sequence (read only; the caller advances it)
+ *   ws:         the workspace xhc_pre filled for the same cfg
+ * The other rows of X are not touched. */
+xhc_status xhc_post_decode(const xhc_config* cfg, const xhc_weights* w, void* X, const void* out, void* conv_state,
+                           const int32_t* steps, void* ws, xhc_stream_t stream);
+
 /* ---------------------------------------------------------------------------
  * xHC-Flash: one attention + MLP block sharing a single routing decision
  * (xHC paper "xHC: Expanded Hyper-Connections", section "xHC-Flash", Eqs.

@@ -26,7 +26,7 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 EXPORTS = (
     "xhc_workspace_bytes", "mhc_workspace_bytes", "xhc_workspace_layout", "mhc_workspace_layout",
     "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_route", "xhc_pre_chained", "xhc_post_chained",
-    "xhcf_workspace_bytes", "xhcf_workspace_layout", "xhcf_pre", "xhcf_mid", "xhcf_post",
+    "xhc_post_decode", "xhcf_workspace_bytes", "xhcf_workspace_layout", "xhcf_pre", "xhcf_mid", "xhcf_post",
     "xhc_last_error",
 )
 
@@ -214,6 +214,10 @@ class Lib:
             fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.POINTER(XhcConfig),
                            ctypes.POINTER(XhcWeights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_void_p]
+        d.xhc_post_decode.restype = ctypes.c_int
+        d.xhc_post_decode.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
         d.xhcf_workspace_bytes.restype = ctypes.c_size_t
         d.xhcf_workspace_bytes.argtypes = [ctypes.POINTER(XhcConfig)]
         d.xhcf_workspace_layout.restype = ctypes.c_int
@@ -358,6 +362,19 @@ class Lib:
         self._ok(self.dll.mhc_post(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
                                    ws.data_ptr(), _stream_ptr(stream)))
 
+
+    # single-token decode: the conv history of each sequence in a 12-slot ring
+    def xhc_post_decode(self, cfg: Config, w: Weights, X, out, conv_state, steps, ws, stream=None):
+        if cfg.S != 1:
+            raise ValueError("decode takes one new token per sequence (S == 1)")
+        self._check_common(cfg, w, X, ws, False, False)
+        _check(out, "out", (cfg.T, cfg.C), cfg.torch_dtype)
+        _check(conv_state, "conv_state", (cfg.B, 12, cfg.C), cfg.torch_dtype)
+        _check(steps, "steps", (cfg.B,), torch.int32)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_post_decode(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
+                                          conv_state.data_ptr(), steps.data_ptr(), ws.data_ptr(),
+                                          _stream_ptr(stream)))
 
     # xHC-Flash block: attention + MLP sharing one routing
     def flash_workspace_bytes(self, cfg: Config) -> int:

@@ -452,6 +452,27 @@ xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const x
   return finish(st);
 }
 
+xhc_status xhc_post_decode(const xhc_config* cfg, const xhc_weights* w, void* X, const void* out, void* conv_state,
+                           const int32_t* steps, void* ws, xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if (cfg->seq != 1) return fail(XHC_ERR_INVALID_ARG, "decode takes one new token per sequence: seq must be 1");
+  if (P.KR != 4)
+    return fail(XHC_ERR_UNSUPPORTED, "decode of an attention-type sublayer needs no history: use xhc_post");
+  if ((s = check_weights(P, w, false)) != XHC_OK) return s;
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, out, ws, nullptr, false)) != XHC_OK) return s;
+  if (!conv_state || !aligned16(conv_state)) return fail(XHC_ERR_INVALID_ARG, "conv_state must be 16-byte aligned");
+  if (!steps || (reinterpret_cast<uintptr_t>(steps) & 3u)) return fail(XHC_ERR_INVALID_ARG, "steps must be an aligned int32 pointer");
+  if (conv_state == X || conv_state == out || conv_state == ws)
+    return fail(XHC_ERR_INVALID_ARG, "conv_state must not alias X, out or ws");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_post_decode(P, X, out, conv_state, steps, w, static_cast<char*>(ws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
 size_t xhcf_workspace_bytes(const xhc_config* cfg) {
   xhc::Plan P;
   return make_flash_plan(cfg, &P) == XHC_OK ? P.total : 0;

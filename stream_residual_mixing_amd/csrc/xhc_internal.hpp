@@ -127,6 +127,8 @@ bool launch_projection(int dtype, int NT, const void* X, int T, long K, const vo
 bool launch_act_fin(const Plan& P, int G, const float* part2, const float* b_res, const float* b_post, float a_res,
                     float a_post, float* h_res, float* h_post, hipStream_t st);
 bool launch_flash_attn_write(const Plan& P, void* X, const void* out, void* inp_m, const char* ws, hipStream_t st);
+bool launch_xhc_post_decode(const Plan& P, void* X, const void* out, void* ring, const int* steps,
+                            const xhc_weights* w, const char* ws, hipStream_t st);
 // xHC-Flash block (xhc_flash.hip)
 bool launch_xhcf_pre(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
                      hipStream_t st);

@@ -458,6 +458,184 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Single-token decode of the MLP-type write: one workgroup per sequence, whose
+// new token's lag-i outputs (i = 1..11) come from a ring of 12 slots (slot
+// s mod 12 holds the output of position s; positions before the sequence
+// start are zero history).  The Gram matrix of the token's basis is reduced
+// over all C channels inside the workgroup, so the write needs one launch;
+// the new output then goes to slot step mod 12, which no lag of this token
+// reads.
+// ---------------------------------------------------------------------------
+constexpr int DRING = 12;
+
+struct DecodeArgs {
+  void* X;
+  const void* out;
+  void* ring;
+  const int* steps;
+  int B, C, N;
+  const int* idx;
+  const float *p, *h_res, *h_post;
+  const float* conv_w;
+  int use_mgs;
+  float eps_mgs;
+};
+
+// KR = 1 (attention-type, no history): the same per-token write without the
+// ring, used for any batch too small to fill the device with 64-token blocks.
+template <class E, int K, int KR>
+__global__ __launch_bounds__(256) void xhc_decode_post_kernel(DecodeArgs a) {
+  using T = typename E::T;
+  using Qd = Quad<E>;
+  static_assert(KR == 1 || KR == 4, "write components");
+  __shared__ float s_g[4][10];
+  __shared__ float s_Q[K][KR];
+  __shared__ float s_H[K][K];
+  __shared__ int s_I[K];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x, C = a.C;
+  int step = KR == 4 ? a.steps[t] : 0;
+  step = step < 0 ? 0 : step;
+  T* __restrict__ X = reinterpret_cast<T*>(a.X);
+  const T* __restrict__ out = reinterpret_cast<const T*>(a.out) + (size_t)t * C;
+  T* __restrict__ ring = KR == 4 ? reinterpret_cast<T*>(a.ring) + (size_t)t * DRING * C : nullptr;
+
+  // basis [out, g1, g2, g3] of channels c..c+3 of this token
+  auto basis = [&](int c, float (&b)[KR][4]) {
+    if constexpr (KR == 1) {
+      Qd::unpack(ldq<E>(out + c), b[0]);
+      return;
+    }
+    float w1[4][4], w2[8][4], w3[12][4];
+    load_conv_weights(a.conv_w, C, c, true, w1, w2, w3);
+    typename Qd::V v[DRING];
+    v[0] = ldq<E>(out + c);
+#pragma unroll
+    for (int i = 1; i < DRING; ++i)
+      v[i] = i <= step ? ldq<E>(ring + (size_t)((step - i) % DRING) * C + c) : typename Qd::V{};
+    float h[DRING][4];
+#pragma unroll
+    for (int i = 0; i < DRING; ++i) Qd::unpack(v[i], h[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float g1 = 0.f, g2 = 0.f, g3 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g1 = fmaf(w1[i][e], h[i][e], g1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g2 = fmaf(w2[i][e], h[i][e], g2);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) g3 = fmaf(w3[i][e], h[i][e], g3);
+      b[0][e] = h[0][e];
+      b[KR > 1 ? 1 : 0][e] = g1;
+      b[KR > 2 ? 2 : 0][e] = g2;
+      b[KR > 3 ? 3 : 0][e] = g3;
+    }
+  };
+
+  // pass 1: Gram matrix of the basis over all channels (fixed-order sums)
+  if (KR == 4 && a.use_mgs) {
+    float gr[10];
+#pragma unroll
+    for (int j = 0; j < 10; ++j) gr[j] = 0.f;
+    for (int c = tid * PCH; c < C; c += 256 * PCH) {
+      float b[KR][4];
+      basis(c, b);
+      int q = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = u; w < 4; ++w) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d = fmaf(b[u][e], b[w][e], d);
+          gr[q++] += d;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+      const float v = wave_sum(gr[j]);
+      if (lane == 0) s_g[wave][j] = v;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Tm[4][4];
+    if (KR == 4 && a.use_mgs) {
+      float G[4][4];
+      int q = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = u; w < 4; ++w) {
+          const float v = (s_g[0][q] + s_g[1][q]) + (s_g[2][q] + s_g[3][q]);
+          G[u][w] = v;
+          G[w][u] = v;
+          ++q;
+        }
+      mgs_from_gram(G, a.eps_mgs, Tm);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.f : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int ij = a.idx[(size_t)t * K + j];
+      s_I[j] = ij < 0 ? 0 : (ij >= a.N ? a.N - 1 : ij);
+      const float pj = a.p[(size_t)t * K + j];
+#pragma unroll
+      for (int i = 0; i < K; ++i) s_H[j][i] = a.h_res[((size_t)t * K + j) * K + i];
+#pragma unroll
+      for (int b = 0; b < KR; ++b) {
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) sum = fmaf(a.h_post[((size_t)t * K + j) * KR + r], Tm[r][b], sum);
+        s_Q[j][b] = pj * sum;
+      }
+    }
+  }
+  __syncthreads();
+
+  // pass 2: mix and gated write of the k active rows, then the ring slot
+  for (int c = tid * PCH; c < C; c += 256 * PCH) {
+    float b[KR][4];
+    basis(c, b);
+    typename Qd::V xq[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) xq[j] = ldq<E>(X + ((size_t)t * a.N + s_I[j]) * C + c);
+    float xa[K][4];
+#pragma unroll
+    for (int j = 0; j < K; ++j) Qd::unpack(xq[j], xa[j]);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float nv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) sum = fmaf(s_H[j][i], xa[i][e], sum);
+#pragma unroll
+        for (int v = 0; v < KR; ++v) sum = fmaf(s_Q[j][v], b[v][e], sum);
+        nv[e] = sum;
+      }
+      *reinterpret_cast<typename Qd::V*>(X + ((size_t)t * a.N + s_I[j]) * C + c) = Qd::pack(nv);
+    }
+    if constexpr (KR == 4) *reinterpret_cast<typename Qd::V*>(ring + (size_t)(step % DRING) * C + c) = ldq<E>(out + c);
+  }
+}
+
+template <class E, int KR>
+static bool decode_launch(const DecodeArgs& a, int K, hipStream_t st) {
+  switch (K) {
+    case 4: xhc_decode_post_kernel<E, 4, KR><<<a.B, 256, 0, st>>>(a); return true;
+    case 2: xhc_decode_post_kernel<E, 2, KR><<<a.B, 256, 0, st>>>(a); return true;
+    case 1: xhc_decode_post_kernel<E, 1, KR><<<a.B, 256, 0, st>>>(a); return true;
+    default: return false;
+  }
+}
+
 template <class E, int K, int KR>
 static void launch_apply(const XhcPostArgs& a, hipStream_t st) {
   dim3 grid((a.T + PT - 1) / PT, a.nslices);
@@ -478,6 +656,15 @@ static bool xhc_post_launch(const Plan& P, void* X, const void* out, const xhc_w
   a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
   a.conv_w = w->conv_w; a.use_mgs = P.use_mgs; a.eps_mgs = P.eps_mgs;
   a.gram = reinterpret_cast<float*>(ws + P.o_gram);
+  if (P.KR == 1 && ((P.T + PT - 1) / PT) * P.nslices < 512) {
+    // too few 64-token blocks to fill the device: one workgroup per token
+    DecodeArgs d;
+    d.X = X; d.out = out; d.ring = nullptr; d.steps = nullptr;
+    d.B = (int)P.T; d.C = P.C; d.N = P.N;
+    d.idx = a.idx; d.p = a.p; d.h_res = a.h_res; d.h_post = a.h_post;
+    d.conv_w = nullptr; d.use_mgs = 0; d.eps_mgs = P.eps_mgs;
+    return decode_launch<E, 1>(d, P.K, st);
+  }
   if (P.KR == 4 && P.use_mgs) {
     dim3 grid((a.T + PT - 1) / PT, a.nslices);
     xhc_gram_kernel<E><<<grid, 256, 0, st>>>(a);
@@ -491,6 +678,19 @@ static bool xhc_post_launch(const Plan& P, void* X, const void* out, const xhc_w
     case 14: launch_apply<E, 1, 4>(a, st); return true;
     default: return false;
   }
+}
+
+bool launch_xhc_post_decode(const Plan& P, void* X, const void* out, void* ring, const int* steps,
+                            const xhc_weights* w, const char* ws, hipStream_t st) {
+  DecodeArgs a;
+  a.X = X; a.out = out; a.ring = ring; a.steps = steps;
+  a.B = (int)P.T; a.C = P.C; a.N = P.N;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.p = reinterpret_cast<const float*>(ws + P.o_p);
+  a.h_res = reinterpret_cast<const float*>(ws + P.o_hres);
+  a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+  a.conv_w = w->conv_w; a.use_mgs = P.use_mgs; a.eps_mgs = P.eps_mgs;
+  return P.dtype == XHC_BF16 ? decode_launch<Bf16, 4>(a, P.K, st) : decode_launch<F32, 4>(a, P.K, st);
 }
 
 // xHC-Flash attention write (Eq. 18) fused with the MLP input correction
