@@ -557,3 +557,102 @@ def xhc_decode_post(X, out, ring, steps, I, p, h_res, h_post, conv_ws, use_mgs=T
     for b in range(B):
         ring_n[b, steps[b] % RING] = out[b]
     return Xn, ring_n
+
+
+# --------------------------------------------------------------------------
+# xHC-Flash-4sub: one routing and four pre-maps shared by two blocks
+# --------------------------------------------------------------------------
+#
+# Readings (the xHC paper's "Four-sublayer extension" paragraph and Appendix
+# E.2; the E.2 displays were lost in extraction):
+#   * routing (z, I, p) and the four pre-maps H_pre^q, q = 1..4, come from the
+#     group-entry state X^(0), from one projection onto [W_r | W_pre^1..4];
+#   * the input of sublayer q is the non-active base sum_{i not in I}
+#     H_pre^q_i x_i^(0) plus sum_j H_pre^q[I_j] x_act_j^(q), the active rows as
+#     they stand before sublayer q (for q = 1 this is the plain dense read);
+#   * sublayers 1-3 write only the active rows, without residual mixing:
+#     x_act_j += p_j sum_r H_post^q_jr v_r^(q) (K_r = 1 after attention, the
+#     temporal basis after the first MLP); the final MLP mixes with H_res and
+#     writes as full xHC does;
+#   * each sublayer's active-side maps (H_post^q, and H_res at the final MLP)
+#     come from RMSNorm of the active rows before that sublayer;
+#   * stored tensors (the bases, each input, the state after each write) are
+#     rounded to the state dtype where they are stored.
+
+def xhcf4_pre(X, W_full, m, k, alpha_pre, b_pre):
+    """Group entry of xHC-Flash-4sub.  X: [T, N, C]; W_full: [N*C, 5N] with
+    columns router | pre^1 | pre^2 | pre^3 | pre^4; alpha_pre, b_pre: four
+    scales and four [N] biases.  Returns z, I, p, h_pre [4][T, N], the first
+    sublayer's input (dense read with H_pre^1) and the non-active bases of
+    sublayers 2..4 [3][T, C] (xHC paper, "Four-sublayer extension";
+    Appendix E.2)."""
+    X = np.asarray(X, dtype=np.float64)
+    W_full = np.asarray(W_full, dtype=np.float64)
+    T, N, C = X.shape
+    x = X.reshape(T, N * C)
+    z = ln_normalize(x) @ W_full[:, :N]
+    I, p = xhc_select(z, m, k)
+    xr = rms_normalize(x)
+    h_pre = [sigmoid(alpha_pre[q] * (xr @ W_full[:, (q + 1) * N:(q + 2) * N]) + np.asarray(b_pre[q]))
+             for q in range(4)]
+    inactive = np.ones((T, N))
+    np.put_along_axis(inactive, I, 0.0, axis=1)
+    inp1 = np.einsum("tn,tnc->tc", h_pre[0], X)
+    bases = [np.einsum("tn,tnc->tc", h_pre[q] * inactive, X) for q in (1, 2, 3)]
+    return dict(z=z, I=I, p=p, h_pre=h_pre, inp1=inp1, bases=bases)
+
+
+def xhcf4_input(base, Xa, I, h_pre_q):
+    """Input of a later sublayer: its non-active base plus its pre-map applied
+    to the current active rows Xa [T, k, C] (reading of Appendix E.2)."""
+    hI = np.take_along_axis(np.asarray(h_pre_q, dtype=np.float64), I, axis=1)
+    return np.asarray(base, dtype=np.float64) + np.einsum("tj,tjc->tc", hI, np.asarray(Xa, dtype=np.float64))
+
+
+def xhcf4_post_map(Xa, W_post, K_r, alpha_post, b_post):
+    """H_post of an unmixed sublayer from its active rows: 2 sigmoid(alpha
+    RMSNorm(vec Xa) W_post + b), W_post [k*C, k*K_r] (entry (j, r) at column
+    j*K_r + r).  Returns [T, k, K_r]."""
+    Xa = np.asarray(Xa, dtype=np.float64)
+    T, k, C = Xa.shape
+    la = rms_normalize(Xa.reshape(T, k * C)) @ np.asarray(W_post, dtype=np.float64)
+    return 2.0 * sigmoid(alpha_post * la.reshape(T, k, K_r) + np.asarray(b_post).reshape(k, K_r))
+
+
+def xhcf4_group(X, outs, W_full, W_posts, W_act_last, m, k, conv_ws, alpha, b, iters=20, use_mgs=True,
+                dtype="f64"):
+    """Two blocks (attention, MLP, attention, MLP) of xHC-Flash-4sub.
+
+    X: [T, N, C]; outs: four [B, S, C] sublayer outputs; W_full [N*C, 5N];
+    W_posts: [W_post^1 [k*C, k], W_post^2 [k*C, k*K_r], W_post^3 [k*C, k]];
+    W_act_last: [k*C, k*k + k*K_r] (W_res, then W_post^4); conv_ws: kernels of
+    the two MLP sublayers (lists of [kappa, C]); alpha = dict(pre=(4), post=(4),
+    res); b = dict(pre=[4 x N], post=[4 arrays], res).
+
+    Returns the group's inputs [4][T, C], the state after each sublayer
+    [4][T, N, C], the maps and the routing."""
+    X = np.asarray(X, dtype=np.float64)
+    T, N, C = X.shape
+    pre = xhcf4_pre(X, W_full, m, k, alpha["pre"], b["pre"])
+    I, p = pre["I"], pre["p"]
+    bases = [round_state(bq, dtype) for bq in pre["bases"]]
+    inputs = [round_state(pre["inp1"], dtype)]
+    states, maps = [], []
+    Xc = X.copy()
+    for q in range(4):
+        Xa = np.take_along_axis(Xc, I[:, :, None], axis=1)
+        if q > 0:
+            inputs.append(round_state(xhcf4_input(bases[q - 1], Xa, I, pre["h_pre"][q]), dtype))
+        mlp = q % 2 == 1
+        K_r = 1 + len(conv_ws[q // 2]) if mlp else 1
+        if q < 3:
+            h_post = xhcf4_post_map(Xa, W_posts[q], K_r, alpha["post"][q], b["post"][q])
+            h_res = np.tile(np.eye(k), (T, 1, 1))
+        else:
+            h_res, h_post = xhcf_mlp_maps(Xc, I, W_act_last, K_r, alpha["res"], alpha["post"][3], b["res"],
+                                          b["post"][3], iters)
+        convs = conv_ws[q // 2] if mlp else []
+        Xc = round_state(xhc_post(Xc, outs[q], I, p, h_res, h_post, convs, use_mgs), dtype)
+        states.append(Xc)
+        maps.append(dict(h_post=h_post, h_res=h_res))
+    return dict(z=pre["z"], I=I, p=p, h_pre=pre["h_pre"], inputs=inputs, bases=bases, states=states, maps=maps)

@@ -173,3 +173,107 @@ def test_flash_block_matches_scalar_brute_force(mlp_convs):
                      ("X1", bf["X1"]), ("X", bf["X"]), ("alpha", bf["alpha_corr"])):
         ref = np.array(ref)
         np.testing.assert_allclose(res[key], ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max(), err_msg=key)
+
+
+# ---------------------------------------------------------------- xHC-Flash-4sub
+
+def flash4_inputs(r, T, N, k, C, B=1, wstd=0.3):
+    S = T // B
+    return dict(
+        X=r.standard_normal((T, N, C)),
+        outs=[r.standard_normal((B, S, C)) for _ in range(4)],
+        W_full=r.standard_normal((N * C, 5 * N)) * wstd,
+        W_posts=[r.standard_normal((k * C, k)) * wstd, r.standard_normal((k * C, 4 * k)) * wstd,
+                 r.standard_normal((k * C, k)) * wstd],
+        W_act_last=r.standard_normal((k * C, k * k + 4 * k)) * wstd,
+        convs=[[r.standard_normal((kap, C)) / kap for kap in (4, 8, 12)] for _ in range(2)],
+        alpha=dict(pre=(0.7, 0.9, 0.6, 1.2), post=(0.8, 0.5, 1.1, 0.6), res=1.1),
+        b=dict(pre=[r.standard_normal(N) * 0.1 for _ in range(4)],
+               post=[r.standard_normal(k) * 0.1, r.standard_normal(4 * k) * 0.1, r.standard_normal(k) * 0.1,
+                     r.standard_normal(4 * k) * 0.1], res=r.standard_normal(k * k) * 0.1),
+    )
+
+
+def run_group(d, m, k, dtype="f64"):
+    return O.xhcf4_group(d["X"], d["outs"], d["W_full"], d["W_posts"], d["W_act_last"], m, k, d["convs"],
+                         d["alpha"], d["b"], dtype=dtype)
+
+
+def test_4sub_inputs_are_dense_reads_of_the_current_state():
+    """Appendix E.2: with routing and the four pre-maps fixed at the group
+    entry and no residual mixing before the last sublayer, each sublayer's
+    input (non-active base + pre-map on the current active rows) equals that
+    pre-map applied to the whole state as it stands before the sublayer."""
+    r = rng(21)
+    T, N, k, m, C = 24, 16, 4, 2, 16
+    d = flash4_inputs(r, T, N, k, C, B=2)
+    g = run_group(d, m, k)
+    prev = [d["X"]] + g["states"][:3]
+    for q in range(4):
+        direct = np.einsum("tn,tnc->tc", g["h_pre"][q], prev[q])
+        np.testing.assert_allclose(g["inputs"][q], direct, rtol=0, atol=1e-12 * np.abs(direct).max(), err_msg=str(q))
+
+
+def test_4sub_first_two_sublayers_are_an_xhc_flash_block():
+    """Up to the second sublayer's input, a 4-sublayer group is an xHC-Flash
+    block with the same router, first two pre-maps and attention post-map:
+    same routing, same attention input and write, and the MLP input of the
+    Eq. 19 correction equals the active-state form."""
+    r = rng(22)
+    T, N, k, m, C = 20, 8, 4, 2, 16
+    d = flash4_inputs(r, T, N, k, C)
+    g = run_group(d, m, k)
+    a = d["alpha"]
+    fl = O.xhcf_block(d["X"], d["outs"][0], d["outs"][1], d["W_full"][:, :3 * N], d["W_posts"][0],
+                      d["W_act_last"], m, k, d["convs"][0], (a["pre"][0], a["pre"][1], a["post"][0], a["res"],
+                                                             a["post"][3]),
+                      d["b"]["pre"][0], d["b"]["pre"][1], d["b"]["post"][0], d["b"]["res"], d["b"]["post"][3])
+    np.testing.assert_array_equal(g["I"], fl["I"])
+    np.testing.assert_allclose(g["inputs"][0], fl["inp_attn"], rtol=1e-13)
+    np.testing.assert_allclose(g["maps"][0]["h_post"][:, :, 0], fl["h_post_attn"], rtol=1e-13)
+    np.testing.assert_allclose(g["states"][0], fl["X1"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(g["inputs"][1], fl["inp_mlp"], rtol=1e-12, atol=1e-12)
+
+
+def test_4sub_unmixed_mlp_post_map_addresses_position_and_component():
+    """The unmixed MLP post-map reads column j*K_r + r for position j and
+    component r: a weight with one non-zero column moves only that entry."""
+    r = rng(23)
+    T, k, C, K_r = 5, 4, 8, 4
+    Xa = r.standard_normal((T, k, C))
+    for j, rr in ((0, 0), (2, 3), (3, 1)):
+        W = np.zeros((k * C, k * K_r))
+        W[:, j * K_r + rr] = r.standard_normal(k * C)
+        h = O.xhcf4_post_map(Xa, W, K_r, 0.9, np.zeros(k * K_r))
+        moved = np.abs(h - 1.0) > 1e-12
+        assert moved[:, j, rr].all() and moved.sum() == T
+
+
+def test_4sub_one_stream_is_four_plain_residual_steps():
+    r = rng(24)
+    T, C = 12, 16
+    d = flash4_inputs(r, T, 1, 1, C)
+    d.update(alpha=dict(pre=(0.0,) * 4, post=(0.0,) * 4, res=0.0),
+             b=dict(pre=[np.full(1, 40.0)] * 4, post=[np.zeros(1), np.zeros(4), np.zeros(1), np.zeros(4)],
+                    res=np.zeros(1)),
+             convs=[[np.zeros((kap, C)) for kap in (4, 8, 12)] for _ in range(2)])
+    g = run_group(d, 1, 1)
+    x = d["X"][:, 0, :]
+    o = [v.reshape(T, C) for v in d["outs"]]
+    run = x.copy()
+    for q in range(4):
+        np.testing.assert_allclose(g["inputs"][q], run, rtol=0, atol=1e-14)
+        run = run + o[q]
+        np.testing.assert_allclose(g["states"][q][:, 0, :], run, rtol=0, atol=1e-14)
+
+
+def test_4sub_changes_only_the_shared_active_rows():
+    r = rng(25)
+    T, N, k, m, C = 16, 16, 4, 2, 16
+    d = flash4_inputs(r, T, N, k, C)
+    d["X"] = O.round_state(d["X"], "bf16")
+    g = run_group(d, m, k, dtype="bf16")
+    for t in range(T):
+        act = set(g["I"][t].tolist())
+        for i in range(N):
+            assert np.array_equal(g["states"][3][t, i], d["X"][t, i]) == (i not in act), (t, i)
