@@ -315,6 +315,81 @@ xhc_status xhcf_mid(const xhc_config* cfg, const xhcf_weights* w, void* X, const
 xhc_status xhcf_post(const xhc_config* cfg, const xhcf_weights* w, void* X, const void* out_mlp, void* ws,
                      xhc_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * xHC-Flash-4sub: two blocks (attention, MLP, attention, MLP) sharing one
+ * routing decision (xHC paper "xHC: Expanded Hyper-Connections", section
+ * "xHC-Flash", paragraph "Four-sublayer extension", and Appendix E.2).
+ *
+ * From the group-entry state X one projection gives the router logits and
+ * four separate pre-maps; the active set I and router weights p are shared by
+ * the four sublayers.  The input of sublayer q is the non-active base
+ * sum_{i not in I} H_pre^q_i x_i of the group-entry state plus
+ * sum_j H_pre^q[I_j] x_{I_j} of the active rows as they stand before sublayer
+ * q, which equals H_pre^q applied to the whole current state.  Sublayers 1-3
+ * write only the active rows, without residual mixing: x_{I_j} gains
+ * p_j sum_r H_post^q_jr v_r (one component after attention, the temporal
+ * basis after the first MLP); each sublayer's post-map comes from RMSNorm of
+ * the active rows before it.  The final MLP is full xHC's: H_res and H_post
+ * from its active rows, then the k x k mix and gated write.
+ *
+ * Per group, on one stream and one workspace:
+ *
+ *   xhcf4_pre (cfg, w, X, inp, bases, ws)          inp: input of sublayer 1
+ *   for q = 1..4:
+ *     out = F_q(inp)
+ *     xhcf4_post(cfg, w, q, X, out, bases, inp, ws)  X written; for q < 4
+ *                                                   inp := input of q + 1
+ *
+ * bases: [3][T][C] of the state dtype (the non-active bases of sublayers
+ * 2-4), caller-owned, written by xhcf4_pre and read by xhcf4_post.  cfg:
+ * N, k, m, C, batch, seq, dtype, sinkhorn_iters, eps; n_convs (0 or 3) and
+ * use_mgs describe both MLP sublayers.  Supported (N, k): (16, 4), (8, 4),
+ * (4, 4), (1, 1).
+ * ------------------------------------------------------------------------- */
+
+/* Weights of one xHC-Flash-4sub group (host struct holding device pointers). */
+typedef struct {
+  /* [N*C][5N], state dtype: router W_r, then the pre-maps of sublayers 1-4 */
+  const void* w_full;
+  /* post-maps of sublayers 1-3, state dtype, rows j*C + c for position j:
+   * [k*C][k] (attention), [k*C][k*K_r] (entry (j, r) at j*K_r + r), [k*C][k] */
+  const void* w_post[3];
+  /* final MLP: [k*C][k*k + k*K_r] = W_res (i*k + j), then W_post (k^2 + j*K_r + r) */
+  const void* w_act_last;
+  /* the two MLP sublayers' [24][C] float kernels (NULL when n_convs == 0) */
+  const float* conv_w[2];
+  /* float biases: pre-maps [N] each; post-maps [k], [k*K_r], [k], [k*K_r]; W_res [k*k] */
+  const float* b_pre[4];
+  const float* b_post[4];
+  const float* b_res;
+  float alpha_pre[4], alpha_post[4], alpha_res;
+} xhcf4_weights;
+
+/* Byte offsets of the public arrays of an xHC-Flash-4sub workspace. */
+typedef struct {
+  size_t idx;       /* [T][k] int32 */
+  size_t p;         /* [T][k] */
+  size_t h_pre;     /* [4][T][N], the pre-maps of sublayers 1-4 */
+  size_t h_post;    /* [T][k][K_q]: the post-map of the next sublayer to write */
+  size_t h_res;     /* [T][k][k], the final MLP's (after xhcf4_post with q = 3) */
+  size_t z_router;  /* [T][N] */
+  size_t total;
+} xhcf4_ws_layout;
+
+size_t xhcf4_workspace_bytes(const xhc_config* cfg);
+xhc_status xhcf4_workspace_layout(const xhc_config* cfg, xhcf4_ws_layout* out);
+
+/* Group entry: routing, the four pre-maps, the first sublayer's input (dense
+ * read of X) and post-map, and the non-active bases of sublayers 2-4. */
+xhc_status xhcf4_pre(const xhc_config* cfg, const xhcf4_weights* w, const void* X, void* inp, void* bases,
+                     void* ws, xhc_stream_t stream);
+
+/* After sublayer q (1..4) with output out: its write to the active rows of X
+ * (in place); for q < 4 also the input of sublayer q + 1 into inp and that
+ * sublayer's active maps into ws. */
+xhc_status xhcf4_post(const xhc_config* cfg, const xhcf4_weights* w, int32_t q, void* X, const void* out,
+                      const void* bases, void* inp, void* ws, xhc_stream_t stream);
+
 /* Message for the last non-OK status returned on this host thread. */
 const char* xhc_last_error(void);
 

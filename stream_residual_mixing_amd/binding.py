@@ -27,6 +27,7 @@ EXPORTS = (
     "xhc_workspace_bytes", "mhc_workspace_bytes", "xhc_workspace_layout", "mhc_workspace_layout",
     "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_route", "xhc_pre_chained", "xhc_post_chained",
     "xhc_post_decode", "xhcf_workspace_bytes", "xhcf_workspace_layout", "xhcf_pre", "xhcf_mid", "xhcf_post",
+    "xhcf4_workspace_bytes", "xhcf4_workspace_layout", "xhcf4_pre", "xhcf4_post",
     "xhc_last_error",
 )
 
@@ -66,6 +67,19 @@ class XhcfWeights(ctypes.Structure):
 class XhcfWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre_attn", "h_pre_mlp", "h_post_attn", "h_res",
                                                "h_post_mlp", "z_router", "total")]
+
+
+class Xhcf4Weights(ctypes.Structure):
+    _fields_ = [
+        ("w_full", ctypes.c_void_p), ("w_post", ctypes.c_void_p * 3), ("w_act_last", ctypes.c_void_p),
+        ("conv_w", ctypes.c_void_p * 2), ("b_pre", ctypes.c_void_p * 4), ("b_post", ctypes.c_void_p * 4),
+        ("b_res", ctypes.c_void_p), ("alpha_pre", ctypes.c_float * 4), ("alpha_post", ctypes.c_float * 4),
+        ("alpha_res", ctypes.c_float),
+    ]
+
+
+class Xhcf4WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre", "h_post", "h_res", "z_router", "total")]
 
 
 class XhcError(RuntimeError):
@@ -167,6 +181,35 @@ class FlashWeights:
         return w
 
 
+@dataclass
+class Flash4Weights:
+    """Device tensors of one xHC-Flash-4sub group (kept alive by this object)."""
+    w_full: torch.Tensor          # [N*C, 5N]
+    w_post: list                  # 3 tensors: [k*C, k], [k*C, k*K_r], [k*C, k]
+    w_act_last: torch.Tensor      # [k*C, k*k + k*K_r]
+    b_pre: list                   # 4 x [N]
+    b_post: list                  # [k], [k*K_r], [k], [k*K_r]
+    b_res: torch.Tensor
+    alpha_pre: tuple
+    alpha_post: tuple
+    alpha_res: float
+    conv_w: list = field(default_factory=lambda: [None, None])
+
+    def c(self) -> Xhcf4Weights:
+        w = Xhcf4Weights()
+        ptr = lambda t: t.data_ptr() if t is not None else 0
+        w.w_full, w.w_act_last, w.b_res = ptr(self.w_full), ptr(self.w_act_last), ptr(self.b_res)
+        for i in range(3):
+            w.w_post[i] = ptr(self.w_post[i])
+        for i in range(2):
+            w.conv_w[i] = ptr(self.conv_w[i])
+        for i in range(4):
+            w.b_pre[i], w.b_post[i] = ptr(self.b_pre[i]), ptr(self.b_post[i])
+            w.alpha_pre[i], w.alpha_post[i] = float(self.alpha_pre[i]), float(self.alpha_post[i])
+        w.alpha_res = float(self.alpha_res)
+        return w
+
+
 def _check(t, name, shape, dtype):
     if t is None:
         raise ValueError(f"{name} is required")
@@ -229,6 +272,17 @@ class Lib:
         d.xhcf_post.restype = ctypes.c_int
         d.xhcf_post.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcfWeights), ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        d.xhcf4_workspace_bytes.restype = ctypes.c_size_t
+        d.xhcf4_workspace_bytes.argtypes = [ctypes.POINTER(XhcConfig)]
+        d.xhcf4_workspace_layout.restype = ctypes.c_int
+        d.xhcf4_workspace_layout.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(Xhcf4WsLayout)]
+        d.xhcf4_pre.restype = ctypes.c_int
+        d.xhcf4_pre.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(Xhcf4Weights), ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        d.xhcf4_post.restype = ctypes.c_int
+        d.xhcf4_post.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(Xhcf4Weights), ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
         d.xhc_last_error.restype = ctypes.c_char_p
         d.xhc_last_error.argtypes = []
 
@@ -452,6 +506,73 @@ class Lib:
                                     ws.data_ptr(), _stream_ptr(stream)))
 
 
+    # xHC-Flash-4sub group: two blocks sharing one routing
+    def flash4_workspace_bytes(self, cfg: Config) -> int:
+        c = cfg.c()
+        return int(self.dll.xhcf4_workspace_bytes(ctypes.byref(c)))
+
+    def flash4_layout(self, cfg: Config) -> Xhcf4WsLayout:
+        c, L = cfg.c(), Xhcf4WsLayout()
+        self._ok(self.dll.xhcf4_workspace_layout(ctypes.byref(c), ctypes.byref(L)))
+        return L
+
+    def flash4_workspace(self, cfg: Config, device="cuda") -> torch.Tensor:
+        n = self.flash4_workspace_bytes(cfg)
+        if n == 0 and cfg.T > 0:
+            self.flash4_layout(cfg)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def flash4_ws_arrays(self, cfg: Config, ws: torch.Tensor, K_q: int) -> dict:
+        """Views of the public arrays; h_post has K_q components (those of the
+        next sublayer to write)."""
+        L = self.flash4_layout(cfg)
+        T, N, k = cfg.T, cfg.N, cfg.k
+
+        def view(off, shape, dt=torch.float32):
+            n = 1
+            for s in shape:
+                n *= s
+            return ws[off: off + 4 * n].view(dt).reshape(shape)
+
+        return dict(idx=view(L.idx, (T, k), torch.int32), p=view(L.p, (T, k)), h_pre=view(L.h_pre, (4, T, N)),
+                    h_post=view(L.h_post, (T, k, K_q)), h_res=view(L.h_res, (T, k, k)), z=view(L.z_router, (T, N)))
+
+    def _check_flash4(self, cfg, w, X, ws):
+        _check(X, "X", (cfg.T, cfg.N, cfg.C), cfg.torch_dtype)
+        need = self.flash4_workspace_bytes(cfg)
+        if ws is None or not ws.is_cuda or ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace must be a GPU tensor of at least {need} bytes")
+        dt, k, N, Kr = cfg.torch_dtype, cfg.k, cfg.N, cfg.K_r
+        _check(w.w_full, "w_full", (N * cfg.C, 5 * N), dt)
+        for i, nc in enumerate((k, k * Kr, k)):
+            _check(w.w_post[i], f"w_post[{i}]", (k * cfg.C, nc), dt)
+        _check(w.w_act_last, "w_act_last", (k * cfg.C, k * k + k * Kr), dt)
+        for i in range(4):
+            _check(w.b_pre[i], f"b_pre[{i}]", (N,), torch.float32)
+            _check(w.b_post[i], f"b_post[{i}]", ((k * Kr) if i % 2 else k,), torch.float32)
+        _check(w.b_res, "b_res", (k * k,), torch.float32)
+        if Kr == 4:
+            for i in range(2):
+                _check(w.conv_w[i], f"conv_w[{i}]", (sum(cfg.kernels), cfg.C), torch.float32)
+
+    def xhcf4_pre(self, cfg: Config, w: Flash4Weights, X, inp, bases, ws, stream=None):
+        self._check_flash4(cfg, w, X, ws)
+        _check(inp, "inp", (cfg.T, cfg.C), cfg.torch_dtype)
+        _check(bases, "bases", (3, cfg.T, cfg.C), cfg.torch_dtype)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhcf4_pre(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), inp.data_ptr(),
+                                    bases.data_ptr(), ws.data_ptr(), _stream_ptr(stream)))
+
+    def xhcf4_post(self, cfg: Config, w: Flash4Weights, q, X, out, bases, inp, ws, stream=None):
+        self._check_flash4(cfg, w, X, ws)
+        _check_out(out, cfg)
+        _check(inp, "inp", (cfg.T, cfg.C), cfg.torch_dtype)
+        _check(bases, "bases", (3, cfg.T, cfg.C), cfg.torch_dtype)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhcf4_post(ctypes.byref(c), ctypes.byref(cw), int(q), X.data_ptr(), out.data_ptr(),
+                                     bases.data_ptr(), inp.data_ptr(), ws.data_ptr(), _stream_ptr(stream)))
+
+
 _INSTANCE = None
 
 
@@ -486,3 +607,14 @@ def flash_weights_to_device(wd: dict, device="cuda") -> FlashWeights:
         **{n: dev(wd[n].float()) for n in ("b_pre_attn", "b_pre_mlp", "b_post_attn", "b_res", "b_post_mlp")},
         **{n: float(wd[n]) for n in ("alpha_pre_attn", "alpha_pre_mlp", "alpha_post_attn", "alpha_res",
                                      "alpha_post_mlp")})
+
+
+def flash4_weights_to_device(wd: dict, device="cuda") -> Flash4Weights:
+    """Move a dict from ``synth.xhcf4_group_weights`` (CPU tensors) to the GPU."""
+    dev = lambda t: t.contiguous().to(device)
+    convs = [torch.cat(c, 0).contiguous().to(device) if c else None for c in wd["conv"]]
+    return Flash4Weights(
+        w_full=dev(wd["w_full"]), w_post=[dev(t) for t in wd["w_post"]], w_act_last=dev(wd["w_act_last"]),
+        b_pre=[dev(t.float()) for t in wd["b_pre"]], b_post=[dev(t.float()) for t in wd["b_post"]],
+        b_res=dev(wd["b_res"].float()), alpha_pre=tuple(wd["alpha_pre"]), alpha_post=tuple(wd["alpha_post"]),
+        alpha_res=float(wd["alpha_res"]), conv_w=convs)

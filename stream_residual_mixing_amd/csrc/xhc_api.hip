@@ -222,6 +222,43 @@ xhc_status make_flash_plan(const xhc_config* cfg, xhc::Plan* P) {
   return XHC_OK;
 }
 
+// xHC-Flash-4sub group plan: the block plan with 5N full-state columns, four
+// pre-maps and the packed post-maps of sublayers 1-3.
+xhc_status make_flash4_plan(const xhc_config* cfg, xhc::Plan* P) {
+  xhc::Plan q;
+  xhc_status s = make_flash_plan(cfg, &q);
+  if (s != XHC_OK) return s;
+  q.ncol_full = 5 * q.N;
+  q.NTF = (q.ncol_full + 15) / 16;
+  const size_t T = (size_t)q.T, N = q.N, K = q.K;
+  const int ntq[3] = {1, (q.K * q.KR + 15) / 16, 1};
+  const int ntmax = q.NTA > ntq[1] ? q.NTA : ntq[1];
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  q.o_idx = take(T * K * 4);
+  q.o_p = take(T * K * 4);
+  q.o_hpre = take(4 * T * N * 4);
+  q.o_hpost = take(T * K * q.KR * 4);
+  q.o_hres = take(T * K * K * 4);
+  q.o_z = take(T * N * 4);
+  q.o_hpre_m = SIZE_MAX; q.o_hpost_a = SIZE_MAX; q.o_wact_a = SIZE_MAX;
+  q.o_colsum = take((1 + 256) * N * 4);
+  q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
+  for (int i = 0; i < 3; ++i) q.o_wq[i] = take((size_t)q.nkb_act * ntq[i] * 64 * 16);
+  q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
+  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
+  q.o_stats = take((size_t)q.KS * T * 2 * 4);
+  q.o_part2 = take((size_t)q.ntiles * q.G2 * (16 * (size_t)ntmax * 16 + 16) * 4);
+  q.o_gram = take((size_t)q.nslices * T * 10 * 4);
+  q.total = q.T == 0 ? 0 : off;
+  *P = q;
+  return XHC_OK;
+}
+
 xhc_status check_flash_weights(const xhc::Plan& P, const xhcf_weights* w, int stage) {
   if (!w) return fail(XHC_ERR_INVALID_ARG, "weights is NULL");
   if (stage == 0) {
@@ -541,6 +578,81 @@ xhc_status xhcf_post(const xhc_config* cfg, const xhcf_weights* w, void* X, cons
   wx.conv_w = w->conv_w;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (!xhc::launch_xhc_post(P, X, out_mlp, &wx, static_cast<char*>(ws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+size_t xhcf4_workspace_bytes(const xhc_config* cfg) {
+  xhc::Plan P;
+  return make_flash4_plan(cfg, &P) == XHC_OK ? P.total : 0;
+}
+
+xhc_status xhcf4_workspace_layout(const xhc_config* cfg, xhcf4_ws_layout* out) {
+  xhc::Plan P;
+  xhc_status s = make_flash4_plan(cfg, &P);
+  if (s != XHC_OK) return s;
+  if (!out) return fail(XHC_ERR_INVALID_ARG, "layout output is NULL");
+  out->idx = P.o_idx;
+  out->p = P.o_p;
+  out->h_pre = P.o_hpre;
+  out->h_post = P.o_hpost;
+  out->h_res = P.o_hres;
+  out->z_router = P.o_z;
+  out->total = P.total;
+  return XHC_OK;
+}
+
+xhc_status xhcf4_pre(const xhc_config* cfg, const xhcf4_weights* w, const void* X, void* inp, void* bases, void* ws,
+                     xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_flash4_plan(cfg, &P);
+  if (s != XHC_OK) return s;
+  if (!w) return fail(XHC_ERR_INVALID_ARG, "weights is NULL");
+  bool ok = w->w_full && aligned16(w->w_full);
+  for (int q = 0; q < 3; ++q) ok = ok && w->w_post[q] && aligned16(w->w_post[q]);
+  ok = ok && w->w_act_last && aligned16(w->w_act_last);
+  if (!ok) return fail(XHC_ERR_INVALID_ARG, "w_full, w_post[0..2] and w_act_last must be 16-byte aligned pointers");
+  for (int q = 0; q < 4; ++q) {
+    if (!w->b_pre[q]) return fail(XHC_ERR_INVALID_ARG, "b_pre[%d] must not be NULL", q);
+    if (!std::isfinite(w->alpha_pre[q])) return fail(XHC_ERR_INVALID_ARG, "alpha scales must be finite");
+  }
+  if (!w->b_post[0] || !std::isfinite(w->alpha_post[0]))
+    return fail(XHC_ERR_INVALID_ARG, "b_post[0] must not be NULL and alpha_post[0] finite");
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, inp, ws, nullptr, false)) != XHC_OK) return s;
+  if (!bases || !aligned16(bases)) return fail(XHC_ERR_INVALID_ARG, "bases must be a 16-byte aligned pointer");
+  if (bases == X || bases == inp || bases == ws) return fail(XHC_ERR_INVALID_ARG, "bases must not alias X, inp or ws");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhcf4_pre(P, w, X, inp, bases, static_cast<char*>(ws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status xhcf4_post(const xhc_config* cfg, const xhcf4_weights* w, int32_t q, void* X, const void* out,
+                      const void* bases, void* inp, void* ws, xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_flash4_plan(cfg, &P);
+  if (s != XHC_OK) return s;
+  if (!w) return fail(XHC_ERR_INVALID_ARG, "weights is NULL");
+  if (q < 1 || q > 4) return fail(XHC_ERR_INVALID_ARG, "sublayer q=%d outside 1..4", q);
+  if ((q == 2 || q == 4) && P.KR == 4 && (!w->conv_w[q / 2 - 1] || !aligned16(w->conv_w[q / 2 - 1])))
+    return fail(XHC_ERR_INVALID_ARG, "conv_w[%d] must be a 16-byte aligned pointer when n_convs == 3", q / 2 - 1);
+  if (q < 4) {
+    if (!w->b_post[q] || !std::isfinite(w->alpha_post[q]))
+      return fail(XHC_ERR_INVALID_ARG, "b_post[%d] must not be NULL and alpha_post[%d] finite", q, q);
+    if (q == 3 && (!w->b_res || !std::isfinite(w->alpha_res)))
+      return fail(XHC_ERR_INVALID_ARG, "b_res must not be NULL and alpha_res finite");
+  }
+  if (P.T == 0) return XHC_OK;
+  if ((s = check_state_ws(X, out, ws, nullptr, false)) != XHC_OK) return s;
+  if (q < 4) {
+    if (!bases || !aligned16(bases) || !inp || !aligned16(inp))
+      return fail(XHC_ERR_INVALID_ARG, "bases and inp must be 16-byte aligned pointers");
+    if (inp == X || inp == ws || inp == out || inp == bases || bases == X || bases == ws)
+      return fail(XHC_ERR_INVALID_ARG, "inp and bases must not alias X, out, ws or each other");
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhcf4_post(P, w, q, X, out, bases, inp, static_cast<char*>(ws), st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }

@@ -72,31 +72,33 @@ __global__ __launch_bounds__(64) void flash_colsum_fin_kernel(const float* __res
 }
 
 struct FlashRouteArgs {
-  int T, m, KS, NP;
+  int T, m, KS, NP;     // NP: columns per token of the projection partials
   long n_el;
-  const float* part;    // [KS][T][NP]: router | pre^A | pre^M
+  const float* part;    // [KS][T][NP]: router | pre-map 0 | pre-map 1 | ...
   const float* stats;   // [KS][T][2]: sum x, sum x^2
   const float* cs;      // [N]
-  const float *b_pa, *b_pm;
-  float a_pa, a_pm, eps;
+  const float* b_pre[4];
+  float a_pre[4], eps;
   int* idx;
-  float *p, *h_pa, *h_pm, *z;
+  float *p, *z;
+  float* h_pre[4];      // [T][N] per pre-map
 };
 
-// One token per thread: LayerNorm-corrected router logits, both RMS-scaled
-// pre-maps, fixed-m + routed top-(k-m) and the router weights.
-template <int N, int K>
+// One token per thread: LayerNorm-corrected router logits, the NPRE
+// RMS-scaled pre-maps, fixed-m + routed top-(k-m) and the router weights.
+template <int N, int K, int NPRE>
 __global__ __launch_bounds__(256) void flash_route_kernel(FlashRouteArgs a) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= a.T) return;
-  float raw[3 * N];
+  constexpr int NC = (1 + NPRE) * N;
+  float raw[NC];
 #pragma unroll
-  for (int c = 0; c < 3 * N; ++c) raw[c] = 0.f;
+  for (int c = 0; c < NC; ++c) raw[c] = 0.f;
   float q1 = 0.f, q2 = 0.f;
   for (int ks = 0; ks < a.KS; ++ks) {
     const float* pp = a.part + ((size_t)ks * a.T + t) * a.NP;
 #pragma unroll
-    for (int c = 0; c < 3 * N; ++c) raw[c] += pp[c];
+    for (int c = 0; c < NC; ++c) raw[c] += pp[c];
     q1 += a.stats[((size_t)ks * a.T + t) * 2];
     q2 += a.stats[((size_t)ks * a.T + t) * 2 + 1];
   }
@@ -104,12 +106,15 @@ __global__ __launch_bounds__(256) void flash_route_kernel(FlashRouteArgs a) {
   float z[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    float hpa, hpm, zz;
-    route_logits(raw[i], raw[N + i], q1, q2, a.cs[i], n_el, a.eps, a.a_pa, a.b_pa[i], true, &z[i], &hpa);
-    route_logits(raw[i], raw[2 * N + i], q1, q2, a.cs[i], n_el, a.eps, a.a_pm, a.b_pm[i], true, &zz, &hpm);
+#pragma unroll
+    for (int q = 0; q < NPRE; ++q) {
+      float hp, zz;
+      route_logits(raw[i], raw[(1 + q) * N + i], q1, q2, a.cs[i], n_el, a.eps, a.a_pre[q], a.b_pre[q][i], true, &zz,
+                   &hp);
+      if (q == 0) z[i] = zz;
+      a.h_pre[q][(size_t)t * N + i] = hp;
+    }
     a.z[(size_t)t * N + i] = z[i];
-    a.h_pa[(size_t)t * N + i] = hpa;
-    a.h_pm[(size_t)t * N + i] = hpm;
   }
   int sel[K];
   route_select<N, K>(z, a.m, sel);
@@ -122,20 +127,23 @@ __global__ __launch_bounds__(256) void flash_route_kernel(FlashRouteArgs a) {
 
 struct FlashReadArgs {
   const void* X;
-  void *inp_a, *inp_m;
-  int T, C;
-  const float *h_pa, *h_pm;
+  void* out[4];
+  int T, C, K;
+  const float* h_pre[4];
+  const int* idx;   // MASK only
 };
 
-// Both readouts from one pass over X (Eq. 17).  A workgroup is one 16-token
-// tile times a slice of 8 contraction blocks; each wave loads its block of
-// all N streams at once (lane (g, r): token r, VEC channels), forms both
-// weighted sums and stores them.
-template <class E, int N>
+// The NPRE readouts from one pass over X (Eq. 17).  A workgroup is one
+// 16-token tile times a slice of 8 contraction blocks; each wave loads its
+// block of all N streams at once (lane (g, r): token r, VEC channels) and
+// forms every weighted sum.  With MASK, readouts 1.. leave out the token's
+// active streams (the non-active bases of xHC-Flash-4sub).
+template <class E, int N, int NPRE, bool MASK>
 __global__ __launch_bounds__(512) void flash_read_kernel(FlashReadArgs a) {
   using T = typename E::T;
   constexpr int VEC = E::VEC, KB = E::KB;
-  __shared__ float s_ha[TM][N], s_hm[TM][N];
+  __shared__ float s_h[NPRE][TM][N];
+  __shared__ uint32_t s_mask[TM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
   const int C = a.C, nkbC = C / KB;
   const int G = (nkbC + TWV - 1) / TWV;
@@ -143,8 +151,17 @@ __global__ __launch_bounds__(512) void flash_read_kernel(FlashReadArgs a) {
   const int t0 = tile * TM;
   for (int u = tid; u < TM * N; u += TNTHR) {
     const int tau = u / N, t = t0 + tau;
-    s_ha[tau][u % N] = t < a.T ? a.h_pa[(size_t)t0 * N + u] : 0.f;
-    s_hm[tau][u % N] = t < a.T ? a.h_pm[(size_t)t0 * N + u] : 0.f;
+#pragma unroll
+    for (int q = 0; q < NPRE; ++q) s_h[q][tau][u % N] = t < a.T ? a.h_pre[q][(size_t)t0 * N + u] : 0.f;
+  }
+  if (MASK && tid < TM) {
+    uint32_t mk = 0;
+    if (t0 + tid < a.T)
+      for (int j = 0; j < a.K; ++j) {
+        const int v = a.idx[(size_t)(t0 + tid) * a.K + j];
+        if (v >= 0 && v < N) mk |= 1u << v;
+      }
+    s_mask[tid] = mk;
   }
   const int kb = slice * TWV + wave;
   const int t = t0 + r;
@@ -158,23 +175,26 @@ __global__ __launch_bounds__(512) void flash_read_kernel(FlashReadArgs a) {
   }
   __syncthreads();
   if (!valid) return;
-  float sa[VEC], sm[VEC];
+  const uint32_t mk = MASK ? s_mask[r] : 0u;
+  float acc[NPRE][VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) { sa[e] = 0.f; sm[e] = 0.f; }
+  for (int q = 0; q < NPRE; ++q)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[q][e] = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float ha = s_ha[r][i], hm = s_hm[r][i];
     float f[VEC];
     E::unpack(v[i], f);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      sa[e] = fmaf(ha, f[e], sa[e]);
-      sm[e] = fmaf(hm, f[e], sm[e]);
+    for (int q = 0; q < NPRE; ++q) {
+      const float h = (q > 0 && ((mk >> i) & 1u)) ? 0.f : s_h[q][r][i];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[q][e] = fmaf(h, f[e], acc[q][e]);
     }
   }
   const size_t o = (size_t)t * C + (size_t)kb * KB + VEC * g;
-  st16_nt(reinterpret_cast<T*>(a.inp_a) + o, E::packv(sa));
-  st16_nt(reinterpret_cast<T*>(a.inp_m) + o, E::packv(sm));
+#pragma unroll
+  for (int q = 0; q < NPRE; ++q) st16_nt(reinterpret_cast<T*>(a.out[q]) + o, E::packv(acc[q]));
 }
 
 struct ActProjArgs {
@@ -248,32 +268,114 @@ __global__ __launch_bounds__(256) void flash_act_proj_kernel(ActProjArgs a) {
 
 struct AttnFinArgs {
   int T, C, G;
-  const float* part;   // [ntiles][G][TM * 16 + TM]
+  const float* part;   // [ntiles][G][TM * NT * 16 + TM]
   const float* b_po;
   float a_po, eps;
-  float* h_post_a;     // [T][K]
+  float* h_post;       // [T][K][KR]
 };
 
-// H_post^A = 2 sigmoid(alpha RMSNorm(vec X_act) W_post^A + b), one token per thread.
-template <int K>
-__global__ __launch_bounds__(256) void flash_attn_fin_kernel(AttnFinArgs a) {
-  constexpr int P = TM * 16 + TM;
+// H_post = 2 sigmoid(alpha RMSNorm(vec X_act) W_post + b) of an unmixed
+// sublayer (entry (j, r) at column j KR + r), one token per thread.
+template <int K, int KR, int NT>
+__global__ __launch_bounds__(256) void flash_post_fin_kernel(AttnFinArgs a) {
+  constexpr int NP = NT * 16, P = TM * NP + TM;
+  static_assert(K * KR <= NP, "post-map columns");
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= a.T) return;
   const int tile = t / TM, tau = t % TM;
-  float raw[K], s2 = 0.f;
+  float raw[K * KR], s2 = 0.f;
 #pragma unroll
-  for (int j = 0; j < K; ++j) raw[j] = 0.f;
+  for (int j = 0; j < K * KR; ++j) raw[j] = 0.f;
   for (int s = 0; s < a.G; ++s) {
     const float* pp = a.part + ((size_t)tile * a.G + s) * P;
 #pragma unroll
-    for (int j = 0; j < K; ++j) raw[j] += pp[tau * 16 + j];
-    s2 += pp[TM * 16 + tau];
+    for (int j = 0; j < K * KR; ++j) raw[j] += pp[tau * NP + j];
+    s2 += pp[TM * NP + tau];
   }
   const float rr = 1.f / sqrtf(s2 / ((float)K * (float)a.C) + a.eps);
 #pragma unroll
-  for (int j = 0; j < K; ++j)
-    a.h_post_a[(size_t)t * K + j] = 2.f * sigmoidf_(fmaf(a.a_po * raw[j], rr, a.b_po[j]));
+  for (int j = 0; j < K * KR; ++j)
+    a.h_post[(size_t)t * K * KR + j] = 2.f * sigmoidf_(fmaf(a.a_po * raw[j], rr, a.b_po[j]));
+}
+
+struct ActInArgs {
+  const void* X;
+  void* inp;
+  const void* base;    // [T][C]: this sublayer's non-active base
+  int T, C, N, G, ntiles;
+  const int* idx;
+  const float* h_pre;  // [T][N]: this sublayer's pre-map
+  const uint4* wp;     // packed [k*C][NT*16] B fragments of its active-map weights
+  float* part;         // [ntiles][G][TM * NT * 16 + TM]
+};
+
+// Input and active-map projection of an xHC-Flash-4sub sublayer from one read
+// of the k active rows: inp = base + sum_j H_pre[I_j] x_j (the active-state
+// form of the input), and the rows against the packed weights, with their
+// sum of squares.  One wave per 16-token tile, G splits of the channels; the
+// k rows of a channel block are loaded together.
+template <class E, int NT, int K>
+__global__ __launch_bounds__(256) void flash_act_input_kernel(ActInArgs a) {
+  using T = typename E::T;
+  constexpr int VEC = E::VEC, KB = E::KB, NP = NT * 16, P = TM * NP + TM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= a.ntiles) return;   // whole waves only; no barrier below
+  const int split = blockIdx.y;
+  const int C = a.C, nkbC = C / KB;
+  const int kc0 = (int)((long)split * nkbC / a.G), kc1 = (int)((long)(split + 1) * nkbC / a.G);
+  const int tok = tile * TM + r;
+  const bool valid = tok < a.T;
+  const int tk = valid ? tok : 0;
+  int row[K];
+  float hI[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    int v = valid ? a.idx[(size_t)tok * K + j] : 0;
+    v = v < 0 ? 0 : (v >= a.N ? a.N - 1 : v);
+    row[j] = v;
+    hI[j] = valid ? a.h_pre[(size_t)tok * a.N + v] : 0.f;
+  }
+  const T* X = reinterpret_cast<const T*>(a.X);
+  const T* base = reinterpret_cast<const T*>(a.base) + (size_t)tk * C + VEC * g;
+  T* inp = reinterpret_cast<T*>(a.inp) + (size_t)tk * C + VEC * g;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float s2 = 0.f;
+  const uint4* wp = a.wp + lane;
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  for (int kbc = kc0; kbc < kc1; ++kbc) {
+    const int c = kbc * KB;
+    u32x4_t xa[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) xa[j] = valid ? ld16v(X + ((size_t)tk * a.N + row[j]) * C + c + VEC * g) : zero;
+    const u32x4_t bv = valid ? ld16v(base + c) : zero;
+    float o[VEC];
+    E::unpack(bv, o);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float f[VEC];
+      E::unpack(xa[j], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        o[e] = fmaf(hI[j], f[e], o[e]);
+        s2 = fmaf(f[e], f[e], s2);
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        acc[n] = E::mma(acc[n], xa[j], __builtin_bit_cast(u32x4_t, wp[(((size_t)j * nkbC + kbc) * NT + n) * WAVE]));
+    }
+    if (valid) st16_nt(inp + c, E::packv(o));
+  }
+  s2 += __shfl_xor(s2, 16, WAVE);
+  s2 += __shfl_xor(s2, 32, WAVE);
+  float* dst = a.part + ((size_t)tile * a.G + split) * P;
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(4 * g + i) * NP + n * 16 + r] = acc[n][i];
+  if (g == 0) dst[TM * NP + r] = s2;
 }
 
 template <class E, int NT, int K>
@@ -304,31 +406,31 @@ bool flash_pre_launch(const Plan& P, const xhcf_weights* w, const void* X, void*
                          st))
     return false;
 
-  FlashRouteArgs r;
+  FlashRouteArgs r{};
   r.T = (int)P.T; r.m = P.m; r.KS = P.KS; r.NP = P.NTF * 16; r.n_el = (long)N * P.C;
   r.part = part; r.stats = stats; r.cs = cs;
-  r.b_pa = w->b_pre_attn; r.b_pm = w->b_pre_mlp;
-  r.a_pa = w->alpha_pre_attn; r.a_pm = w->alpha_pre_mlp; r.eps = P.eps_norm;
+  r.b_pre[0] = w->b_pre_attn; r.b_pre[1] = w->b_pre_mlp;
+  r.a_pre[0] = w->alpha_pre_attn; r.a_pre[1] = w->alpha_pre_mlp; r.eps = P.eps_norm;
   r.idx = reinterpret_cast<int*>(ws + P.o_idx);
   r.p = reinterpret_cast<float*>(ws + P.o_p);
-  r.h_pa = reinterpret_cast<float*>(ws + P.o_hpre);
-  r.h_pm = reinterpret_cast<float*>(ws + P.o_hpre_m);
+  r.h_pre[0] = reinterpret_cast<float*>(ws + P.o_hpre);
+  r.h_pre[1] = reinterpret_cast<float*>(ws + P.o_hpre_m);
   r.z = reinterpret_cast<float*>(ws + P.o_z);
-  flash_route_kernel<N, K><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(r);
+  flash_route_kernel<N, K, 2><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(r);
 
-  FlashReadArgs d;
-  d.X = X; d.inp_a = inp_a; d.inp_m = inp_m; d.T = (int)P.T; d.C = P.C;
-  d.h_pa = r.h_pa; d.h_pm = r.h_pm;
+  FlashReadArgs d{};
+  d.X = X; d.out[0] = inp_a; d.out[1] = inp_m; d.T = (int)P.T; d.C = P.C; d.K = P.K;
+  d.h_pre[0] = r.h_pre[0]; d.h_pre[1] = r.h_pre[1];
   const int nkbC = P.C / E::KB;
-  flash_read_kernel<E, N><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
+  flash_read_kernel<E, N, 2, false><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
 
   float* part2 = reinterpret_cast<float*>(ws + P.o_part2);
   act_proj_launch<E, 1, K>(P, X, ws, reinterpret_cast<const uint4*>(ws + P.o_wact_a), part2, st);
   AttnFinArgs f;
   f.T = (int)P.T; f.C = P.C; f.G = P.G2; f.part = part2;
   f.b_po = w->b_post_attn; f.a_po = w->alpha_post_attn; f.eps = P.eps_norm;
-  f.h_post_a = reinterpret_cast<float*>(ws + P.o_hpost_a);
-  flash_attn_fin_kernel<K><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(f);
+  f.h_post = reinterpret_cast<float*>(ws + P.o_hpost_a);
+  flash_post_fin_kernel<K, 1, 1><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(f);
   return true;
 }
 
@@ -367,7 +469,150 @@ bool flash_mid_dispatch(const Plan& P, const xhcf_weights* w, void* X, const voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// xHC-Flash-4sub: one routing and four pre-maps for two blocks.
+// ---------------------------------------------------------------------------
+template <class E, int N, int K>
+bool flash4_pre_launch(const Plan& P, const xhcf4_weights* w, const void* X, void* inp, void* bases, char* ws,
+                       hipStream_t st) {
+  using TT = typename E::T;
+  const int KRm = P.KR;
+  launch_pack_b(P.dtype, w->w_full, P.nkb_full, P.ncol_full, P.NTF, ws + P.o_wfull, st);
+  const int ncq[3] = {P.K, P.K * KRm, P.K};
+  for (int q = 0; q < 3; ++q)
+    launch_pack_b(P.dtype, w->w_post[q], P.nkb_act, ncq[q], (ncq[q] + 15) / 16, ws + P.o_wq[q], st);
+  launch_pack_b(P.dtype, w->w_act_last, P.nkb_act, P.ncol_act, P.NTA, ws + P.o_wact, st);
+  float* cs = reinterpret_cast<float*>(ws + P.o_colsum);
+  flash_colsum_kernel<E, N><<<CSB, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C, P.ncol_full,
+                                                 cs + N);
+  flash_colsum_fin_kernel<N><<<1, 64, 0, st>>>(cs + N, cs);
+  float* part = reinterpret_cast<float*>(ws + P.o_part);
+  float* stats = reinterpret_cast<float*>(ws + P.o_stats);
+  if (!launch_projection(P.dtype, P.NTF, X, (int)P.T, (long)N * P.C, ws + P.o_wfull, P.nkb_full, P.KS, part, stats,
+                         st))
+    return false;
+  FlashRouteArgs r{};
+  r.T = (int)P.T; r.m = P.m; r.KS = P.KS; r.NP = P.NTF * 16; r.n_el = (long)N * P.C;
+  r.part = part; r.stats = stats; r.cs = cs; r.eps = P.eps_norm;
+  for (int q = 0; q < 4; ++q) {
+    r.b_pre[q] = w->b_pre[q];
+    r.a_pre[q] = w->alpha_pre[q];
+    r.h_pre[q] = reinterpret_cast<float*>(ws + P.o_hpre) + (size_t)q * P.T * N;
+  }
+  r.idx = reinterpret_cast<int*>(ws + P.o_idx);
+  r.p = reinterpret_cast<float*>(ws + P.o_p);
+  r.z = reinterpret_cast<float*>(ws + P.o_z);
+  flash_route_kernel<N, K, 4><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(r);
+
+  FlashReadArgs d{};
+  d.X = X; d.T = (int)P.T; d.C = P.C; d.K = P.K; d.idx = r.idx;
+  d.out[0] = inp;
+  for (int q = 1; q < 4; ++q) d.out[q] = static_cast<TT*>(bases) + (size_t)(q - 1) * P.T * P.C;
+  for (int q = 0; q < 4; ++q) d.h_pre[q] = r.h_pre[q];
+  const int nkbC = P.C / E::KB;
+  flash_read_kernel<E, N, 4, true><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
+
+  // the first sublayer's post-map from the group-entry active rows
+  float* part2 = reinterpret_cast<float*>(ws + P.o_part2);
+  act_proj_launch<E, 1, K>(P, X, ws, reinterpret_cast<const uint4*>(ws + P.o_wq[0]), part2, st);
+  AttnFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.G = P.G2; f.part = part2;
+  f.b_po = w->b_post[0]; f.a_po = w->alpha_post[0]; f.eps = P.eps_norm;
+  f.h_post = reinterpret_cast<float*>(ws + P.o_hpost);
+  flash_post_fin_kernel<K, 1, 1><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(f);
+  return true;
+}
+
+template <class E, int NT, int K>
+void act_input_launch(const Plan& P, const void* X, void* inp, const void* base, const float* h_pre, const char* ws,
+                      const uint4* wp, float* part, hipStream_t st) {
+  ActInArgs a;
+  a.X = X; a.inp = inp; a.base = base; a.T = (int)P.T; a.C = P.C; a.N = P.N; a.G = P.G2; a.ntiles = (int)P.ntiles;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.h_pre = h_pre;
+  a.wp = wp;
+  a.part = part;
+  dim3 grid((unsigned)((P.ntiles + 3) / 4), (unsigned)P.G2);
+  flash_act_input_kernel<E, NT, K><<<grid, 256, 0, st>>>(a);
+}
+
+// Sublayer q (1..4): its write; then, for q < 4, the input of sublayer q + 1
+// and its active maps (a post-map for sublayers 2 and 3, H_res and the
+// post-map for the final MLP).
+template <class E, int K, int KR>
+bool flash4_post_launch(const Plan& P, const xhcf4_weights* w, int q, void* X, const void* out, const void* bases,
+                        void* inp, char* ws, hipStream_t st) {
+  using TT = typename E::T;
+  if (q == 4) {
+    xhc_weights wx{};
+    wx.conv_w = w->conv_w[1];
+    return launch_xhc_post(P, X, out, &wx, ws, st);
+  }
+  if (!launch_unmixed_write(P, q == 2 ? KR : 1, X, out, q == 2 ? w->conv_w[0] : nullptr, ws, st)) return false;
+  const void* base = static_cast<const TT*>(bases) + (size_t)(q - 1) * P.T * P.C;
+  const float* hp = reinterpret_cast<const float*>(ws + P.o_hpre) + (size_t)q * P.T * P.N;
+  float* part2 = reinterpret_cast<float*>(ws + P.o_part2);
+  AttnFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.G = P.G2; f.part = part2; f.eps = P.eps_norm;
+  f.h_post = reinterpret_cast<float*>(ws + P.o_hpost);
+  const unsigned gt = (unsigned)((P.T + 255) / 256);
+  if (q == 1) {   // next: the first MLP, unmixed, K_r components
+    constexpr int NT2 = (K * KR + 15) / 16;
+    act_input_launch<E, NT2, K>(P, X, inp, base, hp, ws, reinterpret_cast<const uint4*>(ws + P.o_wq[1]), part2, st);
+    f.b_po = w->b_post[1]; f.a_po = w->alpha_post[1];
+    flash_post_fin_kernel<K, KR, NT2><<<gt, 256, 0, st>>>(f);
+    return true;
+  }
+  if (q == 2) {   // next: the second attention
+    act_input_launch<E, 1, K>(P, X, inp, base, hp, ws, reinterpret_cast<const uint4*>(ws + P.o_wq[2]), part2, st);
+    f.b_po = w->b_post[2]; f.a_po = w->alpha_post[2];
+    flash_post_fin_kernel<K, 1, 1><<<gt, 256, 0, st>>>(f);
+    return true;
+  }
+  // q == 3, next: the final MLP with its residual map
+  constexpr int NTA = (K * K + K * KR + 15) / 16;
+  act_input_launch<E, NTA, K>(P, X, inp, base, hp, ws, reinterpret_cast<const uint4*>(ws + P.o_wact), part2, st);
+  return launch_act_fin(P, P.G2, part2, w->b_res, w->b_post[3], w->alpha_res, w->alpha_post[3],
+                        reinterpret_cast<float*>(ws + P.o_hres), reinterpret_cast<float*>(ws + P.o_hpost), st);
+}
+
+template <class E>
+bool flash4_pre_dispatch(const Plan& P, const xhcf4_weights* w, const void* X, void* inp, void* bases, char* ws,
+                         hipStream_t st) {
+  switch (P.N * 10 + P.K) {
+    case 164: return flash4_pre_launch<E, 16, 4>(P, w, X, inp, bases, ws, st);
+    case 84: return flash4_pre_launch<E, 8, 4>(P, w, X, inp, bases, ws, st);
+    case 44: return flash4_pre_launch<E, 4, 4>(P, w, X, inp, bases, ws, st);
+    case 11: return flash4_pre_launch<E, 1, 1>(P, w, X, inp, bases, ws, st);
+    default: return false;
+  }
+}
+
+template <class E>
+bool flash4_post_dispatch(const Plan& P, const xhcf4_weights* w, int q, void* X, const void* out, const void* bases,
+                          void* inp, char* ws, hipStream_t st) {
+  switch (P.K * 10 + P.KR) {
+    case 44: return flash4_post_launch<E, 4, 4>(P, w, q, X, out, bases, inp, ws, st);
+    case 41: return flash4_post_launch<E, 4, 1>(P, w, q, X, out, bases, inp, ws, st);
+    case 14: return flash4_post_launch<E, 1, 4>(P, w, q, X, out, bases, inp, ws, st);
+    case 11: return flash4_post_launch<E, 1, 1>(P, w, q, X, out, bases, inp, ws, st);
+    default: return false;
+  }
+}
+
 }  // namespace
+
+bool launch_xhcf4_pre(const Plan& P, const xhcf4_weights* w, const void* X, void* inp, void* bases, char* ws,
+                      hipStream_t st) {
+  return P.dtype == XHC_BF16 ? flash4_pre_dispatch<Bf16>(P, w, X, inp, bases, ws, st)
+                             : flash4_pre_dispatch<F32>(P, w, X, inp, bases, ws, st);
+}
+
+bool launch_xhcf4_post(const Plan& P, const xhcf4_weights* w, int q, void* X, const void* out, const void* bases,
+                       void* inp, char* ws, hipStream_t st) {
+  return P.dtype == XHC_BF16 ? flash4_post_dispatch<Bf16>(P, w, q, X, out, bases, inp, ws, st)
+                             : flash4_post_dispatch<F32>(P, w, q, X, out, bases, inp, ws, st);
+}
 
 bool launch_xhcf_pre(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
                      hipStream_t st) {

@@ -43,6 +43,7 @@ struct Plan {
   bool flash = false;
   int G2 = 1;                       // splits of the active-row projections
   size_t o_hpre_m = SIZE_MAX, o_hpost_a = SIZE_MAX, o_wact_a = SIZE_MAX;
+  size_t o_wq[3] = {SIZE_MAX, SIZE_MAX, SIZE_MAX};   // xHC-Flash-4sub: packed post-maps of sublayers 1-3
 };
 
 // xHC pre, fused one-pass kernel.  sync: [0] ticket counter, [1] status
@@ -129,6 +130,13 @@ bool launch_act_fin(const Plan& P, int G, const float* part2, const float* b_res
 bool launch_flash_attn_write(const Plan& P, void* X, const void* out, void* inp_m, const char* ws, hipStream_t st);
 bool launch_xhc_post_decode(const Plan& P, void* X, const void* out, void* ring, const int* steps,
                             const xhc_weights* w, const char* ws, hipStream_t st);
+bool launch_unmixed_write(const Plan& P, int KR, void* X, const void* out, const float* conv_w, char* ws,
+                          hipStream_t st);
+// xHC-Flash-4sub group (xhc_flash.hip)
+bool launch_xhcf4_pre(const Plan& P, const xhcf4_weights* w, const void* X, void* inp, void* bases, char* ws,
+                      hipStream_t st);
+bool launch_xhcf4_post(const Plan& P, const xhcf4_weights* w, int q, void* X, const void* out, const void* bases,
+                       void* inp, char* ws, hipStream_t st);
 // xHC-Flash block (xhc_flash.hip)
 bool launch_xhcf_pre(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
                      hipStream_t st);

@@ -291,11 +291,13 @@ __global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
 }
 
 // Mix + gated write of the k active rows, in place.  PB tokens per load batch.
-// FL (xHC-Flash attention write, K_r = 1): no residual mix, each active row
-// gains p_j H_post_j out (xHC paper, "xHC-Flash", Eq. 18), and the MLP base
-// readout inp_m gains a out with a = sum_j H_pre^MLP[I_j] p_j H_post_j
-// (Eq. 19), read and rewritten in the same pass over out.
-template <class E, int K, int KR, int PB, bool FL = false>
+// MODE 0: full xHC's write.  MODE 2: no residual mix (H_res = I), the
+// unmixed writes of xHC-Flash (xHC paper, "xHC-Flash", Eq. 18, and the
+// "Four-sublayer extension").  MODE 1 (xHC-Flash attention write, K_r = 1):
+// MODE 2, and the MLP base readout inp_m gains a out with
+// a = sum_j H_pre^MLP[I_j] p_j H_post_j (Eq. 19), read and rewritten in the
+// same pass over out.
+template <class E, int K, int KR, int PB, int MODE = 0>
 __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
   using T = typename E::T;
   using Qd = Quad<E>;
@@ -311,6 +313,7 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
   __shared__ float s_Q[PT][K][KR];
   __shared__ float s_H[PT][K][K];
   __shared__ int s_I[PT][K];
+  constexpr bool FL = MODE == 1, IDM = MODE != 0;
   __shared__ float s_A[FL ? PT : 1];
   static_assert(!FL || KR == 1, "the Flash attention write has one write component");
 
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
       s_I[tau][j] = ij;
       const float pj = a.p[(size_t)t * K + j];
 #pragma unroll
-      for (int i = 0; i < K; ++i) s_H[tau][j][i] = FL ? (i == j ? 1.f : 0.f) : a.h_res[((size_t)t * K + j) * K + i];
+      for (int i = 0; i < K; ++i) s_H[tau][j][i] = IDM ? (i == j ? 1.f : 0.f) : a.h_res[((size_t)t * K + j) * K + i];
       float hpo[KR];
 #pragma unroll
       for (int r = 0; r < KR; ++r) hpo[r] = a.h_post[((size_t)t * K + j) * KR + r];
@@ -636,14 +639,14 @@ static bool decode_launch(const DecodeArgs& a, int K, hipStream_t st) {
   }
 }
 
-template <class E, int K, int KR>
+template <class E, int K, int KR, int MODE = 0>
 static void launch_apply(const XhcPostArgs& a, hipStream_t st) {
   dim3 grid((a.T + PT - 1) / PT, a.nslices);
   // tokens per load batch: measured best of 2, 3, 4, 6 for MLP-type bf16
   // (the batch divides the 12-token history period; fp32 rows are twice as
   // wide, so 4), and of 4, 8, 16 for attention-type
   constexpr int PB = KR == 4 ? (sizeof(typename E::T) == 2 ? 6 : 4) : 8;
-  xhc_apply_kernel<E, K, KR, PB><<<grid, 256, 0, st>>>(a);
+  xhc_apply_kernel<E, K, KR, PB, MODE><<<grid, 256, 0, st>>>(a);
 }
 
 template <class E>
@@ -699,8 +702,8 @@ template <class E>
 static bool flash_attn_launch(const XhcPostArgs& a, int K, hipStream_t st) {
   dim3 grid((a.T + PT - 1) / PT, a.nslices);
   switch (K) {
-    case 4: xhc_apply_kernel<E, 4, 1, 8, true><<<grid, 256, 0, st>>>(a); return true;
-    case 1: xhc_apply_kernel<E, 1, 1, 8, true><<<grid, 256, 0, st>>>(a); return true;
+    case 4: xhc_apply_kernel<E, 4, 1, 8, 1><<<grid, 256, 0, st>>>(a); return true;
+    case 1: xhc_apply_kernel<E, 1, 1, 8, 1><<<grid, 256, 0, st>>>(a); return true;
     default: return false;
   }
 }
@@ -716,6 +719,38 @@ bool launch_flash_attn_write(const Plan& P, void* X, const void* out, void* inp_
   a.inp_m = inp_m;
   a.use_mgs = 0;
   return P.dtype == XHC_BF16 ? flash_attn_launch<Bf16>(a, P.K, st) : flash_attn_launch<F32>(a, P.K, st);
+}
+
+// The unmixed write of an intermediate xHC-Flash-4sub sublayer (H_res = I):
+// K_r = 1 after attention, the temporal basis after the first MLP.
+template <class E>
+static bool unmixed_launch(const Plan& P, int KR, void* X, const void* out, const float* conv_w, char* ws,
+                           hipStream_t st) {
+  XhcPostArgs a{};
+  a.X = X; a.out = out; a.T = (int)P.T; a.S = P.S; a.C = P.C; a.N = P.N; a.nslices = P.nslices;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.p = reinterpret_cast<const float*>(ws + P.o_p);
+  a.h_res = nullptr;
+  a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+  a.conv_w = conv_w; a.use_mgs = P.use_mgs; a.eps_mgs = P.eps_mgs;
+  a.gram = reinterpret_cast<float*>(ws + P.o_gram);
+  if (KR == 4 && P.use_mgs) {
+    dim3 grid((a.T + PT - 1) / PT, a.nslices);
+    xhc_gram_kernel<E><<<grid, 256, 0, st>>>(a);
+  }
+  switch (P.K * 10 + KR) {
+    case 41: launch_apply<E, 4, 1, 2>(a, st); return true;
+    case 44: launch_apply<E, 4, 4, 2>(a, st); return true;
+    case 11: launch_apply<E, 1, 1, 2>(a, st); return true;
+    case 14: launch_apply<E, 1, 4, 2>(a, st); return true;
+    default: return false;
+  }
+}
+
+bool launch_unmixed_write(const Plan& P, int KR, void* X, const void* out, const float* conv_w, char* ws,
+                          hipStream_t st) {
+  return P.dtype == XHC_BF16 ? unmixed_launch<Bf16>(P, KR, X, out, conv_w, ws, st)
+                             : unmixed_launch<F32>(P, KR, X, out, conv_w, ws, st);
 }
 
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {

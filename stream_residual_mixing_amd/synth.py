@@ -15,6 +15,9 @@ rounded once to its storage dtype by PyTorch on the CPU.  Keys:
 * xHC-Flash attention post-map, block b: [seed, 7, b] (a block's other
   weights use the keys above with l = b; its attention and MLP outputs are
   layers 2b and 2b + 1)
+* xHC-Flash-4sub group g: full-state projection [seed, 2, g], post-maps of
+  sublayers 1-3 [seed, 8, 3g + q], final MLP maps [seed, 3, g], the two MLPs'
+  kernels [seed, 4 + j, 2g + i]; its four outputs are layers 4g .. 4g + 3
 
 Distributions (the workloads' own): X, out ~ N(0, 1); projection weights
 ~ N(0, 0.02); conv kernel of size kappa ~ N(0, 1/kappa) (second argument
@@ -137,4 +140,20 @@ def xhcf_block_weights(seed, block, N, k, C, K_r, dtype, kernels=(4, 8, 12)):
         b_pre_attn=torch.zeros(N), b_pre_mlp=torch.zeros(N), b_post_attn=torch.zeros(k),
         b_res=torch.zeros(k * k), b_post_mlp=torch.zeros(k * K_r),
         alpha_pre_attn=ALPHA, alpha_pre_mlp=ALPHA, alpha_post_attn=ALPHA, alpha_res=ALPHA, alpha_post_mlp=ALPHA,
+    )
+
+
+def xhcf4_group_weights(seed, group, N, k, C, K_r, dtype, kernels=(4, 8, 12)):
+    """Weights of one xHC-Flash-4sub group: full-state projection [N*C, 5N]
+    (router, four pre-maps), post-maps of sublayers 1-3, final MLP maps
+    [k*C, k*k + k*K_r], two MLP kernel sets; biases 0, scales alpha."""
+    ncq = (k, k * K_r, k)
+    return dict(
+        w_full=proj_weight(seed, 2, group, N * C, 5 * N, dtype),
+        w_post=[proj_weight(seed, 8, 3 * group + q, k * C, ncq[q], dtype) for q in range(3)],
+        w_act_last=proj_weight(seed, 3, group, k * C, k * k + k * K_r, dtype),
+        conv=[conv_kernels(seed, 2 * group + i, C, kernels) if K_r > 1 else [] for i in range(2)],
+        b_pre=[torch.zeros(N) for _ in range(4)], b_post=[torch.zeros(k), torch.zeros(k * K_r), torch.zeros(k),
+                                                          torch.zeros(k * K_r)],
+        b_res=torch.zeros(k * k), alpha_pre=(ALPHA,) * 4, alpha_post=(ALPHA,) * 4, alpha_res=ALPHA,
     )

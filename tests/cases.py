@@ -403,3 +403,106 @@ def compare_flash(g, o, tol, tokens=None, dtype="bf16"):
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"errors above {tol}: {bad} (all: {errs})"
     return errs
+
+
+# ----------------------------------------------------------- xHC-Flash-4sub
+
+def flash4_oracle_weights(wd):
+    return dict(w_full=f64(wd["w_full"]), w_post=[f64(t) for t in wd["w_post"]], w_act_last=f64(wd["w_act_last"]),
+                conv=[[f64(c) for c in cs] for cs in wd["conv"]],
+                alpha=dict(pre=tuple(wd["alpha_pre"]), post=tuple(wd["alpha_post"]), res=wd["alpha_res"]),
+                b=dict(pre=[f64(t) for t in wd["b_pre"]], post=[f64(t) for t in wd["b_post"]], res=f64(wd["b_res"])))
+
+
+def flash4_inputs(cfg: Config, seed, group=0):
+    """Seeded group-entry state, the four sublayer outputs and the group's
+    weights; tokens whose routing margin is below MARGIN are redrawn."""
+    wd = synth.xhcf4_group_weights(seed, group, cfg.N, cfg.k, cfg.C, cfg.K_r, cfg.dtype)
+    ow = flash4_oracle_weights(wd)
+    attempts = {}
+    X = synth.state(seed, cfg.T, cfg.N, cfg.C, cfg.dtype)
+    for _ in range(20):
+        z = O.xhc_router_logits(f64(X), ow["w_full"][:, :cfg.N])
+        bad = np.nonzero(O.xhc_topk_margin(z, cfg.m, cfg.k) < MARGIN)[0]
+        if bad.size == 0:
+            break
+        for t in bad:
+            attempts[int(t)] = attempts.get(int(t), 0) + 1
+        X[bad] = synth.state_rows(seed, bad, cfg.N, cfg.C, cfg.dtype, attempts)
+    outs = [synth.sublayer_out(seed, 4 * group + q, cfg.B, cfg.S, cfg.C, cfg.dtype) for q in range(4)]
+    return X, outs, wd, ow
+
+
+def oracle_flash4(cfg: Config, X64, outs64, ow, dtype=None):
+    convs = ow["conv"] if cfg.K_r == 4 else [[], []]
+    return O.xhcf4_group(X64, outs64, ow["w_full"], ow["w_post"], ow["w_act_last"], cfg.m, cfg.k, convs,
+                         ow["alpha"], ow["b"], iters=cfg.iters, use_mgs=bool(cfg.use_mgs), dtype=dtype or cfg.dtype)
+
+
+def gpu_flash4(lib, cfg: Config, X, outs, wd, stream=None):
+    """xhcf4_pre and xhcf4_post for q = 1..4 through the C ABI; CPU copies of
+    every sublayer's input and post-map, the state after each sublayer, the
+    routing and the final MLP's residual map."""
+    from stream_residual_mixing_amd.binding import flash4_weights_to_device
+    w = flash4_weights_to_device(wd)
+    Xd = X.to("cuda")
+    inp = torch.empty((cfg.T, cfg.C), dtype=cfg.torch_dtype, device="cuda")
+    bases = torch.empty((3, cfg.T, cfg.C), dtype=cfg.torch_dtype, device="cuda")
+    ws = lib.flash4_workspace(cfg)
+    lib.xhcf4_pre(cfg, w, Xd, inp, bases, ws, stream)
+    kq = [1, cfg.K_r, 1, cfg.K_r]
+    arr = lib.flash4_ws_arrays(cfg, ws, kq[0])
+    res = dict(idx=arr["idx"].cpu(), p=arr["p"].cpu(), h_pre=arr["h_pre"].cpu(), bases=bases.cpu(),
+               inputs=[inp.cpu()], h_post=[arr["h_post"].cpu()], states=[])
+    for q in range(1, 5):
+        lib.xhcf4_post(cfg, w, q, Xd, outs[q - 1].to("cuda"), bases, inp, ws, stream)
+        torch.cuda.synchronize()
+        res["states"].append(Xd.cpu())
+        if q < 4:
+            res["inputs"].append(inp.cpu())
+            arr = lib.flash4_ws_arrays(cfg, ws, kq[q])
+            res["h_post"].append(arr["h_post"].cpu())
+            if q == 3:
+                res["h_res"] = arr["h_res"].cpu()
+    return res
+
+
+def err_with_allowance(g, r, allow, floor=1e-2):
+    """Relative error (floored as in rel_err) after an absolute allowance."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    rms = float(np.sqrt(np.mean(r * r)))
+    den = np.maximum(np.abs(r), floor * rms)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.maximum(np.abs(g - r) - allow, 0.0) / den))
+
+
+def compare_flash4(g, o, tol, dtype):
+    """Every stored tensor of a group.  Each side rounds what it stores (the
+    bases, the rewritten active rows after each sublayer), and two correct
+    roundings may differ by one unit in the last place; after sublayer q a
+    row has been rounded q times, so the state after sublayer q is allowed q
+    units of the largest active row at that channel, and the input of
+    sublayer q one unit of its base plus q - 1 such units (all from oracle
+    values).  Maps and router weights keep the plain bar."""
+    assert np.array_equal(g["idx"].numpy(), o["I"]), "active indices differ"
+    I = o["I"]
+    prev = [None] + o["states"][:3]
+    errs = {"p": rel_err(g["p"].numpy(), o["p"]), "h_pre": rel_err(g["h_pre"].numpy(), np.stack(o["h_pre"]))}
+    for q in range(4):
+        if q == 0:
+            errs["inp1"] = rel_err(f64(g["inputs"][0]), o["inputs"][0])
+        else:
+            big = np.take_along_axis(np.abs(prev[q]), I[:, :, None], axis=1).max(axis=1)
+            allow = ulp(o["bases"][q - 1], dtype) + q * ulp(big, dtype)
+            errs[f"inp{q + 1}"] = err_with_allowance(f64(g["inputs"][q]), o["inputs"][q], allow)
+        st = o["states"][q]
+        big = np.take_along_axis(np.abs(st), I[:, :, None], axis=1).max(axis=1)
+        errs[f"X{q + 1}"] = err_with_allowance(f64(g["states"][q]), st, (q + 1) * ulp(big, dtype)[:, None, :])
+        errs[f"h_post{q + 1}"] = rel_err(g["h_post"][q].numpy().reshape(o["maps"][q]["h_post"].shape),
+                                         o["maps"][q]["h_post"])
+    errs["h_res"] = rel_err(g["h_res"].numpy(), o["maps"][3]["h_res"])
+    errs["bases"] = max(rel_err(f64(g["bases"][i]), o["bases"][i]) for i in range(3))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"errors above {tol}: {bad} (all: {errs})"
+    return errs

@@ -43,7 +43,8 @@ def test_struct_layouts_match_the_header(tmp_path):
     gives the header's structs."""
     import subprocess
     structs = {"xhc_config": XhcConfig, "xhc_weights": XhcWeights, "xhc_ws_layout": binding.XhcWsLayout,
-               "xhcf_weights": binding.XhcfWeights, "xhcf_ws_layout": binding.XhcfWsLayout}
+               "xhcf_weights": binding.XhcfWeights, "xhcf_ws_layout": binding.XhcfWsLayout,
+               "xhcf4_weights": binding.Xhcf4Weights, "xhcf4_ws_layout": binding.Xhcf4WsLayout}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "xhc.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
