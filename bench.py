@@ -49,12 +49,14 @@ WORKLOADS = {
     "mhc_n16_c4096": ("mhc", 16, 16, 0, 4096, 4, 4096, "D"),
     # xHC-Flash: 4 blocks, each an attention + MLP pair sharing one routing
     "xhcf_chain_n16k4_c4096": ("xhcf", 16, 4, 2, 4096, 2, 8192, "AMAMAMAM"),
+    # xHC-Flash-4sub: 2 groups of two blocks sharing one routing
+    "xhcf4_chain_n16k4_c4096": ("xhcf4", 16, 4, 2, 4096, 2, 8192, "AMAMAMAM"),
     # single-token decode: 256 sequences, one new token each, 8 sublayers
     "xhc_decode_n16k4_c4096": ("xhcd", 16, 4, 2, 4096, 256, 1, "AMAMAMAM"),
 }
 DEFAULT = "xhc_chain_n16k4_c4096"
 SEED = {"xhc_chain_n16k4_c4096": 3, "xhc_mlp_n16k4_c2048": 2, "mhc_n4_c4096": 1, "mhc_n16_c4096": 4,
-        "xhcf_chain_n16k4_c4096": 3, "xhc_decode_n16k4_c4096": 5}
+        "xhcf_chain_n16k4_c4096": 3, "xhc_decode_n16k4_c4096": 5, "xhcf4_chain_n16k4_c4096": 3}
 
 
 def log(*a):
@@ -84,6 +86,19 @@ def flash_bytes_per_token(cfg, esz=2):
     return (2 * N + 2) * C * esz, (2 * k + 3) * C * esz, (1 + 2 * k) * C * esz
 
 
+def flash4_bytes_per_token(cfg, esz=2):
+    """Algorithmic bytes per token of an xHC-Flash-4sub group's five calls, in
+    the pages' design of two full-state passes per group: pre reads the state
+    twice and writes the first input and three non-active bases (2N + 4);
+    each intermediate post writes its sublayer (1 + 2k) and forms the next
+    input from its base and the k active rows (1 + k + 1); the last post is
+    full xHC's (1 + 2k).  The active-map projections share the input's read
+    of the k rows."""
+    N, k, C = cfg.N, cfg.k, cfg.C
+    mid = (1 + 2 * k + 2 + k) * C * esz
+    return (2 * N + 4) * C * esz, mid, mid, mid, (1 + 2 * k) * C * esz
+
+
 def bytes_per_token(kind, cfg, esz=2):
     """Algorithmic bytes per token of (pre, post).  Decode: the MLP-type
     write also reads the 11 earlier outputs from the ring and stores the new
@@ -94,12 +109,17 @@ def bytes_per_token(kind, cfg, esz=2):
     if kind == "xhcf":
         # a block is two sublayers: half of its bytes per sublayer
         return sum(flash_bytes_per_token(cfg, esz)) // 2, 0
+    if kind == "xhcf4":
+        return sum(flash4_bytes_per_token(cfg, esz)) // 4, 0
     if kind == "mhc":
         return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.N) * cfg.C * esz
     return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.k) * cfg.C * esz
 
 
 def flops_per_token(kind, cfg):
+    if kind == "xhcf4":   # per sublayer: a quarter of a group's projections
+        N, k, C, KR = cfg.N, cfg.k, cfg.C, 4
+        return (2 * N * C * 5 * N + 2 * k * C * (k + k * KR + k + k * k + k * KR)) // 4
     if kind == "xhcf":   # per sublayer: half of a block's three projections
         N, k, C = cfg.N, cfg.k, cfg.C
         return (2 * N * C * 3 * N + 2 * k * C * k + 2 * k * C * (k * k + 4 * k)) // 2
@@ -120,6 +140,12 @@ def make_inputs(name, kind, cfgs, kinds):
     outs, ws_ = [], []
     for l, cfg in enumerate(cfgs):
         outs.append(synth.sublayer_out(seed, l, cfg.B, cfg.S, cfg.C, "bf16").to("cuda"))
+        if kind == "xhcf4":
+            if l % 4 == 0:
+                from stream_residual_mixing_amd.binding import flash4_weights_to_device
+                ws_.append(flash4_weights_to_device(synth.xhcf4_group_weights(seed, l // 4, cfg.N, cfg.k, cfg.C, 4,
+                                                                               "bf16")))
+            continue
         if kind == "xhcf":
             if l % 2 == 0:
                 from stream_residual_mixing_amd.binding import flash_weights_to_device
@@ -142,6 +168,8 @@ def default_api(name):
         return "flash"
     if kind == "xhcd":
         return "decode"
+    if kind == "xhcf4":
+        return "flash4"
     return "chained" if kind == "xhc" and len(kinds) > 1 else "single"
 
 
@@ -170,6 +198,17 @@ def run_gpu(name, steps, warmup, api):
             calls.append(("xhcf_pre", bp, lambda w=w: lib.xhcf_pre(fcfg, w, X, inp, inp_m, ws, stream)))
             calls.append(("xhcf_mid", bm, lambda w=w, b=b: lib.xhcf_mid(fcfg, w, X, outs[2 * b], inp_m, ws, stream)))
             calls.append(("xhcf_post", bq, lambda w=w, b=b: lib.xhcf_post(fcfg, w, X, outs[2 * b + 1], ws, stream)))
+    elif kind == "xhcf4":
+        fcfg = Config(N=c0.N, k=c0.k, m=c0.m, C=c0.C, B=c0.B, S=c0.S, n_convs=3, dtype="bf16")
+        ws = lib.flash4_workspace(fcfg)
+        bases = torch.empty((3, T, c0.C), dtype=torch.bfloat16, device="cuda")
+        fb = flash4_bytes_per_token(fcfg)
+        for g in range(len(cfgs) // 4):
+            w = weights[g]
+            calls.append(("xhcf4_pre", fb[0], lambda w=w: lib.xhcf4_pre(fcfg, w, X, inp, bases, ws, stream)))
+            for q in range(1, 5):
+                calls.append((f"xhcf4_post{q}", fb[q], lambda w=w, g=g, q=q: lib.xhcf4_post(
+                    fcfg, w, q, X, outs[4 * g + q - 1], bases, inp, ws, stream)))
     elif kind == "xhcd":
         ws = lib.workspace(big)
         ring = torch.zeros((c0.B, 12, c0.C), dtype=torch.bfloat16, device="cuda")
@@ -257,6 +296,19 @@ def cpu_baseline(name, tokens=256):
         sub = Config(N=cfg.N, k=cfg.k, m=cfg.m, C=cfg.C, B=1, S=tokens, n_convs=cfg.n_convs, dtype="bf16")
         X = K.f64(synth.state_rows(seed, range(tokens), cfg.N, cfg.C, "bf16"))
         out = K.f64(synth.out_rows(seed, l, range(tokens), cfg.C, "bf16")).reshape(1, tokens, cfg.C)
+        if kind == "xhcf4":
+            # one group: all four sublayers
+            ow = K.flash4_oracle_weights(synth.xhcf4_group_weights(seed, 0, cfg.N, cfg.k, cfg.C, 4, "bf16"))
+            outs = [K.f64(synth.out_rows(seed, q, range(tokens), cfg.C, "bf16")).reshape(1, tokens, cfg.C)
+                    for q in range(4)]
+            sub.n_convs = 3
+            t = time.perf_counter()
+            K.oracle_flash4(sub, X, outs, ow)
+            dt = time.perf_counter() - t
+            done["A"] = done["M"] = dt / 4
+            total_t += dt
+            total_tok += 4 * tokens
+            break
         if kind == "xhcf":
             # one block: both sublayers of the pair
             ow = K.flash_oracle_weights(synth.xhcf_block_weights(seed, 0, cfg.N, cfg.k, cfg.C, 4, "bf16"))
@@ -284,6 +336,8 @@ def cpu_baseline(name, tokens=256):
     kinds_s = "+".join({"A": "attention", "M": "MLP", "D": "dense"}[k] for k in done)
     if kind == "xhcf":
         kinds_s = "xHC-Flash block (attention + MLP)"
+    if kind == "xhcf4":
+        kinds_s = "xHC-Flash-4sub group (attention, MLP, attention, MLP)"
     return dict(value=total_tok / total_t, unit="tokens/s per layer", cores=int(cores), kind="oracle",
                 sample=f"first {tokens} tokens of batch item 0, one {kinds_s} layer each, float64 NumPy")
 
@@ -414,7 +468,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
     ap.add_argument("--traffic-summary", metavar="PMCDIR", default=None,
                     help="write profiles/<workload>_traffic.json from rocprofv3 counter runs and exit")
-    ap.add_argument("--api", choices=("chained", "single", "flash", "decode"), default=None,
+    ap.add_argument("--api", choices=("chained", "single", "flash", "flash4", "decode"), default=None,
                     help="xHC calls: chained (routing of layer l+1 prepared during layer l; default for "
                          "multi-layer workloads) or single (xhc_pre / xhc_post per layer)")
     args = ap.parse_args()
@@ -473,7 +527,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "kind": kind, "api": api, "N": c0.N,
-                   "k": c0.k if kind in ("xhc", "xhcf") else c0.N,
+                   "k": c0.k if kind in ("xhc", "xhcf", "xhcf4", "xhcd") else c0.N,
                    "m": c0.m, "C": c0.C, "batch": c0.B, "seq": c0.S, "tokens": T, "layers": kinds,
                    "sinkhorn_iters": c0.iters},
         "hbm": {"GBps": round(hbm_gbps, 1), "frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),
