@@ -23,6 +23,12 @@
 #include <mutex>
 #include <tuple>
 
+// contraction blocks a proj_gen lane loads ahead (measured: 4 and 8 within
+// 2% of each other, 16 slower)
+#ifndef XHC_GEN_U
+#define XHC_GEN_U 4
+#endif
+
 namespace xhc {
 
 thread_local const char* g_launch_failure = nullptr;
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(256) void proj_gen_kernel(const typename E::T* __re
     for (int n = 0; n < NT; ++n) acc[n] = E::mma(acc[n], a, wp[(kb * NT + n) * WAVE]);
   };
 
-  constexpr int U = 4;
+  constexpr int U = XHC_GEN_U;
   long kb = kb0;
   for (; kb + U <= kb1; kb += U) {
     uint4 a[U];
