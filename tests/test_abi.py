@@ -174,3 +174,73 @@ def test_flash_layout_and_unsupported_shapes(lib):
         lib.flash_layout(bad)
     assert e.value.status == binding.XHC_ERR_UNSUPPORTED
     assert lib.flash_workspace_bytes(Config(N=16, k=4, m=2, C=256, B=0, S=8, n_convs=3)) == 0
+
+
+def _fw():
+    w = binding.XhcfWeights()
+    for n in ("w_full", "w_post_attn", "w_act_mlp", "conv_w", "b_pre_attn", "b_pre_mlp", "b_post_attn", "b_res",
+              "b_post_mlp"):
+        setattr(w, n, 0x10000)
+    return w
+
+
+def _f4w():
+    w = binding.Xhcf4Weights()
+    w.w_full = w.w_act_last = w.b_res = 0x10000
+    for i in range(3):
+        w.w_post[i] = 0x10000
+    for i in range(2):
+        w.conv_w[i] = 0x10000
+    for i in range(4):
+        w.b_pre[i] = w.b_post[i] = 0x10000
+    return w
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers: run on a host without a GPU only")
+def test_flash_decode_and_4sub_calls_reject_bad_arguments_before_launch(lib):
+    d = lib.dll
+    ok = _cfg(B=1, S=16).c()
+    # xHC-Flash: unsupported (N, k), misaligned or aliased buffers, missing weights
+    bad = _cfg(k=2, m=1).c()
+    assert d.xhcf_pre(ctypes.byref(bad), ctypes.byref(_fw()), 0x20000, 0x30000, 0x50000, 0x40000, None) == \
+        binding.XHC_ERR_UNSUPPORTED
+    assert d.xhcf_pre(ctypes.byref(ok), ctypes.byref(_fw()), 0x20000, 0x30000, 0x30000, 0x40000, None) == \
+        binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
+    assert d.xhcf_mid(ctypes.byref(ok), ctypes.byref(_fw()), 0x20000, 0x30000, 0x50008, 0x40000, None) == \
+        binding.XHC_ERR_INVALID_ARG and "aligned" in lib.last_error()
+    w = _fw()
+    w.conv_w = 0
+    assert d.xhcf_post(ctypes.byref(ok), ctypes.byref(w), 0x20000, 0x30000, 0x40000, None) == \
+        binding.XHC_ERR_INVALID_ARG and "conv_w" in lib.last_error()
+    # decode: one token per sequence, MLP-type only, an aligned steps array
+    xw = XhcWeights()
+    xw.w_full = xw.w_act = xw.b_pre = xw.b_res = xw.b_post = xw.conv_w = 0x10000
+    assert d.xhc_post_decode(ctypes.byref(ok), ctypes.byref(xw), 0x20000, 0x30000, 0x50000, 0x60000, 0x40000,
+                             None) == binding.XHC_ERR_INVALID_ARG and "seq must be 1" in lib.last_error()
+    one = _cfg(B=4, S=1).c()
+    attn = _cfg(B=4, S=1, n_convs=0).c()
+    assert d.xhc_post_decode(ctypes.byref(attn), ctypes.byref(xw), 0x20000, 0x30000, 0x50000, 0x60000, 0x40000,
+                             None) == binding.XHC_ERR_UNSUPPORTED and "xhc_post" in lib.last_error()
+    assert d.xhc_post_decode(ctypes.byref(one), ctypes.byref(xw), 0x20000, 0x30000, 0x50000, 0x60002, 0x40000,
+                             None) == binding.XHC_ERR_INVALID_ARG and "steps" in lib.last_error()
+    assert d.xhc_post_decode(ctypes.byref(one), ctypes.byref(xw), 0x20000, 0x30000, 0x20000, 0x60000, 0x40000,
+                             None) == binding.XHC_ERR_INVALID_ARG
+    # xHC-Flash-4sub: sublayer index, per-sublayer weights, buffers
+    for q in (0, 5):
+        assert d.xhcf4_post(ctypes.byref(ok), ctypes.byref(_f4w()), q, 0x20000, 0x30000, 0x50000, 0x60000, 0x40000,
+                            None) == binding.XHC_ERR_INVALID_ARG and "outside 1..4" in lib.last_error()
+    w4 = _f4w()
+    w4.conv_w[1] = 0
+    assert d.xhcf4_post(ctypes.byref(ok), ctypes.byref(w4), 4, 0x20000, 0x30000, 0x50000, 0x60000, 0x40000,
+                        None) == binding.XHC_ERR_INVALID_ARG and "conv_w[1]" in lib.last_error()
+    w4 = _f4w()
+    w4.b_res = 0
+    assert d.xhcf4_post(ctypes.byref(ok), ctypes.byref(w4), 3, 0x20000, 0x30000, 0x50000, 0x60000, 0x40000,
+                        None) == binding.XHC_ERR_INVALID_ARG and "b_res" in lib.last_error()
+    assert d.xhcf4_pre(ctypes.byref(ok), ctypes.byref(_f4w()), 0x20000, 0x30000, 0x20000, 0x40000, None) == \
+        binding.XHC_ERR_INVALID_ARG and "bases" in lib.last_error()
+    w4 = _f4w()
+    w4.w_post[1] = 0
+    assert d.xhcf4_pre(ctypes.byref(ok), ctypes.byref(w4), 0x20000, 0x30000, 0x50000, 0x40000, None) == \
+        binding.XHC_ERR_INVALID_ARG
+    assert lib.flash4_workspace_bytes(_cfg(k=2, m=1)) == 0
