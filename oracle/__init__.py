@@ -6,8 +6,11 @@ execute this package: only the test suite, the smoke check in
 shares no code with the HIP library (no kernels, headers, helpers, tables or
 pre/post-processing); it receives the seeded inputs as plain arrays.
 
-Everything here is plain NumPy in float64, written step by step from the
-pages' definitions so that it can be checked against them by eye.  Sources,
+``hc_oracle`` is plain NumPy in float64, written step by step from the
+pages' definitions so that it can be checked against them by eye.
+``hc_grad`` repeats one xHC sublayer's forward with PyTorch CPU tensors in
+float64 and differentiates it (the reference for a backward pass); its
+gradients are pinned to central differences of ``hc_oracle``.  Sources,
 cited by page title and section:
 
 * [explainer]  "xHC: sixteen residual streams, four written at a time"
