@@ -212,7 +212,11 @@ xhc_status make_flash_plan(const xhc_config* cfg, xhc::Plan* P) {
   q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
   q.o_wact_a = take((size_t)q.nkb_act * 1 * 64 * 16);
   q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
-  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
+  // projection partials: split-K [KS][T][NTF*16], or per (16-token tile,
+  // slice) of the persistent N = 16 kernel (48 columns + sums + column sums)
+  const size_t part_splitk = (size_t)q.KS * T * q.NTF * 16;
+  const size_t part_tiles = (size_t)q.ntiles * q.Gp * (16 * 48 + 32 + 16);
+  q.o_part = take((part_splitk > part_tiles ? part_splitk : part_tiles) * 4);
   q.o_stats = take((size_t)q.KS * T * 2 * 4);
   const size_t P2 = 16 * (size_t)(q.NTA > 1 ? q.NTA : 1) * 16 + 16;
   q.o_part2 = take((size_t)q.ntiles * q.G2 * P2 * 4);

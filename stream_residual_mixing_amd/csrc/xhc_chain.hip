@@ -810,6 +810,168 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_proj_p_kernel(ProjPArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// xHC-Flash routing projection, persistent (N = 16): the packed full-state
+// weights have three 16-column tiles per block (router, attention pre-map,
+// MLP pre-map).  The first two stay in LDS for the launch as in
+// xhc_proj_p_kernel; the third, for the wave's own block, stays in registers.
+// Partials per (16-token tile, slice): 48 projection columns, sum x and
+// sum x^2 per token, then the slice's router column sums.
+// ---------------------------------------------------------------------------
+struct FlashDims16 {
+  static constexpr int NPF = 48;
+  static constexpr int NSUM = TM * NPF + 2 * TM;
+  static constexpr int P1 = NSUM + 16;
+};
+
+template <class E>
+__global__ __launch_bounds__(PNTHR, 1) void xhcf_proj_p_kernel(ProjPArgs a) {
+  using T = typename E::T;
+  constexpr int N = 16, NTL = 2, NT3 = 3;
+  constexpr int NPF = FlashDims16::NPF, NSUM = FlashDims16::NSUM, P1 = FlashDims16::P1;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  __shared__ u32x4_t s_w[PSB][N][NTL][WAVE];
+  __shared__ float s_red[TWV][NSUM];
+  __shared__ float s_acs[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = wave / PSB, cb = wave % PSB;
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int nsteps = (a.ntiles + PTL - 1) / PTL;
+  const int kb0 = slice * PSB + cb;
+  const uint32_t lane_off =
+      kb0 < nkbC ? (uint32_t)(((size_t)(TM * b + r) * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
+  const T* X = reinterpret_cast<const T*>(a.X);
+  const int full = a.T / (PTL * TM), tail = a.T % (PTL * TM);
+
+  XTile<N> xa, xb;
+  int p = team;
+  load_xtile<E, N>(xa, X, C, p, step_rows(p, full, tail), lane_off);
+  // tiles 0 and 1 of the slice's blocks -> LDS; tile 2 of this wave's block -> registers
+  {
+    constexpr int TOT = PSB * N * NTL * WAVE;
+    constexpr int IT = (TOT + PNTHR - 1) / PNTHR;
+    u32x4_t v[IT];
+#pragma unroll
+    for (int q = 0; q < IT; ++q) {
+      const int u = tid + q * PNTHR;
+      const int l = u % WAVE, n = (u / WAVE) % NTL, i = (u / (WAVE * NTL)) % N, c = u / (WAVE * NTL * N);
+      const int kb = slice * PSB + c;
+      v[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (u < TOT && kb < nkbC) v[q] = ld16v(a.wfull + (((size_t)i * nkbC + kb) * NT3 + n) * WAVE + l);
+    }
+#pragma unroll
+    for (int q = 0; q < IT; ++q) {
+      const int u = tid + q * PNTHR;
+      if (u < TOT) (&s_w[0][0][0][0])[u] = v[q];
+    }
+  }
+  u32x4_t wm[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    wm[i] = kb0 < nkbC ? ld16v(a.wfull + (((size_t)i * nkbC + kb0) * NT3 + 2) * WAVE + lane) : u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
+  slice_colsums<E, N, NTL>(s_w, s_red, s_acs, tid, wave, lane);
+
+  auto step_partials = [&](const XTile<N>& xs, int step) {
+    f32x4_t acc[NTL], acc3 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S1, S2;
+    route_mma<E, N, NTL>(xs, s_w[cb], lane, 0u, acc, S1, S2);
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc3 = E::mma(acc3, xs.x[i], wm[i]);
+    const f32x4_t all[NT3] = {acc[0], acc[1], acc3};
+    acc_to_lds<NT3, NPF>(s_red, wave, g, r, all);
+    sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+    __syncthreads();
+    constexpr int IT = (PTL * P1 + PNTHR - 1) / PNTHR;
+#pragma unroll
+    for (int q = 0; q < IT; ++q) {
+      const int u = tid + q * PNTHR;
+      if (u < PTL * P1) {
+        const int bb = u / P1, v = u % P1;
+        const int tile = PTL * step + bb;
+        float x;
+        if (v < NSUM) {
+          x = 0.f;
+#pragma unroll
+          for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+        } else {
+          x = s_acs[v - NSUM];
+        }
+        if (tile < a.ntiles) a.part[((size_t)tile * G + slice) * P1 + v] = x;
+      }
+    }
+    __syncthreads();
+  };
+
+  while (p < nsteps) {
+    const int p1 = p + nteams;
+    load_xtile<E, N>(xb, X, C, p1, step_rows(p1, full, tail), lane_off);
+    __builtin_amdgcn_sched_barrier(0);
+    step_partials(xa, p);
+    if (p1 >= nsteps) break;
+    const int p2 = p1 + nteams;
+    load_xtile<E, N>(xa, X, C, p2, step_rows(p2, full, tail), lane_off);
+    __builtin_amdgcn_sched_barrier(0);
+    step_partials(xb, p1);
+    p = p2;
+  }
+}
+
+struct FlashRouteFinArgs {
+  int T, C, m, G;
+  const float* part;
+  const float *b_pa, *b_pm;
+  float a_pa, a_pm, eps;
+  int* idx;
+  float *p, *h_pa, *h_pm, *z;
+};
+
+// Routing of a tile from the summed persistent partials (N = 16): router
+// logits, both pre-maps, the active list and router weights.
+template <int K>
+__global__ __launch_bounds__(256) void xhcf_route_fin_kernel(FlashRouteFinArgs a) {
+  constexpr int N = 16, NPF = FlashDims16::NPF, NSUM = FlashDims16::NSUM, P1 = FlashDims16::P1;
+  __shared__ float s_sum[P1];
+  __shared__ float s_z[TM][N];
+  const int tid = threadIdx.x, G = a.G;
+  const int tile = blockIdx.x, t0 = tile * TM;
+  sum_slices<256, 0>(a.part + (size_t)tile * G * P1, G, P1, P1, s_sum, tid);
+  __syncthreads();
+  const float n_el = (float)N * (float)a.C;
+  for (int u = tid; u < TM * N; u += 256) {
+    const int tau = u / N, i = u % N, t = t0 + tau;
+    const bool valid = t < a.T;
+    float z, hpa, hpm, zz;
+    const float q1 = s_sum[TM * NPF + 2 * tau], q2 = s_sum[TM * NPF + 2 * tau + 1], cs = s_sum[NSUM + i];
+    route_logits(s_sum[tau * NPF + i], s_sum[tau * NPF + N + i], q1, q2, cs, n_el, a.eps, a.a_pa, a.b_pa[i], valid,
+                 &z, &hpa);
+    route_logits(s_sum[tau * NPF + i], s_sum[tau * NPF + 2 * N + i], q1, q2, cs, n_el, a.eps, a.a_pm, a.b_pm[i],
+                 valid, &zz, &hpm);
+    s_z[tau][i] = z;
+    if (valid) {
+      a.z[(size_t)t * N + i] = z;
+      a.h_pa[(size_t)t * N + i] = hpa;
+      a.h_pm[(size_t)t * N + i] = hpm;
+    }
+  }
+  __syncthreads();
+  if (tid < TM && t0 + tid < a.T) {
+    const int t = t0 + tid;
+    float zt[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) zt[i] = s_z[tid][i];
+    int sel[K];
+    route_select<N, K>(zt, a.m, sel);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a.idx[(size_t)t * K + j] = sel[j];
+      a.p[(size_t)t * K + j] = j < a.m ? 1.f : sigmoidf_(zt[sel[j]]);
+    }
+  }
+}
+
 // Chained pre pass of a layer that has a next layer (dense read, gather +
 // active partials of this layer, masked routing partials of the next one).
 // The routing of the next step (h_pre rows, then active lists) is loaded by
@@ -1141,6 +1303,30 @@ bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn,
   if (!launch_pack(Pn, wn, wsn, &P, w, ws, &P, ws, st)) return false;
   return P.dtype == XHC_BF16 ? pre_chained_dispatch<Bf16>(P, w, Pn, X, inp, ws, wsn, st)
                              : pre_chained_dispatch<F32>(P, w, Pn, X, inp, ws, wsn, st);
+}
+
+// xHC-Flash routing at N = 16: the persistent projection (packed weights of
+// three tiles at wp, partials at part, Gp slices) and the routing of every tile.
+bool launch_flash_route_p(const Plan& P, const void* X, const void* wp, float* part, const xhcf_weights* w, int* idx,
+                          float* p, float* h_pa, float* h_pm, float* z, hipStream_t st) {
+  if (P.N != 16 || P.ntiles == 0) return false;
+  ProjPArgs a;
+  a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
+  a.wfull = reinterpret_cast<const uint4*>(wp);
+  a.part = part;
+  if (P.dtype == XHC_BF16)
+    xhcf_proj_p_kernel<Bf16><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
+  else
+    xhcf_proj_p_kernel<F32><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
+  FlashRouteFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.Gp; f.part = part;
+  f.b_pa = w->b_pre_attn; f.b_pm = w->b_pre_mlp; f.a_pa = w->alpha_pre_attn; f.a_pm = w->alpha_pre_mlp;
+  f.eps = P.eps_norm;
+  f.idx = idx; f.p = p; f.h_pa = h_pa; f.h_pm = h_pm; f.z = z;
+  switch (P.K) {
+    case 4: xhcf_route_fin_kernel<4><<<(unsigned)P.ntiles, 256, 0, st>>>(f); return true;
+    default: return false;
+  }
 }
 
 bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws,

@@ -397,26 +397,32 @@ bool flash_pre_launch(const Plan& P, const xhcf_weights* w, const void* X, void*
   launch_pack_b(P.dtype, w->w_post_attn, P.nkb_act, P.K, 1, ws + P.o_wact_a, st);
   launch_pack_b(P.dtype, w->w_act_mlp, P.nkb_act, P.ncol_act, P.NTA, ws + P.o_wact, st);
   float* cs = reinterpret_cast<float*>(ws + P.o_colsum);
-  flash_colsum_kernel<E, N><<<CSB, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C, P.ncol_full,
-                                                 cs + N);
-  flash_colsum_fin_kernel<N><<<1, 64, 0, st>>>(cs + N, cs);
   float* part = reinterpret_cast<float*>(ws + P.o_part);
   float* stats = reinterpret_cast<float*>(ws + P.o_stats);
-  if (!launch_projection(P.dtype, P.NTF, X, (int)P.T, (long)N * P.C, ws + P.o_wfull, P.nkb_full, P.KS, part, stats,
-                         st))
-    return false;
-
   FlashRouteArgs r{};
-  r.T = (int)P.T; r.m = P.m; r.KS = P.KS; r.NP = P.NTF * 16; r.n_el = (long)N * P.C;
-  r.part = part; r.stats = stats; r.cs = cs;
-  r.b_pre[0] = w->b_pre_attn; r.b_pre[1] = w->b_pre_mlp;
-  r.a_pre[0] = w->alpha_pre_attn; r.a_pre[1] = w->alpha_pre_mlp; r.eps = P.eps_norm;
   r.idx = reinterpret_cast<int*>(ws + P.o_idx);
   r.p = reinterpret_cast<float*>(ws + P.o_p);
   r.h_pre[0] = reinterpret_cast<float*>(ws + P.o_hpre);
   r.h_pre[1] = reinterpret_cast<float*>(ws + P.o_hpre_m);
   r.z = reinterpret_cast<float*>(ws + P.o_z);
+  if (N == 16 && K == 4) {
+    // persistent projection with the slice's weights on chip
+    if (!launch_flash_route_p(P, X, ws + P.o_wfull, part, w, r.idx, r.p, r.h_pre[0], r.h_pre[1], r.z, st))
+      return false;
+  } else {
+  flash_colsum_kernel<E, N><<<CSB, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C, P.ncol_full,
+                                                 cs + N);
+  flash_colsum_fin_kernel<N><<<1, 64, 0, st>>>(cs + N, cs);
+  if (!launch_projection(P.dtype, P.NTF, X, (int)P.T, (long)N * P.C, ws + P.o_wfull, P.nkb_full, P.KS, part, stats,
+                         st))
+    return false;
+
+  r.T = (int)P.T; r.m = P.m; r.KS = P.KS; r.NP = P.NTF * 16; r.n_el = (long)N * P.C;
+  r.part = part; r.stats = stats; r.cs = cs;
+  r.b_pre[0] = w->b_pre_attn; r.b_pre[1] = w->b_pre_mlp;
+  r.a_pre[0] = w->alpha_pre_attn; r.a_pre[1] = w->alpha_pre_mlp; r.eps = P.eps_norm;
   flash_route_kernel<N, K, 2><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(r);
+  }
 
   FlashReadArgs d{};
   d.X = X; d.out[0] = inp_a; d.out[1] = inp_m; d.T = (int)P.T; d.C = P.C; d.K = P.K;

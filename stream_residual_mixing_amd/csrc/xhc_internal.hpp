@@ -137,6 +137,8 @@ bool launch_xhcf4_pre(const Plan& P, const xhcf4_weights* w, const void* X, void
                       hipStream_t st);
 bool launch_xhcf4_post(const Plan& P, const xhcf4_weights* w, int q, void* X, const void* out, const void* bases,
                        void* inp, char* ws, hipStream_t st);
+bool launch_flash_route_p(const Plan& P, const void* X, const void* wp, float* part, const xhcf_weights* w, int* idx,
+                          float* p, float* h_pa, float* h_pm, float* z, hipStream_t st);
 // xHC-Flash block (xhc_flash.hip)
 bool launch_xhcf_pre(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
                      hipStream_t st);
