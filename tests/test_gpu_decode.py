@@ -25,7 +25,7 @@ def _print(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("dt,C,use_mgs", [("bf16", 1024, 1), ("f32", 256, 1), ("bf16", 512, 0)])
+@pytest.mark.parametrize("dt,C,use_mgs", [("bf16", 1024, 1), ("f32", 256, 1), ("bf16", 512, 0), ("bf16", 1120, 1)])
 def test_decode_step_matches_oracle(lib, dt, C, use_mgs):
     N, k, m = 16, 4, 2
     steps = np.array([0, 3, 11, 12, 40, 7, 1], dtype=np.int32)

@@ -24,6 +24,7 @@ CASES = [
     (8, 4, 2, 256, 2, 30, 3, "bf16"),
     (4, 4, 2, 256, 1, 37, 3, "bf16"),
     (1, 1, 1, 256, 2, 20, 3, "bf16"),
+    (16, 4, 2, 96, 1, 19, 3, "bf16"),
 ]
 
 
