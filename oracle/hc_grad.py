@@ -13,9 +13,14 @@ the backward propagates routing gradients only through the selected logits).
 The Sinkhorn iterations are differentiated through, which is what a backward
 that recomputes them computes (same paragraph).
 
+The backward splits in two halves, the application (``xhc_apply_grads``:
+the maps held fixed) and the generation (``xhc_gen_grads``: given the maps'
+gradients), whose sum is the whole sublayer's gradient.
+
 Pinned in ``tests/test_oracle_grad_pins.py``: the forward against the NumPy
-oracle, and every gradient against central finite differences of the NumPy
-oracle.
+oracle, every gradient of the whole sublayer and of each half against central
+finite differences of the NumPy oracle, and the sum of the halves against the
+whole.
 """
 from __future__ import annotations
 
@@ -71,38 +76,66 @@ def _mgs(comps):
     return vs
 
 
-def xhc_sublayer_forward(X, out, W_full, W_act, m, k, convs, alpha, b_pre, b_res, b_post, iters=20, use_mgs=True):
-    """Torch tensors in, (inp, new state, I, p) out; the steps of
-    ``hc_oracle.xhc_pre`` then ``hc_oracle.xhc_post``."""
+def _select(z, m, k):
+    """Active set: the fixed streams, then routed streams by descending z,
+    ties to the lower index (the same rule as hc_oracle.xhc_select)."""
+    T, N = z.shape
+    zr = z.detach().numpy()
+    I = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        cand = sorted(range(m, N), key=lambda i: (-zr[t, i], i))
+        I[t] = list(range(m)) + cand[: k - m]
+    return I
+
+
+def xhc_generation(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, iters=20, I=None):
+    """Mapping generation (the steps of hc_oracle.xhc_pre without the dense
+    read): torch tensors in, (I, p, h_pre, h_res, h_post) out.  The active
+    set is a selection made without gradient; pass I to hold it fixed."""
     T, N, C = X.shape
-    B, S, _ = out.shape
     a_pre, a_res, a_post = alpha
     x = X.reshape(T, N * C)
     z = _ln(x) @ W_full[:, :N]
-    with torch.no_grad():   # the selection itself: fixed streams, then routed by descending z, ties to the lower index
-        zr = z.detach().numpy()
-        I = np.empty((T, k), dtype=np.int64)
-        for t in range(T):
-            cand = sorted(range(m, N), key=lambda i: (-zr[t, i], i))
-            I[t] = list(range(m)) + cand[: k - m]
+    if I is None:
+        with torch.no_grad():
+            I = _select(z, m, k)
     It = torch.as_tensor(I)
     s = torch.sigmoid(z)
     p = torch.cat([torch.ones(T, m, dtype=X.dtype), torch.gather(s, 1, It[:, m:])], dim=1)
     h_pre = torch.sigmoid(a_pre * (_rms(x) @ W_full[:, N:2 * N]) + b_pre)
-    inp = torch.einsum("tn,tnc->tc", h_pre, X)
     Xa = torch.gather(X, 1, It[:, :, None].expand(T, k, C))
-    K_r = 1 + len(convs)
     la = _rms(Xa.reshape(T, k * C)) @ W_act
     L = a_res * la[:, : k * k].reshape(T, k, k) + b_res.reshape(k, k)
     H = _sinkhorn(L, iters)
     H = H / torch.clamp(H.sum(-1, keepdim=True), min=1.0)
     h_post = 2.0 * torch.sigmoid(a_post * la[:, k * k:].reshape(T, k, K_r) + b_post.reshape(k, K_r))
+    return I, p, h_pre, H, h_post
+
+
+def xhc_application(X, out, I, p, h_pre, H, h_post, convs, use_mgs=True):
+    """Dense read and mapping application with the maps given (the read of
+    hc_oracle.xhc_pre, then hc_oracle.xhc_post): torch tensors in,
+    (inp, new state) out."""
+    T, N, C = X.shape
+    k = I.shape[1]
+    It = torch.as_tensor(I)
+    inp = torch.einsum("tn,tnc->tc", h_pre, X)
+    Xa = torch.gather(X, 1, It[:, :, None].expand(T, k, C))
+    K_r = 1 + len(convs)
     comps = [out] + [_conv(out, w) for w in convs]
     if use_mgs and len(comps) > 1:
         comps = _mgs(comps)
     V = torch.stack(comps, dim=2).reshape(T, K_r, C)
     new_a = torch.einsum("tij,tjc->tic", H, Xa) + p[:, :, None] * torch.einsum("tjr,trc->tjc", h_post, V)
     Xn = X.scatter(1, It[:, :, None].expand(T, k, C), new_a)
+    return inp, Xn
+
+
+def xhc_sublayer_forward(X, out, W_full, W_act, m, k, convs, alpha, b_pre, b_res, b_post, iters=20, use_mgs=True):
+    """Torch tensors in, (inp, new state, I, p) out; the steps of
+    ``hc_oracle.xhc_pre`` then ``hc_oracle.xhc_post``."""
+    I, p, h_pre, H, h_post = xhc_generation(X, W_full, W_act, m, k, 1 + len(convs), alpha, b_pre, b_res, b_post, iters)
+    inp, Xn = xhc_application(X, out, I, p, h_pre, H, h_post, convs, use_mgs)
     return inp, Xn, I, p
 
 
@@ -125,4 +158,41 @@ def xhc_sublayer_grads(X, out, W_full, W_act, m, k, convs, alpha, b_pre, b_res, 
     g["convs"] = [w.grad.numpy().copy() for w in cw]
     g["alpha"] = np.array([a.grad.item() for a in al])
     g["I"] = I
+    return g
+
+
+def xhc_apply_grads(X, out, I, p, h_pre, h_res, h_post, convs, d_inp, d_X, use_mgs=True):
+    """The application half of the backward: gradients of <inp, d_inp> +
+    <X', d_X> with the maps held fixed, with respect to the state (through the
+    dense read and the mix only), the sublayer output, the conv kernels and
+    the maps h_pre [T, N], h_res [T, k, k], h_post [T, k, K_r], p [T, k]."""
+    args = dict(X=_t(X, True), out=_t(out, True), h_pre=_t(h_pre, True), h_res=_t(h_res, True),
+                h_post=_t(h_post, True), p=_t(p, True))
+    cw = [_t(w, True) for w in convs]
+    inp, Xn = xhc_application(args["X"], args["out"], np.asarray(I), args["p"], args["h_pre"], args["h_res"],
+                              args["h_post"], cw, use_mgs)
+    loss = (inp * _t(d_inp)).sum() + (Xn * _t(d_X)).sum()
+    loss.backward()
+    g = {name: t.grad.numpy().copy() for name, t in args.items()}
+    g["convs"] = [w.grad.numpy().copy() for w in cw]
+    return g
+
+
+def xhc_gen_grads(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, I, d_h_pre, d_h_res, d_h_post, d_p,
+                  iters=20):
+    """The generation half of the backward: given the gradients of the maps
+    (d_h_pre [T, N], d_h_res [T, k, k], d_h_post [T, k, K_r], d_p [T, k]),
+    the gradients of sum(map * d_map) with respect to the state (through the
+    norms and projections), the projection weights, the biases and the
+    scales, with the active set I held fixed."""
+    args = dict(X=_t(X, True), W_full=_t(W_full, True), W_act=_t(W_act, True), b_pre=_t(b_pre, True),
+                b_res=_t(b_res, True), b_post=_t(b_post, True))
+    al = [_t(a, True) for a in alpha]
+    _, p, h_pre, H, h_post = xhc_generation(args["X"], args["W_full"], args["W_act"], m, k, K_r, al, args["b_pre"],
+                                            args["b_res"], args["b_post"], iters, I=np.asarray(I))
+    loss = (h_pre * _t(d_h_pre)).sum() + (H * _t(d_h_res)).sum() + (h_post * _t(d_h_post)).sum() + \
+        (p * _t(d_p)).sum()
+    loss.backward()
+    g = {name: t.grad.numpy().copy() for name, t in args.items()}
+    g["alpha"] = np.array([a.grad.item() for a in al])
     return g

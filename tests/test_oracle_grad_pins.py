@@ -111,3 +111,105 @@ def test_one_stream_gradients_are_the_plain_residual():
     g = grads(d, 1, 1, d_inp, d_X)
     np.testing.assert_allclose(g["X"][:, 0], d_inp + d_X[:, 0], rtol=0, atol=1e-15)
     np.testing.assert_allclose(g["out"].reshape(T, C), d_X[:, 0], rtol=0, atol=1e-15)
+
+
+def _maps(d, m, k, K_r):
+    pre = O.xhc_pre(d["X"], d["W_full"], d["W_act"], m, k, K_r, tuple(d["alpha"]), d["b_pre"], d["b_res"],
+                    d["b_post"], iters=20)
+    return pre
+
+
+@pytest.mark.parametrize("mlp,use_mgs", [(True, True), (True, False), (False, True)])
+def test_application_half_matches_central_differences(mlp, use_mgs):
+    """Maps held fixed: the loss <sum_n h_pre[n] X_n, d_inp> + <xhc_post(...),
+    d_X> of the NumPy oracle, differentiated numerically along random
+    directions in the state, the output, the conv kernels and every map."""
+    r = rng(54, int(mlp), int(use_mgs))
+    B, S, N, k, m, C = 2, 13, 6, 3, 1, 8
+    d = case(r, B, S, N, k, m, C, mlp)
+    K_r = 4 if mlp else 1
+    T = B * S
+    pre = _maps(d, m, k, K_r)
+    maps = dict(h_pre=pre["h_pre"], h_res=pre["h_res"], h_post=pre["h_post"], p=pre["p"])
+    d_inp, d_X = r.standard_normal((T, C)), r.standard_normal((T, N, C))
+    g = G.xhc_apply_grads(d["X"], d["out"], pre["I"], maps["p"], maps["h_pre"], maps["h_res"], maps["h_post"],
+                          d["convs"], d_inp, d_X, use_mgs)
+
+    def loss(v):
+        inp = np.einsum("tn,tnc->tc", v["h_pre"], v["X"])
+        Xn = O.xhc_post(v["X"], v["out"], pre["I"], v["p"], v["h_res"], v["h_post"], v["convs"], use_mgs)
+        return float(np.sum(inp * d_inp) + np.sum(Xn * d_X))
+
+    base = dict(maps, X=d["X"], out=d["out"], convs=d["convs"])
+    h = 1e-5
+    for name in ["X", "out", "h_pre", "h_res", "h_post", "p"] + (["convs"] if mlp else []):
+        if name == "convs":
+            dirs = [r.standard_normal(w.shape) for w in d["convs"]]
+            lin = sum(float(np.sum(gw * dw)) for gw, dw in zip(g["convs"], dirs))
+            plus = dict(base, convs=[w + h * dw for w, dw in zip(d["convs"], dirs)])
+            minus = dict(base, convs=[w - h * dw for w, dw in zip(d["convs"], dirs)])
+        else:
+            dv = r.standard_normal(np.shape(base[name]))
+            lin = float(np.sum(g[name] * dv))
+            plus, minus = dict(base), dict(base)
+            plus[name] = base[name] + h * dv
+            minus[name] = base[name] - h * dv
+        fd = (loss(plus) - loss(minus)) / (2 * h)
+        assert abs(fd - lin) <= 1e-7 * max(1.0, abs(fd)), (name, fd, lin)
+
+
+@pytest.mark.parametrize("mlp", [True, False])
+def test_generation_half_matches_central_differences(mlp):
+    """Given map gradients, the loss sum(map * d_map) over the maps of the
+    NumPy oracle's xhc_pre, differentiated numerically along random
+    directions in the state, the weights, the biases and the scales."""
+    r = rng(55, int(mlp))
+    B, S, N, k, m, C = 2, 11, 6, 3, 1, 8
+    d = case(r, B, S, N, k, m, C, mlp)
+    K_r = 4 if mlp else 1
+    T = B * S
+    pre = _maps(d, m, k, K_r)
+    dm = dict(h_pre=r.standard_normal((T, N)), h_res=r.standard_normal((T, k, k)),
+              h_post=r.standard_normal((T, k, K_r)), p=r.standard_normal((T, k)))
+    g = G.xhc_gen_grads(d["X"], d["W_full"], d["W_act"], m, k, K_r, tuple(d["alpha"]), d["b_pre"], d["b_res"],
+                        d["b_post"], pre["I"], dm["h_pre"], dm["h_res"], dm["h_post"], dm["p"])
+
+    def loss(v):
+        q = _maps(v, m, k, K_r)
+        assert np.array_equal(q["I"], pre["I"]), "the active set moved under the perturbation"
+        return sum(float(np.sum(q[n] * dm[n])) for n in dm)
+
+    h = 1e-5
+    for name in ["X", "W_full", "W_act", "b_pre", "b_res", "b_post", "alpha"]:
+        dv = r.standard_normal(np.shape(d[name]))
+        lin = float(np.sum(g[name] * dv))
+        plus, minus = dict(d), dict(d)
+        plus[name] = d[name] + h * dv
+        minus[name] = d[name] - h * dv
+        fd = (loss(plus) - loss(minus)) / (2 * h)
+        assert abs(fd - lin) <= 1e-7 * max(1.0, abs(fd)), (name, fd, lin)
+
+
+@pytest.mark.parametrize("mlp", [True, False])
+def test_halves_add_up_to_the_whole_sublayer(mlp):
+    """Application half, then the generation half fed with its map
+    gradients: the state gradients add, and every other gradient is the whole
+    sublayer's."""
+    r = rng(56, int(mlp))
+    B, S, N, k, m, C = 2, 9, 6, 3, 1, 8
+    d = case(r, B, S, N, k, m, C, mlp)
+    K_r = 4 if mlp else 1
+    T = B * S
+    d_inp, d_X = r.standard_normal((T, C)), r.standard_normal((T, N, C))
+    whole = grads(d, m, k, d_inp, d_X)
+    pre = _maps(d, m, k, K_r)
+    ga = G.xhc_apply_grads(d["X"], d["out"], pre["I"], pre["p"], pre["h_pre"], pre["h_res"], pre["h_post"],
+                           d["convs"], d_inp, d_X)
+    gg = G.xhc_gen_grads(d["X"], d["W_full"], d["W_act"], m, k, K_r, tuple(d["alpha"]), d["b_pre"], d["b_res"],
+                         d["b_post"], pre["I"], ga["h_pre"], ga["h_res"], ga["h_post"], ga["p"])
+    np.testing.assert_allclose(ga["X"] + gg["X"], whole["X"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ga["out"], whole["out"], rtol=1e-10, atol=1e-12)
+    for a, b in zip(ga["convs"], whole["convs"]):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+    for name in ["W_full", "W_act", "b_pre", "b_res", "b_post", "alpha"]:
+        np.testing.assert_allclose(gg[name], whole[name], rtol=1e-10, atol=1e-12)
