@@ -390,6 +390,68 @@ xhc_status xhcf4_pre(const xhc_config* cfg, const xhcf4_weights* w, const void* 
 xhc_status xhcf4_post(const xhc_config* cfg, const xhcf4_weights* w, int32_t q, void* X, const void* out,
                       const void* bases, void* inp, void* ws, xhc_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Backward of one xHC sublayer: the gradients of xhc_pre followed by
+ * xhc_post (xHC paper "xHC: Expanded Hyper-Connections", paragraphs
+ * "Mapping generation" and "Mapping application", differentiated; summary
+ * "小红书xHC：时序特征增强 + 稀疏写回", sections 3.3 and 3.4).  The active set
+ * is a selection: it is held fixed, and the router receives gradient only
+ * through the router weights p of the selected routed streams.  The Sinkhorn
+ * iterations are recomputed and differentiated through.
+ *
+ * Two calls, run in this order with the same backward workspace bws:
+ *   xhc_post_backward  the application half (maps held fixed), and
+ *   xhc_pre_backward   the generation half (through the maps).
+ * Both read the maps that xhc_pre left in ws for the same cfg and X.
+ * ------------------------------------------------------------------------- */
+
+/* Weight gradients (host struct holding device pointers; float, written). */
+typedef struct {
+  float* dW_full;   /* [N*C][2N], layout of xhc_weights.w_full */
+  float* dW_act;    /* [k*C][k*k + k*K_r], layout of xhc_weights.w_act */
+  float* d_b_pre;   /* [N] */
+  float* d_b_res;   /* [k*k] */
+  float* d_b_post;  /* [k*K_r] */
+  float* d_alpha;   /* [3]: alpha_pre, alpha_res, alpha_post */
+} xhc_grads;
+
+/* Byte offsets of the public arrays inside a backward workspace (float). */
+typedef struct {
+  size_t d_h_pre;   /* [T][N]    gradient of H_pre */
+  size_t d_h_res;   /* [T][k][k] gradient of H_res (after the row clamp) */
+  size_t d_h_post;  /* [T][k][K_r] gradient of H_post */
+  size_t d_p;       /* [T][k]    gradient of the router weights p */
+  size_t total;     /* bytes the caller must allocate (0 when T == 0) */
+} xhc_bwd_ws_layout;
+
+size_t xhc_backward_workspace_bytes(const xhc_config* cfg);
+xhc_status xhc_backward_workspace_layout(const xhc_config* cfg, xhc_bwd_ws_layout* out);
+
+/* Application half.
+ *   X:      [T][N][C] the state xhc_pre read (before xhc_post), read only
+ *   out:    [T][C] the sublayer output, read only
+ *   d_inp:  [T][C] gradient of the sublayer input inp, read only
+ *   d_X:    [T][N][C] gradient of the new state, read only
+ *   dX:     [T][N][C] written: the state gradient through the dense read and
+ *           the mix (non-active rows d_X + H_pre[n] d_inp; active row j
+ *           sum_i H_res[i][j] d_X[I_i] + H_pre[I_j] d_inp); may be d_X itself
+ *   d_out:  [T][C] written: gradient of out (through Gram-Schmidt and the
+ *           causal convolutions for MLP-type sublayers)
+ *   d_conv: float [24][C] written, the conv-kernel gradients in conv_w's
+ *           layout (MLP-type; NULL for attention-type)
+ *   ws:     the workspace xhc_pre filled;  bws: xhc_backward_workspace_bytes
+ * X, out, d_inp, d_X, dX, d_out in the state dtype, 16-byte aligned. */
+xhc_status xhc_post_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, const void* out,
+                             const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv,
+                             const void* ws, void* bws, xhc_stream_t stream);
+
+/* Generation half: adds to dX the state gradient through the norms and the
+ * projections (full state for the router and H_pre, active rows for H_res
+ * and H_post) and writes every field of g.  X as for xhc_post_backward; dX
+ * as that call left it (read and written). */
+xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, void* dX,
+                            const xhc_grads* g, const void* ws, void* bws, xhc_stream_t stream);
+
 /* Message for the last non-OK status returned on this host thread. */
 const char* xhc_last_error(void);
 

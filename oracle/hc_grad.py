@@ -88,10 +88,12 @@ def _select(z, m, k):
     return I
 
 
-def xhc_generation(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, iters=20, I=None):
+def xhc_generation(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, iters=20, I=None, X_act_src=None):
     """Mapping generation (the steps of hc_oracle.xhc_pre without the dense
     read): torch tensors in, (I, p, h_pre, h_res, h_post) out.  The active
-    set is a selection made without gradient; pass I to hold it fixed."""
+    set is a selection made without gradient; pass I to hold it fixed.
+    X_act_src (same values as X) feeds the active-row maps instead of X, so
+    that the two paths' state gradients can be told apart."""
     T, N, C = X.shape
     a_pre, a_res, a_post = alpha
     x = X.reshape(T, N * C)
@@ -103,7 +105,7 @@ def xhc_generation(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, ite
     s = torch.sigmoid(z)
     p = torch.cat([torch.ones(T, m, dtype=X.dtype), torch.gather(s, 1, It[:, m:])], dim=1)
     h_pre = torch.sigmoid(a_pre * (_rms(x) @ W_full[:, N:2 * N]) + b_pre)
-    Xa = torch.gather(X, 1, It[:, :, None].expand(T, k, C))
+    Xa = torch.gather(X if X_act_src is None else X_act_src, 1, It[:, :, None].expand(T, k, C))
     la = _rms(Xa.reshape(T, k * C)) @ W_act
     L = a_res * la[:, : k * k].reshape(T, k, k) + b_res.reshape(k, k)
     H = _sinkhorn(L, iters)
@@ -184,15 +186,21 @@ def xhc_gen_grads(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, I, d
     (d_h_pre [T, N], d_h_res [T, k, k], d_h_post [T, k, K_r], d_p [T, k]),
     the gradients of sum(map * d_map) with respect to the state (through the
     norms and projections), the projection weights, the biases and the
-    scales, with the active set I held fixed."""
+    scales, with the active set I held fixed.  The state gradient is also
+    returned split by path: "X_full" through the full-state router and
+    pre-map, "X_act" through the active-row maps ("X" is their sum)."""
     args = dict(X=_t(X, True), W_full=_t(W_full, True), W_act=_t(W_act, True), b_pre=_t(b_pre, True),
                 b_res=_t(b_res, True), b_post=_t(b_post, True))
+    X_act = _t(X, True)
     al = [_t(a, True) for a in alpha]
     _, p, h_pre, H, h_post = xhc_generation(args["X"], args["W_full"], args["W_act"], m, k, K_r, al, args["b_pre"],
-                                            args["b_res"], args["b_post"], iters, I=np.asarray(I))
+                                            args["b_res"], args["b_post"], iters, I=np.asarray(I), X_act_src=X_act)
     loss = (h_pre * _t(d_h_pre)).sum() + (H * _t(d_h_res)).sum() + (h_post * _t(d_h_post)).sum() + \
         (p * _t(d_p)).sum()
     loss.backward()
     g = {name: t.grad.numpy().copy() for name, t in args.items()}
+    g["X_full"] = g["X"]
+    g["X_act"] = X_act.grad.numpy().copy()
+    g["X"] = g["X_full"] + g["X_act"]
     g["alpha"] = np.array([a.grad.item() for a in al])
     return g

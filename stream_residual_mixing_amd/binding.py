@@ -28,6 +28,7 @@ EXPORTS = (
     "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_route", "xhc_pre_chained", "xhc_post_chained",
     "xhc_post_decode", "xhcf_workspace_bytes", "xhcf_workspace_layout", "xhcf_pre", "xhcf_mid", "xhcf_post",
     "xhcf4_workspace_bytes", "xhcf4_workspace_layout", "xhcf4_pre", "xhcf4_post",
+    "xhc_backward_workspace_bytes", "xhc_backward_workspace_layout", "xhc_post_backward", "xhc_pre_backward",
     "xhc_last_error",
 )
 
@@ -80,6 +81,14 @@ class Xhcf4Weights(ctypes.Structure):
 
 class Xhcf4WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "p", "h_pre", "h_post", "h_res", "z_router", "total")]
+
+
+class XhcGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dW_full", "dW_act", "d_b_pre", "d_b_res", "d_b_post", "d_alpha")]
+
+
+class XhcBwdWsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("d_h_pre", "d_h_res", "d_h_post", "d_p", "total")]
 
 
 class XhcError(RuntimeError):
@@ -283,6 +292,17 @@ class Lib:
         d.xhcf4_post.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(Xhcf4Weights), ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p]
+        d.xhc_backward_workspace_bytes.restype = ctypes.c_size_t
+        d.xhc_backward_workspace_bytes.argtypes = [ctypes.POINTER(XhcConfig)]
+        d.xhc_backward_workspace_layout.restype = ctypes.c_int
+        d.xhc_backward_workspace_layout.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcBwdWsLayout)]
+        d.xhc_post_backward.restype = ctypes.c_int
+        d.xhc_post_backward.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights)] + \
+            [ctypes.c_void_p] * 10
+        d.xhc_pre_backward.restype = ctypes.c_int
+        d.xhc_pre_backward.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.POINTER(XhcGrads), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
         d.xhc_last_error.restype = ctypes.c_char_p
         d.xhc_last_error.argtypes = []
 
@@ -429,6 +449,79 @@ class Lib:
         self._ok(self.dll.xhc_post_decode(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
                                           conv_state.data_ptr(), steps.data_ptr(), ws.data_ptr(),
                                           _stream_ptr(stream)))
+
+    # backward of one xHC sublayer
+    def backward_workspace_bytes(self, cfg: Config) -> int:
+        c = cfg.c()
+        return int(self.dll.xhc_backward_workspace_bytes(ctypes.byref(c)))
+
+    def backward_layout(self, cfg: Config) -> XhcBwdWsLayout:
+        c, L = cfg.c(), XhcBwdWsLayout()
+        self._ok(self.dll.xhc_backward_workspace_layout(ctypes.byref(c), ctypes.byref(L)))
+        return L
+
+    def backward_workspace(self, cfg: Config, device="cuda") -> torch.Tensor:
+        n = self.backward_workspace_bytes(cfg)
+        if n == 0 and cfg.T > 0:
+            self.backward_layout(cfg)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def backward_ws_arrays(self, cfg: Config, bws: torch.Tensor) -> dict:
+        """Views of the map gradients in a backward workspace."""
+        L = self.backward_layout(cfg)
+        T, N, k, Kr = cfg.T, cfg.N, cfg.k, cfg.K_r
+
+        def view(off, shape):
+            n = 1
+            for s in shape:
+                n *= s
+            return bws[off: off + 4 * n].view(torch.float32).reshape(shape)
+
+        return dict(h_pre=view(L.d_h_pre, (T, N)), h_res=view(L.d_h_res, (T, k, k)),
+                    h_post=view(L.d_h_post, (T, k, Kr)), p=view(L.d_p, (T, k)))
+
+    def grads(self, cfg: Config, device="cuda") -> dict:
+        """Float gradient buffers for xhc_pre_backward (dict of tensors)."""
+        N, k, C, Kr = cfg.N, cfg.k, cfg.C, cfg.K_r
+        f = dict(dtype=torch.float32, device=device)
+        return dict(W_full=torch.empty((N * C, 2 * N), **f), W_act=torch.empty((k * C, k * k + k * Kr), **f),
+                    b_pre=torch.empty(N, **f), b_res=torch.empty(k * k, **f), b_post=torch.empty(k * Kr, **f),
+                    alpha=torch.empty(3, **f))
+
+    def _check_bws(self, cfg, bws):
+        need = self.backward_workspace_bytes(cfg)
+        if bws is None or not bws.is_cuda or bws.numel() * bws.element_size() < need:
+            raise ValueError(f"backward workspace must be a GPU tensor of at least {need} bytes")
+
+    def xhc_post_backward(self, cfg: Config, w: Weights, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws,
+                          stream=None):
+        self._check_common(cfg, w, X, ws, False, False)
+        dt = cfg.torch_dtype
+        for t, name, shape in ((out, "out", (cfg.T, cfg.C)), (d_inp, "d_inp", (cfg.T, cfg.C)),
+                               (d_X, "d_X", (cfg.T, cfg.N, cfg.C)), (dX, "dX", (cfg.T, cfg.N, cfg.C)),
+                               (d_out, "d_out", (cfg.T, cfg.C))):
+            _check(t, name, shape, dt)
+        if cfg.K_r == 4:
+            _check(d_conv, "d_conv", (sum(cfg.kernels), cfg.C), torch.float32)
+        self._check_bws(cfg, bws)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_post_backward(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
+                                            d_inp.data_ptr(), d_X.data_ptr(), dX.data_ptr(), d_out.data_ptr(),
+                                            d_conv.data_ptr() if d_conv is not None else None, ws.data_ptr(),
+                                            bws.data_ptr(), _stream_ptr(stream)))
+
+    def xhc_pre_backward(self, cfg: Config, w: Weights, X, dX, g: dict, ws, bws, stream=None):
+        self._check_common(cfg, w, X, ws, False, True)
+        _check(dX, "dX", (cfg.T, cfg.N, cfg.C), cfg.torch_dtype)
+        ref = self.grads(cfg, device="meta")
+        for name, t in ref.items():
+            _check(g[name], "d_" + name, tuple(t.shape), torch.float32)
+        self._check_bws(cfg, bws)
+        c, cw = cfg.c(), w.c()
+        gg = XhcGrads(g["W_full"].data_ptr(), g["W_act"].data_ptr(), g["b_pre"].data_ptr(), g["b_res"].data_ptr(),
+                      g["b_post"].data_ptr(), g["alpha"].data_ptr())
+        self._ok(self.dll.xhc_pre_backward(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), dX.data_ptr(),
+                                           ctypes.byref(gg), ws.data_ptr(), bws.data_ptr(), _stream_ptr(stream)))
 
     # xHC-Flash block: attention + MLP sharing one routing
     def flash_workspace_bytes(self, cfg: Config) -> int:

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libxhc.so")
-SOURCES = ["xhc_api.hip", "xhc_kernels.hip", "xhc_pre.hip", "xhc_post.hip", "xhc_chain.hip", "xhc_flash.hip"]
+SOURCES = ["xhc_api.hip", "xhc_kernels.hip", "xhc_pre.hip", "xhc_post.hip", "xhc_chain.hip", "xhc_flash.hip",
+           "xhc_backward.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -661,6 +661,77 @@ xhc_status xhcf4_post(const xhc_config* cfg, const xhcf4_weights* w, int32_t q, 
   return finish(st);
 }
 
+size_t xhc_backward_workspace_bytes(const xhc_config* cfg) {
+  xhc::Plan P;
+  if (make_plan(cfg, false, &P) != XHC_OK) return 0;
+  xhc::BwdPlan B;
+  xhc::make_bwd_plan(P, &B);
+  return B.total;
+}
+
+xhc_status xhc_backward_workspace_layout(const xhc_config* cfg, xhc_bwd_ws_layout* out) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if (!out) return fail(XHC_ERR_INVALID_ARG, "layout output is NULL");
+  xhc::BwdPlan B;
+  xhc::make_bwd_plan(P, &B);
+  out->d_h_pre = B.o_dhpre;
+  out->d_h_res = B.o_dhres;
+  out->d_h_post = B.o_dhpost;
+  out->d_p = B.o_dp;
+  out->total = B.total;
+  return XHC_OK;
+}
+
+xhc_status xhc_post_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, const void* out,
+                             const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv,
+                             const void* ws, void* bws, xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_weights(P, w, false)) != XHC_OK) return s;
+  if (P.T == 0) return XHC_OK;
+  const void* ptrs[] = {X, out, d_inp, d_X, dX, d_out, ws, bws};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q))
+      return fail(XHC_ERR_INVALID_ARG, "X, out, d_inp, d_X, dX, d_out, ws and bws must be 16-byte aligned, non-NULL");
+  if (P.KR == 4 && !d_conv) return fail(XHC_ERR_INVALID_ARG, "d_conv must not be NULL for MLP-type configs");
+  // dX may be d_X; no other pair may alias
+  const void* outs[] = {dX, d_out, bws};
+  const void* ins[] = {X, out, d_inp, ws};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o == i) return fail(XHC_ERR_INVALID_ARG, "outputs dX, d_out and bws must not alias X, out, d_inp or ws");
+  if (dX == d_out || dX == bws || d_out == bws || d_out == d_X || bws == d_X)
+    return fail(XHC_ERR_INVALID_ARG, "dX, d_out and bws must be distinct (only dX may be d_X)");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_post_backward(P, w, X, out, d_inp, d_X, dX, d_out, d_conv, static_cast<const char*>(ws),
+                                     static_cast<char*>(bws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, void* dX,
+                            const xhc_grads* g, const void* ws, void* bws, xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_weights(P, w, true)) != XHC_OK) return s;
+  if (!g || !g->dW_full || !g->dW_act || !g->d_b_pre || !g->d_b_res || !g->d_b_post || !g->d_alpha)
+    return fail(XHC_ERR_INVALID_ARG, "every gradient pointer must be set");
+  if (P.T == 0) return XHC_OK;
+  const void* ptrs[] = {X, dX, ws, bws};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return fail(XHC_ERR_INVALID_ARG, "X, dX, ws and bws must be 16-byte aligned, non-NULL");
+  if (dX == X || dX == ws || dX == bws || bws == X || bws == ws)
+    return fail(XHC_ERR_INVALID_ARG, "dX and bws must not alias X, ws or each other");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_pre_backward(P, w, X, dX, g, static_cast<const char*>(ws), static_cast<char*>(bws), st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
 const char* xhc_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

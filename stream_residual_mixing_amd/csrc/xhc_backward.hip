@@ -1,0 +1,1070 @@
+// libxhc: backward of one xHC sublayer, the gradients of xhc_pre + xhc_post.
+//
+// The forward is differentiated in two halves that meet at the maps
+// (xHC paper "xHC: Expanded Hyper-Connections", paragraphs "Mapping
+// generation" and "Mapping application"; summary "小红书xHC：时序特征增强 +
+// 稀疏写回", sections 3.3 and 3.4):
+//
+//  * application: with the maps fixed, the dense read inp = sum_n H_pre[n] X_n
+//    and the active rewrite X_I' = H_res X_I + diag(p) H_post V give the state
+//    gradient through the read and the mix, the write basis' gradient (then
+//    the Gram-Schmidt and the causal convolutions, transposed) and the maps'
+//    gradients;
+//  * generation: the maps' gradients go back through the sigmoids, the
+//    Sinkhorn iterations (recomputed) and the row clamp, the router weights of
+//    the selected streams, the RMSNorm / LayerNorm and the projections, giving
+//    the state gradient through the norms and every weight gradient.
+//
+// Two small scalar programs are differentiated in forward mode, one tangent
+// per input direction, recomputed from their inputs instead of stored: the
+// Gram-Schmidt coefficients as a function of the K_r x K_r Gram matrix (10
+// symmetric directions) and the Sinkhorn map as a function of its k x k logits
+// (k^2 directions, one lane each).
+//
+// Kernels, in order:
+//  application:  bwd_apply (per token: dot products, scalar stage, dX rows and
+//                the basis gradient), bwd_conv (MLP-type: transposed convs
+//                into d_out, conv-weight partials), bwd_reduce;
+//  generation:   packing + split-K MFMA projections of X and of the gathered
+//                active rows (recomputing the raw logits and norm sums),
+//                bwd_wcolsum, bwd_token (per-token scalars), bwd_sum_rows
+//                (bias / scale gradients), bwd_rows twice (full state, active
+//                rows: dX += W G + c x, weight-gradient partials), bwd_reduce.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "xhc.h"
+#include "xhc_device.hpp"
+#include "xhc_internal.hpp"
+
+namespace xhc {
+
+namespace {
+
+constexpr int BT = 256;      // threads per workgroup
+constexpr int NCONV = 24;    // conv weight rows: kernels 4, 8, 12
+
+__device__ __forceinline__ float ld1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float ld1(const float* p) { return *p; }
+__device__ __forceinline__ void st1(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16(v); }
+__device__ __forceinline__ void st1(float* p, float v) { *p = v; }
+
+// Sum of v over the workgroup (BT threads); every thread receives it.
+__device__ __forceinline__ float block_sum(float v, float* s_tmp) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) s_tmp[wave] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < BT / WAVE; ++w) r += s_tmp[w];
+  return r;
+}
+
+// Write basis of token t at channels c..c+VEC: the output itself and, for
+// MLP-type sublayers, its causal depthwise convolutions with kernels 4, 8, 12
+// (weight rows 0, 4, 12; row off + i multiplies lag i), lags that reach
+// before the sequence start left out.
+template <class E, int KR>
+__device__ __forceinline__ void write_basis(const typename E::T* out_t, int s, int C, int c, const float* conv_w,
+                                            float (&g)[KR][E::VEC]) {
+  constexpr int V = E::VEC;
+  E::unpack(ld16(out_t + c), g[0]);
+  if constexpr (KR == 4) {
+#pragma unroll
+    for (int q = 1; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < V; ++e) g[q][e] = 0.f;
+    const int L = s < 11 ? s : 11;
+    for (int tau = 0; tau <= L; ++tau) {
+      float o[V];
+      E::unpack(ld16(out_t - (long)tau * C + c), o);
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        if (tau >= 4 * q) continue;
+        const int row = (q == 1 ? 0 : q == 2 ? 4 : 12) + tau;
+        const float* w = conv_w + (size_t)row * C + c;
+#pragma unroll
+        for (int e = 0; e < V; ++e) g[q][e] = fmaf(w[e], o[e], g[q][e]);
+      }
+    }
+  }
+}
+
+// Gram-Schmidt coefficients from the Gram matrix M of the raw components:
+// v_r = sum_q A[r][q] g_q, with u <- u - <u, v> / (<v, v> + eps) v taken over
+// the earlier v's in order.  With a tangent direction: M's entries (a, b)
+// and (b, a) moved together (one entry when a == b); returns
+// sum_{r,q} D[r][q] dA[r][q].
+template <int R>
+__device__ float mgs_coef(const float (&M)[R][R], float eps, float (&A)[R][R], int a, int b, const float (&D)[R][R]) {
+  float dA[R][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int q = 0; q < R; ++q) { A[r][q] = (r == q && r == 0) ? 1.f : 0.f; dA[r][q] = 0.f; }
+#pragma unroll
+  for (int r = 1; r < R; ++r) {
+    float u[R], du[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) { u[i] = i == r ? 1.f : 0.f; du[i] = 0.f; }
+#pragma unroll
+    for (int v = 0; v < R; ++v) {
+      if (v >= r) break;
+      float MAv[R], dMAv[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float s = 0.f, ds = 0.f;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          s = fmaf(M[i][j], A[v][j], s);
+          const float dm = ((i == a && j == b) || (i == b && j == a)) ? 1.f : 0.f;
+          ds = fmaf(dm, A[v][j], fmaf(M[i][j], dA[v][j], ds));
+        }
+        MAv[i] = s;
+        dMAv[i] = ds;
+      }
+      float num = 0.f, dnum = 0.f, den = eps, dden = 0.f;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        num = fmaf(u[i], MAv[i], num);
+        dnum = fmaf(du[i], MAv[i], fmaf(u[i], dMAv[i], dnum));
+        den = fmaf(A[v][i], MAv[i], den);
+        dden = fmaf(dA[v][i], MAv[i], fmaf(A[v][i], dMAv[i], dden));
+      }
+      const float cf = num / den;
+      const float dc = (dnum - cf * dden) / den;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        du[i] = du[i] - dc * A[v][i] - cf * dA[v][i];
+        u[i] = u[i] - cf * A[v][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) { A[r][i] = u[i]; dA[r][i] = du[i]; }
+  }
+  float f = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int q = 0; q < R; ++q) f = fmaf(D[r][q], dA[r][q], f);
+  return f;
+}
+
+struct BwdApplyArgs {
+  const void *X, *out, *d_inp, *d_X;
+  void *dX, *d_out, *xa;
+  float* dg;
+  const float* conv_w;
+  const int* idx;
+  const float *p, *h_pre, *h_res, *h_post;
+  float *d_hpre, *d_hres, *d_hpost, *d_p;
+  int T, S, C, use_mgs;
+  float eps_mgs;
+};
+
+// Application half, one workgroup per token.  Pass 1 takes the dot products
+// <d_inp, X_n> (H_pre gradient), <dY_i, X_{I_j}> (H_res gradient),
+// <dY_i, g_q> and the Gram <g_a, g_b> of the raw write components, with dY_i
+// the new state's gradient on active row i; and stores the gathered active
+// rows for the generation half.  The scalar stage gives the H_post and p
+// gradients and the basis gradient as a combination of the dY_i and the g_q.
+// Pass 2 writes dX (non-active rows: d_X + H_pre[n] d_inp; active row j:
+// sum_i H_res[i][j] dY_i + H_pre[I_j] d_inp) and the basis gradient.
+template <class E, int N, int K, int KR>
+__global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
+  using T = typename E::T;
+  constexpr int V = E::VEC;
+  constexpr int NG = KR * (KR + 1) / 2;
+  constexpr int O_H = N, O_E = N + K * K, O_G = O_E + K * KR, NACC = O_G + NG;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int C = a.C;
+  const int s = t % a.S;
+  const T* X = reinterpret_cast<const T*>(a.X) + (size_t)t * N * C;
+  const T* dXn = reinterpret_cast<const T*>(a.d_X) + (size_t)t * N * C;
+  const T* di = reinterpret_cast<const T*>(a.d_inp) + (size_t)t * C;
+  const T* ot = reinterpret_cast<const T*>(a.out) + (size_t)t * C;
+  T* dX = reinterpret_cast<T*>(a.dX) + (size_t)t * N * C;
+  T* xa = reinterpret_cast<T*>(a.xa) + (size_t)t * K * C;
+  __shared__ int s_idx[K], s_pos[N];
+  __shared__ float s_hpre[N], s_mix[K][K];
+  __shared__ float s_red[BT / WAVE][NACC], s_acc[NACC];
+  __shared__ float s_al[KR][K], s_be[KR][KR];
+  if (tid < N) {
+    s_hpre[tid] = a.h_pre[(size_t)t * N + tid];
+    s_pos[tid] = -1;
+  }
+  if (tid < K * K) s_mix[tid / K][tid % K] = a.h_res[(size_t)t * K * K + tid];
+  __syncthreads();
+  if (tid < K) {
+    const int n = a.idx[(size_t)t * K + tid];
+    s_idx[tid] = n;
+    s_pos[n] = tid;
+  }
+  __syncthreads();
+
+  float acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) acc[i] = 0.f;
+  const int ngrp = C / V;
+  for (int cg = tid; cg < ngrp; cg += BT) {
+    const int c = cg * V;
+    float fi[V], y[K][V], xr[K][V], g[KR][V];
+    E::unpack(ld16(di + c), fi);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      E::unpack(ld16(dXn + (size_t)s_idx[i] * C + c), y[i]);
+      const uint4 raw = ld16(X + (size_t)s_idx[i] * C + c);
+      st16(xa + (size_t)i * C + c, raw);
+      E::unpack(raw, xr[i]);
+    }
+    write_basis<E, KR>(ot, s, C, c, a.conv_w, g);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float x[V];
+      E::unpack(ld16(X + (size_t)n * C + c), x);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[n] = fmaf(fi[e], x[e], acc[n]);
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[O_H + i * K + j] = fmaf(y[i][e], xr[j][e], acc[O_H + i * K + j]);
+#pragma unroll
+      for (int q = 0; q < KR; ++q)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[O_E + i * KR + q] = fmaf(y[i][e], g[q][e], acc[O_E + i * KR + q]);
+    }
+    int gi = 0;
+#pragma unroll
+    for (int qa = 0; qa < KR; ++qa)
+#pragma unroll
+      for (int qb = qa; qb < KR; ++qb, ++gi)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[O_G + gi] = fmaf(g[qa][e], g[qb][e], acc[O_G + gi]);
+  }
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) {
+    const float v = wave_sum(acc[i]);
+    if (lane == 0) s_red[wave][i] = v;
+  }
+  __syncthreads();
+  if (tid < NACC) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < BT / WAVE; ++w) v += s_red[w][tid];
+    s_acc[tid] = v;
+  }
+  __syncthreads();
+
+  if (tid == 0) {
+    float Gm[KR][KR], Ec[K][KR], A[KR][KR], D[KR][KR], gam[KR][K], hp[K][KR], pp[K];
+    int gi = 0;
+#pragma unroll
+    for (int qa = 0; qa < KR; ++qa)
+#pragma unroll
+      for (int qb = qa; qb < KR; ++qb, ++gi) Gm[qa][qb] = Gm[qb][qa] = s_acc[O_G + gi];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      pp[i] = a.p[(size_t)t * K + i];
+#pragma unroll
+      for (int q = 0; q < KR; ++q) {
+        Ec[i][q] = s_acc[O_E + i * KR + q];
+        hp[i][q] = a.h_post[((size_t)t * K + i) * KR + q];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < KR; ++r)
+#pragma unroll
+      for (int i = 0; i < K; ++i) gam[r][i] = pp[i] * hp[i][r];
+#pragma unroll
+    for (int r = 0; r < KR; ++r)
+#pragma unroll
+      for (int q = 0; q < KR; ++q) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) d = fmaf(gam[r][i], Ec[i][q], d);
+        D[r][q] = d;
+        s_be[r][q] = 0.f;
+      }
+    const bool mgs = KR > 1 && a.use_mgs;
+    if (mgs) {
+      mgs_coef<KR>(Gm, a.eps_mgs, A, -1, -1, D);
+#pragma unroll
+      for (int qa = 0; qa < KR; ++qa)
+#pragma unroll
+        for (int qb = qa; qb < KR; ++qb) {
+          float Ad[KR][KR];
+          const float f = mgs_coef<KR>(Gm, a.eps_mgs, Ad, qa, qb, D);
+          if (qa == qb) {
+            s_be[qa][qa] += 2.f * f;
+          } else {
+            s_be[qa][qb] += f;
+            s_be[qb][qa] += f;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < KR; ++r)
+#pragma unroll
+        for (int q = 0; q < KR; ++q) A[r][q] = r == q ? 1.f : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float dpv = 0.f;
+#pragma unroll
+      for (int r = 0; r < KR; ++r) {
+        float dq = 0.f;
+#pragma unroll
+        for (int q = 0; q < KR; ++q) dq = fmaf(A[r][q], Ec[i][q], dq);
+        a.d_hpost[((size_t)t * K + i) * KR + r] = pp[i] * dq;
+        dpv = fmaf(hp[i][r], dq, dpv);
+      }
+      a.d_p[(size_t)t * K + i] = dpv;
+    }
+#pragma unroll
+    for (int q = 0; q < KR; ++q)
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        float al = 0.f;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) al = fmaf(A[r][q], gam[r][i], al);
+        s_al[q][i] = al;
+      }
+  }
+  if (tid < N) a.d_hpre[(size_t)t * N + tid] = s_acc[tid];
+  if (tid < K * K) a.d_hres[(size_t)t * K * K + tid] = s_acc[O_H + tid];
+  __syncthreads();
+
+  for (int cg = tid; cg < ngrp; cg += BT) {
+    const int c = cg * V;
+    float fi[V], y[K][V], g[KR][V];
+    E::unpack(ld16(di + c), fi);
+#pragma unroll
+    for (int i = 0; i < K; ++i) E::unpack(ld16(dXn + (size_t)s_idx[i] * C + c), y[i]);
+    if constexpr (KR == 4) write_basis<E, KR>(ot, s, C, c, a.conv_w, g);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float o[V];
+      const int j = s_pos[n];
+      const float h = s_hpre[n];
+      if (j >= 0) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          float v = h * fi[e];
+#pragma unroll
+          for (int i = 0; i < K; ++i) v = fmaf(s_mix[i][j], y[i][e], v);
+          o[e] = v;
+        }
+      } else {
+        E::unpack(ld16(dXn + (size_t)n * C + c), o);
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] = fmaf(h, fi[e], o[e]);
+      }
+      st16(dX + (size_t)n * C + c, E::pack(o));
+    }
+#pragma unroll
+    for (int q = 0; q < KR; ++q) {
+      float o[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) v = fmaf(s_al[q][i], y[i][e], v);
+        if constexpr (KR == 4) {
+#pragma unroll
+          for (int b = 0; b < KR; ++b) v = fmaf(s_be[q][b], g[b][e], v);
+        }
+        o[e] = v;
+      }
+      if constexpr (KR == 4) {
+        float* dst = a.dg + ((size_t)t * KR + q) * C + c;
+#pragma unroll
+        for (int e = 0; e < V; e += 4)
+          *reinterpret_cast<f32x4_t*>(dst + e) = f32x4_t{o[e], o[e + 1], o[e + 2], o[e + 3]};
+      } else {
+        st16(reinterpret_cast<T*>(a.d_out) + (size_t)t * C + c, E::pack(o));
+      }
+    }
+  }
+}
+
+struct BwdConvArgs {
+  const float* dg;
+  const void* out;
+  const float* conv_w;
+  void* d_out;
+  float* part;
+  int T, S, C, TC;
+};
+
+// MLP-type: d_out[t] = dg_0[t] + sum over kernels q and lags i of
+// w_q[i] dg_q[t + i] (same sequence), and the conv-weight gradient partials
+// sum_t dg_q[t] out[t - i] over this workgroup's token range.  One thread per
+// channel.
+template <class E>
+__global__ __launch_bounds__(BT) void bwd_conv_kernel(BwdConvArgs a) {
+  using T = typename E::T;
+  const int c = blockIdx.x * BT + threadIdx.x;
+  if (c >= a.C) return;
+  const int C = a.C;
+  const int t0 = blockIdx.y * a.TC;
+  const int t1 = t0 + a.TC < a.T ? t0 + a.TC : a.T;
+  const T* out = reinterpret_cast<const T*>(a.out);
+  T* d_out = reinterpret_cast<T*>(a.d_out);
+  float w[NCONV], acc[NCONV];
+#pragma unroll
+  for (int r = 0; r < NCONV; ++r) {
+    w[r] = a.conv_w[(size_t)r * C + c];
+    acc[r] = 0.f;
+  }
+  for (int t = t0; t < t1; ++t) {
+    const int s = t % a.S;
+    const float* dgt = a.dg + (size_t)t * 4 * C + c;
+    float d = dgt[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      const int off = q == 1 ? 0 : q == 2 ? 4 : 12;
+#pragma unroll
+      for (int i = 0; i < 4 * q; ++i)
+        if (s + i < a.S) d = fmaf(w[off + i], dgt[((size_t)i * 4 + q) * C], d);
+    }
+    st1(d_out + (size_t)t * C + c, d);
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      const int off = q == 1 ? 0 : q == 2 ? 4 : 12;
+      const float gq = dgt[(size_t)q * C];
+#pragma unroll
+      for (int i = 0; i < 4 * q; ++i)
+        if (i <= s) acc[off + i] = fmaf(gq, ld1(out + (size_t)(t - i) * C + c), acc[off + i]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NCONV; ++r) a.part[((size_t)blockIdx.y * NCONV + r) * C + c] = acc[r];
+}
+
+// out[i] = sum over nch partial arrays of part[ch][i], minus corr[i % ncol]
+// for the first ncorr columns.
+__global__ __launch_bounds__(BT) void bwd_reduce_kernel(const float* __restrict__ part, int nch, long n,
+                                                       float* __restrict__ out, const float* __restrict__ corr,
+                                                       int ncol, int ncorr) {
+  const long i = (long)blockIdx.x * BT + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int ch = 0; ch < nch; ++ch) s += part[(size_t)ch * n + i];
+  if (ncorr > 0) {
+    const int col = (int)(i % ncol);
+    if (col < ncorr) s -= corr[col];
+  }
+  out[i] = s;
+}
+
+// Column sums of W_full's router columns: colsum[n] = sum_row W[row][n].
+template <class E>
+__global__ __launch_bounds__(BT) void bwd_wcolsum_kernel(const typename E::T* __restrict__ W, long R, int ncol,
+                                                         float* __restrict__ colsum) {
+  __shared__ float s_tmp[BT / WAVE];
+  const int n = blockIdx.x;
+  float v = 0.f;
+  for (long r = threadIdx.x; r < R; r += BT) v += ld1(W + (size_t)r * ncol + n);
+  v = block_sum(v, s_tmp);
+  if (threadIdx.x == 0) colsum[n] = v;
+}
+
+// Column sums of the per-token rows [T][ncols]: column col of the bias / scale
+// block goes to its destination (d_b_pre, d_b_res, d_b_post, d_alpha; the
+// router correction sums stay in sums).
+struct BwdSumArgs {
+  const float* rows;
+  long T;
+  int ncols, N, KK, KKR;
+  float *d_b_pre, *d_b_res, *d_b_post, *d_alpha, *sums;
+};
+__global__ __launch_bounds__(BT) void bwd_sum_rows_kernel(BwdSumArgs a) {
+  __shared__ float s_tmp[BT / WAVE];
+  const int col = blockIdx.x;
+  float v = 0.f;
+  for (long t = threadIdx.x; t < a.T; t += BT) v += a.rows[(size_t)t * a.ncols + col];
+  v = block_sum(v, s_tmp);
+  if (threadIdx.x != 0) return;
+  a.sums[col] = v;
+  int c = col;
+  if (c < a.N) { a.d_b_pre[c] = v; return; }
+  c -= a.N;
+  if (c < a.KK) { a.d_b_res[c] = v; return; }
+  c -= a.KK;
+  if (c < a.KKR) { a.d_b_post[c] = v; return; }
+  c -= a.KKR;
+  if (c < 3) a.d_alpha[c] = v;
+}
+
+struct BwdTokArgs {
+  const float *part, *stats;      // full-state raw logits [KS][T][NP], sums [KS][T][2]
+  const float *part_a, *stats_a;  // active-row raw logits [KSa][T][NPA], sums [KSa][T][2]
+  int KS, NP, KSa, NPA;
+  const int* idx;
+  const float *p, *h_pre, *h_post, *z;
+  const float *d_hpre, *d_hres, *d_hpost, *d_p;
+  const float *b_res, *colsum;
+  float a_pre, a_res, a_post, eps;
+  int iters, m, T, C;
+  float *Gt, *Ga, *sc, *brow;
+};
+
+// Generation half, per-token scalars.  16 lanes per token: lane (a, b) < k^2
+// carries the tangent of the Sinkhorn map along its logit (a, b) and returns
+// that logit's gradient; lane 0 then forms the coefficient rows
+//   Gt = [dz / (sigma + eps) | alpha_pre g_pre / rho]   (router | pre-map),
+//   Ga = [alpha_res dL | alpha_post g_post] / rho_a      (active maps),
+// the per-token scalars cx, c0 (full state) and cxa (active rows) of the norm
+// backward, dx = W Gt + cx x + c0, dx_a = W_act Ga + cxa x_a, and its share
+// of the bias / scale gradients and of the router's mean correction.
+template <int N, int K, int KR>
+__global__ __launch_bounds__(BT) void bwd_token_kernel(BwdTokArgs a) {
+  constexpr int KK = K * K, NA = KK + K * KR, NBT = 2 * N + KK + K * KR + 3;
+  const int tl = threadIdx.x >> 4, l = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + tl;
+  const bool valid = t < a.T;
+  const int tt = valid ? t : 0;
+  __shared__ float s_la[16][32], s_dL[16][16];
+  const float KC = (float)K * (float)a.C;
+  float s2a = 0.f;
+  for (int ks = 0; ks < a.KSa; ++ks) s2a += a.stats_a[((size_t)ks * a.T + tt) * 2 + 1];
+  const float rhoa = sqrtf(s2a / KC + a.eps);
+  for (int col = l; col < NA; col += 16) {
+    float v = 0.f;
+    for (int ks = 0; ks < a.KSa; ++ks) v += a.part_a[((size_t)ks * a.T + tt) * a.NPA + col];
+    s_la[tl][col] = v / rhoa;
+  }
+  __syncthreads();
+  if (l < KK) {
+    const int ra = l / K, rb = l % K;
+    float M[K][K], dM[K][K], mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        M[i][j] = fmaf(a.a_res, s_la[tl][i * K + j], a.b_res[i * K + j]);
+        mx = fmaxf(mx, M[i][j]);
+      }
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        M[i][j] = expf(M[i][j] - mx);
+        dM[i][j] = (i == ra && j == rb) ? M[i][j] : 0.f;
+      }
+    for (int it = 0; it < a.iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        float cs = 0.f, dcs = 0.f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) { cs += M[i][j]; dcs += dM[i][j]; }
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const float mv = M[i][j] / cs;
+          dM[i][j] = (dM[i][j] - mv * dcs) / cs;
+          M[i][j] = mv;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        float rs = 0.f, drs = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) { rs += M[i][j]; drs += dM[i][j]; }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const float mv = M[i][j] / rs;
+          dM[i][j] = (dM[i][j] - mv * drs) / rs;
+          M[i][j] = mv;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float rs = 0.f, drs = 0.f;
+#pragma unroll
+      for (int j = 0; j < K; ++j) { rs += M[i][j]; drs += dM[i][j]; }
+      if (rs > 1.f) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const float mv = M[i][j] / rs;
+          dM[i][j] = (dM[i][j] - mv * drs) / rs;
+          M[i][j] = mv;
+        }
+      }
+    }
+    float dl = 0.f;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int j = 0; j < K; ++j) dl = fmaf(a.d_hres[(size_t)tt * KK + i * K + j], dM[i][j], dl);
+    s_dL[tl][l] = dl;
+  }
+  __syncthreads();
+  if (l != 0 || !valid) return;
+
+  const float NC = (float)N * (float)a.C;
+  float s1 = 0.f, s2 = 0.f;
+  for (int ks = 0; ks < a.KS; ++ks) {
+    s1 += a.stats[((size_t)ks * a.T + t) * 2];
+    s2 += a.stats[((size_t)ks * a.T + t) * 2 + 1];
+  }
+  const float mu = s1 / NC, ms = s2 / NC;
+  const float rho = sqrtf(ms + a.eps);
+  const float sig = sqrtf(fmaxf(ms - mu * mu, 0.f));
+  const float sh = sig + a.eps;
+  float* gt = a.Gt + (size_t)t * 2 * N;
+  float* br = a.brow + (size_t)t * NBT;
+  // pre-map: H_pre = sigmoid(alpha_pre y + b_pre), y = (x W_pre) / rho
+  float sdy = 0.f, apre = 0.f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float raw = 0.f;
+    for (int ks = 0; ks < a.KS; ++ks) raw += a.part[((size_t)ks * a.T + t) * a.NP + N + n];
+    const float y = raw / rho;
+    const float h = a.h_pre[(size_t)t * N + n];
+    const float gp = a.d_hpre[(size_t)t * N + n] * h * (1.f - h);
+    const float dy = a.a_pre * gp;
+    gt[N + n] = dy / rho;
+    sdy = fmaf(dy, y, sdy);
+    apre = fmaf(gp, y, apre);
+    br[n] = gp;
+  }
+  float cx = -sdy / (rho * rho * NC);
+  // router: p_i = sigmoid(z_{I_i}) for the routed positions i >= m
+  float dz[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) dz[n] = 0.f;
+  for (int i = a.m; i < K; ++i) {
+    const int n = a.idx[(size_t)t * K + i];
+    const float pv = a.p[(size_t)t * K + i];
+    const float g = a.d_p[(size_t)t * K + i] * pv * (1.f - pv);
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (q == n) dz[q] += g;
+  }
+  float sdz = 0.f, cs = 0.f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    sdz = fmaf(dz[n], a.z[(size_t)t * N + n], sdz);
+    const float gr = dz[n] / sh;
+    gt[n] = gr;
+    cs = fmaf(gr, a.colsum[n], cs);
+    br[NBT - N + n] = mu * gr;
+  }
+  const float cxr = sig > 0.f ? -sdz / (sh * NC * sig) : 0.f;
+  cx += cxr;
+  const float c0 = -cxr * mu - cs / NC;
+  // active maps: H_res = rowclamp(SK(alpha_res la_res + b_res)),
+  // H_post = 2 sigmoid(alpha_post la_post + b_post), la = (x_a W_act) / rho_a
+  float* ga = a.Ga + (size_t)t * NA;
+  float sdl = 0.f, ares = 0.f, apost = 0.f;
+#pragma unroll
+  for (int q = 0; q < KK; ++q) {
+    const float dL = s_dL[tl][q];
+    const float dla = a.a_res * dL;
+    ga[q] = dla / rhoa;
+    sdl = fmaf(dla, s_la[tl][q], sdl);
+    ares = fmaf(dL, s_la[tl][q], ares);
+    br[N + q] = dL;
+  }
+#pragma unroll
+  for (int q = 0; q < K * KR; ++q) {
+    const float sg = 0.5f * a.h_post[(size_t)t * K * KR + q];
+    const float gpo = a.d_hpost[(size_t)t * K * KR + q] * 2.f * sg * (1.f - sg);
+    const float dla = a.a_post * gpo;
+    ga[KK + q] = dla / rhoa;
+    sdl = fmaf(dla, s_la[tl][KK + q], sdl);
+    apost = fmaf(gpo, s_la[tl][KK + q], apost);
+    br[N + KK + q] = gpo;
+  }
+  br[N + NA] = apre;
+  br[N + NA + 1] = ares;
+  br[N + NA + 2] = apost;
+  const float cxa = -sdl / (rhoa * rhoa * KC);
+  a.sc[(size_t)t * 4 + 0] = cx;
+  a.sc[(size_t)t * 4 + 1] = c0;
+  a.sc[(size_t)t * 4 + 2] = cxa;
+  a.sc[(size_t)t * 4 + 3] = 0.f;
+}
+
+struct BwdRowArgs {
+  const void* X;      // rows source [T][R]: the state (full) or the gathered active rows
+  const void* W;      // [R][ncol] state dtype
+  const float* G;     // [T][ncol]
+  const float* sc;    // [T][4]
+  void* dX;           // [T][N][C], read-modify-write
+  const int* idx;     // active lists (act mode)
+  float* part;        // [nch][R][ncol]
+  long R;
+  int ncol, T, TW, N, K, C, act;
+};
+
+// dX += W G_t + c x (+ c0) row by row, and the weight-gradient partials
+// sum_t x_t[row] G_t over this workgroup's token range.  Each thread owns two
+// adjacent rows of the contraction (same stream, adjacent channels) with
+// their weights in registers; the coefficient rows of 64 tokens at a time
+// are staged in LDS.  Full mode: rows of the flattened state, c = cx, plus
+// c0.  Active mode: rows of the gathered active state, c = cxa, scattered to
+// stream I_t[j].
+template <class E, int CM>
+__global__ __launch_bounds__(BT) void bwd_rows_kernel(BwdRowArgs a) {
+  using T = typename E::T;
+  const long r0 = ((long)blockIdx.x * BT + threadIdx.x) * 2;
+  const bool own = r0 < a.R;
+  const int t0 = blockIdx.y * a.TW;
+  const int t1 = t0 + a.TW < a.T ? t0 + a.TW : a.T;
+  __shared__ float s_g[64][CM];
+  __shared__ float s_c[64][2];
+  const T* W = reinterpret_cast<const T*>(a.W);
+  const T* X = reinterpret_cast<const T*>(a.X);
+  T* dX = reinterpret_cast<T*>(a.dX);
+  float w0[CM], w1[CM], acc0[CM], acc1[CM];
+#pragma unroll
+  for (int q = 0; q < CM; ++q) {
+    w0[q] = (own && q < a.ncol) ? ld1(W + (size_t)r0 * a.ncol + q) : 0.f;
+    w1[q] = (own && q < a.ncol) ? ld1(W + (size_t)(r0 + 1) * a.ncol + q) : 0.f;
+    acc0[q] = acc1[q] = 0.f;
+  }
+  const int j = own ? (int)(r0 / a.C) : 0;
+  const int c = own ? (int)(r0 % a.C) : 0;
+  for (int tb = t0; tb < t1; tb += 64) {
+    const int nt = t1 - tb < 64 ? t1 - tb : 64;
+    __syncthreads();
+    for (int u = threadIdx.x; u < 64 * CM; u += BT) {
+      const int tu = u / CM, q = u % CM;
+      s_g[tu][q] = (tu < nt && q < a.ncol) ? a.G[(size_t)(tb + tu) * a.ncol + q] : 0.f;
+    }
+    if (threadIdx.x < 64) {
+      const int tu = threadIdx.x;
+      s_c[tu][0] = tu < nt ? a.sc[(size_t)(tb + tu) * 4 + (a.act ? 2 : 0)] : 0.f;
+      s_c[tu][1] = (tu < nt && !a.act) ? a.sc[(size_t)(tb + tu) * 4 + 1] : 0.f;
+    }
+    __syncthreads();
+    if (!own) continue;
+    for (int u = 0; u < nt; ++u) {
+      const int t = tb + u;
+      const T* xr = X + (size_t)t * a.R + r0;
+      const float x0 = ld1(xr), x1 = ld1(xr + 1);
+      float d0 = fmaf(s_c[u][0], x0, s_c[u][1]), d1 = fmaf(s_c[u][0], x1, s_c[u][1]);
+#pragma unroll
+      for (int q = 0; q < CM; ++q) {
+        const float g = s_g[u][q];
+        d0 = fmaf(g, w0[q], d0);
+        d1 = fmaf(g, w1[q], d1);
+        acc0[q] = fmaf(x0, g, acc0[q]);
+        acc1[q] = fmaf(x1, g, acc1[q]);
+      }
+      T* dr = a.act ? dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + j]) * a.C + c : dX + (size_t)t * a.R + r0;
+      st1(dr, ld1(dr) + d0);
+      st1(dr + 1, ld1(dr + 1) + d1);
+    }
+  }
+  if (!own) return;
+  float* pp = a.part + ((size_t)blockIdx.y * a.R + r0) * a.ncol;
+  for (int q = 0; q < a.ncol; ++q) {
+    pp[q] = acc0[q];
+    pp[a.ncol + q] = acc1[q];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int clampi(long v, int lo, int hi) { return (int)(v < lo ? lo : v > hi ? hi : v); }
+
+}  // namespace
+
+bool make_bwd_plan(const Plan& P, BwdPlan* B) {
+  BwdPlan q;
+  const size_t T = (size_t)P.T, N = P.N, K = P.K, C = P.C, KR = P.KR;
+  const size_t es = P.dtype == XHC_BF16 ? 2 : 4;
+  const int KB = P.dtype == XHC_BF16 ? 32 : 16;
+  q.NC = (long)N * (long)C;
+  q.KC = (long)K * (long)C;
+  q.ncol_f = 2 * P.N;
+  q.ncol_a = P.K * P.K + P.K * P.KR;
+  q.NTF = (q.ncol_f + 15) / 16;
+  q.NTA = (q.ncol_a + 15) / 16;
+  q.nkb_f = q.NC / KB;
+  q.nkb_a = q.KC / KB;
+  const long nblk_t = (P.T + 63) / 64;
+  const long ks = nblk_t > 0 ? (1024 + nblk_t - 1) / nblk_t : 1;
+  q.KS = clampi(ks, 1, 8);
+  if (q.KS > q.nkb_f) q.KS = (int)q.nkb_f;
+  q.KSa = clampi(ks, 1, 8);
+  if (q.KSa > q.nkb_a) q.KSa = (int)q.nkb_a;
+  q.NBT = 2 * P.N + P.K * P.K + P.K * P.KR + 3;
+  // token chunks of the row kernels: about 2048 workgroups, at least 64 tokens each
+  const long maxch = (P.T + 63) / 64 > 0 ? (P.T + 63) / 64 : 1;
+  const long xf = (q.NC / 2 + BT - 1) / BT, xa = (q.KC / 2 + BT - 1) / BT;
+  q.nch_f = clampi((2048 + xf - 1) / xf, 1, 64);
+  if (q.nch_f > maxch) q.nch_f = (int)maxch;
+  q.nch_a = clampi((2048 + xa - 1) / xa, 1, 64);
+  if (q.nch_a > maxch) q.nch_a = (int)maxch;
+  q.TW_f = (int)((P.T + q.nch_f - 1) / q.nch_f);
+  q.TW_a = (int)((P.T + q.nch_a - 1) / q.nch_a);
+  q.nch_c = clampi((P.T + 255) / 256, 1, 1 << 20);
+  q.TC = (int)((P.T + q.nch_c - 1) / q.nch_c);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = al256(off + bytes);
+    return o;
+  };
+  q.o_dhpre = take(T * N * 4);
+  q.o_dhres = take(T * K * K * 4);
+  q.o_dhpost = take(T * K * KR * 4);
+  q.o_dp = take(T * K * 4);
+  q.o_xa = take(T * K * C * es);
+  q.o_dg = KR == 4 ? take(T * 4 * C * 4) : SIZE_MAX;
+  q.o_cpart = KR == 4 ? take((size_t)q.nch_c * NCONV * C * 4) : SIZE_MAX;
+  q.o_wpf = take((size_t)q.nkb_f * q.NTF * 64 * 16);
+  q.o_wpa = take((size_t)q.nkb_a * q.NTA * 64 * 16);
+  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
+  q.o_stats = take((size_t)q.KS * T * 2 * 4);
+  q.o_parta = take((size_t)q.KSa * T * q.NTA * 16 * 4);
+  q.o_statsa = take((size_t)q.KSa * T * 2 * 4);
+  q.o_gt = take(T * q.ncol_f * 4);
+  q.o_ga = take(T * q.ncol_a * 4);
+  q.o_sc = take(T * 4 * 4);
+  q.o_brow = take(T * q.NBT * 4);
+  q.o_bsum = take((size_t)q.NBT * 4);
+  q.o_colsum = take(N * 4);
+  q.o_wpartf = take((size_t)q.nch_f * q.NC * q.ncol_f * 4);
+  q.o_wparta = take((size_t)q.nch_a * q.KC * q.ncol_a * 4);
+  q.total = T == 0 ? 0 : off;
+  *B = q;
+  return true;
+}
+
+namespace {
+
+template <class E, int N, int K, int KR>
+void apply_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, const void* out,
+                  const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws,
+                  char* bws, hipStream_t st) {
+  BwdApplyArgs a{};
+  a.X = X;
+  a.out = out;
+  a.d_inp = d_inp;
+  a.d_X = d_X;
+  a.dX = dX;
+  a.d_out = d_out;
+  a.xa = bws + Bp.o_xa;
+  a.dg = KR == 4 ? reinterpret_cast<float*>(bws + Bp.o_dg) : nullptr;
+  a.conv_w = w->conv_w;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.p = reinterpret_cast<const float*>(ws + P.o_p);
+  a.h_pre = reinterpret_cast<const float*>(ws + P.o_hpre);
+  a.h_res = reinterpret_cast<const float*>(ws + P.o_hres);
+  a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+  a.d_hpre = reinterpret_cast<float*>(bws + Bp.o_dhpre);
+  a.d_hres = reinterpret_cast<float*>(bws + Bp.o_dhres);
+  a.d_hpost = reinterpret_cast<float*>(bws + Bp.o_dhpost);
+  a.d_p = reinterpret_cast<float*>(bws + Bp.o_dp);
+  a.T = (int)P.T;
+  a.S = P.S;
+  a.C = P.C;
+  a.use_mgs = P.use_mgs;
+  a.eps_mgs = P.eps_mgs;
+  bwd_apply_kernel<E, N, K, KR><<<(unsigned)P.T, BT, 0, st>>>(a);
+  if constexpr (KR == 4) {
+    BwdConvArgs c{};
+    c.dg = a.dg;
+    c.out = out;
+    c.conv_w = w->conv_w;
+    c.d_out = d_out;
+    c.part = reinterpret_cast<float*>(bws + Bp.o_cpart);
+    c.T = (int)P.T;
+    c.S = P.S;
+    c.C = P.C;
+    c.TC = Bp.TC;
+    dim3 grid((P.C + BT - 1) / BT, Bp.nch_c);
+    bwd_conv_kernel<E><<<grid, BT, 0, st>>>(c);
+    const long n = (long)NCONV * P.C;
+    bwd_reduce_kernel<<<(unsigned)((n + BT - 1) / BT), BT, 0, st>>>(c.part, Bp.nch_c, n, d_conv, nullptr, 1, 0);
+  }
+}
+
+template <class E, int CM>
+void rows_launch(const BwdRowArgs& a, int nch, hipStream_t st) {
+  dim3 grid((unsigned)((a.R / 2 + BT - 1) / BT), nch);
+  bwd_rows_kernel<E, CM><<<grid, BT, 0, st>>>(a);
+}
+
+template <class E>
+void rows_dispatch(const BwdRowArgs& a, int nch, hipStream_t st) {
+  if (a.ncol <= 8) rows_launch<E, 8>(a, nch, st);
+  else if (a.ncol <= 16) rows_launch<E, 16>(a, nch, st);
+  else rows_launch<E, 32>(a, nch, st);
+}
+
+template <class E, int N, int K, int KR>
+void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
+                const char* ws, char* bws, hipStream_t st) {
+  const int dt = P.dtype;
+  const int T = (int)P.T;
+  float* part = reinterpret_cast<float*>(bws + Bp.o_part);
+  float* stats = reinterpret_cast<float*>(bws + Bp.o_stats);
+  float* parta = reinterpret_cast<float*>(bws + Bp.o_parta);
+  float* statsa = reinterpret_cast<float*>(bws + Bp.o_statsa);
+  const void* xa = bws + Bp.o_xa;
+  launch_pack_b(dt, w->w_full, Bp.nkb_f, Bp.ncol_f, Bp.NTF, bws + Bp.o_wpf, st);
+  launch_pack_b(dt, w->w_act, Bp.nkb_a, Bp.ncol_a, Bp.NTA, bws + Bp.o_wpa, st);
+  launch_projection(dt, Bp.NTF, X, T, Bp.NC, bws + Bp.o_wpf, Bp.nkb_f, Bp.KS, part, stats, st);
+  launch_projection(dt, Bp.NTA, xa, T, Bp.KC, bws + Bp.o_wpa, Bp.nkb_a, Bp.KSa, parta, statsa, st);
+  float* colsum = reinterpret_cast<float*>(bws + Bp.o_colsum);
+  bwd_wcolsum_kernel<E><<<N, BT, 0, st>>>(reinterpret_cast<const typename E::T*>(w->w_full), Bp.NC, Bp.ncol_f,
+                                          colsum);
+  BwdTokArgs a{};
+  a.part = part;
+  a.stats = stats;
+  a.part_a = parta;
+  a.stats_a = statsa;
+  a.KS = Bp.KS;
+  a.NP = Bp.NTF * 16;
+  a.KSa = Bp.KSa;
+  a.NPA = Bp.NTA * 16;
+  a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+  a.p = reinterpret_cast<const float*>(ws + P.o_p);
+  a.h_pre = reinterpret_cast<const float*>(ws + P.o_hpre);
+  a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+  a.z = reinterpret_cast<const float*>(ws + P.o_z);
+  a.d_hpre = reinterpret_cast<const float*>(bws + Bp.o_dhpre);
+  a.d_hres = reinterpret_cast<const float*>(bws + Bp.o_dhres);
+  a.d_hpost = reinterpret_cast<const float*>(bws + Bp.o_dhpost);
+  a.d_p = reinterpret_cast<const float*>(bws + Bp.o_dp);
+  a.b_res = w->b_res;
+  a.colsum = colsum;
+  a.a_pre = w->alpha_pre;
+  a.a_res = w->alpha_res;
+  a.a_post = w->alpha_post;
+  a.eps = P.eps_norm;
+  a.iters = P.iters;
+  a.m = P.m;
+  a.T = T;
+  a.C = P.C;
+  a.Gt = reinterpret_cast<float*>(bws + Bp.o_gt);
+  a.Ga = reinterpret_cast<float*>(bws + Bp.o_ga);
+  a.sc = reinterpret_cast<float*>(bws + Bp.o_sc);
+  a.brow = reinterpret_cast<float*>(bws + Bp.o_brow);
+  bwd_token_kernel<N, K, KR><<<(T + 15) / 16, BT, 0, st>>>(a);
+  BwdSumArgs s{};
+  s.rows = a.brow;
+  s.T = T;
+  s.ncols = Bp.NBT;
+  s.N = N;
+  s.KK = K * K;
+  s.KKR = K * KR;
+  s.d_b_pre = g->d_b_pre;
+  s.d_b_res = g->d_b_res;
+  s.d_b_post = g->d_b_post;
+  s.d_alpha = g->d_alpha;
+  s.sums = reinterpret_cast<float*>(bws + Bp.o_bsum);
+  bwd_sum_rows_kernel<<<Bp.NBT, BT, 0, st>>>(s);
+  // full state
+  BwdRowArgs r{};
+  r.X = X;
+  r.W = w->w_full;
+  r.G = a.Gt;
+  r.sc = a.sc;
+  r.dX = dX;
+  r.idx = a.idx;
+  r.part = reinterpret_cast<float*>(bws + Bp.o_wpartf);
+  r.R = Bp.NC;
+  r.ncol = Bp.ncol_f;
+  r.T = T;
+  r.TW = Bp.TW_f;
+  r.N = N;
+  r.K = K;
+  r.C = P.C;
+  r.act = 0;
+  rows_dispatch<E>(r, Bp.nch_f, st);
+  const long nf = Bp.NC * Bp.ncol_f;
+  bwd_reduce_kernel<<<(unsigned)((nf + BT - 1) / BT), BT, 0, st>>>(r.part, Bp.nch_f, nf, g->dW_full,
+                                                                   s.sums + Bp.NBT - N, Bp.ncol_f, N);
+  // active rows
+  BwdRowArgs ra = r;
+  ra.X = xa;
+  ra.W = w->w_act;
+  ra.G = a.Ga;
+  ra.part = reinterpret_cast<float*>(bws + Bp.o_wparta);
+  ra.R = Bp.KC;
+  ra.ncol = Bp.ncol_a;
+  ra.TW = Bp.TW_a;
+  ra.act = 1;
+  rows_dispatch<E>(ra, Bp.nch_a, st);
+  const long na = Bp.KC * Bp.ncol_a;
+  bwd_reduce_kernel<<<(unsigned)((na + BT - 1) / BT), BT, 0, st>>>(ra.part, Bp.nch_a, na, g->dW_act, nullptr, 1, 0);
+}
+
+template <class E, int KR>
+bool apply_shape(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, const void* out,
+                 const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws, char* bws,
+                 hipStream_t st) {
+#define XHC_BWD_APPLY(n, k) \
+  if (P.N == n && P.K == k) { \
+    apply_launch<E, n, k, KR>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st); \
+    return true; \
+  }
+  XHC_BWD_APPLY(16, 4)
+  XHC_BWD_APPLY(16, 2)
+  XHC_BWD_APPLY(8, 4)
+  XHC_BWD_APPLY(4, 4)
+  XHC_BWD_APPLY(1, 1)
+#undef XHC_BWD_APPLY
+  return false;
+}
+
+template <class E, int KR>
+bool gen_shape(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
+               const char* ws, char* bws, hipStream_t st) {
+#define XHC_BWD_GEN(n, k) \
+  if (P.N == n && P.K == k) { \
+    gen_launch<E, n, k, KR>(P, Bp, w, X, dX, g, ws, bws, st); \
+    return true; \
+  }
+  XHC_BWD_GEN(16, 4)
+  XHC_BWD_GEN(16, 2)
+  XHC_BWD_GEN(8, 4)
+  XHC_BWD_GEN(4, 4)
+  XHC_BWD_GEN(1, 1)
+#undef XHC_BWD_GEN
+  return false;
+}
+
+}  // namespace
+
+bool launch_xhc_post_backward(const Plan& P, const xhc_weights* w, const void* X, const void* out, const void* d_inp,
+                              const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws, char* bws,
+                              hipStream_t st) {
+  BwdPlan Bp;
+  make_bwd_plan(P, &Bp);
+  if (P.dtype == XHC_BF16)
+    return P.KR == 4 ? apply_shape<Bf16, 4>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st)
+                     : apply_shape<Bf16, 1>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st);
+  return P.KR == 4 ? apply_shape<F32, 4>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st)
+                   : apply_shape<F32, 1>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st);
+}
+
+bool launch_xhc_pre_backward(const Plan& P, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
+                             const char* ws, char* bws, hipStream_t st) {
+  BwdPlan Bp;
+  make_bwd_plan(P, &Bp);
+  if (P.dtype == XHC_BF16)
+    return P.KR == 4 ? gen_shape<Bf16, 4>(P, Bp, w, X, dX, g, ws, bws, st)
+                     : gen_shape<Bf16, 1>(P, Bp, w, X, dX, g, ws, bws, st);
+  return P.KR == 4 ? gen_shape<F32, 4>(P, Bp, w, X, dX, g, ws, bws, st)
+                   : gen_shape<F32, 1>(P, Bp, w, X, dX, g, ws, bws, st);
+}
+
+}  // namespace xhc

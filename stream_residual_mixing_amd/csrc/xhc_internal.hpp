@@ -100,6 +100,22 @@ struct MhcPostArgs {
   const float *h_res, *h_post;
 };
 
+// Backward workspace layout (xhc_backward.hip).
+struct BwdPlan {
+  long NC = 0, KC = 0, nkb_f = 0, nkb_a = 0;
+  int ncol_f = 0, ncol_a = 0, NTF = 0, NTA = 0, KS = 1, KSa = 1, NBT = 0;
+  int nch_f = 1, nch_a = 1, TW_f = 0, TW_a = 0, nch_c = 1, TC = 0;
+  size_t o_dhpre = 0, o_dhres = 0, o_dhpost = 0, o_dp = 0, o_xa = 0, o_dg = SIZE_MAX, o_cpart = SIZE_MAX,
+         o_wpf = 0, o_wpa = 0, o_part = 0, o_stats = 0, o_parta = 0, o_statsa = 0, o_gt = 0, o_ga = 0, o_sc = 0,
+         o_brow = 0, o_bsum = 0, o_colsum = 0, o_wpartf = 0, o_wparta = 0, total = 0;
+};
+bool make_bwd_plan(const Plan& P, BwdPlan* B);
+bool launch_xhc_post_backward(const Plan& P, const xhc_weights* w, const void* X, const void* out, const void* d_inp,
+                              const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws, char* bws,
+                              hipStream_t st);
+bool launch_xhc_pre_backward(const Plan& P, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
+                             const char* ws, char* bws, hipStream_t st);
+
 // Set by a launcher that fails for a reason other than an unsupported shape
 // (e.g. the library GEMM); the host layer reports it as XHC_ERR_HIP.
 extern thread_local const char* g_launch_failure;

@@ -1,0 +1,166 @@
+"""GPU parity of the xHC sublayer backward (xhc_post_backward, then
+xhc_pre_backward) against the float64 gradient oracle (oracle/hc_grad.py).
+
+Each case runs xhc_pre on the GPU to leave the maps in the workspace, then
+both backward calls, and compares element by element with the oracle's two
+halves on the same inputs: the maps' gradients (application half), the state
+gradient (sum of the halves), d_out and the conv-kernel gradients
+(application half), and every weight, bias and scale gradient (generation
+half, fed with the oracle's own map gradients).
+
+Tolerance: bf16 cases store dX and d_out in bf16 (relative rounding 2^-9) and
+read bf16 inputs, so they take the forward's bf16 bound; the state gradient
+is stored three times on its way (application half, then the generation
+half's full-state and active-row passes), and where those parts cancel each
+store's rounding is allowed for, one ulp of the value it held.  Float cases
+accumulate in float over up to N*C products per token and T tokens per weight
+gradient and run the Sinkhorn tangent through 20 normalisation rounds in
+float, which the 1e-3 bound covers with margin (the errors printed are about
+1e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import cases as K
+from oracle import hc_grad as G
+from oracle import hc_oracle as O
+from stream_residual_mixing_amd import synth
+from stream_residual_mixing_amd.binding import Config, weights_to_device
+
+pytestmark = pytest.mark.gpu
+
+GTOL = {"bf16": 2e-2, "f32": 1e-3}
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def run_backward(lib, cfg, X, out, wd, d_inp, d_X):
+    w = weights_to_device(wd)
+    Xd, outd = X.cuda(), out.reshape(cfg.T, cfg.C).cuda()
+    inp = torch.empty((cfg.T, cfg.C), dtype=cfg.torch_dtype, device="cuda")
+    ws = lib.workspace(cfg)
+    lib.xhc_pre(cfg, w, Xd, inp, ws)
+    maps = {k: v.clone() for k, v in lib.ws_arrays(cfg, ws).items()}
+    bws = lib.backward_workspace(cfg)
+    dX = torch.empty_like(Xd)
+    d_out = torch.empty_like(outd)
+    d_conv = torch.empty((24, cfg.C), dtype=torch.float32, device="cuda") if cfg.K_r == 4 else None
+    lib.xhc_post_backward(cfg, w, Xd, outd, d_inp.cuda(), d_X.cuda(), dX, d_out, d_conv, ws, bws)
+    dmaps = {k: v.clone() for k, v in lib.backward_ws_arrays(cfg, bws).items()}
+    g = lib.grads(cfg)
+    lib.xhc_pre_backward(cfg, w, Xd, dX, g, ws, bws)
+    torch.cuda.synchronize()
+    res = dict(X=dX.cpu(), out=d_out.cpu(), **{"d_" + k: v.cpu() for k, v in dmaps.items()},
+               **{k: v.cpu() for k, v in g.items()}, I=maps["idx"].cpu().numpy())
+    if d_conv is not None:
+        res["convs"] = d_conv.cpu()
+    return res
+
+
+def oracle_backward(cfg, X, out, ow, d_inp, d_X):
+    X64, out64 = K.f64(X), K.f64(out).reshape(cfg.B, cfg.S, cfg.C)
+    alpha = (ow["alpha_pre"], ow["alpha_res"], ow["alpha_post"])
+    pre = O.xhc_pre(X64, ow["w_full"], ow["w_act"], cfg.m, cfg.k, cfg.K_r, alpha, ow["b_pre"], ow["b_res"],
+                    ow["b_post"], iters=cfg.iters)
+    ga = G.xhc_apply_grads(X64, out64, pre["I"], pre["p"], pre["h_pre"], pre["h_res"], pre["h_post"], ow["conv"],
+                           K.f64(d_inp), K.f64(d_X), bool(cfg.use_mgs))
+    gg = G.xhc_gen_grads(X64, ow["w_full"], ow["w_act"], cfg.m, cfg.k, cfg.K_r, alpha, ow["b_pre"], ow["b_res"],
+                         ow["b_post"], pre["I"], ga["h_pre"], ga["h_res"], ga["h_post"], ga["p"], iters=cfg.iters)
+    return pre, ga, gg
+
+
+def dx_err(cfg, dX, ga, gg):
+    """The state gradient is stored three times in the state dtype: by the
+    application half, after the full-state pass and after the active-row
+    pass of the generation half.  Each store may round by one ulp of the
+    value it holds, which the error is allowed on top of the usual bound."""
+    part1 = ga["X"]
+    part2 = part1 + gg["X_full"]
+    final = part2 + gg["X_act"]
+    allow = sum(K.ulp(np.abs(v), cfg.dtype) for v in (part1, part2, final))
+    return K.err_with_allowance(K.f64(dX), final, allow)
+
+
+def compare(cfg, g, pre, ga, gg):
+    errs = {
+        "I": 0.0 if np.array_equal(g["I"], pre["I"]) else 1.0,
+        "d_h_pre": K.rel_err(K.f64(g["d_h_pre"]), ga["h_pre"]),
+        "d_h_res": K.rel_err(K.f64(g["d_h_res"]), ga["h_res"]),
+        "d_h_post": K.rel_err(K.f64(g["d_h_post"]), ga["h_post"]),
+        "d_p": K.rel_err(K.f64(g["d_p"]), ga["p"]),
+        "dX": dx_err(cfg, g["X"], ga, gg),
+        "d_out": K.rel_err(K.f64(g["out"]), ga["out"].reshape(cfg.T, cfg.C)),
+        "dW_full": K.rel_err(K.f64(g["W_full"]), gg["W_full"]),
+        "dW_act": K.rel_err(K.f64(g["W_act"]), gg["W_act"]),
+        "d_b_pre": K.rel_err(K.f64(g["b_pre"]), gg["b_pre"]),
+        "d_b_res": K.rel_err(K.f64(g["b_res"]), gg["b_res"]),
+        "d_b_post": K.rel_err(K.f64(g["b_post"]), gg["b_post"]),
+        "d_alpha": K.rel_err(K.f64(g["alpha"]), gg["alpha"]),
+    }
+    if "convs" in g:
+        errs["d_conv"] = K.rel_err(K.f64(g["convs"]), np.concatenate(ga["convs"], axis=0))
+    return errs
+
+
+CASES = [
+    # N, k, m, C, B, S, n_convs, use_mgs, dtype
+    (16, 4, 2, 256, 2, 24, 3, 1, "bf16"),
+    (16, 4, 2, 256, 2, 24, 3, 1, "f32"),
+    (16, 4, 2, 128, 1, 30, 3, 0, "f32"),
+    (16, 4, 2, 256, 2, 19, 0, 1, "bf16"),
+    (16, 4, 2, 96, 2, 17, 0, 1, "f32"),
+    (16, 2, 1, 128, 2, 16, 3, 1, "f32"),
+    (8, 4, 1, 160, 1, 33, 3, 1, "f32"),
+    (4, 4, 4, 64, 2, 14, 3, 1, "f32"),
+    (1, 1, 1, 64, 2, 13, 3, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,k,m,C,B,S,nconv,mgs,dt", CASES)
+def test_backward_matches_gradient_oracle(lib, N, k, m, C, B, S, nconv, mgs, dt):
+    cfg = Config(N=N, k=k, m=m, C=C, B=B, S=S, n_convs=nconv, use_mgs=mgs, dtype=dt)
+    _print("backward", dict(N=N, k=k, m=m, C=C, B=B, S=S, n_convs=nconv, use_mgs=mgs, dtype=dt))
+    X, out, wd, ow = K.xhc_inputs(cfg, seed=61)
+    r = np.random.default_rng([61, 5])
+    d_inp = synth._round(r.standard_normal((cfg.T, C)), dt)
+    d_X = synth._round(r.standard_normal((cfg.T, N, C)), dt)
+    g = run_backward(lib, cfg, X, out, wd, d_inp, d_X)
+    pre, ga, gg = oracle_backward(cfg, X, out, ow, d_inp, d_X)
+    errs = compare(cfg, g, pre, ga, gg)
+    _print("  errors", {key: f"{v:.2e}" for key, v in errs.items()})
+    assert errs.pop("I") == 0.0, "active indices differ"
+    bad = {key: v for key, v in errs.items() if not v <= GTOL[dt]}
+    assert not bad, bad
+
+
+def test_backward_in_place_gradient(lib):
+    """dX may be the d_X buffer itself: same result as a separate buffer."""
+    cfg = Config(N=16, k=4, m=2, C=128, B=1, S=20, n_convs=3, dtype="bf16")
+    X, out, wd, ow = K.xhc_inputs(cfg, seed=62)
+    r = np.random.default_rng([62, 5])
+    d_inp = synth._round(r.standard_normal((cfg.T, cfg.C)), "bf16").cuda()
+    d_X = synth._round(r.standard_normal((cfg.T, cfg.N, cfg.C)), "bf16").cuda()
+    w = weights_to_device(wd)
+    Xd, outd = X.cuda(), out.reshape(cfg.T, cfg.C).cuda()
+    inp = torch.empty((cfg.T, cfg.C), dtype=torch.bfloat16, device="cuda")
+    ws = lib.workspace(cfg)
+    lib.xhc_pre(cfg, w, Xd, inp, ws)
+    bws = lib.backward_workspace(cfg)
+    d_conv = torch.empty((24, cfg.C), dtype=torch.float32, device="cuda")
+    res = []
+    for in_place in (False, True):
+        dX = d_X.clone() if in_place else torch.empty_like(d_X)
+        src = dX if in_place else d_X
+        d_out = torch.empty_like(outd)
+        lib.xhc_post_backward(cfg, w, Xd, outd, d_inp, src, dX, d_out, d_conv, ws, bws)
+        g = lib.grads(cfg)
+        lib.xhc_pre_backward(cfg, w, Xd, dX, g, ws, bws)
+        torch.cuda.synchronize()
+        res.append((dX.cpu(), d_out.cpu(), d_conv.cpu(), {k: v.cpu() for k, v in g.items()}))
+    for a, b in zip(res[0][:3], res[1][:3]):
+        assert torch.equal(a, b)
+    for name in res[0][3]:
+        assert torch.equal(res[0][3][name], res[1][3][name]), name

@@ -208,6 +208,10 @@ def test_halves_add_up_to_the_whole_sublayer(mlp):
     gg = G.xhc_gen_grads(d["X"], d["W_full"], d["W_act"], m, k, K_r, tuple(d["alpha"]), d["b_pre"], d["b_res"],
                          d["b_post"], pre["I"], ga["h_pre"], ga["h_res"], ga["h_post"], ga["p"])
     np.testing.assert_allclose(ga["X"] + gg["X"], whole["X"], rtol=1e-10, atol=1e-12)
+    # the active-row path touches only the active rows
+    inactive = np.ones((T, N), dtype=bool)
+    np.put_along_axis(inactive, pre["I"], False, axis=1)
+    assert np.all(gg["X_act"][inactive] == 0.0)
     np.testing.assert_allclose(ga["out"], whole["out"], rtol=1e-10, atol=1e-12)
     for a, b in zip(ga["convs"], whole["convs"]):
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
