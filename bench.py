@@ -53,10 +53,14 @@ WORKLOADS = {
     "xhcf4_chain_n16k4_c4096": ("xhcf4", 16, 4, 2, 4096, 2, 8192, "AMAMAMAM"),
     # single-token decode: 256 sequences, one new token each, 8 sublayers
     "xhc_decode_n16k4_c4096": ("xhcd", 16, 4, 2, 4096, 256, 1, "AMAMAMAM"),
+    # backward of an MLP-type and an attention-type sublayer (the gradients of
+    # xhc_pre + xhc_post), the state gradient carried from the one to the other
+    "xhc_bwd_n16k4_c4096": ("xhcb", 16, 4, 2, 4096, 2, 8192, "AM"),
 }
 DEFAULT = "xhc_chain_n16k4_c4096"
 SEED = {"xhc_chain_n16k4_c4096": 3, "xhc_mlp_n16k4_c2048": 2, "mhc_n4_c4096": 1, "mhc_n16_c4096": 4,
-        "xhcf_chain_n16k4_c4096": 3, "xhc_decode_n16k4_c4096": 5, "xhcf4_chain_n16k4_c4096": 3}
+        "xhcf_chain_n16k4_c4096": 3, "xhc_decode_n16k4_c4096": 5, "xhcf4_chain_n16k4_c4096": 3,
+        "xhc_bwd_n16k4_c4096": 6}
 
 
 def log(*a):
@@ -99,10 +103,24 @@ def flash4_bytes_per_token(cfg, esz=2):
     return (2 * N + 4) * C * esz, mid, mid, mid, (1 + 2 * k) * C * esz
 
 
+def bwd_bytes_per_token(cfg, esz=2):
+    """Algorithmic bytes per token of the backward's two calls.  Application
+    half: read the state (N rows, for the H_pre gradient and the mix), the
+    new state's gradient (N), d_inp and out; write the state gradient (N)
+    and d_out: 3N + 3.  Generation half: read the state once (the norms and
+    projections) and update the state gradient in place: 3N.  Intermediates
+    (the gathered active rows, the basis gradient, the partial weight
+    gradients) are not counted."""
+    N, C = cfg.N, cfg.C
+    return (3 * N + 3) * C * esz, 3 * N * C * esz
+
+
 def bytes_per_token(kind, cfg, esz=2):
     """Algorithmic bytes per token of (pre, post).  Decode: the MLP-type
     write also reads the 11 earlier outputs from the ring and stores the new
-    one (11 + 1 more)."""
+    one (11 + 1 more).  Backward: (application half, generation half)."""
+    if kind == "xhcb":
+        return bwd_bytes_per_token(cfg, esz)
     if kind == "xhcd":
         extra = 12 if cfg.K_r == 4 else 0
         return (cfg.N + 1) * cfg.C * esz, (1 + 2 * cfg.k + extra) * cfg.C * esz
@@ -117,6 +135,8 @@ def bytes_per_token(kind, cfg, esz=2):
 
 
 def flops_per_token(kind, cfg):
+    if kind == "xhcb":   # the projections recomputed, and their transposes for dX and dW
+        return 3 * (2 * cfg.N * cfg.C * 2 * cfg.N + 2 * cfg.k * cfg.C * (cfg.k * cfg.k + cfg.k * cfg.K_r))
     if kind == "xhcf4":   # per sublayer: a quarter of a group's projections
         N, k, C, KR = cfg.N, cfg.k, cfg.C, 4
         return (2 * N * C * 5 * N + 2 * k * C * (k + k * KR + k + k * k + k * KR)) // 4
@@ -170,6 +190,8 @@ def default_api(name):
         return "decode"
     if kind == "xhcf4":
         return "flash4"
+    if kind == "xhcb":
+        return "backward"
     return "chained" if kind == "xhc" and len(kinds) > 1 else "single"
 
 
@@ -209,6 +231,29 @@ def run_gpu(name, steps, warmup, api):
             for q in range(1, 5):
                 calls.append((f"xhcf4_post{q}", fb[q], lambda w=w, g=g, q=q: lib.xhcf4_post(
                     fcfg, w, q, X, outs[4 * g + q - 1], bases, inp, ws, stream)))
+    elif kind == "xhcb":
+        # the maps of each layer, left by xhc_pre, stay in that layer's workspace
+        wss = [lib.workspace(cfg) for cfg in cfgs]
+        for l, cfg in enumerate(cfgs):
+            lib.xhc_pre(cfg, weights[l], X, inp, wss[l], stream)
+        bws = lib.backward_workspace(max(cfgs, key=lib.backward_workspace_bytes))
+        g0 = torch.empty_like(X).normal_()
+        gbuf = [torch.empty_like(X), torch.empty_like(X)]
+        d_inp = torch.empty_like(inp).normal_()
+        d_out = torch.empty_like(inp)
+        d_conv = torch.empty((24, c0.C), dtype=torch.float32, device="cuda")
+        grads = [lib.grads(cfg) for cfg in cfgs]
+        src = g0
+        for j, l in enumerate(reversed(range(len(cfgs)))):
+            cfg, lk = cfgs[l], kinds[l]
+            dst = gbuf[j % 2]
+            bp, bq = bytes_per_token(kind, cfg)
+            calls.append((f"xhc_post_backward_{lk}", bp, lambda cfg=cfg, l=l, s_=src, d_=dst: lib.xhc_post_backward(
+                cfg, weights[l], X, outs[l].reshape(cfg.T, cfg.C), d_inp, s_, d_, d_out,
+                d_conv if cfg.K_r == 4 else None, wss[l], bws, stream)))
+            calls.append((f"xhc_pre_backward_{lk}", bq, lambda cfg=cfg, l=l, d_=dst: lib.xhc_pre_backward(
+                cfg, weights[l], X, d_, grads[l], wss[l], bws, stream)))
+            src = dst
     elif kind == "xhcd":
         ws = lib.workspace(big)
         ring = torch.zeros((c0.B, 12, c0.C), dtype=torch.bfloat16, device="cuda")
@@ -321,7 +366,22 @@ def cpu_baseline(name, tokens=256):
             total_t += dt
             total_tok += 2 * tokens
             break
-        if kind == "mhc":
+        if kind == "xhcb":
+            from oracle import hc_grad as G
+            from oracle import hc_oracle as O
+            ow = K.oracle_weights(synth.xhc_layer_weights(seed, l, cfg.N, cfg.k, cfg.C, cfg.K_r, "bf16"))
+            r = np.random.default_rng([seed, 99, l])
+            d_inp, d_X = r.standard_normal((tokens, cfg.C)), r.standard_normal((tokens, cfg.N, cfg.C))
+            alpha = (ow["alpha_pre"], ow["alpha_res"], ow["alpha_post"])
+            t = time.perf_counter()
+            pre = O.xhc_pre(X, ow["w_full"], ow["w_act"], cfg.m, cfg.k, cfg.K_r, alpha, ow["b_pre"], ow["b_res"],
+                            ow["b_post"], iters=cfg.iters)
+            ga = G.xhc_apply_grads(X, out, pre["I"], pre["p"], pre["h_pre"], pre["h_res"], pre["h_post"],
+                                   ow["conv"], d_inp, d_X)
+            G.xhc_gen_grads(X, ow["w_full"], ow["w_act"], cfg.m, cfg.k, cfg.K_r, alpha, ow["b_pre"], ow["b_res"],
+                            ow["b_post"], pre["I"], ga["h_pre"], ga["h_res"], ga["h_post"], ga["p"],
+                            iters=cfg.iters)
+        elif kind == "mhc":
             ow = K.oracle_weights(synth.mhc_layer_weights(seed, l, cfg.N, cfg.C, "bf16"))
             t = time.perf_counter()
             K.oracle_mhc(sub, X, out, ow)
@@ -334,6 +394,8 @@ def cpu_baseline(name, tokens=256):
         total_t += dt
         total_tok += tokens
     kinds_s = "+".join({"A": "attention", "M": "MLP", "D": "dense"}[k] for k in done)
+    if kind == "xhcb":
+        kinds_s += " backward (maps, both gradient halves; PyTorch CPU autograd in float64)"
     if kind == "xhcf":
         kinds_s = "xHC-Flash block (attention + MLP)"
     if kind == "xhcf4":
@@ -468,7 +530,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
     ap.add_argument("--traffic-summary", metavar="PMCDIR", default=None,
                     help="write profiles/<workload>_traffic.json from rocprofv3 counter runs and exit")
-    ap.add_argument("--api", choices=("chained", "single", "flash", "flash4", "decode"), default=None,
+    ap.add_argument("--api", choices=("chained", "single", "flash", "flash4", "decode", "backward"), default=None,
                     help="xHC calls: chained (routing of layer l+1 prepared during layer l; default for "
                          "multi-layer workloads) or single (xhc_pre / xhc_post per layer)")
     args = ap.parse_args()
@@ -527,7 +589,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "kind": kind, "api": api, "N": c0.N,
-                   "k": c0.k if kind in ("xhc", "xhcf", "xhcf4", "xhcd") else c0.N,
+                   "k": c0.k if kind in ("xhc", "xhcf", "xhcf4", "xhcd", "xhcb") else c0.N,
                    "m": c0.m, "C": c0.C, "batch": c0.B, "seq": c0.S, "tokens": T, "layers": kinds,
                    "sinkhorn_iters": c0.iters},
         "hbm": {"GBps": round(hbm_gbps, 1), "frac_of_peak": round(hbm_gbps / HBM_PEAK_GBPS, 4),

@@ -262,7 +262,12 @@ __global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
   }
   __syncthreads();
 
-  if (tid == 0) {
+  // scalar stage on wave 0: lane l < NG differentiates the Gram-Schmidt
+  // coefficients along the l-th symmetric Gram direction; lane 0 also forms
+  // the H_post / p gradients and the basis-gradient combination.
+  __shared__ float s_F[NG];
+  const bool mgs = KR > 1 && a.use_mgs;
+  if (tid < WAVE) {
     float Gm[KR][KR], Ec[K][KR], A[KR][KR], D[KR][KR], gam[KR][K], hp[K][KR], pp[K];
     int gi = 0;
 #pragma unroll
@@ -290,52 +295,58 @@ __global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
 #pragma unroll
         for (int i = 0; i < K; ++i) d = fmaf(gam[r][i], Ec[i][q], d);
         D[r][q] = d;
-        s_be[r][q] = 0.f;
       }
-    const bool mgs = KR > 1 && a.use_mgs;
-    if (mgs) {
-      mgs_coef<KR>(Gm, a.eps_mgs, A, -1, -1, D);
-#pragma unroll
-      for (int qa = 0; qa < KR; ++qa)
-#pragma unroll
-        for (int qb = qa; qb < KR; ++qb) {
-          float Ad[KR][KR];
-          const float f = mgs_coef<KR>(Gm, a.eps_mgs, Ad, qa, qb, D);
-          if (qa == qb) {
-            s_be[qa][qa] += 2.f * f;
-          } else {
-            s_be[qa][qb] += f;
-            s_be[qb][qa] += f;
-          }
-        }
-    } else {
-#pragma unroll
-      for (int r = 0; r < KR; ++r)
-#pragma unroll
-        for (int q = 0; q < KR; ++q) A[r][q] = r == q ? 1.f : 0.f;
+    if (mgs && tid < NG) {
+      int qa = 0, qb = 0, l = 0;
+      for (int x = 0; x < KR; ++x)
+        for (int y = x; y < KR; ++y, ++l)
+          if (l == tid) { qa = x; qb = y; }
+      float Ad[KR][KR];
+      s_F[tid] = mgs_coef<KR>(Gm, a.eps_mgs, Ad, qa, qb, D);
     }
+    if (tid == 0) {
+      if (mgs) {
+        mgs_coef<KR>(Gm, a.eps_mgs, A, -1, -1, D);
+      } else {
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      float dpv = 0.f;
+        for (int r = 0; r < KR; ++r)
 #pragma unroll
-      for (int r = 0; r < KR; ++r) {
-        float dq = 0.f;
-#pragma unroll
-        for (int q = 0; q < KR; ++q) dq = fmaf(A[r][q], Ec[i][q], dq);
-        a.d_hpost[((size_t)t * K + i) * KR + r] = pp[i] * dq;
-        dpv = fmaf(hp[i][r], dq, dpv);
+          for (int q = 0; q < KR; ++q) A[r][q] = r == q ? 1.f : 0.f;
       }
-      a.d_p[(size_t)t * K + i] = dpv;
-    }
-#pragma unroll
-    for (int q = 0; q < KR; ++q)
 #pragma unroll
       for (int i = 0; i < K; ++i) {
-        float al = 0.f;
+        float dpv = 0.f;
 #pragma unroll
-        for (int r = 0; r < KR; ++r) al = fmaf(A[r][q], gam[r][i], al);
-        s_al[q][i] = al;
+        for (int r = 0; r < KR; ++r) {
+          float dq = 0.f;
+#pragma unroll
+          for (int q = 0; q < KR; ++q) dq = fmaf(A[r][q], Ec[i][q], dq);
+          a.d_hpost[((size_t)t * K + i) * KR + r] = pp[i] * dq;
+          dpv = fmaf(hp[i][r], dq, dpv);
+        }
+        a.d_p[(size_t)t * K + i] = dpv;
       }
+#pragma unroll
+      for (int q = 0; q < KR; ++q)
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          float al = 0.f;
+#pragma unroll
+          for (int r = 0; r < KR; ++r) al = fmaf(A[r][q], gam[r][i], al);
+          s_al[q][i] = al;
+        }
+    }
+  }
+  __syncthreads();
+  if (tid < KR * KR) {
+    const int qa = tid / KR, qb = tid % KR;
+    float be = 0.f;
+    if (mgs) {
+      const int x = qa < qb ? qa : qb, y = qa < qb ? qb : qa;
+      const int l = x * KR - x * (x - 1) / 2 + (y - x);   // index of (x, y) in the upper-triangle order
+      be = x == y ? 2.f * s_F[l] : s_F[l];
+    }
+    s_be[qa][qb] = be;
   }
   if (tid < N) a.d_hpre[(size_t)t * N + tid] = s_acc[tid];
   if (tid < K * K) a.d_hres[(size_t)t * K * K + tid] = s_acc[O_H + tid];
@@ -406,43 +417,85 @@ struct BwdConvArgs {
 // MLP-type: d_out[t] = dg_0[t] + sum over kernels q and lags i of
 // w_q[i] dg_q[t + i] (same sequence), and the conv-weight gradient partials
 // sum_t dg_q[t] out[t - i] over this workgroup's token range.  One thread per
-// channel.
+// channel; two sweeps over the range, each carrying a window of 11 tokens in
+// registers: downwards the later basis gradients (for d_out), upwards the
+// earlier outputs (for the weight gradient).  A window is emptied where a
+// sequence ends, so nothing crosses from one sequence to the next.
 template <class E>
 __global__ __launch_bounds__(BT) void bwd_conv_kernel(BwdConvArgs a) {
   using T = typename E::T;
+  constexpr int L = 11;
   const int c = blockIdx.x * BT + threadIdx.x;
   if (c >= a.C) return;
-  const int C = a.C;
+  const int C = a.C, S = a.S;
   const int t0 = blockIdx.y * a.TC;
   const int t1 = t0 + a.TC < a.T ? t0 + a.TC : a.T;
+  if (t0 >= t1) {
+#pragma unroll
+    for (int r = 0; r < NCONV; ++r) a.part[((size_t)blockIdx.y * NCONV + r) * C + c] = 0.f;
+    return;
+  }
   const T* out = reinterpret_cast<const T*>(a.out);
   T* d_out = reinterpret_cast<T*>(a.d_out);
-  float w[NCONV], acc[NCONV];
+  const float* dg = a.dg + c;
+  float w[NCONV];
 #pragma unroll
-  for (int r = 0; r < NCONV; ++r) {
-    w[r] = a.conv_w[(size_t)r * C + c];
-    acc[r] = 0.f;
+  for (int r = 0; r < NCONV; ++r) w[r] = a.conv_w[(size_t)r * C + c];
+  // downward sweep: F[q][i] = dg_q[t + 1 + i] within the sequence, else 0
+  float F[3][L];
+  {
+    const int tl = t1 - 1, sl = tl % S;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const bool in = sl + 1 + i < S;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) F[q][i] = in ? dg[((size_t)(tl + 1 + i) * 4 + q + 1) * C] : 0.f;
+    }
   }
-  for (int t = t0; t < t1; ++t) {
-    const int s = t % a.S;
-    const float* dgt = a.dg + (size_t)t * 4 * C + c;
-    float d = dgt[0];
+  for (int t = t1 - 1; t >= t0; --t) {
+    float g[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) g[q] = dg[((size_t)t * 4 + q) * C];
+    float d = g[0];
 #pragma unroll
     for (int q = 1; q < 4; ++q) {
       const int off = q == 1 ? 0 : q == 2 ? 4 : 12;
+      d = fmaf(w[off], g[q], d);
 #pragma unroll
-      for (int i = 0; i < 4 * q; ++i)
-        if (s + i < a.S) d = fmaf(w[off + i], dgt[((size_t)i * 4 + q) * C], d);
+      for (int i = 1; i < 4 * q; ++i) d = fmaf(w[off + i], F[q - 1][i - 1], d);
     }
     st1(d_out + (size_t)t * C + c, d);
+    const bool start = t % S == 0;   // t - 1 belongs to the previous sequence
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+#pragma unroll
+      for (int i = L - 1; i > 0; --i) F[q][i] = start ? 0.f : F[q][i - 1];
+      F[q][0] = start ? 0.f : g[q + 1];
+    }
+  }
+  // upward sweep: P[i] = out[t - 1 - i] within the sequence, else 0
+  float P[L], acc[NCONV];
+#pragma unroll
+  for (int r = 0; r < NCONV; ++r) acc[r] = 0.f;
+  {
+    const int s0 = t0 % S;
+#pragma unroll
+    for (int i = 0; i < L; ++i) P[i] = s0 - 1 - i >= 0 ? ld1(out + (size_t)(t0 - 1 - i) * C + c) : 0.f;
+  }
+  for (int t = t0; t < t1; ++t) {
+    const float o = ld1(out + (size_t)t * C + c);
 #pragma unroll
     for (int q = 1; q < 4; ++q) {
       const int off = q == 1 ? 0 : q == 2 ? 4 : 12;
-      const float gq = dgt[(size_t)q * C];
+      const float gq = dg[((size_t)t * 4 + q) * C];
+      acc[off] = fmaf(gq, o, acc[off]);
 #pragma unroll
-      for (int i = 0; i < 4 * q; ++i)
-        if (i <= s) acc[off + i] = fmaf(gq, ld1(out + (size_t)(t - i) * C + c), acc[off + i]);
+      for (int i = 1; i < 4 * q; ++i) acc[off + i] = fmaf(gq, P[i - 1], acc[off + i]);
     }
+    const bool last = (t + 1) % S == 0;   // t + 1 starts a new sequence
+#pragma unroll
+    for (int i = L - 1; i > 0; --i) P[i] = last ? 0.f : P[i - 1];
+    P[0] = last ? 0.f : o;
   }
 #pragma unroll
   for (int r = 0; r < NCONV; ++r) a.part[((size_t)blockIdx.y * NCONV + r) * C + c] = acc[r];
@@ -774,6 +827,156 @@ __global__ __launch_bounds__(BT) void bwd_rows_kernel(BwdRowArgs a) {
   }
 }
 
+// bf16 form of the pass above on MFMA 16x16x32 tiles.  Workgroup: 4 waves x
+// 64 rows (four 16-row tiles per wave), tokens in blocks of 32.  Per block,
+// the coefficient rows are staged in LDS as bf16 hi + lo pairs (G = hi + lo to
+// about 2^-17 relative; both halves go through the MFMA, so the products
+// keep float accuracy), in token-major and column-major copies, and the
+// state rows of the workgroup transposed to [row][token]:
+//   dX tile (16 tokens x 16 rows) = G (16 x 32 columns) . W^T, A = G rows,
+//       B = the wave's W rows (registers for the whole launch), then
+//       + c x + c0 and the read-modify-write of dX;
+//   dW^T tile (16 columns x 16 rows) += G^T (16 x 32 tokens) . X (32 x 16),
+//       accumulated in registers over the token range.
+template <int NR>
+__global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
+  constexpr int TB = 32;            // tokens per block
+  constexpr int RW = 16 * NR;       // rows per wave
+  constexpr int XS = 4 * RW + 8;    // LDS row stride (elements) of the state tile [token][row]
+  constexpr int DS = 4 * RW + 4;    // LDS row stride of the product tile [token][row]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const long rwg = (long)blockIdx.x * 4 * RW;   // first row of the workgroup
+  const int t0 = blockIdx.y * a.TW;
+  const int t1 = t0 + a.TW < a.T ? t0 + a.TW : a.T;
+  __shared__ __align__(16) uint16_t s_x[TB][XS];
+  __shared__ __align__(16) uint16_t s_g[2][TB][32];    // [hi/lo][token][column]
+  __shared__ __align__(16) uint16_t s_gt[2][32][TB];   // [hi/lo][column][token]
+  __shared__ float s_c[TB][2];
+  __shared__ __align__(16) float s_d[16][DS];          // W G for 16 tokens
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X);
+  uint16_t* dX = reinterpret_cast<uint16_t*>(a.dX);
+  const int ncol = a.ncol;
+  const int NTC = (ncol + 15) / 16;
+  // B fragments of the wave's W rows: lane (g, r) of tile j holds W[row][8g .. 8g + 7]
+  uint4 bw[NR];
+  bool tile_in[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const long row = rwg + (long)wave * RW + 16 * j + r;
+    tile_in[j] = rwg + (long)wave * RW + 16 * j < a.R;   // R is a multiple of 32: tiles are whole
+    union { uint16_t h[8]; uint4 u; } f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 8 * g + e;
+      f.h[e] = (tile_in[j] && col < ncol) ? W[(size_t)row * ncol + col] : (uint16_t)0;
+    }
+    bw[j] = f.u;
+  }
+  f32x4_t accw[NR][2];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) accw[j][0] = accw[j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int tb = t0; tb < t1; tb += TB) {
+    const int nt = t1 - tb < TB ? t1 - tb : TB;
+    __syncthreads();
+    // coefficients: thread u takes token u / 8, columns 4 (u % 8) .. + 3
+    {
+      const int tu = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = c4 + e;
+        const float v = (tu < nt && col < ncol) ? a.G[(size_t)(tb + tu) * ncol + col] : 0.f;
+        const uint32_t hi = f32_to_bf16(v);
+        const uint32_t lo = f32_to_bf16(v - __uint_as_float(hi << 16));
+        s_g[0][tu][col] = (uint16_t)hi;
+        s_g[1][tu][col] = (uint16_t)lo;
+        s_gt[0][col][tu] = (uint16_t)hi;
+        s_gt[1][col][tu] = (uint16_t)lo;
+      }
+      if (threadIdx.x < TB) {
+        const int t = threadIdx.x;
+        s_c[t][0] = t < nt ? a.sc[(size_t)(tb + t) * 4 + (a.act ? 2 : 0)] : 0.f;
+        s_c[t][1] = (t < nt && !a.act) ? a.sc[(size_t)(tb + t) * 4 + 1] : 0.f;
+      }
+    }
+    // state rows as they are in memory: 16-byte loads of 8 rows of one token
+    for (int u = threadIdx.x; u < TB * (4 * RW / 8); u += BT) {
+      const int tu = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
+      const long row = rwg + rc;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (tu < nt && row < a.R) v = ld16(X + (size_t)(tb + tu) * a.R + row);
+      *reinterpret_cast<uint4*>(&s_x[tu][rc]) = v;
+    }
+    __syncthreads();
+    // weight gradient: dW^T[col][row] += sum over the block's tokens; the B
+    // fragment (8 tokens of one row) is gathered from the token-major tile
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      if (!tile_in[j]) continue;
+      union { uint16_t h[8]; uint4 u; } f;
+      const int rl = wave * RW + 16 * j + r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f.h[e] = s_x[8 * g + e][rl];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m >= NTC) break;
+        const uint4 ah = *reinterpret_cast<const uint4*>(&s_gt[0][16 * m + r][8 * g]);
+        const uint4 al = *reinterpret_cast<const uint4*>(&s_gt[1][16 * m + r][8 * g]);
+        accw[j][m] = Bf16::mma(Bf16::mma(accw[j][m], ah, f.u), al, f.u);
+      }
+    }
+    // state gradient, 16 tokens at a time: products into LDS, then 16-byte
+    // read-modify-writes of 8 rows of one token, dX += W G + c x + c0
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (16 * h >= nt) break;   // uniform over the workgroup
+      const uint4 ah = *reinterpret_cast<const uint4*>(&s_g[0][16 * h + r][8 * g]);
+      const uint4 al = *reinterpret_cast<const uint4*>(&s_g[1][16 * h + r][8 * g]);
+      if (h) __syncthreads();    // the previous half's products have been read
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const f32x4_t acc = Bf16::mma(Bf16::mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, ah, bw[j]), al, bw[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_d[4 * g + i][wave * RW + 16 * j + r] = acc[i];
+      }
+      __syncthreads();
+      const int nh = nt - 16 * h < 16 ? nt - 16 * h : 16;
+      for (int u = threadIdx.x; u < nh * (4 * RW / 8); u += BT) {
+        const int tu = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
+        const long row = rwg + rc;
+        if (row >= a.R) continue;
+        const int tl = 16 * h + tu;
+        const int t = tb + tl;
+        uint16_t* dr = a.act ? dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + (int)(row / a.C)]) * a.C + row % a.C
+                             : dX + (size_t)t * a.R + row;
+        float v[8], x[8];
+        Bf16::unpack(ld16(dr), v);
+        Bf16::unpack(*reinterpret_cast<const uint4*>(&s_x[tl][rc]), x);
+        const float cx = s_c[tl][0], c0 = s_c[tl][1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += s_d[tu][rc + e] + fmaf(cx, x[e], c0);
+        st16(dr, Bf16::pack(v));
+      }
+    }
+  }
+  // partial weight gradients: lane (g, r) of tile (j, m) holds columns 16m + 4g + i of row 16j + r
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    if (!tile_in[j]) continue;
+    const long row = rwg + (long)wave * RW + 16 * j + r;
+    float* pp = a.part + ((size_t)blockIdx.y * a.R + row) * ncol;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = 16 * m + 4 * g + i;
+        if (col < ncol) pp[col] = accw[j][m][i];
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -805,7 +1008,9 @@ bool make_bwd_plan(const Plan& P, BwdPlan* B) {
   q.NBT = 2 * P.N + P.K * P.K + P.K * P.KR + 3;
   // token chunks of the row kernels: about 2048 workgroups, at least 64 tokens each
   const long maxch = (P.T + 63) / 64 > 0 ? (P.T + 63) / 64 : 1;
-  const long xf = (q.NC / 2 + BT - 1) / BT, xa = (q.KC / 2 + BT - 1) / BT;
+  // rows per workgroup: 256 for the bf16 MFMA pass, 512 for the float one
+  const long rpw = P.dtype == XHC_BF16 ? 256 : 2 * BT;
+  const long xf = (q.NC + rpw - 1) / rpw, xa = (q.KC + rpw - 1) / rpw;
   q.nch_f = clampi((2048 + xf - 1) / xf, 1, 64);
   if (q.nch_f > maxch) q.nch_f = (int)maxch;
   q.nch_a = clampi((2048 + xa - 1) / xa, 1, 64);
@@ -903,6 +1108,11 @@ void rows_launch(const BwdRowArgs& a, int nch, hipStream_t st) {
 
 template <class E>
 void rows_dispatch(const BwdRowArgs& a, int nch, hipStream_t st) {
+  if constexpr (std::is_same<E, Bf16>::value) {
+    dim3 grid((unsigned)((a.R + 4 * 64 - 1) / (4 * 64)), nch);
+    bwd_rows_mfma_kernel<4><<<grid, BT, 0, st>>>(a);
+    return;
+  }
   if (a.ncol <= 8) rows_launch<E, 8>(a, nch, st);
   else if (a.ncol <= 16) rows_launch<E, 16>(a, nch, st);
   else rows_launch<E, 32>(a, nch, st);

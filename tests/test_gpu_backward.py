@@ -116,6 +116,9 @@ CASES = [
     (8, 4, 1, 160, 1, 33, 3, 1, "f32"),
     (4, 4, 4, 64, 2, 14, 3, 1, "f32"),
     (1, 1, 1, 64, 2, 13, 3, 1, "f32"),
+    # the benchmark's channel width, 2 x 160 tokens
+    (16, 4, 2, 4096, 2, 160, 3, 1, "bf16"),
+    (16, 4, 2, 4096, 2, 160, 0, 1, "bf16"),
 ]
 
 
