@@ -44,6 +44,7 @@ namespace {
 
 constexpr int BT = 256;      // threads per workgroup
 constexpr int NCONV = 24;    // conv weight rows: kernels 4, 8, 12
+constexpr int NCOLB = 128;   // workgroups of the first stage of the W_r column sums
 
 __device__ __forceinline__ float ld1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
@@ -517,16 +518,34 @@ __global__ __launch_bounds__(BT) void bwd_reduce_kernel(const float* __restrict_
   out[i] = s;
 }
 
-// Column sums of W_full's router columns: colsum[n] = sum_row W[row][n].
+// Column sums of W_full's router columns, first stage: workgroup b sums the
+// rows b, b + nblk, ... of columns 0..N-1 into part[b][n] (the second stage is
+// bwd_reduce_kernel over the nblk partials).
 template <class E>
 __global__ __launch_bounds__(BT) void bwd_wcolsum_kernel(const typename E::T* __restrict__ W, long R, int ncol,
-                                                         float* __restrict__ colsum) {
-  __shared__ float s_tmp[BT / WAVE];
-  const int n = blockIdx.x;
-  float v = 0.f;
-  for (long r = threadIdx.x; r < R; r += BT) v += ld1(W + (size_t)r * ncol + n);
-  v = block_sum(v, s_tmp);
-  if (threadIdx.x == 0) colsum[n] = v;
+                                                         int N, float* __restrict__ part) {
+  __shared__ float s_tmp[BT / WAVE][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float acc[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) acc[n] = 0.f;
+  for (long row = (long)blockIdx.x * BT + threadIdx.x; row < R; row += (long)gridDim.x * BT) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+      if (n < N) acc[n] += ld1(W + (size_t)row * ncol + n);
+  }
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const float v = wave_sum(acc[n]);
+    if (lane == 0) s_tmp[wave][n] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < N) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < BT / WAVE; ++w) v += s_tmp[w][threadIdx.x];
+    part[(size_t)blockIdx.x * N + threadIdx.x] = v;
+  }
 }
 
 // Column sums of the per-token rows [T][ncols]: column col of the bias / scale
@@ -1044,6 +1063,7 @@ bool make_bwd_plan(const Plan& P, BwdPlan* B) {
   q.o_brow = take(T * q.NBT * 4);
   q.o_bsum = take((size_t)q.NBT * 4);
   q.o_colsum = take(N * 4);
+  q.o_colpart = take((size_t)NCOLB * N * 4);
   q.o_wpartf = take((size_t)q.nch_f * q.NC * q.ncol_f * 4);
   q.o_wparta = take((size_t)q.nch_a * q.KC * q.ncol_a * 4);
   q.total = T == 0 ? 0 : off;
@@ -1133,8 +1153,10 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
   launch_projection(dt, Bp.NTF, X, T, Bp.NC, bws + Bp.o_wpf, Bp.nkb_f, Bp.KS, part, stats, st);
   launch_projection(dt, Bp.NTA, xa, T, Bp.KC, bws + Bp.o_wpa, Bp.nkb_a, Bp.KSa, parta, statsa, st);
   float* colsum = reinterpret_cast<float*>(bws + Bp.o_colsum);
-  bwd_wcolsum_kernel<E><<<N, BT, 0, st>>>(reinterpret_cast<const typename E::T*>(w->w_full), Bp.NC, Bp.ncol_f,
-                                          colsum);
+  float* cpart = reinterpret_cast<float*>(bws + Bp.o_colpart);
+  bwd_wcolsum_kernel<E><<<NCOLB, BT, 0, st>>>(reinterpret_cast<const typename E::T*>(w->w_full), Bp.NC, Bp.ncol_f,
+                                              N, cpart);
+  bwd_reduce_kernel<<<1, BT, 0, st>>>(cpart, NCOLB, N, colsum, nullptr, 1, 0);
   BwdTokArgs a{};
   a.part = part;
   a.stats = stats;

@@ -116,6 +116,8 @@ CASES = [
     (8, 4, 1, 160, 1, 33, 3, 1, "f32"),
     (4, 4, 4, 64, 2, 14, 3, 1, "f32"),
     (1, 1, 1, 64, 2, 13, 3, 1, "f32"),
+    (16, 4, 0, 128, 5, 5, 3, 1, "f32"),     # no fixed streams; sequences shorter than the longest kernel
+    (16, 4, 2, 64, 1, 1, 3, 1, "bf16"),     # one token
     # the benchmark's channel width, 2 x 160 tokens
     (16, 4, 2, 4096, 2, 160, 3, 1, "bf16"),
     (16, 4, 2, 4096, 2, 160, 0, 1, "bf16"),
@@ -167,3 +169,18 @@ def test_backward_in_place_gradient(lib):
         assert torch.equal(a, b)
     for name in res[0][3]:
         assert torch.equal(res[0][3][name], res[1][3][name]), name
+
+
+def test_backward_empty_batch_is_a_no_op(lib):
+    cfg = Config(N=16, k=4, m=2, C=64, B=0, S=8, n_convs=3, dtype="bf16")
+    assert lib.backward_workspace_bytes(cfg) == 0
+    w = weights_to_device(synth.xhc_layer_weights(63, 0, 16, 4, 64, 4, "bf16"))
+    e = torch.empty((0, 16, 64), dtype=torch.bfloat16, device="cuda")
+    e2 = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    ws, bws = lib.workspace(cfg), lib.backward_workspace(cfg)
+    d_conv = torch.full((24, 64), 7.0, device="cuda")
+    lib.xhc_post_backward(cfg, w, e, e2, e2, e, e.clone(), e2.clone(), d_conv, ws, bws)
+    g = lib.grads(cfg)
+    lib.xhc_pre_backward(cfg, w, e, e.clone(), g, ws, bws)
+    torch.cuda.synchronize()
+    assert torch.all(d_conv == 7.0), "nothing is written for an empty batch"
