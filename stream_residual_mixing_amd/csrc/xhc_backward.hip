@@ -897,9 +897,32 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
 #pragma unroll
   for (int j = 0; j < NR; ++j) accw[j][0] = accw[j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Each thread moves 4 chunks of 8 rows of one token per block: chunk k is
+  // token (tid + 256 k) / 32, rows 8 ((tid + 256 k) % 32); chunks 0-1 fall in
+  // the block's first 16 tokens, 2-3 in the second.  The next block's state
+  // chunks and this block's dX chunks are loaded ahead of the compute.
+  constexpr int NCH = TB * (4 * RW / 8) / BT;   // 4
+  static_assert(NCH == 4, "chunk mapping assumes 4 chunks per thread");
+  uint4 xn[NCH];
+  auto load_x = [&](int tb, int nt, uint4 (&dst)[NCH]) {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int u = threadIdx.x + BT * k;
+      const int tu = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
+      const long row = rwg + rc;
+      dst[k] = (tu < nt && row < a.R) ? ld16(X + (size_t)(tb + tu) * a.R + row) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (t0 < t1) load_x(t0, t1 - t0 < TB ? t1 - t0 : TB, xn);
   for (int tb = t0; tb < t1; tb += TB) {
     const int nt = t1 - tb < TB ? t1 - tb : TB;
     __syncthreads();
+    // state rows as they are in memory (loaded during the previous block)
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int u = threadIdx.x + BT * k;
+      *reinterpret_cast<uint4*>(&s_x[u / (4 * RW / 8)][(u % (4 * RW / 8)) * 8]) = xn[k];
+    }
     // coefficients: thread u takes token u / 8, columns 4 (u % 8) .. + 3
     {
       const int tu = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
@@ -920,14 +943,23 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
         s_c[t][1] = (t < nt && !a.act) ? a.sc[(size_t)(tb + t) * 4 + 1] : 0.f;
       }
     }
-    // state rows as they are in memory: 16-byte loads of 8 rows of one token
-    for (int u = threadIdx.x; u < TB * (4 * RW / 8); u += BT) {
+    // this block's dX chunks, then the next block's state chunks
+    uint16_t* dr[NCH];
+    uint4 dv[NCH];
+    bool own[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int u = threadIdx.x + BT * k;
       const int tu = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
       const long row = rwg + rc;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tu < nt && row < a.R) v = ld16(X + (size_t)(tb + tu) * a.R + row);
-      *reinterpret_cast<uint4*>(&s_x[tu][rc]) = v;
+      own[k] = tu < nt && row < a.R;
+      const int t = tb + (own[k] ? tu : 0);
+      const long rr = own[k] ? row : 0;
+      dr[k] = a.act ? dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + (int)(rr / a.C)]) * a.C + rr % a.C
+                    : dX + (size_t)t * a.R + rr;
+      dv[k] = own[k] ? ld16(dr[k]) : make_uint4(0, 0, 0, 0);
     }
+    if (tb + TB < t1) load_x(tb + TB, t1 - tb - TB < TB ? t1 - tb - TB : TB, xn);
     __syncthreads();
     // weight gradient: dW^T[col][row] += sum over the block's tokens; the B
     // fragment (8 tokens of one row) is gathered from the token-major tile
@@ -946,8 +978,8 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
         accw[j][m] = Bf16::mma(Bf16::mma(accw[j][m], ah, f.u), al, f.u);
       }
     }
-    // state gradient, 16 tokens at a time: products into LDS, then 16-byte
-    // read-modify-writes of 8 rows of one token, dX += W G + c x + c0
+    // state gradient, 16 tokens at a time: products into LDS, then the
+    // 16-byte read-modify-writes, dX += W G + c x + c0
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (16 * h >= nt) break;   // uniform over the workgroup
@@ -961,22 +993,19 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
         for (int i = 0; i < 4; ++i) s_d[4 * g + i][wave * RW + 16 * j + r] = acc[i];
       }
       __syncthreads();
-      const int nh = nt - 16 * h < 16 ? nt - 16 * h : 16;
-      for (int u = threadIdx.x; u < nh * (4 * RW / 8); u += BT) {
-        const int tu = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
-        const long row = rwg + rc;
-        if (row >= a.R) continue;
-        const int tl = 16 * h + tu;
-        const int t = tb + tl;
-        uint16_t* dr = a.act ? dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + (int)(row / a.C)]) * a.C + row % a.C
-                             : dX + (size_t)t * a.R + row;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k = 2 * h + kk;
+        if (!own[k]) continue;
+        const int u = threadIdx.x + BT * k;
+        const int tl = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
         float v[8], x[8];
-        Bf16::unpack(ld16(dr), v);
+        Bf16::unpack(dv[k], v);
         Bf16::unpack(*reinterpret_cast<const uint4*>(&s_x[tl][rc]), x);
         const float cx = s_c[tl][0], c0 = s_c[tl][1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += s_d[tu][rc + e] + fmaf(cx, x[e], c0);
-        st16(dr, Bf16::pack(v));
+        for (int e = 0; e < 8; ++e) v[e] += s_d[tl - 16 * h][rc + e] + fmaf(cx, x[e], c0);
+        st16(dr[k], Bf16::pack(v));
       }
     }
   }
