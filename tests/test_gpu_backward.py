@@ -184,3 +184,110 @@ def test_backward_empty_batch_is_a_no_op(lib):
     lib.xhc_pre_backward(cfg, w, e, e.clone(), g, ws, bws)
     torch.cuda.synchronize()
     assert torch.all(d_conv == 7.0), "nothing is written for an empty batch"
+
+
+# ---------------------------------------------------------------- full size
+
+FULL = dict(N=16, k=4, m=2, C=4096, B=2, S=8192)
+FULL_SEED, GRAD_SEED = 64, 564
+
+
+def _mini_case(cfg, seed, layer, t, attempts):
+    """Oracle inputs for sampled token t at full size: the tokens lo..hi of
+    its sequence with lo = t - 11 and hi = t + 11 (clipped to the sequence).
+    dX[t] and the map gradients at t depend on token t and its output window;
+    d_out[t] on the basis gradients of t..t+11, whose bases reach back to
+    t - 11.  Rows come from the per-token generator keys."""
+    S, N, C = cfg.S, cfg.N, cfg.C
+    b, s = divmod(int(t), S)
+    lo, hi = b * S + max(0, s - 11), b * S + min(S - 1, s + 11)
+    rows = range(lo, hi + 1)
+    X = synth.state_rows(seed, rows, N, C, "bf16", attempts)
+    out = synth.out_rows(seed, layer, rows, C, "bf16")
+    d_X = synth.state_rows(GRAD_SEED, rows, N, C, "bf16")
+    d_inp = synth.out_rows(GRAD_SEED, 0, rows, C, "bf16")
+    return lo, hi, X, out, d_X, d_inp
+
+
+def _oracle_token_grads(cfg, ow, t, lo, hi, X, out, d_X, d_inp):
+    W = hi - lo + 1
+    sub = Config(N=cfg.N, k=cfg.k, m=cfg.m, C=cfg.C, B=1, S=W, n_convs=cfg.n_convs, dtype="bf16")
+    pre, ga, gg = oracle_backward(sub, X, out, ow, d_inp, d_X)
+    j = t - lo
+    return dict(I=pre["I"][j], X=ga["X"][j] + gg["X"][j], X_apply=ga["X"][j], X_full=gg["X_full"][j],
+                d_out=ga["out"].reshape(W, cfg.C)[j], h_pre=ga["h_pre"][j], h_res=ga["h_res"][j],
+                h_post=ga["h_post"][j], p=ga["p"][j])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("nconv,layer", [(3, 0), (0, 1)])
+def test_backward_full_size_sampled_tokens(lib, nconv, layer):
+    """The benchmark's shape and launch sequence (2 x 8192 tokens, C = 4096,
+    xhc_pre then both backward calls); sampled tokens compared with the
+    oracle one by one (every token whose maps they depend on has a routing
+    margin of at least 1e-4, redrawn otherwise); every token's state
+    gradient, d_out and every weight gradient checked finite."""
+    cfg = Config(n_convs=nconv, dtype="bf16", **FULL)
+    N, k, C, B, S = cfg.N, cfg.k, cfg.C, cfg.B, cfg.S
+    wd = synth.xhc_layer_weights(FULL_SEED, layer, N, k, C, cfg.K_r, "bf16")
+    ow = K.oracle_weights(wd)
+    toks = K.sample_tokens(B, S, 4, FULL_SEED)
+    attempts, ref = {}, {}
+    for j, t in enumerate(toks):
+        t = int(t)
+        if j % 8 == 0:
+            _print(f"oracle: token {j} of {len(toks)}")
+        for _ in range(20):
+            lo, hi, X, out, d_X, d_inp = _mini_case(cfg, FULL_SEED, layer, t, attempts)
+            z = O.xhc_router_logits(K.f64(X), ow["w_full"][:, :N])
+            mg = O.xhc_topk_margin(z, cfg.m, k)
+            bad = [lo + i for i in range(t - lo, hi - lo + 1) if mg[i] < K.MARGIN]
+            if not bad:
+                break
+            for r_ in bad:
+                attempts[r_] = attempts.get(r_, 0) + 1
+        assert not bad, f"token {t}: no draws with routing margin >= {K.MARGIN}"
+    # a later window may have redrawn rows of an earlier one: the cases are built after all redraws
+    for t in toks:
+        lo, hi, X, out, d_X, d_inp = _mini_case(cfg, FULL_SEED, layer, int(t), attempts)
+        ref[int(t)] = _oracle_token_grads(cfg, ow, int(t), lo, hi, X, out, d_X, d_inp)
+    _print(f"oracle ready: {len(toks)} sampled tokens, {sum(attempts.values())} redraws")
+
+    T = cfg.T
+    Xd = synth.state(FULL_SEED, T, N, C, "bf16", attempts).to("cuda")
+    outd = synth.sublayer_out(FULL_SEED, layer, B, S, C, "bf16").reshape(T, C).to("cuda")
+    d_Xd = synth.state(GRAD_SEED, T, N, C, "bf16").to("cuda")
+    d_inpd = synth.sublayer_out(GRAD_SEED, 0, B, S, C, "bf16").reshape(T, C).to("cuda")
+    _print(f"inputs on the GPU: T={T} N={N} C={C} n_convs={nconv}")
+    w = weights_to_device(wd)
+    inp = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
+    ws = lib.workspace(cfg)
+    lib.xhc_pre(cfg, w, Xd, inp, ws)
+    bws = lib.backward_workspace(cfg)
+    dX = torch.empty_like(Xd)
+    d_out = torch.empty_like(outd)
+    d_conv = torch.empty((24, C), dtype=torch.float32, device="cuda") if nconv else None
+    lib.xhc_post_backward(cfg, w, Xd, outd, d_inpd, d_Xd, dX, d_out, d_conv, ws, bws)
+    dmaps = {key: v.clone() for key, v in lib.backward_ws_arrays(cfg, bws).items()}
+    g = lib.grads(cfg)
+    lib.xhc_pre_backward(cfg, w, Xd, dX, g, ws, bws)
+    torch.cuda.synchronize()
+    for name, v in [("dX", dX), ("d_out", d_out)] + list(g.items()) + ([("d_conv", d_conv)] if nconv else []):
+        assert bool(torch.isfinite(v).all()), f"{name} has non-finite entries"
+    tk = torch.from_numpy(toks).to("cuda")
+    idx = lib.ws_arrays(cfg, ws)["idx"].index_select(0, tk).cpu().numpy()
+    got = dict(X=dX.index_select(0, tk).cpu(), d_out=d_out.index_select(0, tk).cpu(),
+               **{key: v.index_select(0, tk).cpu() for key, v in dmaps.items()})
+    o = {key: np.stack([ref[int(t)][key] for t in toks]) for key in ref[int(toks[0])]}
+    assert np.array_equal(idx, o["I"]), "active indices differ"
+    part2 = o["X_apply"] + o["X_full"]
+    allow = sum(K.ulp(np.abs(v), "bf16") for v in (o["X_apply"], part2, o["X"]))
+    errs = {
+        "dX": K.err_with_allowance(K.f64(got["X"]), o["X"], allow),
+        "d_out": K.rel_err(K.f64(got["d_out"]), o["d_out"]),
+        **{"d_" + key: K.rel_err(K.f64(got[key]), o[key]) for key in ("h_pre", "h_res", "h_post", "p")},
+    }
+    _print("  errors", {key: f"{v:.2e}" for key, v in errs.items()})
+    bad = {key: v for key, v in errs.items() if not v <= GTOL["bf16"]}
+    assert not bad, bad
