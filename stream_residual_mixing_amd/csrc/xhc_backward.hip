@@ -763,7 +763,7 @@ __global__ __launch_bounds__(BT) void bwd_token_kernel(BwdTokArgs a) {
   a.sc[(size_t)t * 4 + 0] = cx;
   a.sc[(size_t)t * 4 + 1] = c0;
   a.sc[(size_t)t * 4 + 2] = cxa;
-  a.sc[(size_t)t * 4 + 3] = 0.f;
+  a.sc[(size_t)t * 4 + 3] = mu;
 }
 
 struct BwdRowArgs {
@@ -779,7 +779,9 @@ struct BwdRowArgs {
 };
 
 // dX += W G_t + c x (+ c0) row by row, and the weight-gradient partials
-// sum_t x_t[row] G_t over this workgroup's token range.  Each thread owns two
+// sum_t x_t[row] G_t over this workgroup's token range (for the router
+// columns of the full state, the centred x_t[row] - mu_t, so that no mean
+// correction is subtracted afterwards).  Each thread owns two
 // adjacent rows of the contraction (same stream, adjacent channels) with
 // their weights in registers; the coefficient rows of 64 tokens at a time
 // are staged in LDS.  Full mode: rows of the flattened state, c = cx, plus
@@ -793,7 +795,7 @@ __global__ __launch_bounds__(BT) void bwd_rows_kernel(BwdRowArgs a) {
   const int t0 = blockIdx.y * a.TW;
   const int t1 = t0 + a.TW < a.T ? t0 + a.TW : a.T;
   __shared__ float s_g[64][CM];
-  __shared__ float s_c[64][2];
+  __shared__ float s_c[64][3];
   const T* W = reinterpret_cast<const T*>(a.W);
   const T* X = reinterpret_cast<const T*>(a.X);
   T* dX = reinterpret_cast<T*>(a.dX);
@@ -817,21 +819,24 @@ __global__ __launch_bounds__(BT) void bwd_rows_kernel(BwdRowArgs a) {
       const int tu = threadIdx.x;
       s_c[tu][0] = tu < nt ? a.sc[(size_t)(tb + tu) * 4 + (a.act ? 2 : 0)] : 0.f;
       s_c[tu][1] = (tu < nt && !a.act) ? a.sc[(size_t)(tb + tu) * 4 + 1] : 0.f;
+      s_c[tu][2] = (tu < nt && !a.act) ? a.sc[(size_t)(tb + tu) * 4 + 3] : 0.f;
     }
     __syncthreads();
     if (!own) continue;
+    const int ncen = a.act ? 0 : a.N;   // centred (router) columns
     for (int u = 0; u < nt; ++u) {
       const int t = tb + u;
       const T* xr = X + (size_t)t * a.R + r0;
       const float x0 = ld1(xr), x1 = ld1(xr + 1);
       float d0 = fmaf(s_c[u][0], x0, s_c[u][1]), d1 = fmaf(s_c[u][0], x1, s_c[u][1]);
+      const float m0 = x0 - s_c[u][2], m1 = x1 - s_c[u][2];
 #pragma unroll
       for (int q = 0; q < CM; ++q) {
         const float g = s_g[u][q];
         d0 = fmaf(g, w0[q], d0);
         d1 = fmaf(g, w1[q], d1);
-        acc0[q] = fmaf(x0, g, acc0[q]);
-        acc1[q] = fmaf(x1, g, acc1[q]);
+        acc0[q] = fmaf(q < ncen ? m0 : x0, g, acc0[q]);
+        acc1[q] = fmaf(q < ncen ? m1 : x1, g, acc1[q]);
       }
       T* dr = a.act ? dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + j]) * a.C + c : dX + (size_t)t * a.R + r0;
       st1(dr, ld1(dr) + d0);
@@ -1251,8 +1256,10 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
   r.act = 0;
   rows_dispatch<E>(r, Bp.nch_f, st);
   const long nf = Bp.NC * Bp.ncol_f;
+  // the bf16 pass accumulates uncentred rows: subtract sum_t mu_t G_t from the router columns
+  const int ncorr = std::is_same<E, Bf16>::value ? N : 0;
   bwd_reduce_kernel<<<(unsigned)((nf + BT - 1) / BT), BT, 0, st>>>(r.part, Bp.nch_f, nf, g->dW_full,
-                                                                   s.sums + Bp.NBT - N, Bp.ncol_f, N);
+                                                                   s.sums + Bp.NBT - N, Bp.ncol_f, ncorr);
   // active rows
   BwdRowArgs ra = r;
   ra.X = xa;
