@@ -44,7 +44,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     import subprocess
     structs = {"xhc_config": XhcConfig, "xhc_weights": XhcWeights, "xhc_ws_layout": binding.XhcWsLayout,
                "xhcf_weights": binding.XhcfWeights, "xhcf_ws_layout": binding.XhcfWsLayout,
-               "xhcf4_weights": binding.Xhcf4Weights, "xhcf4_ws_layout": binding.Xhcf4WsLayout}
+               "xhcf4_weights": binding.Xhcf4Weights, "xhcf4_ws_layout": binding.Xhcf4WsLayout, "xhc_grads": binding.XhcGrads, "xhc_bwd_ws_layout": binding.XhcBwdWsLayout}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "xhc.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -244,3 +244,75 @@ def test_flash_decode_and_4sub_calls_reject_bad_arguments_before_launch(lib):
     assert d.xhcf4_pre(ctypes.byref(ok), ctypes.byref(w4), 0x20000, 0x30000, 0x50000, 0x40000, None) == \
         binding.XHC_ERR_INVALID_ARG
     assert lib.flash4_workspace_bytes(_cfg(k=2, m=1)) == 0
+
+
+def test_backward_layout(lib):
+    """Backward workspace: public arrays aligned, disjoint, inside the total;
+    an empty batch needs none; shapes without kernels are refused."""
+    for cfg in (_cfg(), _cfg(n_convs=0), _cfg(N=8, k=4, m=1, C=256, B=1, S=33, dtype="f32")):
+        n = lib.backward_workspace_bytes(cfg)
+        L = lib.backward_layout(cfg)
+        T, N, k, Kr = cfg.T, cfg.N, cfg.k, cfg.K_r
+        offs = sorted([(L.d_h_pre, T * N * 4), (L.d_h_res, T * k * k * 4), (L.d_h_post, T * k * Kr * 4),
+                       (L.d_p, T * k * 4)])
+        for (o1, s1), (o2, _) in zip(offs, offs[1:]):
+            assert o1 % 256 == 0 and o1 + s1 <= o2
+        assert offs[-1][0] + offs[-1][1] <= n == L.total
+    assert lib.backward_workspace_bytes(_cfg(B=0)) == 0
+    assert lib.backward_workspace_bytes(_cfg(N=16, k=3, m=1)) == 0
+    with pytest.raises(binding.XhcError) as e:
+        lib.backward_layout(_cfg(N=16, k=3, m=1))
+    assert e.value.status == binding.XHC_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers: run on a host without a GPU only")
+def test_backward_calls_reject_bad_arguments_before_launch(lib):
+    d = lib.dll
+    ok = _cfg(B=1, S=16).c()
+    attn = _cfg(B=1, S=16, n_convs=0).c()
+    xw = XhcWeights()
+    xw.w_full = xw.w_act = xw.b_pre = xw.b_res = xw.b_post = xw.conv_w = 0x10000
+    X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws = (0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 0x70000,
+                                                      0x80000, 0x90000, 0xa0000)
+    post = d.xhc_post_backward
+
+    def pb(c, w, *a):
+        return post(ctypes.byref(c), ctypes.byref(w), *a, None)
+    args = [X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws]
+    # misaligned, NULL, aliased
+    bad = list(args)
+    bad[4] = 0x60008
+    assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG and "aligned" in lib.last_error()
+    bad = list(args)
+    bad[0] = None
+    assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG
+    bad = list(args)
+    bad[4] = X
+    assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
+    bad = list(args)
+    bad[5] = d_X
+    assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG
+    # MLP-type needs d_conv and the conv kernels; attention-type needs neither
+    bad = list(args)
+    bad[6] = None
+    assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG and "d_conv" in lib.last_error()
+    w = XhcWeights()
+    w.w_full = w.w_act = w.b_pre = w.b_res = w.b_post = 0x10000
+    assert pb(ok, w, *args) == binding.XHC_ERR_INVALID_ARG and "conv_w" in lib.last_error()
+    # unsupported (N, k) and an empty batch
+    assert pb(_cfg(k=3, m=1).c(), xw, *args) == binding.XHC_ERR_UNSUPPORTED
+    e = _cfg(B=0).c()
+    assert pb(e, xw, *([None] * 9)) == binding.XHC_OK
+    # generation half: every gradient pointer, aligned buffers, no aliasing
+    pre = d.xhc_pre_backward
+    g = binding.XhcGrads(0xb0000, 0xc0000, 0xd0000, 0xd1000, 0xd2000, 0xd3000)
+    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, X, ctypes.byref(g), ws, bws, None) == \
+        binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
+    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, 0x60004, ctypes.byref(g), ws, bws, None) == \
+        binding.XHC_ERR_INVALID_ARG and "aligned" in lib.last_error()
+    g2 = binding.XhcGrads(0xb0000, 0xc0000, 0xd0000, 0xd1000, 0xd2000, 0)
+    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, dX, ctypes.byref(g2), ws, bws, None) == \
+        binding.XHC_ERR_INVALID_ARG and "gradient" in lib.last_error()
+    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, dX, None, ws, bws, None) == binding.XHC_ERR_INVALID_ARG
+    assert pre(ctypes.byref(attn), ctypes.byref(xw), X, dX, ctypes.byref(g), bws, bws, None) == \
+        binding.XHC_ERR_INVALID_ARG
