@@ -457,27 +457,49 @@ def _split_calls(rows):
     return calls
 
 
+def _split_backward_calls(rows):
+    """Backward workload: skip the set-up (xhc_pre of each sublayer); a call
+    starts at an application kernel (xhc_post_backward) or at the first
+    weight-packing kernel of a run of them (xhc_pre_backward)."""
+    calls, prev = [], ""
+    for name, v in rows:
+        if "xhc::" not in name or "xhc_pre_fused_kernel" in name or "xhc_prep_kernel" in name:
+            continue
+        start = "bwd_apply_kernel" in name or ("pack_b_kernel" in name and "pack_b_kernel" not in prev)
+        if start or not calls:
+            calls.append([])
+        calls[-1].append((name, v))
+        prev = name
+    return calls
+
+
 def traffic_summary(workload, pmcdir):
     """Writes profiles/<workload>_traffic.json from the four counter runs
-    under pmcdir (chain_fetch, chain_write, copy_fetch, copy_write)."""
+    under pmcdir (chain_fetch, chain_write, copy_fetch, copy_write; for the
+    backward workload the first two hold its runs)."""
     copy_bytes = 1 << 30
     scale = {}
     for c, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
         vals = [v for n, v in _pmc_rows(os.path.join(pmcdir, sub)) if "copyBuffer" in n and v > 1e5]
         scale[c] = copy_bytes / (sum(vals) / len(vals) * 1024)
-    fetch = _split_calls(_pmc_rows(os.path.join(pmcdir, "chain_fetch")))
-    write = _split_calls(_pmc_rows(os.path.join(pmcdir, "chain_write")))
     kind, cfgs, kinds = layer_configs(workload)
-    names = (["xhc_route"] if kind == "xhc" else []) + [
-        f"{p}_{lk}" for lk in kinds for p in (("xhc_pre_chained", "xhc_post_chained") if kind == "xhc"
-                                              else ("mhc_pre", "mhc_post"))]
+    split = _split_backward_calls if kind == "xhcb" else _split_calls
+    fetch = split(_pmc_rows(os.path.join(pmcdir, "chain_fetch")))
+    write = split(_pmc_rows(os.path.join(pmcdir, "chain_write")))
+    if kind == "xhcb":
+        names = [f"{p}_{lk}" for lk in reversed(kinds) for p in ("xhc_post_backward", "xhc_pre_backward")]
+    else:
+        names = (["xhc_route"] if kind == "xhc" else []) + [
+            f"{p}_{lk}" for lk in kinds for p in (("xhc_pre_chained", "xhc_post_chained") if kind == "xhc"
+                                                  else ("mhc_pre", "mhc_post"))]
     if len(fetch) != len(names) or len(write) != len(names):
         raise SystemExit(f"found {len(fetch)} / {len(write)} calls, expected {len(names)}")
     per = {}
     for name, fc, wc in zip(names, fetch, write):
         fb = sum(v for _, v in fc) * 1024 * scale["FETCH_SIZE"]
         wb = sum(v for _, v in wc) * 1024 * scale["WRITE_SIZE"]
-        per.setdefault(name, []).append((fb, wb, [n.split("(")[0] for n, _ in fc]))
+        per.setdefault(name, []).append((fb, wb, [n.replace("(anonymous namespace)::", "").split("(")[0]
+                                                  for n, _ in fc]))
     out = {"workload": workload, "sources_sha256": sources_hash(), "copy_scale": scale, "calls": {}}
     for name, lst in per.items():
         out["calls"][name] = {"fetch_bytes": sum(x[0] for x in lst) / len(lst),

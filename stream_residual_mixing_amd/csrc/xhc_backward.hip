@@ -174,13 +174,21 @@ struct BwdApplyArgs {
 // gradients and the basis gradient as a combination of the dY_i and the g_q.
 // Pass 2 writes dX (non-active rows: d_X + H_pre[n] d_inp; active row j:
 // sum_i H_res[i][j] dY_i + H_pre[I_j] d_inp) and the basis gradient.
+//
+// MLP-type: workgroups are dispatched to the 8 XCDs in turn; workgroup b
+// takes token (b mod 8) * ceil(T / 8) + b / 8, so that each XCD walks a
+// contiguous run of tokens and the 11-row output windows of neighbouring
+// tokens hit its own L2 (attention-type: token b, which measured faster).
 template <class E, int N, int K, int KR>
 __global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
   using T = typename E::T;
   constexpr int V = E::VEC;
   constexpr int NG = KR * (KR + 1) / 2;
   constexpr int O_H = N, O_E = N + K * K, O_G = O_E + K * KR, NACC = O_G + NG;
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int per_xcd = (a.T + 7) / 8;
+  const int t = KR == 4 ? (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  if (t >= a.T) return;   // the whole workgroup: before any barrier
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int C = a.C;
   const int s = t % a.S;
@@ -1135,7 +1143,7 @@ void apply_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const 
   a.C = P.C;
   a.use_mgs = P.use_mgs;
   a.eps_mgs = P.eps_mgs;
-  bwd_apply_kernel<E, N, K, KR><<<(unsigned)P.T, BT, 0, st>>>(a);
+  bwd_apply_kernel<E, N, K, KR><<<(unsigned)(KR == 4 ? 8 * ((P.T + 7) / 8) : P.T), BT, 0, st>>>(a);
   if constexpr (KR == 4) {
     BwdConvArgs c{};
     c.dg = a.dg;
