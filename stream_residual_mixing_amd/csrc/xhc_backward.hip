@@ -1078,7 +1078,9 @@ bool make_bwd_plan(const Plan& P, BwdPlan* B) {
   if (q.nch_a > maxch) q.nch_a = (int)maxch;
   q.TW_f = (int)((P.T + q.nch_f - 1) / q.nch_f);
   q.TW_a = (int)((P.T + q.nch_a - 1) / q.nch_a);
-  q.nch_c = clampi((P.T + 255) / 256, 1, 1 << 20);
+  // conv-transpose token chunks: about 128 tokens each, at most 1024 chunks
+  // (grid.y and the [chunk][24][C] partials stay bounded for any T)
+  q.nch_c = clampi((P.T + 127) / 128, 1, 1024);
   q.TC = (int)((P.T + q.nch_c - 1) / q.nch_c);
   size_t off = 0;
   auto take = [&](size_t bytes) {
