@@ -598,7 +598,7 @@ struct BwdTokArgs {
 
 // Generation half, per-token scalars.  16 lanes per token: lane (a, b) < k^2
 // carries the tangent of the Sinkhorn map along its logit (a, b) and returns
-// that logit's gradient; lane 0 then forms the coefficient rows
+// that logit's gradient; the token's lanes then form the coefficient rows
 //   Gt = [dz / (sigma + eps) | alpha_pre g_pre / rho]   (router | pre-map),
 //   Ga = [alpha_res dL | alpha_post g_post] / rho_a      (active maps),
 // the per-token scalars cx, c0 (full state) and cxa (active rows) of the norm
@@ -687,83 +687,86 @@ __global__ __launch_bounds__(BT) void bwd_token_kernel(BwdTokArgs a) {
     s_dL[tl][l] = dl;
   }
   __syncthreads();
-  if (l != 0 || !valid) return;
-
+  // the rest with the token's 16 lanes: lane l takes stream l (N <= 16) and
+  // active-map entries l (k^2 <= 16, k K_r <= 16); sums over lanes by the
+  // group butterfly, so every lane holds the same scalars
   const float NC = (float)N * (float)a.C;
   float s1 = 0.f, s2 = 0.f;
   for (int ks = 0; ks < a.KS; ++ks) {
-    s1 += a.stats[((size_t)ks * a.T + t) * 2];
-    s2 += a.stats[((size_t)ks * a.T + t) * 2 + 1];
+    s1 += a.stats[((size_t)ks * a.T + tt) * 2];
+    s2 += a.stats[((size_t)ks * a.T + tt) * 2 + 1];
   }
   const float mu = s1 / NC, ms = s2 / NC;
   const float rho = sqrtf(ms + a.eps);
   const float sig = sqrtf(fmaxf(ms - mu * mu, 0.f));
   const float sh = sig + a.eps;
-  float* gt = a.Gt + (size_t)t * 2 * N;
-  float* br = a.brow + (size_t)t * NBT;
-  // pre-map: H_pre = sigmoid(alpha_pre y + b_pre), y = (x W_pre) / rho
-  float sdy = 0.f, apre = 0.f;
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    float raw = 0.f;
-    for (int ks = 0; ks < a.KS; ++ks) raw += a.part[((size_t)ks * a.T + t) * a.NP + N + n];
-    const float y = raw / rho;
-    const float h = a.h_pre[(size_t)t * N + n];
-    const float gp = a.d_hpre[(size_t)t * N + n] * h * (1.f - h);
-    const float dy = a.a_pre * gp;
-    gt[N + n] = dy / rho;
-    sdy = fmaf(dy, y, sdy);
-    apre = fmaf(gp, y, apre);
-    br[n] = gp;
-  }
-  float cx = -sdy / (rho * rho * NC);
+  float* gt = a.Gt + (size_t)tt * 2 * N;
+  float* br = a.brow + (size_t)tt * NBT;
+  float* ga = a.Ga + (size_t)tt * NA;
+  // pre-map: H_pre = sigmoid(alpha_pre y + b_pre), y = (x W_pre) / rho;
   // router: p_i = sigmoid(z_{I_i}) for the routed positions i >= m
-  float dz[N];
-#pragma unroll
-  for (int n = 0; n < N; ++n) dz[n] = 0.f;
-  for (int i = a.m; i < K; ++i) {
-    const int n = a.idx[(size_t)t * K + i];
-    const float pv = a.p[(size_t)t * K + i];
-    const float g = a.d_p[(size_t)t * K + i] * pv * (1.f - pv);
-#pragma unroll
-    for (int q = 0; q < N; ++q)
-      if (q == n) dz[q] += g;
+  float sdy = 0.f, apre = 0.f, sdz = 0.f, cs = 0.f;
+  if (l < N) {
+    const int n = l;
+    float raw = 0.f;
+    for (int ks = 0; ks < a.KS; ++ks) raw += a.part[((size_t)ks * a.T + tt) * a.NP + N + n];
+    const float y = raw / rho;
+    const float h = a.h_pre[(size_t)tt * N + n];
+    const float gp = a.d_hpre[(size_t)tt * N + n] * h * (1.f - h);
+    const float dy = a.a_pre * gp;
+    sdy = dy * y;
+    apre = gp * y;
+    float dz = 0.f;
+    for (int i = a.m; i < K; ++i)
+      if (a.idx[(size_t)tt * K + i] == n) {
+        const float pv = a.p[(size_t)tt * K + i];
+        dz += a.d_p[(size_t)tt * K + i] * pv * (1.f - pv);
+      }
+    sdz = dz * a.z[(size_t)tt * N + n];
+    const float gr = dz / sh;
+    cs = gr * a.colsum[n];
+    if (valid) {
+      gt[N + n] = dy / rho;
+      br[n] = gp;
+      gt[n] = gr;
+      br[NBT - N + n] = mu * gr;
+    }
   }
-  float sdz = 0.f, cs = 0.f;
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    sdz = fmaf(dz[n], a.z[(size_t)t * N + n], sdz);
-    const float gr = dz[n] / sh;
-    gt[n] = gr;
-    cs = fmaf(gr, a.colsum[n], cs);
-    br[NBT - N + n] = mu * gr;
-  }
-  const float cxr = sig > 0.f ? -sdz / (sh * NC * sig) : 0.f;
-  cx += cxr;
-  const float c0 = -cxr * mu - cs / NC;
   // active maps: H_res = rowclamp(SK(alpha_res la_res + b_res)),
   // H_post = 2 sigmoid(alpha_post la_post + b_post), la = (x_a W_act) / rho_a
-  float* ga = a.Ga + (size_t)t * NA;
   float sdl = 0.f, ares = 0.f, apost = 0.f;
-#pragma unroll
-  for (int q = 0; q < KK; ++q) {
-    const float dL = s_dL[tl][q];
+  if (l < KK) {
+    const float dL = s_dL[tl][l];
     const float dla = a.a_res * dL;
-    ga[q] = dla / rhoa;
-    sdl = fmaf(dla, s_la[tl][q], sdl);
-    ares = fmaf(dL, s_la[tl][q], ares);
-    br[N + q] = dL;
+    sdl = dla * s_la[tl][l];
+    ares = dL * s_la[tl][l];
+    if (valid) {
+      ga[l] = dla / rhoa;
+      br[N + l] = dL;
+    }
   }
-#pragma unroll
-  for (int q = 0; q < K * KR; ++q) {
-    const float sg = 0.5f * a.h_post[(size_t)t * K * KR + q];
-    const float gpo = a.d_hpost[(size_t)t * K * KR + q] * 2.f * sg * (1.f - sg);
+  if (l < K * KR) {
+    const float sg = 0.5f * a.h_post[(size_t)tt * K * KR + l];
+    const float gpo = a.d_hpost[(size_t)tt * K * KR + l] * 2.f * sg * (1.f - sg);
     const float dla = a.a_post * gpo;
-    ga[KK + q] = dla / rhoa;
-    sdl = fmaf(dla, s_la[tl][KK + q], sdl);
-    apost = fmaf(gpo, s_la[tl][KK + q], apost);
-    br[N + KK + q] = gpo;
+    sdl = fmaf(dla, s_la[tl][KK + l], sdl);
+    apost = gpo * s_la[tl][KK + l];
+    if (valid) {
+      ga[KK + l] = dla / rhoa;
+      br[N + KK + l] = gpo;
+    }
   }
+  sdy = group_sum<16>(sdy);
+  apre = group_sum<16>(apre);
+  sdz = group_sum<16>(sdz);
+  cs = group_sum<16>(cs);
+  sdl = group_sum<16>(sdl);
+  ares = group_sum<16>(ares);
+  apost = group_sum<16>(apost);
+  if (l != 0 || !valid) return;
+  const float cxr = sig > 0.f ? -sdz / (sh * NC * sig) : 0.f;
+  const float cx = -sdy / (rho * rho * NC) + cxr;
+  const float c0 = -cxr * mu - cs / NC;
   br[N + NA] = apre;
   br[N + NA + 1] = ares;
   br[N + NA + 2] = apost;
