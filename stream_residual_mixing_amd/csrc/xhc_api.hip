@@ -152,6 +152,7 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     q.o_hres = take(T * K * K * 4);
     q.o_hpost = take(T * K * q.KR * 4);
     q.o_z = take(T * N * 4);
+    q.o_gstat = take(T * (N + 2) * 4);
     q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
     q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
     q.o_part = take((size_t)q.ntiles * GM * P1 * 4);

@@ -25,8 +25,9 @@
 //  application:  bwd_apply (per token: dot products, scalar stage, dX rows and
 //                the basis gradient), bwd_conv (MLP-type: transposed convs
 //                into d_out, conv-weight partials), bwd_reduce;
-//  generation:   packing + split-K MFMA projections of X and of the gathered
-//                active rows (recomputing the raw logits and norm sums),
+//  generation:   packing + split-K MFMA projection of the gathered active rows
+//                (recomputing their raw logits and sums; the full state's were
+//                kept by xhc_pre),
 //                bwd_wcolsum, bwd_token (per-token scalars), bwd_sum_rows
 //                (bias / scale gradients), bwd_rows twice (full state, active
 //                rows: dX += W G + c x, weight-gradient partials), bwd_reduce.
@@ -584,9 +585,9 @@ __global__ __launch_bounds__(BT) void bwd_sum_rows_kernel(BwdSumArgs a) {
 }
 
 struct BwdTokArgs {
-  const float *part, *stats;      // full-state raw logits [KS][T][NP], sums [KS][T][2]
+  const float* gstat;             // from xhc_pre, per token: raw pre-map logits [N], sum x, sum x^2
   const float *part_a, *stats_a;  // active-row raw logits [KSa][T][NPA], sums [KSa][T][2]
-  int KS, NP, KSa, NPA;
+  int KSa, NPA;
   const int* idx;
   const float *p, *h_pre, *h_post, *z;
   const float *d_hpre, *d_hres, *d_hpost, *d_p;
@@ -691,11 +692,8 @@ __global__ __launch_bounds__(BT) void bwd_token_kernel(BwdTokArgs a) {
   // active-map entries l (k^2 <= 16, k K_r <= 16); sums over lanes by the
   // group butterfly, so every lane holds the same scalars
   const float NC = (float)N * (float)a.C;
-  float s1 = 0.f, s2 = 0.f;
-  for (int ks = 0; ks < a.KS; ++ks) {
-    s1 += a.stats[((size_t)ks * a.T + tt) * 2];
-    s2 += a.stats[((size_t)ks * a.T + tt) * 2 + 1];
-  }
+  const float* gs = a.gstat + (size_t)tt * (N + 2);
+  const float s1 = gs[N], s2 = gs[N + 1];
   const float mu = s1 / NC, ms = s2 / NC;
   const float rho = sqrtf(ms + a.eps);
   const float sig = sqrtf(fmaxf(ms - mu * mu, 0.f));
@@ -708,9 +706,7 @@ __global__ __launch_bounds__(BT) void bwd_token_kernel(BwdTokArgs a) {
   float sdy = 0.f, apre = 0.f, sdz = 0.f, cs = 0.f;
   if (l < N) {
     const int n = l;
-    float raw = 0.f;
-    for (int ks = 0; ks < a.KS; ++ks) raw += a.part[((size_t)ks * a.T + tt) * a.NP + N + n];
-    const float y = raw / rho;
+    const float y = gs[n] / rho;
     const float h = a.h_pre[(size_t)tt * N + n];
     const float gp = a.d_hpre[(size_t)tt * N + n] * h * (1.f - h);
     const float dy = a.a_pre * gp;
@@ -1065,8 +1061,6 @@ bool make_bwd_plan(const Plan& P, BwdPlan* B) {
   q.nkb_a = q.KC / KB;
   const long nblk_t = (P.T + 63) / 64;
   const long ks = nblk_t > 0 ? (1024 + nblk_t - 1) / nblk_t : 1;
-  q.KS = clampi(ks, 1, 8);
-  if (q.KS > q.nkb_f) q.KS = (int)q.nkb_f;
   q.KSa = clampi(ks, 1, 8);
   if (q.KSa > q.nkb_a) q.KSa = (int)q.nkb_a;
   q.NBT = 2 * P.N + P.K * P.K + P.K * P.KR + 3;
@@ -1098,10 +1092,7 @@ bool make_bwd_plan(const Plan& P, BwdPlan* B) {
   q.o_xa = take(T * K * C * es);
   q.o_dg = KR == 4 ? take(T * 4 * C * 4) : SIZE_MAX;
   q.o_cpart = KR == 4 ? take((size_t)q.nch_c * NCONV * C * 4) : SIZE_MAX;
-  q.o_wpf = take((size_t)q.nkb_f * q.NTF * 64 * 16);
   q.o_wpa = take((size_t)q.nkb_a * q.NTA * 64 * 16);
-  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
-  q.o_stats = take((size_t)q.KS * T * 2 * 4);
   q.o_parta = take((size_t)q.KSa * T * q.NTA * 16 * 4);
   q.o_statsa = take((size_t)q.KSa * T * 2 * 4);
   q.o_gt = take(T * q.ncol_f * 4);
@@ -1190,14 +1181,11 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
                 const char* ws, char* bws, hipStream_t st) {
   const int dt = P.dtype;
   const int T = (int)P.T;
-  float* part = reinterpret_cast<float*>(bws + Bp.o_part);
-  float* stats = reinterpret_cast<float*>(bws + Bp.o_stats);
   float* parta = reinterpret_cast<float*>(bws + Bp.o_parta);
   float* statsa = reinterpret_cast<float*>(bws + Bp.o_statsa);
   const void* xa = bws + Bp.o_xa;
-  launch_pack_b(dt, w->w_full, Bp.nkb_f, Bp.ncol_f, Bp.NTF, bws + Bp.o_wpf, st);
+  // the full-state projection and sums were kept by xhc_pre; the active rows' are recomputed
   launch_pack_b(dt, w->w_act, Bp.nkb_a, Bp.ncol_a, Bp.NTA, bws + Bp.o_wpa, st);
-  launch_projection(dt, Bp.NTF, X, T, Bp.NC, bws + Bp.o_wpf, Bp.nkb_f, Bp.KS, part, stats, st);
   launch_projection(dt, Bp.NTA, xa, T, Bp.KC, bws + Bp.o_wpa, Bp.nkb_a, Bp.KSa, parta, statsa, st);
   float* colsum = reinterpret_cast<float*>(bws + Bp.o_colsum);
   float* cpart = reinterpret_cast<float*>(bws + Bp.o_colpart);
@@ -1205,12 +1193,9 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
                                               N, cpart);
   bwd_reduce_kernel<<<1, BT, 0, st>>>(cpart, NCOLB, N, colsum, nullptr, 1, 0);
   BwdTokArgs a{};
-  a.part = part;
-  a.stats = stats;
+  a.gstat = reinterpret_cast<const float*>(ws + P.o_gstat);
   a.part_a = parta;
   a.stats_a = statsa;
-  a.KS = Bp.KS;
-  a.NP = Bp.NTF * 16;
   a.KSa = Bp.KSa;
   a.NPA = Bp.NTA * 16;
   a.idx = reinterpret_cast<const int*>(ws + P.o_idx);

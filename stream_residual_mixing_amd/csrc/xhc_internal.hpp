@@ -35,7 +35,7 @@ struct Plan {
   long ntiles = 0;                  // xHC pre: 16-token tiles
   // workspace byte offsets
   size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,
-         o_z = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
+         o_z = SIZE_MAX, o_gstat = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
          o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX, o_gemm_ws = SIZE_MAX,
          total = 0;
   size_t gemm_ws_bytes = 0;
@@ -62,6 +62,7 @@ struct XhcPreArgs {
   int* sync;
   int* idx;
   float *p, *h_pre, *h_res, *h_post, *z;
+  float* gstat;   // per token: the raw pre-map logits [N], then sum x, sum x^2 (for a backward)
 };
 
 struct MhcReadArgs {
@@ -103,10 +104,10 @@ struct MhcPostArgs {
 // Backward workspace layout (xhc_backward.hip).
 struct BwdPlan {
   long NC = 0, KC = 0, nkb_f = 0, nkb_a = 0;
-  int ncol_f = 0, ncol_a = 0, NTF = 0, NTA = 0, KS = 1, KSa = 1, NBT = 0;
+  int ncol_f = 0, ncol_a = 0, NTF = 0, NTA = 0, KSa = 1, NBT = 0;
   int nch_f = 1, nch_a = 1, TW_f = 0, TW_a = 0, nch_c = 1, TC = 0;
   size_t o_dhpre = 0, o_dhres = 0, o_dhpost = 0, o_dp = 0, o_xa = 0, o_dg = SIZE_MAX, o_cpart = SIZE_MAX,
-         o_wpf = 0, o_wpa = 0, o_part = 0, o_stats = 0, o_parta = 0, o_statsa = 0, o_gt = 0, o_ga = 0, o_sc = 0,
+         o_wpa = 0, o_parta = 0, o_statsa = 0, o_gt = 0, o_ga = 0, o_sc = 0,
          o_brow = 0, o_bsum = 0, o_colsum = 0, o_colpart = 0, o_wpartf = 0, o_wparta = 0, total = 0;
 };
 bool make_bwd_plan(const Plan& P, BwdPlan* B);

@@ -164,6 +164,15 @@ __global__ __launch_bounds__(NTHR, 4) void xhc_pre_fused_kernel(XhcPreArgs a) {
       route_logits(sm[tau * NPF + i], sm[tau * NPF + N + i], sm[TM * NPF + 2 * tau], sm[TM * NPF + 2 * tau + 1],
                    sm[TM * NPF + 2 * TM + i], n_el, a.eps, a.a_pre, a.b_pre[i], t0 + tau < a.T, &s_z[tau][i],
                    &s_hpre[tau][i]);
+      // kept for a backward: the raw pre-map logit and the token's sums
+      if (t0 + tau < a.T) {
+        float* gs = a.gstat + (size_t)(t0 + tau) * (N + 2);
+        gs[i] = sm[tau * NPF + N + i];
+        if (i == 0) {
+          gs[N] = sm[TM * NPF + 2 * tau];
+          gs[N + 1] = sm[TM * NPF + 2 * tau + 1];
+        }
+      }
     }
     __syncthreads();
     if (tid < TM) {
@@ -385,6 +394,7 @@ static bool xhc_pre_fused_launch(const Plan& P, const void* X, void* inp, const 
   a.h_res = reinterpret_cast<float*>(ws + P.o_hres);
   a.h_post = reinterpret_cast<float*>(ws + P.o_hpost);
   a.z = reinterpret_cast<float*>(ws + P.o_z);
+  a.gstat = reinterpret_cast<float*>(ws + P.o_gstat);
 
   const int nsync = 2 + 3 * P.ntiles;
   const long nfrag = (P.nkb_full * P.NTF + P.nkb_act * P.NTA) * WAVE;
