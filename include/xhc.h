@@ -402,9 +402,10 @@ xhc_status xhcf4_post(const xhc_config* cfg, const xhcf4_weights* w, int32_t q, 
  * Two calls, run in this order with the same backward workspace bws:
  *   xhc_post_backward  the application half (maps held fixed), and
  *   xhc_pre_backward   the generation half (through the maps).
- * Both read what xhc_pre left in ws for the same cfg and X: the maps, and
- * per token the raw pre-map logits and the sums of x and x^2 (kept there by
- * xhc_pre only: the chained calls' workspaces do not hold them).
+ * Both read what the forward left in ws for the same cfg and X: the maps,
+ * and per token the raw pre-map logits and the sums of x and x^2 (kept there
+ * by xhc_pre, and by the chained calls in the workspace of the sublayer
+ * whose routing they finish).
  * ------------------------------------------------------------------------- */
 
 /* Weight gradients (host struct holding device pointers; float, written). */

@@ -129,6 +129,7 @@ struct RouteFinArgs {
   float a_pre, eps;
   int* idx;
   float *p, *h_pre, *z;
+  float* gstat;   // per token: the raw pre-map logits [N], then sum x, sum x^2 (for a backward)
 };
 
 template <int N, int K>
@@ -187,6 +188,12 @@ __global__ __launch_bounds__(256) void xhc_route_fin_kernel(RouteFinArgs a) {
     if (t < a.T) {
       a.z[(size_t)t * N + i] = s_z[tau][i];
       a.h_pre[(size_t)t * N + i] = s_hpre[tau][i];
+      float* gs = a.gstat + (size_t)t * (N + 2);
+      gs[i] = s_sum[tau * NPF + N + i];
+      if (i == 0) {
+        gs[N] = s_sum[TM * NPF + 2 * tau];
+        gs[N + 1] = s_sum[TM * NPF + 2 * tau + 1];
+      }
     }
   }
   if (tid < TM && t0 + tid < a.T) {
@@ -1223,6 +1230,7 @@ void route_fin_launch(const Plan& P, const xhc_weights* w, char* ws, bool with_c
   f.p = reinterpret_cast<float*>(ws + P.o_p);
   f.h_pre = reinterpret_cast<float*>(ws + P.o_hpre);
   f.z = reinterpret_cast<float*>(ws + P.o_z);
+  f.gstat = reinterpret_cast<float*>(ws + P.o_gstat);
   xhc_route_fin_kernel<N, K><<<(unsigned)P.ntiles, 256, 0, st>>>(f);
 }
 

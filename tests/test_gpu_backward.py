@@ -37,12 +37,18 @@ def _print(*a):
     print(*a, flush=True)
 
 
-def run_backward(lib, cfg, X, out, wd, d_inp, d_X):
+def run_backward(lib, cfg, X, out, wd, d_inp, d_X, chained=False):
+    """Forward maps by xhc_pre (or, chained, by xhc_route + xhc_pre_chained
+    as the first sublayer of a chain), then both backward calls."""
     w = weights_to_device(wd)
     Xd, outd = X.cuda(), out.reshape(cfg.T, cfg.C).cuda()
     inp = torch.empty((cfg.T, cfg.C), dtype=cfg.torch_dtype, device="cuda")
     ws = lib.workspace(cfg)
-    lib.xhc_pre(cfg, w, Xd, inp, ws)
+    if chained:
+        lib.xhc_route(cfg, w, Xd, ws)
+        lib.xhc_pre_chained(cfg, w, None, None, Xd, inp, ws, None)
+    else:
+        lib.xhc_pre(cfg, w, Xd, inp, ws)
     maps = {k: v.clone() for k, v in lib.ws_arrays(cfg, ws).items()}
     bws = lib.backward_workspace(cfg)
     dX = torch.empty_like(Xd)
@@ -136,6 +142,25 @@ def test_backward_matches_gradient_oracle(lib, N, k, m, C, B, S, nconv, mgs, dt)
     pre, ga, gg = oracle_backward(cfg, X, out, ow, d_inp, d_X)
     errs = compare(cfg, g, pre, ga, gg)
     _print("  errors", {key: f"{v:.2e}" for key, v in errs.items()})
+    assert errs.pop("I") == 0.0, "active indices differ"
+    bad = {key: v for key, v in errs.items() if not v <= GTOL[dt]}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("nconv,dt", [(3, "bf16"), (0, "f32")])
+def test_backward_after_chained_forward(lib, nconv, dt):
+    """The chained forward calls keep the same per-token sums as xhc_pre in
+    the workspace of the sublayer whose routing they finish, so the backward
+    runs on a chained workspace too."""
+    cfg = Config(N=16, k=4, m=2, C=256, B=2, S=20, n_convs=nconv, dtype=dt)
+    X, out, wd, ow = K.xhc_inputs(cfg, seed=65)
+    r = np.random.default_rng([65, 5])
+    d_inp = synth._round(r.standard_normal((cfg.T, cfg.C)), dt)
+    d_X = synth._round(r.standard_normal((cfg.T, cfg.N, cfg.C)), dt)
+    g = run_backward(lib, cfg, X, out, wd, d_inp, d_X, chained=True)
+    pre, ga, gg = oracle_backward(cfg, X, out, ow, d_inp, d_X)
+    errs = compare(cfg, g, pre, ga, gg)
+    _print("  chained forward, backward errors", {key: f"{v:.2e}" for key, v in errs.items()})
     assert errs.pop("I") == 0.0, "active indices differ"
     bad = {key: v for key, v in errs.items() if not v <= GTOL[dt]}
     assert not bad, bad
