@@ -889,7 +889,6 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
   const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X);
   uint16_t* dX = reinterpret_cast<uint16_t*>(a.dX);
   const int ncol = a.ncol;
-  const int NTC = (ncol + 15) / 16;
   // B fragments of the wave's W rows: lane (g, r) of tile j holds W[row][8g .. 8g + 7]
   uint4 bw[NR];
   bool tile_in[NR];
@@ -983,8 +982,7 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) f.h[e] = s_x[8 * g + e][rl];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m >= NTC) break;
+      for (int m = 0; m < 2; ++m) {   // both column tiles: columns past ncol are zero in LDS
         const uint4 ah = *reinterpret_cast<const uint4*>(&s_gt[0][16 * m + r][8 * g]);
         const uint4 al = *reinterpret_cast<const uint4*>(&s_gt[1][16 * m + r][8 * g]);
         accw[j][m] = Bf16::mma(Bf16::mma(accw[j][m], ah, f.u), al, f.u);

@@ -123,6 +123,9 @@ CASES = [
     (4, 4, 4, 64, 2, 14, 3, 1, "f32"),
     (1, 1, 1, 64, 2, 13, 3, 1, "f32"),
     (16, 4, 0, 128, 5, 5, 3, 1, "f32"),     # no fixed streams; sequences shorter than the longest kernel
+    (16, 4, 2, 256, 2, 21, 3, 0, "bf16"),    # Gram-Schmidt off, bf16
+    (8, 4, 2, 512, 2, 18, 0, 1, "bf16"),
+    (16, 2, 1, 256, 3, 9, 3, 1, "bf16"),
     (16, 4, 2, 64, 1, 1, 3, 1, "bf16"),     # one token
     # the benchmark's channel width, 2 x 160 tokens
     (16, 4, 2, 4096, 2, 160, 3, 1, "bf16"),
