@@ -126,6 +126,9 @@ CASES = [
     (16, 4, 2, 256, 2, 21, 3, 0, "bf16"),    # Gram-Schmidt off, bf16
     (8, 4, 2, 512, 2, 18, 0, 1, "bf16"),
     (16, 2, 1, 256, 3, 9, 3, 1, "bf16"),
+    (4, 4, 4, 128, 2, 15, 3, 1, "bf16"),
+    (1, 1, 1, 64, 2, 13, 0, 1, "bf16"),
+    (16, 2, 1, 96, 2, 11, 0, 1, "bf16"),
     (16, 4, 2, 64, 1, 1, 3, 1, "bf16"),     # one token
     # the benchmark's channel width, 2 x 160 tokens
     (16, 4, 2, 4096, 2, 160, 3, 1, "bf16"),
