@@ -76,6 +76,18 @@ def test_xhc_bf16_ragged(lib, N, k, m, mlp):
     _print("xhc bf16", N, k, m, mlp, K.compare_xhc(g, o, K.TOL["bf16"]))
 
 
+@pytest.mark.parametrize("N,k,m", [(16, 2, 1), (8, 4, 2), (16, 4, 0), (4, 4, 2), (4, 4, 4), (1, 1, 1)])
+@pytest.mark.parametrize("mlp", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_xhc_every_built_shape(lib, N, k, m, mlp, dtype):
+    """Every built (N, k) in both dtypes, attention- and MLP-type, a ragged tile."""
+    cfg = Config(N=N, k=k, m=m, C=192, B=2, S=29, n_convs=3 if mlp else 0, dtype=dtype)
+    X, out, wd, ow = K.xhc_inputs(cfg, seed=110 + N + k + m + mlp)
+    g = K.gpu_xhc(lib, cfg, X, out, wd)
+    o = K.oracle_xhc(cfg, K.f64(X), K.f64(out), ow)
+    _print("xhc shape", N, k, m, mlp, dtype, K.compare_xhc(g, o, K.TOL[dtype]))
+
+
 @pytest.mark.parametrize("B,S", [(3, 13), (5, 1), (1, 130)])
 def test_xhc_sequence_boundaries(lib, B, S):
     """Causal convolutions restart at every sequence start, also inside a tile."""
