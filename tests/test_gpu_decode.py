@@ -60,6 +60,37 @@ def test_decode_step_matches_oracle(lib, dt, C, use_mgs):
     assert np.array_equal(K.f64(rg), ringo)
 
 
+@pytest.mark.parametrize("N,k,m,dt", [(16, 2, 1, "bf16"), (8, 4, 2, "f32"), (4, 4, 4, "bf16"), (1, 1, 1, "f32"),
+                                      (16, 4, 0, "bf16")])
+def test_decode_step_other_shapes(lib, N, k, m, dt):
+    """Every built (N, k): one decode step against the oracle's, the ring
+    bit for bit."""
+    C = 192
+    steps = np.array([0, 5, 11, 12, 29], dtype=np.int32)
+    B = len(steps)
+    cfg = Config(N=N, k=k, m=m, C=C, B=B, S=1, n_convs=3, dtype=dt)
+    _print("decode step", N, k, m, dt)
+    X, out, wd, ow = K.xhc_inputs(cfg, seed=43)
+    ring = synth._round(np.random.default_rng([43, 9]).standard_normal((B, O.RING, C)), dt)
+    pre = O.xhc_pre(K.f64(X), ow["w_full"], ow["w_act"], m, k, 4, (ow["alpha_pre"], ow["alpha_res"], ow["alpha_post"]),
+                    ow["b_pre"], ow["b_res"], ow["b_post"], iters=cfg.iters)
+    Xo, ringo = O.xhc_decode_post(K.f64(X), K.f64(out).reshape(B, C), K.f64(ring), steps, pre["I"], pre["p"],
+                                  pre["h_res"], pre["h_post"], ow["conv"], True)
+    w = weights_to_device(wd)
+    Xd, outd, ringd = X.cuda(), out.reshape(B, C).cuda(), ring.cuda()
+    inp = torch.empty((B, C), dtype=cfg.torch_dtype, device="cuda")
+    ws = lib.workspace(cfg)
+    lib.xhc_pre(cfg, w, Xd, inp, ws)
+    idx = lib.ws_arrays(cfg, ws)["idx"].cpu().numpy()
+    lib.xhc_post_decode(cfg, w, Xd, outd, ringd, torch.from_numpy(steps).cuda(), ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx, pre["I"]), "active indices differ"
+    err = K.rel_err(K.f64(Xd.cpu()), O.round_state(Xo, dt))
+    _print("  state error", f"{err:.2e}")
+    assert err <= K.TOL[dt]
+    assert np.array_equal(K.f64(ringd.cpu()), ringo)
+
+
 def test_decode_sequence_matches_the_prefill(lib):
     """Two sequences of 20 tokens decoded one token at a time (pre + decode
     write per token, the ring carried on the GPU) against the oracle's

@@ -25,6 +25,10 @@ CASES = [
     (4, 4, 2, 256, 1, 37, 3, "bf16"),
     (1, 1, 1, 256, 2, 20, 3, "bf16"),
     (16, 4, 2, 96, 1, 19, 3, "bf16"),
+    (8, 4, 2, 128, 2, 21, 3, "f32"),
+    (4, 4, 4, 128, 1, 29, 3, "f32"),
+    (1, 1, 1, 64, 2, 17, 3, "f32"),
+    (8, 4, 1, 160, 2, 13, 0, "f32"),
 ]
 
 
