@@ -130,6 +130,9 @@ CASES = [
     (1, 1, 1, 64, 2, 13, 0, 1, "bf16"),
     (16, 2, 1, 96, 2, 11, 0, 1, "bf16"),
     (16, 4, 2, 64, 1, 1, 3, 1, "bf16"),     # one token
+    # wide channels: several channel groups per thread, up to the largest C built
+    (16, 4, 2, 8192, 1, 40, 3, 1, "bf16"),
+    (16, 4, 2, 32768, 1, 14, 3, 1, "bf16"),
     # the benchmark's channel width, 2 x 160 tokens
     (16, 4, 2, 4096, 2, 160, 3, 1, "bf16"),
     (16, 4, 2, 4096, 2, 160, 0, 1, "bf16"),
