@@ -175,6 +175,26 @@ def test_backward_after_chained_forward(lib, nconv, dt):
     assert not bad, bad
 
 
+@pytest.mark.parametrize("iters", [0, 1, 3])
+def test_backward_few_sinkhorn_rounds(lib, iters):
+    """With no Sinkhorn round the map is exp(L - max L), whose row holding the
+    largest logit has an entry 1 and positive others: it sums to more than one
+    and the row clamp acts (its divide is differentiated).  With one or three
+    rounds the map is far from doubly stochastic."""
+    cfg = Config(N=16, k=4, m=2, C=128, B=2, S=14, n_convs=3, iters=iters, dtype="f32")
+    X, out, wd, ow = K.xhc_inputs(cfg, seed=66 + iters)
+    r = np.random.default_rng([66, iters])
+    d_inp = synth._round(r.standard_normal((cfg.T, cfg.C)), "f32")
+    d_X = synth._round(r.standard_normal((cfg.T, cfg.N, cfg.C)), "f32")
+    g = run_backward(lib, cfg, X, out, wd, d_inp, d_X)
+    pre, ga, gg = oracle_backward(cfg, X, out, ow, d_inp, d_X)
+    errs = compare(cfg, g, pre, ga, gg)
+    _print("  sinkhorn rounds", iters, {key: f"{v:.2e}" for key, v in errs.items()})
+    assert errs.pop("I") == 0.0, "active indices differ"
+    bad = {key: v for key, v in errs.items() if not v <= GTOL["f32"]}
+    assert not bad, bad
+
+
 def test_backward_in_place_gradient(lib):
     """dX may be the d_X buffer itself: same result as a separate buffer."""
     cfg = Config(N=16, k=4, m=2, C=128, B=1, S=20, n_convs=3, dtype="bf16")

@@ -113,9 +113,9 @@ def test_one_stream_gradients_are_the_plain_residual():
     np.testing.assert_allclose(g["out"].reshape(T, C), d_X[:, 0], rtol=0, atol=1e-15)
 
 
-def _maps(d, m, k, K_r):
+def _maps(d, m, k, K_r, iters=20):
     pre = O.xhc_pre(d["X"], d["W_full"], d["W_act"], m, k, K_r, tuple(d["alpha"]), d["b_pre"], d["b_res"],
-                    d["b_post"], iters=20)
+                    d["b_post"], iters=iters)
     return pre
 
 
@@ -158,24 +158,31 @@ def test_application_half_matches_central_differences(mlp, use_mgs):
         assert abs(fd - lin) <= 1e-7 * max(1.0, abs(fd)), (name, fd, lin)
 
 
-@pytest.mark.parametrize("mlp", [True, False])
-def test_generation_half_matches_central_differences(mlp):
+@pytest.mark.parametrize("mlp,iters", [(True, 20), (False, 20), (True, 0), (False, 2)])
+def test_generation_half_matches_central_differences(mlp, iters):
     """Given map gradients, the loss sum(map * d_map) over the maps of the
     NumPy oracle's xhc_pre, differentiated numerically along random
-    directions in the state, the weights, the biases and the scales."""
-    r = rng(55, int(mlp))
+    directions in the state, the weights, the biases and the scales.  With
+    no Sinkhorn round the row clamp acts (the row holding the largest logit
+    sums to more than one) and its divide is differentiated."""
+    r = rng(55, int(mlp), iters)
     B, S, N, k, m, C = 2, 11, 6, 3, 1, 8
     d = case(r, B, S, N, k, m, C, mlp)
     K_r = 4 if mlp else 1
     T = B * S
-    pre = _maps(d, m, k, K_r)
+    pre = _maps(d, m, k, K_r, iters)
     dm = dict(h_pre=r.standard_normal((T, N)), h_res=r.standard_normal((T, k, k)),
               h_post=r.standard_normal((T, k, K_r)), p=r.standard_normal((T, k)))
     g = G.xhc_gen_grads(d["X"], d["W_full"], d["W_act"], m, k, K_r, tuple(d["alpha"]), d["b_pre"], d["b_res"],
-                        d["b_post"], pre["I"], dm["h_pre"], dm["h_res"], dm["h_post"], dm["p"])
+                        d["b_post"], pre["I"], dm["h_pre"], dm["h_res"], dm["h_post"], dm["p"], iters=iters)
+    if iters == 0:   # the row clamp acts on some rows: that derivative is what this case pins
+        Xa = np.take_along_axis(d["X"], pre["I"][:, :, None], axis=1).reshape(T, -1)
+        la = O.rms_normalize(Xa) @ d["W_act"]
+        L = d["alpha"][1] * la[:, : k * k].reshape(T, k, k) + np.asarray(d["b_res"]).reshape(k, k)
+        assert (O.sinkhorn(L, 0).sum(-1) > 1.0 + 1e-3).any()
 
     def loss(v):
-        q = _maps(v, m, k, K_r)
+        q = _maps(v, m, k, K_r, iters)
         assert np.array_equal(q["I"], pre["I"]), "the active set moved under the perturbation"
         return sum(float(np.sum(q[n] * dm[n])) for n in dm)
 
