@@ -31,21 +31,40 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libxhc)")
 
 
+def _compile(src: str, obj: str) -> subprocess.CompletedProcess:
+    cmd = [hipcc(), *HIPCC_FLAGS, "-c", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libxhc.so (always recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp, *LINK]
+    """Compile libxhc.so (always recompiles) and return its path.  Each source
+    is compiled to its own object in parallel, then the objects are linked."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1))
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+        print(f"hipcc {' '.join(HIPCC_FLAGS)} -c ... ({len(SOURCES)} sources, {jobs} at a time)", flush=True)
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, SOURCES, objs))
     # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
     noise = "is not a recognized feature for this target"
+    errs = []
+    for src, res in zip(SOURCES, results):
+        err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({res.returncode}):\n{err}")
+        if err.strip():
+            errs.append(err)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *objs, "-o", tmp, *LINK]
+    res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{err}")
+    if verbose and (errs or err.strip()):
+        print("\n".join(errs + [err]), file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -157,7 +157,7 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
     q.o_part = take((size_t)q.ntiles * GM * P1 * 4);
     q.o_part2 = take((size_t)q.ntiles * GM * P2 * 4);
-    q.o_gram = take((size_t)q.nslices * T * 10 * 4);
+    q.o_gram = take((size_t)q.nslices * T * 10 * 8);
     q.o_corr = take((size_t)q.ntiles * GM * P1 * 4);
   }
   q.total = q.T == 0 ? 0 : off;
@@ -221,7 +221,7 @@ xhc_status make_flash_plan(const xhc_config* cfg, xhc::Plan* P) {
   q.o_stats = take((size_t)q.KS * T * 2 * 4);
   const size_t P2 = 16 * (size_t)(q.NTA > 1 ? q.NTA : 1) * 16 + 16;
   q.o_part2 = take((size_t)q.ntiles * q.G2 * P2 * 4);
-  q.o_gram = take((size_t)q.nslices * T * 10 * 4);
+  q.o_gram = take((size_t)q.nslices * T * 10 * 8);
   q.total = q.T == 0 ? 0 : off;
   *P = q;
   return XHC_OK;
@@ -258,7 +258,7 @@ xhc_status make_flash4_plan(const xhc_config* cfg, xhc::Plan* P) {
   q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
   q.o_stats = take((size_t)q.KS * T * 2 * 4);
   q.o_part2 = take((size_t)q.ntiles * q.G2 * (16 * (size_t)ntmax * 16 + 16) * 4);
-  q.o_gram = take((size_t)q.nslices * T * 10 * 4);
+  q.o_gram = take((size_t)q.nslices * T * 10 * 8);
   q.total = q.T == 0 ? 0 : off;
   *P = q;
   return XHC_OK;

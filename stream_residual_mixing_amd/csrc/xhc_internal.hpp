@@ -87,7 +87,7 @@ struct XhcPostArgs {
   const float* conv_w;
   int use_mgs;
   float eps_mgs;
-  float* gram;
+  double* gram;   // Gram partials [nslices][T][10]
   // xHC-Flash attention write only: the MLP base readout [T][C] (updated in
   // place) and the MLP pre-map [T][N]
   void* inp_m = nullptr;

@@ -175,6 +175,48 @@ __device__ __forceinline__ float wave_sum16(const float (&v)[16], int lane) {
   x += dpp_f<DPP_QUAD_XOR1, 0xf>(x);
   return x;
 }
+// The same reduce-scatter on doubles: every lane move above is a fixed
+// permutation of 32-bit lanes, so applying it to the low and the high halves
+// of a double moves the double as a whole.
+__device__ __forceinline__ uint32_t lo32(double x) { return (uint32_t)__double2loint(x); }
+__device__ __forceinline__ uint32_t hi32(double x) { return (uint32_t)__double2hiint(x); }
+__device__ __forceinline__ double mk_d(uint32_t lo, uint32_t hi) { return __hiloint2double((int)hi, (int)lo); }
+template <int CTRL, int BANKS>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo32(x), CTRL, 0xf, BANKS, false);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi32(x), CTRL, 0xf, BANKS, false);
+  return mk_d(l, h);
+}
+
+__device__ __forceinline__ double wave_sum16_d(const double (&v)[16], int lane) {
+  double a[8], b[4], c[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto rl = __builtin_amdgcn_permlane32_swap(lo32(v[i]), lo32(v[8 + i]), false, false);
+    const auto rh = __builtin_amdgcn_permlane32_swap(hi32(v[i]), hi32(v[8 + i]), false, false);
+    a[i] = mk_d(rl[0], rh[0]) + mk_d(rl[1], rh[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto rl = __builtin_amdgcn_permlane16_swap(lo32(a[i]), lo32(a[4 + i]), false, false);
+    const auto rh = __builtin_amdgcn_permlane16_swap(hi32(a[i]), hi32(a[4 + i]), false, false);
+    b[i] = mk_d(rl[0], rh[0]) + mk_d(rl[1], rh[1]);
+  }
+  const bool u8 = (lane & 8) != 0, u4 = (lane & 4) != 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const double lo = b[i] + dpp_d<DPP_ROW_SHL8, 0x3>(b[i]);
+    const double hi = b[2 + i] + dpp_d<DPP_ROW_SHR8, 0xc>(b[2 + i]);
+    c[i] = u8 ? hi : lo;
+  }
+  const double lo = c[0] + dpp_d<DPP_ROW_SHL4, 0x5>(c[0]);
+  const double hi = c[1] + dpp_d<DPP_ROW_SHR4, 0xa>(c[1]);
+  double x = u4 ? hi : lo;
+  x += dpp_d<DPP_QUAD_XOR2, 0xf>(x);
+  x += dpp_d<DPP_QUAD_XOR1, 0xf>(x);
+  return x;
+}
+
 __device__ __forceinline__ int wave_sum16_index(int lane) {
   return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
 }
@@ -182,39 +224,55 @@ __device__ __forceinline__ int wave_sum16_index(int lane) {
 // Modified Gram-Schmidt on coefficient vectors: v_j = sum_a Tm[j][a] basis_a,
 // with <x, y> = x^T G y (G = Gram matrix of the basis).  The same sequence
 // of projections and the same eps as on the vectors themselves (summary
-// 3.3), so the result is exact in real arithmetic.
-__device__ __forceinline__ void mgs_from_gram(const float (&G)[4][4], float eps, float (&Tm)[4][4]) {
+// 3.3), so the result is exact in real arithmetic.  Done in double, on a
+// Gram matrix accumulated in double from exact products of the float basis:
+// with nearly parallel branches the coefficients are large and cancel, and
+// float Gram entries would lose the residuals.
+__device__ __forceinline__ void mgs_from_gram(const double (&G)[4][4], double eps, double (&Tm)[4][4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.f : 0.f;
+    for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.0 : 0.0;
 #pragma unroll
   for (int j = 1; j < 4; ++j) {
-    float u[4];
+    double u[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) u[b] = (j == b) ? 1.f : 0.f;
+    for (int b = 0; b < 4; ++b) u[b] = (j == b) ? 1.0 : 0.0;
 #pragma unroll
     for (int i = 0; i < j; ++i) {
-      float Gt[4];
+      double Gt[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        float s = 0.f;
+        double s = 0.0;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) s = fmaf(G[x][y], Tm[i][y], s);
+        for (int y = 0; y < 4; ++y) s = fma(G[x][y], Tm[i][y], s);
         Gt[x] = s;
       }
-      float num = 0.f, den = 0.f;
+      double num = 0.0, den = 0.0;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        num = fmaf(u[x], Gt[x], num);
-        den = fmaf(Tm[i][x], Gt[x], den);
+        num = fma(u[x], Gt[x], num);
+        den = fma(Tm[i][x], Gt[x], den);
       }
-      const float cf = num / (den + eps);
+      const double cf = num / (den + eps);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) u[x] = fmaf(-cf, Tm[i][x], u[x]);
+      for (int x = 0; x < 4; ++x) u[x] = fma(-cf, Tm[i][x], u[x]);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) Tm[j][b] = u[b];
+  }
+}
+
+// The per-token write coefficients Q[j][b] = p_j sum_r H_post[j][r] Tm[r][b]
+// (Tm the Gram-Schmidt map, identity without it), in double, rounded once.
+template <int KR>
+__device__ __forceinline__ void write_coeffs(const double (&Tm)[4][4], const float* hpo, float pj, float* q) {
+#pragma unroll
+  for (int b = 0; b < KR; ++b) {
+    double s = 0.0;
+#pragma unroll
+    for (int r = 0; r < KR; ++r) s = fma((double)hpo[r], Tm[r][b], s);
+    q[b] = (float)((double)pj * s);
   }
 }
 
@@ -236,7 +294,7 @@ __global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
   const int t0 = blockIdx.x * PT;
   const int t1 = min(t0 + PT, a.T);
   const T* __restrict__ out = reinterpret_cast<const T*>(a.out);
-  __shared__ float s_g[PT][4][10];
+  __shared__ double s_g[PT][4][10];
 
   float w1[4][4], w2[8][4], w3[12][4];
   load_conv_weights(a.conv_w, a.C, cc, act, w1, w2, w3);
@@ -264,20 +322,21 @@ __global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
         s = s + 1 == a.S ? 0 : s + 1;
         float b[4][4];
         conv_basis<q>(h, w1, w2, w3, b);
-        float pr[16];
+        // products of floats are exact in double
+        double pr[16];
         int k = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int v = u; v < 4; ++v) {
-            float d = 0.f;
+            double d = 0.0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) d = fmaf(b[u][e], b[v][e], d);
+            for (int e = 0; e < 4; ++e) d = fma((double)b[u][e], (double)b[v][e], d);
             pr[k++] = d;
           }
 #pragma unroll
-        for (int j = 10; j < 16; ++j) pr[j] = 0.f;
-        const float tot = wave_sum16(pr, lane);
+        for (int j = 10; j < 16; ++j) pr[j] = 0.0;
+        const double tot = wave_sum16_d(pr, lane);
         if ((lane & 3) == 0 && myidx < 10) s_g[t - t0][wave][myidx] = tot;
       }
     });
@@ -320,26 +379,26 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
   // per-token coefficients: Q = diag(p) H_post Tm (Tm = Gram-Schmidt map)
   for (int tau = tid; tau < t1 - t0; tau += 256) {
     const int t = t0 + tau;
-    float Tm[4][4];
+    double Tm[4][4];
     if (KR == 4 && a.use_mgs) {
-      float pg[10];
+      double pg[10];
 #pragma unroll
-      for (int j = 0; j < 10; ++j) pg[j] = 0.f;
+      for (int j = 0; j < 10; ++j) pg[j] = 0.0;
       for (int sl = 0; sl < a.nslices; ++sl)
 #pragma unroll
         for (int j = 0; j < 10; ++j) pg[j] += a.gram[((size_t)sl * a.T + t) * 10 + j];
-      float G[4][4];
+      double G[4][4];
       int q = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int v = u; v < 4; ++v) { G[u][v] = pg[q]; G[v][u] = pg[q]; ++q; }
-      mgs_from_gram(G, a.eps_mgs, Tm);
+      mgs_from_gram(G, (double)a.eps_mgs, Tm);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.f : 0.f;
+        for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.0 : 0.0;
     }
     float acorr = 0.f;
 #pragma unroll
@@ -354,13 +413,7 @@ __global__ __launch_bounds__(256) void xhc_apply_kernel(XhcPostArgs a) {
 #pragma unroll
       for (int r = 0; r < KR; ++r) hpo[r] = a.h_post[((size_t)t * K + j) * KR + r];
       if constexpr (FL) acorr = fmaf(a.h_pre_m[(size_t)t * a.N + ij] * pj, hpo[0], acorr);
-#pragma unroll
-      for (int b = 0; b < KR; ++b) {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < KR; ++r) s = fmaf(hpo[r], Tm[r][b], s);
-        s_Q[tau][j][b] = pj * s;
-      }
+      write_coeffs<KR>(Tm, hpo, pj, &s_Q[tau][j][0]);
     }
     if constexpr (FL) s_A[tau] = acorr;
   }
@@ -492,7 +545,7 @@ __global__ __launch_bounds__(256) void xhc_decode_post_kernel(DecodeArgs a) {
   using T = typename E::T;
   using Qd = Quad<E>;
   static_assert(KR == 1 || KR == 4, "write components");
-  __shared__ float s_g[4][10];
+  __shared__ double s_g[4][10];
   __shared__ float s_Q[K][KR];
   __shared__ float s_H[K][K];
   __shared__ int s_I[K];
@@ -538,9 +591,9 @@ __global__ __launch_bounds__(256) void xhc_decode_post_kernel(DecodeArgs a) {
 
   // pass 1: Gram matrix of the basis over all channels (fixed-order sums)
   if (KR == 4 && a.use_mgs) {
-    float gr[10];
+    double gr[10];
 #pragma unroll
-    for (int j = 0; j < 10; ++j) gr[j] = 0.f;
+    for (int j = 0; j < 10; ++j) gr[j] = 0.0;
     for (int c = tid * PCH; c < C; c += 256 * PCH) {
       float b[KR][4];
       basis(c, b);
@@ -549,39 +602,41 @@ __global__ __launch_bounds__(256) void xhc_decode_post_kernel(DecodeArgs a) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int w = u; w < 4; ++w) {
-          float d = 0.f;
+          double d = 0.0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) d = fmaf(b[u][e], b[w][e], d);
+          for (int e = 0; e < 4; ++e) d = fma((double)b[u][e], (double)b[w][e], d);   // exact products
           gr[q++] += d;
         }
     }
 #pragma unroll
     for (int j = 0; j < 10; ++j) {
-      const float v = wave_sum(gr[j]);
+      double v = gr[j];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
       if (lane == 0) s_g[wave][j] = v;
     }
   }
   __syncthreads();
   if (tid == 0) {
-    float Tm[4][4];
+    double Tm[4][4];
     if (KR == 4 && a.use_mgs) {
-      float G[4][4];
+      double G[4][4];
       int q = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int w = u; w < 4; ++w) {
-          const float v = (s_g[0][q] + s_g[1][q]) + (s_g[2][q] + s_g[3][q]);
+          const double v = (s_g[0][q] + s_g[1][q]) + (s_g[2][q] + s_g[3][q]);
           G[u][w] = v;
           G[w][u] = v;
           ++q;
         }
-      mgs_from_gram(G, a.eps_mgs, Tm);
+      mgs_from_gram(G, (double)a.eps_mgs, Tm);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.f : 0.f;
+        for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.0 : 0.0;
     }
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -590,13 +645,10 @@ __global__ __launch_bounds__(256) void xhc_decode_post_kernel(DecodeArgs a) {
       const float pj = a.p[(size_t)t * K + j];
 #pragma unroll
       for (int i = 0; i < K; ++i) s_H[j][i] = a.h_res[((size_t)t * K + j) * K + i];
+      float hpo[KR];
 #pragma unroll
-      for (int b = 0; b < KR; ++b) {
-        float sum = 0.f;
-#pragma unroll
-        for (int r = 0; r < KR; ++r) sum = fmaf(a.h_post[((size_t)t * K + j) * KR + r], Tm[r][b], sum);
-        s_Q[j][b] = pj * sum;
-      }
+      for (int r = 0; r < KR; ++r) hpo[r] = a.h_post[((size_t)t * K + j) * KR + r];
+      write_coeffs<KR>(Tm, hpo, pj, &s_Q[j][0]);
     }
   }
   __syncthreads();
@@ -650,7 +702,8 @@ static void launch_apply(const XhcPostArgs& a, hipStream_t st) {
 }
 
 template <class E>
-static bool xhc_post_launch(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
+static bool xhc_post_launch(const Plan& P, void* X, const void* out, const xhc_weights* w, const char* ws,
+                            double* gram, hipStream_t st) {
   XhcPostArgs a;
   a.X = X; a.out = out; a.T = (int)P.T; a.S = P.S; a.C = P.C; a.N = P.N; a.nslices = P.nslices;
   a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
@@ -658,7 +711,7 @@ static bool xhc_post_launch(const Plan& P, void* X, const void* out, const xhc_w
   a.h_res = reinterpret_cast<const float*>(ws + P.o_hres);
   a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
   a.conv_w = w->conv_w; a.use_mgs = P.use_mgs; a.eps_mgs = P.eps_mgs;
-  a.gram = reinterpret_cast<float*>(ws + P.o_gram);
+  a.gram = gram;
   if (P.KR == 1 && ((P.T + PT - 1) / PT) * P.nslices < 512) {
     // too few 64-token blocks to fill the device: one workgroup per token
     DecodeArgs d;
@@ -733,7 +786,7 @@ static bool unmixed_launch(const Plan& P, int KR, void* X, const void* out, cons
   a.h_res = nullptr;
   a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
   a.conv_w = conv_w; a.use_mgs = P.use_mgs; a.eps_mgs = P.eps_mgs;
-  a.gram = reinterpret_cast<float*>(ws + P.o_gram);
+  a.gram = reinterpret_cast<double*>(ws + P.o_gram);
   if (KR == 4 && P.use_mgs) {
     dim3 grid((a.T + PT - 1) / PT, a.nslices);
     xhc_gram_kernel<E><<<grid, 256, 0, st>>>(a);
@@ -754,8 +807,9 @@ bool launch_unmixed_write(const Plan& P, int KR, void* X, const void* out, const
 }
 
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
-  return P.dtype == XHC_BF16 ? xhc_post_launch<Bf16>(P, X, out, w, ws, st)
-                             : xhc_post_launch<F32>(P, X, out, w, ws, st);
+  double* gram = reinterpret_cast<double*>(ws + P.o_gram);
+  return P.dtype == XHC_BF16 ? xhc_post_launch<Bf16>(P, X, out, w, ws, gram, st)
+                             : xhc_post_launch<F32>(P, X, out, w, ws, gram, st);
 }
 
 }  // namespace xhc

@@ -18,6 +18,9 @@ rounded once to its storage dtype by PyTorch on the CPU.  Keys:
 * xHC-Flash-4sub group g: full-state projection [seed, 2, g], post-maps of
   sublayers 1-3 [seed, 8, 3g + q], final MLP maps [seed, 3, g], the two MLPs'
   kernels [seed, 4 + j, 2g + i]; its four outputs are layers 4g .. 4g + 3
+* per-token scale and offset of a state row (token t, attempt a), when asked
+  for: [seed, 10, t, a]
+* biases away from zero, layer l, bias b (0 pre, 1 res, 2 post): [seed, 12, l, b]
 
 Distributions (the workloads' own): X, out ~ N(0, 1); projection weights
 ~ N(0, 0.02); conv kernel of size kappa ~ N(0, 1/kappa) (second argument
@@ -49,13 +52,21 @@ def as_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def state_rows(seed, tokens, N, C, dtype, attempts=None) -> torch.Tensor:
-    """State rows [len(tokens), N, C] in the storage dtype (CPU)."""
+def state_rows(seed, tokens, N, C, dtype, attempts=None, affine=False) -> torch.Tensor:
+    """State rows [len(tokens), N, C] in the storage dtype (CPU).
+
+    With ``affine``, token t's row is s_t (Z + o_t) with s_t = 10^u,
+    u ~ U(-1, 1), and o_t ~ U(-4, 4): rows of very different scales whose
+    mean sits up to four standard deviations away from zero."""
     tokens = list(tokens)
     attempts = attempts or {}
     a = np.empty((len(tokens), N * C))
     for r, t in enumerate(tokens):
-        a[r] = _draw((seed, 0, 0, int(t), int(attempts.get(int(t), 0))), N * C)
+        at = int(attempts.get(int(t), 0))
+        a[r] = _draw((seed, 0, 0, int(t), at), N * C)
+        if affine:
+            u, o = np.random.default_rng([seed, 10, int(t), at]).uniform(-1.0, 1.0, 2)
+            a[r] = (10.0 ** u) * (a[r] + 4.0 * o)
     return _round(a, dtype).reshape(len(tokens), N, C)
 
 
@@ -74,10 +85,10 @@ def _fill_rows(dst, T, chunk, make):
     return dst
 
 
-def state(seed, T, N, C, dtype, attempts=None, chunk=256) -> torch.Tensor:
+def state(seed, T, N, C, dtype, attempts=None, chunk=256, affine=False) -> torch.Tensor:
     """Full state [T, N, C] in the storage dtype (CPU), built row by row."""
     X = torch.empty((T, N, C), dtype=DTYPES[dtype])
-    return _fill_rows(X, T, chunk, lambda t0, t1: state_rows(seed, range(t0, t1), N, C, dtype, attempts))
+    return _fill_rows(X, T, chunk, lambda t0, t1: state_rows(seed, range(t0, t1), N, C, dtype, attempts, affine))
 
 
 def out_rows(seed, layer, tokens, C, dtype) -> torch.Tensor:
@@ -157,3 +168,61 @@ def xhcf4_group_weights(seed, group, N, k, C, K_r, dtype, kernels=(4, 8, 12)):
                                                           torch.zeros(k * K_r)],
         b_res=torch.zeros(k * k), alpha_pre=(ALPHA,) * 4, alpha_post=(ALPHA,) * 4, alpha_res=ALPHA,
     )
+
+
+# ------------------------------------------------------------------------
+# Settings that move the maps away from the uniform ones.  At the workloads'
+# own draw (alpha = 0.01, biases 0) every map sits close to its value at
+# zero logits (H_res near the uniform matrix), where one Sinkhorn round and
+# twenty give nearly the same result.  These draws use unit scales, biases
+# ~ N(0, 1) and a residual bias with a strong diagonal, so that the number of
+# rounds, their order and the row clamp all change the maps.
+
+def _biases(seed, layer, n_pre, n_res, n_post, k_res, diag):
+    b_pre = _draw((seed, 12, layer, 0), n_pre)
+    b_res = _draw((seed, 12, layer, 1), n_res) + diag * np.eye(k_res).ravel()
+    b_post = _draw((seed, 12, layer, 2), n_post)
+    return (torch.from_numpy(b_pre).float(), torch.from_numpy(b_res).float(), torch.from_numpy(b_post).float())
+
+
+def conv_kernels_lag0(seed, layer, C, kernels=(4, 8, 12), std=0.05):
+    """Kernels whose lag-0 tap is 1 and whose other taps are small
+    (~ N(0, std)): each convolution branch is then nearly parallel to the
+    sublayer output itself, which is where Gram-Schmidt has the most to do."""
+    ks = []
+    for j, kap in enumerate(kernels):
+        w = _draw((seed, 4 + j, layer), (kap, C), std)
+        w[0] += 1.0
+        ks.append(_round(w, "f32"))
+    return ks
+
+
+def conv_kernels_zero(C, kernels=(4, 8, 12)):
+    """All-zero kernels (the temporal branches switched off)."""
+    return [torch.zeros((kap, C), dtype=torch.float32) for kap in kernels]
+
+
+def xhc_stress_weights(seed, layer, N, k, C, K_r, dtype, alpha_res=1.0, conv="draw", diag=3.0,
+                       kernels=(4, 8, 12)):
+    """An xHC sublayer's weights with unit pre/post scales, residual scale
+    ``alpha_res``, biases ~ N(0, 1) (the residual one plus ``diag`` on its
+    diagonal) and conv kernels drawn as usual ("draw"), all zero ("zero") or
+    lag-0 dominated ("lag0")."""
+    wd = xhc_layer_weights(seed, layer, N, k, C, K_r, dtype, kernels)
+    b_pre, b_res, b_post = _biases(seed, layer, N, k * k, k * K_r, k, diag)
+    wd.update(b_pre=b_pre, b_res=b_res, b_post=b_post, alpha_pre=1.0, alpha_res=float(alpha_res), alpha_post=1.0)
+    if K_r > 1 and conv == "zero":
+        wd["conv"] = conv_kernels_zero(C, kernels)
+    elif K_r > 1 and conv == "lag0":
+        wd["conv"] = conv_kernels_lag0(seed, layer, C, kernels)
+    return wd
+
+
+def mhc_stress_weights(seed, layer, N, C, dtype, alpha_res=1.0, diag=3.0):
+    """An mHC sublayer's weights with unit pre/post scales, residual scale
+    ``alpha_res`` and biases ~ N(0, 1) (the residual one plus ``diag`` on its
+    diagonal)."""
+    wd = mhc_layer_weights(seed, layer, N, C, dtype)
+    b_pre, b_res, b_post = _biases(seed, layer, N, N * N, N, N, diag)
+    wd.update(b_pre=b_pre, b_res=b_res, b_post=b_post, alpha_pre=1.0, alpha_res=float(alpha_res), alpha_post=1.0)
+    return wd

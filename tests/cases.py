@@ -21,17 +21,51 @@ MARGIN = 1e-4   # top-k logit margin below which a token is redrawn
 WINDOW = 12     # a token plus the longest conv kernel's 11 lags
 
 
-def rel_err(g, r, floor=1e-2):
+def _floor_den(r, floor, per_token=True):
+    """max(|r|, floor * RMS), the RMS taken over each token's values (the
+    first axis indexes tokens), so that tokens of very different scales are
+    each measured against their own scale; over the whole array when
+    ``per_token`` is false (sums over tokens, such as weight gradients)."""
+    if per_token and r.ndim >= 2:
+        rms = np.sqrt(np.mean(r.reshape(r.shape[0], -1) ** 2, axis=1)).reshape((-1,) + (1,) * (r.ndim - 1))
+    else:
+        rms = np.sqrt(np.mean(r * r))
+    den = np.maximum(np.abs(r), floor * rms)
+    return np.where(den == 0, 1.0, den)
+
+
+def rel_err(g, r, floor=1e-2, per_token=True):
     """max_e |g - r| / max(|r|, floor * RMS(r)): relative error with a floor
-    so that elements near zero are measured against the array's scale."""
+    so that elements near zero are measured against their token's scale."""
     g = np.asarray(g, np.float64)
     r = np.asarray(r, np.float64)
     if r.size == 0:
         return 0.0
-    rms = float(np.sqrt(np.mean(r * r)))
-    den = np.maximum(np.abs(r), floor * rms)
-    den = np.where(den == 0, 1.0, den)
-    return float(np.max(np.abs(g - r) / den))
+    return float(np.max(np.abs(g.reshape(r.shape) - r) / _floor_den(r, floor, per_token)))
+
+
+def term_err(g, r, S, allow=0.0, floor=1e-2):
+    """max_e (|g - r| - allow) / max(S, floor * RMS of the token's r), where S
+    is the sum of the magnitudes of the terms that make up r (oracle values:
+    for a mix sum_i H_i x_i + write, sum_i |H_i x_i| + |write|).  Floating-
+    point sums are accurate relative to the size of their terms; a mix that
+    cancels to a small result cannot be more accurate than that, in any
+    order of summation.  S >= |r|, so without cancellation this is rel_err."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    if r.size == 0:
+        return 0.0
+    S = np.asarray(S, np.float64)
+    den = np.maximum(S, _floor_den(r, floor) if r.ndim else 1.0)
+    return float(np.max(np.maximum(np.abs(g.reshape(r.shape) - r) - allow, 0.0) / den))
+
+
+def logit_err(g, r):
+    """Router logits: max_e |g - r| / max(|r|, RMS of the token's logits).
+    Each logit sums N*C products; it ranks streams and, through sigmoid,
+    gates them, so it is measured on the scale of its token's logits (a
+    logit near zero carries no relative accuracy of its own)."""
+    return rel_err(g, r, floor=1.0)
 
 
 # --------------------------------------------------------------------- oracle
@@ -48,17 +82,36 @@ def oracle_weights(wd):
 
 
 def oracle_xhc(cfg: Config, X64, out64, ow, dtype=None):
-    """Oracle xHC sublayer.  X64 [T,N,C]; out64 [B,S,C]."""
-    return O.xhc_sublayer(X64, out64, ow["w_full"], ow["w_act"], cfg.m, cfg.k, ow["conv"],
-                          (ow["alpha_pre"], ow["alpha_res"], ow["alpha_post"]),
-                          ow["b_pre"], ow["b_res"], ow["b_post"], iters=cfg.iters,
-                          use_mgs=bool(cfg.use_mgs), dtype=dtype or cfg.dtype)
+    """Oracle xHC sublayer.  X64 [T,N,C]; out64 [B,S,C].  Besides the
+    oracle's results, the scales S_inp and S_X of term_err (from oracle
+    values)."""
+    r = O.xhc_sublayer(X64, out64, ow["w_full"], ow["w_act"], cfg.m, cfg.k, ow["conv"],
+                       (ow["alpha_pre"], ow["alpha_res"], ow["alpha_post"]),
+                       ow["b_pre"], ow["b_res"], ow["b_post"], iters=cfg.iters,
+                       use_mgs=bool(cfg.use_mgs), dtype=dtype or cfg.dtype)
+    X = np.asarray(X64, np.float64)
+    T, N, C = X.shape
+    V = O.xhc_write_basis(out64, ow["conv"], bool(cfg.use_mgs)).reshape(T, -1, C)     # [T, K_r, C]
+    Xa = np.take_along_axis(X, r["I"][:, :, None], axis=1)                          # [T, k, C]
+    sa = (np.einsum("tji,tic->tjc", np.abs(r["h_res"]), np.abs(Xa))
+          + np.einsum("tjr,trc->tjc", np.abs(r["p"][:, :, None] * r["h_post"]), np.abs(V)))
+    S_X = np.abs(X).copy()
+    np.put_along_axis(S_X, r["I"][:, :, None], sa, axis=1)
+    r["S_X"] = S_X
+    r["S_inp"] = np.einsum("tn,tnc->tc", np.abs(r["h_pre"]), np.abs(X))
+    return r
 
 
 def oracle_mhc(cfg: Config, X64, out64, ow, dtype=None):
-    return O.mhc_sublayer(X64, out64.reshape(-1, cfg.C), ow["w_full"],
-                          (ow["alpha_pre"], ow["alpha_post"], ow["alpha_res"]),
-                          ow["b_pre"], ow["b_post"], ow["b_res"], iters=cfg.iters, dtype=dtype or cfg.dtype)
+    r = O.mhc_sublayer(X64, out64.reshape(-1, cfg.C), ow["w_full"],
+                       (ow["alpha_pre"], ow["alpha_post"], ow["alpha_res"]),
+                       ow["b_pre"], ow["b_post"], ow["b_res"], iters=cfg.iters, dtype=dtype or cfg.dtype)
+    X = np.asarray(X64, np.float64)
+    out = np.asarray(out64, np.float64).reshape(-1, cfg.C)
+    r["S_X"] = (np.einsum("tij,tjc->tic", np.abs(r["h_res"]), np.abs(X))
+                + np.abs(r["h_post"])[:, :, None] * np.abs(out)[:, None, :])
+    r["S_inp"] = np.einsum("tn,tnc->tc", np.abs(r["h_pre"]), np.abs(X))
+    return r
 
 
 def margins(cfg: Config, X64, ow):
@@ -66,28 +119,33 @@ def margins(cfg: Config, X64, ow):
     return O.xhc_topk_margin(z, cfg.m, cfg.k)
 
 
-def xhc_inputs(cfg: Config, seed, layer=0, resample=True):
+def xhc_inputs(cfg: Config, seed, layer=0, resample=True, weights=None, affine=False, margin=MARGIN):
     """Seeded X, out and weights for an xHC case; tokens whose routing
-    margin (oracle logits) is below MARGIN are redrawn."""
-    wd = synth.xhc_layer_weights(seed, layer, cfg.N, cfg.k, cfg.C, cfg.K_r, cfg.dtype)
+    margin (oracle logits) is below ``margin`` are redrawn.  ``weights``
+    replaces the workloads' own weight draw (a function of seed, layer, N, k,
+    C, K_r and dtype, as synth.xhc_layer_weights); ``affine`` gives every
+    state row its own scale and offset."""
+    make = weights or synth.xhc_layer_weights
+    wd = make(seed, layer, cfg.N, cfg.k, cfg.C, cfg.K_r, cfg.dtype)
     ow = oracle_weights(wd)
     attempts = {}
-    X = synth.state(seed, cfg.T, cfg.N, cfg.C, cfg.dtype)
+    X = synth.state(seed, cfg.T, cfg.N, cfg.C, cfg.dtype, affine=affine)
     if resample:
         for _ in range(20):
-            bad = np.nonzero(margins(cfg, f64(X), ow) < MARGIN)[0]
+            bad = np.nonzero(margins(cfg, f64(X), ow) < margin)[0]
             if bad.size == 0:
                 break
             for t in bad:
                 attempts[int(t)] = attempts.get(int(t), 0) + 1
-            X[bad] = synth.state_rows(seed, bad, cfg.N, cfg.C, cfg.dtype, attempts)
+            X[bad] = synth.state_rows(seed, bad, cfg.N, cfg.C, cfg.dtype, attempts, affine)
     out = synth.sublayer_out(seed, layer, cfg.B, cfg.S, cfg.C, cfg.dtype)
     return X, out, wd, ow
 
 
-def mhc_inputs(cfg: Config, seed, layer=0):
-    wd = synth.mhc_layer_weights(seed, layer, cfg.N, cfg.C, cfg.dtype)
-    X = synth.state(seed, cfg.T, cfg.N, cfg.C, cfg.dtype)
+def mhc_inputs(cfg: Config, seed, layer=0, weights=None, affine=False):
+    make = weights or synth.mhc_layer_weights
+    wd = make(seed, layer, cfg.N, cfg.C, cfg.dtype)
+    X = synth.state(seed, cfg.T, cfg.N, cfg.C, cfg.dtype, affine=affine)
     out = synth.sublayer_out(seed, layer, cfg.B, cfg.S, cfg.C, cfg.dtype)
     return X, out, wd, oracle_weights(wd)
 
@@ -148,17 +206,19 @@ def oracle_chain(cfgs, X64, outs64, ows):
     return res
 
 
-def xhc_chain_inputs(cfgs, seed, margin):
+def xhc_chain_inputs(cfgs, seed, margin, weights=None, affine=False):
     """Seeded state, per-layer outputs and weights of a chain; tokens whose
     routing margin is below `margin` at any layer of the oracle chain are
-    redrawn (each state row has its own generator key)."""
+    redrawn (each state row has its own generator key).  ``weights`` and
+    ``affine`` as in xhc_inputs."""
     c0 = cfgs[0]
-    wds = [synth.xhc_layer_weights(seed, l, c.N, c.k, c.C, c.K_r, c.dtype) for l, c in enumerate(cfgs)]
+    make = weights or synth.xhc_layer_weights
+    wds = [make(seed, l, c.N, c.k, c.C, c.K_r, c.dtype) for l, c in enumerate(cfgs)]
     ows = [oracle_weights(wd) for wd in wds]
     outs = [synth.sublayer_out(seed, l, c.B, c.S, c.C, c.dtype) for l, c in enumerate(cfgs)]
     outs64 = [f64(o) for o in outs]
     attempts = {}
-    X = synth.state(seed, c0.T, c0.N, c0.C, c0.dtype)
+    X = synth.state(seed, c0.T, c0.N, c0.C, c0.dtype, affine=affine)
     for _ in range(30):
         ref = oracle_chain(cfgs, f64(X), outs64, ows)
         bad = set()
@@ -169,7 +229,7 @@ def xhc_chain_inputs(cfgs, seed, margin):
         bad = sorted(bad)
         for t in bad:
             attempts[t] = attempts.get(t, 0) + 1
-        X[bad] = synth.state_rows(seed, bad, c0.N, c0.C, c0.dtype, attempts)
+        X[bad] = synth.state_rows(seed, bad, c0.N, c0.C, c0.dtype, attempts, affine)
     raise AssertionError("could not draw a chain with the required routing margins")
 
 
@@ -196,26 +256,90 @@ def gpu_xhc_chain(lib, cfgs, X, outs, wds, stream=None):
     return res
 
 
-def compare_carried(g, o, l, dtype):
+def ulp_round(x, dtype):
+    """What two correct roundings of nearly the same value to the state dtype
+    can differ by: one unit in the last place at |x|, taken in the binade
+    above when |x| lies within a unit of it (zero where x is zero)."""
+    x = np.abs(np.asarray(x, np.float64))
+    u = ulp(x * (1.0 + (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23)), dtype)
+    return np.where(x == 0, 0.0, u)
+
+
+def carried_allowances(hist, dtype, ows=None):
+    """Allowances for a chain whose sides each carry their own rounded state.
+
+    ``hist`` holds the oracle's results of layers 0..l in order (I [T,k],
+    h_pre [T,N], inp [T,C], X [T,N,C] after the layer, z [T,N], h_post
+    [T,k,K_r]); ``ows`` the oracle weights of each layer (for the router).
+    Both sides start from the same state.  A layer copies the rows it does
+    not write bit for bit, so their difference is what it was; it writes an
+    active row as a mix of the active rows with non-negative weights summing
+    to at most one plus the write, computes that in float32 and rounds it to
+    the state dtype.  So the difference of row i after layer l is at most
+    A_l[i]: A_{-1} = 0; A_l[i] = A_{l-1}[i] outside the active list;
+    A_l[I_j] = sum_i H_res[j][i] A_{l-1}[I_i] + u inside it, where u
+    is one rounding (two correct roundings differ by one unit, ulp_round) plus
+    the float32 error of the k + K_r products of the mix and the write,
+    (k + K_r + 2) 2^-24 times the largest magnitude they involve (the active
+    rows before and after the layer at that channel).
+    The sublayer input of layer l is allowed one unit of itself plus
+    sum_i H_pre[i] A_{l-1}[i].  The router logits of layer l, z = LN(vec X) W_r,
+    move to first order by at most (sum_j A_j |W_jn| + mean(A) |sum_j W_jn|)/sd
+    + |z_n| RMS(A)/sd (the numerator, the mean and the standard deviation sd
+    of the state entering the layer each shifted by the state's difference).
+    Computed from oracle values only; any other arithmetic difference must
+    stay within the relative bar.  Returns per layer a dict of allowances for
+    inp, X and z."""
+    out = []
+    A = None
+    Xprev = None
+    for l, r in enumerate(hist):
+        I = np.asarray(r["I"], np.int64)
+        Xl = np.asarray(r["X"], np.float64)
+        T, N, C = Xl.shape
+        k = I.shape[1]
+        K_r = np.asarray(r["h_post"]).reshape(T, k, -1).shape[2]
+        if A is None:
+            A = np.zeros(Xl.shape)
+        a_inp = ulp_round(r["inp"], dtype) + np.einsum("tn,tnc->tc", np.asarray(r["h_pre"], np.float64), A)
+        a_z = np.zeros((T, N))
+        if ows is not None and Xprev is not None and np.any(A):
+            Wr = np.asarray(ows[l]["w_full"], np.float64)[:, :N]
+            xf = Xprev.reshape(T, N * C)
+            sd = np.sqrt(np.mean((xf - xf.mean(axis=1, keepdims=True)) ** 2, axis=1))
+            Af = A.reshape(T, N * C)
+            num = Af @ np.abs(Wr) + Af.mean(axis=1)[:, None] * np.abs(Wr.sum(axis=0))[None, :]
+            a_z = (num + np.abs(np.asarray(r["z"], np.float64)) * np.sqrt(np.mean(Af * Af, axis=1))[:, None]) / sd[:, None]
+        Aact = np.take_along_axis(A, I[:, :, None], axis=1)                      # [T, k, C]
+        prev = np.einsum("tji,tic->tjc", np.asarray(r["h_res"], np.float64), Aact)   # [T, k, C]
+        before = Xprev if Xprev is not None else None
+        rows = np.take_along_axis(Xl, I[:, :, None], axis=1)                     # [T, k, C]
+        mag = np.abs(rows).max(axis=1)
+        if before is not None:
+            mag = np.maximum(mag, np.abs(np.take_along_axis(before, I[:, :, None], axis=1)).max(axis=1))
+        arith = (k + K_r + 2) * 2.0 ** -24 * mag                                  # [T, C]
+        A = A.copy()
+        newA = prev + ulp_round(rows, dtype) + arith[:, None, :]
+        np.put_along_axis(A, I[:, :, None], newA, axis=1)
+        out.append(dict(inp=a_inp, X=A, z=a_z))
+        Xprev = Xl
+    return out
+
+
+def compare_carried(g, o, l, dtype, allow):
     """Layer l >= 1 of a chain, where each side carries its own rounded state:
-    exact indices, per-element maps, and the state and sublayer input within a
-    normwise bound of (l + 1) steps per token.  One step is what a layer can
-    add to the difference of the two sides: in bf16 their roundings of an
-    element differ by at most one unit in the last place (2^-7 relative); in
-    fp32 the arithmetic dominates, sums of at most 2^10 terms at 2^-24 each
-    (2^-14).  The k x k mix has non-negative rows summing to at most one, so
-    it does not amplify a max-norm difference, and the maps' own inputs are
-    scaled by alpha = 0.01."""
-    assert np.array_equal(g["idx"].numpy(), o["I"]), "active indices differ"
+    exact indices, per-element maps, and per-element router logits (on their
+    token's scale, logit_err), sublayer input and state (term_err) after the
+    allowances of carried_allowances (oracle values only), all at the bar of
+    the dtype."""
+    assert np.array_equal(g["idx"].numpy(), o["I"]), f"layer {l}: active indices differ"
     errs = {key: rel_err(g[key].numpy().astype(np.float64), o[key]) for key in ("h_pre", "h_res", "h_post", "p")}
-    bound = (l + 1) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -14)
-    for key in ("inp", "X"):
-        d = (f64(g[key]) - o[key]).reshape(len(o[key]), -1)
-        r = o[key].reshape(len(o[key]), -1)
-        errs[key + "_norm"] = float(np.max(np.linalg.norm(d, axis=1) / np.linalg.norm(r, axis=1)))
-    bad = {key: v for key, v in errs.items() if key in ("h_pre", "h_res", "h_post", "p") and not v <= TOL[dtype]}
-    bad.update({key: v for key, v in errs.items() if key.endswith("_norm") and not v <= bound})
-    assert not bad, f"layer {l}: above bound (maps {TOL[dtype]}, state {bound:.3g}): {bad} (all: {errs})"
+    if "z" in g:
+        errs["z"] = err_with_allowance(g["z"].numpy().astype(np.float64), o["z"], allow["z"], floor=1.0)
+    errs["inp"] = term_err(f64(g["inp"]), o["inp"], o["S_inp"], allow["inp"])
+    errs["X"] = term_err(f64(g["X"]), o["X"], o["S_X"], allow["X"])
+    bad = {key: v for key, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, f"layer {l}: above {TOL[dtype]}: {bad} (all: {errs})"
     return errs
 
 
@@ -250,15 +374,15 @@ def gpu_mhc(lib, cfg: Config, X, out, wd, stream=None):
 
 
 def compare_xhc(g, o, tol, tokens=None):
-    """Errors per quantity; indices must match exactly."""
+    """Errors per quantity; indices must match exactly.  inp and X in the
+    term_err measure, the maps in rel_err."""
     sel = slice(None) if tokens is None else tokens
     gi = g["idx"].numpy()[sel]
     assert np.array_equal(gi, o["I"][sel] if tokens is None else o["I"]), "active indices differ"
     errs = {}
-    for key, okey in (("inp", "inp"), ("X", "X"), ("h_pre", "h_pre"), ("h_res", "h_res"),
-                      ("h_post", "h_post"), ("p", "p")):
+    for key in ("inp", "X", "h_pre", "h_res", "h_post", "p"):
         gv = f64(g[key])[sel] if key in ("inp", "X") else g[key].numpy().astype(np.float64)[sel]
-        errs[key] = rel_err(gv, o[okey])
+        errs[key] = term_err(gv, o[key], o["S_" + key]) if key in ("inp", "X") else rel_err(gv, o[key])
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"errors above {tol}: {bad} (all: {errs})"
     return errs
@@ -269,7 +393,7 @@ def compare_mhc(g, o, tol, tokens=None):
     errs = {}
     for key in ("inp", "X", "h_pre", "h_res", "h_post"):
         gv = f64(g[key])[sel] if key in ("inp", "X") else g[key].numpy().astype(np.float64)[sel]
-        errs[key] = rel_err(gv, o[key])
+        errs[key] = term_err(gv, o[key], o["S_" + key]) if key in ("inp", "X") else rel_err(gv, o[key])
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"errors above {tol}: {bad} (all: {errs})"
     return errs
@@ -362,10 +486,7 @@ def corrected_input_err(g, r, base, dtype, floor=1e-2):
     large against the result.  The allowance uses the oracle's base only."""
     g = np.asarray(g, np.float64)
     r = np.asarray(r, np.float64)
-    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
-    den = np.maximum(np.abs(r), floor * rms)
-    den = np.where(den == 0, 1.0, den)
-    return float(np.max(np.maximum(np.abs(g - r) - ulp(base, dtype), 0.0) / den)) if r.size else 0.0
+    return float(np.max(np.maximum(np.abs(g - r) - ulp(base, dtype), 0.0) / _floor_den(r, floor))) if r.size else 0.0
 
 
 def mixed_state_err(g, r, X1, I, dtype, floor=1e-2):
@@ -379,10 +500,7 @@ def mixed_state_err(g, r, X1, I, dtype, floor=1e-2):
     r = np.asarray(r, np.float64)
     big = np.take_along_axis(np.abs(np.asarray(X1, np.float64)), np.asarray(I)[:, :, None], axis=1).max(axis=1)
     allow = ulp(big, dtype)[:, None, :]
-    rms = float(np.sqrt(np.mean(r * r)))
-    den = np.maximum(np.abs(r), floor * rms)
-    den = np.where(den == 0, 1.0, den)
-    return float(np.max(np.maximum(np.abs(g - r) - allow, 0.0) / den))
+    return float(np.max(np.maximum(np.abs(g - r) - allow, 0.0) / _floor_den(r, floor)))
 
 
 def compare_flash(g, o, tol, tokens=None, dtype="bf16"):
@@ -467,14 +585,13 @@ def gpu_flash4(lib, cfg: Config, X, outs, wd, stream=None):
     return res
 
 
-def err_with_allowance(g, r, allow, floor=1e-2):
+def err_with_allowance(g, r, allow, floor=1e-2, per_token=True):
     """Relative error (floored as in rel_err) after an absolute allowance."""
     g = np.asarray(g, np.float64)
     r = np.asarray(r, np.float64)
-    rms = float(np.sqrt(np.mean(r * r)))
-    den = np.maximum(np.abs(r), floor * rms)
-    den = np.where(den == 0, 1.0, den)
-    return float(np.max(np.maximum(np.abs(g - r) - allow, 0.0) / den))
+    if r.size == 0:
+        return 0.0
+    return float(np.max(np.maximum(np.abs(g.reshape(r.shape) - r) - allow, 0.0) / _floor_den(r, floor, per_token)))
 
 
 def compare_flash4(g, o, tol, dtype):

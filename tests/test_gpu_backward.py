@@ -99,15 +99,15 @@ def compare(cfg, g, pre, ga, gg):
         "d_p": K.rel_err(K.f64(g["d_p"]), ga["p"]),
         "dX": dx_err(cfg, g["X"], ga, gg),
         "d_out": K.rel_err(K.f64(g["out"]), ga["out"].reshape(cfg.T, cfg.C)),
-        "dW_full": K.rel_err(K.f64(g["W_full"]), gg["W_full"]),
-        "dW_act": K.rel_err(K.f64(g["W_act"]), gg["W_act"]),
-        "d_b_pre": K.rel_err(K.f64(g["b_pre"]), gg["b_pre"]),
-        "d_b_res": K.rel_err(K.f64(g["b_res"]), gg["b_res"]),
-        "d_b_post": K.rel_err(K.f64(g["b_post"]), gg["b_post"]),
-        "d_alpha": K.rel_err(K.f64(g["alpha"]), gg["alpha"]),
+        "dW_full": K.rel_err(K.f64(g["W_full"]), gg["W_full"], per_token=False),
+        "dW_act": K.rel_err(K.f64(g["W_act"]), gg["W_act"], per_token=False),
+        "d_b_pre": K.rel_err(K.f64(g["b_pre"]), gg["b_pre"], per_token=False),
+        "d_b_res": K.rel_err(K.f64(g["b_res"]), gg["b_res"], per_token=False),
+        "d_b_post": K.rel_err(K.f64(g["b_post"]), gg["b_post"], per_token=False),
+        "d_alpha": K.rel_err(K.f64(g["alpha"]), gg["alpha"], per_token=False),
     }
     if "convs" in g:
-        errs["d_conv"] = K.rel_err(K.f64(g["convs"]), np.concatenate(ga["convs"], axis=0))
+        errs["d_conv"] = K.rel_err(K.f64(g["convs"]), np.concatenate(ga["convs"], axis=0), per_token=False)
     return errs
 
 

@@ -26,13 +26,11 @@ layer uses 1e-4).
 
 Chain tolerance: the first layer sees identical inputs on both sides and is
 held to the per-element bar of the small cases.  From then on each side
-carries its own rounded state.  Per layer, the two sides' rounding of an
-element differs by at most one bf16 ulp (at most 2^-7 of its magnitude),
-the k x k mix has non-negative rows summing to at most one so it does not
-amplify a max-norm difference, and the maps' own inputs are scaled by
-alpha = 0.01 so they barely move; after layer l (from 0) the per-token
-normwise relative difference of inp and of the state is therefore bounded by
-(l + 1) 2^-7.  Indices stay exact and the maps keep the per-element bar.
+carries its own rounded state, and the state and sublayer input get, per
+element, the rounding allowance of cases.carried_allowances (from the
+oracle's values of the sampled token at every earlier layer).  Indices stay
+exact; the maps and the router logits keep the per-element bar at every
+layer.
 """
 import numpy as np
 import pytest
@@ -121,6 +119,9 @@ def run_xhc_layers(lib, N, k, m, C, B, S, kinds, seed, margin, n_random, api="si
     stream = torch.cuda.current_stream()
     toks_d = torch.from_numpy(toks).to("cuda")
     wdev = [weights_to_device(wd) for wd in wds]
+    okeys = ("I", "inp", "X", "h_pre", "h_res", "h_post", "p", "z", "S_inp", "S_X")
+    hist = [{key: np.stack([ref[int(t)][l][key] for t in toks]) for key in okeys} for l in range(len(cfgs))]
+    allow = K.carried_allowances(hist, "bf16", ows)
     if api == "chained":
         lib.xhc_route(cfgs[0], wdev[0], X, wsp[0], stream)
     worst = {}
@@ -147,9 +148,13 @@ def run_xhc_layers(lib, N, k, m, C, B, S, kinds, seed, margin, n_random, api="si
         g = {key: v.index_select(0, toks_d).cpu() for key, v in arr.items()}
         g["inp"] = inp.index_select(0, toks_d).cpu()
         g["X"] = X.index_select(0, toks_d).cpu()
-        o = {key: np.stack([ref[int(t)][l][key] for t in toks])
-             for key in ("I", "inp", "X", "h_pre", "h_res", "h_post", "p")}
-        errs = K.compare_xhc(g, o, K.TOL["bf16"]) if l == 0 else K.compare_carried(g, o, l, "bf16")
+        o = hist[l]
+        if l == 0:
+            errs = K.compare_xhc(g, o, K.TOL["bf16"])
+            errs["z"] = K.logit_err(g["z"].numpy().astype(np.float64), o["z"])
+            assert errs["z"] <= K.TOL["bf16"], f"router logits {errs['z']}"
+        else:
+            errs = K.compare_carried(g, o, l, "bf16", allow[l])
         for key, v in errs.items():
             worst[key] = max(worst.get(key, 0.0), v)
         _print("   ", {key: f"{v:.1e}" for key, v in errs.items()})
