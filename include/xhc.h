@@ -149,6 +149,22 @@ xhc_status xhc_pre(const xhc_config* cfg, const xhc_weights* w,
 xhc_status xhc_post(const xhc_config* cfg, const xhc_weights* w,
                     void* X, const void* out, void* ws, xhc_stream_t stream);
 
+/* xhc_post for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same write, bit for bit, with the workspace read only.  The only memory
+ * the write needs beyond X, out and the maps in ws, the Gram partials of an
+ * MLP-type write with Gram-Schmidt (80 * ceil(C / 1024) * T bytes), lives in
+ * an array inside the library: XHC_NOALLOC_SCRATCH_BYTES bytes per GPU, held
+ * from the first call on that GPU until the process ends.  A call that would
+ * need more returns XHC_ERR_INVALID_ARG and launches nothing.  The call
+ * allocates nothing.  Calls that overlap on one GPU share that array and
+ * race: order them (one stream, or events).
+ * X: [T][N][C] (in place); out: [T][C]; ws: the workspace filled by xhc_pre
+ * (read only). */
+#define XHC_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+xhc_status xhc_post_noalloc(const xhc_config* cfg, const xhc_weights* w,
+                            void* X, const void* out, const void* ws, xhc_stream_t stream);
+
 /* mHC before the sublayer: H_pre, H_post, H_res (Sinkhorn, no clamp) from
  * RMSNorm(vec X), and inp = sum_i H_pre[i] X_i.
  * (xHC paper, "Manifold-Constrained HC"; summary 3.1.) */

@@ -25,7 +25,7 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 # Exported symbols, in the order include/xhc.h declares them.
 EXPORTS = (
     "xhc_workspace_bytes", "mhc_workspace_bytes", "xhc_workspace_layout", "mhc_workspace_layout",
-    "xhc_pre", "xhc_post", "mhc_pre", "mhc_post", "xhc_route", "xhc_pre_chained", "xhc_post_chained",
+    "xhc_pre", "xhc_post", "xhc_post_noalloc", "mhc_pre", "mhc_post", "xhc_route", "xhc_pre_chained", "xhc_post_chained",
     "xhc_post_decode", "xhcf_workspace_bytes", "xhcf_workspace_layout", "xhcf_pre", "xhcf_mid", "xhcf_post",
     "xhcf4_workspace_bytes", "xhcf4_workspace_layout", "xhcf4_pre", "xhcf4_post",
     "xhc_backward_workspace_bytes", "xhc_backward_workspace_layout", "xhc_post_backward", "xhc_pre_backward",
@@ -254,7 +254,7 @@ class Lib:
         for fn in (d.xhc_workspace_layout, d.mhc_workspace_layout):
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWsLayout)]
-        for fn in (d.xhc_pre, d.xhc_post, d.mhc_pre, d.mhc_post):
+        for fn in (d.xhc_pre, d.xhc_post, d.xhc_post_noalloc, d.mhc_pre, d.mhc_post):
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.c_void_p,
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -381,6 +381,14 @@ class Lib:
         c, cw = cfg.c(), w.c()
         self._ok(self.dll.xhc_post(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
                                    ws.data_ptr(), _stream_ptr(stream)))
+
+    def xhc_post_noalloc(self, cfg: Config, w: Weights, X, out, ws, stream=None):
+        """xhc_post with the workspace read only and the library's own scratch."""
+        self._check_common(cfg, w, X, ws, False, False)
+        _check_out(out, cfg)
+        c, cw = cfg.c(), w.c()
+        self._ok(self.dll.xhc_post_noalloc(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
+                                           ws.data_ptr(), _stream_ptr(stream)))
 
     # chained sublayers: routing of sublayer l+1 prepared while sublayer l runs
     def xhc_route(self, cfg: Config, w: Weights, X, ws, stream=None):

@@ -419,6 +419,31 @@ xhc_status xhc_post(const xhc_config* cfg, const xhc_weights* w, void* X, const 
   return post_common(cfg, w, X, out, ws, stream, false);
 }
 
+xhc_status xhc_post_noalloc(const xhc_config* cfg, const xhc_weights* w, void* X, const void* out, const void* ws,
+                            xhc_stream_t stream) {
+  xhc::Plan P;
+  xhc_status s = make_plan(cfg, false, &P);
+  if (s != XHC_OK) return s;
+  if ((s = check_weights(P, w, false)) != XHC_OK) return s;
+  const size_t need = xhc::post_scratch_bytes(P);
+  if (need > XHC_NOALLOC_SCRATCH_BYTES)
+    return fail(XHC_ERR_INVALID_ARG,
+                "xhc_post_noalloc: this write needs %zu bytes of scratch (T=%ld, C=%d), more than the library's %zu",
+                need, P.T, P.C, (size_t)XHC_NOALLOC_SCRATCH_BYTES);
+  if (P.T == 0) return XHC_OK;
+  if (!X || !out || !ws) return fail(XHC_ERR_INVALID_ARG, "X, out and ws must not be NULL");
+  if (!aligned16(X) || !aligned16(out) || !aligned16(ws))
+    return fail(XHC_ERR_INVALID_ARG, "X, out and ws must be 16-byte aligned");
+  if (X == out || X == ws || out == ws) return fail(XHC_ERR_INVALID_ARG, "X, out and ws must not alias");
+  double* sp = nullptr;
+  const hipError_t e = xhc::noalloc_scratch(&sp);
+  if (e != hipSuccess) return fail(XHC_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!xhc::launch_xhc_post_noalloc(P, X, out, w, static_cast<const char*>(ws), sp, st))
+    return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
 xhc_status mhc_pre(const xhc_config* cfg, const xhc_weights* w, const void* X, void* inp, void* ws,
                    xhc_stream_t stream) {
   return pre_common(cfg, w, X, inp, ws, stream, true);

@@ -123,6 +123,12 @@ extern thread_local const char* g_launch_failure;
 
 bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st);
+// The write without allocation: Gram partials in the library's own per-device
+// array (post_scratch_bytes of it), whose address noalloc_scratch returns.
+size_t post_scratch_bytes(const Plan& P);
+hipError_t noalloc_scratch(double** out);
+bool launch_xhc_post_noalloc(const Plan& P, void* X, const void* out, const xhc_weights* w, const char* ws,
+                             double* scratch_ptr, hipStream_t st);
 bool launch_mhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_mhc_post(const Plan& P, void* X, const void* out, char* ws, hipStream_t st);
 

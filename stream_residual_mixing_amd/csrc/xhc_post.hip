@@ -25,6 +25,7 @@
 // channels in registers and slides along the tokens of its block, so `out`
 // is read once per pass (plus an 11-row history at the start of a block).
 // Attention-type sublayers (K_r = 1) skip the first pass.
+#include <mutex>
 #include <type_traits>
 
 #include "xhc_device.hpp"
@@ -810,6 +811,51 @@ bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights*
   double* gram = reinterpret_cast<double*>(ws + P.o_gram);
   return P.dtype == XHC_BF16 ? xhc_post_launch<Bf16>(P, X, out, w, ws, gram, st)
                              : xhc_post_launch<F32>(P, X, out, w, ws, gram, st);
+}
+
+size_t post_scratch_bytes(const Plan& P) {
+  return (P.KR == 4 && P.use_mgs) ? (size_t)P.nslices * (size_t)P.T * 10 * sizeof(double) : 0;
+}
+
+}  // namespace xhc
+
+// ---------------------------------------------------------------------------
+// The write without allocation (xhc_post_noalloc): the Gram partials, the only
+// memory the write needs beyond its inputs and outputs, live in this array,
+// one copy per GPU (each device that runs the library holds its own until the
+// process ends).  Calls that overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) double scratch[XHC_NOALLOC_SCRATCH_BYTES / sizeof(double)];
+
+namespace xhc {
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+}  // namespace
+
+// This device's address of `scratch`, looked up once per device with the
+// device current.  Host code uses only this address, never the symbol itself.
+hipError_t noalloc_scratch(double** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<double*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
+
+bool launch_xhc_post_noalloc(const Plan& P, void* X, const void* out, const xhc_weights* w, const char* ws,
+                             double* scratch_ptr, hipStream_t st) {
+  return P.dtype == XHC_BF16 ? xhc_post_launch<Bf16>(P, X, out, w, ws, scratch_ptr, st)
+                             : xhc_post_launch<F32>(P, X, out, w, ws, scratch_ptr, st);
 }
 
 }  // namespace xhc

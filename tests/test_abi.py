@@ -316,3 +316,23 @@ def test_backward_calls_reject_bad_arguments_before_launch(lib):
     assert pre(ctypes.byref(ok), ctypes.byref(xw), X, dX, None, ws, bws, None) == binding.XHC_ERR_INVALID_ARG
     assert pre(ctypes.byref(attn), ctypes.byref(xw), X, dX, ctypes.byref(g), bws, bws, None) == \
         binding.XHC_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers: run on a host without a GPU only")
+def test_noalloc_write_refuses_what_its_scratch_cannot_hold(lib):
+    """xhc_post_noalloc: an MLP-type write with Gram-Schmidt needs
+    80 * ceil(C / 1024) * T bytes of scratch; above the library's array it is
+    refused on the host, with nothing launched; the attention type needs none."""
+    w = XhcWeights()
+    w.w_full = w.w_act = w.b_pre = w.b_res = w.b_post = w.conv_w = 0x10000
+    fit = _cfg(C=4096, B=1, S=(8 << 20) // 320)
+    over = _cfg(C=4096, B=1, S=(8 << 20) // 320 + 1)
+    assert 80 * 4 * fit.T <= 8 << 20 < 80 * 4 * over.T
+    rc = lib.dll.xhc_post_noalloc(ctypes.byref(over.c()), ctypes.byref(w), 0x20000, 0x30000, 0x40000, None)
+    assert rc == binding.XHC_ERR_INVALID_ARG and "scratch" in lib.last_error()
+    nomgs = _cfg(C=4096, B=1, S=(8 << 20) // 320 + 1, use_mgs=0)
+    rc = lib.dll.xhc_post_noalloc(ctypes.byref(nomgs.c()), ctypes.byref(w), 0x20001, 0x30000, 0x40000, None)
+    assert rc == binding.XHC_ERR_INVALID_ARG and "aligned" in lib.last_error()   # past the scratch check
+    attn = _cfg(C=4096, B=1, S=(8 << 20) // 320 + 1, n_convs=0)
+    rc = lib.dll.xhc_post_noalloc(ctypes.byref(attn.c()), ctypes.byref(w), 0x20000, 0x20000, 0x40000, None)
+    assert rc == binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()     # past the scratch check
