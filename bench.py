@@ -541,6 +541,35 @@ def copy_probe(nbytes=1 << 30, reps=10):
                       "avg_us": round(dt * 1e6, 2)}), flush=True)
 
 
+def read_probe(nbytes=2 << 30, reps=10):
+    """Read-only streams over a state-sized buffer (2 GiB, the chain's state):
+    16-byte loads spread over the device with the default cache policy and
+    with non-temporal loads (libxhc's xhc_probe_read), next to the copy
+    probe.  The achievable rates the layer's kernels are compared with."""
+    import torch
+    from stream_residual_mixing_amd import binding
+    lib = binding.load()
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {"read_probe_bytes": nbytes}
+    for mode, name in ((0, "read_GBps"), (1, "read_nontemporal_GBps")):
+        for _ in range(3):
+            lib.probe_read(src, sink, mode, stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            lib.probe_read(src, sink, mode, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        dt = a.elapsed_time(b) * 1e-3 / reps
+        res[name] = round(nbytes / dt / 1e9, 1)
+        res[name.replace("GBps", "avg_us")] = round(dt * 1e6, 2)
+    print(json.dumps(res), flush=True)
+    copy_probe()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +579,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true", help="time a 1 GiB device copy and exit")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="time read-only streams over a 2 GiB buffer (and the copy probe) and exit")
     ap.add_argument("--traffic-summary", metavar="PMCDIR", default=None,
                     help="write profiles/<workload>_traffic.json from rocprofv3 counter runs and exit")
     ap.add_argument("--api", choices=("chained", "single", "flash", "flash4", "decode", "backward"), default=None,
@@ -570,6 +601,9 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.read_probe:
+        read_probe()
         return
     api = args.api or default_api(args.workload)
     r = run_gpu(args.workload, args.steps, args.warmup, api)

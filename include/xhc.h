@@ -36,8 +36,10 @@
  *     full-state projection weight.
  *   - Every pointer in these calls is a device pointer unless it is the
  *     config or weights struct itself (host memory, read during the call).
- *   - The caller owns every buffer.  The library allocates nothing on the
- *     GPU and keeps no state between calls.
+ *   - The caller owns every buffer.  No call allocates memory.  Between
+ *     calls the library keeps only cached device properties (the number of
+ *     compute units) and, once xhc_post_noalloc has run on a device, the
+ *     address of that device's scratch array.
  *   - Calls are asynchronous on `stream` and stream-ordered: *_pre, then F,
  *     then *_post on the same workspace.  Calls that share a workspace must
  *     not overlap.
@@ -472,6 +474,15 @@ xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const v
                             const xhc_grads* g, const void* ws, void* bws, xhc_stream_t stream);
 
 /* Message for the last non-OK status returned on this host thread. */
+/* Measurement helper, not part of the layer: reads `bytes` bytes at `src`
+ * (device memory, 16-byte aligned, bytes a multiple of 16) with 16-byte
+ * vector loads spread over the whole device and writes one 32-bit word per
+ * workgroup to `sink` (device memory, 4096 words) so that no load is dropped.
+ * mode 0: the default cache policy; mode 1: non-temporal loads.  Timed next
+ * to the layer's kernels, it gives the read rate a plain stream reaches on
+ * the same GPU. */
+xhc_status xhc_probe_read(const void* src, size_t bytes, uint32_t* sink, int mode, xhc_stream_t stream);
+
 const char* xhc_last_error(void);
 
 #ifdef __cplusplus

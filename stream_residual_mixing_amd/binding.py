@@ -29,7 +29,7 @@ EXPORTS = (
     "xhc_post_decode", "xhcf_workspace_bytes", "xhcf_workspace_layout", "xhcf_pre", "xhcf_mid", "xhcf_post",
     "xhcf4_workspace_bytes", "xhcf4_workspace_layout", "xhcf4_pre", "xhcf4_post",
     "xhc_backward_workspace_bytes", "xhc_backward_workspace_layout", "xhc_post_backward", "xhc_pre_backward",
-    "xhc_last_error",
+    "xhc_probe_read", "xhc_last_error",
 )
 
 
@@ -304,9 +304,18 @@ class Lib:
                                        ctypes.c_void_p, ctypes.POINTER(XhcGrads), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
         d.xhc_last_error.restype = ctypes.c_char_p
+        d.xhc_probe_read.restype = ctypes.c_int
+        d.xhc_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         d.xhc_last_error.argtypes = []
 
     # -------------------------------------------------------------- helpers
+    def probe_read(self, src, sink, mode=0, stream=None):
+        """Measurement helper: one read-only pass over the device tensor src."""
+        if not (src.is_cuda and sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= 4096):
+            raise ValueError("probe_read: src and a 4096-word int32 sink on the GPU")
+        self._ok(self.dll.xhc_probe_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), mode,
+                                         _stream_ptr(stream)))
+
     def last_error(self) -> str:
         return self.dll.xhc_last_error().decode()
 

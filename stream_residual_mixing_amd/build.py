@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libxhc.so")
 SOURCES = ["xhc_api.hip", "xhc_kernels.hip", "xhc_pre.hip", "xhc_post.hip", "xhc_chain.hip", "xhc_flash.hip",
-           "xhc_backward.hip"]
+           "xhc_backward.hip", "xhc_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -20,8 +20,7 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-# hipBLASLt: the library GEMM of the wide mHC projection
-LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+LINK: list = []
 
 
 def hipcc() -> str:

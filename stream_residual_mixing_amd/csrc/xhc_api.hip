@@ -10,6 +10,10 @@
 #include "xhc.h"
 #include "xhc_internal.hpp"
 
+#ifndef XHC_MHC_GRID
+#define XHC_MHC_GRID 256   // workgroups the wide mHC projection aims for
+#endif
+
 namespace {
 
 thread_local std::string g_err;
@@ -120,20 +124,24 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
   };
   if (mhc) {
     // Wide maps (N >= 8, bf16): the projection [T x NC] . [NC x (2N + N^2)] is a
-    // real GEMM (N = 16: 618 GFLOP at T = 16384) and goes to the library GEMM,
-    // with the sums of squares from a streaming pass; no split.
-    q.mhc_gemm = q.N >= 8 && q.dtype == XHC_BF16;
-    if (q.mhc_gemm) q.KS = 1;
+    // real GEMM (N = 16: 618 GFLOP at T = 16384), done by a kernel that keeps
+    // 256 tokens per workgroup against weights staged in LDS; its contraction
+    // is split so that the grid covers the device (about 256 workgroups), each
+    // range at least 16 contraction blocks long.
+    q.mhc_wide = q.N >= 8 && q.dtype == XHC_BF16;
+    if (q.mhc_wide) {
+      const long ntile = (q.T + 255) / 256;
+      long ks = ntile > 0 ? (XHC_MHC_GRID + ntile - 1) / ntile : 1;
+      if (ks > 8) ks = 8;
+      while (ks > 1 && q.nkb_full / ks < 16) --ks;
+      q.KS = (int)(ks < 1 ? 1 : ks);
+    }
     q.o_hpre = take(T * N * 4);
     q.o_hres = take(T * N * N * 4);
     q.o_hpost = take(T * N * 4);
-    q.o_wfull = take(q.mhc_gemm ? 0 : (size_t)q.nkb_full * q.NTF * 64 * 16);
+    q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
     q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
     q.o_stats = take((size_t)q.KS * T * 2 * 4);
-    if (q.mhc_gemm) {
-      q.gemm_ws_bytes = (size_t)64 << 20;
-      q.o_gemm_ws = take(q.gemm_ws_bytes);
-    }
   } else {
     // one-pass pre: 16-token tiles, G channel slices of PRE_WV * PRE_NKW blocks
     const long nkbC = q.C / KB;
@@ -200,7 +208,7 @@ xhc_status make_flash_plan(const xhc_config* cfg, xhc::Plan* P) {
     off = align256(off + bytes);
     return o;
   };
-  q.o_sync = SIZE_MAX; q.o_corr = SIZE_MAX; q.o_gemm_ws = SIZE_MAX;
+  q.o_sync = SIZE_MAX; q.o_corr = SIZE_MAX;
   q.o_idx = take(T * K * 4);
   q.o_p = take(T * K * 4);
   q.o_hpre = take(T * N * 4);
@@ -336,10 +344,8 @@ xhc_status pre_common(const xhc_config* cfg, const xhc_weights* w, const void* X
     return fail(XHC_ERR_INVALID_ARG, "X, inp and ws must be 16-byte aligned");
   if (X == inp || X == ws || inp == ws) return fail(XHC_ERR_INVALID_ARG, "X, inp and ws must not alias");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  xhc::g_launch_failure = nullptr;
   const bool ok = mhc ? xhc::launch_mhc_pre(P, X, inp, w, static_cast<char*>(ws), st)
                       : xhc::launch_xhc_pre(P, X, inp, w, static_cast<char*>(ws), st);
-  if (!ok && xhc::g_launch_failure) return fail(XHC_ERR_HIP, "%s", xhc::g_launch_failure);
   if (!ok) return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }
@@ -441,6 +447,16 @@ xhc_status xhc_post_noalloc(const xhc_config* cfg, const xhc_weights* w, void* X
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (!xhc::launch_xhc_post_noalloc(P, X, out, w, static_cast<const char*>(ws), sp, st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
+  return finish(st);
+}
+
+xhc_status xhc_probe_read(const void* src, size_t bytes, uint32_t* sink, int mode, xhc_stream_t stream) {
+  if (!src || !sink) return fail(XHC_ERR_INVALID_ARG, "src and sink must not be NULL");
+  if (!aligned16(src) || bytes % 16 != 0) return fail(XHC_ERR_INVALID_ARG, "src must be 16-byte aligned, bytes a multiple of 16");
+  if (mode != 0 && mode != 1) return fail(XHC_ERR_INVALID_ARG, "mode must be 0 or 1");
+  if (bytes == 0) return XHC_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  xhc::launch_probe_read(src, bytes, sink, mode, st);
   return finish(st);
 }
 

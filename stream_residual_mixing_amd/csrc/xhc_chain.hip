@@ -710,22 +710,38 @@ __device__ __forceinline__ void slice_colsums(const u32x4_t (&s_w)[PSB][N][NTF][
 }
 
 // Next-layer routing projection of one tile (rows in amask masked to zero),
-// with the sums of x and x^2, B operands from LDS.
-template <class E, int N, int NTF>
+// with the sums of x and x^2, B operands from LDS.  The N x NTF weight
+// fragments are read ROUTE_BD - 1 MFMAs ahead of their use (a ring of
+// ROUTE_BD registers), each step pinned by a scheduling barrier: left to
+// itself the compiler reads each fragment right before its MFMA and waits
+// for the LDS every time.
+#ifndef XHC_ROUTE_BD
+#define XHC_ROUTE_BD 2
+#endif
+template <class E, int N, int NTF, int BD = XHC_ROUTE_BD>
 __device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)[N][NTF][WAVE], int lane, uint32_t amask,
                                           f32x4_t (&acc)[NTF], f32x4_t& S1, f32x4_t& S2) {
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
+  constexpr int TOT = N * NTF;
 #pragma unroll
   for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   S1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
   S2 = S1;
+  u32x4_t b[BD];
+#pragma unroll
+  for (int q = 0; q < BD - 1 && q < TOT; ++q) b[q] = w[q / NTF][q % NTF][lane];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const u32x4_t v = ((amask >> i) & 1u) ? zero : xs.x[i];
     mma_sums<E>(v, ones, S1, S2);
 #pragma unroll
-    for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, w[i][n][lane]);
+    for (int n = 0; n < NTF; ++n) {
+      const int q = i * NTF + n;
+      if (q + BD - 1 < TOT) b[(q + BD - 1) % BD] = w[(q + BD - 1) / NTF][(q + BD - 1) % NTF][lane];
+      acc[n] = E::mma(acc[n], v, b[q % BD]);
+      if constexpr (BD > 1) __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 

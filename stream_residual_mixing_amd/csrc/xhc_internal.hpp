@@ -28,7 +28,7 @@ struct Plan {
   int NTF = 0, NTA = 0;             // 16-column MFMA tiles
   long nkb_full = 0, nkb_act = 0;   // contraction blocks
   int KS = 1;                       // split of the full-state contraction (mHC)
-  bool mhc_gemm = false;            // mHC: projection by a library GEMM (wide maps)
+  bool mhc_wide = false;            // mHC: wide maps (N >= 8, bf16) by the 256-token projection kernel
   int nslices = 1;                  // channel slices of the post kernels
   int G = 1;                        // xHC pre: workgroups (channel slices) per 16-token tile
   int Gp = 1;                       // xHC chained: channel slices of the persistent kernels
@@ -36,9 +36,8 @@ struct Plan {
   // workspace byte offsets
   size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,
          o_z = SIZE_MAX, o_gstat = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
-         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX, o_gemm_ws = SIZE_MAX,
+         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX,
          total = 0;
-  size_t gemm_ws_bytes = 0;
   // xHC-Flash block (attention + MLP sharing one routing)
   bool flash = false;
   int G2 = 1;                       // splits of the active-row projections
@@ -117,9 +116,6 @@ bool launch_xhc_post_backward(const Plan& P, const xhc_weights* w, const void* X
 bool launch_xhc_pre_backward(const Plan& P, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
                              const char* ws, char* bws, hipStream_t st);
 
-// Set by a launcher that fails for a reason other than an unsupported shape
-// (e.g. the library GEMM); the host layer reports it as XHC_ERR_HIP.
-extern thread_local const char* g_launch_failure;
 
 bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st);
@@ -131,6 +127,11 @@ bool launch_xhc_post_noalloc(const Plan& P, void* X, const void* out, const xhc_
                              double* scratch_ptr, hipStream_t st);
 bool launch_mhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_mhc_post(const Plan& P, void* X, const void* out, char* ws, hipStream_t st);
+
+// Measurement helper (xhc_probe.hip): a read-only stream of 16-byte loads;
+// PROBE_SINK_WORDS workgroups, one word each written to sink.
+constexpr unsigned PROBE_SINK_WORDS = 4096;
+bool launch_probe_read(const void* src, size_t bytes, uint32_t* sink, int mode, hipStream_t st);
 
 // Weight packing into MFMA B fragments: wf->w_full into wsf (layout Pf),
 // wa->w_act into wsa (layout Pa), and the sync words of wsz (layout Pz)

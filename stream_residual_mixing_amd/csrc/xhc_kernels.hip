@@ -4,6 +4,8 @@
 //   pack_b      weights -> MFMA B fragments (once per call, a few MiB)
 //   proj_gen    one pass over X: split-K bf16/f32 MFMA projection of the raw
 //               (un-normalised) flattened state, plus sum x and sum x^2
+//   mhc_proj    the same for the wide maps (N >= 8, bf16: 2N + N^2 columns),
+//               256 tokens per workgroup with the weights staged in LDS
 //   mhc_read    per 16 tokens: RMS correction, H_pre / H_post, N x N
 //               Sinkhorn, dense read -> inp
 // (the xHC pre stage is the one-pass kernel of xhc_pre.hip)
@@ -16,12 +18,7 @@
 // Hyper-Connections", paragraph "Mapping generation").
 #include "xhc_device.hpp"
 #include "xhc_internal.hpp"
-
-#include <hipblaslt/hipblaslt.h>
-
-#include <map>
-#include <mutex>
-#include <tuple>
+#include "xhc_tile.hpp"
 
 // contraction blocks a proj_gen lane loads ahead (measured: 4 and 8 within
 // 2% of each other, 16 slower)
@@ -30,8 +27,6 @@
 #endif
 
 namespace xhc {
-
-thread_local const char* g_launch_failure = nullptr;
 
 // ---------------------------------------------------------------------------
 // weight packing: fragment (kb, nt, lane = 16 g + col) holds
@@ -124,6 +119,19 @@ __global__ __launch_bounds__(256) void proj_gen_kernel(const typename E::T* __re
 
 constexpr int RT = 16;  // tokens per mHC read block
 
+#ifndef XHC_MHC_READ_NT
+#define XHC_MHC_READ_NT 0
+#endif
+// a 16-byte load of state the dense read uses once
+__device__ __forceinline__ uint4 ld_x(const void* p) {
+  if constexpr (XHC_MHC_READ_NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return ld16(p);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // mhc_read: block = 16 tokens.  N lanes per token (one row of H_res each)
 // build the three maps; then the 4 waves split the channels for the dense read.
@@ -174,29 +182,42 @@ __global__ __launch_bounds__(256) void mhc_read_kernel(MhcReadArgs a) {
   }
   __syncthreads();
 
-  const int g = lane >> 4, r = lane & 15;
-  const int t = t0 + r;
-  const bool valid = t < a.T;
-  const int tt = valid ? t : t0;
-  float hp[N];
+  // dense read: a wave takes one token at a time and its lanes cover 64
+  // consecutive 16-byte pieces of each stream, so every load instruction reads
+  // 1 KiB of contiguous state (whole 128-byte lines)
+  constexpr int VEC = E::VEC;
+  constexpr int U = 2;                       // channel chunks of 64 VEC in flight
+  const int chunk = WAVE * VEC;
+  for (int tau = wave; tau < RT; tau += 4) {
+    const int t = t0 + tau;
+    if (t >= a.T) break;
+    float hp[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) hp[i] = s_hpre[r][i];
-  const int nkbC = C / E::KB;
-  const int kbA = wave * nkbC / 4, kbB = (wave + 1) * nkbC / 4;
-  const T* xt = X + (size_t)tt * N * C + E::VEC * g;
-  for (int kb = kbA; kb < kbB; ++kb) {
-    const int c = kb * E::KB;
-    float o[E::VEC];
+    for (int i = 0; i < N; ++i) hp[i] = s_hpre[tau][i];
+    const T* xt = X + (size_t)t * N * C;
+    for (int c0 = lane * VEC; c0 < C; c0 += U * chunk) {
+      uint4 v[U][N];
 #pragma unroll
-    for (int e = 0; e < E::VEC; ++e) o[e] = 0.f;
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      float f[E::VEC];
-      E::unpack(ld16(xt + (size_t)i * C + c), f);
+        for (int i = 0; i < N; ++i)
+          v[u][i] = c0 + u * chunk < C ? ld_x(xt + (size_t)i * C + c0 + u * chunk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < E::VEC; ++e) o[e] = fmaf(hp[i], f[e], o[e]);
+      for (int u = 0; u < U; ++u) {
+        if (c0 + u * chunk >= C) break;
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          float f[VEC];
+          E::unpack(v[u][i], f);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[e] = fmaf(hp[i], f[e], o[e]);
+        }
+        st16(inp + (size_t)t * C + c0 + u * chunk, E::pack(o));
+      }
     }
-    if (valid) st16(inp + (size_t)t * C + c + E::VEC * g, E::pack(o));
   }
 }
 
@@ -287,109 +308,160 @@ static bool gen_dispatch(int NT, const void* X, int T, long K, const void* Wp, l
 }
 
 // ---------------------------------------------------------------------------
-// Sums of x and x^2 over each token's flattened state (one wave per token,
-// 16-byte loads, eight in flight per lane), for the RMSNorm of the wide mHC
-// maps whose projection runs as a library GEMM.  stats[t] = (sum x, sum x^2).
+// mhc_proj: the wide mHC projection, raw[t][0..ncol) = vec X_t . W_full, with
+// sum x and sum x^2, for bf16 state at N >= 8 (ncol = 2N + N^2: 288 columns
+// at N = 16).  It is a real GEMM ([T x NC] . [NC x ncol], ~290 flop per byte
+// of X at N = 16), so the weights must be reused across many tokens:
+//   - a workgroup owns MP_TOK = 256 tokens and every column, over one of KS
+//     contraction ranges; each wave owns MP_RT consecutive 16-row MFMA tiles
+//     of them and holds their MP_RT x NT accumulators;
+//   - the packed weight fragments of MP_KU contraction blocks at a time go
+//     from global memory straight into LDS (double-buffered, one barrier per
+//     stage) and are read by all eight waves; the state goes straight from
+//     HBM into A fragments, one stage ahead;
+//   - workgroup b takes range b mod KS, so the workgroups sharing an XCD (and
+//     its L2) walk the same weight range.
+// X is read once.  Partials per (range, token), summed by mhc_read.
 // ---------------------------------------------------------------------------
-template <class E>
-__global__ __launch_bounds__(256) void mhc_sumsq_kernel(const typename E::T* __restrict__ X, int T, long NC,
-                                                        float* __restrict__ stats) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const typename E::T* row = X + (size_t)t * NC;
-  constexpr int U = 8;
-  const long step = (long)WAVE * E::VEC;
-  float s1 = 0.f, s2 = 0.f;
-  long c = (long)lane * E::VEC;
-  for (; c + (U - 1) * step < NC; c += U * step) {
-    uint4 v[U];
+#ifndef XHC_MHC_KU
+#define XHC_MHC_KU 4
+#endif
+#ifndef XHC_MHC_RT
+#define XHC_MHC_RT 2
+#endif
+#ifndef XHC_MHC_BD
+#define XHC_MHC_BD 4
+#endif
+constexpr int MP_KU = XHC_MHC_KU;              // contraction blocks per LDS stage
+constexpr int MP_BD = XHC_MHC_BD;              // weight fragments in registers (read ahead)
+constexpr int MP_RT = XHC_MHC_RT;              // 16-token MFMA row tiles per wave
+constexpr int MP_THREADS = 512 * 2 / MP_RT;    // 8 waves of 2 tiles or 4 waves of 4
+constexpr int MP_TOK = MP_THREADS / 64 * 16 * MP_RT;   // 256 tokens per workgroup
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int NT>
+__global__ __launch_bounds__(MP_THREADS, 1) void mhc_proj_kernel(const uint16_t* __restrict__ X, int T, long K,
+                                                                 const uint4* __restrict__ Wp, long nkb, int KS,
+                                                                 float* __restrict__ part, float* __restrict__ stats) {
+  constexpr int CH = MP_KU * NT;                  // 1 KiB weight fragments per stage
+  constexpr int NW = MP_THREADS / WAVE;
+  __shared__ u32x4_t s_w[2][MP_KU][NT][WAVE];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = blockIdx.x % KS, tile = blockIdx.x / KS;
+  const long kb0 = (long)ks * nkb / KS, kb1 = (long)(ks + 1) * nkb / KS;
+  const int t0 = tile * MP_TOK;
+  const int rows = T - t0 < MP_TOK ? T - t0 : MP_TOK;
+  // the workgroup's rows only: loads past T read zeros
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (size_t)t0 * K, (uint32_t)((size_t)rows * K * 2));
+  const uint32_t voff0 = (uint32_t)(((size_t)(wave * 16 * MP_RT + r) * K + 8 * g) * 2);
+
+  f32x4_t acc[MP_RT][NT];
+  float s1[MP_RT], s2[MP_RT];   // token r of each tile, over this lane's 8 of 32 columns
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld16(row + c + u * step);
+  for (int h = 0; h < MP_RT; ++h) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float f[E::VEC];
-      E::unpack(v[u], f);
+    for (int n = 0; n < NT; ++n) acc[h][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1[h] = 0.f;
+    s2[h] = 0.f;
+  }
+
+  // The weight fragments of the stage starting at kbs, straight from global
+  // memory into LDS buffer buf (each lane 16 bytes of a 1 KiB fragment);
+  // fragments past the range are not loaded and not used.
+  auto load_w = [&](long kbs, int buf) {
+    const long inside = (kb1 - kbs) * NT;
 #pragma unroll
-      for (int e = 0; e < E::VEC; ++e) { s1 += f[e]; s2 = fmaf(f[e], f[e], s2); }
+    for (int c = wave; c < CH; c += NW)
+      if (c < inside)
+        __builtin_amdgcn_global_load_lds(Wp + (kbs * NT + c) * WAVE + lane,
+                                         (lds_ptr_t)(&s_w[buf][0][0][0] + (size_t)c * WAVE), 16, 0, 0);
+  };
+  auto load_a = [&](long kbs, u32x4_t (&a)[MP_RT][MP_KU]) {
+#pragma unroll
+    for (int k = 0; k < MP_KU; ++k) {
+      const bool in = kbs + k < kb1;
+      const uint32_t o = (uint32_t)((kbs + k) * 64);
+#pragma unroll
+      for (int h = 0; h < MP_RT; ++h)
+        a[h][k] = in ? ld_b128(rx, voff0 + (uint32_t)(h * 16 * K * 2) + o, 0) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+
+  u32x4_t acur[MP_RT][MP_KU], anext[MP_RT][MP_KU];
+  load_w(kb0, 0);
+  load_a(kb0, acur);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int buf = 0;
+  for (long kbs = kb0; kbs < kb1; kbs += MP_KU) {
+    const bool more = kbs + MP_KU < kb1;
+    if (more) {
+      // the other buffer was last read in the previous stage, before its barrier
+      load_w(kbs + MP_KU, buf ^ 1);
+      load_a(kbs + MP_KU, anext);
+    }
+#pragma unroll
+    for (int k = 0; k < MP_KU; ++k) {
+      if (kbs + k < kb1) {
+#pragma unroll
+        for (int h = 0; h < MP_RT; ++h) {
+          float f[8];
+          Bf16::unpack(acur[h][k], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            s1[h] += f[e];
+            s2[h] = fmaf(f[e], f[e], s2[h]);
+          }
+        }
+        // weight fragments read MP_BD - 1 tiles ahead of their MFMAs, so the
+        // LDS latency hides behind the MFMAs of the tiles before
+        u32x4_t b[MP_BD];
+#pragma unroll
+        for (int q = 0; q < MP_BD - 1 && q < NT; ++q) b[q] = s_w[buf][k][q][lane];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          if (n + MP_BD - 1 < NT) b[(n + MP_BD - 1) % MP_BD] = s_w[buf][k][n + MP_BD - 1][lane];
+#pragma unroll
+          for (int h = 0; h < MP_RT; ++h) acc[h][n] = Bf16::mma(acc[h][n], acur[h][k], b[n % MP_BD]);
+          __builtin_amdgcn_sched_barrier(0);   // keep each read ahead of the MFMAs before its use
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < MP_KU; ++k)
+#pragma unroll
+        for (int h = 0; h < MP_RT; ++h) acur[h][k] = anext[h][k];
+    }
+    // this wave's weight fragments of the next stage are in LDS (its state
+    // loads are wanted next anyway), then everyone's
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    buf ^= 1;
+  }
+  constexpr int NP = NT * 16;
+#pragma unroll
+  for (int h = 0; h < MP_RT; ++h) {
+    // the four lane groups of token r hold its four column groups
+    s1[h] += __shfl_xor(s1[h], 16, WAVE);
+    s1[h] += __shfl_xor(s1[h], 32, WAVE);
+    s2[h] += __shfl_xor(s2[h], 16, WAVE);
+    s2[h] += __shfl_xor(s2[h], 32, WAVE);
+    const int tb = t0 + wave * 16 * MP_RT + h * 16;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tb + 4 * g + i;
+        if (t < T) part[((size_t)ks * T + t) * NP + n * 16 + r] = acc[h][n][i];
+      }
+    if (g == 0 && tb + r < T) {
+      stats[((size_t)ks * T + tb + r) * 2 + 0] = s1[h];
+      stats[((size_t)ks * T + tb + r) * 2 + 1] = s2[h];
     }
   }
-  for (; c < NC; c += step) {
-    float f[E::VEC];
-    E::unpack(ld16(row + c), f);
-#pragma unroll
-    for (int e = 0; e < E::VEC; ++e) { s1 += f[e]; s2 = fmaf(f[e], f[e], s2); }
-  }
-  s1 = wave_sum(s1);
-  s2 = wave_sum(s2);
-  if (lane == 0) {
-    stats[(size_t)t * 2] = s1;
-    stats[(size_t)t * 2 + 1] = s2;
-  }
-}
-
-// The library GEMM of the wide mHC projection: raw[t][0..ncol) = vec X_t . W
-// (bf16 in, float out, rows of raw NP floats apart).  hipBLASLt is column-major,
-// so it computes raw^T (ncol x T, ld NP) = W^T (ncol x NC, ld ncol) X^T (NC x T,
-// ld NC), reading both operands in their row-major layout untransposed.  One
-// handle per device and one algorithm per shape, chosen by the library's
-// heuristic on first use and kept for the process.
-struct LtShape {
-  int dev;
-  long T, NC, ncol, NP;
-  bool operator<(const LtShape& o) const {
-    return std::tie(dev, T, NC, ncol, NP) < std::tie(o.dev, o.T, o.NC, o.ncol, o.NP);
-  }
-};
-struct LtPlan {
-  hipblasLtMatmulDesc_t op = nullptr;
-  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, d = nullptr;
-  hipblasLtMatmulAlgo_t algo{};
-  size_t ws = 0;
-};
-
-static bool lt_gemm(const void* X, const void* W, float* raw, long T, long NC, long ncol, long NP, void* ws,
-                    size_t ws_bytes, hipStream_t st) {
-  static std::mutex mu;
-  static hipblasLtHandle_t handles[64] = {};
-  static std::map<LtShape, LtPlan> plans;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!handles[dev] && hipblasLtCreate(&handles[dev]) != HIPBLAS_STATUS_SUCCESS) return false;
-  const LtShape key{dev, T, NC, ncol, NP};
-  auto it = plans.find(key);
-  if (it == plans.end()) {
-    LtPlan p;
-    const hipblasOperation_t opn = HIPBLAS_OP_N;
-    if (hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &opn, sizeof opn) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &opn, sizeof opn) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, ncol, NC, ncol) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, NC, T, NC) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&p.d, HIP_R_32F, ncol, T, NP) != HIPBLAS_STATUS_SUCCESS)
-      return false;
-    hipblasLtMatmulPreference_t pref = nullptr;
-    const uint64_t maxws = ws_bytes;
-    hipblasLtMatmulHeuristicResult_t res[8];
-    int n = 0;
-    if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return false;
-    const bool ok = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &maxws,
-                                                          sizeof maxws) == HIPBLAS_STATUS_SUCCESS &&
-                    hipblasLtMatmulAlgoGetHeuristic(handles[dev], p.op, p.a, p.b, p.d, p.d, pref, 8, res, &n) ==
-                        HIPBLAS_STATUS_SUCCESS &&
-                    n > 0;
-    hipblasLtMatmulPreferenceDestroy(pref);
-    if (!ok) return false;
-    p.algo = res[0].algo;
-    p.ws = res[0].workspaceSize;
-    it = plans.emplace(key, p).first;
-  }
-  const LtPlan& p = it->second;
-  if (p.ws > ws_bytes) return false;
-  const float one = 1.f, zero = 0.f;
-  return hipblasLtMatmul(handles[dev], p.op, &one, W, p.a, X, p.b, &zero, raw, p.d, raw, p.d, &p.algo, ws, p.ws,
-                         st) == HIPBLAS_STATUS_SUCCESS;
 }
 
 template <class E, int N>
@@ -405,21 +477,23 @@ static void launch_mhc_post(const MhcPostArgs& a, hipStream_t st) {
 
 template <class E>
 static bool mhc_pre_launch(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st) {
-  if (P.mhc_gemm) {
-    const long NC = (long)P.N * P.C;
-    mhc_sumsq_kernel<E><<<(unsigned)((P.T + 3) / 4), 256, 0, st>>>(reinterpret_cast<const typename E::T*>(X),
-                                                                      (int)P.T, NC,
-                                                                      reinterpret_cast<float*>(ws + P.o_stats));
-    if (!lt_gemm(X, w->w_full, reinterpret_cast<float*>(ws + P.o_part), P.T, NC, P.ncol_full, (long)P.NTF * 16,
-                 ws + P.o_gemm_ws, P.gemm_ws_bytes, st)) {
-      g_launch_failure = "hipBLASLt GEMM of the full-state projection failed";
-      return false;
+  launch_pack<E>(w->w_full, P.nkb_full, P.ncol_full, P.NTF, ws + P.o_wfull, st);
+  if (P.mhc_wide) {
+    const long ntile = (P.T + MP_TOK - 1) / MP_TOK;
+    const unsigned grid = (unsigned)(ntile * P.KS);
+    const uint16_t* Xb = reinterpret_cast<const uint16_t*>(X);
+    const uint4* Wp = reinterpret_cast<const uint4*>(ws + P.o_wfull);
+    float* part = reinterpret_cast<float*>(ws + P.o_part);
+    float* stats = reinterpret_cast<float*>(ws + P.o_stats);
+    const long K = (long)P.N * P.C;
+    switch (P.NTF) {
+      case 18: mhc_proj_kernel<18><<<grid, MP_THREADS, 0, st>>>(Xb, (int)P.T, K, Wp, P.nkb_full, P.KS, part, stats); break;
+      case 5: mhc_proj_kernel<5><<<grid, MP_THREADS, 0, st>>>(Xb, (int)P.T, K, Wp, P.nkb_full, P.KS, part, stats); break;
+      default: return false;
     }
-  } else {
-    launch_pack<E>(w->w_full, P.nkb_full, P.ncol_full, P.NTF, ws + P.o_wfull, st);
-    if (!gen_dispatch<E>(P.NTF, X, (int)P.T, (long)P.N * P.C, ws + P.o_wfull, P.nkb_full, P.KS,
-                         reinterpret_cast<float*>(ws + P.o_part), reinterpret_cast<float*>(ws + P.o_stats), st))
-      return false;
+  } else if (!gen_dispatch<E>(P.NTF, X, (int)P.T, (long)P.N * P.C, ws + P.o_wfull, P.nkb_full, P.KS,
+                              reinterpret_cast<float*>(ws + P.o_part), reinterpret_cast<float*>(ws + P.o_stats), st)) {
+    return false;
   }
   MhcReadArgs a;
   a.X = X; a.inp = inp; a.T = (int)P.T; a.C = P.C; a.KS = P.KS;

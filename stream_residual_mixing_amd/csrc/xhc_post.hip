@@ -277,7 +277,10 @@ __device__ __forceinline__ void write_coeffs(const double (&Tm)[4][4], const flo
   }
 }
 
-constexpr int GB = 4;   // tokens per load batch in the Gram pass (HL is a multiple)
+#ifndef XHC_GRAM_GB
+#define XHC_GRAM_GB 4
+#endif
+constexpr int GB = XHC_GRAM_GB;   // tokens per load batch in the Gram pass (HL is a multiple)
 static_assert(HL % GB == 0, "load batches tile a history period");
 
 }  // namespace
