@@ -105,14 +105,15 @@ def flash4_bytes_per_token(cfg, esz=2):
 
 def bwd_bytes_per_token(cfg, esz=2):
     """Algorithmic bytes per token of the backward's two calls.  Application
-    half: read the state (N rows, for the H_pre gradient and the mix), the
-    new state's gradient (N), d_inp and out; write the state gradient (N)
-    and d_out: 3N + 3.  Generation half: read the state once (the norms and
-    projections) and update the state gradient in place: 3N.  Intermediates
-    (the gathered active rows, the basis gradient, the partial weight
+    half: read the state (N rows, for the H_pre and H_res gradients), the new
+    state's gradient on the k active rows, d_inp and out; write d_out:
+    N + k + 3.  Generation half: read the state (the norms and projections),
+    the new state's gradient on the N - k other rows and d_inp; write the
+    state gradient: 3N - k + 1.  Intermediates (the gathered active rows,
+    the active rows' float gradient, the basis gradient, the partial weight
     gradients) are not counted."""
-    N, C = cfg.N, cfg.C
-    return (3 * N + 3) * C * esz, 3 * N * C * esz
+    N, k, C = cfg.N, cfg.k, cfg.C
+    return (N + k + 3) * C * esz, (3 * N - k + 1) * C * esz
 
 
 def bytes_per_token(kind, cfg, esz=2):
@@ -248,11 +249,11 @@ def run_gpu(name, steps, warmup, api):
             cfg, lk = cfgs[l], kinds[l]
             dst = gbuf[j % 2]
             bp, bq = bytes_per_token(kind, cfg)
-            calls.append((f"xhc_post_backward_{lk}", bp, lambda cfg=cfg, l=l, s_=src, d_=dst: lib.xhc_post_backward(
-                cfg, weights[l], X, outs[l].reshape(cfg.T, cfg.C), d_inp, s_, d_, d_out,
+            calls.append((f"xhc_post_backward_{lk}", bp, lambda cfg=cfg, l=l, s_=src: lib.xhc_post_backward(
+                cfg, weights[l], X, outs[l].reshape(cfg.T, cfg.C), d_inp, s_, d_out,
                 d_conv if cfg.K_r == 4 else None, wss[l], bws, stream)))
-            calls.append((f"xhc_pre_backward_{lk}", bq, lambda cfg=cfg, l=l, d_=dst: lib.xhc_pre_backward(
-                cfg, weights[l], X, d_, grads[l], wss[l], bws, stream)))
+            calls.append((f"xhc_pre_backward_{lk}", bq, lambda cfg=cfg, l=l, s_=src, d_=dst: lib.xhc_pre_backward(
+                cfg, weights[l], X, d_inp, s_, d_, grads[l], wss[l], bws, stream)))
             src = dst
     elif kind == "xhcd":
         ws = lib.workspace(big)

@@ -448,32 +448,39 @@ typedef struct {
 size_t xhc_backward_workspace_bytes(const xhc_config* cfg);
 xhc_status xhc_backward_workspace_layout(const xhc_config* cfg, xhc_bwd_ws_layout* out);
 
-/* Application half.
+/* Application half: the gradients of the maps (into bws), of out and of
+ * the conv kernels, and the active rows' share of the state gradient
+ * through the dense read and the mix (active row j: sum_i H_res[i][j]
+ * d_X[I_i] + H_pre[I_j] d_inp), kept in float in bws for xhc_pre_backward.
  *   X:      [T][N][C] the state xhc_pre read (before xhc_post), read only
  *   out:    [T][C] the sublayer output, read only
  *   d_inp:  [T][C] gradient of the sublayer input inp, read only
- *   d_X:    [T][N][C] gradient of the new state, read only
- *   dX:     [T][N][C] written: the state gradient through the dense read and
- *           the mix (non-active rows d_X + H_pre[n] d_inp; active row j
- *           sum_i H_res[i][j] d_X[I_i] + H_pre[I_j] d_inp); may be d_X itself
+ *   d_X:    [T][N][C] gradient of the new state, read only (active rows)
  *   d_out:  [T][C] written: gradient of out (through Gram-Schmidt and the
  *           causal convolutions for MLP-type sublayers)
  *   d_conv: float [24][C] written, the conv-kernel gradients in conv_w's
  *           layout (MLP-type; NULL for attention-type)
  *   ws:     the workspace xhc_pre filled;  bws: xhc_backward_workspace_bytes
- * X, out, d_inp, d_X, dX, d_out in the state dtype, 16-byte aligned. */
+ * X, out, d_inp, d_X, d_out in the state dtype, 16-byte aligned; d_out and
+ * bws alias no input. */
 xhc_status xhc_post_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, const void* out,
-                             const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv,
-                             const void* ws, void* bws, xhc_stream_t stream);
+                             const void* d_inp, const void* d_X, void* d_out, float* d_conv, const void* ws,
+                             void* bws, xhc_stream_t stream);
 
-/* Generation half: adds to dX the state gradient through the norms and the
- * projections (full state for the router and H_pre, active rows for H_res
- * and H_post) and writes every field of g.  X as for xhc_post_backward; dX
- * as that call left it (read and written). */
-xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, void* dX,
-                            const xhc_grads* g, const void* ws, void* bws, xhc_stream_t stream);
+/* Generation half: writes dX, the whole state gradient, and every field of
+ * g.  dX is the application half's part (non-active rows d_X + H_pre[n]
+ * d_inp; the active rows' part as xhc_post_backward left it in bws) plus
+ * the part through the norms and the projections (full state for the
+ * router and H_pre, active rows for H_res and H_post), summed in float and
+ * rounded once to the state dtype (the paper's backward accumulates both
+ * contributions straight into the full state's gradient, "Mapping
+ * application").  X, d_inp and d_X as given to xhc_post_backward (read
+ * only); dX [T][N][C] written, and may be d_X itself (in place); no other
+ * buffer may alias. */
+xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, const void* d_inp,
+                            const void* d_X, void* dX, const xhc_grads* g, const void* ws, void* bws,
+                            xhc_stream_t stream);
 
-/* Message for the last non-OK status returned on this host thread. */
 /* Measurement helper, not part of the layer: reads `bytes` bytes at `src`
  * (device memory, 16-byte aligned, bytes a multiple of 16) with 16-byte
  * vector loads spread over the whole device and writes one 32-bit word per
@@ -483,6 +490,7 @@ xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const v
  * the same GPU. */
 xhc_status xhc_probe_read(const void* src, size_t bytes, uint32_t* sink, int mode, xhc_stream_t stream);
 
+/* Message for the last non-OK status returned on this host thread. */
 const char* xhc_last_error(void);
 
 #ifdef __cplusplus

@@ -298,11 +298,10 @@ class Lib:
         d.xhc_backward_workspace_layout.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcBwdWsLayout)]
         d.xhc_post_backward.restype = ctypes.c_int
         d.xhc_post_backward.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights)] + \
-            [ctypes.c_void_p] * 10
+            [ctypes.c_void_p] * 9
         d.xhc_pre_backward.restype = ctypes.c_int
-        d.xhc_pre_backward.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights), ctypes.c_void_p,
-                                       ctypes.c_void_p, ctypes.POINTER(XhcGrads), ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_void_p]
+        d.xhc_pre_backward.argtypes = [ctypes.POINTER(XhcConfig), ctypes.POINTER(XhcWeights)] + \
+            [ctypes.c_void_p] * 4 + [ctypes.POINTER(XhcGrads), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         d.xhc_last_error.restype = ctypes.c_char_p
         d.xhc_probe_read.restype = ctypes.c_int
         d.xhc_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
@@ -510,26 +509,26 @@ class Lib:
         if bws is None or not bws.is_cuda or bws.numel() * bws.element_size() < need:
             raise ValueError(f"backward workspace must be a GPU tensor of at least {need} bytes")
 
-    def xhc_post_backward(self, cfg: Config, w: Weights, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws,
-                          stream=None):
+    def xhc_post_backward(self, cfg: Config, w: Weights, X, out, d_inp, d_X, d_out, d_conv, ws, bws, stream=None):
         self._check_common(cfg, w, X, ws, False, False)
         dt = cfg.torch_dtype
         for t, name, shape in ((out, "out", (cfg.T, cfg.C)), (d_inp, "d_inp", (cfg.T, cfg.C)),
-                               (d_X, "d_X", (cfg.T, cfg.N, cfg.C)), (dX, "dX", (cfg.T, cfg.N, cfg.C)),
-                               (d_out, "d_out", (cfg.T, cfg.C))):
+                               (d_X, "d_X", (cfg.T, cfg.N, cfg.C)), (d_out, "d_out", (cfg.T, cfg.C))):
             _check(t, name, shape, dt)
         if cfg.K_r == 4:
             _check(d_conv, "d_conv", (sum(cfg.kernels), cfg.C), torch.float32)
         self._check_bws(cfg, bws)
         c, cw = cfg.c(), w.c()
         self._ok(self.dll.xhc_post_backward(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), out.data_ptr(),
-                                            d_inp.data_ptr(), d_X.data_ptr(), dX.data_ptr(), d_out.data_ptr(),
+                                            d_inp.data_ptr(), d_X.data_ptr(), d_out.data_ptr(),
                                             d_conv.data_ptr() if d_conv is not None else None, ws.data_ptr(),
                                             bws.data_ptr(), _stream_ptr(stream)))
 
-    def xhc_pre_backward(self, cfg: Config, w: Weights, X, dX, g: dict, ws, bws, stream=None):
+    def xhc_pre_backward(self, cfg: Config, w: Weights, X, d_inp, d_X, dX, g: dict, ws, bws, stream=None):
         self._check_common(cfg, w, X, ws, False, True)
-        _check(dX, "dX", (cfg.T, cfg.N, cfg.C), cfg.torch_dtype)
+        for t, name, shape in ((d_inp, "d_inp", (cfg.T, cfg.C)), (d_X, "d_X", (cfg.T, cfg.N, cfg.C)),
+                               (dX, "dX", (cfg.T, cfg.N, cfg.C))):
+            _check(t, name, shape, cfg.torch_dtype)
         ref = self.grads(cfg, device="meta")
         for name, t in ref.items():
             _check(g[name], "d_" + name, tuple(t.shape), torch.float32)
@@ -537,8 +536,9 @@ class Lib:
         c, cw = cfg.c(), w.c()
         gg = XhcGrads(g["W_full"].data_ptr(), g["W_act"].data_ptr(), g["b_pre"].data_ptr(), g["b_res"].data_ptr(),
                       g["b_post"].data_ptr(), g["alpha"].data_ptr())
-        self._ok(self.dll.xhc_pre_backward(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), dX.data_ptr(),
-                                           ctypes.byref(gg), ws.data_ptr(), bws.data_ptr(), _stream_ptr(stream)))
+        self._ok(self.dll.xhc_pre_backward(ctypes.byref(c), ctypes.byref(cw), X.data_ptr(), d_inp.data_ptr(),
+                                           d_X.data_ptr(), dX.data_ptr(), ctypes.byref(gg), ws.data_ptr(),
+                                           bws.data_ptr(), _stream_ptr(stream)))
 
     # xHC-Flash block: attention + MLP sharing one routing
     def flash_workspace_bytes(self, cfg: Config) -> int:

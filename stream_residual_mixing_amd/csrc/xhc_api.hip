@@ -727,35 +727,34 @@ xhc_status xhc_backward_workspace_layout(const xhc_config* cfg, xhc_bwd_ws_layou
 }
 
 xhc_status xhc_post_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, const void* out,
-                             const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv,
-                             const void* ws, void* bws, xhc_stream_t stream) {
+                             const void* d_inp, const void* d_X, void* d_out, float* d_conv, const void* ws, void* bws,
+                             xhc_stream_t stream) {
   xhc::Plan P;
   xhc_status s = make_plan(cfg, false, &P);
   if (s != XHC_OK) return s;
   if ((s = check_weights(P, w, false)) != XHC_OK) return s;
   if (P.T == 0) return XHC_OK;
-  const void* ptrs[] = {X, out, d_inp, d_X, dX, d_out, ws, bws};
+  const void* ptrs[] = {X, out, d_inp, d_X, d_out, ws, bws};
   for (const void* q : ptrs)
     if (!q || !aligned16(q))
-      return fail(XHC_ERR_INVALID_ARG, "X, out, d_inp, d_X, dX, d_out, ws and bws must be 16-byte aligned, non-NULL");
+      return fail(XHC_ERR_INVALID_ARG, "X, out, d_inp, d_X, d_out, ws and bws must be 16-byte aligned, non-NULL");
   if (P.KR == 4 && !d_conv) return fail(XHC_ERR_INVALID_ARG, "d_conv must not be NULL for MLP-type configs");
-  // dX may be d_X; no other pair may alias
-  const void* outs[] = {dX, d_out, bws};
-  const void* ins[] = {X, out, d_inp, ws};
+  const void* outs[] = {d_out, bws};
+  const void* ins[] = {X, out, d_inp, d_X, ws};
   for (const void* o : outs)
     for (const void* i : ins)
-      if (o == i) return fail(XHC_ERR_INVALID_ARG, "outputs dX, d_out and bws must not alias X, out, d_inp or ws");
-  if (dX == d_out || dX == bws || d_out == bws || d_out == d_X || bws == d_X)
-    return fail(XHC_ERR_INVALID_ARG, "dX, d_out and bws must be distinct (only dX may be d_X)");
+      if (o == i) return fail(XHC_ERR_INVALID_ARG, "outputs d_out and bws must not alias X, out, d_inp, d_X or ws");
+  if (d_out == bws) return fail(XHC_ERR_INVALID_ARG, "d_out and bws must be distinct");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (!xhc::launch_xhc_post_backward(P, w, X, out, d_inp, d_X, dX, d_out, d_conv, static_cast<const char*>(ws),
+  if (!xhc::launch_xhc_post_backward(P, w, X, out, d_inp, d_X, d_out, d_conv, static_cast<const char*>(ws),
                                      static_cast<char*>(bws), st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }
 
-xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, void* dX,
-                            const xhc_grads* g, const void* ws, void* bws, xhc_stream_t stream) {
+xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const void* X, const void* d_inp,
+                            const void* d_X, void* dX, const xhc_grads* g, const void* ws, void* bws,
+                            xhc_stream_t stream) {
   xhc::Plan P;
   xhc_status s = make_plan(cfg, false, &P);
   if (s != XHC_OK) return s;
@@ -763,13 +762,16 @@ xhc_status xhc_pre_backward(const xhc_config* cfg, const xhc_weights* w, const v
   if (!g || !g->dW_full || !g->dW_act || !g->d_b_pre || !g->d_b_res || !g->d_b_post || !g->d_alpha)
     return fail(XHC_ERR_INVALID_ARG, "every gradient pointer must be set");
   if (P.T == 0) return XHC_OK;
-  const void* ptrs[] = {X, dX, ws, bws};
+  const void* ptrs[] = {X, d_inp, d_X, dX, ws, bws};
   for (const void* q : ptrs)
-    if (!q || !aligned16(q)) return fail(XHC_ERR_INVALID_ARG, "X, dX, ws and bws must be 16-byte aligned, non-NULL");
-  if (dX == X || dX == ws || dX == bws || bws == X || bws == ws)
-    return fail(XHC_ERR_INVALID_ARG, "dX and bws must not alias X, ws or each other");
+    if (!q || !aligned16(q))
+      return fail(XHC_ERR_INVALID_ARG, "X, d_inp, d_X, dX, ws and bws must be 16-byte aligned, non-NULL");
+  // dX may be d_X; no other pair may alias
+  if (dX == X || dX == d_inp || dX == ws || dX == bws || bws == X || bws == d_inp || bws == d_X || bws == ws)
+    return fail(XHC_ERR_INVALID_ARG, "dX and bws must not alias X, d_inp, ws or each other (only dX may be d_X)");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (!xhc::launch_xhc_pre_backward(P, w, X, dX, g, static_cast<const char*>(ws), static_cast<char*>(bws), st))
+  if (!xhc::launch_xhc_pre_backward(P, w, X, d_inp, d_X, dX, g, static_cast<const char*>(ws),
+                                    static_cast<char*>(bws), st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }

@@ -157,7 +157,8 @@ __device__ float mgs_coef(const float (&M)[R][R], float eps, float (&A)[R][R], i
 
 struct BwdApplyArgs {
   const void *X, *out, *d_inp, *d_X;
-  void *dX, *d_out, *xa;
+  void *d_out, *xa;
+  float* dxa;         // [T][K][C]: the active rows' state gradient so far (float)
   float* dg;
   const float* conv_w;
   const int* idx;
@@ -173,8 +174,13 @@ struct BwdApplyArgs {
 // the new state's gradient on active row i; and stores the gathered active
 // rows for the generation half.  The scalar stage gives the H_post and p
 // gradients and the basis gradient as a combination of the dY_i and the g_q.
-// Pass 2 writes dX (non-active rows: d_X + H_pre[n] d_inp; active row j:
-// sum_i H_res[i][j] dY_i + H_pre[I_j] d_inp) and the basis gradient.
+// Pass 2 writes the basis gradient and the active rows' share of the state
+// gradient through the read and the mix (active row j: sum_i H_res[i][j] dY_i
+// + H_pre[I_j] d_inp) in float to the backward workspace.  A non-active row's
+// share, d_X + H_pre[n] d_inp, is formed by the generation half's full-state
+// pass together with its own terms (this pass reads no non-active row of
+// d_X).  Each element of the state gradient is rounded to the state dtype
+// once, by the last pass that adds to it.
 //
 // MLP-type: workgroups are dispatched to the 8 XCDs in turn; workgroup b
 // takes token (b mod 8) * ceil(T / 8) + b / 8, so that each XCD walks a
@@ -197,7 +203,6 @@ __global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
   const T* dXn = reinterpret_cast<const T*>(a.d_X) + (size_t)t * N * C;
   const T* di = reinterpret_cast<const T*>(a.d_inp) + (size_t)t * C;
   const T* ot = reinterpret_cast<const T*>(a.out) + (size_t)t * C;
-  T* dX = reinterpret_cast<T*>(a.dX) + (size_t)t * N * C;
   T* xa = reinterpret_cast<T*>(a.xa) + (size_t)t * K * C;
   __shared__ int s_idx[K], s_pos[N];
   __shared__ float s_hpre[N], s_mix[K][K];
@@ -371,23 +376,21 @@ __global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
     if constexpr (KR == 4) write_basis<E, KR>(ot, s, C, c, a.conv_w, g);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      float o[V];
       const int j = s_pos[n];
-      const float h = s_hpre[n];
       if (j >= 0) {
+        // active position j: sum_i H_res[i][j] dY_i + H_pre[I_j] d_inp, in float
+        float o[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          float v = h * fi[e];
+          float v = s_hpre[n] * fi[e];
 #pragma unroll
           for (int i = 0; i < K; ++i) v = fmaf(s_mix[i][j], y[i][e], v);
           o[e] = v;
         }
-      } else {
-        E::unpack(ld16(dXn + (size_t)n * C + c), o);
+        float* pa = a.dxa + ((size_t)t * K + j) * C + c;
 #pragma unroll
-        for (int e = 0; e < V; ++e) o[e] = fmaf(h, fi[e], o[e]);
+        for (int e = 0; e < V; e += 4) *reinterpret_cast<float4*>(pa + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
       }
-      st16(dX + (size_t)n * C + c, E::pack(o));
     }
 #pragma unroll
     for (int q = 0; q < KR; ++q) {
@@ -595,6 +598,7 @@ struct BwdTokArgs {
   float a_pre, a_res, a_post, eps;
   int iters, m, T, C;
   float *Gt, *Ga, *sc, *brow;
+  float* rsel;                    // [T][N]: H_pre[n] for a stream outside the active list, -1 - (its position) for one in it
 };
 
 // Generation half, per-token scalars.  16 lanes per token: lane (a, b) < k^2
@@ -721,7 +725,11 @@ __global__ __launch_bounds__(BT) void bwd_token_kernel(BwdTokArgs a) {
     sdz = dz * a.z[(size_t)tt * N + n];
     const float gr = dz / sh;
     cs = gr * a.colsum[n];
+    int pos = -1;
+    for (int i = 0; i < K; ++i)
+      if (a.idx[(size_t)tt * K + i] == n) pos = i;
     if (valid) {
+      a.rsel[(size_t)tt * N + n] = pos >= 0 ? -1.f - (float)pos : h;
       gt[N + n] = dy / rho;
       br[n] = gp;
       gt[n] = gr;
@@ -778,9 +786,14 @@ struct BwdRowArgs {
   const void* W;      // [R][ncol] state dtype
   const float* G;     // [T][ncol]
   const float* sc;    // [T][4]
-  void* dX;           // [T][N][C], read-modify-write
-  const int* idx;     // active lists (act mode)
+  void* dX;           // [T][N][C] written (full mode: rows outside the active list; active mode: the active rows)
+  const void* d_X;    // [T][N][C] the new state's gradient (full mode; may be dX)
+  const int* idx;     // active lists
+  const float* rsel;  // [T][N]: H_pre[n] if stream n is outside token t's active list, else -1 - its position
   float* part;        // [nch][R][ncol]
+  const void* dinp;   // [T][C] the sublayer input's gradient (full mode)
+  const float* h_pre;           // [T][N] (full mode)
+  float* dxa;         // [T][K][C] float: the active rows' state gradient between the two passes
   long R;
   int ncol, T, TW, N, K, C, act;
 };
@@ -845,9 +858,30 @@ __global__ __launch_bounds__(BT) void bwd_rows_kernel(BwdRowArgs a) {
         acc0[q] = fmaf(q < ncen ? m0 : x0, g, acc0[q]);
         acc1[q] = fmaf(q < ncen ? m1 : x1, g, acc1[q]);
       }
-      T* dr = a.act ? dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + j]) * a.C + c : dX + (size_t)t * a.R + r0;
-      st1(dr, ld1(dr) + d0);
-      st1(dr + 1, ld1(dr + 1) + d1);
+      if (a.act) {
+        // the active row's gradient so far (float), plus this pass's terms, stored once
+        const float* pa = a.dxa + ((size_t)t * a.K + j) * a.C + c;
+        T* dr = dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + j]) * a.C + c;
+        st1(dr, pa[0] + d0);
+        st1(dr + 1, pa[1] + d1);
+      } else {
+        // plus the application half's share: for a row outside the active
+        // list d_X + H_pre[n] d_inp, stored once; an active row's share is
+        // already in float in the backward workspace (kept there for the
+        // active-row pass)
+        const float h = a.rsel[(size_t)t * a.N + j];
+        if (h >= 0.f) {
+          const T* di = reinterpret_cast<const T*>(a.dinp) + (size_t)t * a.C + c;
+          const T* dy = reinterpret_cast<const T*>(a.d_X) + (size_t)t * a.R + r0;
+          T* dr = dX + (size_t)t * a.R + r0;
+          st1(dr, ld1(dy) + fmaf(h, ld1(di), d0));
+          st1(dr + 1, ld1(dy + 1) + fmaf(h, ld1(di + 1), d1));
+        } else {
+          float* pa = a.dxa + ((size_t)t * a.K + (int)(-1.f - h)) * a.C + c;
+          pa[0] += d0;
+          pa[1] += d1;
+        }
+      }
     }
   }
   if (!own) return;
@@ -914,17 +948,22 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
   // chunks and this block's dX chunks are loaded ahead of the compute.
   constexpr int NCH = TB * (4 * RW / 8) / BT;   // 4
   static_assert(NCH == 4, "chunk mapping assumes 4 chunks per thread");
+  // Full mode also takes each chunk's H_pre or position in the active list
+  // one block ahead, so that the gradient loads need not wait for it.
   uint4 xn[NCH];
-  auto load_x = [&](int tb, int nt, uint4 (&dst)[NCH]) {
+  float hn[NCH];
+  auto load_x = [&](int tb, int nt) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int u = threadIdx.x + BT * k;
       const int tu = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
       const long row = rwg + rc;
-      dst[k] = (tu < nt && row < a.R) ? ld16(X + (size_t)(tb + tu) * a.R + row) : make_uint4(0, 0, 0, 0);
+      const bool in = tu < nt && row < a.R;
+      xn[k] = in ? ld16(X + (size_t)(tb + tu) * a.R + row) : make_uint4(0, 0, 0, 0);
+      if (!a.act) hn[k] = in ? a.rsel[(tb + tu) * a.N + (int)(row / a.C)] : 0.f;
     }
   };
-  if (t0 < t1) load_x(t0, t1 - t0 < TB ? t1 - t0 : TB, xn);
+  if (t0 < t1) load_x(t0, t1 - t0 < TB ? t1 - t0 : TB);
   for (int tb = t0; tb < t1; tb += TB) {
     const int nt = t1 - tb < TB ? t1 - tb : TB;
     __syncthreads();
@@ -954,9 +993,14 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
         s_c[t][1] = (t < nt && !a.act) ? a.sc[(size_t)(tb + t) * 4 + 1] : 0.f;
       }
     }
-    // this block's dX chunks, then the next block's state chunks
+    // this block's gradient chunks, then the next block's state chunks.
+    // Full mode: d_X and d_inp for a row outside the active list, the float
+    // gradient so far for one in it.  Active mode: the active row's float
+    // gradient so far.
     uint16_t* dr[NCH];
-    uint4 dv[NCH];
+    uint4 dv[NCH], fv[NCH];
+    int pos[NCH];
+    float hp[NCH];
     bool own[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -966,11 +1010,29 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
       own[k] = tu < nt && row < a.R;
       const int t = tb + (own[k] ? tu : 0);
       const long rr = own[k] ? row : 0;
-      dr[k] = a.act ? dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + (int)(rr / a.C)]) * a.C + rr % a.C
-                    : dX + (size_t)t * a.R + rr;
-      dv[k] = own[k] ? ld16(dr[k]) : make_uint4(0, 0, 0, 0);
+      const int rj = (int)(rr / a.C), rcol = (int)(rr % a.C);
+      if (a.act) {
+        dr[k] = dX + ((size_t)t * a.N + a.idx[(size_t)t * a.K + rj]) * a.C + rcol;
+        pos[k] = rj;
+      } else {
+        dr[k] = dX + (size_t)t * a.R + rr;
+        hp[k] = hn[k];
+        pos[k] = (own[k] && hp[k] < 0.f) ? (int)(-1.f - hp[k]) : -1;
+      }
+      if (pos[k] >= 0) {
+        // an active row: its float gradient so far
+        const float* pa = a.dxa + ((size_t)t * a.K + pos[k]) * a.C + rcol;
+        dv[k] = own[k] ? ld16(pa) : make_uint4(0, 0, 0, 0);
+        fv[k] = own[k] ? ld16(pa + 4) : make_uint4(0, 0, 0, 0);
+      } else {
+        // a row outside the active list: d_X and d_inp
+        dv[k] = own[k] ? ld16(reinterpret_cast<const uint16_t*>(a.d_X) + (size_t)t * a.R + rr)
+                       : make_uint4(0, 0, 0, 0);
+        fv[k] = own[k] ? ld16(reinterpret_cast<const uint16_t*>(a.dinp) + (size_t)t * a.C + rcol)
+                       : make_uint4(0, 0, 0, 0);
+      }
     }
-    if (tb + TB < t1) load_x(tb + TB, t1 - tb - TB < TB ? t1 - tb - TB : TB, xn);
+    if (tb + TB < t1) load_x(tb + TB, t1 - tb - TB < TB ? t1 - tb - TB : TB);
     __syncthreads();
     // weight gradient: dW^T[col][row] += sum over the block's tokens; the B
     // fragment (8 tokens of one row) is gathered from the token-major tile
@@ -1010,12 +1072,35 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
         const int u = threadIdx.x + BT * k;
         const int tl = u / (4 * RW / 8), rc = (u % (4 * RW / 8)) * 8;
         float v[8], x[8];
-        Bf16::unpack(dv[k], v);
         Bf16::unpack(*reinterpret_cast<const uint4*>(&s_x[tl][rc]), x);
         const float cx = s_c[tl][0], c0 = s_c[tl][1];
+        const int t = tb + tl;
+        if (pos[k] >= 0) {
+          // an active row: its float gradient so far plus this pass's terms;
+          // the active-row pass rounds it once, after adding its own
+          v[0] = __uint_as_float(dv[k].x); v[1] = __uint_as_float(dv[k].y);
+          v[2] = __uint_as_float(dv[k].z); v[3] = __uint_as_float(dv[k].w);
+          v[4] = __uint_as_float(fv[k].x); v[5] = __uint_as_float(fv[k].y);
+          v[6] = __uint_as_float(fv[k].z); v[7] = __uint_as_float(fv[k].w);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += s_d[tl - 16 * h][rc + e] + fmaf(cx, x[e], c0);
-        st16(dr[k], Bf16::pack(v));
+          for (int e = 0; e < 8; ++e) v[e] += s_d[tl - 16 * h][rc + e] + fmaf(cx, x[e], c0);
+          if (a.act) {
+            st16(dr[k], Bf16::pack(v));
+          } else {
+            const long rr = rwg + rc;
+            float* pa = a.dxa + ((size_t)t * a.K + pos[k]) * a.C + rr % a.C;
+            *reinterpret_cast<float4*>(pa) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(pa + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          }
+        } else {
+          // a row outside the active list: d_X + H_pre d_inp + this pass's terms, rounded once
+          float fi[8];
+          Bf16::unpack(fv[k], fi);
+          Bf16::unpack(dv[k], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += fmaf(hp[k], fi[e], s_d[tl - 16 * h][rc + e] + fmaf(cx, x[e], c0));
+          st16(dr[k], Bf16::pack(v));
+        }
       }
     }
   }
@@ -1088,6 +1173,7 @@ bool make_bwd_plan(const Plan& P, BwdPlan* B) {
   q.o_dhpost = take(T * K * KR * 4);
   q.o_dp = take(T * K * 4);
   q.o_xa = take(T * K * C * es);
+  q.o_dxa = take(T * K * C * 4);
   q.o_dg = KR == 4 ? take(T * 4 * C * 4) : SIZE_MAX;
   q.o_cpart = KR == 4 ? take((size_t)q.nch_c * NCONV * C * 4) : SIZE_MAX;
   q.o_wpa = take((size_t)q.nkb_a * q.NTA * 64 * 16);
@@ -1096,6 +1182,7 @@ bool make_bwd_plan(const Plan& P, BwdPlan* B) {
   q.o_gt = take(T * q.ncol_f * 4);
   q.o_ga = take(T * q.ncol_a * 4);
   q.o_sc = take(T * 4 * 4);
+  q.o_rsel = take(T * N * 4);
   q.o_brow = take(T * q.NBT * 4);
   q.o_bsum = take((size_t)q.NBT * 4);
   q.o_colsum = take(N * 4);
@@ -1111,16 +1198,16 @@ namespace {
 
 template <class E, int N, int K, int KR>
 void apply_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, const void* out,
-                  const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws,
-                  char* bws, hipStream_t st) {
+                  const void* d_inp, const void* d_X, void* d_out, float* d_conv, const char* ws, char* bws,
+                  hipStream_t st) {
   BwdApplyArgs a{};
   a.X = X;
   a.out = out;
   a.d_inp = d_inp;
   a.d_X = d_X;
-  a.dX = dX;
   a.d_out = d_out;
   a.xa = bws + Bp.o_xa;
+  a.dxa = reinterpret_cast<float*>(bws + Bp.o_dxa);
   a.dg = KR == 4 ? reinterpret_cast<float*>(bws + Bp.o_dg) : nullptr;
   a.conv_w = w->conv_w;
   a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
@@ -1175,8 +1262,8 @@ void rows_dispatch(const BwdRowArgs& a, int nch, hipStream_t st) {
 }
 
 template <class E, int N, int K, int KR>
-void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
-                const char* ws, char* bws, hipStream_t st) {
+void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, const void* d_inp,
+                const void* d_X, void* dX, const xhc_grads* g, const char* ws, char* bws, hipStream_t st) {
   const int dt = P.dtype;
   const int T = (int)P.T;
   float* parta = reinterpret_cast<float*>(bws + Bp.o_parta);
@@ -1219,6 +1306,7 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
   a.Ga = reinterpret_cast<float*>(bws + Bp.o_ga);
   a.sc = reinterpret_cast<float*>(bws + Bp.o_sc);
   a.brow = reinterpret_cast<float*>(bws + Bp.o_brow);
+  a.rsel = reinterpret_cast<float*>(bws + Bp.o_rsel);
   bwd_token_kernel<N, K, KR><<<(T + 15) / 16, BT, 0, st>>>(a);
   BwdSumArgs s{};
   s.rows = a.brow;
@@ -1240,6 +1328,7 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
   r.G = a.Gt;
   r.sc = a.sc;
   r.dX = dX;
+  r.d_X = d_X;
   r.idx = a.idx;
   r.part = reinterpret_cast<float*>(bws + Bp.o_wpartf);
   r.R = Bp.NC;
@@ -1250,6 +1339,10 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
   r.K = K;
   r.C = P.C;
   r.act = 0;
+  r.dinp = d_inp;
+  r.h_pre = reinterpret_cast<const float*>(ws + P.o_hpre);
+  r.dxa = reinterpret_cast<float*>(bws + Bp.o_dxa);
+  r.rsel = a.rsel;
   rows_dispatch<E>(r, Bp.nch_f, st);
   const long nf = Bp.NC * Bp.ncol_f;
   // the bf16 pass accumulates uncentred rows: subtract sum_t mu_t G_t from the router columns
@@ -1273,11 +1366,11 @@ void gen_launch(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const vo
 
 template <class E, int KR>
 bool apply_shape(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, const void* out,
-                 const void* d_inp, const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws, char* bws,
+                 const void* d_inp, const void* d_X, void* d_out, float* d_conv, const char* ws, char* bws,
                  hipStream_t st) {
 #define XHC_BWD_APPLY(n, k) \
   if (P.N == n && P.K == k) { \
-    apply_launch<E, n, k, KR>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st); \
+    apply_launch<E, n, k, KR>(P, Bp, w, X, out, d_inp, d_X, d_out, d_conv, ws, bws, st); \
     return true; \
   }
   XHC_BWD_APPLY(16, 4)
@@ -1290,11 +1383,11 @@ bool apply_shape(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const v
 }
 
 template <class E, int KR>
-bool gen_shape(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
-               const char* ws, char* bws, hipStream_t st) {
+bool gen_shape(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const void* X, const void* d_inp,
+               const void* d_X, void* dX, const xhc_grads* g, const char* ws, char* bws, hipStream_t st) {
 #define XHC_BWD_GEN(n, k) \
   if (P.N == n && P.K == k) { \
-    gen_launch<E, n, k, KR>(P, Bp, w, X, dX, g, ws, bws, st); \
+    gen_launch<E, n, k, KR>(P, Bp, w, X, d_inp, d_X, dX, g, ws, bws, st); \
     return true; \
   }
   XHC_BWD_GEN(16, 4)
@@ -1309,26 +1402,25 @@ bool gen_shape(const Plan& P, const BwdPlan& Bp, const xhc_weights* w, const voi
 }  // namespace
 
 bool launch_xhc_post_backward(const Plan& P, const xhc_weights* w, const void* X, const void* out, const void* d_inp,
-                              const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws, char* bws,
-                              hipStream_t st) {
+                              const void* d_X, void* d_out, float* d_conv, const char* ws, char* bws, hipStream_t st) {
   BwdPlan Bp;
   make_bwd_plan(P, &Bp);
   if (P.dtype == XHC_BF16)
-    return P.KR == 4 ? apply_shape<Bf16, 4>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st)
-                     : apply_shape<Bf16, 1>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st);
-  return P.KR == 4 ? apply_shape<F32, 4>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st)
-                   : apply_shape<F32, 1>(P, Bp, w, X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws, st);
+    return P.KR == 4 ? apply_shape<Bf16, 4>(P, Bp, w, X, out, d_inp, d_X, d_out, d_conv, ws, bws, st)
+                     : apply_shape<Bf16, 1>(P, Bp, w, X, out, d_inp, d_X, d_out, d_conv, ws, bws, st);
+  return P.KR == 4 ? apply_shape<F32, 4>(P, Bp, w, X, out, d_inp, d_X, d_out, d_conv, ws, bws, st)
+                   : apply_shape<F32, 1>(P, Bp, w, X, out, d_inp, d_X, d_out, d_conv, ws, bws, st);
 }
 
-bool launch_xhc_pre_backward(const Plan& P, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
-                             const char* ws, char* bws, hipStream_t st) {
+bool launch_xhc_pre_backward(const Plan& P, const xhc_weights* w, const void* X, const void* d_inp, const void* d_X,
+                             void* dX, const xhc_grads* g, const char* ws, char* bws, hipStream_t st) {
   BwdPlan Bp;
   make_bwd_plan(P, &Bp);
   if (P.dtype == XHC_BF16)
-    return P.KR == 4 ? gen_shape<Bf16, 4>(P, Bp, w, X, dX, g, ws, bws, st)
-                     : gen_shape<Bf16, 1>(P, Bp, w, X, dX, g, ws, bws, st);
-  return P.KR == 4 ? gen_shape<F32, 4>(P, Bp, w, X, dX, g, ws, bws, st)
-                   : gen_shape<F32, 1>(P, Bp, w, X, dX, g, ws, bws, st);
+    return P.KR == 4 ? gen_shape<Bf16, 4>(P, Bp, w, X, d_inp, d_X, dX, g, ws, bws, st)
+                     : gen_shape<Bf16, 1>(P, Bp, w, X, d_inp, d_X, dX, g, ws, bws, st);
+  return P.KR == 4 ? gen_shape<F32, 4>(P, Bp, w, X, d_inp, d_X, dX, g, ws, bws, st)
+                   : gen_shape<F32, 1>(P, Bp, w, X, d_inp, d_X, dX, g, ws, bws, st);
 }
 
 }  // namespace xhc

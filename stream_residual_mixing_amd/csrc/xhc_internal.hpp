@@ -105,16 +105,16 @@ struct BwdPlan {
   long NC = 0, KC = 0, nkb_f = 0, nkb_a = 0;
   int ncol_f = 0, ncol_a = 0, NTF = 0, NTA = 0, KSa = 1, NBT = 0;
   int nch_f = 1, nch_a = 1, TW_f = 0, TW_a = 0, nch_c = 1, TC = 0;
-  size_t o_dhpre = 0, o_dhres = 0, o_dhpost = 0, o_dp = 0, o_xa = 0, o_dg = SIZE_MAX, o_cpart = SIZE_MAX,
-         o_wpa = 0, o_parta = 0, o_statsa = 0, o_gt = 0, o_ga = 0, o_sc = 0,
+  size_t o_dhpre = 0, o_dhres = 0, o_dhpost = 0, o_dp = 0, o_xa = 0, o_dxa = 0, o_dg = SIZE_MAX,
+         o_cpart = SIZE_MAX,
+         o_wpa = 0, o_parta = 0, o_statsa = 0, o_gt = 0, o_ga = 0, o_sc = 0, o_rsel = 0,
          o_brow = 0, o_bsum = 0, o_colsum = 0, o_colpart = 0, o_wpartf = 0, o_wparta = 0, total = 0;
 };
 bool make_bwd_plan(const Plan& P, BwdPlan* B);
 bool launch_xhc_post_backward(const Plan& P, const xhc_weights* w, const void* X, const void* out, const void* d_inp,
-                              const void* d_X, void* dX, void* d_out, float* d_conv, const char* ws, char* bws,
-                              hipStream_t st);
-bool launch_xhc_pre_backward(const Plan& P, const xhc_weights* w, const void* X, void* dX, const xhc_grads* g,
-                             const char* ws, char* bws, hipStream_t st);
+                              const void* d_X, void* d_out, float* d_conv, const char* ws, char* bws, hipStream_t st);
+bool launch_xhc_pre_backward(const Plan& P, const xhc_weights* w, const void* X, const void* d_inp, const void* d_X,
+                             void* dX, const xhc_grads* g, const char* ws, char* bws, hipStream_t st);
 
 
 bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st);

@@ -278,10 +278,10 @@ def test_backward_calls_reject_bad_arguments_before_launch(lib):
 
     def pb(c, w, *a):
         return post(ctypes.byref(c), ctypes.byref(w), *a, None)
-    args = [X, out, d_inp, d_X, dX, d_out, d_conv, ws, bws]
+    args = [X, out, d_inp, d_X, d_out, d_conv, ws, bws]
     # misaligned, NULL, aliased
     bad = list(args)
-    bad[4] = 0x60008
+    bad[4] = 0x70008
     assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG and "aligned" in lib.last_error()
     bad = list(args)
     bad[0] = None
@@ -290,11 +290,14 @@ def test_backward_calls_reject_bad_arguments_before_launch(lib):
     bad[4] = X
     assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
     bad = list(args)
-    bad[5] = d_X
+    bad[4] = d_X
+    assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
+    bad = list(args)
+    bad[7] = d_out
     assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG
     # MLP-type needs d_conv and the conv kernels; attention-type needs neither
     bad = list(args)
-    bad[6] = None
+    bad[5] = None
     assert pb(ok, xw, *bad) == binding.XHC_ERR_INVALID_ARG and "d_conv" in lib.last_error()
     w = XhcWeights()
     w.w_full = w.w_act = w.b_pre = w.b_res = w.b_post = 0x10000
@@ -302,20 +305,28 @@ def test_backward_calls_reject_bad_arguments_before_launch(lib):
     # unsupported (N, k) and an empty batch
     assert pb(_cfg(k=3, m=1).c(), xw, *args) == binding.XHC_ERR_UNSUPPORTED
     e = _cfg(B=0).c()
-    assert pb(e, xw, *([None] * 9)) == binding.XHC_OK
+    assert pb(e, xw, *([None] * 8)) == binding.XHC_OK
     # generation half: every gradient pointer, aligned buffers, no aliasing
+    # except dX on d_X
     pre = d.xhc_pre_backward
     g = binding.XhcGrads(0xb0000, 0xc0000, 0xd0000, 0xd1000, 0xd2000, 0xd3000)
-    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, X, ctypes.byref(g), ws, bws, None) == \
+
+    def qb(c, *a):
+        return pre(ctypes.byref(c), ctypes.byref(xw), *a, None)
+    assert qb(ok, X, d_inp, d_X, X, ctypes.byref(g), ws, bws) == \
         binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
-    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, 0x60004, ctypes.byref(g), ws, bws, None) == \
+    assert qb(ok, X, d_inp, d_X, d_inp, ctypes.byref(g), ws, bws) == \
+        binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
+    assert qb(ok, X, d_inp, d_X, dX, ctypes.byref(g), ws, d_X) == \
+        binding.XHC_ERR_INVALID_ARG and "alias" in lib.last_error()
+    assert qb(ok, X, d_inp, d_X, 0x60004, ctypes.byref(g), ws, bws) == \
         binding.XHC_ERR_INVALID_ARG and "aligned" in lib.last_error()
+    assert qb(ok, X, None, d_X, dX, ctypes.byref(g), ws, bws) == binding.XHC_ERR_INVALID_ARG
     g2 = binding.XhcGrads(0xb0000, 0xc0000, 0xd0000, 0xd1000, 0xd2000, 0)
-    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, dX, ctypes.byref(g2), ws, bws, None) == \
+    assert qb(ok, X, d_inp, d_X, dX, ctypes.byref(g2), ws, bws) == \
         binding.XHC_ERR_INVALID_ARG and "gradient" in lib.last_error()
-    assert pre(ctypes.byref(ok), ctypes.byref(xw), X, dX, None, ws, bws, None) == binding.XHC_ERR_INVALID_ARG
-    assert pre(ctypes.byref(attn), ctypes.byref(xw), X, dX, ctypes.byref(g), bws, bws, None) == \
-        binding.XHC_ERR_INVALID_ARG
+    assert qb(ok, X, d_inp, d_X, dX, None, ws, bws) == binding.XHC_ERR_INVALID_ARG
+    assert qb(attn, X, d_inp, d_X, dX, ctypes.byref(g), bws, bws) == binding.XHC_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers: run on a host without a GPU only")

@@ -15,7 +15,7 @@ def test_layer_byte_models():
     cfg = Config(N=16, k=4, m=2, C=4096, B=2, S=8192, n_convs=3, dtype="bf16")
     C2 = 4096 * 2
     assert bench.bytes_per_token("xhc", cfg) == (17 * C2, 9 * C2)          # 26C per layer
-    assert bench.bytes_per_token("xhcb", cfg) == (51 * C2, 48 * C2)        # backward: (3N + 3)C, 3N C
+    assert bench.bytes_per_token("xhcb", cfg) == (23 * C2, 45 * C2)        # backward: (N + k + 3)C, (3N - k + 1)C
     assert sum(bench.flash_bytes_per_token(cfg)) == 54 * C2                # Flash: 54C per block
     assert sum(bench.flash4_bytes_per_token(cfg)) == 90 * C2               # 4sub: 90C per group
 

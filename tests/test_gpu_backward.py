@@ -9,10 +9,9 @@ gradient (sum of the halves), d_out and the conv-kernel gradients
 half, fed with the oracle's own map gradients).
 
 Tolerance: bf16 cases store dX and d_out in bf16 (relative rounding 2^-9) and
-read bf16 inputs, so they take the forward's bf16 bound; the state gradient
-is stored three times on its way (application half, then the generation
-half's full-state and active-row passes), and where those parts cancel each
-store's rounding is allowed for, one ulp of the value it held.  Float cases
+read bf16 inputs, so they take the forward's bf16 bound, with no allowance:
+the state gradient's parts (application half, then the generation half's
+full-state and active-row passes) are summed in float and rounded once.  Float cases
 accumulate in float over up to N*C products per token and T tokens per weight
 gradient and run the Sinkhorn tangent through 20 normalisation rounds in
 float, which the 1e-3 bound covers with margin (the errors printed are about
@@ -54,10 +53,11 @@ def run_backward(lib, cfg, X, out, wd, d_inp, d_X, chained=False):
     dX = torch.empty_like(Xd)
     d_out = torch.empty_like(outd)
     d_conv = torch.empty((24, cfg.C), dtype=torch.float32, device="cuda") if cfg.K_r == 4 else None
-    lib.xhc_post_backward(cfg, w, Xd, outd, d_inp.cuda(), d_X.cuda(), dX, d_out, d_conv, ws, bws)
+    d_inpd, d_Xd = d_inp.cuda(), d_X.cuda()
+    lib.xhc_post_backward(cfg, w, Xd, outd, d_inpd, d_Xd, d_out, d_conv, ws, bws)
     dmaps = {k: v.clone() for k, v in lib.backward_ws_arrays(cfg, bws).items()}
     g = lib.grads(cfg)
-    lib.xhc_pre_backward(cfg, w, Xd, dX, g, ws, bws)
+    lib.xhc_pre_backward(cfg, w, Xd, d_inpd, d_Xd, dX, g, ws, bws)
     torch.cuda.synchronize()
     res = dict(X=dX.cpu(), out=d_out.cpu(), **{"d_" + k: v.cpu() for k, v in dmaps.items()},
                **{k: v.cpu() for k, v in g.items()}, I=maps["idx"].cpu().numpy())
@@ -79,15 +79,11 @@ def oracle_backward(cfg, X, out, ow, d_inp, d_X):
 
 
 def dx_err(cfg, dX, ga, gg):
-    """The state gradient is stored three times in the state dtype: by the
-    application half, after the full-state pass and after the active-row
-    pass of the generation half.  Each store may round by one ulp of the
-    value it holds, which the error is allowed on top of the usual bound."""
-    part1 = ga["X"]
-    part2 = part1 + gg["X_full"]
-    final = part2 + gg["X_act"]
-    allow = sum(K.ulp(np.abs(v), cfg.dtype) for v in (part1, part2, final))
-    return K.err_with_allowance(K.f64(dX), final, allow)
+    """The state gradient: the application half's part (through the dense
+    read and the mix) plus the generation half's parts (through the
+    full-state norms and projections, and through the active rows'), formed
+    in float and rounded once to the state dtype; plain relative error."""
+    return K.rel_err(K.f64(dX), ga["X"] + gg["X_full"] + gg["X_act"])
 
 
 def compare(cfg, g, pre, ga, gg):
@@ -214,9 +210,9 @@ def test_backward_in_place_gradient(lib):
         dX = d_X.clone() if in_place else torch.empty_like(d_X)
         src = dX if in_place else d_X
         d_out = torch.empty_like(outd)
-        lib.xhc_post_backward(cfg, w, Xd, outd, d_inp, src, dX, d_out, d_conv, ws, bws)
+        lib.xhc_post_backward(cfg, w, Xd, outd, d_inp, src, d_out, d_conv, ws, bws)
         g = lib.grads(cfg)
-        lib.xhc_pre_backward(cfg, w, Xd, dX, g, ws, bws)
+        lib.xhc_pre_backward(cfg, w, Xd, d_inp, src, dX, g, ws, bws)
         torch.cuda.synchronize()
         res.append((dX.cpu(), d_out.cpu(), d_conv.cpu(), {k: v.cpu() for k, v in g.items()}))
     for a, b in zip(res[0][:3], res[1][:3]):
@@ -233,9 +229,9 @@ def test_backward_empty_batch_is_a_no_op(lib):
     e2 = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     ws, bws = lib.workspace(cfg), lib.backward_workspace(cfg)
     d_conv = torch.full((24, 64), 7.0, device="cuda")
-    lib.xhc_post_backward(cfg, w, e, e2, e2, e, e.clone(), e2.clone(), d_conv, ws, bws)
+    lib.xhc_post_backward(cfg, w, e, e2, e2, e, e2.clone(), d_conv, ws, bws)
     g = lib.grads(cfg)
-    lib.xhc_pre_backward(cfg, w, e, e.clone(), g, ws, bws)
+    lib.xhc_pre_backward(cfg, w, e, e2, e, e.clone(), g, ws, bws)
     torch.cuda.synchronize()
     assert torch.all(d_conv == 7.0), "nothing is written for an empty batch"
 
@@ -322,10 +318,10 @@ def test_backward_full_size_sampled_tokens(lib, nconv, layer):
     dX = torch.empty_like(Xd)
     d_out = torch.empty_like(outd)
     d_conv = torch.empty((24, C), dtype=torch.float32, device="cuda") if nconv else None
-    lib.xhc_post_backward(cfg, w, Xd, outd, d_inpd, d_Xd, dX, d_out, d_conv, ws, bws)
+    lib.xhc_post_backward(cfg, w, Xd, outd, d_inpd, d_Xd, d_out, d_conv, ws, bws)
     dmaps = {key: v.clone() for key, v in lib.backward_ws_arrays(cfg, bws).items()}
     g = lib.grads(cfg)
-    lib.xhc_pre_backward(cfg, w, Xd, dX, g, ws, bws)
+    lib.xhc_pre_backward(cfg, w, Xd, d_inpd, d_Xd, dX, g, ws, bws)
     torch.cuda.synchronize()
     for name, v in [("dX", dX), ("d_out", d_out)] + list(g.items()) + ([("d_conv", d_conv)] if nconv else []):
         assert bool(torch.isfinite(v).all()), f"{name} has non-finite entries"
@@ -335,10 +331,8 @@ def test_backward_full_size_sampled_tokens(lib, nconv, layer):
                **{key: v.index_select(0, tk).cpu() for key, v in dmaps.items()})
     o = {key: np.stack([ref[int(t)][key] for t in toks]) for key in ref[int(toks[0])]}
     assert np.array_equal(idx, o["I"]), "active indices differ"
-    part2 = o["X_apply"] + o["X_full"]
-    allow = sum(K.ulp(np.abs(v), "bf16") for v in (o["X_apply"], part2, o["X"]))
     errs = {
-        "dX": K.err_with_allowance(K.f64(got["X"]), o["X"], allow),
+        "dX": K.rel_err(K.f64(got["X"]), o["X"]),
         "d_out": K.rel_err(K.f64(got["d_out"]), o["d_out"]),
         **{"d_" + key: K.rel_err(K.f64(got[key]), o[key]) for key in ("h_pre", "h_res", "h_post", "p")},
     }
