@@ -528,9 +528,13 @@ xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const x
   if (P.T == 0) return XHC_OK;
   if ((s = check_state_ws(X, out, ws, chained ? ws_next : nullptr, chained)) != XHC_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (!xhc::launch_xhc_post(P, X, out, w, static_cast<char*>(ws), st))
+  // attention-type with a next sublayer: the write and the next routing's
+  // correction in one pass
+  const bool fuse = chained && xhc::chain_post_fused(P);
+  if (!fuse && !xhc::launch_xhc_post(P, X, out, w, static_cast<char*>(ws), st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
-  if (chained && !xhc::launch_xhc_chain_tail(P, Pn, w_next, X, static_cast<char*>(ws), static_cast<char*>(ws_next), st))
+  if (chained && !xhc::launch_xhc_chain_tail(P, Pn, w_next, X, out, static_cast<char*>(ws), static_cast<char*>(ws_next),
+                                             fuse, st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }

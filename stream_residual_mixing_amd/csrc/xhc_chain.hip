@@ -714,25 +714,26 @@ __device__ __forceinline__ void slice_colsums(const u32x4_t (&s_w)[PSB][N][NTF][
 // fragments are read ROUTE_BD - 1 MFMAs ahead of their use (a ring of
 // ROUTE_BD registers), each step pinned by a scheduling barrier: left to
 // itself the compiler reads each fragment right before its MFMA and waits
-// for the LDS every time.
+// for the LDS every time.  The first S0 streams are known to be masked
+// (the fixed streams of the active list) and are skipped.
 #ifndef XHC_ROUTE_BD
 #define XHC_ROUTE_BD 2
 #endif
-template <class E, int N, int NTF, int BD = XHC_ROUTE_BD>
+template <class E, int N, int NTF, int S0 = 0, int BD = XHC_ROUTE_BD>
 __device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)[N][NTF][WAVE], int lane, uint32_t amask,
                                           f32x4_t (&acc)[NTF], f32x4_t& S1, f32x4_t& S2) {
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
-  constexpr int TOT = N * NTF;
+  constexpr int TOT = N * NTF, Q0 = S0 * NTF;
 #pragma unroll
   for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   S1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
   S2 = S1;
   u32x4_t b[BD];
 #pragma unroll
-  for (int q = 0; q < BD - 1 && q < TOT; ++q) b[q] = w[q / NTF][q % NTF][lane];
+  for (int q = Q0; q < Q0 + BD - 1 && q < TOT; ++q) b[q % BD] = w[q / NTF][q % NTF][lane];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
+  for (int i = S0; i < N; ++i) {
     const u32x4_t v = ((amask >> i) & 1u) ? zero : xs.x[i];
     mma_sums<E>(v, ones, S1, S2);
 #pragma unroll
@@ -999,7 +1000,11 @@ __global__ __launch_bounds__(256) void xhcf_route_fin_kernel(FlashRouteFinArgs a
 // active partials of this layer, masked routing partials of the next one).
 // The routing of the next step (h_pre rows, then active lists) is loaded by
 // the first RQ threads along with the state and moved to LDS after compute.
-template <class E, int N, int K, int KR>
+// MS: the number of fixed streams when known at compile time (-1: a.m at run
+// time); fixed position j then reads stream j directly, a routed one selects
+// among streams MS .. N-1 only, and the fixed streams (always in the active
+// list) drop out of the next layer's routing partials without any MFMA.
+template <class E, int N, int K, int KR, int MS>
 __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArgs a) {
   using T = typename E::T;
   using D = RouteDims<N>;
@@ -1107,9 +1112,9 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
       if (tile < a.ntiles && tok < a.T)
         st16_nt(reinterpret_cast<T*>(a.inp) + (size_t)tok * C + kb0 * KB + VEC * g, E::packv(o));
     }
-    // the next step's routing to the other buffer (every wave has finished
-    // reading it before the last barrier of the previous step)
-    store_route(buf ^ 1, rnext);
+    // with m known at run time only, the longer-lived register would spill:
+    // the next step's routing goes to LDS here (see below)
+    if constexpr (MS < 0) store_route(buf ^ 1, rnext);
     // gather of the k active rows, their sum of squares and active projection
     f32x4_t acc2[NTA], SS = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1117,11 +1122,22 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       // position j < m holds stream j; a routed position holds one of m..N-1
-      u32x4_t v = xs.x[j < N ? j : 0];
-      if (j >= a.m) {
+      u32x4_t v;
+      if constexpr (MS >= 0) {
+        if (j < MS) {
+          v = xs.x[j];
+        } else {
+          v = xs.x[MS < N ? MS : 0];
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-          if (i != j) v = (I[j] == i) ? xs.x[i] : v;
+          for (int i = MS + 1; i < N; ++i) v = (I[j] == i) ? xs.x[i] : v;
+        }
+      } else {
+        v = xs.x[j < N ? j : 0];
+        if (j >= a.m) {
+#pragma unroll
+          for (int i = 0; i < N; ++i)
+            if (i != j) v = (I[j] == i) ? xs.x[i] : v;
+        }
       }
       SS = E::mma(SS, v, v);
 #pragma unroll
@@ -1129,7 +1145,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
     }
     // next layer's routing over the rows this layer leaves as they are
     f32x4_t acc[NTF], S1, S2;
-    route_mma<E, N, NTF>(xs, s_w[cb], lane, amask, acc, S1, S2);
+    route_mma<E, N, NTF, (MS > 0 ? MS : 0)>(xs, s_w[cb], lane, amask, acc, S1, S2);
     route_partials<N>(s_red, s_acs, acc, S1, S2, a.look, G, slice, step, a.ntiles, tid, wave, g, r);
     acc_to_lds<NTA, NPA>(s_red, wave, g, r, acc2);
     if ((r >> 2) == g) s_red[wave][TM * NPA + r] = diag_of(SS, r);
@@ -1147,6 +1163,12 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
         if (t16 < a.ntiles) a.part2[((size_t)t16 * G + slice) * P2 + v] = x;
       }
     }
+    // the next step's routing to the other buffer, last: its load was issued
+    // with the next step's state, so waiting for it here rather than early
+    // in this step leaves the whole compute to cover its latency (every wave
+    // has finished reading that buffer before the last barrier of the
+    // previous step)
+    if constexpr (MS >= 0) store_route(buf ^ 1, rnext);
     __syncthreads();
   };
 
@@ -1163,6 +1185,291 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
     __builtin_amdgcn_sched_barrier(0);
     compute(xb, p1, 1, rt);
     p = p2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent post pass of a layer with a next layer: the rewritten rows'
+// share of the next layer's routing (the correction), and for an
+// attention-type layer (FUSE) the write itself, so the new rows are
+// contracted from registers instead of being read back.
+//
+// A workgroup owns one slice of PSB contraction blocks for the whole launch
+// with the next layer's routing fragments of that slice in LDS, and walks
+// steps of PTL 16-token tiles, one wave per (tile, block); lane (g, r) holds
+// token r of its tile, VEC channels of its block.  Per step a lane loads the
+// k active rows of its token (FUSE: and its row of out), FUSE forms the new
+// rows x'_j = sum_i H_res[j][i] x_{I_i} + p_j H_post[j] out (the
+// per-sublayer write's arithmetic, in its order) and stores them in place;
+// then per stream i of the next layer the MFMA takes, per token, the new row
+// that sits in stream i (zero if none) against that stream's fragments, and
+// the new rows' sums of x and x^2 go through the matrix cores as in the pre
+// pass.  The partials of the PSB waves of a tile are summed in LDS and
+// written per (tile, slice) in the routing partials' layout.
+//
+// The state loads run PD steps ahead (PD + 1 register sets), as the k rows
+// of a step are few bytes per lane.  Their addresses need the active lists
+// PD steps ahead, so the lists run one step further: loaded into LDS PD + 1
+// steps ahead, a ring of PD + 2 slots.  FUSE: the write coefficients of the
+// next step are loaded during this one, double-buffered in LDS.
+// ---------------------------------------------------------------------------
+struct PostPArgs {
+  void* X;
+  const void* out;                      // FUSE
+  const int* idx;                       // [T][K]
+  const float *h_res, *p, *h_post;      // FUSE: [T][K][K], [T][K], [T][K]
+  int T, C, G, ntiles;
+  const uint4* wnext;                   // next layer's packed [W_r | W_pre]
+  float* corr;                          // [ntiles][G][P1] (the first NSUM entries of each)
+};
+
+#ifndef XHC_POST_PD
+#define XHC_POST_PD 2
+#endif
+constexpr int POST_PD = XHC_POST_PD;   // steps of state loads in flight ahead of the compute
+
+// Calls f(std::integral_constant<int, Q>) for Q = 0 .. NQ - 1.
+template <int NQ, int Q = 0, class F>
+__device__ __forceinline__ void for_each_c(F&& f) {
+  if constexpr (Q < NQ) {
+    f(std::integral_constant<int, Q>{});
+    for_each_c<NQ, Q + 1>(f);
+  }
+}
+
+template <int K, bool FUSE>
+struct PStep {
+  u32x4_t x[K];
+  u32x4_t o;   // out (FUSE)
+};
+
+template <class E, int N, int K, int MS, bool FUSE>
+__global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  constexpr int PD = POST_PD, NR = PD + 1, NI = PD + 2;
+  constexpr int STT = PTL * TM;                     // tokens per step
+  // per-step rows moved through LDS, in 16-byte units: the active lists,
+  // then (FUSE) H_res, p and H_post
+  constexpr int UI = STT * K / 4, UH = FUSE ? STT * K * K / 4 : 0, UP = FUSE ? STT * K / 4 : 0;
+  // each array is loaded by whole waves of its own, so that its buffer
+  // resource stays uniform over a wave
+  constexpr int WI = (UI + WAVE - 1) / WAVE, WH = (UH + WAVE - 1) / WAVE, WP = (UP + WAVE - 1) / WAVE;
+  static_assert((STT * K) % 4 == 0 && WI + WH + 2 * WP <= TWV, "a step's rows fit one unit per thread");
+  constexpr int CF = FUSE ? STT * (K * K + 2 * K) : 1;
+  __shared__ u32x4_t s_w[PSB][N][NTF][WAVE];
+  __shared__ float s_red[TWV][NSUM];
+  __shared__ int s_idx[NI][STT * K];
+  __shared__ float s_cf[2][CF];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = wave / PSB, cb = wave % PSB;
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int nsteps = (a.ntiles + PTL - 1) / PTL;
+  const int kb0 = slice * PSB + cb;
+  const bool kvalid = kb0 < nkbC;
+  const int tau = TM * b + r;   // the lane's token within a step
+  const int full = a.T / STT, tail = a.T % STT;
+  // byte offset of the lane's fragment within its token's row of one stream
+  const uint32_t cofs = (uint32_t)(((size_t)kb0 * KB + VEC * g) * sizeof(T));
+  T* X = reinterpret_cast<T*>(a.X);
+  const T* out = reinterpret_cast<const T*>(a.out);
+
+  // one 16-byte unit of a step's rows; the resource spans the step's valid
+  // tokens, so anything past them reads zero
+  // Every wave issues the load (one without a share reads an empty range),
+  // so that no memory operation sits under a branch.
+  auto load_unit = [&](int step, bool lists, bool coefs) __attribute__((always_inline)) {
+    const int valid = step_rows(step, full, tail);
+    const size_t ts = valid > 0 ? (size_t)STT * step : 0;
+    const void* base = a.idx;
+    uint32_t bytes = 0, first = 0;
+    if (wave < WI) {
+      base = a.idx + ts * K;
+      bytes = lists ? (uint32_t)(valid * K * 4) : 0u;
+    } else if (wave < WI + WH) {
+      base = a.h_res + ts * K * K;
+      bytes = coefs ? (uint32_t)(valid * K * K * 4) : 0u;
+      first = WI;
+    } else if (wave < WI + WH + WP) {
+      base = a.p + ts * K;
+      bytes = coefs ? (uint32_t)(valid * K * 4) : 0u;
+      first = WI + WH;
+    } else if (wave < WI + WH + 2 * WP) {
+      base = a.h_post + ts * K;
+      bytes = coefs ? (uint32_t)(valid * K * 4) : 0u;
+      first = WI + WH + WP;
+    }
+    return ld_b128(make_rsrc(base, bytes), (uint32_t)(16 * ((wave - (int)first) * WAVE + lane)), 0);
+  };
+  // s_cf: H_res [STT][K][K], then p [STT][K], then H_post [STT][K]
+  auto store_unit = [&](const u32x4_t& v, int islot, int cbuf, bool lists, bool coefs) __attribute__((always_inline)) {
+    if (wave < WI) {
+      const int u = wave * WAVE + lane;
+      if (lists && u < UI) *reinterpret_cast<u32x4_t*>(&s_idx[islot][4 * u]) = v;
+    } else if (wave < WI + WH + 2 * WP && coefs) {
+      // q: the unit within its array; base: the array's first unit in s_cf
+      int q, n, base;
+      if (wave < WI + WH) { q = (wave - WI) * WAVE + lane; n = UH; base = 0; }
+      else if (wave < WI + WH + WP) { q = (wave - WI - WH) * WAVE + lane; n = UP; base = UH; }
+      else { q = (wave - WI - WH - WP) * WAVE + lane; n = UP; base = UH + UP; }
+      if (q < n) *reinterpret_cast<u32x4_t*>(&s_cf[cbuf][4 * (base + q)]) = v;
+    }
+  };
+  // the lane's state loads of a step: its k active rows (FUSE: and out)
+  // The step's rows of X (of out): a wave whose block lies past C gets an
+  // empty range, so its loads read zeros and its stores are dropped.
+  auto x_rsrc = [&](int step) __attribute__((always_inline)) {
+    const int rows = kvalid ? step_rows(step, full, tail) : 0;
+    return make_rsrc(X + (size_t)(rows > 0 ? step : 0) * STT * N * C, (uint32_t)((size_t)rows * N * C * sizeof(T)));
+  };
+  auto issue = [&](PStep<K, FUSE>& st, int step, int islot) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rx = x_rsrc(step);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int ij = s_idx[islot][tau * K + j];
+      ij = ij < 0 ? 0 : (ij >= N ? N - 1 : ij);
+      st.x[j] = ld_b128(rx, (uint32_t)(((size_t)tau * N + ij) * C * sizeof(T)) + cofs, 0);
+    }
+    if constexpr (FUSE) {
+      const int rows = kvalid ? step_rows(step, full, tail) : 0;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (size_t)(rows > 0 ? step : 0) * STT * C,
+                                                  (uint32_t)((size_t)rows * C * sizeof(T)));
+      st.o = ld_b128(ro, (uint32_t)((size_t)tau * C * sizeof(T)) + cofs, 0);
+    }
+  };
+  const __amdgpu_buffer_rsrc_t rcorr = make_rsrc(a.corr, (uint32_t)((size_t)a.ntiles * G * P1 * 4));
+
+  // prologue: routing fragments and column sums of the slice, the lists of
+  // the first PD + 1 steps, the coefficients of the first, then the state
+  // loads of the first PD steps
+  load_wslice<N, NTF>(s_w, a.wnext, nkbC, slice, tid);
+  {
+    u32x4_t v[NI - 1];
+#pragma unroll
+    for (int d = 0; d < NI - 1; ++d) v[d] = load_unit(team + d * nteams, true, d == 0);
+#pragma unroll
+    for (int d = 0; d < NI - 1; ++d) store_unit(v[d], d, 0, true, d == 0);
+  }
+  __syncthreads();
+  PStep<K, FUSE> sr[NR];
+#pragma unroll
+  for (int d = 0; d < PD; ++d) issue(sr[d], team + d * nteams, d);
+
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  const u32x4_t ones = ones_frag<E>();
+  auto compute = [&](const PStep<K, FUSE>& st, int step, int islot, int cbuf) __attribute__((always_inline)) {
+    int I[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int v = s_idx[islot][tau * K + j];
+      I[j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
+    }
+    u32x4_t xn[K];
+    if constexpr (FUSE) {
+      float xa[K][VEC], o[VEC];
+#pragma unroll
+      for (int i = 0; i < K; ++i) E::unpack(st.x[i], xa[i]);
+      E::unpack(st.o, o);
+      const __amdgpu_buffer_rsrc_t rx = x_rsrc(step);
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const float q = s_cf[cbuf][STT * K * K + tau * K + j] * s_cf[cbuf][STT * K * K + STT * K + tau * K + j];
+        float nv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < K; ++i) sum = fmaf(s_cf[cbuf][(tau * K + j) * K + i], xa[i][e], sum);
+          nv[e] = fmaf(q, o[e], sum);
+        }
+        xn[j] = E::packv(nv);
+        st_b128<CP_NT>(xn[j], rx, (uint32_t)(((size_t)tau * N + I[j]) * C * sizeof(T)) + cofs);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) xn[j] = st.x[j];
+    }
+    // sums of x and x^2 over the new rows, and the next layer's projection
+    f32x4_t S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1, acc[NTF];
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) mma_sums<E>(xn[j], ones, S1, S2);
+    // every stream of the next layer: the fixed ones hold rewritten rows too
+    u32x4_t bw[2][NTF];
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) bw[0][n] = s_w[cb][0][n][lane];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + 1 < N) {
+#pragma unroll
+        for (int n = 0; n < NTF; ++n) bw[(i + 1) & 1][n] = s_w[cb][i + 1][n][lane];
+      }
+      // the new row that sits in stream i, if any: with m known, stream
+      // i < m holds fixed position i and only routed positions can hold a
+      // stream i >= m
+      u32x4_t v = zero;
+      if constexpr (MS >= 0) {
+        if (i < MS) {
+          v = xn[i < K ? i : 0];
+        } else {
+#pragma unroll
+          for (int j = MS; j < K; ++j) v = (I[j] == i) ? xn[j] : v;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v = (I[j] == i) ? xn[j] : v;
+      }
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, bw[i & 1][n]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
+    sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+    __syncthreads();
+    // partial sums of the step's tiles; entries past the step or past the
+    // last tile go out of the store's range
+    constexpr int IT = (PTL * NSUM + PNTHR - 1) / PNTHR;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int u0 = tid + k * PNTHR;
+      const bool in = u0 < PTL * NSUM;
+      const int u = in ? u0 : 0;
+      const int bb = u / NSUM, v = u % NSUM;
+      const int tile = PTL * step + bb;
+      float x = 0.f;
+#pragma unroll
+      for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+      st_b32(x, rcorr, in && tile < a.ntiles ? (uint32_t)((((size_t)tile * G + slice) * P1 + v) * 4) : OUT_OF_RANGE);
+    }
+  };
+
+  // steps team + k nteams; ring slots by k
+  for (int k0 = 0;; k0 += NR) {
+    bool done = false;
+    for_each_c<NR>([&](auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      if (done) return;
+      const int k = k0 + q;
+      const int step = team + k * nteams;
+      if (step >= nsteps) { done = true; return; }
+      // rows of later steps: the list PD + 1 steps ahead, the coefficients
+      // of the next step
+      const u32x4_t nv = load_unit(step + (PD + 1) * nteams, true, false);
+      const u32x4_t nc = FUSE ? load_unit(step + nteams, false, true) : zero;
+      issue(sr[(q + PD) % NR], step + PD * nteams, (k + PD) % NI);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(sr[q], step, k % NI, k & 1);
+      store_unit(nv, (k + PD + 1) % NI, 0, true, false);
+      if constexpr (FUSE) store_unit(nc, 0, (k + 1) & 1, false, true);
+      __syncthreads();
+    });
+    if (done) break;
   }
 }
 
@@ -1216,7 +1523,10 @@ void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, con
     // persistent: routing weights of the next layer resident in LDS
     a.G = P.Gp;
     Gpart = P.Gp;
-    xhc_pre_chained_p_kernel<E, N, K, KR><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
+    if (P.m == 2 && K > 2)
+      xhc_pre_chained_p_kernel<E, N, K, KR, 2><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
+    else
+      xhc_pre_chained_p_kernel<E, N, K, KR, -1><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
   } else {
     Gpart = P.G;
     const unsigned grid = (unsigned)(((P.T + TM * RB - 1) / (TM * RB)) * P.G);
@@ -1234,11 +1544,11 @@ void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, con
 }
 
 template <int N, int K>
-void route_fin_launch(const Plan& P, const xhc_weights* w, char* ws, bool with_corr, hipStream_t st) {
+void route_fin_launch(const Plan& P, const xhc_weights* w, char* ws, bool with_corr, int Gc, hipStream_t st) {
   RouteFinArgs f;
-  // routing partials come from the persistent kernels, corrections from the
-  // correction kernel
-  f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.Gp; f.Gc = P.G;
+  // routing partials come from the persistent kernels, corrections (Gc
+  // slices) from the correction kernel or the persistent post pass
+  f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.Gp; f.Gc = Gc;
   f.part = reinterpret_cast<const float*>(ws + P.o_part);
   f.corr = with_corr ? reinterpret_cast<const float*>(ws + P.o_corr) : nullptr;
   f.b_pre = w->b_pre; f.a_pre = w->alpha_pre; f.eps = P.eps_norm;
@@ -1257,12 +1567,42 @@ void route_launch(const Plan& P, const xhc_weights* w, const void* X, char* ws, 
   a.wfull = reinterpret_cast<const uint4*>(ws + P.o_wfull);
   a.part = reinterpret_cast<float*>(ws + P.o_part);
   xhc_proj_p_kernel<E, N><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
-  route_fin_launch<N, K>(P, w, ws, false, st);
+  route_fin_launch<N, K>(P, w, ws, false, 0, st);
 }
 
+#ifndef XHC_POST_FUSE
+#define XHC_POST_FUSE 1
+#endif
+#ifndef XHC_CORR_P
+#define XHC_CORR_P 1
+#endif
+
+// The rewritten rows' share of the next layer's routing, then that layer's
+// routing.  fuse: the write of this (attention-type) layer is done here too.
 template <class E, int N, int K>
-void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws, char* wsn,
-                 hipStream_t st) {
+void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out, const char* ws,
+                 char* wsn, bool fuse, hipStream_t st) {
+  if (fuse || XHC_CORR_P) {
+    PostPArgs a;
+    a.X = X; a.out = out; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
+    a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
+    a.h_res = reinterpret_cast<const float*>(ws + P.o_hres);
+    a.p = reinterpret_cast<const float*>(ws + P.o_p);
+    a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+    a.wnext = reinterpret_cast<const uint4*>(wsn + Pn.o_wfull);
+    a.corr = reinterpret_cast<float*>(wsn + Pn.o_corr);
+    const unsigned grid = (unsigned)persist_grid(P);
+    const bool m2 = P.m == 2 && K > 2;
+    if (fuse) {
+      if (m2) xhc_post_p_kernel<E, N, K, 2, true><<<grid, PNTHR, 0, st>>>(a);
+      else xhc_post_p_kernel<E, N, K, -1, true><<<grid, PNTHR, 0, st>>>(a);
+    } else {
+      if (m2) xhc_post_p_kernel<E, N, K, 2, false><<<grid, PNTHR, 0, st>>>(a);
+      else xhc_post_p_kernel<E, N, K, -1, false><<<grid, PNTHR, 0, st>>>(a);
+    }
+    route_fin_launch<N, K>(Pn, wn, wsn, true, P.Gp, st);
+    return;
+  }
   CorrArgs a;
   a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.G; a.ntiles = (int)P.ntiles; a.m = P.m;
   a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
@@ -1273,7 +1613,7 @@ void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* wn, const voi
     xhc_corr_kernel<E, N, K, CORR_RB, 2><<<(unsigned)(nblk * P.G), NTHR, 0, st>>>(a);
   else
     xhc_corr_kernel<E, N, K, CORR_RB, -1><<<(unsigned)(nblk * P.G), NTHR, 0, st>>>(a);
-  route_fin_launch<N, K>(Pn, wn, wsn, true, st);
+  route_fin_launch<N, K>(Pn, wn, wsn, true, P.G, st);
 }
 
 // Dispatch over the built (N, K) shapes; KR only matters for the active maps.
@@ -1308,10 +1648,10 @@ bool pre_chained_dispatch(const Plan& P, const xhc_weights* w, const Plan* Pn, c
 }
 
 template <class E>
-bool tail_dispatch(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws, char* wsn,
-                   hipStream_t st) {
+bool tail_dispatch(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out, const char* ws,
+                   char* wsn, bool fuse, hipStream_t st) {
   return dispatch_shape(P.N, P.K, [&](auto n, auto k) {
-    tail_launch<E, decltype(n)::value, decltype(k)::value>(P, Pn, wn, X, ws, wsn, st);
+    tail_launch<E, decltype(n)::value, decltype(k)::value>(P, Pn, wn, X, out, ws, wsn, fuse, st);
   });
 }
 
@@ -1353,10 +1693,13 @@ bool launch_flash_route_p(const Plan& P, const void* X, const void* wp, float* p
   }
 }
 
-bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws,
-                           char* wsn, hipStream_t st) {
-  return P.dtype == XHC_BF16 ? tail_dispatch<Bf16>(P, Pn, wn, X, ws, wsn, st)
-                             : tail_dispatch<F32>(P, Pn, wn, X, ws, wsn, st);
+bool chain_post_fused(const Plan& P) { return XHC_POST_FUSE && P.KR == 1 && !P.mhc && !P.flash; }
+
+bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out,
+                           const char* ws, char* wsn, bool fuse, hipStream_t st) {
+  if (fuse && !chain_post_fused(P)) return false;
+  return P.dtype == XHC_BF16 ? tail_dispatch<Bf16>(P, Pn, wn, X, out, ws, wsn, fuse, st)
+                             : tail_dispatch<F32>(P, Pn, wn, X, out, ws, wsn, fuse, st);
 }
 
 // Active maps from active-projection partials laid out [ntiles][G][P2] of

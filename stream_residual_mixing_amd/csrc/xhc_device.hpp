@@ -23,16 +23,15 @@ constexpr int WAVE = 64;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN), by the
+// conversion instruction gfx950 has for it (v_cvt_pk_bf16_f32: two values
+// per instruction, no branch for the NaN case).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 

@@ -142,8 +142,11 @@ bool launch_pack(const Plan* Pf, const xhc_weights* wf, char* wsf, const Plan* P
 bool launch_xhc_route(const Plan& P, const void* X, const xhc_weights* w, char* ws, hipStream_t st);
 bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn, const xhc_weights* wn,
                             const void* X, void* inp, char* ws, char* wsn, hipStream_t st);
-bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, const void* X, const char* ws,
-                           char* wsn, hipStream_t st);
+// The rewritten rows' share of the next layer's routing and that layer's
+// routing; fuse: also this layer's write (attention-type, chain_post_fused).
+bool chain_post_fused(const Plan& P);
+bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out,
+                           const char* ws, char* wsn, bool fuse, hipStream_t st);
 
 // Helpers shared with the xHC-Flash launchers.
 void launch_pack_b(int dtype, const void* W, long nkb, int ncol, int NT, void* out, hipStream_t st);

@@ -70,6 +70,19 @@ __device__ __forceinline__ int ld_co_i(__amdgpu_buffer_rsrc_t rs, uint32_t byte_
   return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)byte_off, 0, CP_SC1));
 }
 
+// Stores through a buffer resource: a store past its range is dropped.
+// Kernels that prefetch across loop iterations store this way instead of
+// under a branch: the compiler's memory-counter waits assume the fewest
+// operations a branch may have issued, so a conditional store or load makes
+// later waits cover the prefetched loads as well.
+template <int AUX = 0>
+__device__ __forceinline__ void st_b128(const u32x4_t& v, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)voff, 0, AUX);
+}
+__device__ __forceinline__ void st_b32(float v, __amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, (int)voff, 0, 0);
+}
+
 // Wait for all of this wave's outstanding memory operations.
 __device__ __forceinline__ void wait_mem() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

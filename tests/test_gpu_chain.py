@@ -91,3 +91,31 @@ def test_chain_f32_several_steps_per_team_c4096(lib):
     """3 sublayers M A M, N=16, k=4, m=2, C=4096 in fp32 (64 slices: 4 teams,
     10 steps of 1 x 300 tokens)."""
     run_chain(lib, K.chain_configs(16, 4, 2, 4096, 1, 300, "MAM", dtype="f32"), seed=27, margin=K.MARGIN)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chained_attention_write_is_the_sublayer_write(lib, dtype):
+    """After an attention-type sublayer with a next sublayer, the chained post
+    call writes the state in the same pass that contracts the new rows for
+    the next routing.  Its write must be the per-sublayer write bit for bit:
+    same maps (left by the chained pre call), same state, same output.
+    N=16, k=4, m=2, C=256, 2 x 16400 tokens, so that xhc_post takes its
+    tiled write and the chained pass its ragged last step."""
+    import torch
+    from stream_residual_mixing_amd import synth
+    from stream_residual_mixing_amd.binding import weights_to_device
+    cfgs = K.chain_configs(16, 4, 2, 256, 2, 16400, "AM", dtype=dtype)
+    c0, c1 = cfgs
+    w = [weights_to_device(synth.xhc_layer_weights(41, l, 16, 4, 256, c.K_r, dtype)) for l, c in enumerate(cfgs)]
+    X = synth.state(41, c0.T, 16, 256, dtype).to("cuda")
+    out = synth.sublayer_out(41, 0, c0.B, c0.S, 256, dtype).reshape(c0.T, 256).to("cuda")
+    inp = torch.empty((c0.T, 256), dtype=c0.torch_dtype, device="cuda")
+    ws0, ws1 = lib.workspace(c0), lib.workspace(c1)
+    lib.xhc_route(c0, w[0], X, ws0)
+    lib.xhc_pre_chained(c0, w[0], c1, w[1], X, inp, ws0, ws1)
+    Xa, Xb = X.clone(), X.clone()
+    lib.xhc_post(c0, w[0], Xa, out, ws0)
+    lib.xhc_post_chained(c0, w[0], c1, w[1], Xb, out, ws0, ws1)
+    torch.cuda.synchronize()
+    assert not torch.equal(Xa, X), "the write changed nothing"
+    assert torch.equal(Xa, Xb), f"{int((Xa != Xb).sum())} elements differ"
