@@ -63,19 +63,25 @@ def ln_normalize(v, eps=EPS_NORM):
 def sinkhorn(logits, iters):
     """Sinkhorn-Knopp projection of a (batch of) square logit matrices.
 
-    Exponentiate (after subtracting the largest logit of each matrix, which
-    changes nothing mathematically), then ``iters`` times: divide every
-    column by its sum, then every row by its sum.  Rows are normalised last,
-    so every row sums to one and the residual error sits on the columns
-    (explainer, "mHC: keep the mixing doubly stochastic"; xHC paper,
-    "Manifold-Constrained HC").
+    The map is K = exp(logits) scaled on both sides, diag(r) K diag(c).  A
+    round first picks the column scales c that give every column of
+    diag(r) K diag(c) a sum of one, then the row scales r that give every
+    row a sum of one; r and c start at one, so zero rounds leave K itself.
+    This is the alternating column-then-row normalisation (explainer, "mHC:
+    keep the mixing doubly stochastic"; xHC paper, "Manifold-Constrained
+    HC") kept as two scale vectors per matrix.  Rows are settled last, so
+    rows sum to one and what is left of the error sits on the columns.  K
+    is formed after subtracting each matrix's largest logit, which cancels
+    in every ratio.
     """
-    L = np.asarray(logits, dtype=np.float64)
-    M = np.exp(L - L.max(axis=(-2, -1), keepdims=True))
+    lg = np.asarray(logits, dtype=np.float64)
+    K = np.exp(lg - lg.max(axis=(-2, -1), keepdims=True))
+    r = np.ones(K.shape[:-1])           # row scales  [..., n]
+    c = np.ones(K.shape[:-2] + K.shape[-1:])   # column scales [..., n]
     for _ in range(iters):
-        M = M / M.sum(axis=-2, keepdims=True)   # columns
-        M = M / M.sum(axis=-1, keepdims=True)   # rows
-    return M
+        c = 1.0 / np.einsum("...i,...ij->...j", r, K)
+        r = 1.0 / np.einsum("...ij,...j->...i", K, c)
+    return r[..., :, None] * K * c[..., None, :]
 
 
 def row_clamp(H):
@@ -246,14 +252,17 @@ def xhc_pre(X, W_full, W_act, m, k, K_r, alpha, b_pre, b_res, b_post, iters=20):
     I, p = xhc_select(z, m, k)
 
     h_pre = sigmoid(a_pre * (rms_normalize(x) @ W_full[:, N:2 * N]) + np.asarray(b_pre))
-    inp = np.einsum("tn,tnc->tc", h_pre, X)
+    # dense read: token t's input is the row vector h_pre[t] times its N x C state
+    inp = np.matmul(h_pre[:, None, :], X)[:, 0, :]
 
-    Xa = np.take_along_axis(X, I[:, :, None], axis=1)          # [T, k, C]
-    la = rms_normalize(Xa.reshape(T, k * C)) @ W_act            # [T, k^2 + k K_r]
-    L = a_res * la[:, : k * k].reshape(T, k, k) + np.asarray(b_res).reshape(k, k)
-    h_res = row_clamp(sinkhorn(L, iters))
-    h_post = 2.0 * sigmoid(a_post * la[:, k * k:].reshape(T, k, K_r)
-                           + np.asarray(b_post).reshape(k, K_r))
+    # the k active rows of each token, in list order, flattened to k*C
+    x_act = X[np.arange(T)[:, None], I].reshape(T, k * C)
+    proj = rms_normalize(x_act) @ W_act
+    res_logits = proj[:, : k * k].reshape(T, k, k)
+    post_logits = proj[:, k * k:].reshape(T, k, K_r)
+    h_res = row_clamp(sinkhorn(a_res * res_logits + np.asarray(b_res).reshape(k, k), iters))
+    # the post map ranges over (0, 2): twice a logistic function
+    h_post = 2.0 * sigmoid(a_post * post_logits + np.asarray(b_post).reshape(k, K_r))
     return dict(inp=inp, z=z, I=I, p=p, h_pre=h_pre, h_res=h_res, h_post=h_post)
 
 
@@ -284,14 +293,15 @@ def gram_schmidt(comps, eps=EPS_MGS):
     from the running vector, u <- u - <u, v_i> / (<v_i, v_i> + eps) v_i, and
     the result is v_{j+1} (summary 3.3; explainer, "What xHC changes").
     """
-    vs = [np.asarray(comps[0], dtype=np.float64)]
-    for g in comps[1:]:
-        u = np.asarray(g, dtype=np.float64).copy()
-        for v in vs:
-            coef = np.sum(u * v, axis=-1, keepdims=True) / (np.sum(v * v, axis=-1, keepdims=True) + eps)
-            u = u - coef * v
-        vs.append(u)
-    return vs
+    # Once component i is final, its projection is taken out of every later
+    # component (each later one then sees the projections on v_1, v_2, ...
+    # in that order, applied to what is left of it, as the recurrence asks).
+    work = [np.array(c, dtype=np.float64) for c in comps]
+    for i, v in enumerate(work):
+        norm2 = np.einsum("...c,...c->...", v, v)[..., None] + eps
+        for j in range(i + 1, len(work)):
+            work[j] = work[j] - (np.einsum("...c,...c->...", work[j], v)[..., None] / norm2) * v
+    return work
 
 
 def xhc_write_basis(out, conv_ws, use_mgs=True, eps=EPS_MGS):

@@ -223,11 +223,11 @@ def test_xhc_with_all_streams_active_equals_mhc():
 
 
 def test_mix_of_identical_streams_returns_that_stream():
-    """Each output stream is a convex combination of input streams (rows of
-    H_res sum to 1), so if every stream holds the same vector the mix
-    returns it unchanged; with one Sinkhorn iteration the column sums are
-    far from 1, so a transposed map would not (explainer, "mHC: keep the
-    mixing doubly stochastic")."""
+    """The rows of H_res sum to one, so a new stream is a weighted average of
+    the old ones and a state whose streams are all the same vector is mixed
+    back into that vector; after a single Sinkhorn round the column sums
+    are far from one, so applying the transposed map would not give it
+    back (explainer, "mHC: keep the mixing doubly stochastic")."""
     r = rng(14)
     N, C, T = 5, 12, 6
     c = r.standard_normal((T, 1, C))
