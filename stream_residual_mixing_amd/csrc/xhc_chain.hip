@@ -757,23 +757,22 @@ __device__ __forceinline__ void route_partials(float (&s_red)[TWV][PM], const fl
   acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
   sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
   __syncthreads();
+  // stores through a resource over the partials: entries past the step or
+  // past the last tile go out of its range (no store under a branch)
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst, (uint32_t)((size_t)ntiles * G * P1 * 4));
   constexpr int IT = (PTL * P1 + PNTHR - 1) / PNTHR;
 #pragma unroll
   for (int k = 0; k < IT; ++k) {
-    const int u = tid + k * PNTHR;
-    if (u < PTL * P1) {
-      const int bb = u / P1, v = u % P1;
-      const int tile = PTL * step + bb;
-      float x;
-      if (v < NSUM) {
-        x = 0.f;
+    const int u0 = tid + k * PNTHR;
+    const bool in = u0 < PTL * P1;
+    const int u = in ? u0 : 0;
+    const int bb = u / P1, v = u % P1;
+    const int tile = PTL * step + bb;
+    float x = 0.f;
 #pragma unroll
-        for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
-      } else {
-        x = s_acs[v - NSUM];
-      }
-      if (tile < ntiles) dst[((size_t)tile * G + slice) * P1 + v] = x;
-    }
+    for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v < NSUM ? v : 0];
+    if (v >= NSUM) x = s_acs[v - NSUM >= 0 ? v - NSUM : 0];
+    st_b32(x, rd, in && tile < ntiles ? (uint32_t)((((size_t)tile * G + slice) * P1 + v) * 4) : OUT_OF_RANGE);
   }
   __syncthreads();
 }
@@ -1035,23 +1034,28 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
   const uint32_t lane_off =
       kvalid ? (uint32_t)(((size_t)(TM * b + r) * N * C + (size_t)kb0 * KB + VEC * g) * sizeof(T)) : OUT_OF_RANGE;
   const T* X = reinterpret_cast<const T*>(a.X);
+  const __amdgpu_buffer_rsrc_t rp2 = make_rsrc(a.part2, (uint32_t)((size_t)a.ntiles * G * P2 * 4));
   const int full = a.T / (PTL * TM), tail = a.T % (PTL * TM);
 
   // The step's routing rows; which array a wave loads is wave-uniform, so no
   // lane waits for its data before the state prefetch is issued.  Units past
   // the valid rows read zeros.
+  // every wave issues the load (a wave without a share reads an empty
+  // range), so that no memory operation sits under a branch
   auto load_route = [&](int step) {
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
     const int valid = step_rows(step, full, tail);
     const int ts = valid > 0 ? PTL * TM * step : 0;
+    const void* base = a.h_pre;
+    uint32_t bytes = 0, unit = (uint32_t)((wave * WAVE + lane) * 16);
     if (wave < WH) {
-      const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h_pre + (size_t)ts * N, (uint32_t)(valid * N * 4));
-      v = ld_b128(rh, (uint32_t)((wave * WAVE + lane) * 16), 0);
+      base = a.h_pre + (size_t)ts * N;
+      bytes = (uint32_t)(valid * N * 4);
     } else if (wave < WH + WI) {
-      const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.idx + (size_t)ts * K, (uint32_t)(valid * K * 4));
-      v = ld_b128(ri, (uint32_t)(((wave - WH) * WAVE + lane) * 16), 0);
+      base = a.idx + (size_t)ts * K;
+      bytes = (uint32_t)(valid * K * 4);
+      unit = (uint32_t)(((wave - WH) * WAVE + lane) * 16);
     }
-    return v;
+    return ld_b128(make_rsrc(base, bytes), unit, 0);
   };
   auto store_route = [&](int buf, const u32x4_t& v) {
     if (wave < WH)
@@ -1097,7 +1101,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
       amask |= 1u << v;
     }
     // dense read over all N streams -> sublayer input
-    if (kvalid) {
+    {
       float o[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[e] = 0.f;
@@ -1109,8 +1113,13 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 #pragma unroll
         for (int e = 0; e < VEC; ++e) o[e] = fmaf(hpi, f[e], o[e]);
       }
-      if (tile < a.ntiles && tok < a.T)
-        st16_nt(reinterpret_cast<T*>(a.inp) + (size_t)tok * C + kb0 * KB + VEC * g, E::packv(o));
+      // the step's rows of inp; a block past C or a token past T is out of range
+      const int rows = kvalid ? step_rows(step, full, tail) : 0;
+      const __amdgpu_buffer_rsrc_t ri = make_rsrc(reinterpret_cast<T*>(a.inp) + (size_t)(rows > 0 ? step : 0) * PTL * TM * C,
+                                                  (uint32_t)((size_t)rows * C * sizeof(T)));
+      st_b128<CP_NT>(E::packv(o), ri, (uint32_t)(((size_t)(TM * b + r) * C + kb0 * KB + VEC * g) * sizeof(T)));
+      (void)tok;
+      (void)tile;
     }
     // with m known at run time only, the longer-lived register would spill:
     // the next step's routing goes to LDS here (see below)
@@ -1153,15 +1162,15 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
     constexpr int IT = (PTL * P2 + PNTHR - 1) / PNTHR;
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
-      const int u = tid + k * PNTHR;
-      if (u < PTL * P2) {
-        const int bb = u / P2, v = u % P2;
-        const int t16 = PTL * step + bb;
-        float x = 0.f;
+      const int u0 = tid + k * PNTHR;
+      const bool in = u0 < PTL * P2;
+      const int u = in ? u0 : 0;
+      const int bb = u / P2, v = u % P2;
+      const int t16 = PTL * step + bb;
+      float x = 0.f;
 #pragma unroll
-        for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
-        if (t16 < a.ntiles) a.part2[((size_t)t16 * G + slice) * P2 + v] = x;
-      }
+      for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+      st_b32(x, rp2, in && t16 < a.ntiles ? (uint32_t)((((size_t)t16 * G + slice) * P2 + v) * 4) : OUT_OF_RANGE);
     }
     // the next step's routing to the other buffer, last: its load was issued
     // with the next step's state, so waiting for it here rather than early

@@ -367,79 +367,82 @@ __global__ __launch_bounds__(MP_THREADS, 1) void mhc_proj_kernel(const uint16_t*
     s2[h] = 0.f;
   }
 
-  // The weight fragments of the stage starting at kbs, straight from global
-  // memory into LDS buffer buf (each lane 16 bytes of a 1 KiB fragment);
-  // fragments past the range are not loaded and not used.
-  auto load_w = [&](long kbs, int buf) {
-    const long inside = (kb1 - kbs) * NT;
+  // The weight fragments of the stage starting at kbs, straight from memory
+  // into LDS buffer buf (each lane 16 bytes of a 1 KiB fragment), through a
+  // resource over the packed weights: fragments past the last block read
+  // zero.  Past this split's range the stage only loads what it will not use.
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wp, (uint32_t)((size_t)nkb * NT * WAVE * 16));
+  // Fragment c = wave + NW q; a wave whose last q falls past CH loads the last
+  // fragment again (the same bytes to the same place), so that every wave
+  // issues the same, compile-time number of loads.
+  auto load_w = [&](long kbs, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = wave; c < CH; c += NW)
-      if (c < inside)
-        __builtin_amdgcn_global_load_lds(Wp + (kbs * NT + c) * WAVE + lane,
-                                         (lds_ptr_t)(&s_w[buf][0][0][0] + (size_t)c * WAVE), 16, 0, 0);
-  };
-  auto load_a = [&](long kbs, u32x4_t (&a)[MP_RT][MP_KU]) {
-#pragma unroll
-    for (int k = 0; k < MP_KU; ++k) {
-      const bool in = kbs + k < kb1;
-      const uint32_t o = (uint32_t)((kbs + k) * 64);
-#pragma unroll
-      for (int h = 0; h < MP_RT; ++h)
-        a[h][k] = in ? ld_b128(rx, voff0 + (uint32_t)(h * 16 * K * 2) + o, 0) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int q = 0; q < (CH + NW - 1) / NW; ++q) {
+      const int c = wave + NW * q < CH ? wave + NW * q : CH - 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(&s_w[buf][0][0][0] + (size_t)c * WAVE), 16,
+                                               (int)(((kbs * NT + c) * WAVE + lane) * 16), 0, 0, 0);
     }
   };
-
-  u32x4_t acur[MP_RT][MP_KU], anext[MP_RT][MP_KU];
-  load_w(kb0, 0);
-  load_a(kb0, acur);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int buf = 0;
-  for (long kbs = kb0; kbs < kb1; kbs += MP_KU) {
-    const bool more = kbs + MP_KU < kb1;
-    if (more) {
-      // the other buffer was last read in the previous stage, before its barrier
-      load_w(kbs + MP_KU, buf ^ 1);
-      load_a(kbs + MP_KU, anext);
-    }
+  // A fragments of a stage; blocks past this split's range read zero (and
+  // so add nothing to the sums and the MFMAs).  No load sits under a branch:
+  // the compiler's memory-counter waits would then also cover the next
+  // stage's loads.
+  auto load_a = [&](long kbs, u32x4_t (&a)[MP_RT][MP_KU]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < MP_KU; ++k) {
-      if (kbs + k < kb1) {
+      const uint32_t o = kbs + k < kb1 ? (uint32_t)((kbs + k) * 64) : OUT_OF_RANGE;
 #pragma unroll
-        for (int h = 0; h < MP_RT; ++h) {
-          float f[8];
-          Bf16::unpack(acur[h][k], f);
+      for (int h = 0; h < MP_RT; ++h) a[h][k] = ld_b128(rx, voff0 + (uint32_t)(h * 16 * K * 2) + o, 0);
+    }
+  };
+  // One stage: issue the next stage's weights (to the other buffer, last read
+  // in the previous stage, before its barrier) and state, then the MFMAs of
+  // this one.  Before the barrier each wave waits for its weight loads only;
+  // the state loads issued after them stay in flight into the next stage.
+  constexpr int WAIT_W = (MP_RT * MP_KU) | (0x7 << 4) | (0xF << 8);   // vmcnt(MP_RT * MP_KU)
+  static_assert(MP_RT * MP_KU < 16, "the wait count fits the low vmcnt bits");
+  auto stage = [&](long kbs, int buf, const u32x4_t (&acur)[MP_RT][MP_KU], u32x4_t (&anext)[MP_RT][MP_KU])
+      __attribute__((always_inline)) {
+    load_w(kbs + MP_KU, buf ^ 1);
+    load_a(kbs + MP_KU, anext);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            s1[h] += f[e];
-            s2[h] = fmaf(f[e], f[e], s2[h]);
-          }
-        }
-        // weight fragments read MP_BD - 1 tiles ahead of their MFMAs, so the
-        // LDS latency hides behind the MFMAs of the tiles before
-        u32x4_t b[MP_BD];
+    for (int k = 0; k < MP_KU; ++k) {
 #pragma unroll
-        for (int q = 0; q < MP_BD - 1 && q < NT; ++q) b[q] = s_w[buf][k][q][lane];
+      for (int h = 0; h < MP_RT; ++h) {
+        float f[8];
+        Bf16::unpack(acur[h][k], f);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (n + MP_BD - 1 < NT) b[(n + MP_BD - 1) % MP_BD] = s_w[buf][k][n + MP_BD - 1][lane];
-#pragma unroll
-          for (int h = 0; h < MP_RT; ++h) acc[h][n] = Bf16::mma(acc[h][n], acur[h][k], b[n % MP_BD]);
-          __builtin_amdgcn_sched_barrier(0);   // keep each read ahead of the MFMAs before its use
+        for (int e = 0; e < 8; ++e) {
+          s1[h] += f[e];
+          s2[h] = fmaf(f[e], f[e], s2[h]);
         }
       }
-    }
-    if (more) {
+      // weight fragments read MP_BD - 1 tiles ahead of their MFMAs, so the
+      // LDS latency hides behind the MFMAs of the tiles before
+      u32x4_t b[MP_BD];
 #pragma unroll
-      for (int k = 0; k < MP_KU; ++k)
+      for (int q = 0; q < MP_BD - 1 && q < NT; ++q) b[q] = s_w[buf][k][q][lane];
 #pragma unroll
-        for (int h = 0; h < MP_RT; ++h) acur[h][k] = anext[h][k];
+      for (int n = 0; n < NT; ++n) {
+        if (n + MP_BD - 1 < NT) b[(n + MP_BD - 1) % MP_BD] = s_w[buf][k][n + MP_BD - 1][lane];
+#pragma unroll
+        for (int h = 0; h < MP_RT; ++h) acc[h][n] = Bf16::mma(acc[h][n], acur[h][k], b[n % MP_BD]);
+        __builtin_amdgcn_sched_barrier(0);   // keep each read ahead of the MFMAs before its use
+      }
     }
-    // this wave's weight fragments of the next stage are in LDS (its state
-    // loads are wanted next anyway), then everyone's
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(WAIT_W);
     __syncthreads();
-    buf ^= 1;
+  };
+
+  u32x4_t a0[MP_RT][MP_KU], a1[MP_RT][MP_KU];
+  load_w(kb0, 0);
+  load_a(kb0, a0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (long kbs = kb0; kbs < kb1; kbs += 2 * MP_KU) {
+    stage(kbs, 0, a0, a1);
+    if (kbs + MP_KU >= kb1) break;
+    stage(kbs + MP_KU, 1, a1, a0);
   }
   constexpr int NP = NT * 16;
 #pragma unroll
