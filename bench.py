@@ -443,14 +443,16 @@ def _pmc_rows(d):
 
 def _split_calls(rows):
     """Group this library's dispatches of one step into calls, in order: a
-    call starts at a weight-packing kernel, at the Gram kernel, or at an apply
-    kernel not preceded by the Gram kernel."""
+    call starts at a weight-packing kernel (xHC or mHC), at the Gram kernel, at an apply
+    kernel not preceded by the Gram kernel, at the persistent post pass that
+    also writes (the chained attention-type post call), or at the mHC write."""
     calls, prev = [], ""
     for name, v in rows:
         if "xhc::" not in name:
             continue
-        start = ("xhc_prep_kernel" in name or "xhc_gram_kernel" in name
-                 or ("xhc_apply_kernel" in name and "xhc_gram_kernel" not in prev))
+        start = ("xhc_prep_kernel" in name or "pack_b_kernel" in name or "xhc_gram_kernel" in name
+                 or ("xhc_apply_kernel" in name and "xhc_gram_kernel" not in prev)
+                 or ("xhc_post_p_kernel" in name and "true>" in name) or "mhc_post_kernel" in name)
         if start or not calls:
             calls.append([])
         calls[-1].append((name, v))
@@ -487,8 +489,11 @@ def traffic_summary(workload, pmcdir):
     split = _split_backward_calls if kind == "xhcb" else _split_calls
     fetch = split(_pmc_rows(os.path.join(pmcdir, "chain_fetch")))
     write = split(_pmc_rows(os.path.join(pmcdir, "chain_write")))
+    api = default_api(workload)
     if kind == "xhcb":
         names = [f"{p}_{lk}" for lk in reversed(kinds) for p in ("xhc_post_backward", "xhc_pre_backward")]
+    elif kind == "xhc" and api == "single":
+        names = [f"{p}_{lk}" for lk in kinds for p in ("xhc_pre", "xhc_post")]
     else:
         names = (["xhc_route"] if kind == "xhc" else []) + [
             f"{p}_{lk}" for lk in kinds for p in (("xhc_pre_chained", "xhc_post_chained") if kind == "xhc"

@@ -1117,7 +1117,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
       const int rows = kvalid ? step_rows(step, full, tail) : 0;
       const __amdgpu_buffer_rsrc_t ri = make_rsrc(reinterpret_cast<T*>(a.inp) + (size_t)(rows > 0 ? step : 0) * PTL * TM * C,
                                                   (uint32_t)((size_t)rows * C * sizeof(T)));
-      st_b128<CP_NT>(E::packv(o), ri, (uint32_t)(((size_t)(TM * b + r) * C + kb0 * KB + VEC * g) * sizeof(T)));
+      st_b128<CP_NT>(E::packv_cvt(o), ri, (uint32_t)(((size_t)(TM * b + r) * C + kb0 * KB + VEC * g) * sizeof(T)));
       (void)tok;
       (void)tile;
     }
@@ -1396,7 +1396,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
           for (int i = 0; i < K; ++i) sum = fmaf(s_cf[cbuf][(tau * K + j) * K + i], xa[i][e], sum);
           nv[e] = fmaf(q, o[e], sum);
         }
-        xn[j] = E::packv(nv);
+        xn[j] = E::packv_cvt(nv);
         st_b128<CP_NT>(xn[j], rx, (uint32_t)(((size_t)tau * N + I[j]) * C * sizeof(T)) + cofs);
       }
     } else {

@@ -23,15 +23,26 @@ constexpr int WAVE = 64;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bfloat16 bits, round to nearest even (NaN stays NaN), by the
-// conversion instruction gfx950 has for it (v_cvt_pk_bf16_f32: two values
-// per instruction, no branch for the NaN case).
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+// The same two roundings by gfx950's conversion instruction v_cvt_pk_bf16_f32
+// (round to nearest even, NaN stays NaN; the same bits).  One instruction for
+// two values, no branch for the NaN case; used by the persistent chained
+// kernels, where it measured faster.  Not the default: in the one-pass pre
+// kernel the compiler's register allocation then spilled.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+__device__ __forceinline__ uint32_t pack_bf16x2_cvt(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
@@ -62,6 +73,10 @@ struct Bf16 {
   __device__ static __forceinline__ u32x4_t packv(const float (&f)[8]) {
     return u32x4_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                    pack_bf16x2(f[6], f[7])};
+  }
+  __device__ static __forceinline__ u32x4_t packv_cvt(const float (&f)[8]) {
+    return u32x4_t{pack_bf16x2_cvt(f[0], f[1]), pack_bf16x2_cvt(f[2], f[3]), pack_bf16x2_cvt(f[4], f[5]),
+                   pack_bf16x2_cvt(f[6], f[7])};
   }
   __device__ static __forceinline__ f32x4_t mma(f32x4_t acc, const u32x4_t& a, const u32x4_t& b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -95,6 +110,7 @@ struct F32 {
   __device__ static __forceinline__ u32x4_t packv(const float (&f)[4]) {
     return u32x4_t{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
   }
+  __device__ static __forceinline__ u32x4_t packv_cvt(const float (&f)[4]) { return packv(f); }
   __device__ static __forceinline__ f32x4_t mma(f32x4_t acc, const u32x4_t& a, const u32x4_t& b) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)

@@ -39,3 +39,24 @@ def test_backward_dispatches_group_into_calls():
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_counter_rows_split_into_calls():
+    """The traffic summary groups one step's dispatches into the calls the
+    bench times: route, then per layer pre and post (the attention-type post
+    is the persistent pass alone, the MLP-type one starts at its Gram pass);
+    for mHC, pre then post."""
+    k = lambda n: (f"void xhc::{n}(xhc::Args)", 1.0)   # noqa: E731
+    chain = [k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_proj_p_kernel<xhc::Bf16, 16>"), k("xhc_route_fin_kernel<16, 4>"),
+             k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_pre_chained_p_kernel<xhc::Bf16, 16, 4, 1, 2>"),
+             k("xhc_act_fin_kernel<4, 1>"),
+             k("xhc_post_p_kernel<xhc::Bf16, 16, 4, 2, true>"), k("xhc_route_fin_kernel<16, 4>"),
+             k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_pre_chained_kernel<xhc::Bf16, 16, 4, 4, false, 1>"),
+             k("xhc_act_fin_kernel<4, 4>"),
+             k("xhc_gram_kernel<xhc::Bf16>"), k("xhc_apply_kernel<xhc::Bf16, 4, 4, 6, 0>"),
+             k("xhc_post_p_kernel<xhc::Bf16, 16, 4, 2, false>"), k("xhc_route_fin_kernel<16, 4>")]
+    calls = bench._split_calls(chain)
+    assert [len(c) for c in calls] == [3, 3, 2, 3, 4]
+    mhc = [k("pack_b_kernel<xhc::Bf16>"), k("mhc_proj_kernel<18>"), k("mhc_read_kernel<xhc::Bf16, 16>"),
+           k("mhc_post_kernel<xhc::Bf16, 16>")]
+    assert [len(c) for c in bench._split_calls(mhc)] == [3, 1]

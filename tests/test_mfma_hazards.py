@@ -1,5 +1,6 @@
 """No MFMA result of the library's kernels is read through a branch before
-its passes have retired (CPU: compiles every source to gfx950 assembly).
+its passes have retired, and no kernel spills registers to scratch (CPU:
+compiles every source to gfx950 assembly).
 
 The bf16 backward row pass once gave wrong weight-gradient columns 3, 7, 11
 and 15 (accumulator element 3 of the first row tile) when its column-tile
@@ -9,6 +10,7 @@ register, with no wait states on that edge.  See tests/mfma_hazards.py for
 the rule checked here.
 """
 import os
+import re
 import shutil
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
@@ -62,3 +64,14 @@ def test_library_kernels_have_no_early_mfma_reads(tmp_path):
     assert n_mfma > 1000, f"only {n_mfma} MFMA instructions in the gfx950 assembly"
     bad = {src: scan(text)[:5] for src, text in outs if scan(text)}
     assert not bad, bad
+    # and no kernel spills registers to scratch memory: a spill turns a
+    # register-resident tile into memory traffic the byte models do not count
+    # (a bf16 conversion form once made the one-pass pre kernel spill 236
+    # bytes per lane, with 1.1 GB of scratch writes per call)
+    spills = {}
+    for src, text in outs:
+        for line in text.splitlines():
+            m = re.match(r"\s*\.set\s+(\S+)\.private_seg_size,\s*(.+?)\s*$", line)
+            if m and m.group(2) != "0":
+                spills.setdefault(src, []).append((m.group(1)[:80], m.group(2)[:40]))
+    assert not spills, spills
