@@ -441,6 +441,14 @@ def _pmc_rows(d):
     return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
 
 
+def _attention_post_pass(name):
+    """The persistent post pass that writes an attention-type sublayer (its
+    last template argument, the write kind, is 1)."""
+    import re
+    m = re.search(r"xhc_post_p_kernel<[^>]*,\s*(\d+)>", name)
+    return bool(m) and m.group(1) == "1"
+
+
 def _split_calls(rows):
     """Group this library's dispatches of one step into calls, in order: a
     call starts at a weight-packing kernel (xHC or mHC), at the Gram kernel, at an apply
@@ -452,7 +460,7 @@ def _split_calls(rows):
             continue
         start = ("xhc_prep_kernel" in name or "pack_b_kernel" in name or "xhc_gram_kernel" in name
                  or ("xhc_apply_kernel" in name and "xhc_gram_kernel" not in prev)
-                 or ("xhc_post_p_kernel" in name and "true>" in name) or "mhc_post_kernel" in name)
+                 or _attention_post_pass(name) or "mhc_post_kernel" in name)
         if start or not calls:
             calls.append([])
         calls[-1].append((name, v))

@@ -167,6 +167,7 @@ xhc_status make_plan(const xhc_config* cfg, bool mhc, xhc::Plan* P) {
     q.o_part2 = take((size_t)q.ntiles * GM * P2 * 4);
     q.o_gram = take((size_t)q.nslices * T * 10 * 8);
     q.o_corr = take((size_t)q.ntiles * GM * P1 * 4);
+    q.o_wcoef = take(T * K * 4 * 4);
   }
   q.total = q.T == 0 ? 0 : off;
   *P = q;
@@ -533,8 +534,8 @@ xhc_status xhc_post_chained(const xhc_config* cfg, const xhc_weights* w, const x
   const bool fuse = chained && xhc::chain_post_fused(P);
   if (!fuse && !xhc::launch_xhc_post(P, X, out, w, static_cast<char*>(ws), st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
-  if (chained && !xhc::launch_xhc_chain_tail(P, Pn, w_next, X, out, static_cast<char*>(ws), static_cast<char*>(ws_next),
-                                             fuse, st))
+  if (chained && !xhc::launch_xhc_chain_tail(P, Pn, w, w_next, X, out, static_cast<char*>(ws),
+                                             static_cast<char*>(ws_next), fuse, st))
     return fail(XHC_ERR_UNSUPPORTED, "no kernel built for this shape");
   return finish(st);
 }

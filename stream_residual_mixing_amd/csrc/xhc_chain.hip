@@ -1199,35 +1199,43 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 
 // ---------------------------------------------------------------------------
 // Persistent post pass of a layer with a next layer: the rewritten rows'
-// share of the next layer's routing (the correction), and for an
-// attention-type layer (FUSE) the write itself, so the new rows are
-// contracted from registers instead of being read back.
+// share of the next layer's routing (the correction), and with it the
+// layer's write (WR = 1 attention-type, 4 MLP-type), so the new rows are
+// contracted from registers instead of being read back (WR = 0: the
+// correction alone, of rows another kernel wrote).
 //
 // A workgroup owns one slice of PSB contraction blocks for the whole launch
 // with the next layer's routing fragments of that slice in LDS, and walks
 // steps of PTL 16-token tiles, one wave per (tile, block); lane (g, r) holds
 // token r of its tile, VEC channels of its block.  Per step a lane loads the
-// k active rows of its token (FUSE: and its row of out), FUSE forms the new
-// rows x'_j = sum_i H_res[j][i] x_{I_i} + p_j H_post[j] out (the
-// per-sublayer write's arithmetic, in its order) and stores them in place;
-// then per stream i of the next layer the MFMA takes, per token, the new row
-// that sits in stream i (zero if none) against that stream's fragments, and
-// the new rows' sums of x and x^2 go through the matrix cores as in the pre
-// pass.  The partials of the PSB waves of a tile are summed in LDS and
-// written per (tile, slice) in the routing partials' layout.
+// k active rows of its token and its row of out (MLP-type: also the row 16
+// tokens earlier), forms the write basis (MLP-type: out and its three causal
+// convolutions, the lags taken from neighbouring lanes by DPP row shifts,
+// conv weights of the slice in LDS), and the new rows
+// x'_j = sum_i H_res[j][i] x_{I_i} + sum_v Q[j][v] basis_v with the
+// per-sublayer write's arithmetic in its order (Q = p_j H_post[j] for the
+// attention type; diag(p) H_post Tm, Tm the Gram-Schmidt map, precomputed
+// per token for the MLP type), and stores them in place; then per stream i
+// of the next layer the MFMA takes, per token, the new row that sits in
+// stream i (zero if none) against that stream's fragments, and the new
+// rows' sums of x and x^2 go through the matrix cores as in the pre pass.
+// The partials of the PSB waves of a tile are summed in LDS and written per
+// (tile, slice) in the routing partials' layout.
 //
-// The state loads run PD steps ahead (PD + 1 register sets), as the k rows
-// of a step are few bytes per lane.  Their addresses need the active lists
-// PD steps ahead, so the lists run one step further: loaded into LDS PD + 1
-// steps ahead, a ring of PD + 2 slots.  FUSE: the write coefficients of the
-// next step are loaded during this one, double-buffered in LDS.
+// The state loads run PD steps ahead (PD + 1 register sets), as the rows of
+// a step are few bytes per lane.  Their addresses need the active lists PD
+// steps ahead, so the lists run one step further: loaded into LDS PD + 1
+// steps ahead, a ring of PD + 2 slots.  The write coefficients of the next
+// step are loaded during this one, double-buffered in LDS.
 // ---------------------------------------------------------------------------
 struct PostPArgs {
   void* X;
-  const void* out;                      // FUSE
+  const void* out;                      // a write: [T][C]
   const int* idx;                       // [T][K]
-  const float *h_res, *p, *h_post;      // FUSE: [T][K][K], [T][K], [T][K]
-  int T, C, G, ntiles;
+  const float *h_res, *p, *h_post;      // a write: [T][K][K]; attention-type: [T][K], [T][K]
+  const float* wq;                      // MLP-type write: [T][K][4] coefficients diag(p) H_post Tm
+  const float* conv_w;                  // MLP-type write: [24][C]
+  int T, S, C, G, ntiles;
   const uint4* wnext;                   // next layer's packed [W_r | W_pre]
   float* corr;                          // [ntiles][G][P1] (the first NSUM entries of each)
 };
@@ -1246,13 +1254,14 @@ __device__ __forceinline__ void for_each_c(F&& f) {
   }
 }
 
-template <int K, bool FUSE>
+template <int K>
 struct PStep {
   u32x4_t x[K];
-  u32x4_t o;   // out (FUSE)
+  u32x4_t o;    // out (a write)
+  u32x4_t op;   // out 16 tokens before (MLP-type write)
 };
 
-template <class E, int N, int K, int MS, bool FUSE>
+template <class E, int N, int K, int MS, int WR>
 __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
   using T = typename E::T;
   using D = RouteDims<N>;
@@ -1260,18 +1269,27 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
   constexpr int KB = E::KB, VEC = E::VEC;
   constexpr int PD = POST_PD, NR = PD + 1, NI = PD + 2;
   constexpr int STT = PTL * TM;                     // tokens per step
+  constexpr int SLC = PSB * KB;                     // channels of a slice
+  static_assert(WR == 0 || WR == 1 || WR == 4, "write kinds: none, attention-type, MLP-type");
   // per-step rows moved through LDS, in 16-byte units: the active lists,
-  // then (FUSE) H_res, p and H_post
-  constexpr int UI = STT * K / 4, UH = FUSE ? STT * K * K / 4 : 0, UP = FUSE ? STT * K / 4 : 0;
+  // then for a write H_res and (attention-type) p and H_post, or (MLP-type)
+  // the write coefficients Q = diag(p) H_post (Gram-Schmidt map)
+  constexpr int E2 = WR == 4 ? 4 * K : (WR == 1 ? K : 0), E3 = WR == 1 ? K : 0;
+  constexpr int UI = STT * K / 4, UH = WR ? STT * K * K / 4 : 0, U2 = STT * E2 / 4, U3 = STT * E3 / 4;
   // each array is loaded by whole waves of its own, so that its buffer
   // resource stays uniform over a wave
-  constexpr int WI = (UI + WAVE - 1) / WAVE, WH = (UH + WAVE - 1) / WAVE, WP = (UP + WAVE - 1) / WAVE;
-  static_assert((STT * K) % 4 == 0 && WI + WH + 2 * WP <= TWV, "a step's rows fit one unit per thread");
-  constexpr int CF = FUSE ? STT * (K * K + 2 * K) : 1;
+  constexpr int WI = (UI + WAVE - 1) / WAVE, WH = (UH + WAVE - 1) / WAVE, W2 = (U2 + WAVE - 1) / WAVE,
+                W3 = (U3 + WAVE - 1) / WAVE;
+  static_assert((STT * K) % 4 == 0 && WI + WH + W2 + W3 <= TWV, "a step's rows fit one unit per thread");
+  constexpr int CF = WR ? STT * (K * K + E2 + E3) : 1;
+  // the per-tile partial sums: per wave, or (MLP-type, whose conv weights
+  // take the room) per pair of block waves, added in two rounds
+  constexpr int RW = WR == 4 ? PTL * 2 : TWV;
   __shared__ u32x4_t s_w[PSB][N][NTF][WAVE];
-  __shared__ float s_red[TWV][NSUM];
+  __shared__ float s_red[RW][NSUM];
   __shared__ int s_idx[NI][STT * K];
   __shared__ float s_cf[2][CF];
+  __shared__ float s_cw[WR == 4 ? 24 : 1][WR == 4 ? SLC : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1289,9 +1307,10 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
   const T* out = reinterpret_cast<const T*>(a.out);
 
   // one 16-byte unit of a step's rows; the resource spans the step's valid
-  // tokens, so anything past them reads zero
-  // Every wave issues the load (one without a share reads an empty range),
-  // so that no memory operation sits under a branch.
+  // tokens, so anything past them reads zero.  Every wave issues the load
+  // (one without a share reads an empty range), so that no memory operation
+  // sits under a branch.
+  const float* arr2 = WR == 4 ? a.wq : a.p;
   auto load_unit = [&](int step, bool lists, bool coefs) __attribute__((always_inline)) {
     const int valid = step_rows(step, full, tail);
     const size_t ts = valid > 0 ? (size_t)STT * step : 0;
@@ -1304,39 +1323,41 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
       base = a.h_res + ts * K * K;
       bytes = coefs ? (uint32_t)(valid * K * K * 4) : 0u;
       first = WI;
-    } else if (wave < WI + WH + WP) {
-      base = a.p + ts * K;
-      bytes = coefs ? (uint32_t)(valid * K * 4) : 0u;
+    } else if (wave < WI + WH + W2) {
+      base = arr2 + ts * E2;
+      bytes = coefs ? (uint32_t)(valid * E2 * 4) : 0u;
       first = WI + WH;
-    } else if (wave < WI + WH + 2 * WP) {
-      base = a.h_post + ts * K;
-      bytes = coefs ? (uint32_t)(valid * K * 4) : 0u;
-      first = WI + WH + WP;
+    } else if (wave < WI + WH + W2 + W3) {
+      base = a.h_post + ts * E3;
+      bytes = coefs ? (uint32_t)(valid * E3 * 4) : 0u;
+      first = WI + WH + W2;
     }
     return ld_b128(make_rsrc(base, bytes), (uint32_t)(16 * ((wave - (int)first) * WAVE + lane)), 0);
   };
-  // s_cf: H_res [STT][K][K], then p [STT][K], then H_post [STT][K]
+  // s_cf: H_res [STT][K][K], then p [STT][K] or Q [STT][K][4], then H_post [STT][K]
   auto store_unit = [&](const u32x4_t& v, int islot, int cbuf, bool lists, bool coefs) __attribute__((always_inline)) {
     if (wave < WI) {
       const int u = wave * WAVE + lane;
       if (lists && u < UI) *reinterpret_cast<u32x4_t*>(&s_idx[islot][4 * u]) = v;
-    } else if (wave < WI + WH + 2 * WP && coefs) {
+    } else if (wave < WI + WH + W2 + W3 && coefs) {
       // q: the unit within its array; base: the array's first unit in s_cf
       int q, n, base;
       if (wave < WI + WH) { q = (wave - WI) * WAVE + lane; n = UH; base = 0; }
-      else if (wave < WI + WH + WP) { q = (wave - WI - WH) * WAVE + lane; n = UP; base = UH; }
-      else { q = (wave - WI - WH - WP) * WAVE + lane; n = UP; base = UH + UP; }
+      else if (wave < WI + WH + W2) { q = (wave - WI - WH) * WAVE + lane; n = U2; base = UH; }
+      else { q = (wave - WI - WH - W2) * WAVE + lane; n = U3; base = UH + U2; }
       if (q < n) *reinterpret_cast<u32x4_t*>(&s_cf[cbuf][4 * (base + q)]) = v;
     }
   };
-  // the lane's state loads of a step: its k active rows (FUSE: and out)
   // The step's rows of X (of out): a wave whose block lies past C gets an
   // empty range, so its loads read zeros and its stores are dropped.
   auto x_rsrc = [&](int step) __attribute__((always_inline)) {
     const int rows = kvalid ? step_rows(step, full, tail) : 0;
     return make_rsrc(X + (size_t)(rows > 0 ? step : 0) * STT * N * C, (uint32_t)((size_t)rows * N * C * sizeof(T)));
   };
-  auto issue = [&](PStep<K, FUSE>& st, int step, int islot) __attribute__((always_inline)) {
+  // the lane's state loads of a step: its k active rows; for a write its row
+  // of out, and (MLP-type) the row 16 tokens before, whose tile supplies the
+  // lags that reach back past this tile's first token
+  auto issue = [&](PStep<K>& st, int step, int islot) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rx = x_rsrc(step);
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -1344,19 +1365,35 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
       ij = ij < 0 ? 0 : (ij >= N ? N - 1 : ij);
       st.x[j] = ld_b128(rx, (uint32_t)(((size_t)tau * N + ij) * C * sizeof(T)) + cofs, 0);
     }
-    if constexpr (FUSE) {
+    if constexpr (WR != 0) {
       const int rows = kvalid ? step_rows(step, full, tail) : 0;
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (size_t)(rows > 0 ? step : 0) * STT * C,
-                                                  (uint32_t)((size_t)rows * C * sizeof(T)));
+      const size_t t0 = rows > 0 ? (size_t)STT * step : 0;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + t0 * C, (uint32_t)((size_t)rows * C * sizeof(T)));
       st.o = ld_b128(ro, (uint32_t)((size_t)tau * C * sizeof(T)) + cofs, 0);
+      if constexpr (WR == 4) {
+        // tokens t0 - 16 .. t0 + rows - 1 (from t0 on the first step)
+        const bool back = t0 >= (size_t)TM;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(out + (back ? t0 - TM : 0) * C,
+                                                    (uint32_t)((size_t)(rows > 0 ? rows + (back ? TM : 0) : 0) * C *
+                                                               sizeof(T)));
+        const uint32_t po = back ? (uint32_t)((size_t)tau * C * sizeof(T)) + cofs
+                                 : (tau >= TM ? (uint32_t)((size_t)(tau - TM) * C * sizeof(T)) + cofs : OUT_OF_RANGE);
+        st.op = ld_b128(rp, po, 0);
+      }
     }
   };
   const __amdgpu_buffer_rsrc_t rcorr = make_rsrc(a.corr, (uint32_t)((size_t)a.ntiles * G * P1 * 4));
 
-  // prologue: routing fragments and column sums of the slice, the lists of
-  // the first PD + 1 steps, the coefficients of the first, then the state
-  // loads of the first PD steps
+  // prologue: routing fragments and column sums of the slice, (MLP-type) its
+  // conv weights, the lists of the first PD + 1 steps, the coefficients of
+  // the first, then the state loads of the first PD steps
   load_wslice<N, NTF>(s_w, a.wnext, nkbC, slice, tid);
+  if constexpr (WR == 4) {
+    for (int u = tid; u < 24 * SLC; u += PNTHR) {
+      const int tap = u / SLC, c = slice * SLC + u % SLC;
+      s_cw[tap][u % SLC] = c < C ? a.conv_w[(size_t)tap * C + c] : 0.f;
+    }
+  }
   {
     u32x4_t v[NI - 1];
 #pragma unroll
@@ -1365,13 +1402,13 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
     for (int d = 0; d < NI - 1; ++d) store_unit(v[d], d, 0, true, d == 0);
   }
   __syncthreads();
-  PStep<K, FUSE> sr[NR];
+  PStep<K> sr[NR];
 #pragma unroll
   for (int d = 0; d < PD; ++d) issue(sr[d], team + d * nteams, d);
 
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
-  auto compute = [&](const PStep<K, FUSE>& st, int step, int islot, int cbuf) __attribute__((always_inline)) {
+  auto compute = [&](const PStep<K>& st, int step, int islot, int cbuf) __attribute__((always_inline)) {
     int I[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -1379,22 +1416,67 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
       I[j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
     }
     u32x4_t xn[K];
-    if constexpr (FUSE) {
-      float xa[K][VEC], o[VEC];
+    if constexpr (WR != 0) {
+      constexpr int NB = WR;   // write components
+      float xa[K][VEC], bs[NB][VEC];
 #pragma unroll
       for (int i = 0; i < K; ++i) E::unpack(st.x[i], xa[i]);
-      E::unpack(st.o, o);
+      E::unpack(st.o, bs[0]);
+      if constexpr (WR == 4) {
+        // the causal convolutions of out along the sequence (kernel sizes
+        // 4, 8, 12; lag-i weights at conv_w row off_j + i), in the per-
+        // sublayer write's order: lag 0 first, each branch accumulated from
+        // zero.  Lag i of token r comes from lane r - i of this tile, or for
+        // r < i from lane r + 16 - i of the 16 rows before; lags before the
+        // token's sequence start are zero.
+        const int spos = (STT * step + tau) % a.S;
+        const int cl = cb * KB + VEC * g;   // the lane's first channel within the slice
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          bs[1][e] = fmaf(s_cw[0][cl + e], bs[0][e], 0.f);
+          bs[2][e] = fmaf(s_cw[4][cl + e], bs[0][e], 0.f);
+          bs[3][e] = fmaf(s_cw[12][cl + e], bs[0][e], 0.f);
+        }
+        for_each_c<11>([&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value + 1;   // lag
+          u32x4_t lg;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            // row_shl (16 - i): lane r < i takes lane r + 16 - i of the rows
+            // before; row_shr i: lane r >= i takes lane r - i of this tile
+            const int pv = __builtin_amdgcn_update_dpp(0, (int)st.op[d], 0x100 + (16 - i), 0xf, 0xf, false);
+            lg[d] = (uint32_t)__builtin_amdgcn_update_dpp(pv, (int)st.o[d], 0x110 + i, 0xf, 0xf, false);
+          }
+          lg = i <= spos ? lg : zero;
+          float h[VEC];
+          E::unpack(lg, h);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            if constexpr (i < 4) bs[1][e] = fmaf(s_cw[i][cl + e], h[e], bs[1][e]);
+            if constexpr (i < 8) bs[2][e] = fmaf(s_cw[4 + i][cl + e], h[e], bs[2][e]);
+            bs[3][e] = fmaf(s_cw[12 + i][cl + e], h[e], bs[3][e]);
+          }
+        });
+      }
       const __amdgpu_buffer_rsrc_t rx = x_rsrc(step);
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const float q = s_cf[cbuf][STT * K * K + tau * K + j] * s_cf[cbuf][STT * K * K + STT * K + tau * K + j];
+        float q[NB];
+        if constexpr (WR == 1) {
+          q[0] = s_cf[cbuf][STT * K * K + tau * K + j] * s_cf[cbuf][STT * K * K + STT * K + tau * K + j];
+        } else {
+#pragma unroll
+          for (int v = 0; v < NB; ++v) q[v] = s_cf[cbuf][STT * K * K + (tau * K + j) * NB + v];
+        }
         float nv[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           float sum = 0.f;
 #pragma unroll
           for (int i = 0; i < K; ++i) sum = fmaf(s_cf[cbuf][(tau * K + j) * K + i], xa[i][e], sum);
-          nv[e] = fmaf(q, o[e], sum);
+#pragma unroll
+          for (int v = 0; v < NB; ++v) sum = fmaf(q[v], bs[v][e], sum);
+          nv[e] = sum;
         }
         xn[j] = E::packv_cvt(nv);
         st_b128<CP_NT>(xn[j], rx, (uint32_t)(((size_t)tau * N + I[j]) * C * sizeof(T)) + cofs);
@@ -1438,8 +1520,33 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
       for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, bw[i & 1][n]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
-    sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+    if constexpr (WR == 4) {
+      // two rounds: blocks 2 and 3 of each tile store, blocks 0 and 1 add
+      if (cb >= 2) {
+        const int w2 = b * 2 + cb - 2;
+#pragma unroll
+        for (int n = 0; n < NTF; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s_red[w2][(4 * g + i) * NPF + n * 16 + r] = acc[n][i];
+        sums_to_lds(&s_red[w2][TM * NPF], g, r, S1, S2);
+      }
+      __syncthreads();
+      if (cb < 2) {
+        const int w2 = b * 2 + cb;
+#pragma unroll
+        for (int n = 0; n < NTF; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s_red[w2][(4 * g + i) * NPF + n * 16 + r] += acc[n][i];
+        if (r == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s_red[w2][TM * NPF + 2 * (4 * g + i)] += S1[i];
+        }
+        if ((r >> 2) == g) s_red[w2][TM * NPF + 2 * r + 1] += diag_of(S2, r);
+      }
+    } else {
+      acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
+      sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+    }
     __syncthreads();
     // partial sums of the step's tiles; entries past the step or past the
     // last tile go out of the store's range
@@ -1451,9 +1558,14 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
       const int u = in ? u0 : 0;
       const int bb = u / NSUM, v = u % NSUM;
       const int tile = PTL * step + bb;
-      float x = 0.f;
+      float x;
+      if constexpr (WR == 4) {
+        x = s_red[bb * 2][v] + s_red[bb * 2 + 1][v];
+      } else {
+        x = 0.f;
 #pragma unroll
-      for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+        for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+      }
       st_b32(x, rcorr, in && tile < a.ntiles ? (uint32_t)((((size_t)tile * G + slice) * P1 + v) * 4) : OUT_OF_RANGE);
     }
   };
@@ -1470,12 +1582,12 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
       // rows of later steps: the list PD + 1 steps ahead, the coefficients
       // of the next step
       const u32x4_t nv = load_unit(step + (PD + 1) * nteams, true, false);
-      const u32x4_t nc = FUSE ? load_unit(step + nteams, false, true) : zero;
+      const u32x4_t nc = WR ? load_unit(step + nteams, false, true) : zero;
       issue(sr[(q + PD) % NR], step + PD * nteams, (k + PD) % NI);
       __builtin_amdgcn_sched_barrier(0);
       compute(sr[q], step, k % NI, k & 1);
       store_unit(nv, (k + PD + 1) % NI, 0, true, false);
-      if constexpr (FUSE) store_unit(nc, 0, (k + 1) & 1, false, true);
+      if constexpr (WR != 0) store_unit(nc, 0, (k + 1) & 1, false, true);
       __syncthreads();
     });
     if (done) break;
@@ -1587,27 +1699,34 @@ void route_launch(const Plan& P, const xhc_weights* w, const void* X, char* ws, 
 #endif
 
 // The rewritten rows' share of the next layer's routing, then that layer's
-// routing.  fuse: the write of this (attention-type) layer is done here too.
+// routing.  fuse: the write of this layer is done here too (for the MLP
+// type after the Gram pass and the per-token write coefficients).
 template <class E, int N, int K>
-void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out, const char* ws,
-                 char* wsn, bool fuse, hipStream_t st) {
+void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* w, const xhc_weights* wn, void* X,
+                 const void* out, char* ws, char* wsn, bool fuse, hipStream_t st) {
   if (fuse || XHC_CORR_P) {
     PostPArgs a;
-    a.X = X; a.out = out; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
+    a.X = X; a.out = out; a.T = (int)P.T; a.S = P.S; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
     a.idx = reinterpret_cast<const int*>(ws + P.o_idx);
     a.h_res = reinterpret_cast<const float*>(ws + P.o_hres);
     a.p = reinterpret_cast<const float*>(ws + P.o_p);
     a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+    a.wq = reinterpret_cast<const float*>(ws + P.o_wcoef);
+    a.conv_w = w ? w->conv_w : nullptr;
     a.wnext = reinterpret_cast<const uint4*>(wsn + Pn.o_wfull);
     a.corr = reinterpret_cast<float*>(wsn + Pn.o_corr);
     const unsigned grid = (unsigned)persist_grid(P);
     const bool m2 = P.m == 2 && K > 2;
-    if (fuse) {
-      if (m2) xhc_post_p_kernel<E, N, K, 2, true><<<grid, PNTHR, 0, st>>>(a);
-      else xhc_post_p_kernel<E, N, K, -1, true><<<grid, PNTHR, 0, st>>>(a);
+    if (fuse && P.KR == 4) {
+      launch_xhc_wcoef(P, out, w, ws, st);
+      if (m2) xhc_post_p_kernel<E, N, K, 2, 4><<<grid, PNTHR, 0, st>>>(a);
+      else xhc_post_p_kernel<E, N, K, -1, 4><<<grid, PNTHR, 0, st>>>(a);
+    } else if (fuse) {
+      if (m2) xhc_post_p_kernel<E, N, K, 2, 1><<<grid, PNTHR, 0, st>>>(a);
+      else xhc_post_p_kernel<E, N, K, -1, 1><<<grid, PNTHR, 0, st>>>(a);
     } else {
-      if (m2) xhc_post_p_kernel<E, N, K, 2, false><<<grid, PNTHR, 0, st>>>(a);
-      else xhc_post_p_kernel<E, N, K, -1, false><<<grid, PNTHR, 0, st>>>(a);
+      if (m2) xhc_post_p_kernel<E, N, K, 2, 0><<<grid, PNTHR, 0, st>>>(a);
+      else xhc_post_p_kernel<E, N, K, -1, 0><<<grid, PNTHR, 0, st>>>(a);
     }
     route_fin_launch<N, K>(Pn, wn, wsn, true, P.Gp, st);
     return;
@@ -1657,10 +1776,10 @@ bool pre_chained_dispatch(const Plan& P, const xhc_weights* w, const Plan* Pn, c
 }
 
 template <class E>
-bool tail_dispatch(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out, const char* ws,
-                   char* wsn, bool fuse, hipStream_t st) {
+bool tail_dispatch(const Plan& P, const Plan& Pn, const xhc_weights* w, const xhc_weights* wn, void* X,
+                   const void* out, char* ws, char* wsn, bool fuse, hipStream_t st) {
   return dispatch_shape(P.N, P.K, [&](auto n, auto k) {
-    tail_launch<E, decltype(n)::value, decltype(k)::value>(P, Pn, wn, X, out, ws, wsn, fuse, st);
+    tail_launch<E, decltype(n)::value, decltype(k)::value>(P, Pn, w, wn, X, out, ws, wsn, fuse, st);
   });
 }
 
@@ -1702,13 +1821,13 @@ bool launch_flash_route_p(const Plan& P, const void* X, const void* wp, float* p
   }
 }
 
-bool chain_post_fused(const Plan& P) { return XHC_POST_FUSE && P.KR == 1 && !P.mhc && !P.flash; }
+bool chain_post_fused(const Plan& P) { return XHC_POST_FUSE && !P.mhc && !P.flash && (P.KR == 1 || P.KR == 4); }
 
-bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out,
-                           const char* ws, char* wsn, bool fuse, hipStream_t st) {
+bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* w, const xhc_weights* wn, void* X,
+                           const void* out, char* ws, char* wsn, bool fuse, hipStream_t st) {
   if (fuse && !chain_post_fused(P)) return false;
-  return P.dtype == XHC_BF16 ? tail_dispatch<Bf16>(P, Pn, wn, X, out, ws, wsn, fuse, st)
-                             : tail_dispatch<F32>(P, Pn, wn, X, out, ws, wsn, fuse, st);
+  return P.dtype == XHC_BF16 ? tail_dispatch<Bf16>(P, Pn, w, wn, X, out, ws, wsn, fuse, st)
+                             : tail_dispatch<F32>(P, Pn, w, wn, X, out, ws, wsn, fuse, st);
 }
 
 // Active maps from active-projection partials laid out [ntiles][G][P2] of

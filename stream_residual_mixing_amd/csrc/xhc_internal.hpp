@@ -36,7 +36,7 @@ struct Plan {
   // workspace byte offsets
   size_t o_idx = SIZE_MAX, o_p = SIZE_MAX, o_hpre = SIZE_MAX, o_hres = SIZE_MAX, o_hpost = SIZE_MAX,
          o_z = SIZE_MAX, o_gstat = SIZE_MAX, o_wfull = 0, o_wact = SIZE_MAX, o_colsum = SIZE_MAX, o_part = 0, o_stats = 0,
-         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX,
+         o_gram = SIZE_MAX, o_part2 = SIZE_MAX, o_sync = SIZE_MAX, o_corr = SIZE_MAX, o_wcoef = SIZE_MAX,
          total = 0;
   // xHC-Flash block (attention + MLP sharing one routing)
   bool flash = false;
@@ -145,8 +145,11 @@ bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn,
 // The rewritten rows' share of the next layer's routing and that layer's
 // routing; fuse: also this layer's write (attention-type, chain_post_fused).
 bool chain_post_fused(const Plan& P);
-bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* wn, void* X, const void* out,
-                           const char* ws, char* wsn, bool fuse, hipStream_t st);
+bool launch_xhc_chain_tail(const Plan& P, const Plan& Pn, const xhc_weights* w, const xhc_weights* wn, void* X,
+                           const void* out, char* ws, char* wsn, bool fuse, hipStream_t st);
+// MLP-type write coefficients for the persistent post pass: the Gram pass,
+// then per token Q = diag(p) H_post Tm into ws + P.o_wcoef ([T][K][4]).
+void launch_xhc_wcoef(const Plan& P, const void* out, const xhc_weights* w, char* ws, hipStream_t st);
 
 // Helpers shared with the xHC-Flash launchers.
 void launch_pack_b(int dtype, const void* W, long nkb, int ncol, int NT, void* out, hipStream_t st);

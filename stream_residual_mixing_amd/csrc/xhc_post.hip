@@ -810,6 +810,84 @@ bool launch_unmixed_write(const Plan& P, int KR, void* X, const void* out, const
                              : unmixed_launch<F32>(P, KR, X, out, conv_w, ws, st);
 }
 
+// Per-token write coefficients of an MLP-type sublayer for the persistent
+// post pass: Q[j][b] = p_j sum_r H_post[j][r] Tm[r][b], Tm the Gram-Schmidt
+// map from the summed Gram partials (identity without Gram-Schmidt), with
+// the apply kernel's arithmetic (the same sums in the same order, the same
+// double-precision map, rounded once), so that both writes give the same
+// bits.  One thread per token.
+struct WcoefArgs {
+  int T, nslices, use_mgs;
+  float eps_mgs;
+  const double* gram;
+  const float *p, *h_post;
+  float* wq;   // [T][K][4]
+};
+
+template <int K>
+__global__ __launch_bounds__(256) void xhc_wcoef_kernel(WcoefArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  double Tm[4][4];
+  if (a.use_mgs) {
+    double pg[10];
+#pragma unroll
+    for (int j = 0; j < 10; ++j) pg[j] = 0.0;
+    for (int sl = 0; sl < a.nslices; ++sl)
+#pragma unroll
+      for (int j = 0; j < 10; ++j) pg[j] += a.gram[((size_t)sl * a.T + t) * 10 + j];
+    double G[4][4];
+    int q = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = u; v < 4; ++v) { G[u][v] = pg[q]; G[v][u] = pg[q]; ++q; }
+    mgs_from_gram(G, (double)a.eps_mgs, Tm);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) Tm[j][b] = (j == b) ? 1.0 : 0.0;
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    float hpo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hpo[r] = a.h_post[((size_t)t * K + j) * 4 + r];
+    write_coeffs<4>(Tm, hpo, a.p[(size_t)t * K + j], a.wq + ((size_t)t * K + j) * 4);
+  }
+}
+
+template <class E>
+static void wcoef_launch(const Plan& P, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
+  XhcPostArgs g{};
+  g.out = out; g.T = (int)P.T; g.S = P.S; g.C = P.C; g.N = P.N; g.nslices = P.nslices;
+  g.conv_w = w->conv_w; g.use_mgs = P.use_mgs; g.eps_mgs = P.eps_mgs;
+  g.gram = reinterpret_cast<double*>(ws + P.o_gram);
+  if (P.use_mgs) {
+    dim3 grid((g.T + PT - 1) / PT, g.nslices);
+    xhc_gram_kernel<E><<<grid, 256, 0, st>>>(g);
+  }
+  WcoefArgs a;
+  a.T = (int)P.T; a.nslices = P.nslices; a.use_mgs = P.use_mgs; a.eps_mgs = P.eps_mgs;
+  a.gram = g.gram;
+  a.p = reinterpret_cast<const float*>(ws + P.o_p);
+  a.h_post = reinterpret_cast<const float*>(ws + P.o_hpost);
+  a.wq = reinterpret_cast<float*>(ws + P.o_wcoef);
+  const unsigned nb = (unsigned)((P.T + 255) / 256);
+  switch (P.K) {
+    case 4: xhc_wcoef_kernel<4><<<nb, 256, 0, st>>>(a); break;
+    case 2: xhc_wcoef_kernel<2><<<nb, 256, 0, st>>>(a); break;
+    case 1: xhc_wcoef_kernel<1><<<nb, 256, 0, st>>>(a); break;
+    default: break;
+  }
+}
+
+void launch_xhc_wcoef(const Plan& P, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
+  if (P.dtype == XHC_BF16) wcoef_launch<Bf16>(P, out, w, ws, st);
+  else wcoef_launch<F32>(P, out, w, ws, st);
+}
+
 bool launch_xhc_post(const Plan& P, void* X, const void* out, const xhc_weights* w, char* ws, hipStream_t st) {
   double* gram = reinterpret_cast<double*>(ws + P.o_gram);
   return P.dtype == XHC_BF16 ? xhc_post_launch<Bf16>(P, X, out, w, ws, gram, st)

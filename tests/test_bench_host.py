@@ -50,13 +50,16 @@ def test_counter_rows_split_into_calls():
     chain = [k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_proj_p_kernel<xhc::Bf16, 16>"), k("xhc_route_fin_kernel<16, 4>"),
              k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_pre_chained_p_kernel<xhc::Bf16, 16, 4, 1, 2>"),
              k("xhc_act_fin_kernel<4, 1>"),
-             k("xhc_post_p_kernel<xhc::Bf16, 16, 4, 2, true>"), k("xhc_route_fin_kernel<16, 4>"),
+             k("xhc_post_p_kernel<xhc::Bf16, 16, 4, 2, 1>"), k("xhc_route_fin_kernel<16, 4>"),
              k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_pre_chained_kernel<xhc::Bf16, 16, 4, 4, false, 1>"),
              k("xhc_act_fin_kernel<4, 4>"),
-             k("xhc_gram_kernel<xhc::Bf16>"), k("xhc_apply_kernel<xhc::Bf16, 4, 4, 6, 0>"),
-             k("xhc_post_p_kernel<xhc::Bf16, 16, 4, 2, false>"), k("xhc_route_fin_kernel<16, 4>")]
+             k("xhc_gram_kernel<xhc::Bf16>"), k("xhc_wcoef_kernel<4>"),
+             k("xhc_post_p_kernel<xhc::Bf16, 16, 4, 2, 4>"), k("xhc_route_fin_kernel<16, 4>"),
+             k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_pre_chained_kernel<xhc::Bf16, 16, 4, 1, false, 1>"),
+             k("xhc_act_fin_kernel<4, 1>"),
+             k("xhc_apply_kernel<xhc::Bf16, 4, 1, 8, 0>")]
     calls = bench._split_calls(chain)
-    assert [len(c) for c in calls] == [3, 3, 2, 3, 4]
+    assert [len(c) for c in calls] == [3, 3, 2, 3, 4, 3, 1]
     mhc = [k("pack_b_kernel<xhc::Bf16>"), k("mhc_proj_kernel<18>"), k("mhc_read_kernel<xhc::Bf16, 16>"),
            k("mhc_post_kernel<xhc::Bf16, 16>")]
     assert [len(c) for c in bench._split_calls(mhc)] == [3, 1]

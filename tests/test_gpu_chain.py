@@ -93,18 +93,21 @@ def test_chain_f32_several_steps_per_team_c4096(lib):
     run_chain(lib, K.chain_configs(16, 4, 2, 4096, 1, 300, "MAM", dtype="f32"), seed=27, margin=K.MARGIN)
 
 
+@pytest.mark.parametrize("kinds", ["AM", "MA"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_chained_attention_write_is_the_sublayer_write(lib, dtype):
-    """After an attention-type sublayer with a next sublayer, the chained post
-    call writes the state in the same pass that contracts the new rows for
-    the next routing.  Its write must be the per-sublayer write bit for bit:
-    same maps (left by the chained pre call), same state, same output.
-    N=16, k=4, m=2, C=256, 2 x 16400 tokens, so that xhc_post takes its
-    tiled write and the chained pass its ragged last step."""
+def test_chained_write_is_the_sublayer_write(lib, kinds, dtype):
+    """With a next sublayer, the chained post call writes the state in the
+    same pass that contracts the new rows for the next routing (after an
+    MLP-type sublayer, with the write basis formed there from out and its
+    causal convolutions).  Its write must be the per-sublayer write bit for
+    bit: same maps (left by the chained pre call), same state, same output.
+    N=16, k=4, m=2, C=256, 2 x 16401 tokens, so that xhc_post takes its
+    tiled write and the chained pass its ragged last step; the sequence
+    start of the second batch item falls inside a tile."""
     import torch
     from stream_residual_mixing_amd import synth
     from stream_residual_mixing_amd.binding import weights_to_device
-    cfgs = K.chain_configs(16, 4, 2, 256, 2, 16400, "AM", dtype=dtype)
+    cfgs = K.chain_configs(16, 4, 2, 256, 2, 16401, kinds, dtype=dtype)
     c0, c1 = cfgs
     w = [weights_to_device(synth.xhc_layer_weights(41, l, 16, 4, 256, c.K_r, dtype)) for l, c in enumerate(cfgs)]
     X = synth.state(41, c0.T, 16, 256, dtype).to("cuda")
