@@ -1430,6 +1430,9 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
         // r < i from lane r + 16 - i of the 16 rows before; lags before the
         // token's sequence start are zero.
         const int spos = (STT * step + tau) % a.S;
+        // whether any token of the wave's tile lies within 11 of its
+        // sequence start (uniform over the wave; most tiles skip the masks)
+        const bool near_start = __builtin_amdgcn_ballot_w64(spos < 11) != 0;
         const int cl = cb * KB + VEC * g;   // the lane's first channel within the slice
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -1447,7 +1450,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
             const int pv = __builtin_amdgcn_update_dpp(0, (int)st.op[d], 0x100 + (16 - i), 0xf, 0xf, false);
             lg[d] = (uint32_t)__builtin_amdgcn_update_dpp(pv, (int)st.o[d], 0x110 + i, 0xf, 0xf, false);
           }
-          lg = i <= spos ? lg : zero;
+          if (near_start) lg = i <= spos ? lg : zero;
           float h[VEC];
           E::unpack(lg, h);
 #pragma unroll
