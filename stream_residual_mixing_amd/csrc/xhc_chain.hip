@@ -55,6 +55,7 @@ struct RouteDims {
   static constexpr int NPF = NTF * 16;
   static constexpr int NSUM = TM * NPF + 2 * TM;  // projection + (sum x, sum x^2) per token
   static constexpr int P1 = NSUM + 16;            // + column sums of W_r
+  static constexpr int FT = (P1 / 2 + WAVE - 1) / WAVE * WAVE;   // routing finalize: a pair of entries per thread
 };
 
 template <int K, int KR>
@@ -63,6 +64,7 @@ struct ActDims {
   static constexpr int NTA = (NA + 15) / 16;
   static constexpr int NPA = NTA * 16;
   static constexpr int P2 = TM * NPA + TM;  // projection + sum of squares per token
+  static constexpr int FT = (P2 / 2 + WAVE - 1) / WAVE * WAVE;   // active finalize: a pair of entries per thread
 };
 
 // Running sum of x and of x^2 over one fragment, in float.  (The packed bf16
@@ -133,57 +135,61 @@ struct RouteFinArgs {
 };
 
 template <int N, int K>
-__global__ __launch_bounds__(256) void xhc_route_fin_kernel(RouteFinArgs a) {
+__global__ __launch_bounds__(RouteDims<N>::FT) void xhc_route_fin_kernel(RouteFinArgs a) {
   using D = RouteDims<N>;
-  constexpr int NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  constexpr int NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1, FT = D::FT;
   __shared__ float s_sum[P1];
   __shared__ float s_z[TM][N];
   __shared__ float s_hpre[TM][N];
   const int tid = threadIdx.x, G = a.G, Gc = a.Gc;
   const int tile = blockIdx.x, t0 = tile * TM;
 
+  // entries u, u + 1 of the tile's partial: the G routing slices, then the
+  // Gc correction slices (projection and sums only), added in that order.
+  // With up to 32 of each, all loads go out at once.
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part + (size_t)tile * G * P1, (uint32_t)((size_t)G * P1 * 4));
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(a.corr ? a.corr + (size_t)tile * Gc * P1 : a.part, a.corr ? (uint32_t)((size_t)Gc * P1 * 4) : 0u);
-  for (int u = 2 * tid; u < P1; u += 2 * 256) {
-    float v0 = 0.f, v1 = 0.f;
-    for (int s0 = 0; s0 < G; s0 += 16) {
-      uint64_t x[16];
+  {
+    const int u = 2 * tid;
+    const uint32_t off = u < P1 ? (uint32_t)(u * 4) : OUT_OF_RANGE;
+    const uint32_t offc = u < NSUM ? (uint32_t)(u * 4) : OUT_OF_RANGE;
+    float v[2] = {0.f, 0.f};
+    if (G <= 32 && Gc <= 32) {
+      uint64_t x[32], y[32];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) x[q] = s0 + q < G ? ld_b64(rp, (uint32_t)(((s0 + q) * P1 + u) * 4)) : 0ull;
+      for (int q = 0; q < 32; ++q) x[q] = ld_b64(rp, off + (uint32_t)(q * P1 * 4));
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (s0 + q < G) {
-          v0 += __uint_as_float((uint32_t)x[q]);
-          v1 += __uint_as_float((uint32_t)(x[q] >> 32));
-        }
-    }
-    if (a.corr && u < NSUM) {
-      for (int s0 = 0; s0 < Gc; s0 += 16) {
-        uint64_t x[16];
+      for (int q = 0; q < 32; ++q) y[q] = ld_b64(rc, offc + (uint32_t)(q * P1 * 4));
 #pragma unroll
-        for (int q = 0; q < 16; ++q) x[q] = s0 + q < Gc ? ld_b64(rc, (uint32_t)(((s0 + q) * P1 + u) * 4)) : 0ull;
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (s0 + q < Gc) {
-            v0 += __uint_as_float((uint32_t)x[q]);
-            v1 += __uint_as_float((uint32_t)(x[q] >> 32));
-          }
+      for (int q = 0; q < 32; ++q) {
+        v[0] += __uint_as_float((uint32_t)x[q]);
+        v[1] += __uint_as_float((uint32_t)(x[q] >> 32));
       }
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        v[0] += __uint_as_float((uint32_t)y[q]);
+        v[1] += __uint_as_float((uint32_t)(y[q] >> 32));
+      }
+    } else {
+      add_slices2<32>(rp, G, P1, off, v);
+      add_slices2<32>(rc, Gc, P1, offc, v);
     }
-    s_sum[u] = v0;
-    s_sum[u + 1] = v1;
+    if (u < P1) {
+      s_sum[u] = v[0];
+      s_sum[u + 1] = v[1];
+    }
   }
   __syncthreads();
   const float n_el = (float)N * (float)a.C;
-  for (int u = tid; u < TM * N; u += 256) {
+  for (int u = tid; u < TM * N; u += FT) {
     const int tau = u / N, i = u % N;
     route_logits(s_sum[tau * NPF + i], s_sum[tau * NPF + N + i], s_sum[TM * NPF + 2 * tau],
                  s_sum[TM * NPF + 2 * tau + 1], s_sum[NSUM + i], n_el, a.eps, a.a_pre, a.b_pre[i], t0 + tau < a.T,
                  &s_z[tau][i], &s_hpre[tau][i]);
   }
   __syncthreads();
-  for (int u = tid; u < TM * N; u += 256) {
+  for (int u = tid; u < TM * N; u += FT) {
     const int tau = u / N, i = u % N, t = t0 + tau;
     if (t < a.T) {
       a.z[(size_t)t * N + i] = s_z[tau][i];
@@ -437,19 +443,27 @@ struct ActFinArgs {
 };
 
 template <int K, int KR>
-__global__ __launch_bounds__(256) void xhc_act_fin_kernel(ActFinArgs a) {
+__global__ __launch_bounds__((ActDims<K, KR>::FT)) void xhc_act_fin_kernel(ActFinArgs a) {
   using A = ActDims<K, KR>;
   constexpr int NPA = A::NPA, P2 = A::P2;
-  __shared__ float s_sum[4][P2];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x * 4 + wave;
-  const bool live = tile < a.ntiles;
+  __shared__ float s_sum[P2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int tile = blockIdx.x;
   const int G = a.G, t0 = tile * TM;
-  static_assert(P2 % 4 == 0, "16-byte loads of the active partials");
-  if (live) sum_slices4<WAVE, 0>(a.part2 + (size_t)tile * G * P2, G, P2, P2, &s_sum[wave][0], lane);
+  // entries u, u + 1 summed over the G slices in order, all loads at once
+  {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.part2 + (size_t)tile * G * P2, (uint32_t)((size_t)G * P2 * 4));
+    const int u = 2 * tid;
+    float v[2] = {0.f, 0.f};
+    add_slices2<32>(rs, G, P2, u < P2 ? (uint32_t)(u * 4) : OUT_OF_RANGE, v);
+    if (u < P2) {
+      s_sum[u] = v[0];
+      s_sum[u + 1] = v[1];
+    }
+  }
   __syncthreads();
-  if (!live) return;
-  const float* sm = &s_sum[wave][0];
+  if (tid >= WAVE) return;   // one wave finishes the tile
+  const float* sm = &s_sum[0];
   constexpr int TPP = WAVE / K;
   constexpr int PASSES = (TM + TPP - 1) / TPP;
 #pragma unroll
@@ -1664,7 +1678,7 @@ void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, con
   f.a_res = w->alpha_res; f.a_post = w->alpha_post; f.eps = P.eps_norm; f.iters = P.iters;
   f.h_res = reinterpret_cast<float*>(ws + P.o_hres);
   f.h_post = reinterpret_cast<float*>(ws + P.o_hpost);
-  xhc_act_fin_kernel<K, KR><<<(unsigned)((P.ntiles + 3) / 4), 256, 0, st>>>(f);
+  xhc_act_fin_kernel<K, KR><<<(unsigned)P.ntiles, ActDims<K, KR>::FT, 0, st>>>(f);
 }
 
 template <int N, int K>
@@ -1681,7 +1695,7 @@ void route_fin_launch(const Plan& P, const xhc_weights* w, char* ws, bool with_c
   f.h_pre = reinterpret_cast<float*>(ws + P.o_hpre);
   f.z = reinterpret_cast<float*>(ws + P.o_z);
   f.gstat = reinterpret_cast<float*>(ws + P.o_gstat);
-  xhc_route_fin_kernel<N, K><<<(unsigned)P.ntiles, 256, 0, st>>>(f);
+  xhc_route_fin_kernel<N, K><<<(unsigned)P.ntiles, RouteDims<N>::FT, 0, st>>>(f);
 }
 
 template <class E, int N, int K>
@@ -1843,12 +1857,12 @@ bool launch_act_fin(const Plan& P, int G, const float* part2, const float* b_res
   f.b_res = b_res; f.b_post = b_post;
   f.a_res = a_res; f.a_post = a_post; f.eps = P.eps_norm; f.iters = P.iters;
   f.h_res = h_res; f.h_post = h_post;
-  const unsigned grid = (unsigned)((P.ntiles + 3) / 4);
+  const unsigned grid = (unsigned)P.ntiles;
   switch (P.K * 10 + P.KR) {
-    case 44: xhc_act_fin_kernel<4, 4><<<grid, 256, 0, st>>>(f); return true;
-    case 41: xhc_act_fin_kernel<4, 1><<<grid, 256, 0, st>>>(f); return true;
-    case 14: xhc_act_fin_kernel<1, 4><<<grid, 256, 0, st>>>(f); return true;
-    case 11: xhc_act_fin_kernel<1, 1><<<grid, 256, 0, st>>>(f); return true;
+    case 44: xhc_act_fin_kernel<4, 4><<<grid, ActDims<4, 4>::FT, 0, st>>>(f); return true;
+    case 41: xhc_act_fin_kernel<4, 1><<<grid, ActDims<4, 1>::FT, 0, st>>>(f); return true;
+    case 14: xhc_act_fin_kernel<1, 4><<<grid, ActDims<1, 4>::FT, 0, st>>>(f); return true;
+    case 11: xhc_act_fin_kernel<1, 1><<<grid, ActDims<1, 1>::FT, 0, st>>>(f); return true;
     default: return false;
   }
 }

@@ -30,6 +30,7 @@
 
 #include "xhc_device.hpp"
 #include "xhc_internal.hpp"
+#include "xhc_tile.hpp"
 
 namespace xhc {
 
@@ -38,6 +39,17 @@ namespace {
 template <class E>
 __device__ __forceinline__ typename Quad<E>::V ldq(const typename E::T* p) {
   return *reinterpret_cast<const typename Quad<E>::V*>(p);
+}
+// The same through a buffer resource (a byte offset past its range reads zeros).
+template <class E>
+__device__ __forceinline__ typename Quad<E>::V ldq_rs(__amdgpu_buffer_rsrc_t rs, uint32_t off);
+template <>
+__device__ __forceinline__ Quad<Bf16>::V ldq_rs<Bf16>(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(Quad<Bf16>::V, ld_b64(rs, off));
+}
+template <>
+__device__ __forceinline__ Quad<F32>::V ldq_rs<F32>(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(Quad<F32>::V, ld_b128(rs, off, 0));
 }
 
 __device__ __forceinline__ void load_conv_weights(const float* __restrict__ cw, int C, int c, bool act,
@@ -128,98 +140,71 @@ __device__ __forceinline__ void for_period(F&& f) {
   }
 }
 
-// Sum of 16 values over the 64 lanes of a wave, as a reduce-scatter: each
-// step halves the values a lane keeps and adds its partner's copy of that
-// half.  On return every lane holds one total: the one with index
-// 8 b5 + 4 b4 + 2 b3 + b2 (bits of the lane id); the four lanes of a group of
-// 4 hold the same value.  All exchanges are VALU lane operations, no LDS:
-//   b5: v_permlane32_swap of (low half, high half) leaves each lane with its
-//       own kept value and its partner's copy of it, so one add finishes it;
-//   b4: v_permlane16_swap (odd and even rows of 16 lanes), the same way;
-//   b3, b2: DPP row shifts by 8 and 4 within a row, each restricted by bank
-//       mask to the lanes that keep that half;
-//   b1, b0: DPP quad permutations (all lanes end with the group's total).
-// Every step adds a kept value and its partner's copy, in the same pairs as a
-// plain xor butterfly.
-template <int CTRL, int BANKS>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, BANKS, false));
-}
+// Sum of the 10 Gram entries over the 64 lanes of a wave, as a reduce-scatter
+// in doubles: each step halves the values a lane keeps and adds its
+// partner's copy of them, so the work falls with every step.  On return a
+// group of 4 lanes holds one total (wave_sum10_index says which).  Every
+// exchange is a VALU lane operation on the two 32-bit halves of a double:
+//   bit 5: v_permlane32_swap of value i (kept by lanes 0-31) and value 5 + i
+//          (kept by lanes 32-63), i < 5, so one add finishes each pair;
+//   bit 4: v_permlane16_swap, even rows keep one value, odd rows another:
+//          pairs (0, 3), (1, 4) of the five, and value 2 with itself (both
+//          rows keep it);
+//   bit 3: DPP row shifts by 8: lanes 0-7 of a row keep the first pair's
+//          value, lanes 8-15 the second's; value 2 goes to lanes 0-7;
+//   bit 2: DPP row shifts by 4: lanes 0-3 of an 8-lane group keep the value
+//          from bit 3, lanes 4-7 value 2 (meaningful where bit 3 is 0);
+//   bits 1, 0: DPP quad permutations (all 4 lanes end with the total).
+// The DPP moves write every lane (lanes whose source lies outside the row
+// read zero and are never selected), so no register has to be cleared first.
 constexpr int DPP_ROW_SHL8 = 0x108, DPP_ROW_SHR8 = 0x118, DPP_ROW_SHL4 = 0x104, DPP_ROW_SHR4 = 0x114;
 constexpr int DPP_QUAD_XOR2 = 0x4e, DPP_QUAD_XOR1 = 0xb1;   // quad_perm [2,3,0,1], [1,0,3,2]
-
-__device__ __forceinline__ float wave_sum16(const float (&v)[16], int lane) {
-  float a[8], b[4], c[2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[8 + i]), false, false);
-    a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[4 + i]), false, false);
-    b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  const bool u8 = (lane & 8) != 0, u4 = (lane & 4) != 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    // lanes 0-7 of a row (banks 0, 1) keep b[i] and add lane l + 8's copy;
-    // lanes 8-15 (banks 2, 3) keep b[2 + i] and add lane l - 8's
-    const float lo = b[i] + dpp_f<DPP_ROW_SHL8, 0x3>(b[i]);
-    const float hi = b[2 + i] + dpp_f<DPP_ROW_SHR8, 0xc>(b[2 + i]);
-    c[i] = u8 ? hi : lo;
-  }
-  const float lo = c[0] + dpp_f<DPP_ROW_SHL4, 0x5>(c[0]);
-  const float hi = c[1] + dpp_f<DPP_ROW_SHR4, 0xa>(c[1]);
-  float x = u4 ? hi : lo;
-  x += dpp_f<DPP_QUAD_XOR2, 0xf>(x);
-  x += dpp_f<DPP_QUAD_XOR1, 0xf>(x);
-  return x;
-}
-// The same reduce-scatter on doubles: every lane move above is a fixed
-// permutation of 32-bit lanes, so applying it to the low and the high halves
-// of a double moves the double as a whole.
 __device__ __forceinline__ uint32_t lo32(double x) { return (uint32_t)__double2loint(x); }
 __device__ __forceinline__ uint32_t hi32(double x) { return (uint32_t)__double2hiint(x); }
 __device__ __forceinline__ double mk_d(uint32_t lo, uint32_t hi) { return __hiloint2double((int)hi, (int)lo); }
-template <int CTRL, int BANKS>
+template <int CTRL>
 __device__ __forceinline__ double dpp_d(double x) {
-  const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo32(x), CTRL, 0xf, BANKS, false);
-  const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi32(x), CTRL, 0xf, BANKS, false);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo32(x), CTRL, 0xf, 0xf, true);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi32(x), CTRL, 0xf, 0xf, true);
   return mk_d(l, h);
 }
+// x (kept where lane bit 5 is 0) and y (kept where it is 1), each plus its copy in the other half
+__device__ __forceinline__ double swap32_add(double x, double y) {
+  const auto rl = __builtin_amdgcn_permlane32_swap(lo32(x), lo32(y), false, false);
+  const auto rh = __builtin_amdgcn_permlane32_swap(hi32(x), hi32(y), false, false);
+  return mk_d(rl[0], rh[0]) + mk_d(rl[1], rh[1]);
+}
+// the same for lane bit 4 (even and odd rows of 16 lanes)
+__device__ __forceinline__ double swap16_add(double x, double y) {
+  const auto rl = __builtin_amdgcn_permlane16_swap(lo32(x), lo32(y), false, false);
+  const auto rh = __builtin_amdgcn_permlane16_swap(hi32(x), hi32(y), false, false);
+  return mk_d(rl[0], rh[0]) + mk_d(rl[1], rh[1]);
+}
 
-__device__ __forceinline__ double wave_sum16_d(const double (&v)[16], int lane) {
-  double a[8], b[4], c[2];
+__device__ __forceinline__ double wave_sum10_d(const double (&v)[10], int lane) {
+  double a[5];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const auto rl = __builtin_amdgcn_permlane32_swap(lo32(v[i]), lo32(v[8 + i]), false, false);
-    const auto rh = __builtin_amdgcn_permlane32_swap(hi32(v[i]), hi32(v[8 + i]), false, false);
-    a[i] = mk_d(rl[0], rh[0]) + mk_d(rl[1], rh[1]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const auto rl = __builtin_amdgcn_permlane16_swap(lo32(a[i]), lo32(a[4 + i]), false, false);
-    const auto rh = __builtin_amdgcn_permlane16_swap(hi32(a[i]), hi32(a[4 + i]), false, false);
-    b[i] = mk_d(rl[0], rh[0]) + mk_d(rl[1], rh[1]);
-  }
+  for (int i = 0; i < 5; ++i) a[i] = swap32_add(v[i], v[5 + i]);
+  const double b0 = swap16_add(a[0], a[3]), b1 = swap16_add(a[1], a[4]), b2 = swap16_add(a[2], a[2]);
   const bool u8 = (lane & 8) != 0, u4 = (lane & 4) != 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const double lo = b[i] + dpp_d<DPP_ROW_SHL8, 0x3>(b[i]);
-    const double hi = b[2 + i] + dpp_d<DPP_ROW_SHR8, 0xc>(b[2 + i]);
-    c[i] = u8 ? hi : lo;
-  }
-  const double lo = c[0] + dpp_d<DPP_ROW_SHL4, 0x5>(c[0]);
-  const double hi = c[1] + dpp_d<DPP_ROW_SHR4, 0xa>(c[1]);
-  double x = u4 ? hi : lo;
-  x += dpp_d<DPP_QUAD_XOR2, 0xf>(x);
-  x += dpp_d<DPP_QUAD_XOR1, 0xf>(x);
+  const double c0lo = b0 + dpp_d<DPP_ROW_SHL8>(b0);
+  const double c0hi = b1 + dpp_d<DPP_ROW_SHR8>(b1);
+  const double c1 = b2 + dpp_d<DPP_ROW_SHL8>(b2);
+  const double c0 = u8 ? c0hi : c0lo;
+  const double dlo = c0 + dpp_d<DPP_ROW_SHL4>(c0);
+  const double dhi = c1 + dpp_d<DPP_ROW_SHR4>(c1);
+  double x = u4 ? dhi : dlo;
+  x += dpp_d<DPP_QUAD_XOR2>(x);
+  x += dpp_d<DPP_QUAD_XOR1>(x);
   return x;
 }
 
-__device__ __forceinline__ int wave_sum16_index(int lane) {
-  return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+// Index of the total wave_sum10_d leaves in this lane, or -1 (no total, or a
+// copy of one another lane group holds).
+__device__ __forceinline__ int wave_sum10_index(int lane) {
+  const int h5 = (lane >> 5) & 1, h4 = (lane >> 4) & 1, h3 = (lane >> 3) & 1, h2 = (lane >> 2) & 1;
+  if (h2 == 0) return (h3 ? (h4 ? 4 : 1) : (h4 ? 3 : 0)) + 5 * h5;
+  return (h3 == 0 && h4 == 0) ? 2 + 5 * h5 : -1;
 }
 
 // Modified Gram-Schmidt on coefficient vectors: v_j = sum_a Tm[j][a] basis_a,
@@ -304,30 +289,42 @@ __global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
   load_conv_weights(a.conv_w, a.C, cc, act, w1, w2, w3);
   float h[HL][4];
   load_history<E>(out, t0, t0 % a.S, a.C, cc, act, h);
-  const int myidx = wave_sum16_index(lane);
+  const int myidx = wave_sum10_index(lane);
+
+  // The block's rows of out through a resource that ends at its last token,
+  // so that the batch loaded ahead past it reads zeros (as does a lane past
+  // C).  Batches of GB rows are loaded one batch ahead of their use.
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(out + (size_t)t0 * a.C, (uint32_t)((size_t)(t1 - t0) * a.C * sizeof(T)));
+  const uint32_t lo = act ? (uint32_t)(cc * sizeof(T)) : OUT_OF_RANGE;
+  const uint32_t rowb = (uint32_t)(a.C * sizeof(T));
+  typename Qd::V cur[GB], nxt[GB];
+#pragma unroll
+  for (int u = 0; u < GB; ++u) nxt[u] = ldq_rs<E>(ro, lo + (uint32_t)u * rowb);
 
   // sequence position of the next token, kept in a scalar register so that
   // the clearing at a sequence start is a branch, not per-element selects
   int s = __builtin_amdgcn_readfirstlane(t0 % a.S);
   for (int tp = t0; tp < t1; tp += HL) {
-    typename Qd::V rows[GB];
     for_period([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       const int t = tp + q;
       if constexpr (q % GB == 0) {
 #pragma unroll
-        for (int u = 0; u < GB; ++u)
-          rows[u] = (act && t + u < t1) ? ldq<E>(out + (size_t)(t + u) * a.C + cc) : typename Qd::V{};
+        for (int u = 0; u < GB; ++u) {
+          cur[u] = nxt[u];
+          nxt[u] = ldq_rs<E>(ro, lo + (uint32_t)(t - t0 + GB + u) * rowb);
+        }
       }
       if (t < t1) {
         float r[4];
-        Qd::unpack(rows[q % GB], r);
+        Qd::unpack(cur[q % GB], r);
         push_history<q>(h, r, s);
         s = s + 1 == a.S ? 0 : s + 1;
         float b[4][4];
         conv_basis<q>(h, w1, w2, w3, b);
         // products of floats are exact in double
-        double pr[16];
+        double pr[10];
         int k = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -338,10 +335,8 @@ __global__ __launch_bounds__(256) void xhc_gram_kernel(XhcPostArgs a) {
             for (int e = 0; e < 4; ++e) d = fma((double)b[u][e], (double)b[v][e], d);
             pr[k++] = d;
           }
-#pragma unroll
-        for (int j = 10; j < 16; ++j) pr[j] = 0.0;
-        const double tot = wave_sum16_d(pr, lane);
-        if ((lane & 3) == 0 && myidx < 10) s_g[t - t0][wave][myidx] = tot;
+        const double tot = wave_sum10_d(pr, lane);
+        if ((lane & 3) == 0 && myidx >= 0) s_g[t - t0][wave][myidx] = tot;
       }
     });
   }

@@ -117,32 +117,26 @@ __device__ __forceinline__ void sum_slices(const float* __restrict__ src, int G,
   }
 }
 
-// Sum of the 8 per-wave partials of element u, in a fixed order.
-// The same with 16-byte loads (n, stride multiples of 4; src 16-byte aligned):
-// twice the bytes in flight per load instruction.
-template <int NTHR, int AUX>
-__device__ __forceinline__ void sum_slices4(const float* __restrict__ src, int G, int stride, int n,
-                                            float* __restrict__ dst, int tid) {
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)((size_t)G * stride * 4));
-  for (int u = 4 * tid; u < n; u += 4 * NTHR) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < G; s0 += 16) {
-      u32x4_t x[16];
+// v[0..1] += sum over s < G, in order s = 0, 1, ..., of the element pair at
+// byte offset off + 4 s stride of the resource rs (whose range ends at slice
+// G, so that slices past it read zero and add nothing; off = OUT_OF_RANGE
+// adds zeros throughout).  The loads of SB slices go out unconditionally and
+// together: with SB >= G the partials cost one memory round trip.
+template <int SB>
+__device__ __forceinline__ void add_slices2(__amdgpu_buffer_rsrc_t rs, int G, int stride, uint32_t off, float (&v)[2]) {
+  for (int s0 = 0; s0 < G; s0 += SB) {
+    uint64_t x[SB];
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        x[q] = s0 + q < G ? ld_b128<AUX>(rs, (uint32_t)(((s0 + q) * stride + u) * 4), 0) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int q = 0; q < SB; ++q) x[q] = ld_b64(rs, off + (uint32_t)((s0 + q) * stride * 4));
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (s0 + q < G) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(x[q][e]);
-        }
+    for (int q = 0; q < SB; ++q) {
+      v[0] += __uint_as_float((uint32_t)x[q]);
+      v[1] += __uint_as_float((uint32_t)(x[q] >> 32));
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[u + e] = v[e];
   }
 }
 
+// Sum of the 8 per-wave partials of element u, in a fixed order.
 template <int PM>
 __device__ __forceinline__ float sum_waves(const float (&r)[TWV][PM], int u) {
   static_assert(TWV == 8, "fixed-order sum written for 8 waves");
