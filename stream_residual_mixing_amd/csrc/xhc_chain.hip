@@ -48,6 +48,10 @@ constexpr int WDP = XHC_PRE_WD;   // weight items in flight ahead of the MFMAs (
 #define XHC_CORR_WD 4
 #endif
 constexpr int WDC = XHC_CORR_WD;  // and for the correction kernel (measured best of 2, 4, 8, 16)
+#ifndef XHC_STATE_AUX
+#define XHC_STATE_AUX 0
+#endif
+constexpr int STATE_AUX = XHC_STATE_AUX;   // cache policy of the persistent kernels' state loads (streaming: ~20% slower)
 
 template <int N>
 struct RouteDims {
@@ -669,7 +673,7 @@ __device__ __forceinline__ void load_xtile(XTile<N>& xs, const typename E::T* X,
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (size_t)(rows > 0 ? step : 0) * PTL * TM * N * C,
                                               (uint32_t)((size_t)rows * N * C * sizeof(TT)));
 #pragma unroll
-  for (int i = 0; i < N; ++i) xs.x[i] = ld_b128(rx, lane_off, (uint32_t)(i * C * (int)sizeof(TT)));
+  for (int i = 0; i < N; ++i) xs.x[i] = ld_b128<STATE_AUX>(rx, lane_off, (uint32_t)(i * C * (int)sizeof(TT)));
 }
 
 // Valid rows of a step (full steps, then the ragged one, then none), written
@@ -731,7 +735,7 @@ __device__ __forceinline__ void slice_colsums(const u32x4_t (&s_w)[PSB][N][NTF][
 // for the LDS every time.  The first S0 streams are known to be masked
 // (the fixed streams of the active list) and are skipped.
 #ifndef XHC_ROUTE_BD
-#define XHC_ROUTE_BD 2
+#define XHC_ROUTE_BD 3
 #endif
 template <class E, int N, int NTF, int S0 = 0, int BD = XHC_ROUTE_BD>
 __device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)[N][NTF][WAVE], int lane, uint32_t amask,
@@ -1255,9 +1259,9 @@ struct PostPArgs {
 };
 
 #ifndef XHC_POST_PD
-#define XHC_POST_PD 2
+#define XHC_POST_PD 1
 #endif
-constexpr int POST_PD = XHC_POST_PD;   // steps of state loads in flight ahead of the compute
+constexpr int POST_PD = XHC_POST_PD;   // steps of state loads in flight ahead of the compute (1 measured best of 1, 2, 3)
 
 // Calls f(std::integral_constant<int, Q>) for Q = 0 .. NQ - 1.
 template <int NQ, int Q = 0, class F>
@@ -1377,7 +1381,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
     for (int j = 0; j < K; ++j) {
       int ij = s_idx[islot][tau * K + j];
       ij = ij < 0 ? 0 : (ij >= N ? N - 1 : ij);
-      st.x[j] = ld_b128(rx, (uint32_t)(((size_t)tau * N + ij) * C * sizeof(T)) + cofs, 0);
+      st.x[j] = ld_b128<STATE_AUX>(rx, (uint32_t)(((size_t)tau * N + ij) * C * sizeof(T)) + cofs, 0);
     }
     if constexpr (WR != 0) {
       const int rows = kvalid ? step_rows(step, full, tail) : 0;
@@ -1419,6 +1423,10 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
   PStep<K> sr[NR];
 #pragma unroll
   for (int d = 0; d < PD; ++d) issue(sr[d], team + d * nteams, d);
+  // The first steps' loads complete here, once: otherwise the compiler's
+  // waits at the loop head, which must also hold on entry (where these are
+  // the latest loads), would drain the prefetch in every later trip.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
@@ -1587,15 +1595,17 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
     }
   };
 
-  // steps team + k nteams; ring slots by k
-  for (int k0 = 0;; k0 += NR) {
-    bool done = false;
+  // steps team + k nteams; ring slots by k.  NR steps per trip and the only
+  // exit at its end (a step past the last one loads and stores nothing): an
+  // exit between steps would be merged by the compiler into a path back to
+  // the loop head, whose memory-counter waits would then drain the loads
+  // issued PD steps ahead.
+  if (team >= nsteps) return;
+  for (int k0 = 0; team + k0 * nteams < nsteps; k0 += NR) {
     for_each_c<NR>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
-      if (done) return;
       const int k = k0 + q;
       const int step = team + k * nteams;
-      if (step >= nsteps) { done = true; return; }
       // rows of later steps: the list PD + 1 steps ahead, the coefficients
       // of the next step
       const u32x4_t nv = load_unit(step + (PD + 1) * nteams, true, false);
@@ -1607,7 +1617,6 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
       if constexpr (WR != 0) store_unit(nc, 0, (k + 1) & 1, false, true);
       __syncthreads();
     });
-    if (done) break;
   }
 }
 
