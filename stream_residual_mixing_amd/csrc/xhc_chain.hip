@@ -52,6 +52,17 @@ constexpr int WDC = XHC_CORR_WD;  // and for the correction kernel (measured bes
 #define XHC_STATE_AUX 0
 #endif
 constexpr int STATE_AUX = XHC_STATE_AUX;   // cache policy of the persistent kernels' state loads (streaming: ~20% slower)
+#ifndef XHC_PRE_ONE_PHASE
+#define XHC_PRE_ONE_PHASE 1
+#endif
+#ifndef XHC_ROW_ST_AUX
+#define XHC_ROW_ST_AUX 0
+#endif
+#ifndef XHC_INP_ST_AUX
+#define XHC_INP_ST_AUX 2
+#endif
+constexpr int ROW_ST_AUX = XHC_ROW_ST_AUX;   // cache policy of the rewritten rows' stores (default: measured ~4% faster per post call than streaming, and the next pre pass reads them)
+constexpr int INP_ST_AUX = XHC_INP_ST_AUX;   // and of the sublayer input's (streaming: measured ~1% faster)
 
 template <int N>
 struct RouteDims {
@@ -682,17 +693,19 @@ __device__ __forceinline__ int step_rows(int step, int full, int tail) {
   return step < full ? PTL * TM : (step == full ? tail : 0);
 }
 
-// The slice's packed routing fragments -> LDS (zero for blocks past C).
-template <int N, int NTF>
-__device__ __forceinline__ void load_wslice(u32x4_t (&s_w)[PSB][N][NTF][WAVE], const uint4* wfull, int nkbC, int slice,
-                                            int tid) {
-  constexpr int TOT = PSB * N * NTF * WAVE;
+// The slice's packed routing fragments of streams FS .. N-1 -> LDS (zero for
+// blocks past C).
+template <int N, int NTF, int FS = 0>
+__device__ __forceinline__ void load_wslice(u32x4_t (&s_w)[PSB][N - FS][NTF][WAVE], const uint4* wfull, int nkbC,
+                                            int slice, int tid) {
+  constexpr int NS = N - FS;
+  constexpr int TOT = PSB * NS * NTF * WAVE;
   constexpr int IT = (TOT + PNTHR - 1) / PNTHR;
   u32x4_t v[IT];
 #pragma unroll
   for (int k = 0; k < IT; ++k) {
     const int u = tid + k * PNTHR;
-    const int l = u % WAVE, n = (u / WAVE) % NTF, i = (u / (WAVE * NTF)) % N, c = u / (WAVE * NTF * N);
+    const int l = u % WAVE, n = (u / WAVE) % NTF, i = FS + (u / (WAVE * NTF)) % NS, c = u / (WAVE * NTF * NS);
     const int kb = slice * PSB + c;
     v[k] = u32x4_t{0u, 0u, 0u, 0u};
     if (u < TOT && kb < nkbC)
@@ -727,6 +740,34 @@ __device__ __forceinline__ void slice_colsums(const u32x4_t (&s_w)[PSB][N][NTF][
   __syncthreads();
 }
 
+// The same column sums from the packed weights in global memory (for a
+// kernel that keeps only some streams' fragments in LDS): the same
+// fragments in the same order, so the same bits.
+template <class E, int N, int NTF, int PM>
+__device__ __forceinline__ void slice_colsums_g(const uint4* wfull, int nkbC, int slice, float (&s_red)[TWV][PM],
+                                                float* s_acs, int tid, int wave, int lane) {
+  if (wave < PSB) {
+    const int kb = slice * PSB + wave;
+    const u32x4_t ones = ones_frag<E>();
+    u32x4_t f[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      f[i] = kb < nkbC ? ld16v(wfull + (((size_t)i * nkbC + kb) * NTF) * WAVE + lane) : u32x4_t{0u, 0u, 0u, 0u};
+    f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) acs = E::mma(acs, ones, f[i]);
+    if (lane < 16) s_red[wave][lane] = acs[0];
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float v = 0.f;
+#pragma unroll
+    for (int c = 0; c < PSB; ++c) v += s_red[c][tid];
+    s_acs[tid] = v;
+  }
+  __syncthreads();
+}
+
 // Next-layer routing projection of one tile (rows in amask masked to zero),
 // with the sums of x and x^2, B operands from LDS.  The N x NTF weight
 // fragments are read ROUTE_BD - 1 MFMAs ahead of their use (a ring of
@@ -737,9 +778,11 @@ __device__ __forceinline__ void slice_colsums(const u32x4_t (&s_w)[PSB][N][NTF][
 #ifndef XHC_ROUTE_BD
 #define XHC_ROUTE_BD 3
 #endif
-template <class E, int N, int NTF, int S0 = 0, int BD = XHC_ROUTE_BD>
-__device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)[N][NTF][WAVE], int lane, uint32_t amask,
-                                          f32x4_t (&acc)[NTF], f32x4_t& S1, f32x4_t& S2) {
+template <class E, int N, int NTF, int S0 = 0, int BD = XHC_ROUTE_BD, int NWS = N>
+__device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)[NWS][NTF][WAVE], int lane,
+                                          uint32_t amask, f32x4_t (&acc)[NTF], f32x4_t& S1, f32x4_t& S2) {
+  static_assert(S0 >= N - NWS, "w holds the fragments of streams N - NWS .. N - 1");
+  constexpr int WOFS = N - NWS;   // stream i's fragments sit at w[i - WOFS]
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
   constexpr int TOT = N * NTF, Q0 = S0 * NTF;
@@ -749,7 +792,7 @@ __device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)
   S2 = S1;
   u32x4_t b[BD];
 #pragma unroll
-  for (int q = Q0; q < Q0 + BD - 1 && q < TOT; ++q) b[q % BD] = w[q / NTF][q % NTF][lane];
+  for (int q = Q0; q < Q0 + BD - 1 && q < TOT; ++q) b[q % BD] = w[q / NTF - WOFS][q % NTF][lane];
 #pragma unroll
   for (int i = S0; i < N; ++i) {
     const u32x4_t v = ((amask >> i) & 1u) ? zero : xs.x[i];
@@ -757,24 +800,21 @@ __device__ __forceinline__ void route_mma(const XTile<N>& xs, const u32x4_t (&w)
 #pragma unroll
     for (int n = 0; n < NTF; ++n) {
       const int q = i * NTF + n;
-      if (q + BD - 1 < TOT) b[(q + BD - 1) % BD] = w[(q + BD - 1) / NTF][(q + BD - 1) % NTF][lane];
+      if (q + BD - 1 < TOT) b[(q + BD - 1) % BD] = w[(q + BD - 1) / NTF - WOFS][(q + BD - 1) % NTF][lane];
       acc[n] = E::mma(acc[n], v, b[q % BD]);
       if constexpr (BD > 1) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// Routing partials of the step's PTL tiles: each wave's block to LDS, then
-// per tile the sum over its PSB blocks in order, plus the slice's column sums.
+// Routing partials of the step's PTL tiles from the per-wave blocks in s_red
+// (written before a barrier): per tile the sum over its PSB blocks in order,
+// plus the slice's column sums, stored per (tile, slice).
 template <int N, int PM>
-__device__ __forceinline__ void route_partials(float (&s_red)[TWV][PM], const float* s_acs, const f32x4_t (&acc)[RouteDims<N>::NTF],
-                                               const f32x4_t& S1, const f32x4_t& S2, float* dst, int G, int slice,
-                                               int step, int ntiles, int tid, int wave, int g, int r) {
+__device__ __forceinline__ void route_partials_store(const float (&s_red)[TWV][PM], const float* s_acs, float* dst,
+                                                     int G, int slice, int step, int ntiles, int tid) {
   using D = RouteDims<N>;
-  constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
-  acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
-  sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
-  __syncthreads();
+  constexpr int NSUM = D::NSUM, P1 = D::P1;
   // stores through a resource over the partials: entries past the step or
   // past the last tile go out of its range (no store under a branch)
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst, (uint32_t)((size_t)ntiles * G * P1 * 4));
@@ -792,6 +832,19 @@ __device__ __forceinline__ void route_partials(float (&s_red)[TWV][PM], const fl
     if (v >= NSUM) x = s_acs[v - NSUM >= 0 ? v - NSUM : 0];
     st_b32(x, rd, in && tile < ntiles ? (uint32_t)((((size_t)tile * G + slice) * P1 + v) * 4) : OUT_OF_RANGE);
   }
+}
+
+// The same with the waves' blocks written to s_red first, between barriers.
+template <int N, int PM>
+__device__ __forceinline__ void route_partials(float (&s_red)[TWV][PM], const float* s_acs, const f32x4_t (&acc)[RouteDims<N>::NTF],
+                                               const f32x4_t& S1, const f32x4_t& S2, float* dst, int G, int slice,
+                                               int step, int ntiles, int tid, int wave, int g, int r) {
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NPF = D::NPF;
+  acc_to_lds<NTF, NPF>(s_red, wave, g, r, acc);
+  sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+  __syncthreads();
+  route_partials_store<N>(s_red, s_acs, dst, G, slice, step, ntiles, tid);
   __syncthreads();
 }
 
@@ -1035,8 +1088,18 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
   constexpr int HQ = PTL * TM * N / 4, IQ = PTL * TM * K / 4;
   constexpr int WH = (HQ + WAVE - 1) / WAVE, WI = (IQ + WAVE - 1) / WAVE;
   static_assert((PTL * TM * N) % 4 == 0 && (PTL * TM * K) % 4 == 0 && WH + WI <= TWV, "routing rows of a step");
-  __shared__ u32x4_t s_w[PSB][N][NTF][WAVE];
+  // With m known the fixed streams 0 .. MS-1 are always in the active list,
+  // so the next layer's routing never reads their fragments: LDS keeps
+  // streams FS .. N-1 only, and the room this frees holds the active
+  // partials apart from the routing ones, so that both go through one
+  // barrier phase per step instead of two.
+  constexpr int FS = MS > 0 && MS < N ? MS : 0;
+  constexpr bool ONE_PHASE =
+      XHC_PRE_ONE_PHASE && FS > 0 && (size_t)PSB * (N - FS) * NTF * WAVE * 16 + (size_t)TWV * (PM + P2) * 4 + 16 * 4 +
+                        (size_t)2 * (WH + WI) * WAVE * 16 <= 160 * 1024;
+  __shared__ u32x4_t s_w[PSB][N - FS][NTF][WAVE];
   __shared__ float s_red[TWV][PM];
+  __shared__ float s_red2[ONE_PHASE ? TWV : 1][ONE_PHASE ? P2 : 1];
   __shared__ float s_acs[16];
   __shared__ u32x4_t s_rh[2][WH * WAVE];
   __shared__ u32x4_t s_ri[2][WI * WAVE];
@@ -1099,10 +1162,13 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
   load_wact();
   u32x4_t rt = load_route(p);
   load_xtile<E, N>(xa, X, C, p, step_rows(p, full, tail), lane_off);
-  load_wslice<N, NTF>(s_w, a.wnext, nkbC, slice, tid);
+  load_wslice<N, NTF, FS>(s_w, a.wnext, nkbC, slice, tid);
   store_route(0, rt);
   __syncthreads();
-  slice_colsums<E, N, NTF>(s_w, s_red, s_acs, tid, wave, lane);
+  if constexpr (FS > 0)
+    slice_colsums_g<E, N, NTF>(a.wnext, nkbC, slice, s_red, s_acs, tid, wave, lane);
+  else
+    slice_colsums<E, N, NTF>(s_w, s_red, s_acs, tid, wave, lane);
 
   auto compute = [&](const XTile<N>& xs, int step, int buf, const u32x4_t& rnext) {
     const int tile = PTL * step + b;
@@ -1135,7 +1201,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
       const int rows = kvalid ? step_rows(step, full, tail) : 0;
       const __amdgpu_buffer_rsrc_t ri = make_rsrc(reinterpret_cast<T*>(a.inp) + (size_t)(rows > 0 ? step : 0) * PTL * TM * C,
                                                   (uint32_t)((size_t)rows * C * sizeof(T)));
-      st_b128<CP_NT>(E::packv_cvt(o), ri, (uint32_t)(((size_t)(TM * b + r) * C + kb0 * KB + VEC * g) * sizeof(T)));
+      st_b128<INP_ST_AUX>(E::packv_cvt(o), ri, (uint32_t)(((size_t)(TM * b + r) * C + kb0 * KB + VEC * g) * sizeof(T)));
       (void)tok;
       (void)tile;
     }
@@ -1172,11 +1238,27 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
     }
     // next layer's routing over the rows this layer leaves as they are
     f32x4_t acc[NTF], S1, S2;
-    route_mma<E, N, NTF, (MS > 0 ? MS : 0)>(xs, s_w[cb], lane, amask, acc, S1, S2);
-    route_partials<N>(s_red, s_acs, acc, S1, S2, a.look, G, slice, step, a.ntiles, tid, wave, g, r);
-    acc_to_lds<NTA, NPA>(s_red, wave, g, r, acc2);
-    if ((r >> 2) == g) s_red[wave][TM * NPA + r] = diag_of(SS, r);
-    __syncthreads();
+    route_mma<E, N, NTF, FS, XHC_ROUTE_BD, N - FS>(xs, s_w[cb], lane, amask, acc, S1, S2);
+    // the active partials' per-wave blocks: in their own LDS rows (one
+    // phase), or in s_red after the routing partials are done (two phases)
+    auto act_to_lds = [&](auto& dst) __attribute__((always_inline)) {
+      acc_to_lds<NTA, NPA>(dst, wave, g, r, acc2);
+      if ((r >> 2) == g) dst[wave][TM * NPA + r] = diag_of(SS, r);
+    };
+    if constexpr (ONE_PHASE) {
+      acc_to_lds<NTF, D::NPF>(s_red, wave, g, r, acc);
+      sums_to_lds(&s_red[wave][TM * D::NPF], g, r, S1, S2);
+      act_to_lds(s_red2);
+      __syncthreads();
+      route_partials_store<N>(s_red, s_acs, a.look, G, slice, step, a.ntiles, tid);
+    } else {
+      route_partials<N>(s_red, s_acs, acc, S1, S2, a.look, G, slice, step, a.ntiles, tid, wave, g, r);
+      act_to_lds(s_red);
+      __syncthreads();
+    }
+    const auto& sr2 = [&]() -> const auto& {
+      if constexpr (ONE_PHASE) return s_red2; else return s_red;
+    }();
     constexpr int IT = (PTL * P2 + PNTHR - 1) / PNTHR;
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
@@ -1187,7 +1269,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
       const int t16 = PTL * step + bb;
       float x = 0.f;
 #pragma unroll
-      for (int c = 0; c < PSB; ++c) x += s_red[bb * PSB + c][v];
+      for (int c = 0; c < PSB; ++c) x += sr2[bb * PSB + c][v];
       st_b32(x, rp2, in && t16 < a.ntiles ? (uint32_t)((((size_t)t16 * G + slice) * P2 + v) * 4) : OUT_OF_RANGE);
     }
     // the next step's routing to the other buffer, last: its load was issued
@@ -1504,7 +1586,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
           nv[e] = sum;
         }
         xn[j] = E::packv_cvt(nv);
-        st_b128<CP_NT>(xn[j], rx, (uint32_t)(((size_t)tau * N + I[j]) * C * sizeof(T)) + cofs);
+        st_b128<ROW_ST_AUX>(xn[j], rx, (uint32_t)(((size_t)tau * N + I[j]) * C * sizeof(T)) + cofs);
       }
     } else {
 #pragma unroll
