@@ -1298,6 +1298,287 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 }
 
 // ---------------------------------------------------------------------------
+// Chained pre pass with the state staged through LDS (bf16, m known, C a
+// multiple of the 128-channel slice).
+//
+// A workgroup of SSB = 4 waves owns one slice of 4 contraction blocks for the
+// launch and walks 16-token tiles, one wave per block.  The tile's rows of
+// the slice (16 tokens x N streams x 256 B) go from HBM straight into LDS by
+// buffer-to-LDS loads, each covering 4 token rows x 256 B: a quarter of the
+// address translations per byte of a load in the MFMA fragment layout
+// (16 rows x 64 B), which is what holds the register-staged kernel back.
+// The loads of the next tile go into the other half of a two-tile ring
+// while this one computes.  Lane l of a load takes 16-byte chunk
+// (l mod 16) xor (token within the tile) of its row, and lands at slot l of
+// the load's 1 KiB, so a fragment read (one chunk of 16 tokens) touches 16
+// different bank groups.  The next layer's routing fragments of the wave's
+// block and this layer's active weights stay in registers for the launch;
+// the active rows are read from LDS at the token's own streams.
+// ---------------------------------------------------------------------------
+#ifndef XHC_PRE_STAGED
+#define XHC_PRE_STAGED 1
+#endif
+constexpr int SSB = 4;                   // contraction blocks per slice, one wave each
+constexpr int SNTHR = SSB * WAVE;        // 256 threads
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Valid tokens of 16-token tile `tile` (full tiles, the ragged one, then none).
+__device__ __forceinline__ int tile_rows(int tile, int full, int tail) {
+  return tile < full ? TM : (tile == full ? tail : 0);
+}
+
+template <class E, int N, int K, int KR, int MS>
+__global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArgs a) {
+  static_assert(std::is_same<E, Bf16>::value, "the staged pre pass is written for bf16 state");
+  static_assert(MS > 0 && MS <= K && MS < N, "the fixed streams are known");
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  using A = ActDims<K, KR>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  constexpr int NTA = A::NTA, NPA = A::NPA, P2 = A::P2;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  constexpr int FS = MS;                       // streams whose routing fragments are read
+  constexpr int ROWB = SSB * KB * 2;           // bytes of a row in the slice (256)
+  constexpr int NQ = TM / 4;                   // token quads per tile
+  constexpr int LPW = N * NQ / SSB;            // buffer-to-LDS loads per wave per tile
+  static_assert(ROWB == 16 * 16 && (N * NQ) % SSB == 0, "a load covers 4 rows x 16 chunks");
+  static_assert(TM * N / 4 <= WAVE && TM * K / 4 <= WAVE, "a tile's routing rows fit one wave each");
+  __shared__ u32x4_t s_x[2][N][NQ][WAVE];      // ring of two tiles: [slot][stream][token quad][16-byte slot]
+  __shared__ float s_red[SSB][NSUM];
+  __shared__ float s_red2[SSB][P2];
+  __shared__ float s_acs[16];
+  __shared__ float s_rh[2][TM * N];
+  __shared__ int s_ri[2][TM * K];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int ntiles = a.ntiles;
+  const int kb0 = slice * SSB + wave;          // this wave's contraction block
+  const T* X = reinterpret_cast<const T*>(a.X);
+  const int full = a.T / TM, tail = a.T % TM;
+  const uint32_t rowstride = (uint32_t)((size_t)N * C * sizeof(T));   // bytes between a token's rows
+
+  // ---- loads of a tile into ring slot q -------------------------------------
+  // Load u of this wave: stream i = (wave LPW + u) / NQ, quad b = ... mod NQ.
+  // Lane l: row (token 4b + (l >> 4)), chunk (l & 15) xor token.
+  const int lrow = lane >> 4, lslot = lane & 15;
+  auto dma = [&](int tile, int q) __attribute__((always_inline)) {
+    const int rows = tile_rows(tile, full, tail);
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(X + (size_t)(rows > 0 ? tile : 0) * TM * N * C, (uint32_t)((size_t)rows * rowstride));
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int v = wave * LPW + u, i = v / NQ, bq = v % NQ;
+      const int tok = 4 * bq + lrow;
+      const uint32_t voff = (uint32_t)tok * rowstride + (uint32_t)(slice * ROWB + ((lslot ^ tok) << 4));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)&s_x[q][i][bq][0], 16, (int)voff,
+                                               (int)((uint32_t)i * C * sizeof(T)), 0, 0);
+    }
+  };
+  // a tile's routing rows: wave 0 the h_pre rows, wave 1 the active lists
+  // (units past the valid tokens read zero; other waves read nothing)
+  auto load_route = [&](int tile) __attribute__((always_inline)) {
+    const int rows = tile_rows(tile, full, tail);
+    const size_t t0 = rows > 0 ? (size_t)TM * tile : 0;
+    const bool wh = wave == 0;
+    const void* base = wh ? (const void*)(a.h_pre + t0 * N) : (const void*)(a.idx + t0 * K);
+    const uint32_t bytes = wh ? (uint32_t)(rows * N * 4) : (wave == 1 ? (uint32_t)(rows * K * 4) : 0u);
+    return ld_b128(make_rsrc(base, bytes), (uint32_t)(lane * 16), 0);
+  };
+  auto store_route = [&](int q, const u32x4_t& v) __attribute__((always_inline)) {
+    if (wave == 0) reinterpret_cast<u32x4_t*>(&s_rh[q][0])[lane] = v;
+    else if (wave == 1 && lane < TM * K / 4) reinterpret_cast<u32x4_t*>(&s_ri[q][0])[lane] = v;
+  };
+
+  // ---- weights in registers -------------------------------------------------
+  // (through resources, unconditionally: a block past C reads zeros)
+  const bool kvalid = kb0 < nkbC;
+  const __amdgpu_buffer_rsrc_t rwn = make_rsrc(a.wnext, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
+  const __amdgpu_buffer_rsrc_t rwa = make_rsrc(a.wact, (uint32_t)((size_t)K * nkbC * NTA * WAVE * 16));
+  const uint32_t lo = kvalid ? (uint32_t)lane * 16 : OUT_OF_RANGE;
+  u32x4_t wn[N - FS][NTF];   // next layer's routing fragments of this block, streams FS .. N-1
+#pragma unroll
+  for (int i = FS; i < N; ++i)
+#pragma unroll
+    for (int n = 0; n < NTF; ++n)
+      wn[i - FS][n] = ld_b128(rwn, lo, (uint32_t)((((size_t)i * nkbC + kb0) * NTF + n) * WAVE * 16));
+  u32x4_t wa[K][NTA];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int n = 0; n < NTA; ++n)
+      wa[j][n] = ld_b128(rwa, lo, (uint32_t)((((size_t)j * nkbC + kb0) * NTA + n) * WAVE * 16));
+  // column sums of the slice's W_r over all N streams (the same fragments in
+  // the same order as the register-staged kernels)
+  {
+    const u32x4_t ones = ones_frag<E>();
+    u32x4_t f[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = ld_b128(rwn, lo, (uint32_t)((((size_t)i * nkbC + kb0) * NTF) * WAVE * 16));
+    f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) acs = E::mma(acs, ones, f[i]);
+    if (lane < 16) s_red[wave][lane] = acs[0];
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float v = 0.f;
+#pragma unroll
+    for (int c = 0; c < SSB; ++c) v += s_red[c][tid];
+    s_acs[tid] = v;
+  }
+
+  int p = team;
+  if (p >= ntiles) return;
+  dma(p, 0);
+  {
+    const u32x4_t rt = load_route(p);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile and its routing rows
+    store_route(0, rt);
+  }
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t rlook = make_rsrc(a.look, (uint32_t)((size_t)ntiles * G * P1 * 4));
+  const __amdgpu_buffer_rsrc_t rp2 = make_rsrc(a.part2, (uint32_t)((size_t)ntiles * G * P2 * 4));
+  // byte offset of this lane's fragment (token r, chunk 4 wave + g) within a
+  // stream's [quad][slot] block of the ring
+  const uint32_t fofs = (uint32_t)(((r >> 2) * WAVE + 16 * (r & 3) + ((4 * wave + g) ^ r)) * 16);
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  const u32x4_t ones = ones_frag<E>();
+
+  // The partial sums of the previous tile (its waves' blocks in s_red and
+  // s_red2), stored per (tile, slice); a tile past the last stores nothing.
+  constexpr int IT1 = (P1 + SNTHR - 1) / SNTHR, IT2 = (P2 + SNTHR - 1) / SNTHR;
+  auto store_partials = [&](int tile) __attribute__((always_inline)) {
+    const bool tin = tile >= 0 && tile < ntiles;
+#pragma unroll
+    for (int it = 0; it < IT1; ++it) {
+      const int u0 = tid + it * SNTHR;
+      const bool in = u0 < P1;
+      const int u = in ? u0 : 0;
+      float x = 0.f;
+#pragma unroll
+      for (int c = 0; c < SSB; ++c) x += s_red[c][u < NSUM ? u : 0];
+      if (u >= NSUM) x = s_acs[u - NSUM >= 0 ? u - NSUM : 0];
+      st_b32(x, rlook, in && tin ? (uint32_t)((((size_t)tile * G + slice) * P1 + u) * 4) : OUT_OF_RANGE);
+    }
+#pragma unroll
+    for (int it = 0; it < IT2; ++it) {
+      const int u0 = tid + it * SNTHR;
+      const bool in = u0 < P2;
+      const int u = in ? u0 : 0;
+      float x = 0.f;
+#pragma unroll
+      for (int c = 0; c < SSB; ++c) x += s_red2[c][u];
+      st_b32(x, rp2, in && tin ? (uint32_t)((((size_t)tile * G + slice) * P2 + u) * 4) : OUT_OF_RANGE);
+    }
+  };
+
+  // One tile, in ring slot Q (a constant, so that the compiler can tell
+  // accesses to the two slots apart).  Every LDS read of the step comes
+  // before the next tile's loads into the other slot are issued: after a
+  // buffer-to-LDS load the compiler makes any later LDS read it cannot
+  // separate from that load's target wait for it.
+  int pprev = -1;
+  auto tile_step = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    const int p1 = p + nteams;
+    const char* xq = reinterpret_cast<const char*>(&s_x[q][0][0][0]);
+    constexpr uint32_t SBYTES = NQ * WAVE * 16;   // bytes of one stream's tile rows in the ring
+    // ---- reads: routing rows, the tile's fragments, the active rows
+    int I[K];
+    uint32_t amask = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int v = s_ri[q][r * K + j];
+      v = v < 0 ? 0 : (v >= N ? N - 1 : v);
+      I[j] = v;
+      amask |= 1u << v;
+    }
+    float hp[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) hp[i] = s_rh[q][r * N + i];
+    u32x4_t x[N], gat[K];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const u32x4_t*>(xq + (uint32_t)i * SBYTES + fofs);
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      gat[j] = j < MS ? x[j < MS ? j : 0] : *reinterpret_cast<const u32x4_t*>(xq + (uint32_t)I[j] * SBYTES + fofs);
+    // ---- the previous tile's partial sums, then every wave is past its reads
+    store_partials(pprev);
+    __syncthreads();
+    // ---- the next tile's loads (past the last tile they read nothing)
+    dma(p1, q ^ 1);
+    const u32x4_t rnext = load_route(p1);
+    // ---- compute from registers
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+    f32x4_t acc[NTF], S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      // the dense read, and the next layer's routing projection of the rows
+      // this layer leaves as they are
+      float f[VEC];
+      E::unpack(x[i], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = fmaf(hp[i], f[e], o[e]);
+      if (i >= FS) {
+        const u32x4_t v = ((amask >> i) & 1u) ? zero : x[i];
+        mma_sums<E>(v, ones, S1, S2);
+#pragma unroll
+        for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, wn[i - FS][n]);
+      }
+    }
+    {
+      const int rows = kvalid ? tile_rows(p, full, tail) : 0;
+      const __amdgpu_buffer_rsrc_t ri =
+          make_rsrc(reinterpret_cast<T*>(a.inp) + (size_t)(rows > 0 ? p : 0) * TM * C, (uint32_t)((size_t)rows * C * sizeof(T)));
+      st_b128<INP_ST_AUX>(E::packv_cvt(o), ri, (uint32_t)(((size_t)r * C + kb0 * KB + VEC * g) * sizeof(T)));
+    }
+    // the k active rows: sum of squares and this layer's active projection
+    f32x4_t acc2[NTA], SS = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NTA; ++n) acc2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      SS = E::mma(SS, gat[j], gat[j]);
+#pragma unroll
+      for (int n = 0; n < NTA; ++n) acc2[n] = E::mma(acc2[n], gat[j], wa[j][n]);
+    }
+    // ---- this tile's per-wave partials and the next tile's routing rows to
+    // LDS; then this wave's loads are complete, and after the barrier every
+    // wave's are
+#pragma unroll
+    for (int n = 0; n < NTF; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_red[wave][(4 * g + i) * NPF + n * 16 + r] = acc[n][i];
+    sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+#pragma unroll
+    for (int n = 0; n < NTA; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_red2[wave][(4 * g + i) * NPA + n * 16 + r] = acc2[n][i];
+    if ((r >> 2) == g) s_red2[wave][TM * NPA + r] = diag_of(SS, r);
+    store_route(q ^ 1, rnext);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    pprev = p;
+    p = p1;
+  };
+  // two tiles per trip and the only exit at its end (a tile past the last
+  // loads and stores nothing)
+  do {
+    tile_step(std::integral_constant<int, 0>{});
+    tile_step(std::integral_constant<int, 1>{});
+  } while (p < ntiles);
+  store_partials(pprev);
+}
+
+// ---------------------------------------------------------------------------
 // Persistent post pass of a layer with a next layer: the rewritten rows'
 // share of the next layer's routing (the correction), and with it the
 // layer's write (WR = 1 attention-type, 4 MLP-type), so the new rows are
@@ -1718,6 +1999,19 @@ constexpr int CORR_RB = XHC_CORR_RB;   // 16-token row blocks per correction wor
 
 // Workgroups of a persistent launch: one per compute unit (their LDS allows
 // no more), Gp slices per team, no more teams than steps.
+// The same for the staged pre pass: one 16-token tile per step.
+int persist_grid_s(const Plan& P) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  long teams = v / P.Gp;
+  if (teams < 1) teams = 1;
+  if (teams > P.ntiles) teams = P.ntiles;
+  if (teams < 1) teams = 1;
+  return (int)(teams * P.Gp);
+}
+
 int persist_grid(const Plan& P) {
   static int ncu[64] = {0};
   int dev = 0;
@@ -1752,6 +2046,12 @@ void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, con
     // persistent: routing weights of the next layer resident in LDS
     a.G = P.Gp;
     Gpart = P.Gp;
+    if constexpr (XHC_PRE_STAGED && std::is_same<E, Bf16>::value && N == 16 && K > 2) {
+      if (P.m == 2 && P.C % (SSB * Bf16::KB) == 0) {
+        xhc_pre_chained_s_kernel<E, N, K, KR, 2><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+        goto fin;
+      }
+    }
     if (P.m == 2 && K > 2)
       xhc_pre_chained_p_kernel<E, N, K, KR, 2><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
     else
@@ -1762,6 +2062,7 @@ void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, con
     xhc_pre_chained_kernel<E, N, K, KR, false, RB><<<grid, NTHR, 0, st>>>(a);
   }
 
+fin:
   ActFinArgs f;
   f.T = (int)P.T; f.C = P.C; f.G = Gpart; f.ntiles = (int)P.ntiles;
   f.part2 = a.part2;
