@@ -1327,6 +1327,35 @@ __device__ __forceinline__ int tile_rows(int tile, int full, int tail) {
   return tile < full ? TM : (tile == full ? tail : 0);
 }
 
+// A tile's rows of the slice (bf16: 16 tokens x N streams x 256 B) from HBM
+// into one ring slot, by the SSB waves of the workgroup: load u of a wave
+// covers stream i, token quad b (4 rows x 256 B); lane l takes chunk
+// (l mod 16) xor token of row (token 4 b + l / 16) and lands at slot l.
+// Past the valid tokens the loads read zero.
+template <int N>
+__device__ __forceinline__ void stage_tile(u32x4_t (&sx)[N][TM / 4][WAVE], const uint16_t* X, int tile, int full,
+                                           int tail, int C, int slice, int wave, int lane) {
+  constexpr int NQ = TM / 4, LPW = N * NQ / SSB;
+  static_assert((N * NQ) % SSB == 0, "the loads of a tile split evenly over the waves");
+  const uint32_t rowstride = (uint32_t)((size_t)N * C * 2);
+  const int rows = tile_rows(tile, full, tail);
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(X + (size_t)(rows > 0 ? tile : 0) * TM * N * C, (uint32_t)((size_t)rows * rowstride));
+  const int lrow = lane >> 4, lslot = lane & 15;
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int v = wave * LPW + u, i = v / NQ, bq = v % NQ;
+    const int tok = 4 * bq + lrow;
+    const uint32_t voff = (uint32_t)tok * rowstride + (uint32_t)(slice * 256 + ((lslot ^ tok) << 4));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)&sx[i][bq][0], 16, (int)voff, (int)((uint32_t)i * C * 2), 0, 0);
+  }
+}
+// Byte offset, within a stream's rows of a ring slot, of lane (g, r)'s
+// fragment of block `wave` of the slice (token r, chunk 4 wave + g).
+__device__ __forceinline__ uint32_t staged_frag(int wave, int g, int r) {
+  return (uint32_t)(((r >> 2) * WAVE + 16 * (r & 3) + ((4 * wave + g) ^ r)) * 16);
+}
+
 template <class E, int N, int K, int KR, int MS>
 __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArgs a) {
   static_assert(std::is_same<E, Bf16>::value, "the staged pre pass is written for bf16 state");
@@ -1338,10 +1367,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   constexpr int NTA = A::NTA, NPA = A::NPA, P2 = A::P2;
   constexpr int KB = E::KB, VEC = E::VEC;
   constexpr int FS = MS;                       // streams whose routing fragments are read
-  constexpr int ROWB = SSB * KB * 2;           // bytes of a row in the slice (256)
   constexpr int NQ = TM / 4;                   // token quads per tile
-  constexpr int LPW = N * NQ / SSB;            // buffer-to-LDS loads per wave per tile
-  static_assert(ROWB == 16 * 16 && (N * NQ) % SSB == 0, "a load covers 4 rows x 16 chunks");
+  static_assert(SSB * KB * 2 == 256, "a load covers 4 rows x 256 B");
   static_assert(TM * N / 4 <= WAVE && TM * K / 4 <= WAVE, "a tile's routing rows fit one wave each");
   __shared__ u32x4_t s_x[2][N][NQ][WAVE];      // ring of two tiles: [slot][stream][token quad][16-byte slot]
   __shared__ float s_red[SSB][NSUM];
@@ -1356,26 +1383,10 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
   const int ntiles = a.ntiles;
   const int kb0 = slice * SSB + wave;          // this wave's contraction block
-  const T* X = reinterpret_cast<const T*>(a.X);
   const int full = a.T / TM, tail = a.T % TM;
-  const uint32_t rowstride = (uint32_t)((size_t)N * C * sizeof(T));   // bytes between a token's rows
 
-  // ---- loads of a tile into ring slot q -------------------------------------
-  // Load u of this wave: stream i = (wave LPW + u) / NQ, quad b = ... mod NQ.
-  // Lane l: row (token 4b + (l >> 4)), chunk (l & 15) xor token.
-  const int lrow = lane >> 4, lslot = lane & 15;
   auto dma = [&](int tile, int q) __attribute__((always_inline)) {
-    const int rows = tile_rows(tile, full, tail);
-    const __amdgpu_buffer_rsrc_t rx =
-        make_rsrc(X + (size_t)(rows > 0 ? tile : 0) * TM * N * C, (uint32_t)((size_t)rows * rowstride));
-#pragma unroll
-    for (int u = 0; u < LPW; ++u) {
-      const int v = wave * LPW + u, i = v / NQ, bq = v % NQ;
-      const int tok = 4 * bq + lrow;
-      const uint32_t voff = (uint32_t)tok * rowstride + (uint32_t)(slice * ROWB + ((lslot ^ tok) << 4));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)&s_x[q][i][bq][0], 16, (int)voff,
-                                               (int)((uint32_t)i * C * sizeof(T)), 0, 0);
-    }
+    stage_tile<N>(s_x[q], reinterpret_cast<const uint16_t*>(a.X), tile, full, tail, C, slice, wave, lane);
   };
   // a tile's routing rows: wave 0 the h_pre rows, wave 1 the active lists
   // (units past the valid tokens read zero; other waves read nothing)
@@ -1444,7 +1455,7 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   const __amdgpu_buffer_rsrc_t rp2 = make_rsrc(a.part2, (uint32_t)((size_t)ntiles * G * P2 * 4));
   // byte offset of this lane's fragment (token r, chunk 4 wave + g) within a
   // stream's [quad][slot] block of the ring
-  const uint32_t fofs = (uint32_t)(((r >> 2) * WAVE + 16 * (r & 3) + ((4 * wave + g) ^ r)) * 16);
+  const uint32_t fofs = staged_frag(wave, g, r);
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
 
@@ -1571,6 +1582,116 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   };
   // two tiles per trip and the only exit at its end (a tile past the last
   // loads and stores nothing)
+  do {
+    tile_step(std::integral_constant<int, 0>{});
+    tile_step(std::integral_constant<int, 1>{});
+  } while (p < ntiles);
+  store_partials(pprev);
+}
+
+// Routing projection of a whole state (first layer of a chain), with the
+// state staged through LDS as in the pre pass above: every stream's rows,
+// no masking, the routing partials alone.
+template <class E, int N>
+__global__ __launch_bounds__(SNTHR, 1) void xhc_proj_s_kernel(ProjPArgs a) {
+  static_assert(std::is_same<E, Bf16>::value, "the staged projection is written for bf16 state");
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  constexpr int KB = E::KB;
+  constexpr int NQ = TM / 4;
+  static_assert(SSB * KB * 2 == 256, "a load covers 4 rows x 256 B");
+  __shared__ u32x4_t s_x[2][N][NQ][WAVE];
+  __shared__ float s_red[SSB][NSUM];
+  __shared__ float s_acs[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int ntiles = a.ntiles;
+  const int kb0 = slice * SSB + wave;
+  const int full = a.T / TM, tail = a.T % TM;
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X);
+
+  // the routing fragments of this block, every stream, in registers; the
+  // slice's column sums of W_r (the same fragments in the same order as the
+  // register-staged kernels)
+  const bool kvalid = kb0 < nkbC;
+  const __amdgpu_buffer_rsrc_t rwn = make_rsrc(a.wfull, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
+  const uint32_t lo = kvalid ? (uint32_t)lane * 16 : OUT_OF_RANGE;
+  u32x4_t wn[N][NTF];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) wn[i][n] = ld_b128(rwn, lo, (uint32_t)((((size_t)i * nkbC + kb0) * NTF + n) * WAVE * 16));
+  const u32x4_t ones = ones_frag<E>();
+  {
+    f32x4_t acs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) acs = E::mma(acs, ones, wn[i][0]);
+    if (lane < 16) s_red[wave][lane] = acs[0];
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float v = 0.f;
+#pragma unroll
+    for (int c = 0; c < SSB; ++c) v += s_red[c][tid];
+    s_acs[tid] = v;
+  }
+  int p = team;
+  if (p >= ntiles) return;
+  stage_tile<N>(s_x[0], X, p, full, tail, C, slice, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.part, (uint32_t)((size_t)ntiles * G * P1 * 4));
+  const uint32_t fofs = staged_frag(wave, g, r);
+  constexpr int IT1 = (P1 + SNTHR - 1) / SNTHR;
+  auto store_partials = [&](int tile) __attribute__((always_inline)) {
+    const bool tin = tile >= 0 && tile < ntiles;
+#pragma unroll
+    for (int it = 0; it < IT1; ++it) {
+      const int u0 = tid + it * SNTHR;
+      const bool in = u0 < P1;
+      const int u = in ? u0 : 0;
+      float x = 0.f;
+#pragma unroll
+      for (int c = 0; c < SSB; ++c) x += s_red[c][u < NSUM ? u : 0];
+      if (u >= NSUM) x = s_acs[u - NSUM >= 0 ? u - NSUM : 0];
+      st_b32(x, rpart, in && tin ? (uint32_t)((((size_t)tile * G + slice) * P1 + u) * 4) : OUT_OF_RANGE);
+    }
+  };
+  int pprev = -1;
+  auto tile_step = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    const int p1 = p + nteams;
+    const char* xq = reinterpret_cast<const char*>(&s_x[q][0][0][0]);
+    constexpr uint32_t SBYTES = NQ * WAVE * 16;
+    u32x4_t x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const u32x4_t*>(xq + (uint32_t)i * SBYTES + fofs);
+    store_partials(pprev);
+    __syncthreads();
+    stage_tile<N>(s_x[q ^ 1], X, p1, full, tail, C, slice, wave, lane);
+    f32x4_t acc[NTF], S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
+#pragma unroll
+    for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      mma_sums<E>(x[i], ones, S1, S2);
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], x[i], wn[i][n]);
+    }
+#pragma unroll
+    for (int n = 0; n < NTF; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_red[wave][(4 * g + i) * NPF + n * 16 + r] = acc[n][i];
+    sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    pprev = p;
+    p = p1;
+  };
   do {
     tile_step(std::integral_constant<int, 0>{});
     tile_step(std::integral_constant<int, 1>{});
@@ -2096,6 +2217,13 @@ void route_launch(const Plan& P, const xhc_weights* w, const void* X, char* ws, 
   a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
   a.wfull = reinterpret_cast<const uint4*>(ws + P.o_wfull);
   a.part = reinterpret_cast<float*>(ws + P.o_part);
+  if constexpr (XHC_PRE_STAGED && std::is_same<E, Bf16>::value && N == 16) {
+    if (P.C % (SSB * Bf16::KB) == 0) {
+      xhc_proj_s_kernel<E, N><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+      route_fin_launch<N, K>(P, w, ws, false, 0, st);
+      return;
+    }
+  }
   xhc_proj_p_kernel<E, N><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
   route_fin_launch<N, K>(P, w, ws, false, 0, st);
 }
