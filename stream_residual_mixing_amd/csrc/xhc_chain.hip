@@ -1356,7 +1356,7 @@ __device__ __forceinline__ uint32_t staged_frag(int wave, int g, int r) {
   return (uint32_t)(((r >> 2) * WAVE + 16 * (r & 3) + ((4 * wave + g) ^ r)) * 16);
 }
 
-template <class E, int N, int K, int KR, int MS>
+template <class E, int N, int K, int KR, int MS, bool LOOK = true>
 __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArgs a) {
   static_assert(std::is_same<E, Bf16>::value, "the staged pre pass is written for bf16 state");
   static_assert(MS > 0 && MS <= K && MS < N, "the fixed streams are known");
@@ -1406,15 +1406,17 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   // ---- weights in registers -------------------------------------------------
   // (through resources, unconditionally: a block past C reads zeros)
   const bool kvalid = kb0 < nkbC;
-  const __amdgpu_buffer_rsrc_t rwn = make_rsrc(a.wnext, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
+  const __amdgpu_buffer_rsrc_t rwn = make_rsrc(LOOK ? a.wnext : a.wact, LOOK ? (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16) : 0u);
   const __amdgpu_buffer_rsrc_t rwa = make_rsrc(a.wact, (uint32_t)((size_t)K * nkbC * NTA * WAVE * 16));
   const uint32_t lo = kvalid ? (uint32_t)lane * 16 : OUT_OF_RANGE;
-  u32x4_t wn[N - FS][NTF];   // next layer's routing fragments of this block, streams FS .. N-1
+  u32x4_t wn[LOOK ? N - FS : 1][NTF];   // next layer's routing fragments of this block, streams FS .. N-1
+  if constexpr (LOOK) {
 #pragma unroll
-  for (int i = FS; i < N; ++i)
+    for (int i = FS; i < N; ++i)
 #pragma unroll
-    for (int n = 0; n < NTF; ++n)
-      wn[i - FS][n] = ld_b128(rwn, lo, (uint32_t)((((size_t)i * nkbC + kb0) * NTF + n) * WAVE * 16));
+      for (int n = 0; n < NTF; ++n)
+        wn[i - FS][n] = ld_b128(rwn, lo, (uint32_t)((((size_t)i * nkbC + kb0) * NTF + n) * WAVE * 16));
+  }
   u32x4_t wa[K][NTA];
 #pragma unroll
   for (int j = 0; j < K; ++j)
@@ -1423,7 +1425,7 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
       wa[j][n] = ld_b128(rwa, lo, (uint32_t)((((size_t)j * nkbC + kb0) * NTA + n) * WAVE * 16));
   // column sums of the slice's W_r over all N streams (the same fragments in
   // the same order as the register-staged kernels)
-  {
+  if constexpr (LOOK) {
     const u32x4_t ones = ones_frag<E>();
     u32x4_t f[N];
 #pragma unroll
@@ -1451,7 +1453,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   }
   __syncthreads();
 
-  const __amdgpu_buffer_rsrc_t rlook = make_rsrc(a.look, (uint32_t)((size_t)ntiles * G * P1 * 4));
+  const __amdgpu_buffer_rsrc_t rlook =
+      make_rsrc(LOOK ? a.look : a.part2, LOOK ? (uint32_t)((size_t)ntiles * G * P1 * 4) : 0u);
   const __amdgpu_buffer_rsrc_t rp2 = make_rsrc(a.part2, (uint32_t)((size_t)ntiles * G * P2 * 4));
   // byte offset of this lane's fragment (token r, chunk 4 wave + g) within a
   // stream's [quad][slot] block of the ring
@@ -1464,16 +1467,18 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   constexpr int IT1 = (P1 + SNTHR - 1) / SNTHR, IT2 = (P2 + SNTHR - 1) / SNTHR;
   auto store_partials = [&](int tile) __attribute__((always_inline)) {
     const bool tin = tile >= 0 && tile < ntiles;
+    if constexpr (LOOK) {
 #pragma unroll
-    for (int it = 0; it < IT1; ++it) {
-      const int u0 = tid + it * SNTHR;
-      const bool in = u0 < P1;
-      const int u = in ? u0 : 0;
-      float x = 0.f;
+      for (int it = 0; it < IT1; ++it) {
+        const int u0 = tid + it * SNTHR;
+        const bool in = u0 < P1;
+        const int u = in ? u0 : 0;
+        float x = 0.f;
 #pragma unroll
-      for (int c = 0; c < SSB; ++c) x += s_red[c][u < NSUM ? u : 0];
-      if (u >= NSUM) x = s_acs[u - NSUM >= 0 ? u - NSUM : 0];
-      st_b32(x, rlook, in && tin ? (uint32_t)((((size_t)tile * G + slice) * P1 + u) * 4) : OUT_OF_RANGE);
+        for (int c = 0; c < SSB; ++c) x += s_red[c][u < NSUM ? u : 0];
+        if (u >= NSUM) x = s_acs[u - NSUM >= 0 ? u - NSUM : 0];
+        st_b32(x, rlook, in && tin ? (uint32_t)((((size_t)tile * G + slice) * P1 + u) * 4) : OUT_OF_RANGE);
+      }
     }
 #pragma unroll
     for (int it = 0; it < IT2; ++it) {
@@ -1538,7 +1543,7 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
       E::unpack(x[i], f);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[e] = fmaf(hp[i], f[e], o[e]);
-      if (i >= FS) {
+      if (LOOK && i >= FS) {
         const u32x4_t v = ((amask >> i) & 1u) ? zero : x[i];
         mma_sums<E>(v, ones, S1, S2);
 #pragma unroll
@@ -1564,11 +1569,13 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
     // ---- this tile's per-wave partials and the next tile's routing rows to
     // LDS; then this wave's loads are complete, and after the barrier every
     // wave's are
+    if constexpr (LOOK) {
 #pragma unroll
-    for (int n = 0; n < NTF; ++n)
+      for (int n = 0; n < NTF; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_red[wave][(4 * g + i) * NPF + n * 16 + r] = acc[n][i];
-    sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+        for (int i = 0; i < 4; ++i) s_red[wave][(4 * g + i) * NPF + n * 16 + r] = acc[n][i];
+      sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
+    }
 #pragma unroll
     for (int n = 0; n < NTA; ++n)
 #pragma unroll
@@ -2178,6 +2185,16 @@ void pre_chained_launch(const Plan& P, const xhc_weights* w, const Plan* Pn, con
     else
       xhc_pre_chained_p_kernel<E, N, K, KR, -1><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
   } else {
+    if constexpr (XHC_PRE_STAGED && std::is_same<E, Bf16>::value && N == 16 && K > 2) {
+      if (P.m == 2 && P.C % (SSB * Bf16::KB) == 0) {
+        // the last sublayer of a chain: the same staged pass without the
+        // next layer's routing
+        a.G = P.Gp;
+        Gpart = P.Gp;
+        xhc_pre_chained_s_kernel<E, N, K, KR, 2, false><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+        goto fin;
+      }
+    }
     Gpart = P.G;
     const unsigned grid = (unsigned)(((P.T + TM * RB - 1) / (TM * RB)) * P.G);
     xhc_pre_chained_kernel<E, N, K, KR, false, RB><<<grid, NTHR, 0, st>>>(a);
