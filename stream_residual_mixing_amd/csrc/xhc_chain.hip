@@ -1318,6 +1318,9 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 #ifndef XHC_PRE_STAGED
 #define XHC_PRE_STAGED 1
 #endif
+#ifndef XHC_STAGE_AUX
+#define XHC_STAGE_AUX 2   // streaming: whole 128-byte lines per load here (measured ~7% faster per pre call, 13% per routing call)
+#endif
 constexpr int SSB = 4;                   // contraction blocks per slice, one wave each
 constexpr int SNTHR = SSB * WAVE;        // 256 threads
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -1347,7 +1350,8 @@ __device__ __forceinline__ void stage_tile(u32x4_t (&sx)[N][TM / 4][WAVE], const
     const int v = wave * LPW + u, i = v / NQ, bq = v % NQ;
     const int tok = 4 * bq + lrow;
     const uint32_t voff = (uint32_t)tok * rowstride + (uint32_t)(slice * 256 + ((lslot ^ tok) << 4));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)&sx[i][bq][0], 16, (int)voff, (int)((uint32_t)i * C * 2), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)&sx[i][bq][0], 16, (int)voff, (int)((uint32_t)i * C * 2), 0,
+                                             XHC_STAGE_AUX);
   }
 }
 // Byte offset, within a stream's rows of a ring slot, of lane (g, r)'s
