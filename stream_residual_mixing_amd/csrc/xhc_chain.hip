@@ -173,9 +173,9 @@ __global__ __launch_bounds__(RouteDims<N>::FT) void xhc_route_fin_kernel(RouteFi
     if (G <= 32 && Gc <= 32) {
       uint64_t x[32], y[32];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) x[q] = ld_b64(rp, off + (uint32_t)(q * P1 * 4));
+      for (int q = 0; q < 32; ++q) x[q] = ld_b64<XHC_FIN_AUX>(rp, off + (uint32_t)(q * P1 * 4));
 #pragma unroll
-      for (int q = 0; q < 32; ++q) y[q] = ld_b64(rc, offc + (uint32_t)(q * P1 * 4));
+      for (int q = 0; q < 32; ++q) y[q] = ld_b64<XHC_FIN_AUX>(rc, offc + (uint32_t)(q * P1 * 4));
 #pragma unroll
       for (int q = 0; q < 32; ++q) {
         v[0] += __uint_as_float((uint32_t)x[q]);
@@ -1031,7 +1031,7 @@ __global__ __launch_bounds__(256) void xhcf_route_fin_kernel(FlashRouteFinArgs a
   __shared__ float s_z[TM][N];
   const int tid = threadIdx.x, G = a.G;
   const int tile = blockIdx.x, t0 = tile * TM;
-  sum_slices<256, 0>(a.part + (size_t)tile * G * P1, G, P1, P1, s_sum, tid);
+  sum_slices<256, XHC_FIN_AUX>(a.part + (size_t)tile * G * P1, G, P1, P1, s_sum, tid);
   __syncthreads();
   const float n_el = (float)N * (float)a.C;
   for (int u = tid; u < TM * N; u += 256) {

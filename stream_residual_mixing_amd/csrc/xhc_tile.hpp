@@ -117,6 +117,9 @@ __device__ __forceinline__ void sum_slices(const float* __restrict__ src, int G,
   }
 }
 
+#ifndef XHC_FIN_AUX
+#define XHC_FIN_AUX 2   // streaming loads of the slice partials in the finalize kernels (each read once; measured ~2% per chain step)
+#endif
 // v[0..1] += sum over s < G, in order s = 0, 1, ..., of the element pair at
 // byte offset off + 4 s stride of the resource rs (whose range ends at slice
 // G, so that slices past it read zero and add nothing; off = OUT_OF_RANGE
@@ -127,7 +130,7 @@ __device__ __forceinline__ void add_slices2(__amdgpu_buffer_rsrc_t rs, int G, in
   for (int s0 = 0; s0 < G; s0 += SB) {
     uint64_t x[SB];
 #pragma unroll
-    for (int q = 0; q < SB; ++q) x[q] = ld_b64(rs, off + (uint32_t)((s0 + q) * stride * 4));
+    for (int q = 0; q < SB; ++q) x[q] = ld_b64<XHC_FIN_AUX>(rs, off + (uint32_t)((s0 + q) * stride * 4));
 #pragma unroll
     for (int q = 0; q < SB; ++q) {
       v[0] += __uint_as_float((uint32_t)x[q]);
