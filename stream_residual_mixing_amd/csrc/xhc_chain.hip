@@ -1307,8 +1307,12 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 // buffer-to-LDS loads, each covering 4 token rows x 256 B: a quarter of the
 // address translations per byte of a load in the MFMA fragment layout
 // (16 rows x 64 B), which is what holds the register-staged kernel back.
-// The loads of the next tile go into the other half of a two-tile ring
-// while this one computes.  Lane l of a load takes 16-byte chunk
+// Two tiles' loads are in flight while one computes: a step reads its tile
+// from one slot of a two-tile ring into registers, and once every wave is
+// past those reads the slot takes the loads of the tile two steps on, while
+// the other slot's (issued a step earlier) complete.  The two slots are
+// separate LDS arrays, so that the compiler tells a read of one from the
+// loads into the other.  Lane l of a load takes 16-byte chunk
 // (l mod 16) xor (token within the tile) of its row, and lands at slot l of
 // the load's 1 KiB, so a fragment read (one chunk of 16 tokens) touches 16
 // different bank groups.  The next layer's routing fragments of the wave's
@@ -1321,9 +1325,36 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_pre_chained_p_kernel(PreChainArg
 #ifndef XHC_STAGE_AUX
 #define XHC_STAGE_AUX 2   // streaming: whole 128-byte lines per load here (measured ~7% faster per pre call, 13% per routing call)
 #endif
+#ifndef XHC_STAGE_AHEAD
+#define XHC_STAGE_AHEAD 2   // tiles whose loads are in flight while one computes (1 or 2)
+#endif
+constexpr int STAGE_AHEAD = XHC_STAGE_AHEAD;
+static_assert(STAGE_AHEAD == 1 || STAGE_AHEAD == 2, "one or two tiles ahead");
 constexpr int SSB = 4;                   // contraction blocks per slice, one wave each
 constexpr int SNTHR = SSB * WAVE;        // 256 threads
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt vmcnt(n): at most n of this wave's vector memory operations
+// still outstanding (they complete in issue order).
+template <int NV>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | 0x0F70);
+}
+// Workgroup barrier of the staged passes: this wave's LDS operations
+// complete, at most NV of its vector memory operations outstanding (63: any
+// number), then s_barrier.  It takes the place of __syncthreads, whose
+// workgroup release fence also waits for every buffer-to-LDS load in flight,
+// including those of tiles that no wave reads before a later barrier.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int NV>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | 0x0070);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Valid tokens of 16-token tile `tile` (full tiles, the ragged one, then none).
 __device__ __forceinline__ int tile_rows(int tile, int full, int tail) {
@@ -1374,7 +1405,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   constexpr int NQ = TM / 4;                   // token quads per tile
   static_assert(SSB * KB * 2 == 256, "a load covers 4 rows x 256 B");
   static_assert(TM * N / 4 <= WAVE && TM * K / 4 <= WAVE, "a tile's routing rows fit one wave each");
-  __shared__ u32x4_t s_x[2][N][NQ][WAVE];      // ring of two tiles: [slot][stream][token quad][16-byte slot]
+  __shared__ u32x4_t s_x0[N][NQ][WAVE];        // ring of two tiles: [stream][token quad][16-byte slot]
+  __shared__ u32x4_t s_x1[N][NQ][WAVE];
   __shared__ float s_red[SSB][NSUM];
   __shared__ float s_red2[SSB][P2];
   __shared__ float s_acs[16];
@@ -1389,9 +1421,14 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   const int kb0 = slice * SSB + wave;          // this wave's contraction block
   const int full = a.T / TM, tail = a.T % TM;
 
-  auto dma = [&](int tile, int q) __attribute__((always_inline)) {
-    stage_tile<N>(s_x[q], reinterpret_cast<const uint16_t*>(a.X), tile, full, tail, C, slice, wave, lane);
+  auto dma = [&](int tile, auto qc) __attribute__((always_inline)) {
+    if constexpr (decltype(qc)::value == 0)
+      stage_tile<N>(s_x0, reinterpret_cast<const uint16_t*>(a.X), tile, full, tail, C, slice, wave, lane);
+    else
+      stage_tile<N>(s_x1, reinterpret_cast<const uint16_t*>(a.X), tile, full, tail, C, slice, wave, lane);
   };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
   // a tile's routing rows: wave 0 the h_pre rows, wave 1 the active lists
   // (units past the valid tokens read zero; other waves read nothing)
   auto load_route = [&](int tile) __attribute__((always_inline)) {
@@ -1449,13 +1486,15 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
 
   int p = team;
   if (p >= ntiles) return;
-  dma(p, 0);
+  constexpr int LPW = N * NQ / SSB;   // buffer-to-LDS loads per wave and tile
+  dma(p, Q0{});
   {
     const u32x4_t rt = load_route(p);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the first tile and its routing rows
+    if constexpr (STAGE_AHEAD == 2) dma(p + nteams, Q1{});
+    wait_vmcnt<STAGE_AHEAD == 2 ? LPW : 0>();   // the first tile and its routing rows
     store_route(0, rt);
   }
-  __syncthreads();
+  stage_barrier<STAGE_AHEAD == 2 ? LPW : 0>();
 
   const __amdgpu_buffer_rsrc_t rlook =
       make_rsrc(LOOK ? a.look : a.part2, LOOK ? (uint32_t)((size_t)ntiles * G * P1 * 4) : 0u);
@@ -1501,11 +1540,14 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   // before the next tile's loads into the other slot are issued: after a
   // buffer-to-LDS load the compiler makes any later LDS read it cannot
   // separate from that load's target wait for it.
+  // vector memory operations of one step, every one issued unconditionally:
+  // the partial stores, the routing rows, the tile loads, the store of inp
+  constexpr int VM_STEP = (LOOK ? IT1 : 0) + IT2 + 1 + LPW + 1;
   int pprev = -1;
   auto tile_step = [&](auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
     const int p1 = p + nteams;
-    const char* xq = reinterpret_cast<const char*>(&s_x[q][0][0][0]);
+    const char* xq = reinterpret_cast<const char*>(q == 0 ? &s_x0[0][0][0] : &s_x1[0][0][0]);
     constexpr uint32_t SBYTES = NQ * WAVE * 16;   // bytes of one stream's tile rows in the ring
     // ---- reads: routing rows, the tile's fragments, the active rows
     int I[K];
@@ -1528,10 +1570,13 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
       gat[j] = j < MS ? x[j < MS ? j : 0] : *reinterpret_cast<const u32x4_t*>(xq + (uint32_t)I[j] * SBYTES + fofs);
     // ---- the previous tile's partial sums, then every wave is past its reads
     store_partials(pprev);
-    __syncthreads();
-    // ---- the next tile's loads (past the last tile they read nothing)
-    dma(p1, q ^ 1);
+    stage_barrier<63>();
+    // ---- the next tile's routing rows, then the loads of the tile two steps
+    // on into this slot (or, one ahead, of the next into the other); past the
+    // last tile they read nothing
     const u32x4_t rnext = load_route(p1);
+    if constexpr (STAGE_AHEAD == 2) dma(p1 + nteams, qc);
+    else dma(p1, std::integral_constant<int, q ^ 1>{});
     // ---- compute from registers
     float o[VEC];
 #pragma unroll
@@ -1571,8 +1616,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
       for (int n = 0; n < NTA; ++n) acc2[n] = E::mma(acc2[n], gat[j], wa[j][n]);
     }
     // ---- this tile's per-wave partials and the next tile's routing rows to
-    // LDS; then this wave's loads are complete, and after the barrier every
-    // wave's are
+    // LDS; then this wave's loads of the next tile are complete (two ahead:
+    // all but this step's), and after the barrier every wave's are
     if constexpr (LOOK) {
 #pragma unroll
       for (int n = 0; n < NTF; ++n)
@@ -1586,18 +1631,18 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
       for (int i = 0; i < 4; ++i) s_red2[wave][(4 * g + i) * NPA + n * 16 + r] = acc2[n][i];
     if ((r >> 2) == g) s_red2[wave][TM * NPA + r] = diag_of(SS, r);
     store_route(q ^ 1, rnext);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
+    stage_barrier<STAGE_AHEAD == 2 ? VM_STEP : 0>();
     pprev = p;
     p = p1;
   };
   // two tiles per trip and the only exit at its end (a tile past the last
   // loads and stores nothing)
   do {
-    tile_step(std::integral_constant<int, 0>{});
-    tile_step(std::integral_constant<int, 1>{});
+    tile_step(Q0{});
+    tile_step(Q1{});
   } while (p < ntiles);
   store_partials(pprev);
+  wait_vmcnt<0>();   // no load into LDS outlives the workgroup
 }
 
 // Routing projection of a whole state (first layer of a chain), with the
@@ -1611,7 +1656,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_proj_s_kernel(ProjPArgs a) {
   constexpr int KB = E::KB;
   constexpr int NQ = TM / 4;
   static_assert(SSB * KB * 2 == 256, "a load covers 4 rows x 256 B");
-  __shared__ u32x4_t s_x[2][N][NQ][WAVE];
+  __shared__ u32x4_t s_x0[N][NQ][WAVE];
+  __shared__ u32x4_t s_x1[N][NQ][WAVE];
   __shared__ float s_red[SSB][NSUM];
   __shared__ float s_acs[16];
 
@@ -1651,9 +1697,10 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_proj_s_kernel(ProjPArgs a) {
   }
   int p = team;
   if (p >= ntiles) return;
-  stage_tile<N>(s_x[0], X, p, full, tail, C, slice, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
+  constexpr int LPW = N * NQ / SSB;
+  stage_tile<N>(s_x0, X, p, full, tail, C, slice, wave, lane);
+  if constexpr (STAGE_AHEAD == 2) stage_tile<N>(s_x1, X, p + nteams, full, tail, C, slice, wave, lane);
+  stage_barrier<STAGE_AHEAD == 2 ? LPW : 0>();
 
   const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.part, (uint32_t)((size_t)ntiles * G * P1 * 4));
   const uint32_t fofs = staged_frag(wave, g, r);
@@ -1672,18 +1719,22 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_proj_s_kernel(ProjPArgs a) {
       st_b32(x, rpart, in && tin ? (uint32_t)((((size_t)tile * G + slice) * P1 + u) * 4) : OUT_OF_RANGE);
     }
   };
+  constexpr int VM_STEP = IT1 + LPW;   // vector memory operations of one step
   int pprev = -1;
   auto tile_step = [&](auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
     const int p1 = p + nteams;
-    const char* xq = reinterpret_cast<const char*>(&s_x[q][0][0][0]);
+    const char* xq = reinterpret_cast<const char*>(q == 0 ? &s_x0[0][0][0] : &s_x1[0][0][0]);
     constexpr uint32_t SBYTES = NQ * WAVE * 16;
     u32x4_t x[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const u32x4_t*>(xq + (uint32_t)i * SBYTES + fofs);
     store_partials(pprev);
-    __syncthreads();
-    stage_tile<N>(s_x[q ^ 1], X, p1, full, tail, C, slice, wave, lane);
+    stage_barrier<63>();
+    // two ahead: the tile two steps on into this slot; one ahead: the next
+    // into the other
+    if constexpr ((STAGE_AHEAD == 2) == (q == 0)) stage_tile<N>(s_x0, X, STAGE_AHEAD == 2 ? p1 + nteams : p1, full, tail, C, slice, wave, lane);
+    else stage_tile<N>(s_x1, X, STAGE_AHEAD == 2 ? p1 + nteams : p1, full, tail, C, slice, wave, lane);
     f32x4_t acc[NTF], S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
 #pragma unroll
     for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1698,8 +1749,7 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_proj_s_kernel(ProjPArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_red[wave][(4 * g + i) * NPF + n * 16 + r] = acc[n][i];
     sums_to_lds(&s_red[wave][TM * NPF], g, r, S1, S2);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
+    stage_barrier<STAGE_AHEAD == 2 ? VM_STEP : 0>();
     pprev = p;
     p = p1;
   };
@@ -1708,6 +1758,7 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_proj_s_kernel(ProjPArgs a) {
     tile_step(std::integral_constant<int, 1>{});
   } while (p < ntiles);
   store_partials(pprev);
+  wait_vmcnt<0>();   // no load into LDS outlives the workgroup
 }
 
 // ---------------------------------------------------------------------------
