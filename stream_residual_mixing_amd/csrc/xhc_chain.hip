@@ -2167,6 +2167,345 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Persistent attention-type post pass with the rows staged through LDS (bf16,
+// m known, C a multiple of the 128-channel slice): the write and its share
+// of the next layer's routing, with the arithmetic of the register-staged
+// pass above, in its order.
+//
+// A workgroup of SSB = 4 waves owns one slice and walks steps of two 16-token
+// tiles; wave w takes contraction block w of both tiles.  A step's k active
+// rows and its rows of out come from HBM by buffer-to-LDS loads of 4 token
+// rows x 256 B into one slot of a two-step ring; as in the staged pre pass a
+// step reads its slot into registers first, and the slot then takes the
+// loads of the step two on (whose addresses need that step's active lists:
+// the lists are in LDS three steps ahead).  The new rows go to LDS in the
+// fragment layout, and the next step reads them back row by row and stores
+// them, 4 rows x 256 B per store.  The next layer's routing fragments of the
+// wave's block (every stream) stay in registers, one wave per SIMD.
+// ---------------------------------------------------------------------------
+#ifndef XHC_POST_STAGED
+#define XHC_POST_STAGED 1
+#endif
+#ifndef XHC_POST_STAGE_AUX
+#define XHC_POST_STAGE_AUX 2   // streaming loads (measured: 318 -> 314 us per call)
+#endif
+#ifndef XHC_POST_ROW_ST_AUX
+#define XHC_POST_ROW_ST_AUX 2  // streaming row stores: whole lines here; with the default policy the dirty lines
+                               // are written back during the next pre pass (measured: that pass 488 -> 478 us)
+#endif
+template <class E, int N, int K, int MS>
+__global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
+  static_assert(std::is_same<E, Bf16>::value, "the staged post pass is written for bf16 state");
+  static_assert(MS > 0 && MS <= K && MS < N, "the fixed streams are known");
+  using T = typename E::T;
+  using D = RouteDims<N>;
+  constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
+  constexpr int KB = E::KB, VEC = E::VEC;
+  constexpr int STT = 2 * TM;                   // tokens per step
+  constexpr int SQ = STT / 4;                   // token quads per step
+  constexpr int NKD = K + 1;                    // ring kinds: the k active positions, then out
+  constexpr int NDMA = NKD * SQ;
+  static_assert(NDMA % SSB == 0 && (K * SQ) % SSB == 0, "a step's loads and stores split evenly over the waves");
+  constexpr int LPW = NDMA / SSB;               // buffer-to-LDS loads per wave and step
+  constexpr int NST = K * SQ / SSB;             // row stores per wave and step
+  constexpr int CF = STT * (K * K + 2 * K);     // H_res [STT][K][K], p [STT][K], H_post [STT][K]
+  constexpr int NL = 4;                         // ring of active lists
+  static_assert(STT * K * K / 4 <= SNTHR, "a step's coefficient arrays take one unit per thread");
+  static_assert(SSB * KB * 2 == 256, "a load covers 4 rows x 256 B");
+  __shared__ u32x4_t s_y0[NKD][SQ][WAVE];       // ring of two steps: [kind][token quad][16-byte slot]
+  __shared__ u32x4_t s_y1[NKD][SQ][WAVE];
+  __shared__ u32x4_t s_n[K][SQ][WAVE];          // the step's new rows, in the ring's layout
+  __shared__ float s_red[SSB][2][NSUM];
+  __shared__ int s_idx[NL][STT * K];
+  __shared__ float s_cf[2][CF];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int C = a.C, G = a.G, nkbC = C / KB;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int nsteps = (a.ntiles + 1) / 2;
+  const int kb0 = slice * SSB + wave;
+  const int full = a.T / STT, tail = a.T % STT;
+  const uint32_t rowstride = (uint32_t)((size_t)N * C * sizeof(T));
+  const uint32_t orow = (uint32_t)((size_t)C * sizeof(T));
+  T* X = reinterpret_cast<T*>(a.X);
+  const T* out = reinterpret_cast<const T*>(a.out);
+  auto srows = [&](int step) { return step < full ? STT : (step == full ? tail : 0); };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+
+  int p = team;
+  if (p >= nsteps) return;
+
+  // ---- next layer's routing fragments of this block, every stream
+  const __amdgpu_buffer_rsrc_t rwn = make_rsrc(a.wnext, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
+  u32x4_t wn[N][NTF];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int n = 0; n < NTF; ++n)
+      wn[i][n] = ld_b128(rwn, (uint32_t)lane * 16, (uint32_t)((((size_t)i * nkbC + kb0) * NTF + n) * WAVE * 16));
+
+  // ---- a step's lists and coefficients, one 16-byte unit per thread (units
+  // past the array or the step's valid tokens read zero)
+  auto load_lists = [&](int step) __attribute__((always_inline)) {
+    const int rows = srows(step);
+    const size_t t0 = rows > 0 ? (size_t)STT * step : 0;
+    return ld_b128(make_rsrc(a.idx + t0 * K, (uint32_t)(rows * K * 4)), (uint32_t)tid * 16, 0);
+  };
+  struct Coefs { u32x4_t h, c2, c3; };
+  auto load_coefs = [&](int step) __attribute__((always_inline)) {
+    const int rows = srows(step);
+    const size_t t0 = rows > 0 ? (size_t)STT * step : 0;
+    Coefs c;
+    c.h = ld_b128(make_rsrc(a.h_res + t0 * K * K, (uint32_t)(rows * K * K * 4)), (uint32_t)tid * 16, 0);
+    c.c2 = ld_b128(make_rsrc(a.p + t0 * K, (uint32_t)(rows * K * 4)), (uint32_t)tid * 16, 0);
+    c.c3 = ld_b128(make_rsrc(a.h_post + t0 * K, (uint32_t)(rows * K * 4)), (uint32_t)tid * 16, 0);
+    return c;
+  };
+  auto store_lists = [&](int slot, const u32x4_t& v) __attribute__((always_inline)) {
+    if (tid < STT * K / 4) reinterpret_cast<u32x4_t*>(&s_idx[slot][0])[tid] = v;
+  };
+  auto store_coefs = [&](int buf, const Coefs& c) __attribute__((always_inline)) {
+    if (tid < STT * K * K / 4) reinterpret_cast<u32x4_t*>(&s_cf[buf][0])[tid] = c.h;
+    if (tid < STT * K / 4) {
+      reinterpret_cast<u32x4_t*>(&s_cf[buf][STT * K * K])[tid] = c.c2;
+      reinterpret_cast<u32x4_t*>(&s_cf[buf][STT * K * K + STT * K])[tid] = c.c3;
+    }
+  };
+
+  // ---- a step's rows into a ring slot.  Load v of the step is (kind, quad):
+  // kinds 0..K-1 the active positions, K out; lane l takes row (token
+  // 4 quad + l / 16), chunk (l mod 16) xor (token mod 16).  A position's
+  // stream comes from the step's list in LDS, read before the loads go out.
+  const int lrow = lane >> 4, lslot = lane & 15;
+  auto dma_streams = [&](int lslotidx, int (&ist)[LPW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int v = wave * LPW + u;
+      const int j = v / SQ, tok = 4 * (v % SQ) + lrow;
+      const int iv = s_idx[lslotidx][tok * K + (j < K ? j : 0)];
+      ist[u] = iv < 0 ? 0 : (iv >= N ? N - 1 : iv);
+    }
+  };
+  auto dma = [&](int step, auto qc, const int (&ist)[LPW]) __attribute__((always_inline)) {
+    const int rows = srows(step);
+    const size_t t0 = rows > 0 ? (size_t)STT * step : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + t0 * N * C, (uint32_t)((size_t)rows * rowstride));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + t0 * C, (uint32_t)((size_t)rows * orow));
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int v = wave * LPW + u;            // uniform over the wave
+      const int j = v / SQ, bq = v % SQ;
+      const int tok = 4 * bq + lrow;
+      const bool isx = j < K;
+      const uint32_t off = (uint32_t)tok * (isx ? rowstride : orow) + (isx ? (uint32_t)ist[u] * orow : 0u) +
+                           (uint32_t)(slice * 256 + ((lslot ^ (tok & 15)) << 4));
+      u32x4_t* dst = decltype(qc)::value == 0 ? &s_y0[j][bq][0] : &s_y1[j][bq][0];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? rx : ro, (lds_ptr_t)dst, 16, (int)off, 0, 0, XHC_POST_STAGE_AUX);
+    }
+  };
+
+  // ---- prologue: the first three steps' lists, the first step's
+  // coefficients, then the rows of the first two steps
+  {
+    const u32x4_t l0 = load_lists(p), l1 = load_lists(p + nteams), l2 = load_lists(p + 2 * nteams);
+    const Coefs c0 = load_coefs(p);
+    wait_vmcnt<0>();
+    store_lists(0, l0);
+    store_lists(1, l1);
+    store_lists(2, l2);
+    store_coefs(0, c0);
+  }
+  __syncthreads();
+  {
+    int ist[LPW];
+    dma_streams(0, ist);
+    dma(p, Q0{}, ist);
+    dma_streams(1, ist);
+    dma(p + nteams, Q1{}, ist);
+  }
+  stage_barrier<LPW>();
+
+  const __amdgpu_buffer_rsrc_t rcorr = make_rsrc(a.corr, (uint32_t)((size_t)a.ntiles * G * P1 * 4));
+  const uint32_t fofs0 = staged_frag(wave, g, r);   // tile 0's fragment within a kind; tile 1 is 4 quads on
+  constexpr uint32_t KBYTES = SQ * WAVE * 16;       // bytes of one kind of a step
+  constexpr uint32_t TBYTES = 4 * WAVE * 16;        // bytes of one tile of a kind
+  const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  const u32x4_t ones = ones_frag<E>();
+  constexpr int IT = (2 * NSUM + SNTHR - 1) / SNTHR;
+  // vector memory operations of one step, every one issued unconditionally:
+  // row stores, partial stores, the lists, the coefficients, the tile loads
+  constexpr int VM_STEP = NST + IT + 1 + 3 + LPW;
+
+  // the new rows of step `st` (in s_n) to their rows of X, and its partials
+  auto store_step = [&](int st, int lslotidx) __attribute__((always_inline)) {
+    u32x4_t stv[NST];
+    int sti[NST];
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int v = wave * NST + u, j = v / SQ, bq = v % SQ;
+      stv[u] = s_n[j][bq][lane];
+      const int iv = s_idx[lslotidx][(4 * bq + lrow) * K + j];
+      sti[u] = iv < 0 ? 0 : (iv >= N ? N - 1 : iv);
+    }
+    float xs[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u0 = tid + it * SNTHR;
+      const int u = u0 < 2 * NSUM ? u0 : 0;
+      const int bb = u / NSUM, vv = u % NSUM;
+      float x = 0.f;
+#pragma unroll
+      for (int c = 0; c < SSB; ++c) x += s_red[c][bb][vv];
+      xs[it] = x;
+    }
+    const int rows = st >= 0 ? srows(st) : 0;
+    const size_t t0 = rows > 0 ? (size_t)STT * st : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + t0 * N * C, (uint32_t)((size_t)rows * rowstride));
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
+      const int v = wave * NST + u, bq = v % SQ;
+      const int tok = 4 * bq + lrow;
+      st_b128<XHC_POST_ROW_ST_AUX>(stv[u], rx, (uint32_t)tok * rowstride + (uint32_t)sti[u] * orow +
+                                                   (uint32_t)(slice * 256 + ((lslot ^ (tok & 15)) << 4)));
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u0 = tid + it * SNTHR;
+      const bool in = u0 < 2 * NSUM;
+      const int u = in ? u0 : 0;
+      const int bb = u / NSUM, vv = u % NSUM;
+      const int tile = 2 * st + bb;
+      st_b32(xs[it], rcorr, in && st >= 0 && tile < a.ntiles ? (uint32_t)((((size_t)tile * G + slice) * P1 + vv) * 4)
+                                                            : OUT_OF_RANGE);
+    }
+  };
+
+  int pprev = -1, k = 0;
+  auto step_fn = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    const int p1 = p + nteams, p2 = p1 + nteams, p3 = p2 + nteams;
+    const int lcur = k & 3, lnx2 = (k + 2) & 3, lprev = (k + 3) & 3;
+    const char* yq = reinterpret_cast<const char*>(q == 0 ? &s_y0[0][0][0] : &s_y1[0][0][0]);
+    // ---- reads: this step's lists, coefficients and fragments; the active
+    // streams of the step two on
+    int I[2][K];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int v = s_idx[lcur][(TM * tt + r) * K + j];
+        I[tt][j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
+      }
+    u32x4_t x[2][K], o[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint32_t f = fofs0 + (uint32_t)tt * TBYTES;
+#pragma unroll
+      for (int j = 0; j < K; ++j) x[tt][j] = *reinterpret_cast<const u32x4_t*>(yq + (uint32_t)j * KBYTES + f);
+      o[tt] = *reinterpret_cast<const u32x4_t*>(yq + (uint32_t)K * KBYTES + f);
+    }
+    float hr[2][K][K], cq[2][K];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tau = TM * tt + r;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) hr[tt][j][i] = s_cf[q][(tau * K + j) * K + i];
+        cq[tt][j] = s_cf[q][STT * K * K + tau * K + j] * s_cf[q][STT * K * K + STT * K + tau * K + j];
+      }
+    }
+    int ist[LPW];
+    dma_streams(lnx2, ist);
+    // ---- the previous step's rows and partials; then every wave is past
+    // its reads of this slot
+    store_step(pprev, lprev);
+    stage_barrier<63>();
+    // ---- lists three steps on, coefficients of the next step, then the
+    // rows of the step two on into this slot (past the last step they read
+    // nothing)
+    const u32x4_t lnx = load_lists(p3);
+    const Coefs cnx = load_coefs(p1);
+    dma(p2, qc, ist);
+    // ---- compute: per tile the write, then the correction
+    u32x4_t xn[2][K];
+    f32x4_t acc[2][NTF], S1[2], S2[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float xa[K][VEC], b0[VEC];
+#pragma unroll
+      for (int i = 0; i < K; ++i) E::unpack(x[tt][i], xa[i]);
+      E::unpack(o[tt], b0);
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        float nv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < K; ++i) sum = fmaf(hr[tt][j][i], xa[i][e], sum);
+          nv[e] = fmaf(cq[tt][j], b0[e], sum);
+        }
+        xn[tt][j] = E::packv_cvt(nv);
+      }
+      // sums of x and x^2 over the new rows, and the next layer's
+      // projection: per stream, the new row that sits in it (zero if none)
+      S1[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      S2[tt] = S1[tt];
+#pragma unroll
+      for (int n = 0; n < NTF; ++n) acc[tt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < K; ++j) mma_sums<E>(xn[tt][j], ones, S1[tt], S2[tt]);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        u32x4_t v = zero;
+        if (i < MS) {
+          v = xn[tt][i < K ? i : 0];
+        } else {
+#pragma unroll
+          for (int j = MS; j < K; ++j) v = (I[tt][j] == i) ? xn[tt][j] : v;
+        }
+#pragma unroll
+        for (int n = 0; n < NTF; ++n) acc[tt][n] = E::mma(acc[tt][n], v, wn[i][n]);
+      }
+    }
+    // ---- the new rows, the partials, the lists and coefficients to LDS;
+    // then this wave's loads of the next step are complete (all but this
+    // step's operations), and after the barrier every wave's are
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&s_n[0][0][0]) + (uint32_t)j * KBYTES + fofs0 +
+                                    (uint32_t)tt * TBYTES) = xn[tt][j];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int n = 0; n < NTF; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_red[wave][tt][(4 * g + i) * NPF + n * 16 + r] = acc[tt][n][i];
+      sums_to_lds(&s_red[wave][tt][TM * NPF], g, r, S1[tt], S2[tt]);
+    }
+    store_lists(lprev, lnx);
+    store_coefs(q ^ 1, cnx);
+    stage_barrier<VM_STEP>();
+    pprev = p;
+    p = p1;
+    ++k;
+  };
+  // two steps per trip and the only exit at its end (a step past the last
+  // loads and stores nothing)
+  do {
+    step_fn(Q0{});
+    step_fn(Q1{});
+  } while (p < nsteps);
+  store_step(pprev, (k + 3) & 3);
+  wait_vmcnt<0>();   // no load into LDS outlives the workgroup
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 namespace {
@@ -2331,6 +2670,13 @@ void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* w, const xhc_
       if (m2) xhc_post_p_kernel<E, N, K, 2, 4><<<grid, PNTHR, 0, st>>>(a);
       else xhc_post_p_kernel<E, N, K, -1, 4><<<grid, PNTHR, 0, st>>>(a);
     } else if (fuse) {
+      if constexpr (XHC_POST_STAGED && std::is_same<E, Bf16>::value && N == 16 && K > 2) {
+        if (m2 && P.C % (SSB * Bf16::KB) == 0) {
+          xhc_post_s_kernel<E, N, K, 2><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+          route_fin_launch<N, K>(Pn, wn, wsn, true, P.Gp, st);
+          return;
+        }
+      }
       if (m2) xhc_post_p_kernel<E, N, K, 2, 1><<<grid, PNTHR, 0, st>>>(a);
       else xhc_post_p_kernel<E, N, K, -1, 1><<<grid, PNTHR, 0, st>>>(a);
     } else {
