@@ -2167,36 +2167,43 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent attention-type post pass with the rows staged through LDS (bf16,
-// m known, C a multiple of the 128-channel slice): the write and its share
-// of the next layer's routing, with the arithmetic of the register-staged
-// pass above, in its order.
+// Persistent post pass with the rows staged through LDS (bf16, m known, C a
+// multiple of the 128-channel slice): the write (WR = 1 attention-type, 4
+// MLP-type) and its share of the next layer's routing, with the arithmetic
+// of the register-staged pass above, in its order.
 //
 // A workgroup of SSB = 4 waves owns one slice and walks steps of two 16-token
 // tiles; wave w takes contraction block w of both tiles.  A step's k active
-// rows and its rows of out come from HBM by buffer-to-LDS loads of 4 token
-// rows x 256 B into one slot of a two-step ring; as in the staged pre pass a
-// step reads its slot into registers first, and the slot then takes the
-// loads of the step two on (whose addresses need that step's active lists:
-// the lists are in LDS three steps ahead).  The new rows go to LDS in the
-// fragment layout, and the next step reads them back row by row and stores
-// them, 4 rows x 256 B per store.  The next layer's routing fragments of the
-// wave's block (every stream) stay in registers, one wave per SIMD.
+// rows and its rows of out (MLP-type: also the 16 rows of out before the
+// step, whose last ones the first tile's lags reach) come from HBM by
+// buffer-to-LDS loads of 4 token rows x 256 B into one slot of a two-step
+// ring; as in the staged pre pass a step reads its slot into registers
+// first, and the slot then takes the loads of the step two on (whose
+// addresses need that step's active lists: the lists are in LDS three steps
+// ahead).  The new rows go to LDS in the fragment layout, and the next step
+// reads them back row by row and stores them, 4 rows x 256 B per store.  The
+// next layer's routing fragments of the wave's block (every stream) stay in
+// registers, one wave per SIMD.
 // ---------------------------------------------------------------------------
 #ifndef XHC_POST_STAGED
 #define XHC_POST_STAGED 1
 #endif
+#ifndef XHC_POST_STAGED_M
+#define XHC_POST_STAGED_M 0   // MLP-type too (correct, but 492 -> 576 us per call: its convolutions at one wave per
+                              // SIMD are slower than the register-staged pass at two)
+#endif
 #ifndef XHC_POST_STAGE_AUX
-#define XHC_POST_STAGE_AUX 2   // streaming loads (measured: 318 -> 314 us per call)
+#define XHC_POST_STAGE_AUX 2   // streaming loads (measured: 318 -> 314 us per attention-type call)
 #endif
 #ifndef XHC_POST_ROW_ST_AUX
 #define XHC_POST_ROW_ST_AUX 2  // streaming row stores: whole lines here; with the default policy the dirty lines
                                // are written back during the next pre pass (measured: that pass 488 -> 478 us)
 #endif
-template <class E, int N, int K, int MS>
+template <class E, int N, int K, int MS, int WR>
 __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
   static_assert(std::is_same<E, Bf16>::value, "the staged post pass is written for bf16 state");
   static_assert(MS > 0 && MS <= K && MS < N, "the fixed streams are known");
+  static_assert(WR == 1 || WR == 4, "write kinds: attention-type, MLP-type");
   using T = typename E::T;
   using D = RouteDims<N>;
   constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
@@ -2204,20 +2211,29 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
   constexpr int STT = 2 * TM;                   // tokens per step
   constexpr int SQ = STT / 4;                   // token quads per step
   constexpr int NKD = K + 1;                    // ring kinds: the k active positions, then out
-  constexpr int NDMA = NKD * SQ;
+  constexpr int NBQ = WR == 4 ? TM / 4 : 0;     // quads of the 16 rows of out before the step
+  constexpr int NDMA = NKD * SQ + NBQ;
   static_assert(NDMA % SSB == 0 && (K * SQ) % SSB == 0, "a step's loads and stores split evenly over the waves");
   constexpr int LPW = NDMA / SSB;               // buffer-to-LDS loads per wave and step
   constexpr int NST = K * SQ / SSB;             // row stores per wave and step
-  constexpr int CF = STT * (K * K + 2 * K);     // H_res [STT][K][K], p [STT][K], H_post [STT][K]
+  constexpr int SLC = SSB * KB;                 // channels of a slice
+  // per-step coefficients: H_res [STT][K][K], then p [STT][K] and H_post
+  // [STT][K] (attention-type) or Q = diag(p) H_post Tm [STT][K][4] (MLP-type)
+  constexpr int E2 = WR == 4 ? 4 * K : K, E3 = WR == 4 ? 0 : K;
+  constexpr int CF = STT * (K * K + E2 + E3);
+  constexpr int NCL = WR == 4 ? 2 : 3;          // coefficient loads per thread
   constexpr int NL = 4;                         // ring of active lists
-  static_assert(STT * K * K / 4 <= SNTHR, "a step's coefficient arrays take one unit per thread");
+  static_assert(STT * K * K / 4 <= SNTHR && STT * E2 / 4 <= SNTHR, "a step's coefficient arrays take one unit per thread");
   static_assert(SSB * KB * 2 == 256, "a load covers 4 rows x 256 B");
   __shared__ u32x4_t s_y0[NKD][SQ][WAVE];       // ring of two steps: [kind][token quad][16-byte slot]
   __shared__ u32x4_t s_y1[NKD][SQ][WAVE];
+  __shared__ u32x4_t s_b0[WR == 4 ? NBQ : 1][WAVE];   // MLP-type: the 16 rows of out before the step
+  __shared__ u32x4_t s_b1[WR == 4 ? NBQ : 1][WAVE];
   __shared__ u32x4_t s_n[K][SQ][WAVE];          // the step's new rows, in the ring's layout
   __shared__ float s_red[SSB][2][NSUM];
   __shared__ int s_idx[NL][STT * K];
   __shared__ float s_cf[2][CF];
+  __shared__ float s_cw[WR == 4 ? 24 : 1][WR == 4 ? SLC : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2237,7 +2253,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
   int p = team;
   if (p >= nsteps) return;
 
-  // ---- next layer's routing fragments of this block, every stream
+  // ---- next layer's routing fragments of this block, every stream; the
+  // slice's conv weights (MLP-type)
   const __amdgpu_buffer_rsrc_t rwn = make_rsrc(a.wnext, (uint32_t)((size_t)N * nkbC * NTF * WAVE * 16));
   u32x4_t wn[N][NTF];
 #pragma unroll
@@ -2245,9 +2262,26 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
 #pragma unroll
     for (int n = 0; n < NTF; ++n)
       wn[i][n] = ld_b128(rwn, (uint32_t)lane * 16, (uint32_t)((((size_t)i * nkbC + kb0) * NTF + n) * WAVE * 16));
+  if constexpr (WR == 4) {
+    // all loads first, then the stores: one memory round trip
+    static_assert((24 * SLC) % SNTHR == 0, "the conv weights of a slice split evenly over the threads");
+    constexpr int NW = 24 * SLC / SNTHR;
+    float cw[NW];
+#pragma unroll
+    for (int it = 0; it < NW; ++it) {
+      const int u = tid + it * SNTHR, tap = u / SLC, c = slice * SLC + u % SLC;
+      cw[it] = a.conv_w[(size_t)tap * C + c];
+    }
+#pragma unroll
+    for (int it = 0; it < NW; ++it) {
+      const int u = tid + it * SNTHR;
+      s_cw[u / SLC][u % SLC] = cw[it];
+    }
+  }
 
   // ---- a step's lists and coefficients, one 16-byte unit per thread (units
   // past the array or the step's valid tokens read zero)
+  const float* arr2 = WR == 4 ? a.wq : a.p;
   auto load_lists = [&](int step) __attribute__((always_inline)) {
     const int rows = srows(step);
     const size_t t0 = rows > 0 ? (size_t)STT * step : 0;
@@ -2259,8 +2293,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
     const size_t t0 = rows > 0 ? (size_t)STT * step : 0;
     Coefs c;
     c.h = ld_b128(make_rsrc(a.h_res + t0 * K * K, (uint32_t)(rows * K * K * 4)), (uint32_t)tid * 16, 0);
-    c.c2 = ld_b128(make_rsrc(a.p + t0 * K, (uint32_t)(rows * K * 4)), (uint32_t)tid * 16, 0);
-    c.c3 = ld_b128(make_rsrc(a.h_post + t0 * K, (uint32_t)(rows * K * 4)), (uint32_t)tid * 16, 0);
+    c.c2 = ld_b128(make_rsrc(arr2 + t0 * E2, (uint32_t)(rows * E2 * 4)), (uint32_t)tid * 16, 0);
+    if constexpr (E3 > 0) c.c3 = ld_b128(make_rsrc(a.h_post + t0 * E3, (uint32_t)(rows * E3 * 4)), (uint32_t)tid * 16, 0);
     return c;
   };
   auto store_lists = [&](int slot, const u32x4_t& v) __attribute__((always_inline)) {
@@ -2268,16 +2302,16 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
   };
   auto store_coefs = [&](int buf, const Coefs& c) __attribute__((always_inline)) {
     if (tid < STT * K * K / 4) reinterpret_cast<u32x4_t*>(&s_cf[buf][0])[tid] = c.h;
-    if (tid < STT * K / 4) {
-      reinterpret_cast<u32x4_t*>(&s_cf[buf][STT * K * K])[tid] = c.c2;
-      reinterpret_cast<u32x4_t*>(&s_cf[buf][STT * K * K + STT * K])[tid] = c.c3;
-    }
+    if (tid < STT * E2 / 4) reinterpret_cast<u32x4_t*>(&s_cf[buf][STT * K * K])[tid] = c.c2;
+    if constexpr (E3 > 0)
+      if (tid < STT * E3 / 4) reinterpret_cast<u32x4_t*>(&s_cf[buf][STT * K * K + STT * E2])[tid] = c.c3;
   };
 
-  // ---- a step's rows into a ring slot.  Load v of the step is (kind, quad):
-  // kinds 0..K-1 the active positions, K out; lane l takes row (token
-  // 4 quad + l / 16), chunk (l mod 16) xor (token mod 16).  A position's
-  // stream comes from the step's list in LDS, read before the loads go out.
+  // ---- a step's rows into a ring slot.  Load v of the step: kinds 0..K-1
+  // the active positions, K out (quads 0..SQ-1 each), then (MLP-type) the
+  // NBQ quads of the rows before; lane l takes row (token 4 quad + l / 16),
+  // chunk (l mod 16) xor (token mod 16).  A position's stream comes from the
+  // step's list in LDS, read before the loads go out.
   const int lrow = lane >> 4, lslot = lane & 15;
   auto dma_streams = [&](int lslotidx, int (&ist)[LPW]) __attribute__((always_inline)) {
 #pragma unroll
@@ -2293,16 +2327,21 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
     const size_t t0 = rows > 0 ? (size_t)STT * step : 0;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + t0 * N * C, (uint32_t)((size_t)rows * rowstride));
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + t0 * C, (uint32_t)((size_t)rows * orow));
+    const bool back = rows > 0 && t0 >= (size_t)TM;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(out + (back ? t0 - TM : 0) * C, back ? (uint32_t)(TM * orow) : 0u);
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int v = wave * LPW + u;            // uniform over the wave
-      const int j = v / SQ, bq = v % SQ;
+      const bool isx = v < K * SQ, isb = v >= NKD * SQ;
+      const int j = isb ? K : v / SQ, bq = isb ? v - NKD * SQ : v % SQ;
       const int tok = 4 * bq + lrow;
-      const bool isx = j < K;
       const uint32_t off = (uint32_t)tok * (isx ? rowstride : orow) + (isx ? (uint32_t)ist[u] * orow : 0u) +
                            (uint32_t)(slice * 256 + ((lslot ^ (tok & 15)) << 4));
-      u32x4_t* dst = decltype(qc)::value == 0 ? &s_y0[j][bq][0] : &s_y1[j][bq][0];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? rx : ro, (lds_ptr_t)dst, 16, (int)off, 0, 0, XHC_POST_STAGE_AUX);
+      u32x4_t* dst;
+      if constexpr (decltype(qc)::value == 0) dst = isb ? &s_b0[bq][0] : &s_y0[j][bq][0];
+      else dst = isb ? &s_b1[bq][0] : &s_y1[j][bq][0];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isx ? rx : (isb ? rb : ro), (lds_ptr_t)dst, 16, (int)off, 0, 0,
+                                               XHC_POST_STAGE_AUX);
     }
   };
 
@@ -2333,10 +2372,11 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
   constexpr uint32_t TBYTES = 4 * WAVE * 16;        // bytes of one tile of a kind
   const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
   const u32x4_t ones = ones_frag<E>();
+  const int cl = wave * KB + VEC * g;               // the lane's first channel within the slice
   constexpr int IT = (2 * NSUM + SNTHR - 1) / SNTHR;
   // vector memory operations of one step, every one issued unconditionally:
   // row stores, partial stores, the lists, the coefficients, the tile loads
-  constexpr int VM_STEP = NST + IT + 1 + 3 + LPW;
+  constexpr int VM_STEP = NST + IT + 1 + NCL + LPW;
 
   // the new rows of step `st` (in s_n) to their rows of X, and its partials
   auto store_step = [&](int st, int lslotidx) __attribute__((always_inline)) {
@@ -2388,8 +2428,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
     const int p1 = p + nteams, p2 = p1 + nteams, p3 = p2 + nteams;
     const int lcur = k & 3, lnx2 = (k + 2) & 3, lprev = (k + 3) & 3;
     const char* yq = reinterpret_cast<const char*>(q == 0 ? &s_y0[0][0][0] : &s_y1[0][0][0]);
-    // ---- reads: this step's lists, coefficients and fragments; the active
-    // streams of the step two on
+    // ---- reads: this step's lists and fragments; the active streams of the
+    // step two on
     int I[2][K];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -2398,7 +2438,7 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
         const int v = s_idx[lcur][(TM * tt + r) * K + j];
         I[tt][j] = v < 0 ? 0 : (v >= N ? N - 1 : v);
       }
-    u32x4_t x[2][K], o[2];
+    u32x4_t x[2][K], o[2], ob = zero;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t f = fofs0 + (uint32_t)tt * TBYTES;
@@ -2406,17 +2446,8 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
       for (int j = 0; j < K; ++j) x[tt][j] = *reinterpret_cast<const u32x4_t*>(yq + (uint32_t)j * KBYTES + f);
       o[tt] = *reinterpret_cast<const u32x4_t*>(yq + (uint32_t)K * KBYTES + f);
     }
-    float hr[2][K][K], cq[2][K];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tau = TM * tt + r;
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-#pragma unroll
-        for (int i = 0; i < K; ++i) hr[tt][j][i] = s_cf[q][(tau * K + j) * K + i];
-        cq[tt][j] = s_cf[q][STT * K * K + tau * K + j] * s_cf[q][STT * K * K + STT * K + tau * K + j];
-      }
-    }
+    if constexpr (WR == 4)
+      ob = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(q == 0 ? &s_b0[0][0] : &s_b1[0][0]) + fofs0);
     int ist[LPW];
     dma_streams(lnx2, ist);
     // ---- the previous step's rows and partials; then every wave is past
@@ -2428,66 +2459,113 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_post_s_kernel(PostPArgs a) {
     // nothing)
     const u32x4_t lnx = load_lists(p3);
     const Coefs cnx = load_coefs(p1);
+    // (kept ahead of the tile loads, so that waiting for them does not wait
+    // for the tile loads too)
+    __builtin_amdgcn_sched_barrier(0);
     dma(p2, qc, ist);
-    // ---- compute: per tile the write, then the correction
-    u32x4_t xn[2][K];
-    f32x4_t acc[2][NTF], S1[2], S2[2];
+    // ---- per tile: the write, its rows to LDS, the correction and its
+    // partials to LDS
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      float xa[K][VEC], b0[VEC];
+      const int tau = TM * tt + r;
+      constexpr int NB = WR;   // write components
+      float xa[K][VEC], bs[NB][VEC];
 #pragma unroll
       for (int i = 0; i < K; ++i) E::unpack(x[tt][i], xa[i]);
-      E::unpack(o[tt], b0);
+      E::unpack(o[tt], bs[0]);
+      if constexpr (WR == 4) {
+        // the causal convolutions of out along the sequence (kernel sizes
+        // 4, 8, 12; lag-i weights at conv_w row off_j + i) in the
+        // per-sublayer write's order: lag i of token r from lane r - i of
+        // this tile, or for r < i from lane r + 16 - i of the 16 rows before
+        // (tile 0: the rows before the step; tile 1: tile 0); lags before
+        // the token's sequence start are zero
+        const u32x4_t opv = tt == 0 ? ob : o[0];
+        const int spos = (STT * p + tau) % a.S;
+        const bool near_start = __builtin_amdgcn_ballot_w64(spos < 11) != 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          bs[1][e] = fmaf(s_cw[0][cl + e], bs[0][e], 0.f);
+          bs[2][e] = fmaf(s_cw[4][cl + e], bs[0][e], 0.f);
+          bs[3][e] = fmaf(s_cw[12][cl + e], bs[0][e], 0.f);
+        }
+        for_each_c<11>([&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value + 1;   // lag
+          u32x4_t lg;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int pv = __builtin_amdgcn_update_dpp(0, (int)opv[d], 0x100 + (16 - i), 0xf, 0xf, false);
+            lg[d] = (uint32_t)__builtin_amdgcn_update_dpp(pv, (int)o[tt][d], 0x110 + i, 0xf, 0xf, false);
+          }
+          if (near_start) lg = i <= spos ? lg : zero;
+          float h[VEC];
+          E::unpack(lg, h);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            if constexpr (i < 4) bs[1][e] = fmaf(s_cw[i][cl + e], h[e], bs[1][e]);
+            if constexpr (i < 8) bs[2][e] = fmaf(s_cw[4 + i][cl + e], h[e], bs[2][e]);
+            bs[3][e] = fmaf(s_cw[12 + i][cl + e], h[e], bs[3][e]);
+          }
+        });
+      }
+      u32x4_t xn[K];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
+        float cq[NB];
+        if constexpr (WR == 1) {
+          cq[0] = s_cf[q][STT * K * K + tau * K + j] * s_cf[q][STT * K * K + STT * K + tau * K + j];
+        } else {
+#pragma unroll
+          for (int v = 0; v < NB; ++v) cq[v] = s_cf[q][STT * K * K + (tau * K + j) * NB + v];
+        }
+        float hr[K];
+#pragma unroll
+        for (int i = 0; i < K; ++i) hr[i] = s_cf[q][(tau * K + j) * K + i];
         float nv[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           float sum = 0.f;
 #pragma unroll
-          for (int i = 0; i < K; ++i) sum = fmaf(hr[tt][j][i], xa[i][e], sum);
-          nv[e] = fmaf(cq[tt][j], b0[e], sum);
+          for (int i = 0; i < K; ++i) sum = fmaf(hr[i], xa[i][e], sum);
+#pragma unroll
+          for (int v = 0; v < NB; ++v) sum = fmaf(cq[v], bs[v][e], sum);
+          nv[e] = sum;
         }
-        xn[tt][j] = E::packv_cvt(nv);
+        xn[j] = E::packv_cvt(nv);
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&s_n[0][0][0]) + (uint32_t)j * KBYTES + fofs0 +
+                                    (uint32_t)tt * TBYTES) = xn[j];
       }
       // sums of x and x^2 over the new rows, and the next layer's
       // projection: per stream, the new row that sits in it (zero if none)
-      S1[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      S2[tt] = S1[tt];
+      f32x4_t acc[NTF], S1 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S2 = S1;
 #pragma unroll
-      for (int n = 0; n < NTF; ++n) acc[tt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NTF; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < K; ++j) mma_sums<E>(xn[tt][j], ones, S1[tt], S2[tt]);
+      for (int j = 0; j < K; ++j) mma_sums<E>(xn[j], ones, S1, S2);
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         u32x4_t v = zero;
         if (i < MS) {
-          v = xn[tt][i < K ? i : 0];
+          v = xn[i < K ? i : 0];
         } else {
 #pragma unroll
-          for (int j = MS; j < K; ++j) v = (I[tt][j] == i) ? xn[tt][j] : v;
+          for (int j = MS; j < K; ++j) v = (I[tt][j] == i) ? xn[j] : v;
         }
 #pragma unroll
-        for (int n = 0; n < NTF; ++n) acc[tt][n] = E::mma(acc[tt][n], v, wn[i][n]);
+        for (int n = 0; n < NTF; ++n) acc[n] = E::mma(acc[n], v, wn[i][n]);
       }
-    }
-    // ---- the new rows, the partials, the lists and coefficients to LDS;
-    // then this wave's loads of the next step are complete (all but this
-    // step's operations), and after the barrier every wave's are
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int j = 0; j < K; ++j)
-        *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(&s_n[0][0][0]) + (uint32_t)j * KBYTES + fofs0 +
-                                    (uint32_t)tt * TBYTES) = xn[tt][j];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
       for (int n = 0; n < NTF; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_red[wave][tt][(4 * g + i) * NPF + n * 16 + r] = acc[tt][n][i];
-      sums_to_lds(&s_red[wave][tt][TM * NPF], g, r, S1[tt], S2[tt]);
+        for (int i = 0; i < 4; ++i) s_red[wave][tt][(4 * g + i) * NPF + n * 16 + r] = acc[n][i];
+      sums_to_lds(&s_red[wave][tt][TM * NPF], g, r, S1, S2);
+      // the second tile reads its weights and coefficients from LDS again
+      // rather than keeping the first tile's in registers
+      asm volatile("" ::: "memory");
     }
+    // ---- the lists and coefficients to LDS; then this wave's loads of the
+    // next step are complete (all but this step's operations), and after the
+    // barrier every wave's are
     store_lists(lprev, lnx);
     store_coefs(q ^ 1, cnx);
     stage_barrier<VM_STEP>();
@@ -2667,12 +2745,19 @@ void tail_launch(const Plan& P, const Plan& Pn, const xhc_weights* w, const xhc_
     const bool m2 = P.m == 2 && K > 2;
     if (fuse && P.KR == 4) {
       launch_xhc_wcoef(P, out, w, ws, st);
+      if constexpr (XHC_POST_STAGED_M && std::is_same<E, Bf16>::value && N == 16 && K > 2) {
+        if (m2 && P.C % (SSB * Bf16::KB) == 0) {
+          xhc_post_s_kernel<E, N, K, 2, 4><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+          route_fin_launch<N, K>(Pn, wn, wsn, true, P.Gp, st);
+          return;
+        }
+      }
       if (m2) xhc_post_p_kernel<E, N, K, 2, 4><<<grid, PNTHR, 0, st>>>(a);
       else xhc_post_p_kernel<E, N, K, -1, 4><<<grid, PNTHR, 0, st>>>(a);
     } else if (fuse) {
       if constexpr (XHC_POST_STAGED && std::is_same<E, Bf16>::value && N == 16 && K > 2) {
         if (m2 && P.C % (SSB * Bf16::KB) == 0) {
-          xhc_post_s_kernel<E, N, K, 2><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+          xhc_post_s_kernel<E, N, K, 2, 1><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
           route_fin_launch<N, K>(Pn, wn, wsn, true, P.Gp, st);
           return;
         }
