@@ -1953,9 +1953,19 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
   // the first, then the state loads of the first PD steps
   load_wslice<N, NTF>(s_w, a.wnext, nkbC, slice, tid);
   if constexpr (WR == 4) {
-    for (int u = tid; u < 24 * SLC; u += PNTHR) {
-      const int tap = u / SLC, c = slice * SLC + u % SLC;
-      s_cw[tap][u % SLC] = c < C ? a.conv_w[(size_t)tap * C + c] : 0.f;
+    // all loads first, then the stores: one memory round trip
+    static_assert((24 * SLC) % PNTHR == 0, "the conv weights of a slice split evenly over the threads");
+    constexpr int NW = 24 * SLC / PNTHR;
+    float cw[NW];
+#pragma unroll
+    for (int it = 0; it < NW; ++it) {
+      const int u = tid + it * PNTHR, tap = u / SLC, c = slice * SLC + u % SLC;
+      cw[it] = c < C ? a.conv_w[(size_t)tap * C + c] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < NW; ++it) {
+      const int u = tid + it * PNTHR;
+      s_cw[u / SLC][u % SLC] = cw[it];
     }
   }
   {
