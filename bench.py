@@ -442,10 +442,11 @@ def _pmc_rows(d):
 
 
 def _attention_post_pass(name):
-    """The persistent post pass that writes an attention-type sublayer (its
-    last template argument, the write kind, is 1)."""
+    """The persistent post pass that writes an attention-type sublayer
+    (register- or LDS-staged; its last template argument, the write kind,
+    is 1)."""
     import re
-    m = re.search(r"xhc_post_p_kernel<[^>]*,\s*(\d+)>", name)
+    m = re.search(r"xhc_post_[ps]_kernel<[^>]*,\s*(\d+)>", name)
     return bool(m) and m.group(1) == "1"
 
 
