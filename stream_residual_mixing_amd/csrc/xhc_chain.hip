@@ -1334,28 +1334,6 @@ constexpr int SSB = 4;                   // contraction blocks per slice, one wa
 constexpr int SNTHR = SSB * WAVE;        // 256 threads
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// s_waitcnt vmcnt(n): at most n of this wave's vector memory operations
-// still outstanding (they complete in issue order).
-template <int NV>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(NV >= 0 && NV < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | 0x0F70);
-}
-// Workgroup barrier of the staged passes: this wave's LDS operations
-// complete, at most NV of its vector memory operations outstanding (63: any
-// number), then s_barrier.  It takes the place of __syncthreads, whose
-// workgroup release fence also waits for every buffer-to-LDS load in flight,
-// including those of tiles that no wave reads before a later barrier.  The
-// empty asm statements keep the compiler from moving memory accesses across.
-template <int NV>
-__device__ __forceinline__ void stage_barrier() {
-  static_assert(NV >= 0 && NV < 64, "vmcnt is 6 bits");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | 0x0070);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Valid tokens of 16-token tile `tile` (full tiles, the ragged one, then none).
 __device__ __forceinline__ int tile_rows(int tile, int full, int tail) {
   return tile < full ? TM : (tile == full ? tail : 0);

@@ -333,6 +333,12 @@ static bool gen_dispatch(int NT, const void* X, int T, long K, const void* Wp, l
 #ifndef XHC_MHC_BD
 #define XHC_MHC_BD 4
 #endif
+#ifndef XHC_MHC_STAGED
+#define XHC_MHC_STAGED 1   // the state staged through LDS, two stages ahead
+#endif
+#ifndef XHC_MHC_STATE_AUX
+#define XHC_MHC_STATE_AUX 2   // cache policy of the staged state loads (whole 128-byte lines: streaming)
+#endif
 constexpr int MP_KU = XHC_MHC_KU;              // contraction blocks per LDS stage
 constexpr int MP_BD = XHC_MHC_BD;              // weight fragments in registers (read ahead)
 constexpr int MP_RT = XHC_MHC_RT;              // 16-token MFMA row tiles per wave
@@ -347,7 +353,12 @@ __global__ __launch_bounds__(MP_THREADS, 1) void mhc_proj_kernel(const uint16_t*
                                                                  float* __restrict__ part, float* __restrict__ stats) {
   constexpr int CH = MP_KU * NT;                  // 1 KiB weight fragments per stage
   constexpr int NW = MP_THREADS / WAVE;
-  __shared__ u32x4_t s_w[2][MP_KU][NT][WAVE];
+  // the two weight buffers are separate LDS arrays, so that the compiler
+  // tells a read of one from the loads into the other
+  __shared__ u32x4_t s_w0[MP_KU][NT][WAVE];
+  __shared__ u32x4_t s_w1[MP_KU][NT][WAVE];
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ks = blockIdx.x % KS, tile = blockIdx.x / KS;
@@ -376,11 +387,12 @@ __global__ __launch_bounds__(MP_THREADS, 1) void mhc_proj_kernel(const uint16_t*
   // Fragment c = wave + NW q; a wave whose last q falls past CH loads the last
   // fragment again (the same bytes to the same place), so that every wave
   // issues the same, compile-time number of loads.
-  auto load_w = [&](long kbs, int buf) __attribute__((always_inline)) {
+  auto load_w = [&](long kbs, auto bc) __attribute__((always_inline)) {
+    u32x4_t* wb = decltype(bc)::value == 0 ? &s_w0[0][0][0] : &s_w1[0][0][0];
 #pragma unroll
     for (int q = 0; q < (CH + NW - 1) / NW; ++q) {
       const int c = wave + NW * q < CH ? wave + NW * q : CH - 1;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(&s_w[buf][0][0][0] + (size_t)c * WAVE), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(wb + (size_t)c * WAVE), 16,
                                                (int)(((kbs * NT + c) * WAVE + lane) * 16), 0, 0, 0);
     }
   };
@@ -402,9 +414,11 @@ __global__ __launch_bounds__(MP_THREADS, 1) void mhc_proj_kernel(const uint16_t*
   // the state loads issued after them stay in flight into the next stage.
   constexpr int WAIT_W = (MP_RT * MP_KU) | (0x7 << 4) | (0xF << 8);   // vmcnt(MP_RT * MP_KU)
   static_assert(MP_RT * MP_KU < 16, "the wait count fits the low vmcnt bits");
-  auto stage = [&](long kbs, int buf, const u32x4_t (&acur)[MP_RT][MP_KU], u32x4_t (&anext)[MP_RT][MP_KU])
+  auto stage = [&](long kbs, auto bc, const u32x4_t (&acur)[MP_RT][MP_KU], u32x4_t (&anext)[MP_RT][MP_KU])
       __attribute__((always_inline)) {
-    load_w(kbs + MP_KU, buf ^ 1);
+    constexpr int buf = decltype(bc)::value;
+    const u32x4_t(&sw)[MP_KU][NT][WAVE] = buf == 0 ? s_w0 : s_w1;
+    load_w(kbs + MP_KU, std::integral_constant<int, buf ^ 1>{});
     load_a(kbs + MP_KU, anext);
 #pragma unroll
     for (int k = 0; k < MP_KU; ++k) {
@@ -422,10 +436,10 @@ __global__ __launch_bounds__(MP_THREADS, 1) void mhc_proj_kernel(const uint16_t*
       // LDS latency hides behind the MFMAs of the tiles before
       u32x4_t b[MP_BD];
 #pragma unroll
-      for (int q = 0; q < MP_BD - 1 && q < NT; ++q) b[q] = s_w[buf][k][q][lane];
+      for (int q = 0; q < MP_BD - 1 && q < NT; ++q) b[q] = sw[k][q][lane];
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        if (n + MP_BD - 1 < NT) b[(n + MP_BD - 1) % MP_BD] = s_w[buf][k][n + MP_BD - 1][lane];
+        if (n + MP_BD - 1 < NT) b[(n + MP_BD - 1) % MP_BD] = sw[k][n + MP_BD - 1][lane];
 #pragma unroll
         for (int h = 0; h < MP_RT; ++h) acc[h][n] = Bf16::mma(acc[h][n], acur[h][k], b[n % MP_BD]);
         __builtin_amdgcn_sched_barrier(0);   // keep each read ahead of the MFMAs before its use
@@ -435,15 +449,107 @@ __global__ __launch_bounds__(MP_THREADS, 1) void mhc_proj_kernel(const uint16_t*
     __syncthreads();
   };
 
-  u32x4_t a0[MP_RT][MP_KU], a1[MP_RT][MP_KU];
-  load_w(kb0, 0);
-  load_a(kb0, a0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (long kbs = kb0; kbs < kb1; kbs += 2 * MP_KU) {
-    stage(kbs, 0, a0, a1);
-    if (kbs + MP_KU >= kb1) break;
-    stage(kbs + MP_KU, 1, a1, a0);
+  if constexpr (XHC_MHC_STAGED) {
+    // The state through LDS: a stage's rows of the workgroup (256 tokens x
+    // 2 blocks x 64 B) go from HBM into one slot of a two-stage ring with
+    // buffer-to-LDS loads of 8 rows x 128 B.  A stage reads its A fragments
+    // from its slot into registers first; once every wave is past those
+    // reads the slot takes the state of the stage two on, while the other
+    // slot's (issued a stage earlier) completes.  The slots are separate LDS
+    // arrays, so the compiler tells a read of one from the loads into the
+    // other, and the barriers are stage_barrier, without the release fence
+    // that would wait for those loads.
+    static_assert(MP_KU == 2 && NW * MP_RT * 16 == MP_TOK, "a stage is 256 rows x 128 B");
+    constexpr int NDB = MP_TOK / 8;           // 1 KiB loads per stage
+    constexpr int LPW = NDB / NW;             // per wave
+    static_assert(NDB % NW == 0, "the loads of a stage split evenly over the waves");
+    __shared__ u32x4_t s_a0[NDB][WAVE];
+    __shared__ u32x4_t s_a1[NDB][WAVE];
+    const int lr = lane >> 3, ls = lane & 7;
+    // load d covers rows 8 d .. 8 d + 7 of the workgroup (half d mod 2 of
+    // tile d / 2); lane l takes row 8 d + l / 8 and, at slot l mod 8, the
+    // 16-byte chunk (l mod 8) xor ((row within the tile) / 2 mod 8) of its
+    // 128 bytes (chunk c: block c / 4, lane group c mod 4).  Blocks past
+    // this split's range read zero.
+    auto dma_a = [&](long kbs, auto qc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < LPW; ++u) {
+        const int d = wave * LPW + u;
+        const int rr = (d & 1) * 8 + lr, row = d * 8 + lr;
+        const int c = ls ^ ((rr >> 1) & 7);
+        const long blk = kbs + (c >> 2);
+        const uint32_t off =
+            blk < kb1 ? (uint32_t)((size_t)row * K * 2 + (size_t)blk * 64 + (size_t)(c & 3) * 16) : OUT_OF_RANGE;
+        u32x4_t* dst = decltype(qc)::value == 0 ? &s_a0[d][0] : &s_a1[d][0];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)dst, 16, (int)off, 0, 0, XHC_MHC_STATE_AUX);
+      }
+    };
+    // lane (g, r)'s fragment of tile h, block k: row r, chunk 4 k + g
+    auto afrag = [&](const char* sa, int h, int k) __attribute__((always_inline)) {
+      const int ti = wave * MP_RT + h;
+      return *reinterpret_cast<const u32x4_t*>(sa + ti * 2048 + r * 128 + (((4 * k + g) ^ ((r >> 1) & 7)) << 4));
+    };
+    auto stage_s = [&](long kbs, auto qc) __attribute__((always_inline)) {
+      constexpr int q = decltype(qc)::value;
+      const char* sa = reinterpret_cast<const char*>(q == 0 ? &s_a0[0][0] : &s_a1[0][0]);
+      const u32x4_t(&sw)[MP_KU][NT][WAVE] = q == 0 ? s_w0 : s_w1;
+      u32x4_t acur[MP_RT][MP_KU];
+#pragma unroll
+      for (int h = 0; h < MP_RT; ++h)
+#pragma unroll
+        for (int k = 0; k < MP_KU; ++k) acur[h][k] = afrag(sa, h, k);
+      stage_barrier<63>();   // every wave is past its reads of this slot
+      load_w(kbs + MP_KU, std::integral_constant<int, q ^ 1>{});
+      dma_a(kbs + 2 * MP_KU, qc);
+#pragma unroll
+      for (int k = 0; k < MP_KU; ++k) {
+#pragma unroll
+        for (int h = 0; h < MP_RT; ++h) {
+          float f[8];
+          Bf16::unpack(acur[h][k], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            s1[h] += f[e];
+            s2[h] = fmaf(f[e], f[e], s2[h]);
+          }
+        }
+        u32x4_t b[MP_BD];
+#pragma unroll
+        for (int qq = 0; qq < MP_BD - 1 && qq < NT; ++qq) b[qq] = sw[k][qq][lane];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          if (n + MP_BD - 1 < NT) b[(n + MP_BD - 1) % MP_BD] = sw[k][n + MP_BD - 1][lane];
+#pragma unroll
+          for (int h = 0; h < MP_RT; ++h) acc[h][n] = Bf16::mma(acc[h][n], acur[h][k], b[n % MP_BD]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // the next stage's weights (this stage's loads) and state (the
+      // previous stage's) are in: all but this stage's state loads
+      stage_barrier<LPW>();
+    };
+    load_w(kb0, Q0{});
+    dma_a(kb0, Q0{});
+    dma_a(kb0 + MP_KU, Q1{});
+    stage_barrier<LPW>();
+    // two stages per trip; a stage past the range reads zero fragments and
+    // adds nothing
+    for (long kbs = kb0; kbs < kb1; kbs += 2 * MP_KU) {
+      stage_s(kbs, Q0{});
+      stage_s(kbs + MP_KU, Q1{});
+    }
+    wait_vmcnt<0>();   // no load into LDS outlives the workgroup
+  } else {
+    u32x4_t a0[MP_RT][MP_KU], a1[MP_RT][MP_KU];
+    load_w(kb0, Q0{});
+    load_a(kb0, a0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (long kbs = kb0; kbs < kb1; kbs += 2 * MP_KU) {
+      stage(kbs, Q0{}, a0, a1);
+      if (kbs + MP_KU >= kb1) break;
+      stage(kbs + MP_KU, Q1{}, a1, a0);
+    }
   }
   constexpr int NP = NT * 16;
 #pragma unroll

@@ -83,6 +83,28 @@ __device__ __forceinline__ void st_b32(float v, __amdgpu_buffer_rsrc_t rs, uint3
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, (int)voff, 0, 0);
 }
 
+// s_waitcnt vmcnt(n): at most n of this wave's vector memory operations
+// still outstanding (they complete in issue order).
+template <int NV>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | 0x0F70);
+}
+// Workgroup barrier of the passes that stage through LDS: this wave's LDS operations
+// complete, at most NV of its vector memory operations outstanding (63: any
+// number), then s_barrier.  It takes the place of __syncthreads, whose
+// workgroup release fence also waits for every buffer-to-LDS load in flight,
+// including those of tiles that no wave reads before a later barrier.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int NV>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | 0x0070);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait for all of this wave's outstanding memory operations.
 __device__ __forceinline__ void wait_mem() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
