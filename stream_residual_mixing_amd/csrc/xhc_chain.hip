@@ -913,6 +913,7 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_proj_p_kernel(ProjPArgs a) {
 // sum x^2 per token, then the slice's router column sums.
 // ---------------------------------------------------------------------------
 struct FlashDims16 {
+  static constexpr int NTF = 3;
   static constexpr int NPF = 48;
   static constexpr int NSUM = TM * NPF + 2 * TM;
   static constexpr int P1 = NSUM + 16;
@@ -1625,11 +1626,12 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
 
 // Routing projection of a whole state (first layer of a chain), with the
 // state staged through LDS as in the pre pass above: every stream's rows,
-// no masking, the routing partials alone.
-template <class E, int N>
+// no masking, the routing partials alone.  D gives the column tiles and the
+// partial layout: RouteDims<N> (W_r, W_pre) or, for xHC-Flash,
+// FlashDims16 (router, attention and MLP pre-maps).
+template <class E, int N, class D = RouteDims<N>>
 __global__ __launch_bounds__(SNTHR, 1) void xhc_proj_s_kernel(ProjPArgs a) {
   static_assert(std::is_same<E, Bf16>::value, "the staged projection is written for bf16 state");
-  using D = RouteDims<N>;
   constexpr int NTF = D::NTF, NPF = D::NPF, NSUM = D::NSUM, P1 = D::P1;
   constexpr int KB = E::KB;
   constexpr int NQ = TM / 4;
@@ -2834,10 +2836,14 @@ bool launch_flash_route_p(const Plan& P, const void* X, const void* wp, float* p
   a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
   a.wfull = reinterpret_cast<const uint4*>(wp);
   a.part = part;
-  if (P.dtype == XHC_BF16)
-    xhcf_proj_p_kernel<Bf16><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
-  else
+  if (P.dtype == XHC_BF16) {
+    if (XHC_PRE_STAGED && P.C % (SSB * Bf16::KB) == 0)
+      xhc_proj_s_kernel<Bf16, 16, FlashDims16><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+    else
+      xhcf_proj_p_kernel<Bf16><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
+  } else {
     xhcf_proj_p_kernel<F32><<<(unsigned)persist_grid(P), PNTHR, 0, st>>>(a);
+  }
   FlashRouteFinArgs f;
   f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.Gp; f.part = part;
   f.b_pa = w->b_pre_attn; f.b_pm = w->b_pre_mlp; f.a_pa = w->alpha_pre_attn; f.a_pm = w->alpha_pre_mlp;
