@@ -264,7 +264,11 @@ xhc_status make_flash4_plan(const xhc_config* cfg, xhc::Plan* P) {
   q.o_wfull = take((size_t)q.nkb_full * q.NTF * 64 * 16);
   for (int i = 0; i < 3; ++i) q.o_wq[i] = take((size_t)q.nkb_act * ntq[i] * 64 * 16);
   q.o_wact = take((size_t)q.nkb_act * q.NTA * 64 * 16);
-  q.o_part = take((size_t)q.KS * T * q.NTF * 16 * 4);
+  // projection partials: split-K [KS][T][NTF*16], or per (16-token tile,
+  // slice) of the staged persistent N = 16 kernel
+  const size_t part_splitk = (size_t)q.KS * T * q.NTF * 16;
+  const size_t part_tiles = xhc::flash4_route_p_applies(q) ? (size_t)q.ntiles * q.Gp * xhc::FLASH4_P1 : 0;
+  q.o_part = take((part_splitk > part_tiles ? part_splitk : part_tiles) * 4);
   q.o_stats = take((size_t)q.KS * T * 2 * 4);
   q.o_part2 = take((size_t)q.ntiles * q.G2 * (16 * (size_t)ntmax * 16 + 16) * 4);
   q.o_gram = take((size_t)q.nslices * T * 10 * 8);

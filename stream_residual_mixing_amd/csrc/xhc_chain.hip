@@ -1014,6 +1014,15 @@ __global__ __launch_bounds__(PNTHR, 1) void xhcf_proj_p_kernel(ProjPArgs a) {
   }
 }
 
+// The xHC-Flash-4sub projection: router and four pre-maps per block.
+struct Flash4Dims16 {
+  static constexpr int NTF = 5;
+  static constexpr int NPF = 80;
+  static constexpr int NSUM = TM * NPF + 2 * TM;
+  static constexpr int P1 = NSUM + 16;
+};
+static_assert(Flash4Dims16::P1 == (int)FLASH4_P1, "the workspace sizes the 4sub partials with FLASH4_P1");
+
 struct FlashRouteFinArgs {
   int T, C, m, G;
   const float* part;
@@ -1063,6 +1072,58 @@ __global__ __launch_bounds__(256) void xhcf_route_fin_kernel(FlashRouteFinArgs a
     for (int j = 0; j < K; ++j) {
       a.idx[(size_t)t * K + j] = sel[j];
       a.p[(size_t)t * K + j] = j < a.m ? 1.f : sigmoidf_(zt[sel[j]]);
+    }
+  }
+}
+
+// Routing of a tile from the summed persistent partials of the xHC-Flash-4sub
+// projection (N = 16): router logits, the four pre-maps, the active list and
+// router weights (per token the arithmetic of the split-K path's routing
+// kernel, from partials summed over the slices in order).
+struct Flash4RouteFinArgs {
+  int T, C, m, G;
+  const float* part;
+  float eps;
+  Flash4Route o;
+};
+template <int K>
+__global__ __launch_bounds__(256) void xhcf4_route_fin_kernel(Flash4RouteFinArgs a) {
+  constexpr int N = 16, NPF = Flash4Dims16::NPF, NSUM = Flash4Dims16::NSUM, P1 = Flash4Dims16::P1;
+  __shared__ float s_sum[P1];
+  __shared__ float s_z[TM][N];
+  const int tid = threadIdx.x, G = a.G;
+  const int tile = blockIdx.x, t0 = tile * TM;
+  sum_slices<256, XHC_FIN_AUX>(a.part + (size_t)tile * G * P1, G, P1, P1, s_sum, tid);
+  __syncthreads();
+  const float n_el = (float)N * (float)a.C;
+  for (int u = tid; u < TM * N; u += 256) {
+    const int tau = u / N, i = u % N, t = t0 + tau;
+    const bool valid = t < a.T;
+    const float q1 = s_sum[TM * NPF + 2 * tau], q2 = s_sum[TM * NPF + 2 * tau + 1], cs = s_sum[NSUM + i];
+    float z = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float hp, zz;
+      route_logits(s_sum[tau * NPF + i], s_sum[tau * NPF + (1 + q) * N + i], q1, q2, cs, n_el, a.eps, a.o.a_pre[q],
+                   a.o.b_pre[q][i], valid, &zz, &hp);
+      if (q == 0) z = zz;
+      if (valid) a.o.h_pre[q][(size_t)t * N + i] = hp;
+    }
+    s_z[tau][i] = z;
+    if (valid) a.o.z[(size_t)t * N + i] = z;
+  }
+  __syncthreads();
+  if (tid < TM && t0 + tid < a.T) {
+    const int t = t0 + tid;
+    float zt[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) zt[i] = s_z[tid][i];
+    int sel[K];
+    route_select<N, K>(zt, a.m, sel);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a.o.idx[(size_t)t * K + j] = sel[j];
+      a.o.p[(size_t)t * K + j] = j < a.m ? 1.f : sigmoidf_(zt[sel[j]]);
     }
   }
 }
@@ -2825,6 +2886,28 @@ bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn,
   if (!launch_pack(Pn, wn, wsn, &P, w, ws, &P, ws, st)) return false;
   return P.dtype == XHC_BF16 ? pre_chained_dispatch<Bf16>(P, w, Pn, X, inp, ws, wsn, st)
                              : pre_chained_dispatch<F32>(P, w, Pn, X, inp, ws, wsn, st);
+}
+
+bool flash4_route_p_applies(const Plan& P) {
+  return XHC_PRE_STAGED && P.N == 16 && P.K == 4 && P.dtype == XHC_BF16 && P.C % (SSB * Bf16::KB) == 0 &&
+         P.ntiles > 0;
+}
+
+// xHC-Flash-4sub routing at N = 16: the staged persistent projection (packed
+// weights of five tiles at wp, partials at part, Gp slices), then the routing
+// of every tile.
+bool launch_flash4_route_p(const Plan& P, const void* X, const void* wp, float* part, const Flash4Route& o,
+                           hipStream_t st) {
+  if (!flash4_route_p_applies(P)) return false;
+  ProjPArgs a;
+  a.X = X; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.ntiles = (int)P.ntiles;
+  a.wfull = reinterpret_cast<const uint4*>(wp);
+  a.part = part;
+  xhc_proj_s_kernel<Bf16, 16, Flash4Dims16><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+  Flash4RouteFinArgs f;
+  f.T = (int)P.T; f.C = P.C; f.m = P.m; f.G = P.Gp; f.part = part; f.eps = P.eps_norm; f.o = o;
+  xhcf4_route_fin_kernel<4><<<(unsigned)P.ntiles, 256, 0, st>>>(f);
+  return true;
 }
 
 // xHC-Flash routing at N = 16: the persistent projection (packed weights of

@@ -488,18 +488,8 @@ bool flash4_pre_launch(const Plan& P, const xhcf4_weights* w, const void* X, voi
   for (int q = 0; q < 3; ++q)
     launch_pack_b(P.dtype, w->w_post[q], P.nkb_act, ncq[q], (ncq[q] + 15) / 16, ws + P.o_wq[q], st);
   launch_pack_b(P.dtype, w->w_act_last, P.nkb_act, P.ncol_act, P.NTA, ws + P.o_wact, st);
-  float* cs = reinterpret_cast<float*>(ws + P.o_colsum);
-  flash_colsum_kernel<E, N><<<CSB, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C, P.ncol_full,
-                                                 cs + N);
-  flash_colsum_fin_kernel<N><<<1, 64, 0, st>>>(cs + N, cs);
   float* part = reinterpret_cast<float*>(ws + P.o_part);
-  float* stats = reinterpret_cast<float*>(ws + P.o_stats);
-  if (!launch_projection(P.dtype, P.NTF, X, (int)P.T, (long)N * P.C, ws + P.o_wfull, P.nkb_full, P.KS, part, stats,
-                         st))
-    return false;
   FlashRouteArgs r{};
-  r.T = (int)P.T; r.m = P.m; r.KS = P.KS; r.NP = P.NTF * 16; r.n_el = (long)N * P.C;
-  r.part = part; r.stats = stats; r.cs = cs; r.eps = P.eps_norm;
   for (int q = 0; q < 4; ++q) {
     r.b_pre[q] = w->b_pre[q];
     r.a_pre[q] = w->alpha_pre[q];
@@ -508,7 +498,29 @@ bool flash4_pre_launch(const Plan& P, const xhcf4_weights* w, const void* X, voi
   r.idx = reinterpret_cast<int*>(ws + P.o_idx);
   r.p = reinterpret_cast<float*>(ws + P.o_p);
   r.z = reinterpret_cast<float*>(ws + P.o_z);
-  flash_route_kernel<N, K, 4><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(r);
+  if (flash4_route_p_applies(P)) {
+    // the staged persistent projection, partials per (tile, slice)
+    Flash4Route o;
+    for (int q = 0; q < 4; ++q) {
+      o.b_pre[q] = r.b_pre[q];
+      o.a_pre[q] = r.a_pre[q];
+      o.h_pre[q] = r.h_pre[q];
+    }
+    o.idx = r.idx; o.p = r.p; o.z = r.z;
+    if (!launch_flash4_route_p(P, X, ws + P.o_wfull, part, o, st)) return false;
+  } else {
+    float* cs = reinterpret_cast<float*>(ws + P.o_colsum);
+    flash_colsum_kernel<E, N><<<CSB, 256, 0, st>>>(reinterpret_cast<const TT*>(w->w_full), (long)N * P.C,
+                                                   P.ncol_full, cs + N);
+    flash_colsum_fin_kernel<N><<<1, 64, 0, st>>>(cs + N, cs);
+    float* stats = reinterpret_cast<float*>(ws + P.o_stats);
+    if (!launch_projection(P.dtype, P.NTF, X, (int)P.T, (long)N * P.C, ws + P.o_wfull, P.nkb_full, P.KS, part,
+                           stats, st))
+      return false;
+    r.T = (int)P.T; r.m = P.m; r.KS = P.KS; r.NP = P.NTF * 16; r.n_el = (long)N * P.C;
+    r.part = part; r.stats = stats; r.cs = cs; r.eps = P.eps_norm;
+    flash_route_kernel<N, K, 4><<<(unsigned)((P.T + 255) / 256), 256, 0, st>>>(r);
+  }
 
   FlashReadArgs d{};
   d.X = X; d.T = (int)P.T; d.C = P.C; d.K = P.K; d.idx = r.idx;

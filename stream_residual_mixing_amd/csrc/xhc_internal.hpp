@@ -169,6 +169,20 @@ bool launch_xhcf4_post(const Plan& P, const xhcf4_weights* w, int q, void* X, co
                        void* inp, char* ws, hipStream_t st);
 bool launch_flash_route_p(const Plan& P, const void* X, const void* wp, float* part, const xhcf_weights* w, int* idx,
                           float* p, float* h_pa, float* h_pm, float* z, hipStream_t st);
+// xHC-Flash-4sub routing at N = 16 from the LDS-staged persistent projection
+// (bf16 state, C a multiple of 128 channels): partials per (16-token tile,
+// channel slice) of FLASH4_P1 floats at part, then the routing of every tile.
+constexpr size_t FLASH4_P1 = 16 * 80 + 2 * 16 + 16;
+struct Flash4Route {
+  const float* b_pre[4];
+  float a_pre[4];
+  int* idx;
+  float *p, *z;
+  float* h_pre[4];
+};
+bool flash4_route_p_applies(const Plan& P);
+bool launch_flash4_route_p(const Plan& P, const void* X, const void* wp, float* part, const Flash4Route& o,
+                           hipStream_t st);
 // xHC-Flash block (xhc_flash.hip)
 bool launch_xhcf_pre(const Plan& P, const xhcf_weights* w, const void* X, void* inp_a, void* inp_m, char* ws,
                      hipStream_t st);
