@@ -1685,6 +1685,148 @@ __global__ __launch_bounds__(SNTHR, 1) void xhc_pre_chained_s_kernel(PreChainArg
   wait_vmcnt<0>();   // no load into LDS outlives the workgroup
 }
 
+// xHC-Flash readouts staged through LDS (N = 16, bf16, C a multiple of 128):
+// the NPRE weighted sums of a token's streams (the pages' readout equation
+// of xHC-Flash) from one pass over the state, as flash_read_kernel computes
+// them and in its order, with the rows loaded as in the staged pre pass (a
+// persistent workgroup of 4 waves per 128-channel slice, 16-token tiles,
+// two tiles in flight).  With MASK, readouts 1.. leave out the token's
+// active streams (the non-active bases of xHC-Flash-4sub).
+struct FlashReadSArgs {
+  const void* X;
+  void* out[4];
+  const float* h_pre[4];
+  const int* idx;   // MASK only
+  int T, C, G, K, ntiles;
+};
+template <int NPRE, bool MASK>
+__global__ __launch_bounds__(SNTHR, 1) void flash_read_s_kernel(FlashReadSArgs a) {
+  using E = Bf16;
+  using T = typename E::T;
+  constexpr int N = 16, KB = E::KB, VEC = E::VEC, NQ = TM / 4;
+  constexpr int KMAX = 4;
+  static_assert(NPRE * TM * N / 4 <= SNTHR, "a tile's readout weights take one unit per thread");
+  __shared__ u32x4_t s_x0[N][NQ][WAVE];
+  __shared__ u32x4_t s_x1[N][NQ][WAVE];
+  __shared__ float s_h[2][NPRE][TM * N];
+  __shared__ int s_ri[2][TM * KMAX];
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int C = a.C, G = a.G, K = a.K;
+  const int slice = blockIdx.x % G, team = blockIdx.x / G, nteams = gridDim.x / G;
+  const int ntiles = a.ntiles;
+  const int kb0 = slice * SSB + wave;
+  const int full = a.T / TM, tail = a.T % TM;
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X);
+
+  auto dma = [&](int tile, auto qc) __attribute__((always_inline)) {
+    if constexpr (decltype(qc)::value == 0) stage_tile<N>(s_x0, X, tile, full, tail, C, slice, wave, lane);
+    else stage_tile<N>(s_x1, X, tile, full, tail, C, slice, wave, lane);
+  };
+  // a tile's readout weights: thread u loads 16 bytes of readout u / 64
+  // (a 16 x 16 float block), and (MASK) the first 16 lanes of wave 0 the
+  // active lists; units past the valid tokens read zero
+  struct Rows { u32x4_t h, li; };
+  auto load_rows = [&](int tile) __attribute__((always_inline)) {
+    const int rows = tile_rows(tile, full, tail);
+    const size_t t0 = rows > 0 ? (size_t)TM * tile : 0;
+    const int q = wave < NPRE ? wave : 0;   // uniform over the wave
+    Rows v;
+    v.h = ld_b128(make_rsrc(a.h_pre[q] + t0 * N, wave < NPRE ? (uint32_t)(rows * N * 4) : 0u), (uint32_t)(lane * 16), 0);
+    if constexpr (MASK)
+      v.li = ld_b128(make_rsrc(a.idx + t0 * K, (uint32_t)(rows * K * 4)), (uint32_t)(tid * 16), 0);
+    return v;
+  };
+  auto store_rows = [&](int q, const Rows& v) __attribute__((always_inline)) {
+    if (wave < NPRE) reinterpret_cast<u32x4_t*>(&s_h[q][wave][0])[lane] = v.h;
+    if constexpr (MASK)
+      if (tid * 4 < TM * K) reinterpret_cast<u32x4_t*>(&s_ri[q][0])[tid] = v.li;
+  };
+
+  int p = team;
+  if (p >= ntiles) return;
+  constexpr int LPW = N * NQ / SSB;
+  dma(p, Q0{});
+  {
+    const Rows v = load_rows(p);
+    dma(p + nteams, Q1{});
+    wait_vmcnt<LPW>();
+    store_rows(0, v);
+  }
+  stage_barrier<LPW>();
+
+  const uint32_t fofs = staged_frag(wave, g, r);
+  constexpr uint32_t SBYTES = NQ * WAVE * 16;
+  // vector memory operations of one step: the next tile's rows, the tile
+  // loads, the readout stores
+  constexpr int VM_STEP = 1 + (MASK ? 1 : 0) + LPW + NPRE;
+  auto tile_step = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    const int p1 = p + nteams;
+    const char* xq = reinterpret_cast<const char*>(q == 0 ? &s_x0[0][0][0] : &s_x1[0][0][0]);
+    u32x4_t x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = *reinterpret_cast<const u32x4_t*>(xq + (uint32_t)i * SBYTES + fofs);
+    float h[NPRE][N];
+#pragma unroll
+    for (int qq = 0; qq < NPRE; ++qq)
+#pragma unroll
+      for (int i = 0; i < N; ++i) h[qq][i] = s_h[q][qq][r * N + i];
+    uint32_t mk = 0;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const int v = j < K ? s_ri[q][r * K + j] : -1;
+        if (v >= 0 && v < N) mk |= 1u << v;
+      }
+    }
+    stage_barrier<63>();   // every wave is past its reads of this slot
+    const Rows nx = load_rows(p1);
+    dma(p1 + nteams, qc);
+    float acc[NPRE][VEC];
+#pragma unroll
+    for (int qq = 0; qq < NPRE; ++qq)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[qq][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float f[VEC];
+      E::unpack(x[i], f);
+#pragma unroll
+      for (int qq = 0; qq < NPRE; ++qq) {
+        const float hv = (qq > 0 && ((mk >> i) & 1u)) ? 0.f : h[qq][i];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[qq][e] = fmaf(hv, f[e], acc[qq][e]);
+      }
+    }
+    {
+      const int rows = kb0 < C / KB ? tile_rows(p, full, tail) : 0;
+      const size_t t0 = rows > 0 ? (size_t)TM * p : 0;
+      const uint32_t o = (uint32_t)(((size_t)r * C + (size_t)kb0 * KB + VEC * g) * sizeof(T));
+#pragma unroll
+      for (int qq = 0; qq < NPRE; ++qq)
+        st_b128<CP_NT>(E::packv(acc[qq]),
+                       make_rsrc(reinterpret_cast<T*>(a.out[qq]) + t0 * C, (uint32_t)((size_t)rows * C * sizeof(T))), o);
+    }
+    store_rows(q ^ 1, nx);
+    stage_barrier<VM_STEP>();
+    p = p1;
+  };
+  do {
+    tile_step(Q0{});
+    tile_step(Q1{});
+  } while (p < ntiles);
+  wait_vmcnt<0>();   // no load into LDS outlives the workgroup
+}
+
+bool flash_read_s_applies(const Plan& P) {
+  return XHC_PRE_STAGED && P.N == 16 && P.dtype == XHC_BF16 && P.C % (SSB * Bf16::KB) == 0 && P.ntiles > 0 &&
+         P.K <= 4;
+}
+
 // Routing projection of a whole state (first layer of a chain), with the
 // state staged through LDS as in the pre pass above: every stream's rows,
 // no masking, the routing partials alone.  D gives the column tiles and the
@@ -2886,6 +3028,22 @@ bool launch_xhc_pre_chained(const Plan& P, const xhc_weights* w, const Plan* Pn,
   if (!launch_pack(Pn, wn, wsn, &P, w, ws, &P, ws, st)) return false;
   return P.dtype == XHC_BF16 ? pre_chained_dispatch<Bf16>(P, w, Pn, X, inp, ws, wsn, st)
                              : pre_chained_dispatch<F32>(P, w, Pn, X, inp, ws, wsn, st);
+}
+
+// xHC-Flash readouts at N = 16 from the staged pass: NPRE outputs (4 with
+// the active streams left out of readouts 1.., else 2).
+bool launch_flash_read_s(const Plan& P, const void* X, void* const* out, const float* const* h_pre, const int* idx,
+                         int npre, hipStream_t st) {
+  if (!flash_read_s_applies(P) || (npre != 2 && npre != 4)) return false;
+  FlashReadSArgs a;
+  a.X = X; a.idx = idx; a.T = (int)P.T; a.C = P.C; a.G = P.Gp; a.K = P.K; a.ntiles = (int)P.ntiles;
+  for (int q = 0; q < 4; ++q) {
+    a.out[q] = q < npre ? out[q] : nullptr;
+    a.h_pre[q] = q < npre ? h_pre[q] : nullptr;
+  }
+  if (npre == 2) flash_read_s_kernel<2, false><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+  else flash_read_s_kernel<4, true><<<(unsigned)persist_grid_s(P), SNTHR, 0, st>>>(a);
+  return true;
 }
 
 bool flash4_route_p_applies(const Plan& P) {

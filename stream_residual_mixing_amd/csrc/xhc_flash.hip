@@ -428,7 +428,11 @@ bool flash_pre_launch(const Plan& P, const xhcf_weights* w, const void* X, void*
   d.X = X; d.out[0] = inp_a; d.out[1] = inp_m; d.T = (int)P.T; d.C = P.C; d.K = P.K;
   d.h_pre[0] = r.h_pre[0]; d.h_pre[1] = r.h_pre[1];
   const int nkbC = P.C / E::KB;
-  flash_read_kernel<E, N, 2, false><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
+  if (flash_read_s_applies(P)) {
+    if (!launch_flash_read_s(P, X, d.out, d.h_pre, nullptr, 2, st)) return false;
+  } else {
+    flash_read_kernel<E, N, 2, false><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
+  }
 
   float* part2 = reinterpret_cast<float*>(ws + P.o_part2);
   act_proj_launch<E, 1, K>(P, X, ws, reinterpret_cast<const uint4*>(ws + P.o_wact_a), part2, st);
@@ -528,7 +532,11 @@ bool flash4_pre_launch(const Plan& P, const xhcf4_weights* w, const void* X, voi
   for (int q = 1; q < 4; ++q) d.out[q] = static_cast<TT*>(bases) + (size_t)(q - 1) * P.T * P.C;
   for (int q = 0; q < 4; ++q) d.h_pre[q] = r.h_pre[q];
   const int nkbC = P.C / E::KB;
-  flash_read_kernel<E, N, 4, true><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
+  if (flash_read_s_applies(P)) {
+    if (!launch_flash_read_s(P, X, d.out, d.h_pre, d.idx, 4, st)) return false;
+  } else {
+    flash_read_kernel<E, N, 4, true><<<(unsigned)(P.ntiles * ((nkbC + TWV - 1) / TWV)), TNTHR, 0, st>>>(d);
+  }
 
   // the first sublayer's post-map from the group-entry active rows
   float* part2 = reinterpret_cast<float*>(ws + P.o_part2);

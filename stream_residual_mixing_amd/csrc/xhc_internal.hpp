@@ -181,6 +181,12 @@ struct Flash4Route {
   float* h_pre[4];
 };
 bool flash4_route_p_applies(const Plan& P);
+// xHC-Flash readouts at N = 16 staged through LDS (bf16, C a multiple of 128
+// channels): npre = 2 (Flash) or 4 with the active streams left out of
+// readouts 1.. (Flash-4sub).  False when it does not apply.
+bool flash_read_s_applies(const Plan& P);
+bool launch_flash_read_s(const Plan& P, const void* X, void* const* out, const float* const* h_pre, const int* idx,
+                         int npre, hipStream_t st);
 bool launch_flash4_route_p(const Plan& P, const void* X, const void* wp, float* part, const Flash4Route& o,
                            hipStream_t st);
 // xHC-Flash block (xhc_flash.hip)
