@@ -448,7 +448,21 @@ bool launch_pack(const Plan* Pf, const xhc_weights* wf, char* wsf, const Plan* P
   return true;
 }
 
+#ifndef XHC_PRE_VIA_CHAIN_MIN_T
+#define XHC_PRE_VIA_CHAIN_MIN_T 4096
+#endif
+// Large bf16 batches at N = 16, k > 2, m = 2, C a multiple of 128: the
+// routing pass and the last-sublayer pre pass of the chained calls (both
+// staged through LDS) instead of the one-pass kernel above, whose
+// workgroups wait for each other's routing partials.
+static bool pre_via_chain(const Plan& P) {
+  return P.dtype == XHC_BF16 && P.N == 16 && P.K > 2 && P.m == 2 && P.C % 128 == 0 &&
+         P.T >= XHC_PRE_VIA_CHAIN_MIN_T;
+}
+
 bool launch_xhc_pre(const Plan& P, const void* X, void* inp, const xhc_weights* w, char* ws, hipStream_t st) {
+  if (pre_via_chain(P))
+    return launch_xhc_route(P, X, w, ws, st) && launch_xhc_pre_chained(P, w, nullptr, nullptr, X, inp, ws, nullptr, st);
   return P.dtype == XHC_BF16 ? xhc_pre_fused_launch<Bf16>(P, X, inp, w, ws, st)
                              : xhc_pre_fused_launch<F32>(P, X, inp, w, ws, st);
 }
