@@ -450,16 +450,20 @@ def _attention_post_pass(name):
     return bool(m) and m.group(1) == "1"
 
 
-def _split_calls(rows):
+def _split_calls(rows, single=False):
     """Group this library's dispatches of one step into calls, in order: a
     call starts at a weight-packing kernel (xHC or mHC), at the Gram kernel, at an apply
     kernel not preceded by the Gram kernel, at the persistent post pass that
-    also writes (the chained attention-type post call), or at the mHC write."""
+    also writes (the chained attention-type post call), or at the mHC write.
+    With per-sublayer calls (single), a weight-packing kernel right after the
+    routing finalize continues the call: a large xhc_pre runs the routing
+    pass and then the pre pass, each with its own packing."""
     calls, prev = [], ""
     for name, v in rows:
         if "xhc::" not in name:
             continue
-        start = ("xhc_prep_kernel" in name or "pack_b_kernel" in name or "xhc_gram_kernel" in name
+        cont = single and "xhc_prep_kernel" in name and "xhc_route_fin_kernel" in prev
+        start = (("xhc_prep_kernel" in name and not cont) or "pack_b_kernel" in name or "xhc_gram_kernel" in name
                  or ("xhc_apply_kernel" in name and "xhc_gram_kernel" not in prev)
                  or _attention_post_pass(name) or "mhc_post_kernel" in name)
         if start or not calls:
@@ -469,13 +473,19 @@ def _split_calls(rows):
     return calls
 
 
+_FORWARD_PRE_KERNELS = ("xhc_pre_fused_kernel", "xhc_prep_kernel", "xhc_proj_s_kernel", "xhc_proj_p_kernel",
+                        "xhc_route_fin_kernel", "xhc_pre_chained_s_kernel", "xhc_pre_chained_kernel",
+                        "xhc_act_fin_kernel")
+
+
 def _split_backward_calls(rows):
-    """Backward workload: skip the set-up (xhc_pre of each sublayer); a call
-    starts at an application kernel (xhc_post_backward) or at the first
-    weight-packing kernel of a run of them (xhc_pre_backward)."""
+    """Backward workload: skip the set-up (xhc_pre of each sublayer, by any
+    of its kernels); a call starts at an application kernel
+    (xhc_post_backward) or at the first weight-packing kernel of a run of
+    them (xhc_pre_backward)."""
     calls, prev = [], ""
     for name, v in rows:
-        if "xhc::" not in name or "xhc_pre_fused_kernel" in name or "xhc_prep_kernel" in name:
+        if "xhc::" not in name or any(k in name for k in _FORWARD_PRE_KERNELS):
             continue
         start = "bwd_apply_kernel" in name or ("pack_b_kernel" in name and "pack_b_kernel" not in prev)
         if start or not calls:
@@ -495,10 +505,14 @@ def traffic_summary(workload, pmcdir):
         vals = [v for n, v in _pmc_rows(os.path.join(pmcdir, sub)) if "copyBuffer" in n and v > 1e5]
         scale[c] = copy_bytes / (sum(vals) / len(vals) * 1024)
     kind, cfgs, kinds = layer_configs(workload)
-    split = _split_backward_calls if kind == "xhcb" else _split_calls
+    api = default_api(workload)
+    if kind == "xhcb":
+        split = _split_backward_calls
+    else:
+        def split(rows):
+            return _split_calls(rows, single=(api == "single"))
     fetch = split(_pmc_rows(os.path.join(pmcdir, "chain_fetch")))
     write = split(_pmc_rows(os.path.join(pmcdir, "chain_write")))
-    api = default_api(workload)
     if kind == "xhcb":
         names = [f"{p}_{lk}" for lk in reversed(kinds) for p in ("xhc_post_backward", "xhc_pre_backward")]
     elif kind == "xhc" and api == "single":

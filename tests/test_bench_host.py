@@ -24,6 +24,11 @@ def test_backward_dispatches_group_into_calls():
     k = "xhc::"
     rows = [(f"void {k}xhc_prep_kernel<Bf16>", 1.0), (f"void {k}xhc_pre_fused_kernel<Bf16, 16, 4, 4>", 1.0),
             (f"void {k}xhc_pre_fused_kernel<Bf16, 16, 4, 1>", 1.0), ("normal_kernel", 5.0)]
+    # a large set-up xhc_pre: the routing pass, then the last-sublayer pre pass
+    rows += [(f"void {k}{n}", 1.0) for n in ("xhc_prep_kernel<Bf16>", "xhc_proj_s_kernel<Bf16, 16, RouteDims<16>>",
+                                             "xhc_route_fin_kernel<16, 4>", "xhc_prep_kernel<Bf16>",
+                                             "xhc_pre_chained_s_kernel<Bf16, 16, 4, 4, 2, false>",
+                                             "xhc_act_fin_kernel<4, 4>")]
     post_m = [f"void {k}(anonymous namespace)::bwd_apply_kernel<Bf16, 16, 4, 4>(Args)",
               f"void {k}(anonymous namespace)::bwd_conv_kernel<Bf16>(Args)", f"{k}(anonymous namespace)::bwd_reduce_kernel"]
     pre = [f"void {k}pack_b_kernel<Bf16>", f"void {k}pack_b_kernel<Bf16>", f"void {k}proj_gen_kernel<Bf16, 2>",
@@ -63,3 +68,16 @@ def test_counter_rows_split_into_calls():
     mhc = [k("pack_b_kernel<xhc::Bf16>"), k("mhc_proj_kernel<18>"), k("mhc_read_kernel<xhc::Bf16, 16>"),
            k("mhc_post_kernel<xhc::Bf16, 16>")]
     assert [len(c) for c in bench._split_calls(mhc)] == [3, 1]
+    # the staged attention-type post pass starts its call too
+    staged = [k("xhc_post_s_kernel<xhc::Bf16, 16, 4, 2, 1>"), k("xhc_route_fin_kernel<16, 4>"),
+              k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_pre_chained_s_kernel<xhc::Bf16, 16, 4, 4, 2, true>"),
+              k("xhc_act_fin_kernel<4, 4>")]
+    assert [len(c) for c in bench._split_calls(staged)] == [2, 3]
+    # per-sublayer calls: a large xhc_pre is the routing pass and then the
+    # pre pass, one call; the MLP-type xhc_post starts at its Gram pass
+    single = [k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_proj_s_kernel<xhc::Bf16, 16>"), k("xhc_route_fin_kernel<16, 4>"),
+              k("xhc_prep_kernel<xhc::Bf16>"), k("xhc_pre_chained_s_kernel<xhc::Bf16, 16, 4, 4, 2, false>"),
+              k("xhc_act_fin_kernel<4, 4>"), k("xhc_gram_kernel<xhc::Bf16>"),
+              k("xhc_apply_kernel<xhc::Bf16, 4, 4, 6, 0>")]
+    assert [len(c) for c in bench._split_calls(single, single=True)] == [6, 2]
+    assert [len(c) for c in bench._split_calls(single)] == [3, 3, 2]
