@@ -1990,6 +1990,9 @@ struct PostPArgs {
 #ifndef XHC_POST_PD
 #define XHC_POST_PD 1
 #endif
+#ifndef XHC_POST_NS_SPLIT
+#define XHC_POST_NS_SPLIT 1
+#endif
 constexpr int POST_PD = XHC_POST_PD;   // steps of state loads in flight ahead of the compute (1 measured best of 1, 2, 3)
 
 // Calls f(std::integral_constant<int, Q>) for Q = 0 .. NQ - 1.
@@ -2201,26 +2204,40 @@ __global__ __launch_bounds__(PNTHR, 1) void xhc_post_p_kernel(PostPArgs a) {
           bs[2][e] = fmaf(s_cw[4][cl + e], bs[0][e], 0.f);
           bs[3][e] = fmaf(s_cw[12][cl + e], bs[0][e], 0.f);
         }
-        for_each_c<11>([&](auto ic) __attribute__((always_inline)) {
-          constexpr int i = decltype(ic)::value + 1;   // lag
-          u32x4_t lg;
+        // lags 1 .. 11; with MASKED, those reaching before the token's
+        // sequence start read zero
+        auto lags = [&](auto masked) __attribute__((always_inline)) {
+          for_each_c<11>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value + 1;   // lag
+            u32x4_t lg;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            // row_shl (16 - i): lane r < i takes lane r + 16 - i of the rows
-            // before; row_shr i: lane r >= i takes lane r - i of this tile
-            const int pv = __builtin_amdgcn_update_dpp(0, (int)st.op[d], 0x100 + (16 - i), 0xf, 0xf, false);
-            lg[d] = (uint32_t)__builtin_amdgcn_update_dpp(pv, (int)st.o[d], 0x110 + i, 0xf, 0xf, false);
-          }
-          if (near_start) lg = i <= spos ? lg : zero;
-          float h[VEC];
-          E::unpack(lg, h);
+            for (int d = 0; d < 4; ++d) {
+              // row_shl (16 - i): lane r < i takes lane r + 16 - i of the rows
+              // before; row_shr i: lane r >= i takes lane r - i of this tile
+              const int pv = __builtin_amdgcn_update_dpp(0, (int)st.op[d], 0x100 + (16 - i), 0xf, 0xf, false);
+              lg[d] = (uint32_t)__builtin_amdgcn_update_dpp(pv, (int)st.o[d], 0x110 + i, 0xf, 0xf, false);
+            }
+            if constexpr (decltype(masked)::value) lg = i <= spos ? lg : zero;
+            float h[VEC];
+            E::unpack(lg, h);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            if constexpr (i < 4) bs[1][e] = fmaf(s_cw[i][cl + e], h[e], bs[1][e]);
-            if constexpr (i < 8) bs[2][e] = fmaf(s_cw[4 + i][cl + e], h[e], bs[2][e]);
-            bs[3][e] = fmaf(s_cw[12 + i][cl + e], h[e], bs[3][e]);
-          }
-        });
+            for (int e = 0; e < VEC; ++e) {
+              if constexpr (i < 4) bs[1][e] = fmaf(s_cw[i][cl + e], h[e], bs[1][e]);
+              if constexpr (i < 8) bs[2][e] = fmaf(s_cw[4 + i][cl + e], h[e], bs[2][e]);
+              bs[3][e] = fmaf(s_cw[12 + i][cl + e], h[e], bs[3][e]);
+            }
+          });
+        };
+        // Two copies under a branch that is uniform over the wave: left to
+        // itself the compiler turns the mask into selects on every lag of
+        // every tile (~55 vector instructions per step) though most tiles
+        // lie clear of a sequence start.
+        if constexpr (XHC_POST_NS_SPLIT) {
+          if (near_start) lags(std::true_type{});
+          else lags(std::false_type{});
+        } else {
+          lags(std::true_type{});
+        }
       }
       const __amdgpu_buffer_rsrc_t rx = x_rsrc(step);
 #pragma unroll
