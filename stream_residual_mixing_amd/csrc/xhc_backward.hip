@@ -228,13 +228,13 @@ __global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
   for (int cg = tid; cg < ngrp; cg += BT) {
     const int c = cg * V;
     float fi[V], y[K][V], xr[K][V], g[KR][V];
+    uint4 raw[K];
     E::unpack(ld16(di + c), fi);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       E::unpack(ld16(dXn + (size_t)s_idx[i] * C + c), y[i]);
-      const uint4 raw = ld16(X + (size_t)s_idx[i] * C + c);
-      st16(xa + (size_t)i * C + c, raw);
-      E::unpack(raw, xr[i]);
+      raw[i] = ld16(X + (size_t)s_idx[i] * C + c);
+      E::unpack(raw[i], xr[i]);
     }
     write_basis<E, KR>(ot, s, C, c, a.conv_w, g);
 #pragma unroll
@@ -262,6 +262,11 @@ __global__ __launch_bounds__(BT) void bwd_apply_kernel(BwdApplyArgs a) {
       for (int qb = qa; qb < KR; ++qb, ++gi)
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[O_G + gi] = fmaf(g[qa][e], g[qb][e], acc[O_G + gi]);
+    // the gathered active rows for the generation half, stored after every
+    // load of the step (a store in between would keep the later loads, which
+    // the compiler cannot prove apart from it, from going out early)
+#pragma unroll
+    for (int i = 0; i < K; ++i) st16(xa + (size_t)i * C + c, raw[i]);
   }
 #pragma unroll
   for (int i = 0; i < NACC; ++i) {
@@ -950,8 +955,11 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
   static_assert(NCH == 4, "chunk mapping assumes 4 chunks per thread");
   // Full mode also takes each chunk's H_pre or position in the active list
   // one block ahead, so that the gradient loads need not wait for it.
+  // The block's coefficient rows (thread u: token u / 8, columns 4 (u % 8)
+  // .. + 3) and per-token scalars come with its state chunks, a block ahead.
   uint4 xn[NCH];
   float hn[NCH];
+  float gn[4], scn[2] = {0.f, 0.f};
   auto load_x = [&](int tb, int nt) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -962,41 +970,24 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
       xn[k] = in ? ld16(X + (size_t)(tb + tu) * a.R + row) : make_uint4(0, 0, 0, 0);
       if (!a.act) hn[k] = in ? a.rsel[(tb + tu) * a.N + (int)(row / a.C)] : 0.f;
     }
+    const int tu = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      gn[e] = (tu < nt && c4 + e < ncol) ? a.G[(size_t)(tb + tu) * ncol + c4 + e] : 0.f;
+    if (threadIdx.x < TB) {
+      const int t = threadIdx.x;
+      scn[0] = t < nt ? a.sc[(size_t)(tb + t) * 4 + (a.act ? 2 : 0)] : 0.f;
+      scn[1] = (t < nt && !a.act) ? a.sc[(size_t)(tb + t) * 4 + 1] : 0.f;
+    }
   };
   if (t0 < t1) load_x(t0, t1 - t0 < TB ? t1 - t0 : TB);
   for (int tb = t0; tb < t1; tb += TB) {
     const int nt = t1 - tb < TB ? t1 - tb : TB;
     __syncthreads();
-    // state rows as they are in memory (loaded during the previous block)
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int u = threadIdx.x + BT * k;
-      *reinterpret_cast<uint4*>(&s_x[u / (4 * RW / 8)][(u % (4 * RW / 8)) * 8]) = xn[k];
-    }
-    // coefficients: thread u takes token u / 8, columns 4 (u % 8) .. + 3
-    {
-      const int tu = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int col = c4 + e;
-        const float v = (tu < nt && col < ncol) ? a.G[(size_t)(tb + tu) * ncol + col] : 0.f;
-        const uint32_t hi = f32_to_bf16(v);
-        const uint32_t lo = f32_to_bf16(v - __uint_as_float(hi << 16));
-        s_g[0][tu][col] = (uint16_t)hi;
-        s_g[1][tu][col] = (uint16_t)lo;
-        s_gt[0][col][tu] = (uint16_t)hi;
-        s_gt[1][col][tu] = (uint16_t)lo;
-      }
-      if (threadIdx.x < TB) {
-        const int t = threadIdx.x;
-        s_c[t][0] = t < nt ? a.sc[(size_t)(tb + t) * 4 + (a.act ? 2 : 0)] : 0.f;
-        s_c[t][1] = (t < nt && !a.act) ? a.sc[(size_t)(tb + t) * 4 + 1] : 0.f;
-      }
-    }
-    // this block's gradient chunks, then the next block's state chunks.
-    // Full mode: d_X and d_inp for a row outside the active list, the float
-    // gradient so far for one in it.  Active mode: the active row's float
-    // gradient so far.
+    // this block's gradient chunks first, so that their latency runs under
+    // the staging and the products below.  Full mode: d_X and d_inp for a row
+    // outside the active list, the float gradient so far for one in it.
+    // Active mode: the active row's float gradient so far.
     uint16_t* dr[NCH];
     uint4 dv[NCH], fv[NCH];
     int pos[NCH];
@@ -1032,6 +1023,32 @@ __global__ __launch_bounds__(BT) void bwd_rows_mfma_kernel(BwdRowArgs a) {
                        : make_uint4(0, 0, 0, 0);
       }
     }
+    // state rows as they are in memory (loaded during the previous block)
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int u = threadIdx.x + BT * k;
+      *reinterpret_cast<uint4*>(&s_x[u / (4 * RW / 8)][(u % (4 * RW / 8)) * 8]) = xn[k];
+    }
+    // coefficients (loaded during the previous block)
+    {
+      const int tu = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = c4 + e;
+        const float v = gn[e];
+        const uint32_t hi = f32_to_bf16(v);
+        const uint32_t lo = f32_to_bf16(v - __uint_as_float(hi << 16));
+        s_g[0][tu][col] = (uint16_t)hi;
+        s_g[1][tu][col] = (uint16_t)lo;
+        s_gt[0][col][tu] = (uint16_t)hi;
+        s_gt[1][col][tu] = (uint16_t)lo;
+      }
+      if (threadIdx.x < TB) {
+        s_c[threadIdx.x][0] = scn[0];
+        s_c[threadIdx.x][1] = scn[1];
+      }
+    }
+    // then the next block's state chunks and coefficients
     if (tb + TB < t1) load_x(tb + TB, t1 - tb - TB < TB ? t1 - tb - TB : TB);
     __syncthreads();
     // weight gradient: dW^T[col][row] += sum over the block's tokens; the B
